@@ -1,0 +1,77 @@
+// Device helpers shared by the libeagle kernels (gfx950, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/eagle.h"
+
+#define EDEV __device__ __forceinline__
+
+namespace eagle {
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+constexpr int kIdxNone = 0x7fffffff;  // loses every (key desc, idx asc) tie
+
+EDEV float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN kept quiet).
+EDEV uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+EDEV float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+EDEV float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+EDEV double wave_sum_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+EDEV int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// (key desc, idx asc) order.
+EDEV bool beats(float ka, int ia, float kb, int ib) { return ka > kb || (ka == kb && ia < ib); }
+EDEV bool beats_d(double ka, int ia, double kb, int ib) { return ka > kb || (ka == kb && ia < ib); }
+
+// Wave-wide argmax under (key desc, idx asc); every lane ends with the winner.
+EDEV void wave_argmax(float& key, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    float k2 = __shfl_xor(key, o);
+    int i2 = __shfl_xor(idx, o);
+    if (beats(k2, i2, key, idx)) { key = k2; idx = i2; }
+  }
+}
+
+EDEV void wave_argmax_d(double& key, int& idx) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    double k2 = __shfl_xor(key, o);
+    int i2 = __shfl_xor(idx, o);
+    if (beats_d(k2, i2, key, idx)) { key = k2; idx = i2; }
+  }
+}
+
+EDEV void set_status(int32_t* st, int bits) {
+  if (st) atomicOr(st, bits);
+}
+
+}  // namespace eagle

@@ -1,0 +1,207 @@
+// Host side of libeagle: the C ABI declared in include/eagle.h.  Every entry
+// point validates its arguments on the host (before any HIP call), carves its
+// scratch out of the caller's workspace and enqueues its kernels on the
+// caller's stream.
+#include <math.h>
+
+#include "common.h"
+#include "kernels.h"
+
+using namespace eagle;
+
+namespace {
+
+constexpr size_t kCounterBytes = 64 * 1024;           // ticket counters at the workspace head
+constexpr int kMaxTickets = (int)(kCounterBytes / 4);
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// Shape checks shared by expand and accept.
+int check_tree_params(const eagle_tree_params* p) {
+  if (!p) return EAGLE_ERR_NULL;
+  const int64_t B = p->batch, V = p->vocab, D = p->depth, k = p->topk, m = p->m;
+  if (B < 1 || B > (1 << 20)) return EAGLE_ERR_SHAPE;
+  if (k < 1 || k > EAGLE_MAX_TOPK) return EAGLE_ERR_SHAPE;
+  if (D < 1 || D > EAGLE_MAX_DEPTH) return EAGLE_ERR_SHAPE;
+  if (V < k || V > EAGLE_MAX_VOCAB) return EAGLE_ERR_SHAPE;
+  const int64_t S = 1 + (D - 1) * k, P = S * k;
+  if (P > EAGLE_MAX_POOL) return EAGLE_ERR_SHAPE;
+  if (m < 1 || m > P || m + 1 > EAGLE_MAX_NODES) return EAGLE_ERR_SHAPE;
+  if (!(p->temperature >= 0.f) || !isfinite(p->temperature)) return EAGLE_ERR_SHAPE;
+  return EAGLE_OK;
+}
+
+int check_attn(int32_t B, int32_t n, int32_t hq, int32_t hkv, int32_t dh, int32_t Lmax, int32_t dtype) {
+  if (B < 1 || n < 1 || n > EAGLE_MAX_NODES || hq < 1 || hkv < 1 || hq % hkv != 0 || Lmax < 0) return EAGLE_ERR_SHAPE;
+  if ((int64_t)n * (hq / hkv) > (1 << 16)) return EAGLE_ERR_SHAPE;
+  if (dtype == EAGLE_BF16) {
+    if (dh != 64 && dh != 128) return EAGLE_ERR_DTYPE;
+  } else if (dtype == EAGLE_F32) {
+    if (dh != 16 && dh != 32 && dh != 64 && dh != 128) return EAGLE_ERR_DTYPE;
+  } else {
+    return EAGLE_ERR_DTYPE;
+  }
+  return EAGLE_OK;
+}
+
+int check_lm(int32_t rows, int32_t hidden, int32_t vocab, int32_t dtype) {
+  if (rows < 1 || hidden < 1 || vocab < 1 || vocab > (1 << 24)) return EAGLE_ERR_SHAPE;
+  if (dtype == EAGLE_BF16) {
+    if (hidden % 128 != 0) return EAGLE_ERR_SHAPE;
+  } else if (dtype == EAGLE_F32) {
+    if (hidden > 16384) return EAGLE_ERR_SHAPE;  // the fp32 path keeps one input row in LDS
+  } else {
+    return EAGLE_ERR_DTYPE;
+  }
+  if (lm_mtiles(rows) > kMaxTickets) return EAGLE_ERR_SHAPE;
+  return EAGLE_OK;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? EAGLE_OK : EAGLE_ERR_LAUNCH; }
+
+float* stage_area(void* ws) { return reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes); }
+
+}  // namespace
+
+extern "C" {
+
+int32_t eagle_abi_version(void) { return (1 << 16) | 0; }
+
+const char* eagle_error_string(int32_t code) {
+  switch (code) {
+    case EAGLE_OK: return "ok";
+    case EAGLE_ERR_NULL: return "null pointer";
+    case EAGLE_ERR_SHAPE: return "invalid shape";
+    case EAGLE_ERR_DTYPE: return "unsupported dtype";
+    case EAGLE_ERR_WORKSPACE: return "workspace too small";
+    case EAGLE_ERR_LAUNCH: return "kernel launch failed";
+    case EAGLE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    default: return "unknown error";
+  }
+}
+
+size_t eagle_workspace_size(const eagle_tree_params* p, int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_prefix,
+                            int32_t hidden) {
+  if (check_tree_params(p) != EAGLE_OK) return 0;
+  const int B = p->batch, V = p->vocab, k = p->topk, D = p->depth;
+  const int S = 1 + (D - 1) * k, N = p->m + 1;
+  size_t need = exp_ws_bytes(B, S, V, k);
+  if (hq > 0 && hkv > 0 && head_dim > 0) {
+    const int dt = head_dim == 64 || head_dim == 128 ? EAGLE_BF16 : EAGLE_F32;
+    if (check_attn(B, N, hq, hkv, head_dim, max_prefix, dt) != EAGLE_OK) return 0;
+    const AttnPlan pl = attn_plan(B, N, hq, hkv, head_dim, max_prefix, dt);
+    const size_t a = attn_ws_bytes(B, hkv, head_dim, pl);
+    if (a > need) need = a;
+  }
+  if (hidden > 0) {
+    const size_t l = lm_ws_bytes(B * N, V);
+    if (l > need) need = l;
+  }
+  need = (need + 255) / 256 * 256;
+  return kCounterBytes + need;
+}
+
+int eagle_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws) return EAGLE_ERR_NULL;
+  if (ws_bytes < kCounterBytes) return EAGLE_ERR_WORKSPACE;
+  return launch_status(launch_zero_ints(static_cast<int32_t*>(ws), kCounterBytes / 4, (hipStream_t)stream));
+}
+
+int eagle_expand_tree(const eagle_tree_params* p, const float* draft_logits, const int32_t* root_token,
+                      int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
+                      int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_tok, float* pool_q,
+                      int32_t* pool_flat, int32_t* slot_src, float* slot_stats, void* ws, size_t ws_bytes,
+                      int32_t* dev_status, void* stream) {
+  int rc = check_tree_params(p);
+  if (rc != EAGLE_OK) return rc;
+  if (!draft_logits || !root_token || !node_tok || !node_parent || !node_depth || !node_sib || !node_slot ||
+      !node_value || !node_q || !pool_tok || !pool_q || !pool_flat || !slot_src || !slot_stats || !ws)
+    return EAGLE_ERR_NULL;
+  if (!aligned16(draft_logits)) return EAGLE_ERR_ALIGN;
+  const int B = p->batch, V = p->vocab, k = p->topk, D = p->depth;
+  const int S = 1 + (D - 1) * k;
+  if (ws_bytes < kCounterBytes + exp_ws_bytes(B, S, V, k)) return EAGLE_ERR_WORKSPACE;
+  return launch_status(launch_expand(B, S, V, D, k, p->m, p->temperature, p->seed, p->round_id, draft_logits,
+                                     root_token, node_tok, node_parent, node_depth, node_sib, node_slot, node_value,
+                                     node_q, pool_tok, pool_q, pool_flat, slot_src, slot_stats, stage_area(ws),
+                                     dev_status, (hipStream_t)stream));
+}
+
+int eagle_build_tree_mask(int32_t batch, int32_t n, const int32_t* node_parent, const int32_t* node_depth,
+                          const int32_t* prefix_len, uint64_t* mask, int32_t* pos, int32_t* dev_status,
+                          void* stream) {
+  if (batch < 1 || n < 1 || n > EAGLE_MAX_NODES) return EAGLE_ERR_SHAPE;
+  if (!node_parent || !node_depth || !prefix_len || !mask || !pos) return EAGLE_ERR_NULL;
+  return launch_status(launch_tree_mask(batch, n, node_parent, node_depth, prefix_len, mask, pos, dev_status,
+                                        (hipStream_t)stream));
+}
+
+int eagle_tree_attention(int32_t batch, int32_t n, int32_t hq, int32_t hkv, int32_t head_dim, int32_t max_prefix,
+                         int32_t dtype, const void* q, const void* k_prefix, const void* v_prefix,
+                         const int32_t* prefix_len, const void* k_tree, const void* v_tree, const uint64_t* mask,
+                         float scale, void* out, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  int rc = check_attn(batch, n, hq, hkv, head_dim, max_prefix, dtype);
+  if (rc != EAGLE_OK) return rc;
+  if (!isfinite(scale)) return EAGLE_ERR_SHAPE;
+  if (!q || !prefix_len || !k_tree || !v_tree || !mask || !out || !ws) return EAGLE_ERR_NULL;
+  if (max_prefix > 0 && (!k_prefix || !v_prefix)) return EAGLE_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k_tree) || !aligned16(v_tree) || !aligned16(out) ||
+      (max_prefix > 0 && (!aligned16(k_prefix) || !aligned16(v_prefix))))
+    return EAGLE_ERR_ALIGN;
+  const AttnPlan pl = attn_plan(batch, n, hq, hkv, head_dim, max_prefix, dtype);
+  if (ws_bytes < kCounterBytes + attn_ws_bytes(batch, hkv, head_dim, pl)) return EAGLE_ERR_WORKSPACE;
+  return launch_status(launch_attention(batch, n, hq, hkv, head_dim, max_prefix, dtype, q, k_prefix, v_prefix,
+                                        prefix_len, k_tree, v_tree, mask, scale, out, stage_area(ws), pl, dev_status,
+                                        (hipStream_t)stream));
+}
+
+int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dtype, const void* x, const void* w,
+                         float temperature, float* logits, float* row_stats, int32_t* row_argmax, float* probs,
+                         void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  int rc = check_lm(rows, hidden, vocab, dtype);
+  if (rc != EAGLE_OK) return rc;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return EAGLE_ERR_SHAPE;
+  if (!x || !w || !logits || !row_stats || !row_argmax || !ws) return EAGLE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w)) return EAGLE_ERR_ALIGN;
+  if (ws_bytes < kCounterBytes + lm_ws_bytes(rows, vocab)) return EAGLE_ERR_WORKSPACE;
+  return launch_status(launch_lmhead(rows, hidden, vocab, dtype, x, w, temperature, logits, row_stats, row_argmax,
+                                     probs, stage_area(ws), static_cast<int32_t*>(ws), dev_status,
+                                     (hipStream_t)stream));
+}
+
+int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok, const int32_t* node_parent,
+                        const int32_t* node_slot, const int32_t* pool_tok, const int32_t* pool_flat,
+                        const float* target_logits, const float* target_stats, const int32_t* target_argmax,
+                        const float* draft_logits, const float* slot_stats, const float* uniforms,
+                        int32_t* accept_len, int32_t* accept_path, int32_t* committed, int32_t* n_committed,
+                        int32_t* near_tie, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  int rc = check_tree_params(p);
+  if (rc != EAGLE_OK) return rc;
+  (void)ws;
+  (void)ws_bytes;
+  const bool greedy = !(p->temperature > 0.f);
+  if (!node_tok || !node_parent || !node_slot || !pool_tok || !pool_flat || !accept_len || !accept_path ||
+      !committed || !n_committed || !near_tie)
+    return EAGLE_ERR_NULL;
+  if (greedy ? !target_argmax : (!target_logits || !target_stats || !draft_logits || !slot_stats || !uniforms))
+    return EAGLE_ERR_NULL;
+  const int S = 1 + (p->depth - 1) * p->topk;
+  (void)S;
+  return launch_status(launch_accept(p->batch, p->m + 1, p->vocab, p->depth, p->topk, p->temperature, node_tok,
+                                     node_parent, node_slot, pool_tok, pool_flat, target_logits, target_stats,
+                                     target_argmax, draft_logits, slot_stats, uniforms, accept_len, accept_path,
+                                     committed, n_committed, near_tie, dev_status, (hipStream_t)stream));
+}
+
+int eagle_gather_rows(int32_t n_rows, int32_t row_elems, int32_t dtype, const void* table, int32_t table_rows,
+                      const int32_t* idx, void* out, int32_t* dev_status, void* stream) {
+  if (n_rows < 0 || row_elems < 1 || table_rows < 1) return EAGLE_ERR_SHAPE;
+  if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
+  if (n_rows == 0) return EAGLE_OK;
+  if (!table || !idx || !out) return EAGLE_ERR_NULL;
+  const int esz = dtype == EAGLE_F32 ? 4 : 2;
+  return launch_status(launch_gather(n_rows, row_elems * esz, table, table_rows, idx, out, dev_status,
+                                     (hipStream_t)stream));
+}
+
+}  // extern "C"

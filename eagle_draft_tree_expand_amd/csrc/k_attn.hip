@@ -1,0 +1,344 @@
+// Tree-masked verify attention: every tree query attends to all prefix keys of
+// its request and to the tree keys its ancestor mask allows.
+//
+// Method: EAGLE-1 notes ("EAGLE: Speculative Sampling Requires Rethinking
+// Feature Uncertainty"), sections 3.1 and 3.3 (tree attention: one target
+// forward scores the whole draft tree); hubwiz "LLM 推测性解码原理解读",
+// section 5 (each root-to-leaf path is scored as an independent sequence).
+//
+// Work split (flash-decoding style): one workgroup per (request b, kv head g,
+// key split).  Splits 0..nsplit-1 cover the prefix in runs of split_keys keys;
+// split nsplit covers the n tree keys under the mask.  All n*(hq/hkv) query
+// rows of the kv head live in the workgroup, so each K/V byte is read from HBM
+// once per split.  Each split writes unnormalised partials (O, running max,
+// running sum); attn_merge combines them with log-sum-exp weights.
+//
+// bf16 path (MFMA, gfx950 v_mfma_f32_16x16x32_bf16): scores are computed
+// transposed, S^T = K Q^T, so the softmax'ed tile is already in the B-operand
+// layout of O^T = V^T P^T (no shuffles); K is staged in LDS row-major and V
+// transposed.  fp32 path: plain FMA loop (small fp32 shapes).
+#include "common.h"
+#include "kernels.h"
+
+namespace eagle {
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr int kKT = 64;       // keys per LDS tile
+constexpr int kQT = 4;        // 16-row query tiles per wave
+constexpr int kRowsPerWG = 256;  // 4 waves x 4 tiles x 16 rows
+
+union B8 {
+  bf16x8 v;
+  uint4 u;
+  uint2 h[2];
+};
+
+// Partial record of one query row: O[DH], m, l.
+EDEV float* partial_row(float* ws, int b, int g, int hkv, int nsp1, int split, int rows_pad, int r, int DH) {
+  return ws + ((((size_t)b * hkv + g) * nsp1 + split) * rows_pad + r) * (DH + 2);
+}
+
+template <int DH>
+__global__ __launch_bounds__(256) void attn_split_bf16_kernel(
+    int n, int hq, int hkv, int Lmax, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
+    const uint16_t* __restrict__ vp, const int32_t* __restrict__ plen, const uint16_t* __restrict__ kt,
+    const uint16_t* __restrict__ vt, const uint64_t* __restrict__ mask, float scale, float* __restrict__ ws,
+    int rows, int rows_pad, int split_keys, int nsplit) {
+  constexpr int KPAD = DH + 8;    // K row stride in LDS (bf16 elements)
+  constexpr int VPAD = kKT + 8;   // V^T row stride in LDS
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * KPAD];
+  __shared__ __attribute__((aligned(16))) uint16_t Vts[DH * VPAD];
+
+  const int nrb = (rows + kRowsPerWG - 1) / kRowsPerWG;
+  const int split = blockIdx.x, g = blockIdx.y / nrb, rb = blockIdx.y - g * nrb, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = blockDim.x;
+  const int G = hq / hkv;
+  const int row0 = rb * kRowsPerWG + wave * 64;  // first query row of this wave
+  const int W = (n + 63) >> 6;
+  const bool tree = split == nsplit;
+  const int L = min(max(plen[b], 0), Lmax);  // prefix lengths beyond the buffer are clamped
+  int k_begin, k_end;
+  if (tree) { k_begin = 0; k_end = n; }
+  else { k_begin = split * split_keys; k_end = min(L, k_begin + split_keys); }
+
+  // Query tiles of this wave: rows [row0, row0 + 64).
+  const int col = lane & 15, grp = lane >> 4;
+  bf16x8 qreg[kQT][DH / 32];
+  const uint64_t* mrow[kQT];
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) {
+    const int r = row0 + t * 16 + col;
+    const bool ok = r < rows;
+    const int node = ok ? r / G : 0, h = g * G + (ok ? r % G : 0);
+    const uint16_t* qp = q + (((size_t)b * n + node) * hq + h) * DH;
+#pragma unroll
+    for (int ds = 0; ds < DH / 32; ++ds) {
+      B8 x;
+      x.u = ok ? *reinterpret_cast<const uint4*>(qp + ds * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
+      qreg[t][ds] = x.v;
+    }
+    mrow[t] = mask + ((size_t)b * n + node) * W;
+  }
+
+  floatx4 o[kQT][DH / 16];
+  float mrun[kQT], lrun[kQT];
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) {
+    mrun[t] = kNegInf;
+    lrun[t] = 0.f;
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt) o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  }
+
+  const uint16_t* kbase = tree ? kt + ((size_t)b * n * hkv + g) * DH : kp + (((size_t)b * hkv + g) * Lmax) * DH;
+  const uint16_t* vbase = tree ? vt + ((size_t)b * n * hkv + g) * DH : vp + (((size_t)b * hkv + g) * Lmax) * DH;
+  const size_t kstride = tree ? (size_t)hkv * DH : (size_t)DH;
+  const bool wave_active = row0 < rows;
+
+  for (int t0 = k_begin; t0 < k_end; t0 += kKT) {
+    // Stage K (row-major) and V (transposed) for keys [t0, t0 + 64).
+    __syncthreads();
+    for (int x = tid; x < kKT * (DH / 8); x += nthr) {
+      const int kk = x / (DH / 8), dc = (x - kk * (DH / 8)) * 8;
+      const int key = t0 + kk;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (key < k_end) {
+        kv = *reinterpret_cast<const uint4*>(kbase + (size_t)key * kstride + dc);
+        vv = *reinterpret_cast<const uint4*>(vbase + (size_t)key * kstride + dc);
+      }
+      *reinterpret_cast<uint4*>(&Ks[kk * KPAD + dc]) = kv;
+      const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vts[(dc + e) * VPAD + kk] = ve[e];
+    }
+    __syncthreads();
+    if (!wave_active) continue;
+
+#pragma unroll
+    for (int t = 0; t < kQT; ++t) {
+      // S^T tile: 64 keys x 16 queries, lane holds keys 16*kt + 4*grp + i of query col.
+      floatx4 s[4];
+#pragma unroll
+      for (int kt4 = 0; kt4 < 4; ++kt4) {
+        s[kt4] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ds = 0; ds < DH / 32; ++ds) {
+          B8 a;
+          a.u = *reinterpret_cast<const uint4*>(&Ks[(kt4 * 16 + col) * KPAD + ds * 32 + grp * 8]);
+          s[kt4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, qreg[t][ds], s[kt4], 0, 0, 0);
+        }
+      }
+      // scale + mask, tile max
+      float mx = kNegInf;
+#pragma unroll
+      for (int kt4 = 0; kt4 < 4; ++kt4)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = t0 + kt4 * 16 + grp * 4 + i;
+          bool vis = key < k_end;
+          if (tree && vis) vis = (mrow[t][key >> 6] >> (key & 63)) & 1ull;  // rows >= n read node 0
+          const float v = vis ? s[kt4][i] * scale : kNegInf;
+          s[kt4][i] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(mrun[t], mx);
+      const float alpha = (mnew == kNegInf) ? 1.f : __expf(mrun[t] - mnew);
+      mrun[t] = mnew;
+      float psum = 0.f;
+      B8 pb[2];
+#pragma unroll
+      for (int kt4 = 0; kt4 < 4; ++kt4) {
+        uint16_t hb[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float p = (s[kt4][i] == kNegInf) ? 0.f : __expf(s[kt4][i] - mnew);
+          psum += p;
+          hb[i] = f32_to_bf16(p);
+        }
+        pb[kt4 >> 1].h[kt4 & 1] = make_uint2((uint32_t)hb[0] | ((uint32_t)hb[1] << 16),
+                                             (uint32_t)hb[2] | ((uint32_t)hb[3] << 16));
+      }
+      lrun[t] = lrun[t] * alpha + psum;
+#pragma unroll
+      for (int dt = 0; dt < DH / 16; ++dt) {
+        o[t][dt] *= alpha;
+#pragma unroll
+        for (int beta = 0; beta < 2; ++beta) {
+          B8 a;
+          const uint16_t* vr = &Vts[(dt * 16 + col) * VPAD + beta * 32 + grp * 4];
+          a.h[0] = *reinterpret_cast<const uint2*>(vr);
+          a.h[1] = *reinterpret_cast<const uint2*>(vr + 16);
+          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, pb[beta].v, o[t][dt], 0, 0, 0);
+        }
+      }
+    }
+  }
+  if (!wave_active) return;
+
+  // Write partials: O^T lane holds d = 16*dt + 4*grp + i of query col.
+#pragma unroll
+  for (int t = 0; t < kQT; ++t) {
+    float l = lrun[t];
+    l += __shfl_xor(l, 16);
+    l += __shfl_xor(l, 32);
+    const int r = row0 + t * 16 + col;
+    if (r >= rows) continue;
+    float* pr = partial_row(ws, b, g, hkv, nsplit + 1, split, rows_pad, r, DH);
+#pragma unroll
+    for (int dt = 0; dt < DH / 16; ++dt)
+      *reinterpret_cast<float4*>(pr + dt * 16 + grp * 4) = make_float4(o[t][dt][0], o[t][dt][1], o[t][dt][2], o[t][dt][3]);
+    if (grp == 0) { pr[DH] = mrun[t]; pr[DH + 1] = l; }
+  }
+}
+
+// fp32 path: one thread per query row, keys staged in LDS.
+template <int DH>
+__global__ __launch_bounds__(256) void attn_split_f32_kernel(
+    int n, int hq, int hkv, int Lmax, const float* __restrict__ q, const float* __restrict__ kp,
+    const float* __restrict__ vp, const int32_t* __restrict__ plen, const float* __restrict__ kt,
+    const float* __restrict__ vt, const uint64_t* __restrict__ mask, float scale, float* __restrict__ ws,
+    int rows, int rows_pad, int split_keys, int nsplit) {
+  constexpr int TK = 32;
+  __shared__ float Ks[TK * DH], Vs[TK * DH];
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x;
+  const int G = hq / hkv;
+  const int W = (n + 63) >> 6;
+  const bool tree = split == nsplit;
+  const int L = min(max(plen[b], 0), Lmax);  // prefix lengths beyond the buffer are clamped
+  int k_begin, k_end;
+  if (tree) { k_begin = 0; k_end = n; }
+  else { k_begin = split * split_keys; k_end = min(L, k_begin + split_keys); }
+  const float* kbase = tree ? kt + ((size_t)b * n * hkv + g) * DH : kp + (((size_t)b * hkv + g) * Lmax) * DH;
+  const float* vbase = tree ? vt + ((size_t)b * n * hkv + g) * DH : vp + (((size_t)b * hkv + g) * Lmax) * DH;
+  const size_t kstride = tree ? (size_t)hkv * DH : (size_t)DH;
+
+  for (int r0 = 0; r0 < rows; r0 += blockDim.x) {
+    const int r = r0 + tid;
+    const bool ok = r < rows;
+    const int node = ok ? r / G : 0, h = g * G + (ok ? r % G : 0);
+    float qv[DH], ov[DH];
+    const float* qp = q + (((size_t)b * n + node) * hq + h) * DH;
+    for (int d = 0; d < DH; ++d) { qv[d] = ok ? qp[d] : 0.f; ov[d] = 0.f; }
+    float m = kNegInf, l = 0.f;
+    for (int t0 = k_begin; t0 < k_end; t0 += TK) {
+      __syncthreads();
+      for (int x = tid; x < TK * DH; x += blockDim.x) {
+        const int kk = x / DH, d = x - kk * DH;
+        const int key = t0 + kk;
+        Ks[x] = key < k_end ? kbase[(size_t)key * kstride + d] : 0.f;
+        Vs[x] = key < k_end ? vbase[(size_t)key * kstride + d] : 0.f;
+      }
+      __syncthreads();
+      if (!ok) continue;
+      for (int kk = 0; kk < TK; ++kk) {
+        const int key = t0 + kk;
+        if (key >= k_end) break;
+        if (tree && !((mask[((size_t)b * n + node) * W + (key >> 6)] >> (key & 63)) & 1ull)) continue;
+        float sc = 0.f;
+        for (int d = 0; d < DH; ++d) sc = fmaf(qv[d], Ks[kk * DH + d], sc);
+        sc *= scale;
+        const float mn = fmaxf(m, sc);
+        const float a = (m == kNegInf) ? 0.f : expf(m - mn);
+        const float p = expf(sc - mn);
+        l = l * a + p;
+        for (int d = 0; d < DH; ++d) ov[d] = ov[d] * a + p * Vs[kk * DH + d];
+        m = mn;
+      }
+    }
+    if (ok) {
+      float* pr = partial_row(ws, b, g, hkv, nsplit + 1, split, rows_pad, r, DH);
+      for (int d = 0; d < DH; ++d) pr[d] = ov[d];
+      pr[DH] = m;
+      pr[DH + 1] = l;
+    }
+  }
+}
+
+// grid (n, hq, B), block DH threads: combine the splits of one (node, head).
+template <bool BF16>
+__global__ __launch_bounds__(128) void attn_merge_kernel(int n, int hq, int hkv, int DH, const float* __restrict__ ws,
+                                                         int rows_pad, int nsplit, void* __restrict__ out) {
+  const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int G = hq / hkv, g = h / G, r = i * G + (h - g * G);
+  float M = kNegInf;
+  for (int s = 0; s <= nsplit; ++s) M = fmaxf(M, partial_row(const_cast<float*>(ws), b, g, hkv, nsplit + 1, s, rows_pad, r, DH)[DH]);
+  for (int d = threadIdx.x; d < DH; d += blockDim.x) {
+    float acc = 0.f, L = 0.f;
+    for (int s = 0; s <= nsplit; ++s) {
+      const float* pr = partial_row(const_cast<float*>(ws), b, g, hkv, nsplit + 1, s, rows_pad, r, DH);
+      const float ms = pr[DH];
+      if (ms == kNegInf) continue;
+      const float w = expf(ms - M);
+      L += pr[DH + 1] * w;
+      acc += pr[d] * w;
+    }
+    const float v = L > 0.f ? acc / L : 0.f;
+    const size_t o = (((size_t)b * n + i) * hq + h) * DH + d;
+    if (BF16) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16(v);
+    else reinterpret_cast<float*>(out)[o] = v;
+  }
+}
+
+}  // namespace
+
+AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, int dtype) {
+  AttnPlan pl;
+  pl.rows = n * (hq / hkv);
+  pl.rows_pad = (pl.rows + 15) / 16 * 16;
+  const int target = (512 + B * hkv - 1) / (B * hkv);
+  int sk = (max_prefix + target - 1) / (target > 0 ? target : 1);
+  sk = (sk + kKT - 1) / kKT * kKT;
+  if (sk < 256) sk = 256;
+  if (sk > 1024) sk = 1024;
+  pl.split_keys = sk;
+  pl.nsplit = (max_prefix + sk - 1) / sk;
+  (void)head_dim;
+  (void)dtype;
+  return pl;
+}
+
+hipError_t launch_attention(int B, int n, int hq, int hkv, int DH, int Lmax, int dtype, const void* q, const void* kp,
+                            const void* vp, const int32_t* plen, const void* kt, const void* vt, const uint64_t* mask,
+                            float scale, void* out, float* ws, const AttnPlan& pl, int32_t* status, hipStream_t st) {
+  (void)status;
+  if (dtype == EAGLE_BF16) {
+    const int nrb = (pl.rows + kRowsPerWG - 1) / kRowsPerWG;
+    dim3 grid(pl.nsplit + 1, hkv * nrb, B);
+    const int threads = 256;
+#define EAGLE_ATTN_BF16(D)                                                                                           \
+  attn_split_bf16_kernel<D><<<grid, threads, 0, st>>>(n, hq, hkv, Lmax, (const uint16_t*)q, (const uint16_t*)kp,    \
+                                                      (const uint16_t*)vp, plen, (const uint16_t*)kt,               \
+                                                      (const uint16_t*)vt, mask, scale, ws, pl.rows, pl.rows_pad,   \
+                                                      pl.split_keys, pl.nsplit)
+    if (DH == 64) EAGLE_ATTN_BF16(64);
+    else EAGLE_ATTN_BF16(128);
+#undef EAGLE_ATTN_BF16
+  } else {
+    dim3 grid(pl.nsplit + 1, hkv, B);
+#define EAGLE_ATTN_F32(D)                                                                                          \
+  attn_split_f32_kernel<D><<<grid, 256, 0, st>>>(n, hq, hkv, Lmax, (const float*)q, (const float*)kp,             \
+                                                 (const float*)vp, plen, (const float*)kt, (const float*)vt, mask, \
+                                                 scale, ws, pl.rows, pl.rows_pad, pl.split_keys, pl.nsplit)
+    if (DH <= 16) EAGLE_ATTN_F32(16);
+    else if (DH <= 32) EAGLE_ATTN_F32(32);
+    else if (DH <= 64) EAGLE_ATTN_F32(64);
+    else EAGLE_ATTN_F32(128);
+#undef EAGLE_ATTN_F32
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  dim3 mg(n, hq, B);
+  const int mt = DH < 128 ? DH : 128;
+  if (dtype == EAGLE_BF16) attn_merge_kernel<true><<<mg, mt, 0, st>>>(n, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
+  else attn_merge_kernel<false><<<mg, mt, 0, st>>>(n, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
+  return hipGetLastError();
+}
+
+}  // namespace eagle

@@ -1,0 +1,75 @@
+// Host-side launchers of the libeagle kernels (one definition per .hip file).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace eagle {
+
+// ---- expansion (k_expand.hip) ----
+constexpr int kExpThreads = 256;
+constexpr int kExpChunk = 4096;          // vocab entries per scan workgroup (16 per thread)
+constexpr int kExpUnitsPerChunk = 4;     // one candidate record per wave
+constexpr int kExpExtra = 2;             // extra candidates kept per wave beyond k
+constexpr int kExpRescanCap = 2048;      // candidate capacity of the rare full-row re-scan
+
+inline int exp_chunks(int V) { return (V + kExpChunk - 1) / kExpChunk; }
+inline int exp_kp(int k) { return k + kExpExtra; }
+inline size_t exp_unit_floats(int k) { return 2 + 2 * (size_t)exp_kp(k); }
+inline size_t exp_ws_bytes(int B, int S, int V, int k) {
+  return (size_t)B * S * exp_chunks(V) * kExpUnitsPerChunk * exp_unit_floats(k) * sizeof(float);
+}
+
+hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint64_t seed,
+                         uint64_t round_id, const float* rows, const int32_t* root,
+                         int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
+                         int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
+                         int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                         float* slot_stats, float* ws_units, int32_t* status, hipStream_t st);
+
+// ---- mask + gather (k_mask.hip) ----
+hipError_t launch_tree_mask(int B, int n, const int32_t* parent, const int32_t* depth,
+                            const int32_t* prefix_len, uint64_t* mask, int32_t* pos,
+                            int32_t* status, hipStream_t st);
+hipError_t launch_gather(int n_rows, int row_bytes, const void* table, int table_rows,
+                         const int32_t* idx, void* out, int32_t* status, hipStream_t st);
+hipError_t launch_zero_ints(int32_t* p, size_t n, hipStream_t st);
+
+// ---- attention (k_attn.hip) ----
+struct AttnPlan {
+  int rows;        // query rows per (request, kv head) = n * (hq / hkv)
+  int rows_pad;    // rows rounded up to the MFMA tile
+  int split_keys;  // prefix keys per split workgroup
+  int nsplit;      // prefix splits (+1 split for the tree keys)
+};
+AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, int dtype);
+inline size_t attn_ws_bytes(int B, int hkv, int head_dim, const AttnPlan& pl) {
+  return (size_t)B * hkv * (pl.nsplit + 1) * pl.rows_pad * (head_dim + 2) * sizeof(float);
+}
+hipError_t launch_attention(int B, int n, int hq, int hkv, int head_dim, int max_prefix, int dtype,
+                            const void* q, const void* kp, const void* vp, const int32_t* plen,
+                            const void* kt, const void* vt, const uint64_t* mask, float scale,
+                            void* out, float* ws, const AttnPlan& pl, int32_t* status,
+                            hipStream_t st);
+
+// ---- LM head (k_lmhead.hip) ----
+constexpr int kLmTileN = 256;            // vocab columns per workgroup
+constexpr int kLmTileM = 64;             // rows per workgroup
+inline int lm_ntiles(int V) { return (V + kLmTileN - 1) / kLmTileN; }
+inline int lm_mtiles(int rows) { return (rows + kLmTileM - 1) / kLmTileM; }
+inline size_t lm_ws_bytes(int rows, int V) { return (size_t)rows * lm_ntiles(V) * 4 * sizeof(float); }
+hipError_t launch_lmhead(int rows, int hidden, int V, int dtype, const void* x, const void* w,
+                         float T, float* logits, float* row_stats, int32_t* row_argmax,
+                         float* probs, float* ws_part, int32_t* tickets, int32_t* status,
+                         hipStream_t st);
+
+// ---- acceptance (k_accept.hip) ----
+hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32_t* node_tok,
+                         const int32_t* node_parent, const int32_t* node_slot,
+                         const int32_t* pool_tok, const int32_t* pool_flat, const float* tlog,
+                         const float* tstats, const int32_t* targmax, const float* dlog,
+                         const float* sstats, const float* uniforms, int32_t* accept_len,
+                         int32_t* accept_path, int32_t* committed, int32_t* n_committed,
+                         int32_t* near_tie, int32_t* status, hipStream_t st);
+
+}  // namespace eagle

@@ -1,0 +1,92 @@
+"""The five round entry points (and helpers) on torch device tensors.
+
+Thin wrappers over the C ABI: they check tensor dtypes/shapes, pass raw device
+pointers and the current HIP stream, and raise EagleError on a non-zero return
+code.  No computation happens here.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import _lib
+from ._lib import EAGLE_BF16, EAGLE_F32, TreeParams, check
+
+_DT = {torch.float32: EAGLE_F32, torch.bfloat16: EAGLE_BF16}
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream():
+    return torch.cuda.current_stream().cuda_stream
+
+
+def tree_params(batch, vocab, depth, topk, m, temperature, seed=0, round_id=0) -> TreeParams:
+    return TreeParams(int(batch), int(vocab), int(depth), int(topk), int(m), float(temperature),
+                      int(seed) & (2**64 - 1), int(round_id) & (2**64 - 1))
+
+
+def workspace_size(p: TreeParams, hq=0, hkv=0, head_dim=0, max_prefix=0, hidden=0) -> int:
+    return int(_lib.load().eagle_workspace_size(p, hq, hkv, head_dim, max_prefix, hidden))
+
+
+def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    check("eagle_workspace_init", _lib.load().eagle_workspace_init(_ptr(ws), nbytes, _stream()))
+    return ws
+
+
+def expand_tree(p: TreeParams, draft_logits, root_token, out, ws, status=None):
+    """out: dict with node_tok/node_parent/node_depth/node_sib/node_slot/node_value/node_q,
+    pool_tok/pool_q/pool_flat, slot_src, slot_stats (device tensors)."""
+    assert draft_logits.dtype == torch.float32 and draft_logits.is_contiguous()
+    rc = _lib.load().eagle_expand_tree(
+        p, _ptr(draft_logits), _ptr(root_token),
+        _ptr(out["node_tok"]), _ptr(out["node_parent"]), _ptr(out["node_depth"]), _ptr(out["node_sib"]),
+        _ptr(out["node_slot"]), _ptr(out["node_value"]), _ptr(out["node_q"]),
+        _ptr(out["pool_tok"]), _ptr(out["pool_q"]), _ptr(out["pool_flat"]), _ptr(out["slot_src"]),
+        _ptr(out["slot_stats"]), _ptr(ws), ws.numel(), _ptr(status), _stream())
+    check("eagle_expand_tree", rc)
+
+
+def build_tree_mask(batch, n, node_parent, node_depth, prefix_len, mask, pos, status=None):
+    rc = _lib.load().eagle_build_tree_mask(batch, n, _ptr(node_parent), _ptr(node_depth), _ptr(prefix_len),
+                                          _ptr(mask), _ptr(pos), _ptr(status), _stream())
+    check("eagle_build_tree_mask", rc)
+
+
+def tree_attention(batch, n, hq, hkv, head_dim, max_prefix, q, k_prefix, v_prefix, prefix_len, k_tree, v_tree,
+                   mask, scale, out, ws, status=None):
+    dt = _DT[q.dtype]
+    rc = _lib.load().eagle_tree_attention(batch, n, hq, hkv, head_dim, max_prefix, dt, _ptr(q), _ptr(k_prefix),
+                                         _ptr(v_prefix), _ptr(prefix_len), _ptr(k_tree), _ptr(v_tree), _ptr(mask),
+                                         float(scale), _ptr(out), _ptr(ws), ws.numel(), _ptr(status), _stream())
+    check("eagle_tree_attention", rc)
+
+
+def lmhead_softmax(rows, hidden, vocab, x, w, temperature, logits, row_stats, row_argmax, ws, probs=None,
+                   status=None):
+    dt = _DT[x.dtype]
+    rc = _lib.load().eagle_lmhead_softmax(rows, hidden, vocab, dt, _ptr(x), _ptr(w), float(temperature),
+                                         _ptr(logits), _ptr(row_stats), _ptr(row_argmax), _ptr(probs), _ptr(ws),
+                                         ws.numel(), _ptr(status), _stream())
+    check("eagle_lmhead_softmax", rc)
+
+
+def verify_accept(p: TreeParams, tree, target_logits, target_stats, target_argmax, draft_logits, slot_stats,
+                  uniforms, out, ws, status=None):
+    rc = _lib.load().eagle_verify_accept(
+        p, _ptr(tree["node_tok"]), _ptr(tree["node_parent"]), _ptr(tree["node_slot"]), _ptr(tree["pool_tok"]),
+        _ptr(tree["pool_flat"]), _ptr(target_logits), _ptr(target_stats), _ptr(target_argmax),
+        _ptr(draft_logits), _ptr(slot_stats), _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["accept_path"]),
+        _ptr(out["committed"]), _ptr(out["n_committed"]), _ptr(out["near_tie"]), _ptr(ws), ws.numel(),
+        _ptr(status), _stream())
+    check("eagle_verify_accept", rc)
+
+
+def gather_rows(n_rows, row_elems, table, idx, out, status=None):
+    dt = _DT[table.dtype]
+    rc = _lib.load().eagle_gather_rows(n_rows, row_elems, dt, _ptr(table), table.shape[0], _ptr(idx), _ptr(out),
+                                      _ptr(status), _stream())
+    check("eagle_gather_rows", rc)

@@ -1,0 +1,231 @@
+"""One draft-tree round on the device, wired through the C ABI.
+
+`DeviceRound` owns the device buffers of a workload shape and runs
+
+    expand -> mask -> (gather tree q/k/v rows) -> tree attention -> LM head -> accept
+
+on the current HIP stream, every step in libeagle's kernels.  `DeviceInputs`
+holds one input set on the device.  `device_draft_rows` builds the synthetic
+draft rows "target logits + noise" slot by slot with the same kernels (the
+ancestor-only mask makes a node's target logits depend on its root path only,
+so they can be computed before the tree exists).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import ops
+
+_TORCH_DT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _t(a, dtype=None, device="cuda"):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.to(device)
+
+
+class DeviceWeights:
+    """Inputs shared by every input set: LM-head weight and per-token q/k/v rows."""
+
+    def __init__(self, inp, device="cuda"):
+        c = inp.cfg
+        dt = _TORCH_DT[c.dtype]
+        self.w = _t(inp.w, dt, device)
+        self.q_tab = _t(inp.q_tab, dt, device)
+        self.k_tab = _t(inp.k_tab, dt, device)
+        self.v_tab = _t(inp.v_tab, dt, device)
+
+
+class DeviceInputs:
+    """One input set: prefix KV, prefix lengths, roots, uniforms, draft rows, noise."""
+
+    def __init__(self, inp, device="cuda", with_eps=False):
+        c = inp.cfg
+        dt = _TORCH_DT[c.dtype]
+        self.k_prefix = _t(inp.k_prefix, dt, device)
+        self.v_prefix = _t(inp.v_prefix, dt, device)
+        self.prefix_len = _t(inp.prefix_len, torch.int32, device)
+        self.roots = _t(inp.roots, torch.int32, device)
+        self.uniforms = _t(inp.uniforms, torch.float32, device)
+        self.seed = inp.gumbel_seed
+        self.sigma = inp.sigma
+        self.rows = torch.zeros((c.B, c.S, c.V), dtype=torch.float32, device=device)
+        self.eps = _t(inp.eps, torch.float32, device) if with_eps else None
+
+    def set_rows(self, rows_np):
+        self.rows.copy_(torch.from_numpy(np.ascontiguousarray(rows_np, dtype=np.float32)))
+
+
+class DeviceRound:
+    """Device buffers + the five entry points of one round for a config."""
+
+    def __init__(self, cfg, device="cuda", n=None, B=None):
+        self.cfg = c = cfg
+        self.B = B = B or c.B
+        self.N = N = n or c.N
+        self.dev = device
+        dt = _TORCH_DT[c.dtype]
+        i32, f32 = torch.int32, torch.float32
+        z = lambda *s, dtype=i32: torch.zeros(s, dtype=dtype, device=device)  # noqa: E731
+        self.tree = {k: z(B, N) for k in ("node_tok", "node_parent", "node_depth", "node_sib", "node_slot")}
+        self.tree["node_value"] = z(B, N, dtype=f32)
+        self.tree["node_q"] = z(B, N, dtype=f32)
+        self.tree["pool_tok"] = z(B, c.S, c.k)
+        self.tree["pool_q"] = z(B, c.S, c.k, dtype=f32)
+        self.tree["pool_flat"] = z(B, c.S, c.k)
+        self.tree["slot_src"] = z(B, c.S)
+        self.tree["slot_stats"] = z(B, c.S, 2, dtype=f32)
+        W = (N + 63) // 64
+        self.mask = torch.zeros((B, N, W), dtype=torch.int64, device=device)
+        self.pos = z(B, N)
+        self.q = torch.zeros((B, N, c.hq, c.dh), dtype=dt, device=device)
+        self.kt = torch.zeros((B, N, c.hkv, c.dh), dtype=dt, device=device)
+        self.vt = torch.zeros((B, N, c.hkv, c.dh), dtype=dt, device=device)
+        self.x = torch.zeros((B, N, c.hq, c.dh), dtype=dt, device=device)
+        self.logits = torch.zeros((B * N, c.V), dtype=f32, device=device)
+        self.stats = z(B * N, 2, dtype=f32)
+        self.argmax = z(B * N)
+        self.acc = {"accept_len": z(B), "accept_path": z(B, c.D), "committed": z(B, c.D + 1),
+                    "n_committed": z(B), "near_tie": z(B)}
+        self.status = z(1)
+        self.scale = float(np.float32(1.0 / math.sqrt(c.dh)))
+        p = self.params(1.0)
+        nbytes = ops.workspace_size(p, c.hq, c.hkv, c.dh, c.Lmax, c.H)
+        if nbytes == 0:
+            raise ValueError("invalid round shape")
+        self.ws = ops.new_workspace(nbytes, device)
+
+    def params(self, T, round_id=0, seed=0, depth=None, m=None):
+        c = self.cfg
+        return ops.tree_params(self.B, c.V, depth or c.D, c.k, m or (self.N - 1), T, seed, round_id)
+
+    # -- the stages -----------------------------------------------------------
+    def expand(self, data, T, round_id=0):
+        ops.expand_tree(self.params(T, round_id, data.seed), data.rows, data.roots, self.tree, self.ws, self.status)
+
+    def mask_pos(self, data):
+        ops.build_tree_mask(self.B, self.N, self.tree["node_parent"], self.tree["node_depth"], data.prefix_len,
+                            self.mask, self.pos, self.status)
+
+    def gather_qkv(self, wts, node_tok=None):
+        c = self.cfg
+        tok = (node_tok if node_tok is not None else self.tree["node_tok"]).reshape(-1)
+        n = tok.numel()
+        ops.gather_rows(n, c.hq * c.dh, wts.q_tab, tok, self.q, self.status)
+        ops.gather_rows(n, c.hkv * c.dh, wts.k_tab, tok, self.kt, self.status)
+        ops.gather_rows(n, c.hkv * c.dh, wts.v_tab, tok, self.vt, self.status)
+
+    def attention(self, data):
+        c = self.cfg
+        ops.tree_attention(self.B, self.N, c.hq, c.hkv, c.dh, c.Lmax, self.q, data.k_prefix, data.v_prefix,
+                           data.prefix_len, self.kt, self.vt, self.mask, self.scale, self.x, self.ws, self.status)
+
+    def lmhead(self, wts, T):
+        c = self.cfg
+        ops.lmhead_softmax(self.B * self.N, c.H, c.V, self.x.view(self.B * self.N, c.H), wts.w, T, self.logits,
+                           self.stats, self.argmax, self.ws, status=self.status)
+
+    def accept(self, data, T, round_id=0):
+        ops.verify_accept(self.params(T, round_id, data.seed), self.tree, self.logits, self.stats, self.argmax,
+                          data.rows, self.tree["slot_stats"], data.uniforms, self.acc, self.ws, self.status)
+
+    def step(self, wts, data, T, round_id=0):
+        """One whole round (all five entry points, plus the q/k/v row gathers)."""
+        self.expand(data, T, round_id)
+        self.mask_pos(data)
+        self.gather_qkv(wts)
+        self.attention(data)
+        self.lmhead(wts, T)
+        self.accept(data, T, round_id)
+
+    def host(self):
+        """Copy every output to host numpy arrays (synchronises)."""
+        out = {k: v.cpu().numpy() for k, v in self.tree.items()}
+        out.update({k: v.cpu().numpy() for k, v in self.acc.items()})
+        out["mask"] = self.mask.cpu().numpy().view(np.uint64)
+        out["pos"] = self.pos.cpu().numpy()
+        out["x"] = self.x.float().cpu().numpy()
+        out["logits"] = self.logits.cpu().numpy()
+        out["stats"] = self.stats.cpu().numpy()
+        out["argmax"] = self.argmax.cpu().numpy()
+        out["status"] = int(self.status.item())
+        return out
+
+
+def device_draft_rows(cfg, wts, data, T, round_id=0, device="cuda"):
+    """Fill data.rows with synthetic draft rows, slot by slot, on the device.
+
+    Slot s of request b gets the target logits at the node it expands
+    (attention on the node's root path alone, then the LM head) plus
+    sigma_b * eps[b, s].  Workloads marked "iid" get sigma_b * eps directly.
+    Frontier nodes are found with eagle_expand_tree itself, depth by depth.
+    """
+    c = cfg
+    if data.eps is None:
+        raise ValueError("input set was created without noise")
+    sig = torch.from_numpy(np.asarray(data.sigma, np.float32)).to(device).view(c.B, 1)
+    if c.draft == "iid":
+        data.rows.copy_(data.eps * sig.view(c.B, 1, 1))
+        return
+    data.rows.zero_()
+    for d in range(c.D):
+        # frontier of depth d: slot 0 (root) or the k slots 1+(d-1)k+i
+        if d == 0:
+            paths = [[[int(r)]] for r in data.roots.cpu().numpy()]
+            slots = [0]
+        else:
+            Sd = 1 + d * c.k
+            Pd = Sd * c.k
+            part = DeviceRound(c.with_(D=d + 1, m=min(c.m, Pd)), device, n=min(c.m, Pd) + 1)
+            tmp = DeviceInputs.__new__(DeviceInputs)
+            tmp.rows = data.rows[:, :Sd].contiguous()
+            tmp.roots, tmp.seed = data.roots, data.seed
+            part.expand(tmp, T, round_id)
+            pool_tok = part.tree["pool_tok"].cpu().numpy()
+            slot_src = part.tree["slot_src"].cpu().numpy()
+            slots = [1 + (d - 1) * c.k + i for i in range(c.k)]
+            paths = []
+            for b in range(c.B):
+                pb = []
+                for s in slots:
+                    toks, e = [], int(slot_src[b, s])
+                    while e >= 0:
+                        toks.append(int(pool_tok[b, e // c.k, e % c.k]))
+                        e = int(slot_src[b, e // c.k]) if e // c.k > 0 else -1
+                    pb.append([int(data.roots[b].item())] + toks[::-1])
+                paths.append(pb)
+        # mini tree per request: root + one chain per frontier node (no sharing)
+        nf = len(slots)
+        n = 1 + nf * d
+        tok = np.zeros((c.B, n), np.int32)
+        par = np.full((c.B, n), -1, np.int32)
+        dep = np.zeros((c.B, n), np.int32)
+        ends = []
+        for i in range(nf):
+            for t in range(d):
+                j = 1 + i * d + t
+                par[:, j] = 0 if t == 0 else j - 1
+                dep[:, j] = t + 1
+            ends.append(1 + i * d + d - 1 if d > 0 else 0)
+        for b in range(c.B):
+            tok[b, 0] = paths[b][0][0]
+            for i in range(nf):
+                for t in range(d):
+                    tok[b, 1 + i * d + t] = paths[b][i][t + 1]
+        mini = DeviceRound(c, device, n=n)
+        mini.tree["node_parent"].copy_(torch.from_numpy(par))
+        mini.tree["node_depth"].copy_(torch.from_numpy(dep))
+        mini.tree["node_tok"].copy_(torch.from_numpy(tok))
+        mini.mask_pos(data)
+        mini.gather_qkv(wts)
+        mini.attention(data)
+        mini.lmhead(wts, T)
+        z = mini.logits.view(c.B, n, c.V)
+        for i, s in enumerate(slots):
+            data.rows[:, s] = z[:, ends[i]] + sig * data.eps[:, s]
+    torch.cuda.synchronize()

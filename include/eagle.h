@@ -1,0 +1,251 @@
+/*
+ * eagle.h — C ABI of libeagle: one EAGLE-style draft-tree round on an MI355X
+ * (gfx950).
+ *
+ * Five stream-ordered entry points run the round on device memory:
+ *
+ *   eagle_expand_tree      draft rows -> dynamic draft tree (expand, rerank, flatten)
+ *   eagle_build_tree_mask  parent links -> ancestor-only attention mask + positions
+ *   eagle_tree_attention   one tree-masked attention pass over prefix KV + tree
+ *   eagle_lmhead_softmax   LM-head logits + per-row softmax statistics + argmax
+ *   eagle_verify_accept    recursive speculative sampling down the tree
+ *
+ * plus workspace helpers and one row-gather helper.
+ *
+ * Conventions (all entry points):
+ *   - Every pointer argument named as a tensor is DEVICE memory owned by the
+ *     caller; the library never allocates, frees or retains it.  Parameter
+ *     structs (eagle_tree_params) are HOST memory, read during the call only.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t passed as
+ *     void*, NULL = the default stream).  Nothing is synchronised.
+ *   - Tensors are dense, row-major, with the shapes given below; int32 ids,
+ *     fp32 logits and statistics, activations and weights in the dtype named
+ *     by an `eagle_dtype` argument (bf16 = raw 16-bit patterns).
+ *   - Return value: EAGLE_OK (0) or a negative EAGLE_ERR_* code.  Argument
+ *     checks happen on the host before anything is enqueued; a call that
+ *     returns an error has enqueued nothing.
+ *   - Data-dependent conditions found on the device (a token id out of range,
+ *     a non-finite logit, ...) do not abort: they OR EAGLE_STATUS_* bits into
+ *     *dev_status (an optional device int32, may be NULL), to be read by the
+ *     caller after synchronising.
+ *   - Workspace: `ws` is caller-provided device scratch of `ws_bytes` bytes,
+ *     at least eagle_workspace_size(...).  Before its first use it must be
+ *     initialised once with eagle_workspace_init (the library keeps a few
+ *     completion counters in it and returns them to zero after each call).
+ *     Calls that share one workspace must be ordered (same stream); calls on
+ *     different streams need different workspaces.
+ *   - Calls are deterministic: identical inputs give bit-identical outputs.
+ *
+ * Sources of the method (cited by page title and section):
+ *   [E1] "EAGLE: Speculative Sampling Requires Rethinking Feature Uncertainty"
+ *        (papercache.org notes).
+ *   [E2] "EAGLE-2: Faster Inference of Language Models with Dynamic Draft
+ *        Trees" (tom-jerr.github.io notes).
+ *   [HW] "LLM 推测性解码原理解读" (hubwiz.com blog on speculative decoding and
+ *        EAGLE-3).
+ *
+ * Symbols: B batch, V vocab, D depth (draft levels), k children per expanded
+ * node, m selected draft nodes, N = m + 1 tree nodes (flat index 0 = root,
+ * the last committed token), S = 1 + (D-1)k expanded slots, P = S*k pool
+ * entries (every child ever created), W = ceil(N/64) mask words.
+ */
+#ifndef EAGLE_H
+#define EAGLE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes -------------------------------------------------------- */
+#define EAGLE_OK             0
+#define EAGLE_ERR_NULL      -1  /* a required pointer is NULL                    */
+#define EAGLE_ERR_SHAPE     -2  /* a size is out of range or inconsistent        */
+#define EAGLE_ERR_DTYPE     -3  /* unsupported dtype for this entry point/shape  */
+#define EAGLE_ERR_WORKSPACE -4  /* workspace missing or smaller than required    */
+#define EAGLE_ERR_LAUNCH    -5  /* the HIP runtime refused a launch              */
+#define EAGLE_ERR_ALIGN     -6  /* a tensor pointer is not 16-byte aligned       */
+
+/* ---- device status bits (OR-ed into *dev_status) ------------------------- */
+#define EAGLE_STATUS_TOKEN_RANGE   0x1  /* an input token id was outside [0, V)          */
+#define EAGLE_STATUS_NONFINITE     0x2  /* a logit was NaN/Inf (treated as -inf)         */
+#define EAGLE_STATUS_ZERO_RESIDUAL 0x4  /* residual mass 0 after a rejection: P kept     */
+#define EAGLE_STATUS_TOPK_RESCAN   0x8  /* child selection re-scanned a row (info only)  */
+#define EAGLE_STATUS_BAD_TREE      0x10 /* parent links not a valid flattened tree       */
+#define EAGLE_STATUS_CAND_OVERFLOW 0x20 /* child re-scan candidate list overflowed       */
+
+/* ---- limits -------------------------------------------------------------- */
+#define EAGLE_MAX_TOPK   16
+#define EAGLE_MAX_DEPTH  16
+#define EAGLE_MAX_NODES  256        /* N = m + 1 */
+#define EAGLE_MAX_POOL   4096       /* P = S * k */
+#define EAGLE_MAX_VOCAB  (1 << 19)
+
+typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
+
+/* Parameters of one round (host struct).
+ *   temperature > 0: sampling at temperature T (both the target and the draft
+ *   distributions are softmax(logits / T), [HW] section 2);
+ *   temperature == 0: greedy (children = top-k logits, acceptance = argmax
+ *   match, [E1] appendix A.1; tree values then use confidences at T = 1).
+ *   seed, round_id: key and counter words of the Philox4x32-10 draws that
+ *   sample non-greedy children. */
+typedef struct eagle_tree_params {
+    int32_t  batch;        /* B >= 1                         */
+    int32_t  vocab;        /* V, k <= V <= EAGLE_MAX_VOCAB   */
+    int32_t  depth;        /* D, 1..EAGLE_MAX_DEPTH          */
+    int32_t  topk;         /* k, 1..EAGLE_MAX_TOPK           */
+    int32_t  m;            /* 1 <= m <= P, m + 1 <= EAGLE_MAX_NODES */
+    float    temperature;  /* T >= 0                         */
+    uint64_t seed;
+    uint64_t round_id;
+} eagle_tree_params;
+
+/* Bytes of workspace that every entry point below needs for a round of these
+ * sizes (the maximum over the entry points; the same buffer may serve all of
+ * them in stream order).  hq/hkv/head_dim/max_prefix describe the verify
+ * attention, hidden the LM-head input width.  Returns 0 on invalid sizes. */
+size_t eagle_workspace_size(const eagle_tree_params* p, int32_t hq, int32_t hkv,
+                            int32_t head_dim, int32_t max_prefix, int32_t hidden);
+
+/* Zero the workspace's counter area (enqueued on `stream`, no memset node).
+ * Call once after allocating a workspace. */
+int eagle_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Dynamic draft-tree expansion, rerank and flattening for every request.
+ * Source: [E2] "Expanding the Draft Tree" (value V_i = product of draft
+ * confidences on the root path; expand the current layer's top-k by value),
+ * "Rerank draft tokens" (keep the top-m by value, shallower first at equal
+ * value, giving a connected tree), "Tree Attention Mask" (flatten);
+ * [E1] appendix A.1 (greedy: top-k children; otherwise k sampled children).
+ *
+ * In:  draft_logits [B, S, V] fp32: row s of request b holds the draft logits
+ *        at the node expanded as slot s.  Slot 0 is the root; the frontier
+ *        node of rank i at depth d (1 <= d < D) is slot 1 + (d-1)k + i.
+ *      root_token [B] int32.
+ * Out: node_tok, node_parent (-1 for the root), node_depth, node_sib (rank
+ *        among its parent's children in sampling order, -1 root), node_slot
+ *        (slot the node was expanded as, -1 if never expanded): [B, N] int32;
+ *      node_value, node_q: [B, N] fp32 (path value, own confidence; 1 at root);
+ *      pool_tok [B, S, k] int32: children of each slot in sampling order;
+ *      pool_q [B, S, k] fp32: their confidences;
+ *      pool_flat [B, S, k] int32: flat index of each child or -1 if pruned;
+ *      slot_src [B, S] int32: pool index (s' * k + j) of the node slot s
+ *        expands (-1 for slot 0);
+ *      slot_stats [B, S, 2] fp32: (max_v t_v, sum_v exp(t_v - max)) of each
+ *        slot row, t = logits / T' (T' = T, or 1 when greedy).
+ * Flat order: root, then by (depth, parent's flat index, sibling rank).
+ * Non-greedy children are the k largest Gumbel keys fp32(z_v / T) + g_v,
+ * g = -ln(-ln u_v), u_v from Philox4x32-10 with counter (v >> 2, s, b,
+ * round_id mod 2^32), key (seed low, seed high), output word v & 3, mapped to
+ * (2 * (x >> 9) + 1) * 2^-24; keys are compared in fp64, ties to the lower id.
+ * Status: TOKEN_RANGE (root id), NONFINITE, TOPK_RESCAN, CAND_OVERFLOW. */
+int eagle_expand_tree(const eagle_tree_params* p, const float* draft_logits,
+                      const int32_t* root_token,
+                      int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
+                      int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
+                      int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                      float* slot_stats, void* ws, size_t ws_bytes, int32_t* dev_status,
+                      void* stream);
+
+/* Ancestor-only tree attention mask and positions.
+ * Source: [E2] "Tree Attention Mask" (each token sees only its ancestors,
+ * never another branch); [HW] section 5.
+ * In:  node_parent [B, n] int32 (flattened order: parent index < own index,
+ *        -1 for node 0), node_depth [B, n] int32, prefix_len [B] int32.
+ * Out: mask [B, n, W] uint64: bit j of row i is set iff j == i or j is an
+ *        ancestor of i (bit j % 64 of word j / 64);
+ *      pos [B, n] int32 = prefix_len[b] + depth.
+ * Status: BAD_TREE if a parent index is not in [0, i) (row i then sees itself only). */
+int eagle_build_tree_mask(int32_t batch, int32_t n, const int32_t* node_parent,
+                          const int32_t* node_depth, const int32_t* prefix_len,
+                          uint64_t* mask, int32_t* pos, int32_t* dev_status, void* stream);
+
+/* One tree-masked attention pass of the tree queries over the prefix KV and
+ * the tree itself.  Source: [E1] sections 3.1/3.3 (tree attention scores the
+ * whole draft tree in one target forward); [HW] section 5 (every root-to-leaf
+ * path is scored as if it were an independent sequence).
+ * In:  q [B, n, hq, head_dim]; k_prefix, v_prefix [B, hkv, max_prefix, head_dim]
+ *        (first prefix_len[b] positions used); prefix_len [B] int32 (0..max_prefix);
+ *      k_tree, v_tree [B, n, hkv, head_dim]; mask [B, n, W] uint64 as above;
+ *      scale: score = scale * (q . k).  Query head h reads kv head h / (hq / hkv).
+ * Out: out [B, n, hq, head_dim], same dtype as q.
+ * dtype: EAGLE_BF16 (head_dim 64 or 128, MFMA) or EAGLE_F32 (head_dim <= 128).
+ * Softmax and accumulation are fp32. */
+int eagle_tree_attention(int32_t batch, int32_t n, int32_t hq, int32_t hkv, int32_t head_dim,
+                         int32_t max_prefix, int32_t dtype, const void* q,
+                         const void* k_prefix, const void* v_prefix, const int32_t* prefix_len,
+                         const void* k_tree, const void* v_tree, const uint64_t* mask,
+                         float scale, void* out, void* ws, size_t ws_bytes,
+                         int32_t* dev_status, void* stream);
+
+/* LM-head logits at every row and the statistics of softmax(logits / T').
+ * Source: [E1] background A3: p_{j+1} = LMHead(f_j) at every position.
+ * In:  x [rows, hidden], w [vocab, hidden] (dtype), temperature T >= 0
+ *        (T' = T, or 1 when T == 0).
+ * Out: logits [rows, vocab] fp32 (= x . w^T, fp32 accumulation);
+ *      row_stats [rows, 2] fp32: (M, S) = (max_v z_v / T', sum_v exp(z_v/T' - M));
+ *      row_argmax [rows] int32: argmax_v z_v, lowest id on ties;
+ *      probs [rows, vocab] fp32 or NULL: exp(z/T' - M) / S when non-NULL.
+ * dtype EAGLE_BF16 needs hidden % 64 == 0. */
+int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dtype,
+                         const void* x, const void* w, float temperature, float* logits,
+                         float* row_stats, int32_t* row_argmax, float* probs, void* ws,
+                         size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* Recursive speculative sampling down each request's tree.
+ * Source: [E1] background A3 (accept x with probability min(1, p(x)/q(x));
+ * on rejection draw from norm(max(0, p - q))), section 3.3 and appendix A.2
+ * (at each tree node try the k candidates in turn against the adjusted
+ * distribution; draw from it only when all are rejected); [HW] section 1
+ * (bonus token when the walk ends at a leaf; at least 1 and at most
+ * accepted + 1 committed tokens); greedy ([E1] A.1): follow the child equal
+ * to the target argmax.
+ * Candidates of node u are all k sampled children of its slot, in sampling
+ * order, including pruned ones; accepting a pruned child commits it and ends
+ * the walk.  After rejecting x_j the draft law loses x_j and is renormalised
+ * (draws without replacement).  Trial j at node u uses uniforms[b, u, j]; the
+ * final draw (residual or bonus) uses uniforms[b, u, k] by inverse CDF in
+ * token-id order (first token whose cumulative mass exceeds u * total).
+ * In:  tree arrays from eagle_expand_tree (node_tok, node_parent, node_slot
+ *        [B, N]; pool_tok, pool_flat [B, S, k]);
+ *      target_logits [B*N, V] fp32 (row b*N + u = verify logits at flat node u),
+ *      target_stats [B*N, 2] and target_argmax [B*N] from eagle_lmhead_softmax
+ *        (argmax is read only when greedy);
+ *      draft_logits [B, S, V] fp32 and slot_stats [B, S, 2] (as for expand);
+ *      uniforms [B, N, k + 1] fp32 in [0, 1) (unused when greedy).
+ * Out: accept_len [B] (accepted tree nodes), accept_path [B, D] (their flat
+ *        indices, -1 padded), committed [B, D + 1] (committed tokens, -1
+ *        padded), n_committed [B] = accept_len + 1, near_tie [B] (decisions
+ *        whose uniform lay within 1e-6 of the deciding threshold).
+ * Status: ZERO_RESIDUAL, TOKEN_RANGE. */
+int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok,
+                        const int32_t* node_parent, const int32_t* node_slot,
+                        const int32_t* pool_tok, const int32_t* pool_flat,
+                        const float* target_logits, const float* target_stats,
+                        const int32_t* target_argmax, const float* draft_logits,
+                        const float* slot_stats, const float* uniforms,
+                        int32_t* accept_len, int32_t* accept_path, int32_t* committed,
+                        int32_t* n_committed, int32_t* near_tie, void* ws, size_t ws_bytes,
+                        int32_t* dev_status, void* stream);
+
+/* Row gather: out[r, :] = table[idx[r], :] for r < n_rows (row_elems elements
+ * of `dtype` per row).  The verify layer's tree queries/keys/values are
+ * per-token rows looked up this way.  Ids outside [0, table_rows) give a zero
+ * row and set TOKEN_RANGE. */
+int eagle_gather_rows(int32_t n_rows, int32_t row_elems, int32_t dtype, const void* table,
+                      int32_t table_rows, const int32_t* idx, void* out, int32_t* dev_status,
+                      void* stream);
+
+/* Human-readable name of a return code. */
+const char* eagle_error_string(int32_t code);
+
+/* ABI version: (major << 16) | minor. */
+int32_t eagle_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* EAGLE_H */

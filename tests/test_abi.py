@@ -1,0 +1,131 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host with the documented
+codes before touching the device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "eagle.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from eagle_draft_tree_expand_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from eagle_draft_tree_expand_amd import build
+        build.build()
+    return _lib.load()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(eagle_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_five_entry_points():
+    names = declared_functions()
+    for n in ("eagle_expand_tree", "eagle_build_tree_mask", "eagle_tree_attention", "eagle_lmhead_softmax",
+              "eagle_verify_accept"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    from eagle_draft_tree_expand_amd import _lib
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_version_and_error_strings(lib):
+    assert lib.eagle_abi_version() >> 16 == 1
+    assert lib.eagle_error_string(-4) == b"workspace too small"
+    assert lib.eagle_error_string(0) == b"ok"
+
+
+def _params(**kw):
+    from eagle_draft_tree_expand_amd import ops
+    d = dict(batch=1, vocab=1000, depth=3, topk=2, m=5, temperature=1.0)
+    d.update(kw)
+    return ops.tree_params(d["batch"], d["vocab"], d["depth"], d["topk"], d["m"], d["temperature"])
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(m=0), -2), (dict(m=11), -2), (dict(topk=17), -2), (dict(topk=0), -2), (dict(depth=0), -2),
+    (dict(depth=17), -2), (dict(vocab=1), -2), (dict(temperature=-1.0), -2), (dict(batch=0), -2),
+    (dict(temperature=float("nan")), -2),
+])
+def test_expand_rejects_bad_shapes(lib, kw, code):
+    p = _params(**kw)
+    args = [FAKE] * 16
+    rc = lib.eagle_expand_tree(ctypes.byref(p), *args[:14], FAKE, 1 << 30, None, None)
+    assert rc == code
+
+
+def test_expand_null_align_workspace(lib):
+    p = _params()
+    ptrs = [FAKE] * 14
+    assert lib.eagle_expand_tree(ctypes.byref(p), None, *ptrs[1:], FAKE, 1 << 30, None, None) == -1
+    assert lib.eagle_expand_tree(ctypes.byref(p), FAKE + 4, *ptrs[1:], FAKE, 1 << 30, None, None) == -6
+    assert lib.eagle_expand_tree(ctypes.byref(p), *ptrs, FAKE, 100, None, None) == -4
+    assert lib.eagle_expand_tree(None, *ptrs, FAKE, 1 << 30, None, None) == -1
+
+
+def test_workspace_size(lib):
+    p = _params()
+    n = lib.eagle_workspace_size(ctypes.byref(p), 4, 2, 128, 300, 512)
+    assert n > 65536 and n % 256 == 0
+    assert lib.eagle_workspace_size(ctypes.byref(_params(m=11)), 4, 2, 128, 300, 512) == 0
+    assert lib.eagle_workspace_size(ctypes.byref(p), 4, 3, 128, 300, 512) == 0   # hq % hkv
+
+
+def test_attention_rejects(lib):
+    f = lib.eagle_tree_attention
+    ok = (1, 5, 4, 2, 128, 100, 1)
+    tail = [FAKE] * 7
+    assert f(*ok, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) != -2
+    assert f(1, 5, 4, 3, 128, 100, 1, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) == -2
+    assert f(1, 5, 4, 2, 96, 100, 1, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) == -3
+    assert f(1, 5, 4, 2, 128, 100, 7, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) == -3
+    assert f(1, 0, 4, 2, 128, 100, 1, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) == -2
+    assert f(1, 257, 4, 2, 128, 100, 1, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) == -2
+    assert f(*ok, None, *tail[1:], 0.1, FAKE, FAKE, 1 << 30, None, None) == -1
+    assert f(*ok, FAKE + 2, *tail[1:], 0.1, FAKE, FAKE, 1 << 30, None, None) == -6
+    assert f(*ok, *tail, float("inf"), FAKE, FAKE, 1 << 30, None, None) == -2
+    assert f(*ok, *tail, 0.1, FAKE, FAKE, 1000, None, None) == -4
+
+
+def test_lmhead_rejects(lib):
+    f = lib.eagle_lmhead_softmax
+    assert f(10, 100, 500, 1, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -2  # hidden%128
+    assert f(10, 128, 500, 2, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -3
+    assert f(0, 128, 500, 1, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -2
+    assert f(10, 128, 500, 1, None, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -1
+    assert f(10, 128, 500, 1, FAKE, FAKE, -2.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -2
+    assert f(10, 128, 500, 1, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 10, None, None) == -4
+
+
+def test_mask_gather_accept_reject(lib):
+    assert lib.eagle_build_tree_mask(1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert lib.eagle_build_tree_mask(1, 300, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
+    assert lib.eagle_build_tree_mask(1, 5, None, FAKE, FAKE, FAKE, FAKE, None, None) == -1
+    assert lib.eagle_gather_rows(4, 8, 5, FAKE, 10, FAKE, FAKE, None, None) == -3
+    assert lib.eagle_gather_rows(4, 0, 1, FAKE, 10, FAKE, FAKE, None, None) == -2
+    assert lib.eagle_gather_rows(0, 8, 1, None, 10, None, None, None, None) == 0
+    p = _params()
+    args = [FAKE] * 16
+    assert lib.eagle_verify_accept(ctypes.byref(_params(m=0)), *args, FAKE, 1 << 20, None, None) == -2
+    args[0] = None
+    assert lib.eagle_verify_accept(ctypes.byref(p), *args, FAKE, 1 << 20, None, None) == -1
+
+
+def test_workspace_init_rejects(lib):
+    assert lib.eagle_workspace_init(None, 1 << 20, None) == -1
+    assert lib.eagle_workspace_init(FAKE, 100, None) == -4
