@@ -1,0 +1,249 @@
+"""Benchmark: draft-tree verify rounds/s and committed tokens/s on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config 8b] [--temp 1.0]
+
+A step is one whole round (expand -> mask -> tree attention -> LM head ->
+accept, plus the tree q/k/v row gathers) through the C ABI on synthetic
+inputs already resident in HBM.  Input sets rotate (8 by default) so that
+per-round data (draft rows, prefix KV) is not served from the 256 MB
+Infinity Cache; the LM-head weight is one copy.  Prints one JSON line.
+
+The LM-head kernel (one launch per round) is timed with HIP events on the
+stream it runs on, giving its achieved HBM bandwidth against 8 TB/s.  The CPU
+oracle is timed on a bounded sample of the same workload as a reference point
+(never a target).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "lmhead_8b_bs1_traffic.txt")
+LMHEAD_SRC = os.path.join(ROOT, "eagle_draft_tree_expand_amd", "csrc", "k_lmhead.hip")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def lmhead_bytes(cfg, rows):
+    """Algorithmic bytes of one LM-head launch: W once, X, fp32 logits out."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    return cfg.V * cfg.H * esz + rows * cfg.H * esz + rows * cfg.V * 4
+
+
+def round_bytes(cfg, prefix_total):
+    """Algorithmic bytes of one round: draft rows, prefix KV, tree Q/K/V and O, W, X, logits."""
+    esz = 2 if cfg.dtype == "bf16" else 4
+    rows = cfg.B * cfg.N
+    draft = cfg.B * cfg.S * cfg.V * 4
+    kv = prefix_total * cfg.hkv * cfg.dh * esz * 2
+    tree = rows * (cfg.hq + 2 * cfg.hkv) * cfg.dh * esz + rows * cfg.hq * cfg.dh * esz
+    return draft + kv + tree + lmhead_bytes(cfg, rows)
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per LM-head launch from the committed rocprofv3 counter summary,
+    only if it was taken on the current kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kv = {}
+    for line in open(TRAFFIC_FILE):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256_16") != source_hash(LMHEAD_SRC):
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def setup(cfg_name, T, n_sets, device="cuda"):
+    import torch
+
+    import synth
+    from eagle_draft_tree_expand_amd import round as dround
+    cfg = synth.get_config(cfg_name)
+    t0 = time.time()
+    inps = [synth.make_inputs(cfg, s) for s in range(n_sets)]
+    wts = dround.DeviceWeights(inps[0], device)
+    sets = []
+    for inp in inps:
+        d = dround.DeviceInputs(inp, device, with_eps=True)
+        dround.device_draft_rows(cfg, wts, d, T)
+        d.eps = None  # only the rows are needed from here on
+        sets.append(d)
+    torch.cuda.synchronize()
+    log(f"[bench] {cfg_name}: inputs + device pre-pass for {n_sets} sets in {time.time() - t0:.1f}s")
+    return cfg, inps, wts, sets
+
+
+def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda"):
+    """Warm up, then time exactly `steps` rounds; LM-head launches timed with events."""
+    import torch
+
+    from eagle_draft_tree_expand_amd import round as dround
+    dr = dround.DeviceRound(cfg, device)
+    for i in range(warmup):
+        dr.step(wts, sets[i % len(sets)], T, round_id=i)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_start.record()
+    for i in range(steps):
+        d = sets[i % len(sets)]
+        dr.expand(d, T, i)
+        dr.mask_pos(d)
+        dr.gather_qkv(wts)
+        dr.attention(d)
+        ev[i][0].record()
+        dr.lmhead(wts, T)
+        ev[i][1].record()
+        dr.accept(d, T, i)
+    t_end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_start.elapsed_time(t_end)
+    lm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    # committed tokens: replay the same rounds untimed (results are deterministic)
+    committed = 0
+    for i in range(steps):
+        d = sets[i % len(sets)]
+        dr.step(wts, d, T, round_id=i)
+        committed += int(dr.acc["n_committed"].sum().item())
+    status = int(dr.status.item())
+    return dict(total_ms=total_ms, wall_s=wall, lm_ms=lm_ms, committed=committed, status=status)
+
+
+def cpu_baseline(cfg_name, T, inp, budget_s=25.0):
+    """The oracle, untuned, on a bounded sample: whole rounds of set 0 (pre-pass excluded)."""
+    from threadpoolctl import threadpool_info
+
+    from oracle import round as oround
+    wts = oround._Weights(inp)
+    t0 = time.time()
+    rows = oround.target_draft_rows(inp, T, wts)
+    prep = time.time() - t0
+    n, committed = 0, 0
+    t0 = time.time()
+    while True:
+        r = oround.run_round(inp, T, rows=rows, round_id=n, weights=wts)
+        committed += sum(a["n_committed"] for a in r["accept"])
+        n += 1
+        el = time.time() - t0
+        if el > budget_s * 0.5 or n >= 8:
+            break
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    log(f"[bench] oracle: pre-pass {prep:.1f}s, {n} rounds in {el:.1f}s")
+    return {"value": n * inp.cfg.B / el, "unit": "trees/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} whole rounds of the {cfg_name} workload (input set 0, round ids 0..{n - 1}), "
+                      f"draft-row pre-pass excluded; {committed / el:.3f} committed tokens/s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="8b")
+    ap.add_argument("--temp", type=float, default=1.0)
+    ap.add_argument("--sets", type=int, default=8)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the greedy and batch-64 extra lines")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(each request's round fits one GPU; see the sharding notes in DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+
+    cfg, inps, wts, sets = setup(args.config, args.temp, args.sets)
+    r = time_rounds(cfg, wts, sets, args.temp, args.steps, args.warmup)
+    ms = r["total_ms"] / args.steps
+    rounds_s = 1000.0 / ms
+    trees_s = rounds_s * cfg.B
+    tok_s = r["committed"] / (r["total_ms"] / 1000.0)
+    rows = cfg.B * cfg.N
+    lm_b = lmhead_bytes(cfg, rows)
+    achieved = lm_b / (r["lm_ms"] / 1000.0) / 1e9
+    prefix_total = int(sum(int(s.prefix_len.sum().item()) for s in sets) / len(sets))
+    rb = round_bytes(cfg, prefix_total)
+    traffic = read_traffic() if args.config == "8b" else None
+    out = {
+        "metric": "draft-tree verify rounds/sec + committed tokens/sec (8B shape, bs=1 and 64)",
+        "value": round(trees_s, 2),
+        "unit": "trees/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: batch {cfg.B}, hidden {cfg.H}, {cfg.hq}q/{cfg.hkv}kv heads x "
+                               f"{cfg.dh}, prefix {cfg.L[0]}-{cfg.L[1]}, vocab {cfg.V}, depth {cfg.D}, "
+                               f"top-k {cfg.k}, m {cfg.m}, T={args.temp}",
+                   "global_batch": cfg.B, "seq_len": cfg.Lmax, "parallelism": "single GPU",
+                   "input_sets": len(sets)},
+        "committed_tokens_per_s": round(tok_s, 1),
+        "tau_synthetic": round(r["committed"] / (args.steps * cfg.B), 4),
+        "round_hbm_fraction": round(rb / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": "lmhead_bf16 (eagle_lmhead_softmax)", "bytes_per_launch": lm_b,
+                     "avg_launch_ms": round(r["lm_ms"], 5)},
+        "device_status": r["status"],
+    }
+    if not args.no_extra and args.config == "8b":
+        gsteps = max(20, args.steps // 4)
+        g = time_rounds(cfg, wts, sets, 0.0, gsteps, 5)
+        out["greedy"] = {"trees_per_s": round(1000.0 * gsteps / g["total_ms"] * cfg.B, 2),
+                         "committed_tokens_per_s": round(g["committed"] / (g["total_ms"] / 1000.0), 1),
+                         "lmhead_ms": round(g["lm_ms"], 5)}
+        del sets
+        torch.cuda.empty_cache()
+        try:
+            cfg64, _, wts64, sets64 = setup("b64", 1.0, 2)
+            b = time_rounds(cfg64, wts64, sets64, 1.0, 10, 2)
+            ms64 = b["total_ms"] / 10
+            flops = 2.0 * cfg64.B * cfg64.N * cfg64.H * cfg64.V
+            out["b64"] = {"trees_per_s": round(1000.0 / ms64 * cfg64.B, 1), "ms_per_round": round(ms64, 3),
+                          "committed_tokens_per_s": round(b["committed"] / (b["total_ms"] / 1000.0), 1),
+                          "lmhead_ms": round(b["lm_ms"], 4),
+                          "lmhead_mfma_frac": round(flops / (b["lm_ms"] / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+            del sets64, wts64
+        except Exception as e:  # report, do not hide the main line
+            out["b64"] = {"error": repr(e)[:200]}
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(args.config, args.temp, inps[0])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

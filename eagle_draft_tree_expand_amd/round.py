@@ -94,7 +94,7 @@ class DeviceRound:
                     "n_committed": z(B), "near_tie": z(B)}
         self.status = z(1)
         self.scale = float(np.float32(1.0 / math.sqrt(c.dh)))
-        p = self.params(1.0)
+        p = self.params(1.0, m=min(max(self.N - 1, 1), c.P))  # sizing only: at least one draft node
         nbytes = ops.workspace_size(p, c.hq, c.hkv, c.dh, c.Lmax, c.H)
         if nbytes == 0:
             raise ValueError("invalid round shape")

@@ -66,12 +66,16 @@ def target_draft_rows(inp, T, weights=None):
         sig = np.float64(inp.sigma[b])
 
         def frontier_fn(items, b=b, sig=sig):
-            # The k frontier nodes of one depth: attend on each node's root path.
+            # The k frontier nodes of one depth: attend on each node's root path,
+            # then one LM-head product for the depth.
+            xs = []
             for s, path in items:
                 n = len(path)
                 x, _ = attention_rows(inp, b, path, np.arange(n) - 1)
-                z = wts.logits(x[-1:])[0]
-                rows[b, s] = (z + sig * inp.eps[b, s].astype(np.float64)).astype(np.float32)
+                xs.append(x[-1])
+            z = wts.logits(np.stack(xs))
+            for (s, _), zr in zip(items, z):
+                rows[b, s] = (zr + sig * inp.eps[b, s].astype(np.float64)).astype(np.float32)
 
         def children_fn(s, path, b=b):
             toks, q, _, _, _ = expand.children_of_row(rows[b, s], T, c.k, inp.gumbel_seed, s, b, 0)

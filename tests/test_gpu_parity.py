@@ -47,7 +47,7 @@ EXPAND_CASES = [
     ("mid_bf16", dict(), 0.0),
     ("mid_f32", dict(), 1.0),
     ("mid_bf16", dict(V=4096 * 3 + 17, k=16, D=3, m=40), 1.0),   # widest k, ragged vocab tail
-    ("mid_bf16", dict(V=64, k=5, D=4, m=85), 1.0),                # m = P, tiny vocab
+    ("mid_bf16", dict(V=64, k=5, D=4, m=80), 1.0),                # m = P, tiny vocab
     ("mid_bf16", dict(V=1000, k=1, D=6, m=6), 1.0),               # chain
     ("mid_bf16", dict(V=1000, k=3, D=1, m=2), 0.0),               # depth 1
 ]
@@ -96,7 +96,7 @@ def test_expand_is_deterministic(rt):
 
 
 # ---------------------------------------------------------------- mask
-@pytest.mark.parametrize("name,kw", [("mid_bf16", {}), ("mid_bf16", dict(V=64, k=5, D=4, m=85)),
+@pytest.mark.parametrize("name,kw", [("mid_bf16", {}), ("mid_bf16", dict(V=64, k=5, D=4, m=80)),
                                      ("mid_bf16", dict(V=1000, k=8, D=8, m=200))])
 def test_mask_matches_oracle(rt, name, kw):
     cfg = small_cfg(name, **kw)
@@ -119,7 +119,7 @@ def test_mask_matches_oracle(rt, name, kw):
 # ---------------------------------------------------------------- attention
 ATTN_CASES = [
     ("mid_bf16", {}, 2e-2),
-    ("mid_bf16", dict(hq=8, hkv=2, m=40, L=(1, 700)), 2e-2),     # 4 row tiles per wave, ragged prefix
+    ("mid_bf16", dict(hq=8, hkv=2, k=4, m=40, L=(1, 700), H=1024), 2e-2),  # 160 rows, ragged prefix
     ("mid_bf16", dict(hq=16, hkv=1, m=20, H=2048), 2e-2),         # 336 rows: two row blocks
     ("mid_bf16", dict(hq=2, hkv=2, dh=64, H=128), 2e-2),          # head_dim 64
     ("mid_bf16", dict(L=(0, 0)), 2e-2),                           # empty prefix: tree only
@@ -153,8 +153,8 @@ def test_attention_matches_oracle(rt, name, kw, tol):
 # ---------------------------------------------------------------- LM head
 LM_CASES = [
     ("mid_bf16", {}, 1.0),
-    ("mid_bf16", dict(V=257, H=256), 0.0),
-    ("mid_bf16", dict(B=2, m=60, V=3000, H=384), 0.8),     # 122 rows: two row blocks
+    ("mid_bf16", dict(V=257, H=256, hq=2), 0.0),
+    ("mid_bf16", dict(B=2, D=5, k=4, m=60, V=3000, H=384, hq=3, hkv=1), 0.8),  # 122 rows: two row blocks
     ("mid_f32", {}, 1.0),
     ("tiny", {}, 1.0),
 ]
