@@ -12,7 +12,6 @@ using namespace eagle;
 namespace {
 
 constexpr size_t kCounterBytes = 64 * 1024;           // ticket counters at the workspace head
-constexpr int kMaxTickets = (int)(kCounterBytes / 4);
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
@@ -53,7 +52,7 @@ int check_lm(int32_t rows, int32_t hidden, int32_t vocab, int32_t dtype) {
   } else {
     return EAGLE_ERR_DTYPE;
   }
-  if (lm_mtiles(rows) > kMaxTickets) return EAGLE_ERR_SHAPE;
+  if ((int64_t)lm_mtiles(rows) > 65535) return EAGLE_ERR_SHAPE;
   return EAGLE_OK;
 }
 
@@ -156,17 +155,33 @@ int eagle_tree_attention(int32_t batch, int32_t n, int32_t hq, int32_t hkv, int3
 }
 
 int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dtype, const void* x, const void* w,
-                         float temperature, float* logits, float* row_stats, int32_t* row_argmax, float* probs,
-                         void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+                         int32_t w_layout, float temperature, float* logits, float* row_stats, int32_t* row_argmax,
+                         float* probs, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
   int rc = check_lm(rows, hidden, vocab, dtype);
   if (rc != EAGLE_OK) return rc;
+  if (w_layout != EAGLE_W_ROWMAJOR && w_layout != EAGLE_W_PACKED) return EAGLE_ERR_SHAPE;
+  if (w_layout == EAGLE_W_PACKED && dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
   if (!(temperature >= 0.f) || !isfinite(temperature)) return EAGLE_ERR_SHAPE;
   if (!x || !w || !logits || !row_stats || !row_argmax || !ws) return EAGLE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w)) return EAGLE_ERR_ALIGN;
   if (ws_bytes < kCounterBytes + lm_ws_bytes(rows, vocab)) return EAGLE_ERR_WORKSPACE;
-  return launch_status(launch_lmhead(rows, hidden, vocab, dtype, x, w, temperature, logits, row_stats, row_argmax,
-                                     probs, stage_area(ws), static_cast<int32_t*>(ws), dev_status,
-                                     (hipStream_t)stream));
+  return launch_status(launch_lmhead(rows, hidden, vocab, dtype, w_layout, x, w, temperature, logits, row_stats,
+                                     row_argmax, probs, stage_area(ws), dev_status, (hipStream_t)stream));
+}
+
+size_t eagle_lmhead_packed_bytes(int32_t vocab, int32_t hidden, int32_t dtype) {
+  if (dtype != EAGLE_BF16 || check_lm(1, hidden, vocab, dtype) != EAGLE_OK) return 0;
+  return lm_packed_bytes(vocab, hidden);
+}
+
+int eagle_lmhead_pack_weight(int32_t vocab, int32_t hidden, int32_t dtype, const void* w, void* w_packed,
+                             void* stream) {
+  if (dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
+  int rc = check_lm(1, hidden, vocab, dtype);
+  if (rc != EAGLE_OK) return rc;
+  if (!w || !w_packed) return EAGLE_ERR_NULL;
+  if (!aligned16(w) || !aligned16(w_packed)) return EAGLE_ERR_ALIGN;
+  return launch_status(launch_pack_lmhead(vocab, hidden, w, w_packed, (hipStream_t)stream));
 }
 
 int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok, const int32_t* node_parent,

@@ -14,10 +14,9 @@
 // from global memory into registers, one 128-wide hidden chunk ahead of the
 // MFMAs, while the small X tile is staged through LDS.  The epilogue writes the
 // fp32 logits and a per-(row, tile) record (max z/T', sum exp, max z, argmax);
-// the last workgroup of each row block (atomic ticket) merges the records into
-// the row statistics, so one launch yields logits + stats + argmax.
-// fp32 kernel (lmhead_f32): one thread per vocab column; same records, merged by
-// a separate small kernel.
+// a second small launch (one workgroup per row) merges the records into the row
+// statistics and the argmax.  fp32 kernel (lmhead_f32): one thread per vocab
+// column, same records.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,7 +27,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKC = 128;             // hidden values per pipeline chunk
+constexpr int kKC = 64;              // hidden values per pipeline chunk (two MFMA k-steps)
 constexpr int kXPad = kKC + 8;       // LDS row stride of the X chunk (bf16)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -59,47 +58,12 @@ EDEV void rec_merge(Rec& a, const Rec& b) {
   if (beats(b.zmax, b.arg, a.zmax, a.arg)) { a.zmax = b.zmax; a.arg = b.arg; }
 }
 
-// Merge the records of rows [m0, m0 + nrows) into final stats (fp64 sums).
-// Called by a full workgroup; one wave per row at a time.
-EDEV void finalize_rows(const float* part, int ntiles, int m0, int nrows, float* row_stats, int32_t* row_argmax) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int r = wave; r < nrows; r += nw) {
-    const int m = m0 + r;
-    const float* pr = part + (size_t)m * ntiles * 4;
-    float tm = kNegInf, zm = kNegInf;
-    int ai = kIdxNone;
-    for (int t = lane; t < ntiles; t += 64) {
-      tm = fmaxf(tm, pr[t * 4]);
-      const float z = pr[t * 4 + 2];
-      const int a = __float_as_int(pr[t * 4 + 3]);
-      if (beats(z, a, zm, ai)) { zm = z; ai = a; }
-    }
-    const float M = wave_max(tm);
-    wave_argmax(zm, ai);
-    double s = 0.0;
-    if (M != kNegInf)
-      for (int t = lane; t < ntiles; t += 64) {
-        const float tt = pr[t * 4], ss = pr[t * 4 + 1];
-        if (tt != kNegInf) s += (double)ss * exp((double)tt - (double)M);
-      }
-    s = wave_sum_d(s);
-    if (lane == 0) {
-      row_stats[(size_t)m * 2] = M;
-      row_stats[(size_t)m * 2 + 1] = (float)s;
-      row_argmax[m] = ai == kIdxNone ? 0 : ai;
-    }
-  }
-}
-
+template <bool PACKED>
 __global__ __launch_bounds__(256) void lmhead_bf16_kernel(int rows, int H, int V, float Tp,
                                                           const uint16_t* __restrict__ x,
                                                           const uint16_t* __restrict__ w, float* __restrict__ logits,
-                                                          float* __restrict__ part, int32_t* __restrict__ tickets,
-                                                          float* __restrict__ row_stats,
-                                                          int32_t* __restrict__ row_argmax, int32_t* status) {
-  __shared__ __attribute__((aligned(16))) uint16_t Xs[kLmTileM * kXPad];
+                                                          float* __restrict__ part, int32_t* status) {
   __shared__ Rec wrec[4][kLmTileM];
-  __shared__ int is_last;
 
   const int ntiles = gridDim.x;
   const int nt_idx = blockIdx.x, mt_idx = blockIdx.y;
@@ -107,84 +71,61 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(int rows, int H, int V
   const int col = lane & 15, grp = lane >> 4;
   const int m0 = mt_idx * kLmTileM;
   const int n0 = nt_idx * kLmTileN + wave * 64;
+  const int nch = H / kKC;
 
-  // B-operand source rows of this lane: vocab n0 + nt*16 + col (clamped in range).
-  const uint16_t* wrow[4];
+  // Operand sources of this lane.  A = X rows m0 + mt*16 + col (clamped), k
+  // offset grp*8 within each 32-wide k-step.  B = W: row-major rows
+  // n0 + nt*16 + col (clamped), or the packed layout, where this wave's 64 rows
+  // form one contiguous stream: chunk c, load j is the 1 KB at
+  // ((g*nch + c)*8 + j)*512 elements, lane l reading its 16 bytes at l*8.
+  size_t roff[4], xoff[4];
 #pragma unroll
-  for (int nt = 0; nt < 4; ++nt) {
-    int n = n0 + nt * 16 + col;
-    n = n < V ? n : V - 1;
-    wrow[nt] = w + (size_t)n * H + grp * 8;
+  for (int t = 0; t < 4; ++t) {
+    roff[t] = PACKED ? ((size_t)(nt_idx * 4 + wave) * nch * 8 * 512 + (size_t)lane * 8)
+                     : (size_t)min(n0 + t * 16 + col, V - 1) * H + grp * 8;
+    xoff[t] = (size_t)min(m0 + t * 16 + col, rows - 1) * H + grp * 8;
   }
-  // X chunk loader: 64 rows x 128 values = 1024 uint4, 4 per thread.
-  uint4 xr[4];
-  auto load_x = [&](int k0) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + i * 256;
-      const int r = e >> 4, c = (e & 15) * 8;
-      int m = m0 + r;
-      m = m < rows ? m : rows - 1;
-      xr[i] = *reinterpret_cast<const uint4*>(x + (size_t)m * H + k0 + c);
-    }
-  };
-  auto store_x = [&]() {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = tid + i * 256;
-      const int r = e >> 4, c = (e & 15) * 8;
-      *reinterpret_cast<uint4*>(&Xs[r * kXPad + c]) = xr[i];
-    }
-  };
-
   floatx4 acc[4][4];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  B8 wcur[kKC / 32][4], wnxt[kKC / 32][4];
-#pragma unroll
-  for (int ks = 0; ks < kKC / 32; ++ks)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) wcur[ks][nt].w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[nt] + ks * 32));
-  load_x(0);
-  store_x();
-  __syncthreads();
-
-  const int nchunks = H / kKC;
-  for (int c = 0; c < nchunks; ++c) {
-    const bool more = c + 1 < nchunks;
-    if (more) {
-      const int k1 = (c + 1) * kKC;
-#pragma unroll
-      for (int ks = 0; ks < kKC / 32; ++ks)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          wnxt[ks][nt].w = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(wrow[nt] + k1 + ks * 32));
-      load_x(k1);
-    }
-#pragma unroll
-    for (int ks = 0; ks < kKC / 32; ++ks) {
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        B8 a;
-        a.u = *reinterpret_cast<const uint4*>(&Xs[(mt * 16 + col) * kXPad + ks * 32 + grp * 8]);
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, wcur[ks][nt].v, acc[mt][nt], 0, 0, 0);
-      }
-    }
-    if (more) {
-      __syncthreads();
-      store_x();
-      __syncthreads();
-#pragma unroll
-      for (int ks = 0; ks < kKC / 32; ++ks)
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) wcur[ks][nt] = wnxt[ks][nt];
-    }
+  // Every wave runs independently (no LDS, no barrier): it streams its 64 W
+  // rows from HBM and reads the small X tile through L2/L1, one 64-wide chunk
+  // ahead of its MFMAs in two register buffers.  Loads are unconditional
+  // (chunk indices clamp at the end) so the pipeline counters stay exact.
+  u32x4 wa[8], wb[8], xa[8], xb[8];
+#define LM_LOAD(wbuf, xbuf, c)                                                                                  \
+  {                                                                                                            \
+    const int k0 = (c) * kKC;                                                                                  \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                            \
+      wbuf[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(                                   \
+          w + (PACKED ? roff[0] + ((size_t)(c) * 8 + j) * 512 : roff[j & 3] + k0 + (j >> 2) * 32)));             \
+      xbuf[j] = *reinterpret_cast<const u32x4*>(x + xoff[j & 3] + k0 + (j >> 2) * 32);                          \
+    }                                                                                                          \
   }
+#define LM_COMPUTE(wbuf, xbuf)                                                                   \
+  _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                             \
+    _Pragma("unroll") for (int mt = 0; mt < 4; ++mt) {                                           \
+      B8 a;                                                                                      \
+      a.w = xbuf[ks * 4 + mt];                                                                   \
+      _Pragma("unroll") for (int nt = 0; nt < 4; ++nt) {                                         \
+        B8 bb;                                                                                   \
+        bb.w = wbuf[ks * 4 + nt];                                                                \
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bb.v, acc[mt][nt], 0, 0, 0);  \
+      }                                                                                          \
+    }                                                                                            \
+  }
+  LM_LOAD(wa, xa, 0)
+  for (int c = 0; c < nch; c += 2) {  // nch is even (hidden % 128 == 0)
+    LM_LOAD(wb, xb, c + 1)
+    LM_COMPUTE(wa, xa)
+    LM_LOAD(wa, xa, min(c + 2, nch - 1))
+    LM_COMPUTE(wb, xb)
+  }
+#undef LM_COMPUTE
+#undef LM_LOAD
 
   // Epilogue: logits + per-row record over this wave's 64 columns.
   bool bad = false;
@@ -230,26 +171,15 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(int rows, int H, int V
   }
   if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
   __syncthreads();
-  if (tid < kLmTileM) {
+  const int nrows = min(kLmTileM, rows - m0);
+  if (tid < nrows) {
     Rec rc = wrec[0][tid];
 #pragma unroll
     for (int wv = 1; wv < 4; ++wv) rec_merge(rc, wrec[wv][tid]);
-    const int m = m0 + tid;
-    if (m < rows) {
-      float* pr = part + ((size_t)m * ntiles + nt_idx) * 4;
-      *reinterpret_cast<float4*>(pr) = make_float4(rc.tmax, rc.s, rc.zmax, __int_as_float(rc.arg));
-    }
+    float* pr = part + ((size_t)(m0 + tid) * ntiles + nt_idx) * 4;
+    *reinterpret_cast<float4*>(pr) = make_float4(rc.tmax, rc.s, rc.zmax, __int_as_float(rc.arg));
   }
-  // Last workgroup of this row block merges every tile's record.
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) is_last = atomicAdd(&tickets[mt_idx], 1) == ntiles - 1;
-  __syncthreads();
-  if (!is_last) return;
-  __threadfence();
-  const int nrows = min(kLmTileM, rows - m0);
-  finalize_rows(part, ntiles, m0, nrows, row_stats, row_argmax);
-  if (tid == 0) atomicExch(&tickets[mt_idx], 0);
+
 }
 
 // fp32: block = 256 vocab columns of one row.  Reference-precision path for
@@ -292,10 +222,47 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(int rows, int H, int V,
   }
 }
 
+// One workgroup per row: merge the row's per-tile records (fp64 sum).
 __global__ __launch_bounds__(256) void lm_finalize_kernel(int rows, int ntiles, const float* __restrict__ part,
                                                           float* __restrict__ row_stats, int32_t* __restrict__ row_argmax) {
-  const int m0 = blockIdx.x * 4;
-  finalize_rows(part, ntiles, m0, min(4, rows - m0), row_stats, row_argmax);
+  __shared__ float shf[4];
+  __shared__ double shd[4];
+  __shared__ int shi[4];
+  const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* pr = part + (size_t)m * ntiles * 4;
+  float tm = kNegInf, zm = kNegInf;
+  int ai = kIdxNone;
+  for (int t = tid; t < ntiles; t += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(pr + (size_t)t * 4);
+    tm = fmaxf(tm, v.x);
+    if (beats(v.z, __float_as_int(v.w), zm, ai)) { zm = v.z; ai = __float_as_int(v.w); }
+  }
+  tm = wave_max(tm);
+  wave_argmax(zm, ai);
+  if (lane == 0) { shf[wave] = tm; shd[wave] = (double)zm; shi[wave] = ai; }
+  __syncthreads();
+  float M = shf[0];
+  float bz = (float)shd[0];
+  int ba = shi[0];
+  for (int w = 1; w < 4; ++w) {
+    M = fmaxf(M, shf[w]);
+    if (beats((float)shd[w], shi[w], bz, ba)) { bz = (float)shd[w]; ba = shi[w]; }
+  }
+  __syncthreads();
+  double s = 0.0;
+  if (M != kNegInf)
+    for (int t = tid; t < ntiles; t += 256) {
+      const float tt = pr[(size_t)t * 4], ss = pr[(size_t)t * 4 + 1];
+      if (tt != kNegInf) s += (double)ss * exp((double)tt - (double)M);
+    }
+  s = wave_sum_d(s);
+  if (lane == 0) shd[wave] = s;
+  __syncthreads();
+  if (tid == 0) {
+    row_stats[(size_t)m * 2] = M;
+    row_stats[(size_t)m * 2 + 1] = (float)((shd[0] + shd[1]) + (shd[2] + shd[3]));
+    row_argmax[m] = ba == kIdxNone ? 0 : ba;
+  }
 }
 
 __global__ __launch_bounds__(256) void probs_kernel(int rows, int V, float Tp, const float* __restrict__ logits,
@@ -309,26 +276,62 @@ __global__ __launch_bounds__(256) void probs_kernel(int rows, int V, float Tp, c
   }
 }
 
+// Row-major W [V, H] -> packed layout (see lmhead_bf16_kernel): one thread per
+// 16-byte unit; rows beyond V are zero.
+__global__ __launch_bounds__(256) void pack_w_kernel(int V, int H, const uint16_t* __restrict__ w,
+                                                     uint16_t* __restrict__ wp, size_t units) {
+  const int nch = H / kKC;
+  for (size_t u = (size_t)blockIdx.x * blockDim.x + threadIdx.x; u < units; u += (size_t)gridDim.x * blockDim.x) {
+    const int l = (int)(u & 63);
+    const size_t q = u >> 6;
+    const int j = (int)(q & 7);
+    const size_t gc = q >> 3;
+    const int c = (int)(gc % nch);
+    const size_t g = gc / nch;
+    const size_t row = g * 64 + (j & 3) * 16 + (l & 15);
+    const int k = c * kKC + (j >> 2) * 32 + (l >> 4) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < (size_t)V) v = *reinterpret_cast<const u32x4*>(w + row * H + k);
+    *reinterpret_cast<u32x4*>(wp + u * 8) = v;
+  }
+}
+
 }  // namespace
 
-hipError_t launch_lmhead(int rows, int H, int V, int dtype, const void* x, const void* w, float T, float* logits,
-                         float* row_stats, int32_t* row_argmax, float* probs, float* ws_part, int32_t* tickets,
+size_t lm_packed_bytes(int V, int H) { return (size_t)((V + 63) / 64) * (H / kKC) * 8 * 64 * 16; }
+
+hipError_t launch_pack_lmhead(int V, int H, const void* w, void* wp, hipStream_t st) {
+  const size_t units = lm_packed_bytes(V, H) / 16;
+  const int grid = (int)((units + 255) / 256 < 16384 ? (units + 255) / 256 : 16384);
+  pack_w_kernel<<<grid, 256, 0, st>>>(V, H, (const uint16_t*)w, (uint16_t*)wp, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const void* x, const void* w, float T,
+                         float* logits, float* row_stats, int32_t* row_argmax, float* probs, float* ws_part,
                          int32_t* status, hipStream_t st) {
   const float Tp = (T > 0.f) ? T : 1.0f;
   const int ntiles = lm_ntiles(V);
   if (dtype == EAGLE_BF16) {
     dim3 grid(ntiles, lm_mtiles(rows));
-    lmhead_bf16_kernel<<<grid, 256, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
-                                             ws_part, tickets, row_stats, row_argmax, status);
+    if (w_layout == EAGLE_W_PACKED)
+      lmhead_bf16_kernel<true><<<grid, 256, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
+                                                     ws_part, status);
+    else
+      lmhead_bf16_kernel<false><<<grid, 256, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
+                                                      ws_part, status);
   } else {
     dim3 grid(ntiles, rows);
     lmhead_f32_kernel<<<grid, 256, (size_t)H * sizeof(float), st>>>(rows, H, V, Tp, (const float*)x,
                                                                     (const float*)w, logits, ws_part, status);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    lm_finalize_kernel<<<(rows + 3) / 4, 256, 0, st>>>(rows, ntiles, ws_part, row_stats, row_argmax);
   }
   hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // A separate launch merges the per-tile records: the kernel boundary makes
+  // every workgroup's records visible (an in-kernel agent-scope fence would
+  // write back each XCD's whole L2 per workgroup).
+  lm_finalize_kernel<<<rows, 256, 0, st>>>(rows, ntiles, ws_part, row_stats, row_argmax);
+  e = hipGetLastError();
   if (e != hipSuccess || probs == nullptr) return e;
   const size_t total = (size_t)rows * V;
   const int grid = (int)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);

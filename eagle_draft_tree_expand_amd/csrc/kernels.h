@@ -58,10 +58,11 @@ constexpr int kLmTileM = 64;             // rows per workgroup
 inline int lm_ntiles(int V) { return (V + kLmTileN - 1) / kLmTileN; }
 inline int lm_mtiles(int rows) { return (rows + kLmTileM - 1) / kLmTileM; }
 inline size_t lm_ws_bytes(int rows, int V) { return (size_t)rows * lm_ntiles(V) * 4 * sizeof(float); }
-hipError_t launch_lmhead(int rows, int hidden, int V, int dtype, const void* x, const void* w,
+hipError_t launch_lmhead(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,
                          float T, float* logits, float* row_stats, int32_t* row_argmax,
-                         float* probs, float* ws_part, int32_t* tickets, int32_t* status,
-                         hipStream_t st);
+                         float* probs, float* ws_part, int32_t* status, hipStream_t st);
+size_t lm_packed_bytes(int V, int hidden);
+hipError_t launch_pack_lmhead(int V, int hidden, const void* w, void* wp, hipStream_t st);
 
 // ---- acceptance (k_accept.hip) ----
 hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32_t* node_tok,

@@ -9,7 +9,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import EAGLE_BF16, EAGLE_F32, TreeParams, check
+from ._lib import EAGLE_BF16, EAGLE_F32, EAGLE_W_PACKED, EAGLE_W_ROWMAJOR, TreeParams, check
 
 _DT = {torch.float32: EAGLE_F32, torch.bfloat16: EAGLE_BF16}
 
@@ -66,12 +66,25 @@ def tree_attention(batch, n, hq, hkv, head_dim, max_prefix, q, k_prefix, v_prefi
 
 
 def lmhead_softmax(rows, hidden, vocab, x, w, temperature, logits, row_stats, row_argmax, ws, probs=None,
-                   status=None):
+                   status=None, packed=False):
     dt = _DT[x.dtype]
-    rc = _lib.load().eagle_lmhead_softmax(rows, hidden, vocab, dt, _ptr(x), _ptr(w), float(temperature),
+    layout = EAGLE_W_PACKED if packed else EAGLE_W_ROWMAJOR
+    rc = _lib.load().eagle_lmhead_softmax(rows, hidden, vocab, dt, _ptr(x), _ptr(w), layout, float(temperature),
                                          _ptr(logits), _ptr(row_stats), _ptr(row_argmax), _ptr(probs), _ptr(ws),
                                          ws.numel(), _ptr(status), _stream())
     check("eagle_lmhead_softmax", rc)
+
+
+def pack_lmhead_weight(w):
+    """Packed copy of a row-major bf16 LM-head weight [vocab, hidden] (new device tensor)."""
+    vocab, hidden = w.shape
+    n = int(_lib.load().eagle_lmhead_packed_bytes(vocab, hidden, EAGLE_BF16))
+    if n == 0:
+        raise ValueError("no packed layout for this shape/dtype")
+    wp = torch.empty(n // 2, dtype=torch.bfloat16, device=w.device)
+    check("eagle_lmhead_pack_weight",
+          _lib.load().eagle_lmhead_pack_weight(vocab, hidden, EAGLE_BF16, _ptr(w), _ptr(wp), _stream()))
+    return wp
 
 
 def verify_accept(p: TreeParams, tree, target_logits, target_stats, target_argmax, draft_logits, slot_stats,

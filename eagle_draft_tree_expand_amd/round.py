@@ -32,10 +32,13 @@ def _t(a, dtype=None, device="cuda"):
 class DeviceWeights:
     """Inputs shared by every input set: LM-head weight and per-token q/k/v rows."""
 
-    def __init__(self, inp, device="cuda"):
+    def __init__(self, inp, device="cuda", packed=True):
         c = inp.cfg
         dt = _TORCH_DT[c.dtype]
         self.w = _t(inp.w, dt, device)
+        # bf16 weights are also packed once into the MFMA-native streaming layout
+        self.packed = packed and c.dtype == "bf16"
+        self.w_packed = ops.pack_lmhead_weight(self.w) if self.packed else None
         self.q_tab = _t(inp.q_tab, dt, device)
         self.k_tab = _t(inp.k_tab, dt, device)
         self.v_tab = _t(inp.v_tab, dt, device)
@@ -127,8 +130,9 @@ class DeviceRound:
 
     def lmhead(self, wts, T):
         c = self.cfg
-        ops.lmhead_softmax(self.B * self.N, c.H, c.V, self.x.view(self.B * self.N, c.H), wts.w, T, self.logits,
-                           self.stats, self.argmax, self.ws, status=self.status)
+        w = wts.w_packed if wts.packed else wts.w
+        ops.lmhead_softmax(self.B * self.N, c.H, c.V, self.x.view(self.B * self.N, c.H), w, T, self.logits,
+                           self.stats, self.argmax, self.ws, status=self.status, packed=wts.packed)
 
     def accept(self, data, T, round_id=0):
         ops.verify_accept(self.params(T, round_id, data.seed), self.tree, self.logits, self.stats, self.argmax,

@@ -85,6 +85,12 @@ extern "C" {
 
 typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
 
+/* Layout of the LM-head weight.  ROWMAJOR: [vocab, hidden] as given.
+ * PACKED: produced once by eagle_lmhead_pack_weight (bf16 only): every group
+ * of 64 vocab rows becomes one contiguous stream ordered exactly as the MFMA
+ * operand loads consume it, so each wave reads 1 KB contiguous per load. */
+typedef enum { EAGLE_W_ROWMAJOR = 0, EAGLE_W_PACKED = 1 } eagle_w_layout;
+
 /* Parameters of one round (host struct).
  *   temperature > 0: sampling at temperature T (both the target and the draft
  *   distributions are softmax(logits / T), [HW] section 2);
@@ -183,17 +189,28 @@ int eagle_tree_attention(int32_t batch, int32_t n, int32_t hq, int32_t hkv, int3
 
 /* LM-head logits at every row and the statistics of softmax(logits / T').
  * Source: [E1] background A3: p_{j+1} = LMHead(f_j) at every position.
- * In:  x [rows, hidden], w [vocab, hidden] (dtype), temperature T >= 0
- *        (T' = T, or 1 when T == 0).
+ * In:  x [rows, hidden], w (dtype) in layout w_layout: [vocab, hidden]
+ *        row-major, or EAGLE_W_PACKED (bf16, from eagle_lmhead_pack_weight);
+ *      temperature T >= 0 (T' = T, or 1 when T == 0).
  * Out: logits [rows, vocab] fp32 (= x . w^T, fp32 accumulation);
  *      row_stats [rows, 2] fp32: (M, S) = (max_v z_v / T', sum_v exp(z_v/T' - M));
  *      row_argmax [rows] int32: argmax_v z_v, lowest id on ties;
  *      probs [rows, vocab] fp32 or NULL: exp(z/T' - M) / S when non-NULL.
- * dtype EAGLE_BF16 needs hidden % 64 == 0. */
+ * dtype EAGLE_BF16 needs hidden % 128 == 0; fp32 needs hidden <= 16384. */
 int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dtype,
-                         const void* x, const void* w, float temperature, float* logits,
-                         float* row_stats, int32_t* row_argmax, float* probs, void* ws,
-                         size_t ws_bytes, int32_t* dev_status, void* stream);
+                         const void* x, const void* w, int32_t w_layout, float temperature,
+                         float* logits, float* row_stats, int32_t* row_argmax, float* probs,
+                         void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* Bytes of the packed LM-head weight for (vocab, hidden) in bf16 (0 if the
+ * shape or dtype has no packed form). */
+size_t eagle_lmhead_packed_bytes(int32_t vocab, int32_t hidden, int32_t dtype);
+
+/* Pack a row-major bf16 LM-head weight w [vocab, hidden] into w_packed
+ * (eagle_lmhead_packed_bytes bytes, 16-byte aligned; rows past vocab are
+ * zero-filled).  A one-time layout transform done when weights are loaded. */
+int eagle_lmhead_pack_weight(int32_t vocab, int32_t hidden, int32_t dtype, const void* w,
+                             void* w_packed, void* stream);
 
 /* Recursive speculative sampling down each request's tree.
  * Source: [E1] background A3 (accept x with probability min(1, p(x)/q(x));

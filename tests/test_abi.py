@@ -104,12 +104,26 @@ def test_attention_rejects(lib):
 
 def test_lmhead_rejects(lib):
     f = lib.eagle_lmhead_softmax
-    assert f(10, 100, 500, 1, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -2  # hidden%128
-    assert f(10, 128, 500, 2, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -3
-    assert f(0, 128, 500, 1, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -2
-    assert f(10, 128, 500, 1, None, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -1
-    assert f(10, 128, 500, 1, FAKE, FAKE, -2.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None) == -2
-    assert f(10, 128, 500, 1, FAKE, FAKE, 1.0, FAKE, FAKE, FAKE, None, FAKE, 10, None, None) == -4
+    good = (FAKE, FAKE, 0, 1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None)
+    assert f(10, 100, 500, 1, *good) == -2                      # bf16 needs hidden % 128
+    assert f(10, 128, 500, 2, *good) == -3                      # dtype
+    assert f(0, 128, 500, 1, *good) == -2
+    assert f(10, 128, 500, 1, None, *good[1:]) == -1
+    assert f(10, 128, 500, 1, FAKE, FAKE, 0, -2.0, *good[4:]) == -2
+    assert f(10, 128, 500, 1, FAKE, FAKE, 7, 1.0, *good[4:]) == -2    # layout
+    assert f(10, 128, 500, 0, FAKE, FAKE, 1, 1.0, *good[4:]) == -3    # packed is bf16 only
+    assert f(10, 128, 500, 1, *good[:-3], 10, None, None) == -4
+    assert f(10, 20000, 500, 0, *good) == -2                    # fp32 row must fit LDS
+
+
+def test_packed_weight_size_and_rejects(lib):
+    assert lib.eagle_lmhead_packed_bytes(128256, 4096, 1) == ((128256 + 63) // 64) * 64 * 4096 * 2
+    assert lib.eagle_lmhead_packed_bytes(100, 256, 1) == 128 * 256 * 2
+    assert lib.eagle_lmhead_packed_bytes(100, 100, 1) == 0
+    assert lib.eagle_lmhead_packed_bytes(100, 256, 0) == 0
+    assert lib.eagle_lmhead_pack_weight(100, 256, 0, FAKE, FAKE, None) == -3
+    assert lib.eagle_lmhead_pack_weight(100, 256, 1, None, FAKE, None) == -1
+    assert lib.eagle_lmhead_pack_weight(100, 256, 1, FAKE, FAKE + 8, None) == -6
 
 
 def test_mask_gather_accept_reject(lib):

@@ -160,16 +160,19 @@ LM_CASES = [
 ]
 
 
+@pytest.mark.parametrize("packed", [True, False])
 @pytest.mark.parametrize("name,kw,T", LM_CASES)
-def test_lmhead_matches_oracle(rt, name, kw, T):
+def test_lmhead_matches_oracle(rt, name, kw, T, packed):
     cfg = small_cfg(name, **kw)
+    if packed and cfg.dtype != "bf16":
+        pytest.skip("packed layout is bf16 only")
     inp = synth.make_inputs(cfg)
     rng = np.random.default_rng(5)
     X = rng.standard_normal((cfg.B * cfg.N, cfg.H)).astype(np.float32)
     if cfg.dtype == "bf16":
         X = synth.bf16_round(X)
     dr = rt.DeviceRound(cfg)
-    wts = rt.DeviceWeights(inp)
+    wts = rt.DeviceWeights(inp, packed=packed)
     dr.x.copy_(torch.from_numpy(X).to(dr.x.dtype).view(dr.x.shape))
     dr.lmhead(wts, T)
     dev = dr.host()
@@ -182,6 +185,25 @@ def test_lmhead_matches_oracle(rt, name, kw, T):
     clear = (srt[:, -1] - srt[:, -2]) > 1e-5 * np.abs(srt[:, -1]).clip(1e-3)
     assert np.array_equal(dev["argmax"][clear], np.argmax(z64, axis=1)[clear])
     assert dev["status"] == 0
+
+
+def test_pack_layout(rt):
+    """Packed weight = the documented permutation of the row-major weight, zero past vocab."""
+    from eagle_draft_tree_expand_amd import ops
+    V, H = 200, 256
+    w = synth.bf16_round(np.random.default_rng(3).standard_normal((V, H)).astype(np.float32))
+    wt = torch.from_numpy(w).to(torch.bfloat16).cuda()
+    wp = ops.pack_lmhead_weight(wt).float().cpu().numpy()
+    nch = H // 64
+    assert wp.size == ((V + 63) // 64) * nch * 8 * 64 * 8
+    units = wp.reshape(-1, 8)
+    for u in range(0, units.shape[0], 37):
+        l, j, gc = u % 64, (u // 64) % 8, u // 512
+        c, g = gc % nch, gc // nch
+        row = g * 64 + (j & 3) * 16 + (l & 15)
+        k = c * 64 + (j >> 2) * 32 + (l >> 4) * 8
+        ref = w[row, k:k + 8] if row < V else np.zeros(8, np.float32)
+        assert np.array_equal(units[u], ref)
 
 
 def test_lmhead_full_8b_sampled(rt):
