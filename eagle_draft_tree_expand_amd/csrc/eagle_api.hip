@@ -97,13 +97,13 @@ size_t eagle_workspace_size(const eagle_tree_params* p, int32_t hq, int32_t hkv,
     if (l > need) need = l;
   }
   need = (need + 255) / 256 * 256;
-  return kCounterBytes + need;
+  return (kCounterBytes + need + accept_mail_bytes(B) + 255) / 256 * 256;
 }
 
 int eagle_workspace_init(void* ws, size_t ws_bytes, void* stream) {
   if (!ws) return EAGLE_ERR_NULL;
-  if (ws_bytes < kCounterBytes) return EAGLE_ERR_WORKSPACE;
-  return launch_status(launch_zero_ints(static_cast<int32_t*>(ws), kCounterBytes / 4, (hipStream_t)stream));
+  if (ws_bytes < kCounterBytes || ws_bytes % 4 != 0) return EAGLE_ERR_WORKSPACE;
+  return launch_status(launch_zero_ints(static_cast<int32_t*>(ws), ws_bytes / 4, (hipStream_t)stream));
 }
 
 int eagle_expand_tree(const eagle_tree_params* p, const float* draft_logits, const int32_t* root_token,
@@ -192,20 +192,21 @@ int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok, con
                         int32_t* near_tie, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
   int rc = check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
-  (void)ws;
-  (void)ws_bytes;
   const bool greedy = !(p->temperature > 0.f);
   if (!node_tok || !node_parent || !node_slot || !pool_tok || !pool_flat || !accept_len || !accept_path ||
-      !committed || !n_committed || !near_tie)
+      !committed || !n_committed || !near_tie || !ws)
     return EAGLE_ERR_NULL;
   if (greedy ? !target_argmax : (!target_logits || !target_stats || !draft_logits || !slot_stats || !uniforms))
     return EAGLE_ERR_NULL;
-  const int S = 1 + (p->depth - 1) * p->topk;
-  (void)S;
+  const size_t mail = accept_mail_bytes(p->batch);
+  if (ws_bytes < kCounterBytes + mail) return EAGLE_ERR_WORKSPACE;
+  void* mailbox = static_cast<char*>(ws) + ((ws_bytes - mail) & ~(size_t)255) - 0;
+  if ((size_t)(static_cast<char*>(mailbox) - static_cast<char*>(ws)) + mail > ws_bytes) return EAGLE_ERR_WORKSPACE;
   return launch_status(launch_accept(p->batch, p->m + 1, p->vocab, p->depth, p->topk, p->temperature, node_tok,
                                      node_parent, node_slot, pool_tok, pool_flat, target_logits, target_stats,
-                                     target_argmax, draft_logits, slot_stats, uniforms, accept_len, accept_path,
-                                     committed, n_committed, near_tie, dev_status, (hipStream_t)stream));
+                                     target_argmax, draft_logits, slot_stats, uniforms, mailbox, accept_len,
+                                     accept_path, committed, n_committed, near_tie, dev_status,
+                                     (hipStream_t)stream));
 }
 
 int eagle_gather_rows(int32_t n_rows, int32_t row_elems, int32_t dtype, const void* table, int32_t table_rows,

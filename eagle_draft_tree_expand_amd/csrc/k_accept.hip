@@ -9,17 +9,29 @@
 // and accepted + 1 committed tokens).  Greedy: follow the child equal to the
 // target argmax (EAGLE-1 notes, A.1).
 //
-// One workgroup of 1024 threads per request.  The adjusted distributions are
-// never materialised: after rejecting x_0..x_{j-1} (drawn without replacement
-// from q) the unnormalised residual is max(0, p(y) - s_j q(y)) for untried y
-// and a frozen value f_i for each tried x_i, with s_0 = 0, Z_0 = R_0 = 1,
+// The adjusted distributions are never materialised: after rejecting
+// x_0..x_{j-1} (drawn without replacement from q) the unnormalised residual is
+// max(0, p(y) - s_j q(y)) for untried y and a frozen value f_i for each tried
+// x_i, with s_0 = 0, Z_0 = R_0 = 1,
 //   s_{j+1} = s_j + Z_j / R_j,  R_{j+1} = R_j - q(x_j),
-//   f_j = max(0, p(x_j) - s_{j+1} q(x_j)),  Z_{j+1} = sum of the residual,
+//   f_j = max(0, p(x_j) - s_{j+1} q(x_j)),  Z_{j+1} = sum of the residual
 // (induction on P <- norm(max(0, P - Q)), Q <- Q without x_j, renormalised).
-// So each rejection costs one vocabulary reduction G(s) = sum_y max(0, p - s q),
-// and the final draw one more pass over a single 4096-token chunk.  The
-// acceptance ratio of trial j is max(0, p(x_j) - s_j q(x_j)) R_j / (Z_j q(x_j)),
-// with p(x_j), q(x_j) evaluated in fp64.
+// Each rejection therefore costs one vocabulary reduction
+// G(s) = sum_y max(0, p(y) - s q(y)); the acceptance ratio of trial j is
+// max(0, p(x_j) - s_j q(x_j)) R_j / (Z_j q(x_j)) with p(x_j), q(x_j) in fp64.
+//
+// Parallel layout: a group of G workgroups per request, launched
+// cooperatively (all resident).  Every workgroup runs the same walk (same
+// inputs, same code: identical decisions) and owns a contiguous vocabulary
+// slice; a reduction is one pass over the slice plus an exchange of the G
+// partial sums through per-request mailbox words.  A word carries its own
+// validity tag, [1 | epoch 13 | step 10 | value 40], written and read with relaxed
+// agent-scope atomics, so no memory fence (which would write back a whole L2)
+// is needed.  Two banks alternate by step parity, so a workgroup can publish
+// step t+1 while slower ones still read step t.  The partial's value is the
+// top 40 bits of its fp64 (28-bit mantissa); every workgroup sums the G
+// decoded values in index order, so all agree bit for bit.  Spins are bounded:
+// a timeout sets EAGLE_STATUS_SYNC_TIMEOUT and the walk continues.
 #include "common.h"
 #include "kernels.h"
 
@@ -27,15 +39,15 @@ namespace eagle {
 
 namespace {
 
-constexpr int kThreads = 1024;
+constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
-constexpr int kChunk = kThreads * 4;         // token ids per reduction chunk
-constexpr int kMaxChunks = (EAGLE_MAX_VOCAB + kChunk - 1) / kChunk;
 constexpr double kTie = 1e-6;
+constexpr int kSpinMax = 1 << 18;
+constexpr int kAccGroupCap = 32;  // largest group used (exchange cost grows with the group)  // polls per wait (a fraction of a second)
 
 struct Rows {
   const float* zp;  // target logits row of the node
-  const float* zq;  // draft logits row of the node's slot (may be null when s == 0)
+  const float* zq;  // draft logits row of the node's slot (unused when s == 0)
   float Mp, Mq, Tp;
   double invSp, invSq;
 };
@@ -49,15 +61,25 @@ EDEV double resid_term(float zp, float zq, const Rows& R, double s) {
   return d > 0.0 ? d : 0.0;
 }
 
-// fp64 probabilities of one token (used for acceptance ratios and R).
+EDEV double resid_at(const Rows& R, int v, double s) { return resid_term(R.zp[v], s != 0.0 ? R.zq[v] : 0.f, R, s); }
+
+// fp64 probabilities of one token (acceptance ratios and R).
 EDEV double prob64(float z, float M, double invS, float Tp) {
   if (!isfinite(z)) return 0.0;
   return exp((double)(z / Tp) - (double)M) * invS;
 }
 
-struct Shared {
-  double csum[kMaxChunks];          // chunk sums of the last reduction
-  double wpart[kMaxChunks][kWaves]; // per-wave partials
+// Tags always carry the top bit, so zero-filled words never match.
+EDEV uint64_t tag_of(uint32_t epoch, int step) {
+  return (1ull << 63) | ((uint64_t)(epoch & 0x1FFFu) << 50) | ((uint64_t)(step & 1023) << 40);
+}
+constexpr uint64_t kTagMask = ~((1ull << 40) - 1);
+EDEV uint64_t encode_val(double v) { return (uint64_t)__double_as_longlong(v) >> 24; }
+EDEV double decode_val(uint64_t w) { return __longlong_as_double((long long)((w & ((1ull << 40) - 1)) << 24)); }
+
+struct Smem {
+  double red[kWaves];
+  double vals[kAccMaxGroup];   // decoded partials of the last reduction, by workgroup
   double scan[kWaves];
   double bc_d[4];
   int bc_i[4];
@@ -65,166 +87,210 @@ struct Shared {
   double tried_f[EAGLE_MAX_TOPK];
 };
 
-// All threads: chunk sums and total of the residual at s (tried tokens not
-// yet corrected).  Result total broadcast to all threads.
-EDEV double reduce_pass(const Rows& R, double s, int V, Shared& sh) {
+EDEV void publish(uint64_t* w, uint64_t v) { __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+EDEV uint64_t peek(uint64_t* w) { return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// Spin until *w carries `tag`; returns the word (bounded).
+EDEV uint64_t await_tag(uint64_t* w, uint64_t tag, int* timed_out) {
+  if (*timed_out) return tag;  // after one timeout the group no longer waits
+  uint64_t v = peek(w);
+  int it = 0;
+  while ((v & kTagMask) != tag) {
+    if (++it > kSpinMax) { *timed_out = 1; return tag; }
+    __builtin_amdgcn_s_sleep(1);
+    v = peek(w);
+  }
+  return v;
+}
+
+struct Group {
+  int G, g, lo, hi;  // group size, own index, own vocabulary slice [lo, hi)
+  int span;          // slice length (workgroup j owns [j*span, (j+1)*span))
+  Mailbox* mb;
+  uint32_t epoch;
+  int step;
+};
+
+// All threads of every workgroup of the group: Z = G(s) over the vocabulary
+// (tried tokens not corrected); per-workgroup partials left in sm.vals.
+EDEV double group_reduce(const Rows& R, double s, Group& gr, Smem& sm, int* timed_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nch = (V + kChunk - 1) / kChunk;
-  const bool vec = ((V & 3) == 0) && (((uintptr_t)R.zp & 15) == 0) && (R.zq == nullptr || ((uintptr_t)R.zq & 15) == 0);
-  for (int c = 0; c < nch; ++c) {
-    const int base = c * kChunk + tid * 4;
-    double a = 0.0;
-    if (vec && base + 3 < V) {
+  double a = 0.0;
+  const bool vec = ((((uintptr_t)R.zp) | (s != 0.0 ? (uintptr_t)R.zq : 0)) & 15) == 0;
+  for (int base = gr.lo + tid * 4; base < gr.hi; base += kThreads * 4) {
+    if (vec && base + 3 < gr.hi) {
       const float4 p4 = *reinterpret_cast<const float4*>(R.zp + base);
       float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
       if (s != 0.0) q4 = *reinterpret_cast<const float4*>(R.zq + base);
-      a = resid_term(p4.x, q4.x, R, s) + resid_term(p4.y, q4.y, R, s) + resid_term(p4.z, q4.z, R, s) +
-          resid_term(p4.w, q4.w, R, s);
+      a += resid_term(p4.x, q4.x, R, s) + resid_term(p4.y, q4.y, R, s) + resid_term(p4.z, q4.z, R, s) +
+           resid_term(p4.w, q4.w, R, s);
     } else {
-      for (int e = 0; e < 4; ++e) {
-        const int v = base + e;
-        if (v < V) a += resid_term(R.zp[v], s != 0.0 ? R.zq[v] : 0.f, R, s);
-      }
+      for (int e = 0; e < 4; ++e)
+        if (base + e < gr.hi) a += resid_at(R, base + e, s);
     }
-    a = wave_sum_d(a);
-    if (lane == 0) sh.wpart[c][wave] = a;
   }
+  a = wave_sum_d(a);
+  if (lane == 0) sm.red[wave] = a;
   __syncthreads();
-  for (int c = tid; c < nch; c += kThreads) {
-    double t = 0.0;
-    for (int w = 0; w < kWaves; ++w) t += sh.wpart[c][w];
-    sh.csum[c] = t;
+  const uint64_t tag = tag_of(gr.epoch, gr.step);
+  uint64_t* bank = gr.mb->bank[gr.step & 1];
+  if (tid == 0) {
+    const double part = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
+    publish(bank + gr.g, tag | encode_val(part));
   }
+  if (wave == 0 && lane < gr.G) sm.vals[lane] = decode_val(await_tag(bank + lane, tag, timed_out));
   __syncthreads();
   if (tid == 0) {
     double t = 0.0;
-    for (int c = 0; c < nch; ++c) t += sh.csum[c];
-    sh.bc_d[0] = t;
+    for (int j = 0; j < gr.G; ++j) t += sm.vals[j];
+    sm.bc_d[0] = t;
   }
   __syncthreads();
-  const double tot = sh.bc_d[0];
+  const double tot = sm.bc_d[0];
   __syncthreads();
+  ++gr.step;
   return tot;
 }
 
-// All threads: inverse-CDF draw from the residual at s (chunk sums from the
-// reduce_pass at the same s), tried tokens replaced by their frozen values.
-// Returns the token and counts a near tie into *ties (thread 0).
-EDEV int draw_pass(const Rows& R, double s, int V, int ntried, double uval, Shared& sh, int* ties) {
+// Inverse-CDF draw from the residual at s (partials from the group_reduce at
+// the same s), tried tokens replaced by their frozen values.  Every workgroup
+// finds the owning workgroup; that one locates the token in its slice and
+// posts it to the mailbox.  Returns the token in workgroup 0 (others: -1).
+EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr, Smem& sm, int V, int* ties,
+                    int* timed_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nch = (V + kChunk - 1) / kChunk;
+  // Corrected per-workgroup sums: add (f_i - current term) to the owner of x_i.
   if (tid == 0) {
-    // corrected chunk sums and total
     for (int i = 0; i < ntried; ++i) {
-      const int x = sh.tried_x[i];
-      const double cur = resid_term(R.zp[x], s != 0.0 ? R.zq[x] : 0.f, R, s);
-      sh.csum[x / kChunk] += sh.tried_f[i] - cur;
+      const int x = sm.tried_x[i];
+      const int owner = min(x / gr.span, gr.G - 1);
+      sm.vals[owner] += sm.tried_f[i] - resid_at(R, x, s);
     }
     double tot = 0.0;
-    for (int c = 0; c < nch; ++c) tot += sh.csum[c] > 0.0 ? sh.csum[c] : 0.0;
+    for (int j = 0; j < gr.G; ++j) tot += sm.vals[j] > 0.0 ? sm.vals[j] : 0.0;
     const double target = uval * tot;
     double cum = 0.0;
-    int cstar = -1;
-    for (int c = 0; c < nch; ++c) {
-      const double cs = sh.csum[c] > 0.0 ? sh.csum[c] : 0.0;
-      if (cs > 0.0 && cum + cs > target) { cstar = c; break; }
-      cum += cs;
+    int gstar = -1;
+    for (int j = 0; j < gr.G; ++j) {
+      const double c = sm.vals[j] > 0.0 ? sm.vals[j] : 0.0;
+      if (c > 0.0 && cum + c > target) { gstar = j; break; }
+      cum += c;
     }
-    if (cstar < 0) {  // rounding: take the last chunk with mass
-      for (int c = nch - 1; c >= 0; --c)
-        if (sh.csum[c] > 0.0) { cstar = c; break; }
+    if (gstar < 0) {
+      for (int j = gr.G - 1; j >= 0; --j)
+        if (sm.vals[j] > 0.0) { gstar = j; break; }
       cum = 0.0;
-      for (int c = 0; c < cstar; ++c) cum += sh.csum[c] > 0.0 ? sh.csum[c] : 0.0;
+      for (int j = 0; j < gstar; ++j) cum += sm.vals[j] > 0.0 ? sm.vals[j] : 0.0;
     }
-    sh.bc_i[0] = cstar;
-    sh.bc_d[1] = target - cum;  // offset inside the chunk
-    sh.bc_d[2] = tot;
+    sm.bc_i[0] = gstar < 0 ? 0 : gstar;
+    sm.bc_d[1] = target - cum;
+    sm.bc_d[2] = tot;
   }
   __syncthreads();
-  const int cstar = sh.bc_i[0];
-  const double off = sh.bc_d[1], tot = sh.bc_d[2];
-  // per-thread values of the chunk (ids cstar*4096 + 4*tid + e)
-  double val[4];
-  double mine = 0.0;
-  for (int e = 0; e < 4; ++e) {
-    const int v = (cstar < 0 ? 0 : cstar) * kChunk + tid * 4 + e;
-    double x = 0.0;
-    if (cstar >= 0 && v < V) {
-      x = resid_term(R.zp[v], s != 0.0 ? R.zq[v] : 0.f, R, s);
-      for (int i = 0; i < ntried; ++i)
-        if (sh.tried_x[i] == v) x = sh.tried_f[i];
-    }
-    val[e] = x;
-    mine += x;
-  }
-  // inclusive scan over threads (id order)
-  double inc = mine;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const double y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) sh.scan[wave] = inc;
-  __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int w = 0; w < kWaves; ++w) { const double y = sh.scan[w]; sh.scan[w] = t; t += y; }
-    sh.bc_i[1] = -1;
-  }
-  __syncthreads();
-  inc += sh.scan[wave];
-  const double exc = inc - mine;
-  // the thread whose [exc, inc) holds off picks inside its 4 values
-  if (mine > 0.0 && exc <= off && off < inc) {
-    double c = exc;
-    int pick = -1;
-    for (int e = 0; e < 4; ++e) {
-      if (val[e] > 0.0 && c + val[e] > off) {
-        pick = e;
-        if ((off - c) < kTie * tot || (c + val[e] - off) < kTie * tot) atomicAdd(ties, 1);
-        break;
+  const int gstar = sm.bc_i[0];
+  const double off0 = sm.bc_d[1], tot = sm.bc_d[2];
+  const uint64_t rtag = tag_of(gr.epoch, gr.step);
+  int token = -1;
+  if (gr.g == gstar) {
+    // scan the own slice in id order, 1024 tokens (4 per thread) per pass
+    double off = off0;
+    int found = -1, tie = 0, last_pos = -1;
+    for (int base = gr.lo; base < gr.hi && found < 0; base += kThreads * 4) {
+      double val[4], mine = 0.0;
+      for (int e = 0; e < 4; ++e) {
+        const int v = base + tid * 4 + e;
+        double x = 0.0;
+        if (v < gr.hi) {
+          x = resid_at(R, v, s);
+          for (int i = 0; i < ntried; ++i)
+            if (sm.tried_x[i] == v) x = sm.tried_f[i];
+        }
+        val[e] = x;
+        mine += x;
       }
-      c += val[e];
+      double inc = mine;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const double y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+      }
+      if (lane == 63) sm.scan[wave] = inc;
+      __syncthreads();
+      if (tid == 0) {
+        double t = 0.0;
+        for (int w = 0; w < kWaves; ++w) { const double y = sm.scan[w]; sm.scan[w] = t; t += y; }
+        sm.bc_d[3] = t;  // pass total
+        sm.bc_i[1] = -1;
+        sm.bc_i[2] = 0;
+        sm.bc_i[3] = -1;
+      }
+      __syncthreads();
+      inc += sm.scan[wave];
+      const double exc = inc - mine;
+      if (mine > 0.0 && exc <= off && off < inc) {
+        double c = exc;
+        int pick = -1, t2 = 0;
+        for (int e = 0; e < 4; ++e) {
+          if (val[e] > 0.0 && c + val[e] > off) {
+            pick = e;
+            if ((off - c) < kTie * tot || (c + val[e] - off) < kTie * tot) t2 = 1;
+            break;
+          }
+          c += val[e];
+        }
+        if (pick < 0)
+          for (int e = 3; e >= 0; --e)
+            if (val[e] > 0.0) { pick = e; break; }
+        atomicMax(&sm.bc_i[1], base + tid * 4 + pick);
+        if (t2) atomicOr(&sm.bc_i[2], 1);
+      }
+      // remember the last positive token of the slice (rounding fallback)
+      int lp = -1;
+      for (int e = 3; e >= 0; --e)
+        if (val[e] > 0.0) { lp = base + tid * 4 + e; break; }
+      if (lp >= 0) atomicMax(&sm.bc_i[3], lp);
+      __syncthreads();
+      found = sm.bc_i[1];
+      tie |= sm.bc_i[2];
+      if (sm.bc_i[3] >= 0) last_pos = sm.bc_i[3];
+      off -= sm.bc_d[3];
+      __syncthreads();
     }
-    if (pick < 0) for (int e = 3; e >= 0; --e) if (val[e] > 0.0) { pick = e; break; }
-    atomicMax(&sh.bc_i[1], cstar * kChunk + tid * 4 + pick);
-  }
-  __syncthreads();
-  if (tid == 0 && sh.bc_i[1] < 0) {
-    // rounding beyond the chunk's last positive value: take the last positive id
-    int last = -1;
-    for (int e = kChunk - 1; e >= 0 && last < 0 && cstar >= 0; --e) {
-      const int v = cstar * kChunk + e;
-      if (v >= V) continue;
-      double x = resid_term(R.zp[v], s != 0.0 ? R.zq[v] : 0.f, R, s);
-      for (int i = 0; i < ntried; ++i)
-        if (sh.tried_x[i] == v) x = sh.tried_f[i];
-      if (x > 0.0) last = v;
+    if (found < 0) found = last_pos >= 0 ? last_pos : gr.lo;
+    token = found;
+    if (tid == 0) {
+      if (tie) atomicAdd(ties, 1);
+      if (gr.g != 0) publish(&gr.mb->result, rtag | (uint64_t)(uint32_t)token);
     }
-    sh.bc_i[1] = last < 0 ? 0 : last;
   }
-  __syncthreads();
-  const int y = sh.bc_i[1];
-  __syncthreads();
-  return y;
+  if (gr.g == 0 && gstar != 0) {
+    if (tid == 0) {
+      const uint64_t w = await_tag(&gr.mb->result, rtag, timed_out);
+      sm.bc_i[0] = (int)(uint32_t)(w & 0xFFFFFFFFu);
+    }
+    __syncthreads();
+    token = sm.bc_i[0];
+  }
+  ++gr.step;
+  return gr.g == 0 ? token : -1;
 }
 
 __global__ __launch_bounds__(kThreads) void accept_kernel(
-    int N, int V, int D, int k, float T, const int32_t* __restrict__ node_tok, const int32_t* __restrict__ node_parent,
-    const int32_t* __restrict__ node_slot, const int32_t* __restrict__ pool_tok, const int32_t* __restrict__ pool_flat,
-    const float* __restrict__ tlog, const float* __restrict__ tstats, const int32_t* __restrict__ targmax,
-    const float* __restrict__ dlog, const float* __restrict__ sstats, const float* __restrict__ uniforms,
-    int32_t* accept_len, int32_t* accept_path, int32_t* committed, int32_t* n_committed, int32_t* near_tie,
-    int32_t* status) {
-  __shared__ Shared sh;
-  __shared__ int ties;
+    int b0, int G, int N, int V, int D, int k, float T, const int32_t* __restrict__ node_tok,
+    const int32_t* __restrict__ node_parent, const int32_t* __restrict__ node_slot, const int32_t* __restrict__ pool_tok,
+    const int32_t* __restrict__ pool_flat, const float* __restrict__ tlog, const float* __restrict__ tstats,
+    const int32_t* __restrict__ targmax, const float* __restrict__ dlog, const float* __restrict__ sstats,
+    const float* __restrict__ uniforms, Mailbox* __restrict__ mail, int32_t* accept_len, int32_t* accept_path,
+    int32_t* committed, int32_t* n_committed, int32_t* near_tie, int32_t* status) {
+  __shared__ Smem sm;
+  __shared__ int ties, timed_out;
   __shared__ int path[EAGLE_MAX_DEPTH + 1];
   __shared__ int comm[EAGLE_MAX_DEPTH + 2];
   __shared__ int npath, ncomm;
-  __shared__ int cur_u, cur_slot, acc_j, zero_resid;
+  __shared__ int cur_u, cur_slot, acc_j, zero_resid, follow, stale;
   __shared__ double st_s, st_Z, st_R;
 
-  const int b = blockIdx.x, tid = threadIdx.x;
+  const int b = b0 + (int)blockIdx.x / G, g = (int)blockIdx.x % G, tid = threadIdx.x;
   const int S = 1 + (D - 1) * k;
   const bool greedy = !(T > 0.f);
   const float Tp = greedy ? 1.f : T;
@@ -234,11 +300,11 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
   const int32_t* ptok = pool_tok + (size_t)b * S * k;
   const int32_t* pflat = pool_flat + (size_t)b * S * k;
   const float* U = uniforms + (size_t)b * N * (k + 1);
-  if (tid == 0) { ties = 0; npath = 0; ncomm = 0; cur_u = 0; zero_resid = 0; }
+  if (tid == 0) { ties = 0; timed_out = 0; npath = 0; ncomm = 0; cur_u = 0; zero_resid = 0; }
   __syncthreads();
 
   if (greedy) {
-    if (tid == 0) {
+    if (g == 0 && tid == 0) {
       int u = 0;
       for (int step = 0; step <= D; ++step) {
         const int y = targmax[(size_t)b * N + u];
@@ -252,31 +318,47 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       }
     }
   } else {
+    Group gr;
+    gr.G = G;
+    gr.g = g;
+    const int span = ((V + G - 1) / G + 3) / 4 * 4;
+    gr.lo = min(V, g * span);
+    gr.hi = min(V, gr.lo + span);
+    gr.span = span;
+    gr.mb = mail + b;
+    gr.epoch = __hip_atomic_load(&gr.mb->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    gr.step = 0;
+    if (tid == 0) {  // retire this workgroup's stale words from earlier calls
+      const uint64_t reset = tag_of(gr.epoch, 1023);
+      publish(&gr.mb->bank[0][g], reset);
+      publish(&gr.mb->bank[1][g], reset);
+    }
     for (int step = 0; step <= D; ++step) {
       if (tid == 0) cur_slot = nslot[cur_u];
       __syncthreads();
       const int u = cur_u, slot = cur_slot;
-      const float* zp = tlog + ((size_t)b * N + u) * V;
       Rows R;
-      R.zp = zp;
+      R.zp = tlog + ((size_t)b * N + u) * V;
       R.Tp = Tp;
       R.Mp = tstats[((size_t)b * N + u) * 2];
       R.invSp = 1.0 / (double)tstats[((size_t)b * N + u) * 2 + 1];
+      R.zq = nullptr;
+      R.Mq = 0.f;
+      R.invSq = 0.0;
       if (slot < 0 || slot >= S) {
         // never expanded: bonus token from the target
-        R.zq = nullptr; R.Mq = 0.f; R.invSq = 0.0;
-        reduce_pass(R, 0.0, V, sh);
-        const int y = draw_pass(R, 0.0, V, 0, (double)U[(size_t)u * (k + 1) + k], sh, &ties);
-        if (tid == 0) comm[ncomm++] = y;
+        group_reduce(R, 0.0, gr, sm, &timed_out);
+        const int y = group_draw(R, 0.0, 0, (double)U[(size_t)u * (k + 1) + k], gr, sm, V, &ties, &timed_out);
+        if (g == 0 && tid == 0) comm[ncomm++] = y;
         break;
       }
       R.zq = dlog + ((size_t)b * S + slot) * V;
       R.Mq = sstats[((size_t)b * S + slot) * 2];
       R.invSq = 1.0 / (double)sstats[((size_t)b * S + slot) * 2 + 1];
-      if (tid == 0) { st_s = 0.0; st_Z = 1.0; st_R = 1.0; acc_j = -1; }
+      if (tid == 0) { st_s = 0.0; st_Z = 1.0; st_R = 1.0; acc_j = -1; stale = 0; }
       __syncthreads();
       int ntried = 0;
-      bool stale = false;  // chunk sums do not match st_s
+      double s_fin = 0.0;
       for (int j = 0; j < k; ++j) {
         if (tid == 0) {
           const int x = ptok[(size_t)slot * k + j];
@@ -302,33 +384,32 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
           const int x = ptok[(size_t)slot * k + j];
           const int xc = (x < 0 || x >= V) ? 0 : x;
           const double qx = prob64(R.zq[xc], R.Mq, R.invSq, Tp);
-          sh.bc_d[3] = st_s + st_Z / st_R;          // candidate s_{j+1}
-          sh.tried_x[ntried] = xc;
+          sm.bc_d[3] = st_s + st_Z / st_R;
+          sm.tried_x[ntried] = xc;
           st_R = st_R - qx;
         }
         __syncthreads();
-        const double snew = sh.bc_d[3];
-        const double G = reduce_pass(R, snew, V, sh);
+        const double snew = sm.bc_d[3];
+        const double Gs = group_reduce(R, snew, gr, sm, &timed_out);
         if (tid == 0) {
-          double Z = G;
+          double Z = Gs;
           for (int i = 0; i < ntried; ++i) {
-            const int xi = sh.tried_x[i];
-            Z += sh.tried_f[i] - resid_term(R.zp[xi], R.zq[xi], R, snew);
+            const int xi = sm.tried_x[i];
+            Z += sm.tried_f[i] - resid_at(R, xi, snew);
           }
-          const int xj = sh.tried_x[ntried];
+          const int xj = sm.tried_x[ntried];
           if (Z > 0.0) {
-            sh.tried_f[ntried] = resid_term(R.zp[xj], R.zq[xj], R, snew);
+            sm.tried_f[ntried] = resid_at(R, xj, snew);
             st_s = snew;
             st_Z = Z;
-            sh.bc_i[2] = 0;
+            stale = 0;
           } else {  // zero residual mass: keep P
-            sh.tried_f[ntried] = resid_term(R.zp[xj], R.zq[xj], R, st_s);
+            sm.tried_f[ntried] = resid_at(R, xj, st_s);
             zero_resid = 1;
-            sh.bc_i[2] = 1;
+            stale = 1;
           }
         }
         __syncthreads();
-        stale = sh.bc_i[2] != 0;
         ++ntried;
       }
       if (acc_j >= 0) {
@@ -339,24 +420,29 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
           if (f > 0 && f < N && npath < D) {
             path[npath++] = f;
             cur_u = f;
-            sh.bc_i[3] = 1;
+            follow = 1;
           } else {
-            sh.bc_i[3] = 0;
+            follow = 0;
           }
         }
         __syncthreads();
-        if (!sh.bc_i[3]) break;
+        if (!follow) break;
         continue;
       }
-      // all k rejected: draw from the residual at st_s
-      const double s_fin = st_s;
-      if (stale) reduce_pass(R, s_fin, V, sh);
-      const int y = draw_pass(R, s_fin, V, ntried, (double)U[(size_t)u * (k + 1) + k], sh, &ties);
-      if (tid == 0) comm[ncomm++] = y;
+      // all k rejected: draw from the residual at st_s.  If the last reduction
+      // was not at st_s (zero-residual case), redo it.
+      s_fin = st_s;
+      if (stale) group_reduce(R, s_fin, gr, sm, &timed_out);
+      const int y = group_draw(R, s_fin, ntried, (double)U[(size_t)u * (k + 1) + k], gr, sm, V, &ties, &timed_out);
+      if (g == 0 && tid == 0) comm[ncomm++] = y;
       break;
     }
+    __syncthreads();
+    if (g == 0 && tid == 0) __hip_atomic_store(&gr.mb->epoch, gr.epoch + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   __syncthreads();
+  if (tid == 0 && timed_out) set_status(status, EAGLE_STATUS_SYNC_TIMEOUT);
+  if (g != 0) return;
   if (tid == 0 && zero_resid) set_status(status, EAGLE_STATUS_ZERO_RESIDUAL);
   if (tid <= D) {
     if (tid < D) accept_path[(size_t)b * D + tid] = tid < npath ? path[tid] : -1;
@@ -374,13 +460,41 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
 hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32_t* node_tok,
                          const int32_t* node_parent, const int32_t* node_slot, const int32_t* pool_tok,
                          const int32_t* pool_flat, const float* tlog, const float* tstats, const int32_t* targmax,
-                         const float* dlog, const float* sstats, const float* uniforms, int32_t* accept_len,
-                         int32_t* accept_path, int32_t* committed, int32_t* n_committed, int32_t* near_tie,
-                         int32_t* status, hipStream_t st) {
-  accept_kernel<<<B, kThreads, 0, st>>>(N, V, D, k, T, node_tok, node_parent, node_slot, pool_tok, pool_flat, tlog,
-                                       tstats, targmax, dlog, sstats, uniforms, accept_len, accept_path, committed,
-                                       n_committed, near_tie, status);
-  return hipGetLastError();
+                         const float* dlog, const float* sstats, const float* uniforms, void* mail,
+                         int32_t* accept_len, int32_t* accept_path, int32_t* committed, int32_t* n_committed,
+                         int32_t* near_tie, int32_t* status, hipStream_t st) {
+  const bool greedy = !(T > 0.f);
+  // Group size: as many workgroups per request as stay co-resident; requests
+  // beyond the resident capacity go in further launches.
+  static int capacity[64] = {0};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= 64) dev = 0;
+  if (capacity[dev] == 0) {
+    int per_cu = 0, cus = 0;
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_kernel, kThreads, 0);
+    if (e != hipSuccess) return e;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    capacity[dev] = per_cu * cus > 0 ? per_cu * cus : 1;
+  }
+  const int cap = capacity[dev];
+  int G = 1;
+  if (!greedy)
+    while (G * 2 <= kAccGroupCap && (size_t)B * G * 2 <= (size_t)cap && G * 2 * 1024 <= V) G *= 2;
+  const int per_launch = cap / G > 0 ? cap / G : 1;
+  Mailbox* mb = static_cast<Mailbox*>(mail);
+  for (int b0 = 0; b0 < B; b0 += per_launch) {
+    const int nb = B - b0 < per_launch ? B - b0 : per_launch;
+    void* args[] = {&b0, &G, &N, &V, &D, &k, &T, &node_tok, &node_parent, &node_slot, &pool_tok, &pool_flat, &tlog,
+                    &tstats, &targmax, &dlog, &sstats, &uniforms, &mb, &accept_len, &accept_path, &committed,
+                    &n_committed, &near_tie, &status};
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(accept_kernel), dim3(nb * G), dim3(kThreads), args,
+                                   0, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 }  // namespace eagle

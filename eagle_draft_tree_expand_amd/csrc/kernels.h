@@ -65,11 +65,20 @@ size_t lm_packed_bytes(int V, int hidden);
 hipError_t launch_pack_lmhead(int V, int hidden, const void* w, void* wp, hipStream_t st);
 
 // ---- acceptance (k_accept.hip) ----
+constexpr int kAccMaxGroup = 64;         // workgroups per request in the cooperative walk
+// Per-request mailbox of the walk (kept at the tail of the workspace).
+struct Mailbox {
+  uint64_t bank[2][kAccMaxGroup];
+  uint64_t result;
+  uint32_t epoch;
+  uint32_t pad[13];
+};
+inline size_t accept_mail_bytes(int B) { return (size_t)B * sizeof(Mailbox); }
 hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32_t* node_tok,
                          const int32_t* node_parent, const int32_t* node_slot,
                          const int32_t* pool_tok, const int32_t* pool_flat, const float* tlog,
                          const float* tstats, const int32_t* targmax, const float* dlog,
-                         const float* sstats, const float* uniforms, int32_t* accept_len,
+                         const float* sstats, const float* uniforms, void* mail, int32_t* accept_len,
                          int32_t* accept_path, int32_t* committed, int32_t* n_committed,
                          int32_t* near_tie, int32_t* status, hipStream_t st);
 

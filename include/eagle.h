@@ -29,11 +29,11 @@
  *     *dev_status (an optional device int32, may be NULL), to be read by the
  *     caller after synchronising.
  *   - Workspace: `ws` is caller-provided device scratch of `ws_bytes` bytes,
- *     at least eagle_workspace_size(...).  Before its first use it must be
- *     initialised once with eagle_workspace_init (the library keeps a few
- *     completion counters in it and returns them to zero after each call).
- *     Calls that share one workspace must be ordered (same stream); calls on
- *     different streams need different workspaces.
+ *     sized with eagle_workspace_size(...) for the round it serves.  Before
+ *     its first use it must be initialised once with eagle_workspace_init
+ *     (the acceptance walk keeps per-request mailboxes at its tail that
+ *     persist across calls).  Calls that share one workspace must be ordered
+ *     (same stream); calls on different streams need different workspaces.
  *   - Calls are deterministic: identical inputs give bit-identical outputs.
  *
  * Sources of the method (cited by page title and section):
@@ -75,6 +75,7 @@ extern "C" {
 #define EAGLE_STATUS_TOPK_RESCAN   0x8  /* child selection re-scanned a row (info only)  */
 #define EAGLE_STATUS_BAD_TREE      0x10 /* parent links not a valid flattened tree       */
 #define EAGLE_STATUS_CAND_OVERFLOW 0x20 /* child re-scan candidate list overflowed       */
+#define EAGLE_STATUS_SYNC_TIMEOUT  0x40 /* a walk workgroup gave up waiting for its group */
 
 /* ---- limits -------------------------------------------------------------- */
 #define EAGLE_MAX_TOPK   16
@@ -116,8 +117,8 @@ typedef struct eagle_tree_params {
 size_t eagle_workspace_size(const eagle_tree_params* p, int32_t hq, int32_t hkv,
                             int32_t head_dim, int32_t max_prefix, int32_t hidden);
 
-/* Zero the workspace's counter area (enqueued on `stream`, no memset node).
- * Call once after allocating a workspace. */
+/* Zero the whole workspace (enqueued on `stream` as a fill kernel, not a
+ * memset).  Call once after allocating a workspace. */
 int eagle_workspace_init(void* ws, size_t ws_bytes, void* stream);
 
 /* Dynamic draft-tree expansion, rerank and flattening for every request.
