@@ -43,7 +43,10 @@ struct UnitView {
   EDEV void set_idx(int r, int v) { p[2 + KP + r] = __int_as_float(v); }
 };
 
-template <bool GREEDY>
+// MODE: kGreedy (key z), kSampleT1 (key z + g, T = 1), kSampleT (key z/T + g).
+constexpr int kGreedy = 0, kSampleT1 = 1, kSampleT = 2;
+
+template <int MODE>
 __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
     const float* __restrict__ rows, int S, int V, float Tp, uint32_t k0, uint32_t k1,
     uint32_t round_lo, int KP, float* __restrict__ units, int32_t* status) {
@@ -67,7 +70,7 @@ __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
       for (int e = 0; e < 4; ++e) zz[e] = (base + e < V) ? z[base + e] : kNegInf;
     }
     uint4 w4 = make_uint4(0, 0, 0, 0);
-    if (!GREEDY) w4 = philox4x32_10(make_uint4((uint32_t)base >> 2, (uint32_t)s, (uint32_t)b, round_lo), k0, k1);
+    if (MODE != kGreedy) w4 = philox4x32_10(make_uint4((uint32_t)base >> 2, (uint32_t)s, (uint32_t)b, round_lo), k0, k1);
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = it * 4 + e;
@@ -75,12 +78,12 @@ __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
       float x = zz[e];
       if (valid && !isfinite(x)) { bad = true; x = kNegInf; }
       if (!valid) x = kNegInf;
-      t[j] = x / Tp;
-      if (GREEDY) {
+      t[j] = MODE == kSampleT ? x / Tp : x;
+      if (MODE == kGreedy) {
         key[j] = x;
       } else {
         const uint32_t wd = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
-        key[j] = (x == kNegInf) ? kNegInf : t[j] + gumbel_f32(word_to_uniform(wd));
+        key[j] = t[j] + gumbel_fast(wd);  // -inf stays -inf
       }
     }
   }
@@ -93,37 +96,85 @@ __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
   const float wm = wave_max(lm);
   float ls = 0.f;
   if (wm != kNegInf) {
+    constexpr float kLog2e = 1.44269504088896341f;
 #pragma unroll
-    for (int j = 0; j < kPer; ++j) ls += (t[j] == kNegInf) ? 0.f : expf(t[j] - wm);
+    for (int j = 0; j < kPer; ++j) ls += __builtin_amdgcn_exp2f((t[j] - wm) * kLog2e);  // exp2(-inf) = 0
   }
   const float wsum = wave_sum(ls);
 
-  // The wave's KP best (key desc, idx asc), by repeated wave argmax.
+  // The wave's KP best (key desc, idx asc).  Keys become order-preserving
+  // unsigned codes (0 = past the end of the vocabulary).  The KP-th largest
+  // of the 64 lane maxima, found bit by bit with ballots, bounds the wave's
+  // KP-th best key from below, so only elements at or above it can be in the
+  // top KP; they are compacted into LDS (usually ~KP of them) and each finds
+  // its rank by counting.  If more than 64 qualify (heavy ties, or a sparse
+  // tail) the wave falls back to KP rounds of wave argmax.
   UnitView u{units + ((size_t)row * gridDim.x * kExpUnitsPerChunk + (size_t)chunk * kExpUnitsPerChunk + wave) * (2 + 2 * KP), KP};
-  uint32_t taken = 0;
   auto idx_of = [&](int j) { return chunk * kExpChunk + (j >> 2) * (kExpThreads * 4) + tid * 4 + (j & 3); };
-  float bk = kNegInf;
-  int bi = kIdxNone;
+  uint32_t uk[kPer];
+  uint32_t lmax = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const int id = idx_of(j);
-    if (id < V && beats(key[j], id, bk, bi)) { bk = key[j]; bi = id; }
+    const uint32_t bits = __float_as_uint(key[j] + 0.0f);  // -0 -> +0: they tie like equal keys
+    const uint32_t code = bits ^ ((uint32_t)((int32_t)bits >> 31) | 0x80000000u);
+    uk[j] = idx_of(j) < V ? code : 0u;
+    lmax = max(lmax, uk[j]);
   }
-  for (int r = 0; r < KP; ++r) {
-    float wk = bk;
-    int wi = bi;
-    wave_argmax(wk, wi);
-    if (lane == 0) { u.key(r) = wk; u.set_idx(r, wi); }
-    if (wi != kIdxNone && bi == wi) {  // owner lane: drop the winner, find its next best
+  uint32_t thr = 0;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j)
-        if (idx_of(j) == wi) taken |= 1u << j;
-      bk = kNegInf;
-      bi = kIdxNone;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = thr | (1u << bit);
+    if (__popcll(__ballot(lmax >= c)) >= (unsigned)KP) thr = c;
+  }
+  thr = max(thr, 1u);
+  __shared__ uint64_t cand[4][64];
+  int total = 0;
 #pragma unroll
-      for (int j = 0; j < kPer; ++j) {
-        const int id = idx_of(j);
-        if (id < V && !((taken >> j) & 1u) && beats(key[j], id, bk, bi)) { bk = key[j]; bi = id; }
+  for (int j = 0; j < kPer; ++j) {
+    const bool take = uk[j] >= thr;
+    const uint64_t mask = __ballot(take);
+    const int pos = total + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+    if (take && pos < 64) cand[wave][pos] = ((uint64_t)uk[j] << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx_of(j));
+    total += __popcll(mask);
+  }
+  if (total <= 64) {
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const uint64_t mine = lane < total ? cand[wave][lane] : 0ull;
+    int r = 0;
+    for (int c = 0; c < total; ++c) r += cand[wave][c] > mine ? 1 : 0;
+    if (lane < total && r < KP) {
+      const uint32_t code = (uint32_t)(mine >> 32);
+      const uint32_t bits = (code & 0x80000000u) ? (code & 0x7fffffffu) : ~code;
+      u.key(r) = __uint_as_float(bits);
+      u.set_idx(r, (int)(0xffffffffu - (uint32_t)mine));
+    }
+    if (lane >= total && lane < KP) { u.key(lane) = kNegInf; u.set_idx(lane, kIdxNone); }
+  } else {
+    float bk = kNegInf;
+    int bi = kIdxNone;
+#pragma unroll
+    for (int j = 0; j < kPer; ++j) {
+      const int id = idx_of(j);
+      if (id < V && beats(key[j], id, bk, bi)) { bk = key[j]; bi = id; }
+    }
+    uint32_t taken = 0;
+    for (int r = 0; r < KP; ++r) {
+      float wk = bk;
+      int wi = bi;
+      wave_argmax(wk, wi);
+      if (lane == 0) { u.key(r) = wk; u.set_idx(r, wi); }
+      if (wi != kIdxNone && bi == wi) {  // owner lane: drop the winner, find its next best
+#pragma unroll
+        for (int j = 0; j < kPer; ++j)
+          if (idx_of(j) == wi) taken |= 1u << j;
+        bk = kNegInf;
+        bi = kIdxNone;
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+          const int id = idx_of(j);
+          if (id < V && !((taken >> j) & 1u) && beats(key[j], id, bk, bi)) { bk = key[j]; bi = id; }
+        }
       }
     }
   }
@@ -183,13 +234,55 @@ __device__ double exact_key(const float* z, int idx, int s, int b, float Tp, uin
   return (double)t + gumbel_f64(token_uniform(idx, s, b, round_lo, k0, k1));
 }
 
+// Bound on |fp32 candidate key - fp64 key| (fp32 rounding of t + g, and of g).
+EDEV double key_slack(double key) { return 8e-7 * (fabs(key) + 24.0); }
+
+// The k best of nc (key, idx) candidates in LDS under (key desc, idx asc)
+// into sel_key/sel_idx (kIdxNone past the end).  Up to one candidate per
+// thread: each counts the candidates that beat it, which is its rank; more
+// (rare): k rounds of block argmax.  The caller syncs afterwards.
+__device__ void block_topk(double* xkey, int* xidx, int nc, int k, double* sel_key, int* sel_idx,
+                           double* shd, int* shi) {
+  const int tid = threadIdx.x;
+  if (nc <= kExpThreads) {
+    if (tid < k && tid >= nc) { sel_key[tid] = -__builtin_huge_val(); sel_idx[tid] = kIdxNone; }
+    if (tid < nc) {
+      const double v = xkey[tid];
+      const int vi = xidx[tid];
+      int r = 0;
+      for (int c = 0; c < nc; ++c) r += beats_d(xkey[c], xidx[c], v, vi) ? 1 : 0;
+      if (r < k) { sel_key[r] = v; sel_idx[r] = vi; }
+    }
+    return;
+  }
+  double bk = -__builtin_huge_val();
+  int bi = kIdxNone, bc = -1;
+  for (int c = tid; c < nc; c += kExpThreads)
+    if (beats_d(xkey[c], xidx[c], bk, bi)) { bk = xkey[c]; bi = xidx[c]; bc = c; }
+  for (int r = 0; r < k; ++r) {
+    double wk = bk;
+    int wi = bi;
+    block_argmax_256(wk, wi, shd, shi);
+    if (tid == 0) { sel_key[r] = wk; sel_idx[r] = wi; }
+    if (wi != kIdxNone && bi == wi) {  // owner: hide the winner, find its next best
+      xkey[bc] = -__builtin_huge_val();
+      xidx[bc] = kIdxNone;
+      bk = -__builtin_huge_val();
+      bi = kIdxNone;
+      bc = -1;
+      for (int c = tid; c < nc; c += kExpThreads)
+        if (beats_d(xkey[c], xidx[c], bk, bi)) { bk = xkey[c]; bi = xidx[c]; bc = c; }
+    }
+  }
+}
+
 template <bool GREEDY>
 __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
     const float* __restrict__ rows, int S, int V, float Tp, uint32_t k0, uint32_t k1,
     uint32_t round_lo, int k, int KP, int C, const float* __restrict__ units,
     int32_t* __restrict__ pool_tok, float* __restrict__ pool_q, float* __restrict__ slot_stats,
     int32_t* status) {
-  extern __shared__ unsigned char smem_raw[];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int row = blockIdx.x;
   const int b = row / S, s = row - b * S;
   const int tid = threadIdx.x;
@@ -197,6 +290,9 @@ __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
   const int UF = 2 + 2 * KP;
   const float* z = rows + (size_t)row * V;
   const float* ub = units + (size_t)row * U * UF;
+  double* xkey = reinterpret_cast<double*>(smem_raw);          // [kExpRescanCap]
+  int* xidx = reinterpret_cast<int*>(xkey + kExpRescanCap);     // [kExpRescanCap]
+  float* heads = reinterpret_cast<float*>(xidx + kExpRescanCap);  // [U] best key of each record
 
   __shared__ double shd[4];
   __shared__ float shf[4];
@@ -204,10 +300,15 @@ __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
   __shared__ double sel_key[EAGLE_MAX_TOPK];
   __shared__ int sel_idx[EAGLE_MAX_TOPK];
   __shared__ int n_cand;
+  __shared__ float head_k;
 
-  // Row statistics from the wave records.
+  // Row statistics and record heads.
+  if (tid == 0) { n_cand = 0; head_k = kNegInf; }
   float lm = kNegInf;
-  for (int x = tid; x < U; x += kExpThreads) lm = fmaxf(lm, ub[(size_t)x * UF]);
+  for (int x = tid; x < U; x += kExpThreads) {
+    lm = fmaxf(lm, ub[(size_t)x * UF]);
+    heads[x] = __float_as_int(ub[(size_t)x * UF + 2 + KP]) == kIdxNone ? kNegInf : ub[(size_t)x * UF + 2];
+  }
   const float M = block_max_256(lm, shf);
   double ls = 0.0;
   if (M != kNegInf)
@@ -217,79 +318,78 @@ __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
     }
   const double Sd = block_sum_256(ls, shd);
 
-  // Candidates with exact keys.
+  // The k-th best record head bounds the k-th best fp32 key from below (k
+  // records each hold a key at least that large).  Fewer than k records: no
+  // bound.
+  for (int x = tid; x < U; x += kExpThreads) {
+    const float h = heads[x];
+    int r = 0;
+    for (int y = 0; y < U; ++y) {
+      const float w = heads[y];
+      r += (w > h || (w == h && y < x)) ? 1 : 0;
+    }
+    if (r == k - 1) head_k = h;
+  }
+  __syncthreads();
+
+  // Candidates: every record entry whose fp32 key can still reach the k-th
+  // place.  Greedy keys are the logits themselves (exact); sampling keys are
+  // within key_slack of the fp64 key, so the bound drops by twice the slack.
+  const float Hk = head_k;
+  const double thr = GREEDY ? (double)Hk : (double)Hk - 2.0 * key_slack(Hk);
   const int ncand0 = U * KP;
-  const int cap = ncand0 > kExpRescanCap ? ncand0 : kExpRescanCap;
-  double* ckey = reinterpret_cast<double*>(smem_raw);
-  int* cidx = reinterpret_cast<int*>(smem_raw + sizeof(double) * cap);
   for (int c = tid; c < ncand0; c += kExpThreads) {
     const int x = c / KP, r = c - x * KP;
     const int id = __float_as_int(ub[(size_t)x * UF + 2 + KP + r]);
-    if (id == kIdxNone || id < 0 || id >= V) {
-      ckey[c] = -__builtin_huge_val();
-      cidx[c] = kIdxNone;
-    } else {
-      ckey[c] = exact_key<GREEDY>(z, id, s, b, Tp, k0, k1, round_lo);
-      cidx[c] = id;
-    }
-  }
-  if (tid == 0) n_cand = ncand0;
-  __syncthreads();
-
-  for (int pass = 0; pass < 2; ++pass) {
-    const int nc = n_cand;
-    // Select the k best by repeated block argmax.
-    double bk = -__builtin_huge_val();
-    int bi = kIdxNone;
-    for (int c = tid; c < nc; c += kExpThreads)
-      if (beats_d(ckey[c], cidx[c], bk, bi)) { bk = ckey[c]; bi = cidx[c]; }
-    for (int r = 0; r < k; ++r) {
-      double wk = bk;
-      int wi = bi;
-      block_argmax_256(wk, wi, shd, shi);
-      if (tid == 0) { sel_key[r] = wk; sel_idx[r] = wi; }
-      if (wi != kIdxNone && bi == wi) {
-        bk = -__builtin_huge_val();
-        bi = kIdxNone;
-        for (int c = tid; c < nc; c += kExpThreads) {
-          if (cidx[c] == wi) { cidx[c] = kIdxNone; ckey[c] = -__builtin_huge_val(); }
-          else if (beats_d(ckey[c], cidx[c], bk, bi)) { bk = ckey[c]; bi = cidx[c]; }
-        }
+    const float ka = ub[(size_t)x * UF + 2 + r];
+    if (id != kIdxNone && id >= 0 && id < V && (double)ka >= thr) {
+      const int slot = atomicAdd(&n_cand, 1);
+      if (slot < kExpRescanCap) {
+        xidx[slot] = id;
+        xkey[slot] = (double)ka;
       }
     }
+  }
+  __syncthreads();
+  if (!GREEDY) {
+    const int nc = min(n_cand, kExpRescanCap);
+    for (int c = tid; c < nc; c += kExpThreads) xkey[c] = exact_key<false>(z, xidx[c], s, b, Tp, k0, k1, round_lo);
     __syncthreads();
-    if (GREEDY || pass == 1) break;
+  }
 
-    // Proof that no dropped logit can reach the k-th exact key: every wave
-    // record that is full must end strictly below it (minus the fp32 key error).
+  for (int pass = 0; pass < 2; ++pass) {
+    const int nc = min(n_cand, kExpRescanCap);
+    if (n_cand > kExpRescanCap && tid == 0) set_status(status, EAGLE_STATUS_CAND_OVERFLOW);
+    block_topk(xkey, xidx, nc, k, sel_key, sel_idx, shd, shi);
+    __syncthreads();
+    // Greedy: every token is in exactly one record and each record holds its
+    // slice's KP >= k best in exact order, so the union holds the top k.
+    if (GREEDY || pass == 1) break;
+    // Sampling: proof that no logit outside the records can reach the k-th
+    // exact key: every full record must end strictly below it (minus slack).
     const double Ek = sel_key[k - 1];
-    const double delta = 8e-7 * (fabs(Ek) + 24.0);
+    const double delta = key_slack(Ek);
     int need = 0;
     for (int x = tid; x < U; x += kExpThreads) {
       const int last = __float_as_int(ub[(size_t)x * UF + 2 + KP + (KP - 1)]);
       if (last != kIdxNone && (double)ub[(size_t)x * UF + 2 + (KP - 1)] + delta >= Ek) need = 1;
     }
     if (!block_or_256(need, shi)) break;
-
     // Rare: re-scan the row, keeping every logit whose fp32 key can reach Ek.
     if (tid == 0) { n_cand = 0; set_status(status, EAGLE_STATUS_TOPK_RESCAN); }
     __syncthreads();
-    const double thr = Ek - delta;
+    const double thr2 = Ek - delta;
     for (int v = tid; v < V; v += kExpThreads) {
       const float zz = z[v];
       if (!isfinite(zz)) continue;
       const float t = zz / Tp;
       const float ka = t + gumbel_f32(token_uniform(v, s, b, round_lo, k0, k1));
-      if ((double)ka >= thr) {
+      if ((double)ka >= thr2) {
         const int slot = atomicAdd(&n_cand, 1);
-        if (slot < cap) { cidx[slot] = v; ckey[slot] = exact_key<GREEDY>(z, v, s, b, Tp, k0, k1, round_lo); }
+        if (slot < kExpRescanCap) { xidx[slot] = v; xkey[slot] = exact_key<false>(z, v, s, b, Tp, k0, k1, round_lo); }
       }
     }
     __syncthreads();
-    if (n_cand > cap) {
-      if (tid == 0) { set_status(status, EAGLE_STATUS_CAND_OVERFLOW); n_cand = cap; }
-      __syncthreads();
-    }
   }
 
   if (tid < k) {
@@ -315,154 +415,188 @@ __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
 // = [k + (d-2)k^2, k + (d-1)k^2).  Pool-index order equals (depth, cidx) order,
 // so every tie-break "(depth asc, cidx asc)" is "pool index asc".
 
-struct TreeSmem {
-  float* val;
-  float* q;
-  int* lrank;
-  int* sorted;
-  int* slot_of;
-  int* flat_of;
-  int* gkey;
-  int* slot_src;
-};
 
 EDEV int layer_lo(int d, int k) { return d == 1 ? 0 : k + (d - 2) * k * k; }
 EDEV int layer_n(int d, int k) { return d == 1 ? k : k * k; }
 EDEV int depth_of(int e, int k) { return e < k ? 1 : 2 + (e - k) / (k * k); }
-EDEV bool vbeats(const float* val, int f, int e) { return val[f] > val[e] || (val[f] == val[e] && f < e); }
 
+// Order key of a pool node: value bits (values are >= 0, so their bit
+// patterns order like the values) over the complement of the pool index, so
+// that "larger key" is exactly (value desc, pool index asc).  All keys are
+// distinct; 0 is below every real key.
+EDEV uint64_t node_key(float v, int e) {
+  return ((uint64_t)__float_as_uint(v) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+EDEV float key_value(uint64_t key) { return __uint_as_float((uint32_t)(key >> 32)); }
+EDEV int key_node(uint64_t key) { return (int)(0xffffffffu - (uint32_t)key); }
+
+// One workgroup per request; everything in LDS.
+//  1. layers, one block step each: every node of the layer counts the keys
+//     of its layer above its own, which is its layer rank; the k best become
+//     the next frontier (slots) and give their children the values
+//     parent value * q;
+//  2. rerank: the m largest keys of the pool.  Only the first min(m, n) of
+//     each layer's sorted keys can make it; each of them adds, for every
+//     other layer, the count of larger keys there (binary search) to its
+//     layer rank;
+//  3. flatten: BFS order (depth, parent flat index, sibling rank) is the order
+//     of (depth, path of sibling ranks from the root) read as a number, so a
+//     selected node's flat index is 1 + the count of selected nodes before it.
 __global__ __launch_bounds__(256) void tree_assemble_kernel(
     int S, int k, int D, int m, int V, const int32_t* __restrict__ root_token,
     const int32_t* __restrict__ pool_tok_g, const float* __restrict__ pool_q_g,
     int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
     int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_flat_g,
     int32_t* slot_src_g, int32_t* status) {
-  extern __shared__ unsigned char smem_raw[];
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int P = S * k, N = m + 1;
-  TreeSmem sm;
-  sm.val = reinterpret_cast<float*>(smem_raw);
-  sm.q = sm.val + P;
-  sm.lrank = reinterpret_cast<int*>(sm.q + P);
-  sm.sorted = sm.lrank + P;
-  sm.slot_of = sm.sorted + P;
-  sm.flat_of = sm.slot_of + P;
-  sm.gkey = sm.flat_of + P;
-  sm.slot_src = sm.gkey + P;
-  __shared__ int cnt[EAGLE_MAX_DEPTH + 2];
-  __shared__ int base[EAGLE_MAX_DEPTH + 2];
+  const int LS = (k * k + 1) & ~1;                                 // layer stride (keys), even
+  uint64_t* lay = reinterpret_cast<uint64_t*>(smem_raw);          // [D][LS] keys in pool order, 0 padded
+  uint64_t* skeys = lay + D * LS;                                  // [D][LS] keys sorted desc
+  uint64_t* spath = skeys + D * LS;                                // [S] path of the node at each slot
+  uint64_t* sel_key = spath + S;                                   // [m] (depth, path) of each selected node
+  uint64_t* sel_key2 = sel_key + m;                                // [m] path alone (deep trees)
+  float* q = reinterpret_cast<float*>(sel_key2 + m);               // [P]
+  int* lrank = reinterpret_cast<int*>(q + P);                      // [P] rank inside the layer
+  int* flat_of = lrank + P;                                        // [P] flat index or -1
+  int* slot_src = flat_of + P;                                     // [S]
+  int* sel_e = slot_src + S;                                       // [m] pool index of each selected node
+  int* sel_dep = sel_e + m;                                        // [m]
+  __shared__ int n_sel;
 
   const float* pq = pool_q_g + (size_t)b * P;
   for (int e = tid; e < P; e += nt) {
-    sm.q[e] = pq[e];
-    sm.val[e] = e < k ? pq[e] : 0.f;  // layer 1: V = 1 * q
-    sm.slot_of[e] = -1;
-    sm.flat_of[e] = -1;
+    const float qe = pq[e];
+    q[e] = qe;
+    flat_of[e] = -1;
   }
-  for (int x = tid; x < S; x += nt) sm.slot_src[x] = -1;
-  if (tid <= D + 1) cnt[tid] = 0;
+  for (int x = tid; x < D * LS; x += nt) lay[x] = x < k ? node_key(pq[x], x) : 0ull;  // layer 1: value = 1 * q
+  for (int x = tid; x < S; x += nt) slot_src[x] = -1;
+  if (tid == 0) n_sel = 0;
   __syncthreads();
 
-  // Layer by layer: rank within the layer, frontier -> slots, children values.
+  // 1. Layers.
   for (int d = 1; d <= D; ++d) {
-    const int lo = layer_lo(d, k), n = layer_n(d, k);
-    for (int x = tid; x < n; x += nt) {
-      const int e = lo + x;
+    const int lo = layer_lo(d, k), n = layer_n(d, k), dl = d - 1;
+    const uint64_t* L = lay + dl * LS;
+    const int tpe = n <= 64 ? 4 : n <= 128 ? 2 : 1;  // threads per node (a lane group)
+    const int x = tid / tpe, part = tid & (tpe - 1);
+    if (x < n) {
+      const uint64_t K = L[x];
+      const int n2 = (n + 1) >> 1;
       int r = 0;
-      for (int y = 0; y < n; ++y) r += vbeats(sm.val, lo + y, e) ? 1 : 0;
-      sm.lrank[e] = r;
-      sm.sorted[lo + r] = e;
-      if (d < D && r < k) {
-        const int slot = 1 + (d - 1) * k + r;
-        sm.slot_src[slot] = e;
-        sm.slot_of[e] = slot;
+#pragma unroll 4
+      for (int y2 = part; y2 < n2; y2 += tpe) {
+        const ulonglong2 w = reinterpret_cast<const ulonglong2*>(L)[y2];
+        r += (w.x > K ? 1 : 0) + (w.y > K ? 1 : 0);
       }
-    }
-    __syncthreads();
-    if (d < D) {
-      for (int c = tid; c < k * k; c += nt) {
-        const int slot = 1 + (d - 1) * k + c / k;
-        const int child = slot * k + (c % k);
-        const int par = sm.slot_src[slot];
-        sm.val[child] = sm.val[par] * sm.q[child];
+      if (tpe >= 2) r += __shfl_xor(r, 1);
+      if (tpe >= 4) r += __shfl_xor(r, 2);
+      const int e = lo + x;
+      if (part == 0) {
+        lrank[e] = r;
+        skeys[dl * LS + r] = K;
       }
-      __syncthreads();
-    }
-  }
-
-  // Rerank: global rank = own layer rank + members of other layers that beat e.
-  for (int e = tid; e < P; e += nt) {
-    int g = sm.lrank[e];
-    if (g < m) {
-      const int de = depth_of(e, k);
-      for (int d = 1; d <= D && g < m; ++d) {
-        if (d == de) continue;
-        const int lo = layer_lo(d, k), n = layer_n(d, k);
-        int a = 0, z = n;  // count of sorted prefix beating e
-        while (a < z) {
-          const int mid = (a + z) >> 1;
-          if (vbeats(sm.val, sm.sorted[lo + mid], e)) a = mid + 1; else z = mid;
+      if (d < D && r < k) {  // frontier: slot 1 + (d-1)k + r, children in the next layer
+        const int slot = 1 + dl * k + r;
+        if (part == 0) {
+          slot_src[slot] = e;
+          spath[slot] = d == 1 ? (uint64_t)x : ((spath[e / k] << 4) | (uint64_t)(e % k));
         }
-        g += a;
+        const float v = key_value(K);
+        uint64_t* Ln = lay + d * LS;
+#pragma unroll 4
+        for (int j = part; j < k; j += tpe) {
+          const int c = slot * k + j;
+          Ln[r * k + j] = node_key(v * q[c], c);
+        }
       }
     }
-    if (g < m) {
-      sm.flat_of[e] = 0;  // selected, flat index assigned below
-      atomicAdd(&cnt[depth_of(e, k)], 1);
-    }
+    __syncthreads();
   }
-  __syncthreads();
-  if (tid == 0) {
-    base[1] = 1;
-    for (int d = 1; d <= D; ++d) base[d + 1] = base[d] + cnt[d];
+
+  // 2. Rerank.
+  const int c1 = min(m, k), cm = min(m, k * k);
+  const int ncand = c1 + (D - 1) * cm;
+  const int iters = 32 - __clz(cm);  // halvings that cover a prefix of cm keys
+  for (int c = tid; c < ncand; c += nt) {
+    const int dc = c < c1 ? 0 : 1 + (c - c1) / cm;
+    const int r = c < c1 ? c : (c - c1) - (dc - 1) * cm;
+    const uint64_t K = skeys[dc * LS + r];
+    int g = r;
+    for (int d0 = 0; d0 < D; d0 += 2) {  // two layers' searches interleaved
+      const int d1 = d0 + 1;
+      const int len0 = d0 == dc ? 0 : (d0 == 0 ? c1 : cm);
+      const int len1 = (d1 >= D || d1 == dc) ? 0 : cm;
+      const uint64_t* A = skeys + d0 * LS;
+      const uint64_t* B2 = skeys + (d1 < D ? d1 : d0) * LS;
+      int lo0 = 0, hi0 = len0, lo1 = 0, hi1 = len1;
+      for (int it = 0; it < iters; ++it) {
+        const int m0 = (lo0 + hi0) >> 1, m1 = (lo1 + hi1) >> 1;
+        const bool a0 = lo0 < hi0, a1 = lo1 < hi1;
+        const bool b0 = A[a0 ? m0 : 0] > K, b1 = B2[a1 ? m1 : 0] > K;
+        lo0 = (a0 && b0) ? m0 + 1 : lo0;
+        hi0 = (a0 && !b0) ? m0 : hi0;
+        lo1 = (a1 && b1) ? m1 + 1 : lo1;
+        hi1 = (a1 && !b1) ? m1 : hi1;
+      }
+      g += lo0 + lo1;
+    }
+    if (g < m) {
+      const int i = atomicAdd(&n_sel, 1);
+      if (i < m) {
+        const int e = key_node(K);
+        const int de = dc + 1;
+        const uint64_t path = de == 1 ? (uint64_t)e : ((spath[e / k] << 4) | (uint64_t)(e % k));
+        sel_e[i] = e;
+        sel_dep[i] = de;
+        sel_key[i] = D < 16 ? (((uint64_t)de << 60) | path) : (uint64_t)de;
+        sel_key2[i] = path;
+      }
+    }
   }
   __syncthreads();
 
-  // Flatten: (depth, parent flat index, sibling rank).
-  int bad = 0;
-  for (int d = 1; d <= D; ++d) {
-    const int lo = layer_lo(d, k), n = layer_n(d, k);
-    for (int x = tid; x < n; x += nt) {
-      const int e = lo + x;
-      if (sm.flat_of[e] < 0) continue;
-      int pf = 0;
-      if (d > 1) {
-        pf = sm.flat_of[sm.slot_src[e / k]];
-        if (pf <= 0) bad = 1;
+  // 3. Flatten.
+  const int cnt = n_sel < m ? n_sel : m;
+  for (int i = tid; i < cnt; i += nt) {
+    const uint64_t key = sel_key[i];
+    int r = 0;
+    if (D < 16) {  // depth and path fit one word
+      for (int j = 0; j < cnt; ++j) r += sel_key[j] < key ? 1 : 0;
+    } else {
+      const uint64_t key2 = sel_key2[i];
+      for (int j = 0; j < cnt; ++j) {
+        const uint64_t kj = sel_key[j];
+        r += (kj < key || (kj == key && sel_key2[j] < key2)) ? 1 : 0;
       }
-      sm.gkey[e] = pf * k + (e % k);
     }
-    __syncthreads();
-    for (int x = tid; x < n; x += nt) {
-      const int e = lo + x;
-      if (sm.flat_of[e] < 0) continue;
-      int r = 0;
-      for (int y = 0; y < n; ++y) {
-        const int f = lo + y;
-        r += (sm.flat_of[f] >= 0 && sm.gkey[f] < sm.gkey[e]) ? 1 : 0;
-      }
-      const int flat = base[d] + r;
-      if (flat >= N) { bad = 1; continue; }  // cannot happen for a strict rank order; never write out of range
-      const size_t o = (size_t)b * N + flat;
-      node_tok[o] = pool_tok_g[(size_t)b * P + e];
-      node_parent[o] = d == 1 ? 0 : sm.gkey[e] / k;
-      node_depth[o] = d;
-      node_sib[o] = e % k;
-      node_slot[o] = sm.slot_of[e];
-      node_value[o] = sm.val[e];
-      node_q[o] = sm.q[e];
-      sm.lrank[e] = flat;  // lrank no longer needed: holds the flat index
+    flat_of[sel_e[i]] = 1 + r;
+  }
+  __syncthreads();
+  int bad = (tid == 0 && n_sel != m) ? 1 : 0;  // keys are distinct, so exactly m are selected
+  for (int i = tid; i < cnt; i += nt) {
+    const int e = sel_e[i], de = sel_dep[i], f = flat_of[e];
+    int pf = 0;
+    if (de > 1) {
+      const int pe = slot_src[e / k];
+      pf = pe >= 0 ? flat_of[pe] : -1;
+      if (pf < 0) bad = 1;  // parent not selected: the tree would not be connected
     }
-    __syncthreads();
-    for (int x = tid; x < n; x += nt) {
-      const int e = lo + x;
-      if (sm.flat_of[e] >= 0) sm.flat_of[e] = sm.lrank[e];
-    }
-    __syncthreads();
+    const int lr = lrank[e];
+    const size_t o = (size_t)b * N + f;
+    node_tok[o] = pool_tok_g[(size_t)b * P + e];
+    node_parent[o] = pf;
+    node_depth[o] = de;
+    node_sib[o] = e % k;
+    node_slot[o] = (de < D && lr < k) ? 1 + (de - 1) * k + lr : -1;
+    node_value[o] = key_value(skeys[(de - 1) * LS + lr]);
+    node_q[o] = q[e];
   }
   if (bad) set_status(status, EAGLE_STATUS_BAD_TREE);
-  for (int e = tid; e < P; e += nt) pool_flat_g[(size_t)b * P + e] = sm.flat_of[e];
-  for (int x = tid; x < S; x += nt) slot_src_g[(size_t)b * S + x] = sm.slot_src[x];
+  for (int e = tid; e < P; e += nt) pool_flat_g[(size_t)b * P + e] = flat_of[e] > 0 ? flat_of[e] : -1;
+  for (int x = tid; x < S; x += nt) slot_src_g[(size_t)b * S + x] = slot_src[x];
   if (tid == 0) {
     const size_t o = (size_t)b * N;
     int rt = root_token[b];
@@ -493,14 +627,15 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
   const int C = exp_chunks(V);
   dim3 g1(C, B * S);
   if (greedy)
-    expand_scan_kernel<true><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, ws_units, status);
+    expand_scan_kernel<kGreedy><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, ws_units, status);
+  else if (Tp == 1.0f)
+    expand_scan_kernel<kSampleT1><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, ws_units, status);
   else
-    expand_scan_kernel<false><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, ws_units, status);
+    expand_scan_kernel<kSampleT><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, ws_units, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int ncand = C * kExpUnitsPerChunk * KP;
-  const int cap = ncand > kExpRescanCap ? ncand : kExpRescanCap;
-  const size_t sm2 = (size_t)cap * (sizeof(double) + sizeof(int));
+  const int U = C * kExpUnitsPerChunk;
+  const size_t sm2 = (size_t)kExpRescanCap * (sizeof(double) + sizeof(int)) + (size_t)U * sizeof(float);
   if (greedy)
     expand_merge_kernel<true><<<B * S, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, ws_units,
                                                              pool_tok, pool_q, slot_stats, status);
@@ -510,7 +645,9 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int P = S * k;
-  const size_t sm3 = (size_t)P * 7 * 4 + (size_t)S * 4;
+  const size_t LS = (size_t)((k * k + 1) & ~1);
+  const size_t sm3 = (2 * (size_t)D * LS + S + 2 * (size_t)m) * 8 + (size_t)P * 3 * 4 + (size_t)S * 4 +
+                     (size_t)m * 2 * 4;
   tree_assemble_kernel<<<B, 256, sm3, st>>>(S, k, D, m, V, root, pool_tok, pool_q, node_tok, node_parent,
                                             node_depth, node_sib, node_slot, node_value, node_q, pool_flat,
                                             slot_src, status);
