@@ -27,9 +27,12 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
-constexpr int kKT = 64;       // keys per LDS tile
-constexpr int kQT = 4;        // 16-row query tiles per wave
-constexpr int kRowsPerWG = 256;  // 4 waves x 4 tiles x 16 rows
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kKT = 64;            // keys per LDS tile
+constexpr int kQT = 2;             // 16-row query tiles per wave
+constexpr int kAttnThreads = 512;  // 8 waves
+constexpr int kRowsPerWG = 256;    // 8 waves x 2 tiles x 16 rows
 
 union B8 {
   bf16x8 v;
@@ -43,29 +46,31 @@ EDEV float* partial_row(float* ws, int b, int g, int hkv, int nsp1, int split, i
 }
 
 template <int DH>
-__global__ __launch_bounds__(256) void attn_split_bf16_kernel(
+__global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
     int n, int hq, int hkv, int Lmax, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const int32_t* __restrict__ plen, const uint16_t* __restrict__ kt,
     const uint16_t* __restrict__ vt, const uint64_t* __restrict__ mask, float scale, float* __restrict__ ws,
     int rows, int rows_pad, int split_keys, int nsplit) {
   constexpr int KPAD = DH + 8;    // K row stride in LDS (bf16 elements)
   constexpr int VPAD = kKT + 8;   // V^T row stride in LDS
+  constexpr float kLog2e = 1.44269504088896341f, kLn2 = 0.693147180559945309f;
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * KPAD];
   __shared__ __attribute__((aligned(16))) uint16_t Vts[DH * VPAD];
 
   const int nrb = (rows + kRowsPerWG - 1) / kRowsPerWG;
   const int split = blockIdx.x, g = blockIdx.y / nrb, rb = blockIdx.y - g * nrb, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nthr = blockDim.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = hq / hkv;
-  const int row0 = rb * kRowsPerWG + wave * 64;  // first query row of this wave
+  const int row0 = rb * kRowsPerWG + wave * (kQT * 16);  // first query row of this wave
   const int W = (n + 63) >> 6;
   const bool tree = split == nsplit;
   const int L = min(max(plen[b], 0), Lmax);  // prefix lengths beyond the buffer are clamped
   int k_begin, k_end;
   if (tree) { k_begin = 0; k_end = n; }
   else { k_begin = split * split_keys; k_end = min(L, k_begin + split_keys); }
+  const float sl2 = scale * kLog2e;  // scores are kept in the log2 domain
 
-  // Query tiles of this wave: rows [row0, row0 + 64).
+  // Query tiles of this wave.
   const int col = lane & 15, grp = lane >> 4;
   bf16x8 qreg[kQT][DH / 32];
   const uint64_t* mrow[kQT];
@@ -99,75 +104,102 @@ __global__ __launch_bounds__(256) void attn_split_bf16_kernel(
   const size_t kstride = tree ? (size_t)hkv * DH : (size_t)DH;
   const bool wave_active = row0 < rows;
 
+  // K/V tiles of 64 keys: this thread's share of the next tile is loaded
+  // into registers while the current tile is in use, then written to LDS
+  // (K row-major, V transposed) between two barriers.
+  constexpr int kChunks = kKT * (DH / 8) / kAttnThreads;  // 16-byte chunks per thread per tile
+  uint4 kreg[kChunks], vreg[kChunks];
+#define ATTN_LOAD_TILE(T0)                                                                   \
+  _Pragma("unroll") for (int i = 0; i < kChunks; ++i) {                                      \
+    const int x = tid + i * kAttnThreads, kk = x / (DH / 8), dc = (x - kk * (DH / 8)) * 8;   \
+    const int key = (T0) + kk;                                                               \
+    kreg[i] = make_uint4(0, 0, 0, 0);                                                        \
+    vreg[i] = make_uint4(0, 0, 0, 0);                                                        \
+    if (key < k_end) {                                                                       \
+      kreg[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * kstride + dc);         \
+      vreg[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * kstride + dc);         \
+    }                                                                                        \
+  }
+  if (k_begin < k_end) ATTN_LOAD_TILE(k_begin)
   for (int t0 = k_begin; t0 < k_end; t0 += kKT) {
-    // Stage K (row-major) and V (transposed) for keys [t0, t0 + 64).
     __syncthreads();
-    for (int x = tid; x < kKT * (DH / 8); x += nthr) {
-      const int kk = x / (DH / 8), dc = (x - kk * (DH / 8)) * 8;
-      const int key = t0 + kk;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (key < k_end) {
-        kv = *reinterpret_cast<const uint4*>(kbase + (size_t)key * kstride + dc);
-        vv = *reinterpret_cast<const uint4*>(vbase + (size_t)key * kstride + dc);
-      }
-      *reinterpret_cast<uint4*>(&Ks[kk * KPAD + dc]) = kv;
-      const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vv);
+#pragma unroll
+    for (int i = 0; i < kChunks; ++i) {
+      const int x = tid + i * kAttnThreads, kk = x / (DH / 8), dc = (x - kk * (DH / 8)) * 8;
+      *reinterpret_cast<uint4*>(&Ks[kk * KPAD + dc]) = kreg[i];
+      const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vreg[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) Vts[(dc + e) * VPAD + kk] = ve[e];
     }
     __syncthreads();
+    if (t0 + kKT < k_end) ATTN_LOAD_TILE(t0 + kKT)
     if (!wave_active) continue;
-
+    // Masking is needed only in the tree split and in a ragged last tile.
+    const bool masked = tree || t0 + kKT > k_end;
 #pragma unroll
     for (int t = 0; t < kQT; ++t) {
       // S^T tile: 64 keys x 16 queries, lane holds keys 16*kt + 4*grp + i of query col.
-      floatx4 s[4];
+      floatx4 sc[4];
 #pragma unroll
       for (int kt4 = 0; kt4 < 4; ++kt4) {
-        s[kt4] = floatx4{0.f, 0.f, 0.f, 0.f};
+        sc[kt4] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ds = 0; ds < DH / 32; ++ds) {
           B8 a;
           a.u = *reinterpret_cast<const uint4*>(&Ks[(kt4 * 16 + col) * KPAD + ds * 32 + grp * 8]);
-          s[kt4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, qreg[t][ds], s[kt4], 0, 0, 0);
+          sc[kt4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, qreg[t][ds], sc[kt4], 0, 0, 0);
         }
       }
-      // scale + mask, tile max
       float mx = kNegInf;
+      if (masked) {
+        // tiles start at multiples of 64 in the tree split; rows >= n read node 0
+        const uint64_t mw = tree ? mrow[t][t0 >> 6] : ~0ull;
 #pragma unroll
-      for (int kt4 = 0; kt4 < 4; ++kt4)
+        for (int kt4 = 0; kt4 < 4; ++kt4)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int key = t0 + kt4 * 16 + grp * 4 + i;
-          bool vis = key < k_end;
-          if (tree && vis) vis = (mrow[t][key >> 6] >> (key & 63)) & 1ull;  // rows >= n read node 0
-          const float v = vis ? s[kt4][i] * scale : kNegInf;
-          s[kt4][i] = v;
-          mx = fmaxf(mx, v);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int key = t0 + kt4 * 16 + grp * 4 + i;
+            const bool vis = key < k_end && ((mw >> (key & 63)) & 1ull);
+            const float v = vis ? sc[kt4][i] * sl2 : kNegInf;
+            sc[kt4][i] = v;
+            mx = fmaxf(mx, v);
+          }
+      } else {
+#pragma unroll
+        for (int kt4 = 0; kt4 < 4; ++kt4)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float v = sc[kt4][i] * sl2;
+            sc[kt4][i] = v;
+            mx = fmaxf(mx, v);
+          }
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 16));
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float mnew = fmaxf(mrun[t], mx);
-      const float alpha = (mnew == kNegInf) ? 1.f : __expf(mrun[t] - mnew);
+      const float mref = mnew == kNegInf ? 0.f : mnew;  // keeps exp2(-inf - mref) = 0
+      const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mref);
       mrun[t] = mnew;
       float psum = 0.f;
       B8 pb[2];
 #pragma unroll
       for (int kt4 = 0; kt4 < 4; ++kt4) {
-        uint16_t hb[4];
+        float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = (s[kt4][i] == kNegInf) ? 0.f : __expf(s[kt4][i] - mnew);
-          psum += p;
-          hb[i] = f32_to_bf16(p);
+          p[i] = __builtin_amdgcn_exp2f(sc[kt4][i] - mref);
+          psum += p[i];
         }
-        pb[kt4 >> 1].h[kt4 & 1] = make_uint2((uint32_t)hb[0] | ((uint32_t)hb[1] << 16),
-                                             (uint32_t)hb[2] | ((uint32_t)hb[3] << 16));
+        const bf16x2 lo2 = {(__bf16)p[0], (__bf16)p[1]}, hi2 = {(__bf16)p[2], (__bf16)p[3]};
+        pb[kt4 >> 1].h[kt4 & 1] = make_uint2(__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2));
       }
       lrun[t] = lrun[t] * alpha + psum;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < DH / 16; ++dt) o[t][dt] *= alpha;
+      }
 #pragma unroll
       for (int dt = 0; dt < DH / 16; ++dt) {
-        o[t][dt] *= alpha;
 #pragma unroll
         for (int beta = 0; beta < 2; ++beta) {
           B8 a;
@@ -179,9 +211,11 @@ __global__ __launch_bounds__(256) void attn_split_bf16_kernel(
       }
     }
   }
+#undef ATTN_LOAD_TILE
   if (!wave_active) return;
 
-  // Write partials: O^T lane holds d = 16*dt + 4*grp + i of query col.
+  // Write partials (running max back in the natural-log domain): O^T lane
+  // holds d = 16*dt + 4*grp + i of query col.
 #pragma unroll
   for (int t = 0; t < kQT; ++t) {
     float l = lrun[t];
@@ -193,7 +227,7 @@ __global__ __launch_bounds__(256) void attn_split_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < DH / 16; ++dt)
       *reinterpret_cast<float4*>(pr + dt * 16 + grp * 4) = make_float4(o[t][dt][0], o[t][dt][1], o[t][dt][2], o[t][dt][3]);
-    if (grp == 0) { pr[DH] = mrun[t]; pr[DH + 1] = l; }
+    if (grp == 0) { pr[DH] = mrun[t] == kNegInf ? kNegInf : mrun[t] * kLn2; pr[DH + 1] = l; }
   }
 }
 
@@ -292,10 +326,13 @@ AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, 
   AttnPlan pl;
   pl.rows = n * (hq / hkv);
   pl.rows_pad = (pl.rows + 15) / 16 * 16;
-  const int target = (512 + B * hkv - 1) / (B * hkv);
+  // Enough splits to give every CU a workgroup (256 CUs), each at least two
+  // 64-key tiles so that the register prefetch has something to overlap.
+  const int per = B * hkv;
+  const int target = (256 + per - 1) / per;
   int sk = (max_prefix + target - 1) / (target > 0 ? target : 1);
   sk = (sk + kKT - 1) / kKT * kKT;
-  if (sk < 256) sk = 256;
+  if (sk < 128) sk = 128;
   if (sk > 1024) sk = 1024;
   pl.split_keys = sk;
   pl.nsplit = (max_prefix + sk - 1) / sk;
@@ -311,7 +348,7 @@ hipError_t launch_attention(int B, int n, int hq, int hkv, int DH, int Lmax, int
   if (dtype == EAGLE_BF16) {
     const int nrb = (pl.rows + kRowsPerWG - 1) / kRowsPerWG;
     dim3 grid(pl.nsplit + 1, hkv * nrb, B);
-    const int threads = 256;
+    const int threads = kAttnThreads;
 #define EAGLE_ATTN_BF16(D)                                                                                           \
   attn_split_bf16_kernel<D><<<grid, threads, 0, st>>>(n, hq, hkv, Lmax, (const uint16_t*)q, (const uint16_t*)kp,    \
                                                       (const uint16_t*)vp, plen, (const uint16_t*)kt,               \
