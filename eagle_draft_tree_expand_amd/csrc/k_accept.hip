@@ -42,8 +42,8 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = kThreads / 64;
 constexpr double kTie = 1e-6;
-constexpr int kSpinMax = 1 << 18;
-constexpr int kAccGroupCap = 32;  // largest group used (exchange cost grows with the group)  // polls per wait (a fraction of a second)
+constexpr int kSpinMax = 1 << 18;  // polls per wait (a fraction of a second)
+constexpr int kAccGroupCap = 32;   // largest group used (exchange cost grows with the group)
 
 struct Rows {
   const float* zp;  // target logits row of the node
