@@ -47,6 +47,7 @@ int check_lm(int32_t rows, int32_t hidden, int32_t vocab, int32_t dtype) {
   if (rows < 1 || hidden < 1 || vocab < 1 || vocab > (1 << 24)) return EAGLE_ERR_SHAPE;
   if (dtype == EAGLE_BF16) {
     if (hidden % 128 != 0) return EAGLE_ERR_SHAPE;
+    if ((int64_t)rows * hidden >= ((int64_t)1 << 31)) return EAGLE_ERR_SHAPE;  // 32-bit X offsets
   } else if (dtype == EAGLE_F32) {
     if (hidden > 16384) return EAGLE_ERR_SHAPE;  // the fp32 path keeps one input row in LDS
   } else {

@@ -7,16 +7,17 @@
 // section 2).
 //
 // bf16 kernel (lmhead_bf16): logits = X W^T on MFMA (v_mfma_f32_16x16x32_bf16,
-// fp32 accumulation).  One workgroup = 64 rows x 256 vocab columns; 4 waves,
-// each owning 64 columns.  For the skinny shapes of a verify round (one or a
-// few 64-row tiles) the kernel streams W exactly once from HBM: each lane loads
-// its B-operand fragments (8 consecutive hidden values of one vocab row) straight
-// from global memory into registers, one 128-wide hidden chunk ahead of the
-// MFMAs, while the small X tile is staged through LDS.  The epilogue writes the
-// fp32 logits and a per-(row, tile) record (max z/T', sum exp, max z, argmax);
-// a second small launch (one workgroup per row) merges the records into the row
-// statistics and the argmax.  fp32 kernel (lmhead_f32): one thread per vocab
-// column, same records.
+// fp32 accumulation).  One workgroup = 64 rows x 512 vocab columns, 8 waves:
+// four column quarters of 128 columns times two halves of the hidden
+// dimension.  For the skinny shapes of a verify round (one or a few 64-row
+// tiles) the kernel streams W exactly once from HBM: each lane loads its
+// B-operand fragments straight from global memory into registers, one 64-wide
+// hidden chunk ahead of the MFMAs, and reads the small X tile through L2/L1.
+// The two hidden halves are summed through LDS; the epilogue writes the fp32
+// logits and a per-(row, tile) record (max z/T', sum exp, max z, argmax); a
+// second small launch (one workgroup per row) merges the records into the row
+// statistics and the argmax.  fp32 kernel (lmhead_f32): one thread per two
+// vocab columns, same records.
 #include "common.h"
 #include "kernels.h"
 
@@ -28,6 +29,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 constexpr int kKC = 64;              // hidden values per pipeline chunk (two MFMA k-steps)
+constexpr float kLog2e = 1.44269504088896341f;
 constexpr int kXPad = kKC + 8;       // LDS row stride of the X chunk (bf16)
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -59,94 +61,140 @@ EDEV void rec_merge(Rec& a, const Rec& b) {
 }
 
 template <bool PACKED>
-__global__ __launch_bounds__(256) void lmhead_bf16_kernel(int rows, int H, int V, float Tp,
-                                                          const uint16_t* __restrict__ x,
-                                                          const uint16_t* __restrict__ w, float* __restrict__ logits,
-                                                          float* __restrict__ part, int32_t* status) {
+__global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H, int V, float Tp,
+                                                                 const uint16_t* __restrict__ x,
+                                                                 const uint16_t* __restrict__ w,
+                                                                 float* __restrict__ logits, float* __restrict__ part,
+                                                                 int32_t* status) {
+  constexpr int NT = 8;  // 16-column n-tiles per wave: 128 vocab columns
+  __shared__ floatx4 xch[4][2][NT][64];  // accumulator exchange between the two hidden halves (64 KB)
   __shared__ Rec wrec[4][kLmTileM];
 
   const int ntiles = gridDim.x;
   const int nt_idx = blockIdx.x, mt_idx = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wq = wave & 3, kh = wave >> 2;  // column quarter, hidden half
   const int col = lane & 15, grp = lane >> 4;
   const int m0 = mt_idx * kLmTileM;
-  const int n0 = nt_idx * kLmTileN + wave * 64;
+  const int n0 = nt_idx * kLmTileN + wq * (NT * 16);  // first vocab column of this wave
   const int nch = H / kKC;
+  const int c0 = kh * (nch / 2), c1 = kh ? nch : nch / 2;
+  const int ngroups = (V + 63) / 64;
 
   // Operand sources of this lane.  A = X rows m0 + mt*16 + col (clamped), k
   // offset grp*8 within each 32-wide k-step.  B = W: row-major rows
-  // n0 + nt*16 + col (clamped), or the packed layout, where this wave's 64 rows
-  // form one contiguous stream: chunk c, load j is the 1 KB at
+  // n0 + nt*16 + col (clamped), or the packed layout, where each 64-row group
+  // is one contiguous stream: chunk c, load j of group g is the 1 KB at
   // ((g*nch + c)*8 + j)*512 elements, lane l reading its 16 bytes at l*8.
-  size_t roff[4], xoff[4];
+  // Packed addresses are a wave-uniform base plus the lane's 16 bytes.
+  const uint16_t* wq0 = w + (size_t)min(n0 / 64, ngroups - 1) * nch * 4096;      // this wave's first group
+  const uint16_t* wq1 = w + (size_t)min(n0 / 64 + 1, ngroups - 1) * nch * 4096;  // and its second
+  size_t wrow[PACKED ? 1 : NT];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    roff[t] = PACKED ? ((size_t)(nt_idx * 4 + wave) * nch * 8 * 512 + (size_t)lane * 8)
-                     : (size_t)min(n0 + t * 16 + col, V - 1) * H + grp * 8;
-    xoff[t] = (size_t)min(m0 + t * 16 + col, rows - 1) * H + grp * 8;
-  }
-  floatx4 acc[4][4];
+  for (int t = 0; t < (PACKED ? 1 : NT); ++t) wrow[t] = (size_t)min(n0 + t * 16 + col, V - 1) * H + grp * 8;
+  uint32_t xoff[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) xoff[t] = (uint32_t)min(m0 + t * 16 + col, rows - 1) * (uint32_t)H + grp * 8;
+  floatx4 acc[4][NT];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // Every wave runs independently (no LDS, no barrier): it streams its 64 W
-  // rows from HBM and reads the small X tile through L2/L1, one 64-wide chunk
-  // ahead of its MFMAs in two register buffers.  Loads are unconditional
-  // (chunk indices clamp at the end) so the pipeline counters stay exact.
-  u32x4 wa[8], wb[8], xa[8], xb[8];
-#define LM_LOAD(wbuf, xbuf, c)                                                                                  \
-  {                                                                                                            \
-    const int k0 = (c) * kKC;                                                                                  \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) {                                                            \
-      wbuf[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(                                   \
-          w + (PACKED ? roff[0] + ((size_t)(c) * 8 + j) * 512 : roff[j & 3] + k0 + (j >> 2) * 32)));             \
-      xbuf[j] = *reinterpret_cast<const u32x4*>(x + xoff[j & 3] + k0 + (j >> 2) * 32);                          \
-    }                                                                                                          \
+  // Every wave streams its 128 W rows over one half of the hidden dimension
+  // (no LDS, no barrier in the loop) and reads the small X tile through
+  // L2/L1, one 64-wide chunk ahead of its MFMAs in two register buffers.
+  // Loads are unconditional (chunk indices clamp at the end) so the pipeline
+  // counters stay exact.
+  u32x4 wa[2 * NT], wb[2 * NT], xa[8], xb[8];
+#define LM_LOAD(wbuf, xbuf, c)                                                                                     \
+  {                                                                                                               \
+    const int k0 = (c) * kKC;                                                                                     \
+    _Pragma("unroll") for (int j = 0; j < 2 * NT; ++j) {                                                          \
+      const int t = (j >> 3) * 4 + (j & 3), ks = (j >> 2) & 1;                                                    \
+      const uint16_t* src = PACKED ? (t < 4 ? wq0 : wq1) + ((size_t)(c) * 8 + ks * 4 + (t & 3)) * 512 + lane * 8  \
+                                   : w + wrow[PACKED ? 0 : t] + k0 + ks * 32;                                     \
+      wbuf[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));                                 \
+    }                                                                                                             \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                                 \
+      xbuf[j] = *reinterpret_cast<const u32x4*>(x + xoff[j & 3] + k0 + (j >> 2) * 32);                            \
   }
-#define LM_COMPUTE(wbuf, xbuf)                                                                   \
-  _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                             \
-    _Pragma("unroll") for (int mt = 0; mt < 4; ++mt) {                                           \
-      B8 a;                                                                                      \
-      a.w = xbuf[ks * 4 + mt];                                                                   \
-      _Pragma("unroll") for (int nt = 0; nt < 4; ++nt) {                                         \
-        B8 bb;                                                                                   \
-        bb.w = wbuf[ks * 4 + nt];                                                                \
-        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bb.v, acc[mt][nt], 0, 0, 0);  \
-      }                                                                                          \
-    }                                                                                            \
+#define LM_COMPUTE(wbuf, xbuf)                                                                    \
+  _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                              \
+    _Pragma("unroll") for (int mt = 0; mt < 4; ++mt) {                                            \
+      B8 a;                                                                                       \
+      a.w = xbuf[ks * 4 + mt];                                                                    \
+      _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                            \
+        B8 bb;                                                                                    \
+        bb.w = wbuf[(t >> 2) * 8 + ks * 4 + (t & 3)];                                             \
+        acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bb.v, acc[mt][t], 0, 0, 0);     \
+      }                                                                                           \
+    }                                                                                             \
   }
-  LM_LOAD(wa, xa, 0)
-  for (int c = 0; c < nch; c += 2) {  // nch is even (hidden % 128 == 0)
+  LM_LOAD(wa, xa, c0)
+  int c = c0;
+  for (; c + 1 < c1; c += 2) {
     LM_LOAD(wb, xb, c + 1)
     LM_COMPUTE(wa, xa)
-    LM_LOAD(wa, xa, min(c + 2, nch - 1))
+    LM_LOAD(wa, xa, min(c + 2, c1 - 1))
     LM_COMPUTE(wb, xb)
   }
+  if (c < c1) LM_COMPUTE(wa, xa)  // odd number of chunks in this half
 #undef LM_COMPUTE
 #undef LM_LOAD
 
-  // Epilogue: logits + per-row record over this wave's 64 columns.
+  // Sum the two hidden halves through LDS: rows 0..31 end in the kh = 0
+  // waves, rows 32..63 in the kh = 1 waves, which then share the epilogue.
+  if (kh == 1) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) xch[wq][mt][t][lane] = acc[mt][t];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[mt][t] += xch[wq][mt][t][lane];
+  }
+  __syncthreads();
+  if (kh == 0) {
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) xch[wq][mt][t][lane] = acc[mt + 2][t];
+  }
+  __syncthreads();
+  if (kh == 1) {  // this wave's rows move to acc[0..1] (constant indices keep acc in registers)
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t) acc[mt][t] = acc[mt + 2][t] + xch[wq][mt][t][lane];
+  }
+
+  // Epilogue: logits + per-row record over this wave's 128 columns, rows
+  // kh*32 + [0, 32).
   bool bad = false;
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+  for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = mt * 16 + grp * 4 + i;
+      const int r = kh * 32 + mt * 16 + grp * 4 + i;
       const int m = m0 + r;
       float zm = kNegInf;
       int ai = kIdxNone;
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int n = n0 + nt * 16 + col;
-        float z = acc[mt][nt][i];
+      for (int t = 0; t < NT; ++t) {
+        const int n = n0 + t * 16 + col;
+        float z = acc[mt][t][i];
         if (n < V) {
           if (m < rows) logits[(size_t)m * V + n] = z;
           if (!isfinite(z)) { bad = true; z = kNegInf; }
           if (beats(z, n, zm, ai)) { zm = z; ai = n; }
         }
-        acc[mt][nt][i] = (n < V) ? z : kNegInf;
+        acc[mt][t][i] = (n < V) ? z : kNegInf;
       }
       // reduce over the 16 lanes sharing this row (xor 1..8 keeps grp)
 #pragma unroll
@@ -156,17 +204,17 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(int rows, int H, int V
         if (beats(z2, a2, zm, ai)) { zm = z2; ai = a2; }
       }
       const float tmax = zm / Tp;  // division is monotone: max z/T' = fl(max z / T')
+      // sum of exp(z/T' - tmax) as exp2(z * (log2e/T') - tmax * log2e): one
+      // FMA and the hardware exp2 per logit (exp2(-inf) = 0)
       float s = 0.f;
       if (zm != kNegInf) {
+        const float c = kLog2e / Tp, off = tmax * kLog2e;
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const float z = acc[mt][nt][i];
-          s += (z == kNegInf) ? 0.f : expf(z / Tp - tmax);
-        }
+        for (int t = 0; t < NT; ++t) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][t][i], c, -off));
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
-      if (col == 0) wrec[wave][r] = Rec{zm == kNegInf ? kNegInf : tmax, s, zm, ai};
+      if (col == 0) wrec[wq][r] = Rec{zm == kNegInf ? kNegInf : tmax, s, zm, ai};
     }
   }
   if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
@@ -179,11 +227,10 @@ __global__ __launch_bounds__(256) void lmhead_bf16_kernel(int rows, int H, int V
     float* pr = part + ((size_t)(m0 + tid) * ntiles + nt_idx) * 4;
     *reinterpret_cast<float4*>(pr) = make_float4(rc.tmax, rc.s, rc.zmax, __int_as_float(rc.arg));
   }
-
 }
 
-// fp32: block = 256 vocab columns of one row.  Reference-precision path for
-// small fp32 shapes.
+// fp32: block = kLmTileN vocab columns of one row, two per thread.
+// Reference-precision path for small fp32 shapes.
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(int rows, int H, int V, float Tp, const float* __restrict__ x,
                                                          const float* __restrict__ w, float* __restrict__ logits,
                                                          float* __restrict__ part, int32_t* status) {
@@ -192,21 +239,30 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(int rows, int H, int V,
   const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int k = tid; k < H; k += 256) xs[k] = x[(size_t)m * H + k];
   __syncthreads();
-  const int n = blockIdx.x * 256 + tid;
-  float z = kNegInf;
-  if (n < V) {
-    const float* wr = w + (size_t)n * H;
-    float a = 0.f;
-    for (int k = 0; k < H; ++k) a = fmaf(xs[k], wr[k], a);
-    logits[(size_t)m * V + n] = a;
-    z = a;
-    if (!isfinite(z)) { set_status(status, EAGLE_STATUS_NONFINITE); z = kNegInf; }
+  float zc[2];
+  float zm = kNegInf;
+  int ai = kIdxNone;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = blockIdx.x * kLmTileN + h * 256 + tid;
+    float z = kNegInf;
+    if (n < V) {
+      const float* wr = w + (size_t)n * H;
+      float a = 0.f;
+      for (int k = 0; k < H; ++k) a = fmaf(xs[k], wr[k], a);
+      logits[(size_t)m * V + n] = a;
+      z = a;
+      if (!isfinite(z)) { set_status(status, EAGLE_STATUS_NONFINITE); z = kNegInf; }
+      if (beats(z, n, zm, ai)) { zm = z; ai = n; }
+    }
+    zc[h] = z;
   }
-  float zm = z;
-  int ai = n < V ? n : kIdxNone;
   wave_argmax(zm, ai);
   const float tmax = zm / Tp;
-  float s = (z == kNegInf || zm == kNegInf) ? 0.f : expf(z / Tp - tmax);
+  float s = 0.f;
+  if (zm != kNegInf)
+#pragma unroll
+    for (int h = 0; h < 2; ++h) s += (zc[h] == kNegInf) ? 0.f : expf(zc[h] / Tp - tmax);
   s = wave_sum(s);
   __shared__ Rec wr4[4];
   if (lane == 0) wr4[wave] = Rec{zm == kNegInf ? kNegInf : tmax, s, zm, ai};
@@ -315,10 +371,10 @@ hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const 
   if (dtype == EAGLE_BF16) {
     dim3 grid(ntiles, lm_mtiles(rows));
     if (w_layout == EAGLE_W_PACKED)
-      lmhead_bf16_kernel<true><<<grid, 256, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
+      lmhead_bf16_kernel<true><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
                                                      ws_part, status);
     else
-      lmhead_bf16_kernel<false><<<grid, 256, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
+      lmhead_bf16_kernel<false><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
                                                       ws_part, status);
   } else {
     dim3 grid(ntiles, rows);

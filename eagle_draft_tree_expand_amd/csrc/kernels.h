@@ -53,8 +53,9 @@ hipError_t launch_attention(int B, int n, int hq, int hkv, int head_dim, int max
                             hipStream_t st);
 
 // ---- LM head (k_lmhead.hip) ----
-constexpr int kLmTileN = 256;            // vocab columns per workgroup
+constexpr int kLmTileN = 512;            // vocab columns per workgroup (one stats record per row)
 constexpr int kLmTileM = 64;             // rows per workgroup
+constexpr int kLmThreads = 512;          // bf16: 4 column quarters x 2 hidden halves
 inline int lm_ntiles(int V) { return (V + kLmTileN - 1) / kLmTileN; }
 inline int lm_mtiles(int rows) { return (rows + kLmTileM - 1) / kLmTileM; }
 inline size_t lm_ws_bytes(int rows, int V) { return (size_t)rows * lm_ntiles(V) * 4 * sizeof(float); }
