@@ -45,6 +45,8 @@ constexpr double kTie = 1e-6;
 constexpr int kSpinMax = 1 << 18;  // polls per wait (a fraction of a second)
 constexpr int kAccGroupCap = 32;   // largest group used (exchange cost grows with the group)
 
+constexpr int kCacheMax = 8192;  // slice tokens whose exponential terms fit the LDS token cache (64 KB)
+
 struct Rows {
   const float* zp;  // target logits row of the node
   const float* zq;  // draft logits row of the node's slot (unused when s == 0)
@@ -52,16 +54,16 @@ struct Rows {
   double invSp, invSq;
 };
 
-// Residual term of one token from fp32 exponentials (the bulk formula).
-EDEV double resid_term(float zp, float zq, const Rows& R, double s) {
-  const double p = isfinite(zp) ? (double)expf(zp / R.Tp - R.Mp) * R.invSp : 0.0;
+// fp32 exponential term of one logit: exp(z/T' - M), 0 for a non-finite z.
+EDEV float eterm(float z, float M, float Tp) { return isfinite(z) ? expf(z / Tp - M) : 0.f; }
+
+// Residual of one token at s from its two terms (s == 0: p alone), in fp64.
+EDEV double resid_e(float ep, float eq, const Rows& R, double s) {
+  const double p = (double)ep * R.invSp;
   if (s == 0.0) return p;
-  const double q = isfinite(zq) ? (double)expf(zq / R.Tp - R.Mq) * R.invSq : 0.0;
-  const double d = p - s * q;
+  const double d = p - s * ((double)eq * R.invSq);
   return d > 0.0 ? d : 0.0;
 }
-
-EDEV double resid_at(const Rows& R, int v, double s) { return resid_term(R.zp[v], s != 0.0 ? R.zq[v] : 0.f, R, s); }
 
 // fp64 probabilities of one token (acceptance ratios and R).
 EDEV double prob64(float z, float M, double invS, float Tp) {
@@ -83,7 +85,11 @@ struct Smem {
   double scan[kWaves];
   double bc_d[4];
   int bc_i[4];
-  int tried_x[EAGLE_MAX_TOPK];
+  // the current node's k children (sampling order): token, fp64 p and q, fp32 terms
+  int cx[EAGLE_MAX_TOPK];
+  double cpx[EAGLE_MAX_TOPK], cqx[EAGLE_MAX_TOPK];
+  float cep[EAGLE_MAX_TOPK], ceq[EAGLE_MAX_TOPK];
+  int tried_x[EAGLE_MAX_TOPK];  // tried token i is child i
   double tried_f[EAGLE_MAX_TOPK];
 };
 
@@ -109,47 +115,88 @@ struct Group {
   Mailbox* mb;
   uint32_t epoch;
   int step;
+  float2* cache;     // LDS terms (ep, eq) of the slice's tokens for the current node, or null
+  int cstate;        // 0 empty, 1 ep filled, 2 ep and eq filled
 };
+
+// The two exponential terms of the 4 tokens base..base+3 of this thread's
+// slice position ci: from the LDS cache when it holds the current node, else
+// from the logits (and kept in the cache).  Tokens past the slice give 0.
+EDEV void slice_terms(const Rows& R, bool need_q, bool from_cache, const Group& gr, int base, int ci, bool vec,
+                      float ep[4], float eq[4]) {
+  if (from_cache) {
+    const float4 c0 = *reinterpret_cast<const float4*>(&gr.cache[ci]);
+    const float4 c1 = *reinterpret_cast<const float4*>(&gr.cache[ci + 2]);
+    ep[0] = c0.x; eq[0] = c0.y; ep[1] = c0.z; eq[1] = c0.w;
+    ep[2] = c1.x; eq[2] = c1.y; ep[3] = c1.z; eq[3] = c1.w;
+    return;
+  }
+  float zp[4], zq[4];
+  if (vec && base + 3 < gr.hi) {
+    const float4 p4 = *reinterpret_cast<const float4*>(R.zp + base);
+    zp[0] = p4.x; zp[1] = p4.y; zp[2] = p4.z; zp[3] = p4.w;
+    if (need_q) {
+      const float4 q4 = *reinterpret_cast<const float4*>(R.zq + base);
+      zq[0] = q4.x; zq[1] = q4.y; zq[2] = q4.z; zq[3] = q4.w;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      zp[e] = base + e < gr.hi ? R.zp[base + e] : kNegInf;
+      if (need_q) zq[e] = base + e < gr.hi ? R.zq[base + e] : kNegInf;
+    }
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    ep[e] = base + e < gr.hi ? eterm(zp[e], R.Mp, R.Tp) : 0.f;
+    eq[e] = (need_q && base + e < gr.hi) ? eterm(zq[e], R.Mq, R.Tp) : 0.f;
+  }
+  if (gr.cache) {
+    *reinterpret_cast<float4*>(&gr.cache[ci]) = make_float4(ep[0], eq[0], ep[1], eq[1]);
+    *reinterpret_cast<float4*>(&gr.cache[ci + 2]) = make_float4(ep[2], eq[2], ep[3], eq[3]);
+  }
+}
+
+EDEV bool cache_ready(const Group& gr, bool need_q) {
+  return gr.cache && (gr.cstate == 2 || (gr.cstate == 1 && !need_q));
+}
 
 // All threads of every workgroup of the group: Z = G(s) over the vocabulary
 // (tried tokens not corrected); per-workgroup partials left in sm.vals.
 EDEV double group_reduce(const Rows& R, double s, Group& gr, Smem& sm, int* timed_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const bool need_q = s != 0.0;
+  const bool from_cache = cache_ready(gr, need_q);
+  const bool vec = ((((uintptr_t)R.zp) | (need_q ? (uintptr_t)R.zq : 0)) & 15) == 0;
   double a = 0.0;
-  const bool vec = ((((uintptr_t)R.zp) | (s != 0.0 ? (uintptr_t)R.zq : 0)) & 15) == 0;
-  for (int base = gr.lo + tid * 4; base < gr.hi; base += kThreads * 4) {
-    if (vec && base + 3 < gr.hi) {
-      const float4 p4 = *reinterpret_cast<const float4*>(R.zp + base);
-      float4 q4 = make_float4(0.f, 0.f, 0.f, 0.f);
-      if (s != 0.0) q4 = *reinterpret_cast<const float4*>(R.zq + base);
-      a += resid_term(p4.x, q4.x, R, s) + resid_term(p4.y, q4.y, R, s) + resid_term(p4.z, q4.z, R, s) +
-           resid_term(p4.w, q4.w, R, s);
-    } else {
-      for (int e = 0; e < 4; ++e)
-        if (base + e < gr.hi) a += resid_at(R, base + e, s);
-    }
+  for (int base = gr.lo + tid * 4, ci = tid * 4; base < gr.hi; base += kThreads * 4, ci += kThreads * 4) {
+    float ep[4], eq[4];
+    slice_terms(R, need_q, from_cache, gr, base, ci, vec, ep, eq);
+    a += (resid_e(ep[0], eq[0], R, s) + resid_e(ep[1], eq[1], R, s)) +
+         (resid_e(ep[2], eq[2], R, s) + resid_e(ep[3], eq[3], R, s));
   }
+  if (gr.cache && !from_cache) gr.cstate = need_q ? 2 : 1;
   a = wave_sum_d(a);
   if (lane == 0) sm.red[wave] = a;
   __syncthreads();
-  const uint64_t tag = tag_of(gr.epoch, gr.step);
-  uint64_t* bank = gr.mb->bank[gr.step & 1];
-  if (tid == 0) {
-    const double part = (sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3]);
-    publish(bank + gr.g, tag | encode_val(part));
+  // Wave 0 publishes this workgroup's partial, collects all G of them and
+  // sums them with a butterfly: identical inputs and order in every
+  // workgroup, so every workgroup gets the same total bit for bit.
+  if (wave == 0) {
+    const uint64_t tag = tag_of(gr.epoch, gr.step);
+    uint64_t* bank = gr.mb->bank[gr.step & 1];
+    if (lane == 0) publish(bank + gr.g, tag | encode_val((sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3])));
+    double v = 0.0;
+    if (lane < gr.G) {
+      v = decode_val(await_tag(bank + lane, tag, timed_out));
+      sm.vals[lane] = v;
+    }
+    v = wave_sum_d(v);
+    if (lane == 0) sm.bc_d[0] = v;
   }
-  if (wave == 0 && lane < gr.G) sm.vals[lane] = decode_val(await_tag(bank + lane, tag, timed_out));
-  __syncthreads();
-  if (tid == 0) {
-    double t = 0.0;
-    for (int j = 0; j < gr.G; ++j) t += sm.vals[j];
-    sm.bc_d[0] = t;
-  }
-  __syncthreads();
-  const double tot = sm.bc_d[0];
   __syncthreads();
   ++gr.step;
-  return tot;
+  return sm.bc_d[0];
 }
 
 // Inverse-CDF draw from the residual at s (partials from the group_reduce at
@@ -164,7 +211,7 @@ EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr,
     for (int i = 0; i < ntried; ++i) {
       const int x = sm.tried_x[i];
       const int owner = min(x / gr.span, gr.G - 1);
-      sm.vals[owner] += sm.tried_f[i] - resid_at(R, x, s);
+      sm.vals[owner] += sm.tried_f[i] - resid_e(sm.cep[i], sm.ceq[i], R, s);
     }
     double tot = 0.0;
     for (int j = 0; j < gr.G; ++j) tot += sm.vals[j] > 0.0 ? sm.vals[j] : 0.0;
@@ -193,15 +240,21 @@ EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr,
   int token = -1;
   if (gr.g == gstar) {
     // scan the own slice in id order, 1024 tokens (4 per thread) per pass
+    const bool need_q = s != 0.0;
+    const bool from_cache = cache_ready(gr, need_q);
+    const bool vec = ((((uintptr_t)R.zp) | (need_q ? (uintptr_t)R.zq : 0)) & 15) == 0;
     double off = off0;
     int found = -1, tie = 0, last_pos = -1;
-    for (int base = gr.lo; base < gr.hi && found < 0; base += kThreads * 4) {
+    for (int base0 = gr.lo, ci0 = 0; base0 < gr.hi && found < 0; base0 += kThreads * 4, ci0 += kThreads * 4) {
+      const int base = base0 + tid * 4, ci = ci0 + tid * 4;
       double val[4], mine = 0.0;
+      float ep[4] = {0.f, 0.f, 0.f, 0.f}, eq[4] = {0.f, 0.f, 0.f, 0.f};
+      if (base < gr.hi) slice_terms(R, need_q, from_cache, gr, base, ci, vec, ep, eq);
       for (int e = 0; e < 4; ++e) {
-        const int v = base + tid * 4 + e;
+        const int v = base + e;
         double x = 0.0;
         if (v < gr.hi) {
-          x = resid_at(R, v, s);
+          x = resid_e(ep[e], eq[e], R, s);
           for (int i = 0; i < ntried; ++i)
             if (sm.tried_x[i] == v) x = sm.tried_f[i];
         }
@@ -241,13 +294,13 @@ EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr,
         if (pick < 0)
           for (int e = 3; e >= 0; --e)
             if (val[e] > 0.0) { pick = e; break; }
-        atomicMax(&sm.bc_i[1], base + tid * 4 + pick);
+        atomicMax(&sm.bc_i[1], base + pick);
         if (t2) atomicOr(&sm.bc_i[2], 1);
       }
       // remember the last positive token of the slice (rounding fallback)
       int lp = -1;
       for (int e = 3; e >= 0; --e)
-        if (val[e] > 0.0) { lp = base + tid * 4 + e; break; }
+        if (val[e] > 0.0) { lp = base + e; break; }
       if (lp >= 0) atomicMax(&sm.bc_i[3], lp);
       __syncthreads();
       found = sm.bc_i[1];
@@ -276,12 +329,13 @@ EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr,
 }
 
 __global__ __launch_bounds__(kThreads) void accept_kernel(
-    int b0, int G, int N, int V, int D, int k, float T, const int32_t* __restrict__ node_tok,
+    int b0, int G, int N, int V, int D, int k, float T, int cache_tokens, const int32_t* __restrict__ node_tok,
     const int32_t* __restrict__ node_parent, const int32_t* __restrict__ node_slot, const int32_t* __restrict__ pool_tok,
     const int32_t* __restrict__ pool_flat, const float* __restrict__ tlog, const float* __restrict__ tstats,
     const int32_t* __restrict__ targmax, const float* __restrict__ dlog, const float* __restrict__ sstats,
     const float* __restrict__ uniforms, Mailbox* __restrict__ mail, int32_t* accept_len, int32_t* accept_path,
     int32_t* committed, int32_t* n_committed, int32_t* near_tie, int32_t* status) {
+  extern __shared__ __attribute__((aligned(16))) float2 tcache[];  // [cache_tokens] when the slice fits
   __shared__ Smem sm;
   __shared__ int ties, timed_out;
   __shared__ int path[EAGLE_MAX_DEPTH + 1];
@@ -328,6 +382,8 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     gr.mb = mail + b;
     gr.epoch = __hip_atomic_load(&gr.mb->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     gr.step = 0;
+    gr.cache = cache_tokens >= span ? tcache : nullptr;
+    gr.cstate = 0;
     if (tid == 0) {  // retire this workgroup's stale words from earlier calls
       const uint64_t reset = tag_of(gr.epoch, 1023);
       publish(&gr.mb->bank[0][g], reset);
@@ -337,6 +393,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       if (tid == 0) cur_slot = nslot[cur_u];
       __syncthreads();
       const int u = cur_u, slot = cur_slot;
+      gr.cstate = 0;  // a new node: the token cache is refilled by its first pass
       Rows R;
       R.zp = tlog + ((size_t)b * N + u) * V;
       R.Tp = Tp;
@@ -355,18 +412,30 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       R.zq = dlog + ((size_t)b * S + slot) * V;
       R.Mq = sstats[((size_t)b * S + slot) * 2];
       R.invSq = 1.0 / (double)sstats[((size_t)b * S + slot) * 2 + 1];
+      // The node's k children, loaded once (one thread each).  An id out of
+      // range is flagged and scored as token 0.
+      if (tid < k) {
+        const int x = ptok[(size_t)slot * k + tid];
+        const bool ok = x >= 0 && x < V;
+        const int xc = ok ? x : 0;
+        const float zpx = R.zp[xc], zqx = R.zq[xc];
+        sm.cx[tid] = ok ? x : -1;
+        sm.tried_x[tid] = xc;
+        sm.cpx[tid] = prob64(zpx, R.Mp, R.invSp, Tp);
+        sm.cqx[tid] = prob64(zqx, R.Mq, R.invSq, Tp);
+        sm.cep[tid] = eterm(zpx, R.Mp, Tp);
+        sm.ceq[tid] = eterm(zqx, R.Mq, Tp);
+      }
       if (tid == 0) { st_s = 0.0; st_Z = 1.0; st_R = 1.0; acc_j = -1; stale = 0; }
       __syncthreads();
       int ntried = 0;
       double s_fin = 0.0;
       for (int j = 0; j < k; ++j) {
         if (tid == 0) {
-          const int x = ptok[(size_t)slot * k + j];
-          if (x < 0 || x >= V) {
+          if (sm.cx[j] < 0) {
             set_status(status, EAGLE_STATUS_TOKEN_RANGE);
           } else {
-            const double px = prob64(R.zp[x], R.Mp, R.invSp, Tp);
-            const double qx = prob64(R.zq[x], R.Mq, R.invSq, Tp);
+            const double px = sm.cpx[j], qx = sm.cqx[j];
             const double num = st_s == 0.0 ? px : fmax(0.0, px - st_s * qx);
             double ratio;
             if (qx > 0.0 && st_R > 0.0) ratio = num * st_R / (st_Z * qx);
@@ -376,35 +445,26 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
             if (fabs(uu - a) < kTie) ++ties;
             if (uu < a) acc_j = j;
           }
+          if (acc_j < 0) {  // rejected: s_{j+1} and R_{j+1}
+            sm.bc_d[3] = st_s + st_Z / st_R;
+            st_R = st_R - sm.cqx[j];
+          }
         }
         __syncthreads();
         if (acc_j >= 0) break;
-        // rejected: s_{j+1}, R_{j+1}, frozen f_j, then Z_{j+1} by one reduction
-        if (tid == 0) {
-          const int x = ptok[(size_t)slot * k + j];
-          const int xc = (x < 0 || x >= V) ? 0 : x;
-          const double qx = prob64(R.zq[xc], R.Mq, R.invSq, Tp);
-          sm.bc_d[3] = st_s + st_Z / st_R;
-          sm.tried_x[ntried] = xc;
-          st_R = st_R - qx;
-        }
-        __syncthreads();
+        // Z_{j+1} by one reduction, corrected for the tried tokens; f_j frozen
         const double snew = sm.bc_d[3];
         const double Gs = group_reduce(R, snew, gr, sm, &timed_out);
         if (tid == 0) {
           double Z = Gs;
-          for (int i = 0; i < ntried; ++i) {
-            const int xi = sm.tried_x[i];
-            Z += sm.tried_f[i] - resid_at(R, xi, snew);
-          }
-          const int xj = sm.tried_x[ntried];
+          for (int i = 0; i < ntried; ++i) Z += sm.tried_f[i] - resid_e(sm.cep[i], sm.ceq[i], R, snew);
           if (Z > 0.0) {
-            sm.tried_f[ntried] = resid_at(R, xj, snew);
+            sm.tried_f[ntried] = resid_e(sm.cep[ntried], sm.ceq[ntried], R, snew);
             st_s = snew;
             st_Z = Z;
             stale = 0;
           } else {  // zero residual mass: keep P
-            sm.tried_f[ntried] = resid_at(R, xj, st_s);
+            sm.tried_f[ntried] = resid_e(sm.cep[ntried], sm.ceq[ntried], R, st_s);
             zero_resid = 1;
             stale = 1;
           }
@@ -473,7 +533,7 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
   if (dev < 0 || dev >= 64) dev = 0;
   if (capacity[dev] == 0) {
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_kernel, kThreads, 0);
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_kernel, kThreads, kCacheMax * sizeof(float2));
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -484,14 +544,18 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
   if (!greedy)
     while (G * 2 <= kAccGroupCap && (size_t)B * G * 2 <= (size_t)cap && G * 2 * 1024 <= V) G *= 2;
   const int per_launch = cap / G > 0 ? cap / G : 1;
+  // token cache: the slice's exponential terms stay in LDS across the passes at a node
+  const int span = ((V + G - 1) / G + 3) / 4 * 4;
+  int cache_tokens = (!greedy && span <= kCacheMax) ? span : 0;
+  const size_t lds = (size_t)cache_tokens * sizeof(float2);
   Mailbox* mb = static_cast<Mailbox*>(mail);
   for (int b0 = 0; b0 < B; b0 += per_launch) {
     const int nb = B - b0 < per_launch ? B - b0 : per_launch;
-    void* args[] = {&b0, &G, &N, &V, &D, &k, &T, &node_tok, &node_parent, &node_slot, &pool_tok, &pool_flat, &tlog,
+    void* args[] = {&b0, &G, &N, &V, &D, &k, &T, &cache_tokens, &node_tok, &node_parent, &node_slot, &pool_tok, &pool_flat, &tlog,
                     &tstats, &targmax, &dlog, &sstats, &uniforms, &mb, &accept_len, &accept_path, &committed,
                     &n_committed, &near_tie, &status};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(accept_kernel), dim3(nb * G), dim3(kThreads), args,
-                                   0, st);
+                                   lds, st);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
