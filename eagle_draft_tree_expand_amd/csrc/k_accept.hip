@@ -20,8 +20,14 @@
 // G(s) = sum_y max(0, p(y) - s q(y)); the acceptance ratio of trial j is
 // max(0, p(x_j) - s_j q(x_j)) R_j / (Z_j q(x_j)) with p(x_j), q(x_j) in fp64.
 //
-// Parallel layout: a group of G workgroups per request, launched
-// cooperatively (all resident).  Every workgroup runs the same walk (same
+// Parallel layout: a group of G workgroups per request, in one grid no
+// larger than the device's resident capacity for this kernel (occupancy times
+// compute units), so that in-stream order (the previous kernel has finished)
+// leaves every workgroup resident at once.  A plain launch is used: a
+// cooperative launch costs ~16 us more per call on this GPU.  If other work
+// shares the GPU and keeps part of the grid from starting, the bounded waits
+// time out and set EAGLE_STATUS_SYNC_TIMEOUT instead of hanging.  Every
+// workgroup runs the same walk (same
 // inputs, same code: identical decisions) and owns a contiguous vocabulary
 // slice; a reduction is one pass over the slice plus an exchange of the G
 // partial sums through per-request mailbox words.  A word carries its own
@@ -551,11 +557,10 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
   Mailbox* mb = static_cast<Mailbox*>(mail);
   for (int b0 = 0; b0 < B; b0 += per_launch) {
     const int nb = B - b0 < per_launch ? B - b0 : per_launch;
-    void* args[] = {&b0, &G, &N, &V, &D, &k, &T, &cache_tokens, &node_tok, &node_parent, &node_slot, &pool_tok, &pool_flat, &tlog,
-                    &tstats, &targmax, &dlog, &sstats, &uniforms, &mb, &accept_len, &accept_path, &committed,
-                    &n_committed, &near_tie, &status};
-    e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(accept_kernel), dim3(nb * G), dim3(kThreads), args,
-                                   lds, st);
+    accept_kernel<<<dim3(nb * G), dim3(kThreads), lds, st>>>(b0, G, N, V, D, k, T, cache_tokens, node_tok, node_parent,
+        node_slot, pool_tok, pool_flat, tlog, tstats, targmax, dlog, sstats, uniforms, mb, accept_len, accept_path,
+        committed, n_committed, near_tie, status);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
