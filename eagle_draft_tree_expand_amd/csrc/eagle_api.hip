@@ -217,8 +217,33 @@ int eagle_gather_rows(int32_t n_rows, int32_t row_elems, int32_t dtype, const vo
   if (n_rows == 0) return EAGLE_OK;
   if (!table || !idx || !out) return EAGLE_ERR_NULL;
   const int esz = dtype == EAGLE_F32 ? 4 : 2;
-  return launch_status(launch_gather(n_rows, row_elems * esz, table, table_rows, idx, out, dev_status,
-                                     (hipStream_t)stream));
+  GatherSet gs{};
+  gs.n = 1;
+  gs.table[0] = table;
+  gs.out[0] = out;
+  gs.row_units[0] = row_elems * esz;
+  return launch_status(launch_gather(n_rows, gs, table_rows, idx, dev_status, (hipStream_t)stream));
+}
+
+int eagle_gather_rows_multi(int32_t n_tables, int32_t n_rows, int32_t dtype, int32_t table_rows, const int32_t* idx,
+                            const int32_t* row_elems, const void* const* tables, void* const* outs,
+                            int32_t* dev_status, void* stream) {
+  if (n_tables < 1 || n_tables > kGatherMaxTables || n_rows < 0 || table_rows < 1) return EAGLE_ERR_SHAPE;
+  if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
+  if (!row_elems || !tables || !outs) return EAGLE_ERR_NULL;
+  const int esz = dtype == EAGLE_F32 ? 4 : 2;
+  GatherSet gs{};
+  gs.n = n_tables;
+  for (int t = 0; t < n_tables; ++t) {
+    if (row_elems[t] < 1) return EAGLE_ERR_SHAPE;
+    if (n_rows > 0 && (!tables[t] || !outs[t])) return EAGLE_ERR_NULL;
+    gs.table[t] = tables[t];
+    gs.out[t] = outs[t];
+    gs.row_units[t] = row_elems[t] * esz;
+  }
+  if (n_rows == 0) return EAGLE_OK;
+  if (!idx) return EAGLE_ERR_NULL;
+  return launch_status(launch_gather(n_rows, gs, table_rows, idx, dev_status, (hipStream_t)stream));
 }
 
 }  // extern "C"

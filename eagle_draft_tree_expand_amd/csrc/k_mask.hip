@@ -42,10 +42,15 @@ __global__ __launch_bounds__(256) void tree_mask_kernel(int n, int W, const int3
   }
 }
 
+// grid (x, n_tables): out_t[r, :] = table_t[idx[r], :] for every table t of
+// the set (one launch for several tables sharing the ids).
 template <typename V>
-__global__ __launch_bounds__(256) void gather_kernel(int n_rows, int row_vecs, const V* __restrict__ table,
-                                                     int table_rows, const int32_t* __restrict__ idx,
-                                                     V* __restrict__ out, int32_t* status) {
+__global__ __launch_bounds__(256) void gather_kernel(int n_rows, GatherSet gs, int table_rows,
+                                                     const int32_t* __restrict__ idx, int32_t* status) {
+  const int ti = blockIdx.y;
+  const int row_vecs = gs.row_units[ti];
+  const V* __restrict__ table = static_cast<const V*>(gs.table[ti]);
+  V* __restrict__ out = static_cast<V*>(gs.out[ti]);
   const size_t total = (size_t)n_rows * row_vecs;
   for (size_t x = (size_t)blockIdx.x * blockDim.x + threadIdx.x; x < total; x += (size_t)gridDim.x * blockDim.x) {
     const int r = (int)(x / row_vecs);
@@ -56,7 +61,7 @@ __global__ __launch_bounds__(256) void gather_kernel(int n_rows, int row_vecs, c
       v = table[(size_t)t * row_vecs + c];
     } else {
       memset(&v, 0, sizeof(V));
-      if (c == 0) set_status(status, EAGLE_STATUS_TOKEN_RANGE);
+      if (c == 0 && ti == 0) set_status(status, EAGLE_STATUS_TOKEN_RANGE);
     }
     out[x] = v;
   }
@@ -75,30 +80,25 @@ hipError_t launch_tree_mask(int B, int n, const int32_t* parent, const int32_t* 
   return hipGetLastError();
 }
 
-hipError_t launch_gather(int n_rows, int row_bytes, const void* table, int table_rows, const int32_t* idx, void* out,
-                         int32_t* status, hipStream_t st) {
-  const size_t total_bytes = (size_t)n_rows * row_bytes;
-  if (total_bytes == 0) return hipSuccess;
-  const bool al16 = (((uintptr_t)table | (uintptr_t)out) & 15u) == 0;
-  const bool al4 = (((uintptr_t)table | (uintptr_t)out) & 3u) == 0;
-  if (row_bytes % 16 == 0 && al16) {
-    const int vecs = row_bytes / 16;
-    const size_t total = (size_t)n_rows * vecs;
-    const int grid = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-    gather_kernel<uint4><<<grid, 256, 0, st>>>(n_rows, vecs, (const uint4*)table, table_rows, idx, (uint4*)out, status);
-  } else if (row_bytes % 4 == 0 && al4) {
-    const int vecs = row_bytes / 4;
-    const size_t total = (size_t)n_rows * vecs;
-    const int grid = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-    gather_kernel<uint32_t><<<grid, 256, 0, st>>>(n_rows, vecs, (const uint32_t*)table, table_rows, idx, (uint32_t*)out,
-                                                  status);
-  } else {
-    const int vecs = row_bytes / 2;
-    const size_t total = (size_t)n_rows * vecs;
-    const int grid = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
-    gather_kernel<uint16_t><<<grid, 256, 0, st>>>(n_rows, vecs, (const uint16_t*)table, table_rows, idx, (uint16_t*)out,
-                                                  status);
+hipError_t launch_gather(int n_rows, GatherSet gs, int table_rows, const int32_t* idx, int32_t* status,
+                         hipStream_t st) {
+  // gs.row_units holds row bytes on entry; the widest access every table allows is used for all
+  if (n_rows == 0 || gs.n == 0) return hipSuccess;
+  uintptr_t addr = 0;
+  int common = 0, maxb = 0;
+  for (int t = 0; t < gs.n; ++t) {
+    addr |= (uintptr_t)gs.table[t] | (uintptr_t)gs.out[t];
+    common |= gs.row_units[t];
+    maxb = gs.row_units[t] > maxb ? gs.row_units[t] : maxb;
   }
+  const int w = ((common % 16) == 0 && (addr & 15u) == 0) ? 16 : ((common % 4) == 0 && (addr & 3u) == 0) ? 4 : 2;
+  for (int t = 0; t < gs.n; ++t) gs.row_units[t] /= w;
+  const size_t total = (size_t)n_rows * (maxb / w);
+  const int gx = (int)((total + 255) / 256 < 4096 ? (total + 255) / 256 : 4096);
+  const dim3 grid(gx, gs.n);
+  if (w == 16) gather_kernel<uint4><<<grid, 256, 0, st>>>(n_rows, gs, table_rows, idx, status);
+  else if (w == 4) gather_kernel<uint32_t><<<grid, 256, 0, st>>>(n_rows, gs, table_rows, idx, status);
+  else gather_kernel<uint16_t><<<grid, 256, 0, st>>>(n_rows, gs, table_rows, idx, status);
   return hipGetLastError();
 }
 

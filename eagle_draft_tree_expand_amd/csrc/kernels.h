@@ -31,8 +31,15 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
 hipError_t launch_tree_mask(int B, int n, const int32_t* parent, const int32_t* depth,
                             const int32_t* prefix_len, uint64_t* mask, int32_t* pos,
                             int32_t* status, hipStream_t st);
-hipError_t launch_gather(int n_rows, int row_bytes, const void* table, int table_rows,
-                         const int32_t* idx, void* out, int32_t* status, hipStream_t st);
+constexpr int kGatherMaxTables = 4;
+struct GatherSet {
+  const void* table[kGatherMaxTables];
+  void* out[kGatherMaxTables];
+  int row_units[kGatherMaxTables];
+  int n;
+};
+hipError_t launch_gather(int n_rows, GatherSet gs, int table_rows, const int32_t* idx, int32_t* status,
+                         hipStream_t st);
 hipError_t launch_zero_ints(int32_t* p, size_t n, hipStream_t st);
 
 // ---- attention (k_attn.hip) ----

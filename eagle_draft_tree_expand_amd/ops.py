@@ -103,3 +103,16 @@ def gather_rows(n_rows, row_elems, table, idx, out, status=None):
     rc = _lib.load().eagle_gather_rows(n_rows, row_elems, dt, _ptr(table), table.shape[0], _ptr(idx), _ptr(out),
                                       _ptr(status), _stream())
     check("eagle_gather_rows", rc)
+
+
+def gather_rows_multi(n_rows, idx, pairs, status=None):
+    """One launch: out[r, :] = table[idx[r], :] for every (table, out) in `pairs` (at most 4)."""
+    import ctypes
+    n = len(pairs)
+    dt = _DT[pairs[0][0].dtype]
+    elems = (ctypes.c_int32 * n)(*[int(t.numel() // t.shape[0]) for t, _ in pairs])
+    tabs = (ctypes.c_void_p * n)(*[_ptr(t) for t, _ in pairs])
+    outs = (ctypes.c_void_p * n)(*[_ptr(o) for _, o in pairs])
+    rc = _lib.load().eagle_gather_rows_multi(n, n_rows, dt, pairs[0][0].shape[0], _ptr(idx), ctypes.addressof(elems),
+                                            ctypes.addressof(tabs), ctypes.addressof(outs), _ptr(status), _stream())
+    check("eagle_gather_rows_multi", rc)

@@ -119,9 +119,7 @@ class DeviceRound:
         c = self.cfg
         tok = (node_tok if node_tok is not None else self.tree["node_tok"]).reshape(-1)
         n = tok.numel()
-        ops.gather_rows(n, c.hq * c.dh, wts.q_tab, tok, self.q, self.status)
-        ops.gather_rows(n, c.hkv * c.dh, wts.k_tab, tok, self.kt, self.status)
-        ops.gather_rows(n, c.hkv * c.dh, wts.v_tab, tok, self.vt, self.status)
+        ops.gather_rows_multi(n, tok, [(wts.q_tab, self.q), (wts.k_tab, self.kt), (wts.v_tab, self.vt)], self.status)
 
     def attention(self, data):
         c = self.cfg

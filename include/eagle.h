@@ -257,6 +257,19 @@ int eagle_gather_rows(int32_t n_rows, int32_t row_elems, int32_t dtype, const vo
                       int32_t table_rows, const int32_t* idx, void* out, int32_t* dev_status,
                       void* stream);
 
+/* Several row gathers with one id list in one launch: for t < n_tables (at
+ * most 4), outs[t][r, :] = tables[t][idx[r], :] for r < n_rows, with
+ * row_elems[t] elements of `dtype` per row.  row_elems, tables and outs are
+ * HOST arrays of n_tables entries (tables/outs holding device pointers); all
+ * tables have table_rows rows.  The verify layer's tree queries, keys and
+ * values (per-token rows, the synthetic stand-in for the target layer's
+ * projections) are gathered this way in one launch.  Ids outside
+ * [0, table_rows) give zero rows and set TOKEN_RANGE.  Errors as
+ * eagle_gather_rows; n_tables outside [1, 4] is a SHAPE error. */
+int eagle_gather_rows_multi(int32_t n_tables, int32_t n_rows, int32_t dtype, int32_t table_rows,
+                            const int32_t* idx, const int32_t* row_elems, const void* const* tables,
+                            void* const* outs, int32_t* dev_status, void* stream);
+
 /* Human-readable name of a return code. */
 const char* eagle_error_string(int32_t code);
 

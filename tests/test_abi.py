@@ -140,6 +140,25 @@ def test_mask_gather_accept_reject(lib):
     assert lib.eagle_verify_accept(ctypes.byref(p), *args, FAKE, 1 << 20, None, None) == -1
 
 
+def test_gather_multi_rejects(lib):
+    elems = (ctypes.c_int32 * 3)(8, 4, 4)
+    tabs = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    outs = (ctypes.c_void_p * 3)(FAKE, FAKE, FAKE)
+    a = [ctypes.addressof(elems), ctypes.addressof(tabs), ctypes.addressof(outs)]
+    assert lib.eagle_gather_rows_multi(0, 4, 1, 10, FAKE, *a, None, None) == -2   # no table
+    assert lib.eagle_gather_rows_multi(5, 4, 1, 10, FAKE, *a, None, None) == -2   # more than 4
+    assert lib.eagle_gather_rows_multi(3, 4, 7, 10, FAKE, *a, None, None) == -3   # dtype
+    assert lib.eagle_gather_rows_multi(3, 4, 1, 0, FAKE, *a, None, None) == -2    # empty table
+    assert lib.eagle_gather_rows_multi(3, 4, 1, 10, None, *a, None, None) == -1   # no ids
+    assert lib.eagle_gather_rows_multi(3, 4, 1, 10, FAKE, None, a[1], a[2], None, None) == -1
+    outs[1] = None
+    assert lib.eagle_gather_rows_multi(3, 4, 1, 10, FAKE, *a, None, None) == -1
+    outs[1] = FAKE
+    elems[2] = 0
+    assert lib.eagle_gather_rows_multi(3, 4, 1, 10, FAKE, *a, None, None) == -2
+    assert lib.eagle_gather_rows_multi(1, 0, 1, 10, None, *a, None, None) == 0    # nothing to do
+
+
 def test_workspace_init_rejects(lib):
     assert lib.eagle_workspace_init(None, 1 << 20, None) == -1
     assert lib.eagle_workspace_init(FAKE, 100, None) == -4

@@ -321,3 +321,27 @@ def test_device_prepass_rows_match_oracle(rt):
     rt.device_draft_rows(cfg, wts, data, 1.0)
     got = data.rows.cpu().numpy()
     assert np.abs(got - ora_rows).max() <= 1e-4 * (1 + np.abs(ora_rows).max())
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("dtype,widths", [("bf16", (512, 128, 128)), ("f32", (12, 8, 8)), ("bf16", (3, 5, 7))])
+def test_gather_rows_multi_exact(rt, dtype, widths):
+    """One launch gathers several tables with one id list, bit-exact; bad ids give zero rows + TOKEN_RANGE."""
+    import torch
+    from eagle_draft_tree_expand_amd import ops
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    g = torch.Generator().manual_seed(7)
+    rows, n = 97, 300
+    tabs = [torch.randn(rows, w, generator=g).to(tdt).cuda() for w in widths]
+    idx = torch.randint(0, rows, (n,), generator=g, dtype=torch.int32)
+    idx[5] = rows        # out of range
+    idx[17] = -1
+    outs = [torch.full((n, w), 3.0, dtype=tdt, device="cuda") for w in widths]
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ops.gather_rows_multi(n, idx.cuda(), list(zip(tabs, outs)), status)
+    ok = (idx >= 0) & (idx < rows)
+    for t, o in zip(tabs, outs):
+        ref = torch.zeros_like(o).cpu()
+        ref[ok] = t.cpu()[idx[ok].long()]
+        assert torch.equal(o.cpu(), ref)
+    assert int(status.item()) & 0x1
