@@ -296,23 +296,52 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(
 }
 
 // grid (n, hq, B), block DH threads: combine the splits of one (node, head).
+// The split maxima and sums are read once in parallel (one thread per
+// split); each output element then sums its splits with the resulting
+// weights, eight loads in flight at a time.
 template <bool BF16>
 __global__ __launch_bounds__(128) void attn_merge_kernel(int n, int hq, int hkv, int DH, const float* __restrict__ ws,
                                                          int rows_pad, int nsplit, void* __restrict__ out) {
+  extern __shared__ float wgt[];  // [nsplit + 1] weights exp(m_s - M)
+  __shared__ float red[2][2];
   const int i = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = (blockDim.x + 63) >> 6;
   const int G = hq / hkv, g = h / G, r = i * G + (h - g * G);
-  float M = kNegInf;
-  for (int s = 0; s <= nsplit; ++s) M = fmaxf(M, partial_row(const_cast<float*>(ws), b, g, hkv, nsplit + 1, s, rows_pad, r, DH)[DH]);
-  for (int d = threadIdx.x; d < DH; d += blockDim.x) {
-    float acc = 0.f, L = 0.f;
-    for (int s = 0; s <= nsplit; ++s) {
-      const float* pr = partial_row(const_cast<float*>(ws), b, g, hkv, nsplit + 1, s, rows_pad, r, DH);
-      const float ms = pr[DH];
-      if (ms == kNegInf) continue;
-      const float w = expf(ms - M);
-      L += pr[DH + 1] * w;
-      acc += pr[d] * w;
+  const int nsp1 = nsplit + 1;
+  const float* p0 = partial_row(const_cast<float*>(ws), b, g, hkv, nsp1, 0, rows_pad, r, DH);
+  const size_t sstride = (size_t)rows_pad * (DH + 2);  // floats between splits of one row
+  float mloc = kNegInf;
+  for (int s = tid; s < nsp1; s += blockDim.x) {
+    const float ms = p0[s * sstride + DH];
+    wgt[s] = ms;
+    mloc = fmaxf(mloc, ms);
+  }
+  mloc = wave_max(mloc);
+  if (lane == 0) red[0][wave] = mloc;
+  __syncthreads();
+  const float M = nw > 1 ? fmaxf(red[0][0], red[0][1]) : red[0][0];
+  float lloc = 0.f;
+  for (int s = tid; s < nsp1; s += blockDim.x) {
+    const float ms = wgt[s];
+    const float w = ms == kNegInf ? 0.f : expf(ms - M);
+    wgt[s] = w;
+    lloc += p0[s * sstride + DH + 1] * w;
+  }
+  lloc = wave_sum(lloc);
+  if (lane == 0) red[1][wave] = lloc;
+  __syncthreads();
+  const float L = nw > 1 ? red[1][0] + red[1][1] : red[1][0];
+  for (int d = tid; d < DH; d += blockDim.x) {
+    float acc = 0.f;
+    int s = 0;
+    for (; s + 8 <= nsp1; s += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = p0[(s + j) * sstride + d];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) acc += v[j] * wgt[s + j];
     }
+    for (; s < nsp1; ++s) acc += p0[s * sstride + d] * wgt[s];
     const float v = L > 0.f ? acc / L : 0.f;
     const size_t o = (((size_t)b * n + i) * hq + h) * DH + d;
     if (BF16) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16(v);
@@ -372,9 +401,10 @@ hipError_t launch_attention(int B, int n, int hq, int hkv, int DH, int Lmax, int
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   dim3 mg(n, hq, B);
-  const int mt = DH < 128 ? DH : 128;
-  if (dtype == EAGLE_BF16) attn_merge_kernel<true><<<mg, mt, 0, st>>>(n, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
-  else attn_merge_kernel<false><<<mg, mt, 0, st>>>(n, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
+  const int mt = DH <= 64 ? 64 : 128;  // whole waves (the merge reduces across lanes)
+  const size_t lds = (size_t)(pl.nsplit + 1) * sizeof(float);
+  if (dtype == EAGLE_BF16) attn_merge_kernel<true><<<mg, mt, lds, st>>>(n, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
+  else attn_merge_kernel<false><<<mg, mt, lds, st>>>(n, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
   return hipGetLastError();
 }
 

@@ -19,7 +19,7 @@
 //                 best in sampling order, their confidences q.  Proves that
 //                 the candidate set holds the exact top-k (else re-scans the
 //                 row: rare).
-//   tree_assemble grid B, 256 threads, all state in LDS.  Values, frontier
+//   tree_assemble grid B, 1024 threads, all state in LDS.  Values, frontier
 //                 ranks per layer, rerank of the pool by merging per-layer
 //                 sorted lists, BFS flattening.
 #include "common.h"
@@ -430,6 +430,8 @@ EDEV uint64_t node_key(float v, int e) {
 EDEV float key_value(uint64_t key) { return __uint_as_float((uint32_t)(key >> 32)); }
 EDEV int key_node(uint64_t key) { return (int)(0xffffffffu - (uint32_t)key); }
 
+constexpr int kTreeThreads = 1024;  // one workgroup per request: every layer step has the CU to itself
+
 // One workgroup per request; everything in LDS.
 //  1. layers, one block step each: every node of the layer counts the keys
 //     of its layer above its own, which is its layer rank; the k best become
@@ -442,7 +444,7 @@ EDEV int key_node(uint64_t key) { return (int)(0xffffffffu - (uint32_t)key); }
 //  3. flatten: BFS order (depth, parent flat index, sibling rank) is the order
 //     of (depth, path of sibling ranks from the root) read as a number, so a
 //     selected node's flat index is 1 + the count of selected nodes before it.
-__global__ __launch_bounds__(256) void tree_assemble_kernel(
+__global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     int S, int k, int D, int m, int V, const int32_t* __restrict__ root_token,
     const int32_t* __restrict__ pool_tok_g, const float* __restrict__ pool_q_g,
     int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
@@ -480,7 +482,8 @@ __global__ __launch_bounds__(256) void tree_assemble_kernel(
   for (int d = 1; d <= D; ++d) {
     const int lo = layer_lo(d, k), n = layer_n(d, k), dl = d - 1;
     const uint64_t* L = lay + dl * LS;
-    const int tpe = n <= 64 ? 4 : n <= 128 ? 2 : 1;  // threads per node (a lane group)
+    // threads per node (a lane group of a power of two <= 16 that fits the block)
+    const int tpe = n * 16 <= nt ? 16 : n * 8 <= nt ? 8 : n * 4 <= nt ? 4 : n * 2 <= nt ? 2 : 1;
     const int x = tid / tpe, part = tid & (tpe - 1);
     if (x < n) {
       const uint64_t K = L[x];
@@ -491,8 +494,7 @@ __global__ __launch_bounds__(256) void tree_assemble_kernel(
         const ulonglong2 w = reinterpret_cast<const ulonglong2*>(L)[y2];
         r += (w.x > K ? 1 : 0) + (w.y > K ? 1 : 0);
       }
-      if (tpe >= 2) r += __shfl_xor(r, 1);
-      if (tpe >= 4) r += __shfl_xor(r, 2);
+      for (int o = 1; o < tpe; o <<= 1) r += __shfl_xor(r, o);
       const int e = lo + x;
       if (part == 0) {
         lrank[e] = r;
@@ -648,7 +650,7 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
   const size_t LS = (size_t)((k * k + 1) & ~1);
   const size_t sm3 = (2 * (size_t)D * LS + S + 2 * (size_t)m) * 8 + (size_t)P * 3 * 4 + (size_t)S * 4 +
                      (size_t)m * 2 * 4;
-  tree_assemble_kernel<<<B, 256, sm3, st>>>(S, k, D, m, V, root, pool_tok, pool_q, node_tok, node_parent,
+  tree_assemble_kernel<<<B, kTreeThreads, sm3, st>>>(S, k, D, m, V, root, pool_tok, pool_q, node_tok, node_parent,
                                             node_depth, node_sib, node_slot, node_value, node_q, pool_flat,
                                             slot_src, status);
   return hipGetLastError();
