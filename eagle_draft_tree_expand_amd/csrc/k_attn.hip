@@ -70,6 +70,35 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
   else { k_begin = split * split_keys; k_end = min(L, k_begin + split_keys); }
   const float sl2 = scale * kLog2e;  // scores are kept in the log2 domain
 
+  const uint16_t* kbase = tree ? kt + ((size_t)b * n * hkv + g) * DH : kp + (((size_t)b * hkv + g) * Lmax) * DH;
+  const uint16_t* vbase = tree ? vt + ((size_t)b * n * hkv + g) * DH : vp + (((size_t)b * hkv + g) * Lmax) * DH;
+  const size_t kstride = tree ? (size_t)hkv * DH : (size_t)DH;
+  const bool wave_active = row0 < rows;
+
+  // K/V tiles of 64 keys: this thread's share of the next tile is loaded
+  // into registers while the current tile is in use, then written to LDS
+  // (K row-major, V transposed) between two barriers.  A thread owns two
+  // consecutive keys of one 8-wide d chunk, so its V^T writes are 4-byte
+  // (key pair) words and the 32 threads of a chunk fill 128 contiguous bytes
+  // of each V^T row (no bank conflicts).
+  constexpr int kPairs = (kKT / 2) * (DH / 8);                          // key-pair chunks per tile
+  constexpr int kChunks = (kPairs + kAttnThreads - 1) / kAttnThreads;  // per thread
+  uint4 kreg[2 * kChunks], vreg[2 * kChunks];
+#define ATTN_LOAD_TILE(T0)                                                                   \
+  _Pragma("unroll") for (int i = 0; i < kChunks; ++i) {                                      \
+    const int x = tid + i * kAttnThreads, kp = x & 31, dc = (x >> 5) * 8;                    \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                          \
+      const int key = (T0) + 2 * kp + h;                                                     \
+      kreg[2 * i + h] = make_uint4(0, 0, 0, 0);                                              \
+      vreg[2 * i + h] = make_uint4(0, 0, 0, 0);                                              \
+      if (x < kPairs && key < k_end) {                                                       \
+        kreg[2 * i + h] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * kstride + dc); \
+        vreg[2 * i + h] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * kstride + dc); \
+      }                                                                                      \
+    }                                                                                        \
+  }
+  if (k_begin < k_end) ATTN_LOAD_TILE(k_begin)  // first K/V tile in flight while Q loads
+
   // Query tiles of this wave.
   const int col = lane & 15, grp = lane >> 4;
   bf16x8 qreg[kQT][DH / 32];
@@ -99,57 +128,47 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
     for (int dt = 0; dt < DH / 16; ++dt) o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  const uint16_t* kbase = tree ? kt + ((size_t)b * n * hkv + g) * DH : kp + (((size_t)b * hkv + g) * Lmax) * DH;
-  const uint16_t* vbase = tree ? vt + ((size_t)b * n * hkv + g) * DH : vp + (((size_t)b * hkv + g) * Lmax) * DH;
-  const size_t kstride = tree ? (size_t)hkv * DH : (size_t)DH;
-  const bool wave_active = row0 < rows;
-
-  // K/V tiles of 64 keys: this thread's share of the next tile is loaded
-  // into registers while the current tile is in use, then written to LDS
-  // (K row-major, V transposed) between two barriers.
-  constexpr int kChunks = kKT * (DH / 8) / kAttnThreads;  // 16-byte chunks per thread per tile
-  uint4 kreg[kChunks], vreg[kChunks];
-#define ATTN_LOAD_TILE(T0)                                                                   \
-  _Pragma("unroll") for (int i = 0; i < kChunks; ++i) {                                      \
-    const int x = tid + i * kAttnThreads, kk = x / (DH / 8), dc = (x - kk * (DH / 8)) * 8;   \
-    const int key = (T0) + kk;                                                               \
-    kreg[i] = make_uint4(0, 0, 0, 0);                                                        \
-    vreg[i] = make_uint4(0, 0, 0, 0);                                                        \
-    if (key < k_end) {                                                                       \
-      kreg[i] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * kstride + dc);         \
-      vreg[i] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * kstride + dc);         \
-    }                                                                                        \
-  }
-  if (k_begin < k_end) ATTN_LOAD_TILE(k_begin)
   for (int t0 = k_begin; t0 < k_end; t0 += kKT) {
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      const int x = tid + i * kAttnThreads, kk = x / (DH / 8), dc = (x - kk * (DH / 8)) * 8;
-      *reinterpret_cast<uint4*>(&Ks[kk * KPAD + dc]) = kreg[i];
-      const uint16_t* ve = reinterpret_cast<const uint16_t*>(&vreg[i]);
+      const int x = tid + i * kAttnThreads, kp = x & 31, dc = (x >> 5) * 8;
+      if (x >= kPairs) break;
+      *reinterpret_cast<uint4*>(&Ks[(2 * kp) * KPAD + dc]) = kreg[2 * i];
+      *reinterpret_cast<uint4*>(&Ks[(2 * kp + 1) * KPAD + dc]) = kreg[2 * i + 1];
+      const uint16_t* v0 = reinterpret_cast<const uint16_t*>(&vreg[2 * i]);
+      const uint16_t* v1 = reinterpret_cast<const uint16_t*>(&vreg[2 * i + 1]);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Vts[(dc + e) * VPAD + kk] = ve[e];
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<uint32_t*>(&Vts[(dc + e) * VPAD + 2 * kp]) = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
     }
     __syncthreads();
     if (t0 + kKT < k_end) ATTN_LOAD_TILE(t0 + kKT)
     if (!wave_active) continue;
     // Masking is needed only in the tree split and in a ragged last tile.
     const bool masked = tree || t0 + kKT > k_end;
+    // S^T tiles of both query tiles: 64 keys x 16 queries each, lane holds
+    // keys 16*kt4 + 4*grp + i of query col.  Each K fragment read from LDS
+    // feeds the MFMAs of both query tiles.
+    floatx4 sc[kQT][4];
+#pragma unroll
+    for (int t = 0; t < kQT; ++t)
+#pragma unroll
+      for (int kt4 = 0; kt4 < 4; ++kt4) sc[t][kt4] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kt4 = 0; kt4 < 4; ++kt4) {
+#pragma unroll
+      for (int ds = 0; ds < DH / 32; ++ds) {
+        B8 a;
+        a.u = *reinterpret_cast<const uint4*>(&Ks[(kt4 * 16 + col) * KPAD + ds * 32 + grp * 8]);
+#pragma unroll
+        for (int t = 0; t < kQT; ++t)
+          sc[t][kt4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, qreg[t][ds], sc[t][kt4], 0, 0, 0);
+      }
+    }
+    B8 pb[kQT][2];
 #pragma unroll
     for (int t = 0; t < kQT; ++t) {
-      // S^T tile: 64 keys x 16 queries, lane holds keys 16*kt + 4*grp + i of query col.
-      floatx4 sc[4];
-#pragma unroll
-      for (int kt4 = 0; kt4 < 4; ++kt4) {
-        sc[kt4] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int ds = 0; ds < DH / 32; ++ds) {
-          B8 a;
-          a.u = *reinterpret_cast<const uint4*>(&Ks[(kt4 * 16 + col) * KPAD + ds * 32 + grp * 8]);
-          sc[kt4] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, qreg[t][ds], sc[kt4], 0, 0, 0);
-        }
-      }
       float mx = kNegInf;
       if (masked) {
         // tiles start at multiples of 64 in the tree split; rows >= n read node 0
@@ -160,8 +179,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
           for (int i = 0; i < 4; ++i) {
             const int key = t0 + kt4 * 16 + grp * 4 + i;
             const bool vis = key < k_end && ((mw >> (key & 63)) & 1ull);
-            const float v = vis ? sc[kt4][i] * sl2 : kNegInf;
-            sc[kt4][i] = v;
+            const float v = vis ? sc[t][kt4][i] * sl2 : kNegInf;
+            sc[t][kt4][i] = v;
             mx = fmaxf(mx, v);
           }
       } else {
@@ -169,8 +188,8 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
         for (int kt4 = 0; kt4 < 4; ++kt4)
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const float v = sc[kt4][i] * sl2;
-            sc[kt4][i] = v;
+            const float v = sc[t][kt4][i] * sl2;
+            sc[t][kt4][i] = v;
             mx = fmaxf(mx, v);
           }
       }
@@ -181,33 +200,35 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
       const float alpha = __builtin_amdgcn_exp2f(mrun[t] - mref);
       mrun[t] = mnew;
       float psum = 0.f;
-      B8 pb[2];
 #pragma unroll
       for (int kt4 = 0; kt4 < 4; ++kt4) {
         float p[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          p[i] = __builtin_amdgcn_exp2f(sc[kt4][i] - mref);
+          p[i] = __builtin_amdgcn_exp2f(sc[t][kt4][i] - mref);
           psum += p[i];
         }
         const bf16x2 lo2 = {(__bf16)p[0], (__bf16)p[1]}, hi2 = {(__bf16)p[2], (__bf16)p[3]};
-        pb[kt4 >> 1].h[kt4 & 1] = make_uint2(__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2));
+        pb[t][kt4 >> 1].h[kt4 & 1] = make_uint2(__builtin_bit_cast(uint32_t, lo2), __builtin_bit_cast(uint32_t, hi2));
       }
       lrun[t] = lrun[t] * alpha + psum;
       if (__any(alpha != 1.f)) {
 #pragma unroll
         for (int dt = 0; dt < DH / 16; ++dt) o[t][dt] *= alpha;
       }
+    }
+    // O^T += V^T P^T for both query tiles; each V^T fragment read once.
 #pragma unroll
-      for (int dt = 0; dt < DH / 16; ++dt) {
+    for (int dt = 0; dt < DH / 16; ++dt) {
 #pragma unroll
-        for (int beta = 0; beta < 2; ++beta) {
-          B8 a;
-          const uint16_t* vr = &Vts[(dt * 16 + col) * VPAD + beta * 32 + grp * 4];
-          a.h[0] = *reinterpret_cast<const uint2*>(vr);
-          a.h[1] = *reinterpret_cast<const uint2*>(vr + 16);
-          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, pb[beta].v, o[t][dt], 0, 0, 0);
-        }
+      for (int beta = 0; beta < 2; ++beta) {
+        B8 a;
+        const uint16_t* vr = &Vts[(dt * 16 + col) * VPAD + beta * 32 + grp * 4];
+        a.h[0] = *reinterpret_cast<const uint2*>(vr);
+        a.h[1] = *reinterpret_cast<const uint2*>(vr + 16);
+#pragma unroll
+        for (int t = 0; t < kQT; ++t)
+          o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, pb[t][beta].v, o[t][dt], 0, 0, 0);
       }
     }
   }
