@@ -278,6 +278,171 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(int rows, int H, int V,
   }
 }
 
+// Tiled GEMM for many rows: logits = X W^T with 256 x 256 output tiles per
+// workgroup (4 waves, each a 128 x 128 quadrant of 8 x 8 MFMA tiles with fp32
+// accumulators), 64-wide hidden steps double-buffered in LDS: the next step's
+// X and W tiles are loaded into registers while the current one feeds the
+// MFMAs, then stored to the other LDS buffer (one barrier per step).  W comes
+// from the packed layout (64-row groups of contiguous 1 KB loads) or row-major.
+// Workgroups are mapped so that the row tiles sharing a vocab tile run on one
+// XCD (workgroups go round-robin over the 8 XCDs), keeping that W tile in the
+// XCD's L2 while all row tiles read it.  The epilogue writes the logits and a
+// stats record per (row, 256-column tile), the same record the streaming
+// kernel writes per 512 columns.
+constexpr int kGK = 64;            // hidden values per step
+constexpr int kGPad = kGK + 8;     // LDS row stride (bf16)
+constexpr int kGStage = 2 * kGemmTile * kGPad;  // bf16 elements of one LDS stage (X tile then W tile)
+
+template <bool PACKED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_gemm_kernel(
+    int rows, int H, int V, float Tp, int nm, int nn, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
+    float* __restrict__ logits, float* __restrict__ part, int32_t* status) {
+  extern __shared__ __attribute__((aligned(16))) uint16_t gsm[];  // [2][kGStage]
+  __shared__ Rec hrec[2][kGemmTile];
+
+  // XCD-aware tile order: workgroup id = xcd + 8 j; on each XCD the row tiles
+  // of one vocab tile are consecutive.
+  const int bid = blockIdx.x, xcd = bid & 7, j = bid >> 3;
+  const int mt_idx = j % nm, nt_idx = (j / nm) * 8 + xcd;
+  if (nt_idx >= nn) return;  // padding of the grid to a multiple of 8 vocab tiles
+  const int m0 = mt_idx * kGemmTile, n0 = nt_idx * kGemmTile;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave >> 1, wn = wave & 1;
+  const int col = lane & 15, grp = lane >> 4;
+  const int nch = H / kGK;
+  const int ngroups = (V + 63) / 64;
+
+  // This thread's 8 X and 8 W 16-byte units per step.  X unit i: tile row
+  // (tid >> 3) + 32 i, hidden offset (tid & 7) * 8.  Packed W unit i: 64-row
+  // group i >> 1 of the tile, load (tid >> 6) + 4 (i & 1) of the chunk, lane
+  // tid & 63; row-major W unit i: tile column (tid >> 3) + 32 i.
+  uint32_t xrow[8];  // element offsets of the (clamped) X rows
+#pragma unroll
+  for (int i = 0; i < 8; ++i) xrow[i] = (uint32_t)min(m0 + (tid >> 3) + 32 * i, rows - 1) * (uint32_t)H;
+  const int xk = (tid & 7) * 8;
+  const uint16_t* wg[4];  // packed: the tile's four 64-row groups; row-major: unused
+  size_t wrow[PACKED ? 1 : 8];
+  if (PACKED) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) wg[q] = w + (size_t)min(n0 / 64 + q, ngroups - 1) * nch * 4096 + (size_t)(tid & 63) * 8;
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) wrow[i] = (size_t)min(n0 + (tid >> 3) + 32 * i, V - 1) * H + xk;
+  }
+  floatx4 acc[8][8];
+#pragma unroll
+  for (int a = 0; a < 8; ++a)
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+  u32x4 xr_[8], wr_[8];
+#define G_LOAD(c)                                                                                          \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                          \
+    xr_[i] = *reinterpret_cast<const u32x4*>(x + xrow[i] + (size_t)(c) * kGK + xk);                        \
+    const uint16_t* ws_ = PACKED ? wg[PACKED ? (i >> 1) : 0] + ((size_t)(c) * 8 + (tid >> 6) + 4 * (i & 1)) * 512 \
+                                 : w + wrow[PACKED ? 0 : i] + (size_t)(c) * kGK;                            \
+    wr_[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ws_));                              \
+  }
+#define G_STORE(buf)                                                                                       \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                          \
+    const int xr = (tid >> 3) + 32 * i;                                                                    \
+    *reinterpret_cast<u32x4*>(gsm + (buf) * kGStage + xr * kGPad + xk) = xr_[i];                           \
+    int wr, wk;                                                                                            \
+    if (PACKED) {                                                                                          \
+      const int jj = (tid >> 6) + 4 * (i & 1), l = tid & 63;                                               \
+      wr = (i >> 1) * 64 + (jj & 3) * 16 + (l & 15);                                                       \
+      wk = (jj >> 2) * 32 + (l >> 4) * 8;                                                                  \
+    } else {                                                                                               \
+      wr = (tid >> 3) + 32 * i;                                                                            \
+      wk = xk;                                                                                             \
+    }                                                                                                      \
+    *reinterpret_cast<u32x4*>(gsm + (buf) * kGStage + kGemmTile * kGPad + wr * kGPad + wk) = wr_[i];      \
+  }
+  G_LOAD(0)
+  G_STORE(0)
+  __syncthreads();
+  for (int c = 0; c < nch; ++c) {
+    const int buf = c & 1;
+    if (c + 1 < nch) G_LOAD(c + 1)
+    const uint16_t* As = gsm + buf * kGStage + (wm * 128 + col) * kGPad + grp * 8;
+    const uint16_t* Bs = gsm + buf * kGStage + kGemmTile * kGPad + (wn * 128 + col) * kGPad + grp * 8;
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      B8 bf[8];
+#pragma unroll
+      for (int t = 0; t < 8; ++t) bf[t].w = *reinterpret_cast<const u32x4*>(Bs + t * 16 * kGPad + ks * 32);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) {
+        B8 af;
+        af.w = *reinterpret_cast<const u32x4*>(As + mt * 16 * kGPad + ks * 32);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, bf[nt].v, acc[mt][nt], 0, 0, 0);
+      }
+    }
+    if (c + 1 < nch) G_STORE(buf ^ 1)
+    __syncthreads();
+  }
+#undef G_LOAD
+#undef G_STORE
+
+  // Epilogue: logits and the stats of each row over this wave's 128 columns,
+  // then the two column halves of the tile merged through LDS.  One row at a
+  // time: its 8 values per lane are copied out of the accumulators.
+  bool bad = false;
+  const int nbase = n0 + wn * 128;
+#pragma unroll
+  for (int mt = 0; mt < 8; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = wm * 128 + mt * 16 + grp * 4 + i;
+      const int m = m0 + r;
+      float zv[8];
+      float zm = kNegInf;
+      int ai = kIdxNone;
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt) {
+        const int n = nbase + nt * 16 + col;
+        float z = acc[mt][nt][i];
+        if (n < V) {
+          if (m < rows) logits[(size_t)m * V + n] = z;
+          if (!isfinite(z)) { bad = true; z = kNegInf; }
+          if (z > zm) { zm = z; ai = n; }  // columns ascend with nt: ties keep the lower id
+        } else {
+          z = kNegInf;
+        }
+        zv[nt] = z;
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        const float z2 = __shfl_xor(zm, o);
+        const int a2 = __shfl_xor(ai, o);
+        if (beats(z2, a2, zm, ai)) { zm = z2; ai = a2; }
+      }
+      const float tmax = zm / Tp;
+      float s = 0.f;
+      if (zm != kNegInf) {
+        const float cc = kLog2e / Tp, off = tmax * kLog2e;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) s += __builtin_amdgcn_exp2f(fmaf(zv[nt], cc, -off));
+      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+      if (col == 0) hrec[wn][r] = Rec{zm == kNegInf ? kNegInf : tmax, s, zm, ai};
+    }
+  }
+  if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
+  __syncthreads();
+  const int m = m0 + tid;
+  if (m < rows) {
+    Rec rc = hrec[0][tid];
+    rec_merge(rc, hrec[1][tid]);
+    float* pr = part + ((size_t)m * nn + nt_idx) * 4;
+    *reinterpret_cast<float4*>(pr) = make_float4(rc.tmax, rc.s, rc.zmax, __int_as_float(rc.arg));
+  }
+}
+
 // One workgroup per row: merge the row's per-tile records (fp64 sum).
 __global__ __launch_bounds__(256) void lm_finalize_kernel(int rows, int ntiles, const float* __restrict__ part,
                                                           float* __restrict__ row_stats, int32_t* __restrict__ row_argmax) {
@@ -367,8 +532,19 @@ hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const 
                          float* logits, float* row_stats, int32_t* row_argmax, float* probs, float* ws_part,
                          int32_t* status, hipStream_t st) {
   const float Tp = (T > 0.f) ? T : 1.0f;
-  const int ntiles = lm_ntiles(V);
-  if (dtype == EAGLE_BF16) {
+  int ntiles = lm_ntiles(V);
+  if (dtype == EAGLE_BF16 && rows >= kGemmMinRows) {
+    const int nm = (rows + kGemmTile - 1) / kGemmTile, nn = lm_gemm_ntiles(V);
+    ntiles = nn;
+    const int grid = nm * ((nn + 7) / 8) * 8;
+    const size_t lds = (size_t)2 * kGStage * sizeof(uint16_t);
+    if (w_layout == EAGLE_W_PACKED)
+      lmhead_gemm_kernel<true><<<grid, 256, lds, st>>>(rows, H, V, Tp, nm, nn, (const uint16_t*)x,
+                                                       (const uint16_t*)w, logits, ws_part, status);
+    else
+      lmhead_gemm_kernel<false><<<grid, 256, lds, st>>>(rows, H, V, Tp, nm, nn, (const uint16_t*)x,
+                                                        (const uint16_t*)w, logits, ws_part, status);
+  } else if (dtype == EAGLE_BF16) {
     dim3 grid(ntiles, lm_mtiles(rows));
     if (w_layout == EAGLE_W_PACKED)
       lmhead_bf16_kernel<true><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,

@@ -65,7 +65,12 @@ constexpr int kLmTileM = 64;             // rows per workgroup
 constexpr int kLmThreads = 512;          // bf16: 4 column quarters x 2 hidden halves
 inline int lm_ntiles(int V) { return (V + kLmTileN - 1) / kLmTileN; }
 inline int lm_mtiles(int rows) { return (rows + kLmTileM - 1) / kLmTileM; }
-inline size_t lm_ws_bytes(int rows, int V) { return (size_t)rows * lm_ntiles(V) * 4 * sizeof(float); }
+// Large row counts (many requests per round) take a tiled GEMM: 256 x 256
+// output tiles, one stats record per (row, 256-column tile).
+constexpr int kGemmTile = 256;
+constexpr int kGemmMinRows = 193;        // from 4 row tiles of the streaming kernel on
+inline int lm_gemm_ntiles(int V) { return (V + kGemmTile - 1) / kGemmTile; }
+inline size_t lm_ws_bytes(int rows, int V) { return (size_t)rows * lm_gemm_ntiles(V) * 4 * sizeof(float); }
 hipError_t launch_lmhead(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,
                          float T, float* logits, float* row_stats, int32_t* row_argmax,
                          float* probs, float* ws_part, int32_t* status, hipStream_t st);

@@ -157,6 +157,9 @@ LM_CASES = [
     ("mid_bf16", dict(B=2, D=5, k=4, m=60, V=3000, H=384, hq=3, hkv=1), 0.8),  # 122 rows: two row blocks
     ("mid_f32", {}, 1.0),
     ("tiny", {}, 1.0),
+    # many rows: the tiled GEMM path (ragged row and vocab tiles)
+    ("mid_bf16", dict(B=40), 1.0),                                  # 600 rows x 5003, hidden 512
+    ("mid_bf16", dict(B=20, V=300, H=256, hq=2), 0.5),              # 300 rows x 300, hidden 256
 ]
 
 
@@ -228,6 +231,35 @@ def test_lmhead_full_8b_sampled(rt):
         assert abs(dev["stats"][r, 0] - st[0, 0]) <= 1e-6 * abs(st[0, 0])
         assert abs(dev["stats"][r, 1] - st[0, 1]) <= 1e-5 * st[0, 1]
         assert dev["argmax"][r] == am[0]
+
+
+def test_lmhead_gemm_b64_sampled(rt):
+    """Batch-64 8B LM head (3904 x 4096 x 128256) on the tiled GEMM: sampled logits and row stats."""
+    cfg = synth.get_config("8b")
+    inp = synth.make_inputs(cfg)
+    rng = np.random.default_rng(9)
+    B = 64
+    X = synth.bf16_round((0.05 * rng.standard_normal((B * cfg.N, cfg.H))).astype(np.float32))
+    dr = rt.DeviceRound(cfg, B=B)
+    wts = rt.DeviceWeights(inp)
+    dr.x.copy_(torch.from_numpy(X).to(dr.x.dtype).view(dr.x.shape))
+    dr.lmhead(wts, 1.0)
+    torch.cuda.synchronize()
+    rows = rng.integers(0, B * cfg.N, size=24)
+    rows[:2] = [0, B * cfg.N - 1]
+    cols = rng.integers(0, cfg.V, size=300)
+    cols[:3] = [0, cfg.V - 1, 255]
+    lg = dr.logits[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ref = X[rows].astype(np.float64) @ inp.w[cols].astype(np.float64).T
+    assert np.abs(lg[:, cols] - ref).max() / np.abs(ref).max() <= 1e-5
+    stats = dr.stats.cpu().numpy()
+    am = dr.argmax.cpu().numpy()
+    for j, r in enumerate(rows[:6]):
+        st, a = olm.row_stats(lg[j:j + 1], 1.0)
+        assert abs(stats[r, 0] - st[0, 0]) <= 1e-6 * abs(st[0, 0])
+        assert abs(stats[r, 1] - st[0, 1]) <= 1e-5 * st[0, 1]
+        assert am[r] == a[0]
+    assert int(dr.status.item()) == 0
 
 
 # ---------------------------------------------------------------- acceptance
