@@ -280,112 +280,133 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(int rows, int H, int V,
 
 // Tiled GEMM for many rows: logits = X W^T with 256 x 256 output tiles per
 // workgroup (4 waves, each a 128 x 128 quadrant of 8 x 8 MFMA tiles with fp32
-// accumulators), 64-wide hidden steps double-buffered in LDS: the next step's
-// X and W tiles are loaded into registers while the current one feeds the
-// MFMAs, then stored to the other LDS buffer (one barrier per step).  W comes
-// from the packed layout (64-row groups of contiguous 1 KB loads) or row-major.
-// Workgroups are mapped so that the row tiles sharing a vocab tile run on one
-// XCD (workgroups go round-robin over the 8 XCDs), keeping that W tile in the
-// XCD's L2 while all row tiles read it.  The epilogue writes the logits and a
-// stats record per (row, 256-column tile), the same record the streaming
-// kernel writes per 512 columns.
-constexpr int kGK = 64;            // hidden values per step
-constexpr int kGPad = kGK + 8;     // LDS row stride (bf16)
-constexpr int kGStage = 2 * kGemmTile * kGPad;  // bf16 elements of one LDS stage (X tile then W tile)
+// accumulators).  The hidden dimension goes in steps of 32 through a 4-stage
+// LDS ring filled by direct global-to-LDS loads (global_load_lds_dwordx4:
+// lane l's 16 bytes land at the destination + 16 l), issued three steps
+// ahead.  Every 1 KB LDS block is one MFMA operand in lane order: A block mt =
+// X rows 16 mt.. (lane l: row l % 16, hidden 8 (l / 16)..); B block nt = W rows
+// 16 nt.. the same way, which in the packed weight layout is one contiguous
+// 1 KB load.  Workgroups are mapped so that the row tiles sharing a vocab tile
+// run on one XCD (workgroups go round-robin over the 8 XCDs), keeping that W
+// tile in the XCD's L2 while all row tiles read it.  The epilogue writes the
+// logits and a stats record per (row, 256-column tile), the same record the
+// streaming kernel writes per 512 columns.
+constexpr int kGK = 32;        // hidden values per step
+constexpr int kGStages = 4;    // LDS ring depth (loads run kGStages - 1 steps ahead)
+constexpr int kGBlock = 512;   // bf16 elements of one 1 KB operand block
+constexpr int kGThreads = 512;     // 8 waves: 4 row quarters x 2 column halves, two per SIMD
+constexpr int kGLoadsPerStep = 4;  // direct loads each wave issues per step (32 blocks / 8 waves)
+
+// s_waitcnt immediate that waits for at most n outstanding vector memory
+// operations (other counters unconstrained): vmcnt bits [3:0] and [15:14].
+EDEV constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 template <bool PACKED>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void lmhead_gemm_kernel(
+__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_gemm_kernel(
     int rows, int H, int V, float Tp, int nm, int nn, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
     float* __restrict__ logits, float* __restrict__ part, int32_t* status) {
-  extern __shared__ __attribute__((aligned(16))) uint16_t gsm[];  // [2][kGStage]
+  // the ring: four separate arrays, so that the waits for the direct loads into
+  // one of them need not cover the loads still flying into the others
+  __shared__ __attribute__((aligned(1024))) uint16_t ring0[32 * kGBlock];  // A 16 blocks | B 16 blocks
+  __shared__ __attribute__((aligned(1024))) uint16_t ring1[32 * kGBlock];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring2[32 * kGBlock];
+  __shared__ __attribute__((aligned(1024))) uint16_t ring3[32 * kGBlock];
   __shared__ Rec hrec[2][kGemmTile];
 
-  // XCD-aware tile order: workgroup id = xcd + 8 j; on each XCD the row tiles
-  // of one vocab tile are consecutive.
+  // XCD-aware tile order: workgroup id = xcd + 8 j.  On each XCD, runs of 32
+  // consecutive j (about what its 32 CUs hold at once) form a block of 4 row
+  // tiles x 8 vocab tiles, so every X and W slab read into the XCD's L2
+  // serves 8 or 4 workgroups; vocab tiles of XCD x are those = x mod 8.
   const int bid = blockIdx.x, xcd = bid & 7, j = bid >> 3;
-  const int mt_idx = j % nm, nt_idx = (j / nm) * 8 + xcd;
-  if (nt_idx >= nn) return;  // padding of the grid to a multiple of 8 vocab tiles
+  const int jb = j & 31, blk = j >> 5, nmb = (nm + 3) / 4;
+  const int mt_idx = (blk % nmb) * 4 + (jb >> 3);
+  const int nt_idx = ((blk / nmb) * 8 + (jb & 7)) * 8 + xcd;
+  if (mt_idx >= nm || nt_idx >= nn) return;  // padding of the grid to whole blocks
   const int m0 = mt_idx * kGemmTile, n0 = nt_idx * kGemmTile;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave >> 1, wn = wave & 1;  // rows 64 wm.., columns 128 wn..
   const int col = lane & 15, grp = lane >> 4;
-  const int nch = H / kGK;
+  const int nch = H / 64;
+  const int nsteps = H / kGK;
   const int ngroups = (V + 63) / 64;
 
-  // This thread's 8 X and 8 W 16-byte units per step.  X unit i: tile row
-  // (tid >> 3) + 32 i, hidden offset (tid & 7) * 8.  Packed W unit i: 64-row
-  // group i >> 1 of the tile, load (tid >> 6) + 4 (i & 1) of the chunk, lane
-  // tid & 63; row-major W unit i: tile column (tid >> 3) + 32 i.
-  uint32_t xrow[8];  // element offsets of the (clamped) X rows
+  // Sources of this wave's 4 blocks per step: A blocks mt = 2 wave + q and
+  // B blocks nt = 2 wave + q (q < 2).
+  uint32_t xoff[2];  // element offset of this lane's X row (clamped) + its 8-wide hidden offset
 #pragma unroll
-  for (int i = 0; i < 8; ++i) xrow[i] = (uint32_t)min(m0 + (tid >> 3) + 32 * i, rows - 1) * (uint32_t)H;
-  const int xk = (tid & 7) * 8;
-  const uint16_t* wg[4];  // packed: the tile's four 64-row groups; row-major: unused
-  size_t wrow[PACKED ? 1 : 8];
-  if (PACKED) {
+  for (int q = 0; q < 2; ++q)
+    xoff[q] = (uint32_t)min(m0 + (2 * wave + q) * 16 + col, rows - 1) * (uint32_t)H + grp * 8;
+  const uint16_t* wsrc[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wg[q] = w + (size_t)min(n0 / 64 + q, ngroups - 1) * nch * 4096 + (size_t)(tid & 63) * 8;
-  } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) wrow[i] = (size_t)min(n0 + (tid >> 3) + 32 * i, V - 1) * H + xk;
+  for (int q = 0; q < 2; ++q) {
+    const int nt = 2 * wave + q;
+    if (PACKED) {  // group nt / 4, load (nt % 4) of a 32-wide half chunk
+      const int g = min(n0 / 64 + nt / 4, ngroups - 1);
+      wsrc[q] = w + ((size_t)g * nch * 8 + (nt & 3)) * 512 + (size_t)lane * 8;
+    } else {
+      wsrc[q] = w + (size_t)min(n0 + nt * 16 + col, V - 1) * H + grp * 8;
+    }
   }
-  floatx4 acc[8][8];
+#define G_ISSUE_Q(st, dst, q)                                                                               \
+  {                                                                                                         \
+    const int k0 = (st) * kGK;                                                                              \
+    __builtin_amdgcn_global_load_lds(x + xoff[q] + k0, dst + (2 * wave + (q)) * kGBlock, 16, 0, 0);        \
+    const uint16_t* ws_ = PACKED ? wsrc[q] + ((size_t)((st) >> 1) * 8 + ((st) & 1) * 4) * 512              \
+                                 : wsrc[q] + k0;                                                            \
+    __builtin_amdgcn_global_load_lds(ws_, dst + (16 + 2 * wave + (q)) * kGBlock, 16, 0, 0);                 \
+  }
+#define G_ISSUE(st, dst)                                                                                    \
+  {                                                                                                         \
+    _Pragma("unroll") for (int q = 0; q < 2; ++q) G_ISSUE_Q(st, dst, q)                                     \
+  }
+
+  floatx4 acc[4][8];
 #pragma unroll
-  for (int a = 0; a < 8; ++a)
+  for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < 8; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  u32x4 xr_[8], wr_[8];
-#define G_LOAD(c)                                                                                          \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                          \
-    xr_[i] = *reinterpret_cast<const u32x4*>(x + xrow[i] + (size_t)(c) * kGK + xk);                        \
-    const uint16_t* ws_ = PACKED ? wg[PACKED ? (i >> 1) : 0] + ((size_t)(c) * 8 + (tid >> 6) + 4 * (i & 1)) * 512 \
-                                 : w + wrow[PACKED ? 0 : i] + (size_t)(c) * kGK;                            \
-    wr_[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(ws_));                              \
-  }
-#define G_STORE(buf)                                                                                       \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i) {                                                          \
-    const int xr = (tid >> 3) + 32 * i;                                                                    \
-    *reinterpret_cast<u32x4*>(gsm + (buf) * kGStage + xr * kGPad + xk) = xr_[i];                           \
-    int wr, wk;                                                                                            \
-    if (PACKED) {                                                                                          \
-      const int jj = (tid >> 6) + 4 * (i & 1), l = tid & 63;                                               \
-      wr = (i >> 1) * 64 + (jj & 3) * 16 + (l & 15);                                                       \
-      wk = (jj >> 2) * 32 + (l >> 4) * 8;                                                                  \
-    } else {                                                                                               \
-      wr = (tid >> 3) + 32 * i;                                                                            \
-      wk = xk;                                                                                             \
+  // One step: wait for this wave's loads of step st (later steps may still
+  // fly), barrier (every wave's blocks are in; the buffer of step st - 1 is
+  // free), issue step st + 3 into that buffer, then the 64 MFMAs.
+#define G_STEP(st, cur, nxt)                                                                               \
+  {                                                                                                        \
+    const int ahead = min(kGStages - 2, nsteps - 1 - (st));                                                \
+    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGLoadsPerStep));                            \
+    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGLoadsPerStep));                           \
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                                                         \
+    /* a bare barrier: the waits above already cover this wave's loads, and a */                          \
+    /* fenced barrier would also wait for the steps still in flight */                                     \
+    asm volatile("" ::: "memory");                                                                         \
+    __builtin_amdgcn_s_barrier();                                                                          \
+    asm volatile("" ::: "memory");                                                                         \
+    /* all 16 operand reads first: the MFMAs start as the first ones land; */                             \
+    /* the direct loads of step st + 3 go out between the first MFMAs */                                   \
+    B8 bf[8], af[4];                                                                                       \
+    _Pragma("unroll") for (int t = 0; t < 8; ++t)                                                          \
+      bf[t].w = *reinterpret_cast<const u32x4*>(cur + (16 + wn * 8 + t) * kGBlock + lane * 8);            \
+    _Pragma("unroll") for (int t = 0; t < 4; ++t)                                                          \
+      af[t].w = *reinterpret_cast<const u32x4*>(cur + (wm * 4 + t) * kGBlock + lane * 8);                 \
+    _Pragma("unroll") for (int mt = 0; mt < 4; ++mt) {                                                     \
+      _Pragma("unroll") for (int nt = 0; nt < 8; ++nt)                                                     \
+        acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt].v, bf[nt].v, acc[mt][nt], 0, 0, 0);   \
+      if (mt == 0 && (st) + kGStages - 1 < nsteps) G_ISSUE((st) + kGStages - 1, nxt)                       \
     }                                                                                                      \
-    *reinterpret_cast<u32x4*>(gsm + (buf) * kGStage + kGemmTile * kGPad + wr * kGPad + wk) = wr_[i];      \
   }
-  G_LOAD(0)
-  G_STORE(0)
-  __syncthreads();
-  for (int c = 0; c < nch; ++c) {
-    const int buf = c & 1;
-    if (c + 1 < nch) G_LOAD(c + 1)
-    const uint16_t* As = gsm + buf * kGStage + (wm * 128 + col) * kGPad + grp * 8;
-    const uint16_t* Bs = gsm + buf * kGStage + kGemmTile * kGPad + (wn * 128 + col) * kGPad + grp * 8;
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      B8 bf[8];
-#pragma unroll
-      for (int t = 0; t < 8; ++t) bf[t].w = *reinterpret_cast<const u32x4*>(Bs + t * 16 * kGPad + ks * 32);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        B8 af;
-        af.w = *reinterpret_cast<const u32x4*>(As + mt * 16 * kGPad + ks * 32);
-#pragma unroll
-        for (int nt = 0; nt < 8; ++nt)
-          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af.v, bf[nt].v, acc[mt][nt], 0, 0, 0);
-      }
-    }
-    if (c + 1 < nch) G_STORE(buf ^ 1)
-    __syncthreads();
+  // nsteps = H / 32 is a multiple of 4 (hidden % 128 == 0)
+  G_ISSUE(0, ring0)
+  G_ISSUE(1, ring1)
+  G_ISSUE(2, ring2)
+  for (int st = 0; st < nsteps; st += 4) {
+    G_STEP(st, ring0, ring3)
+    G_STEP(st + 1, ring1, ring0)
+    G_STEP(st + 2, ring2, ring1)
+    G_STEP(st + 3, ring3, ring2)
   }
-#undef G_LOAD
-#undef G_STORE
+#undef G_STEP
+#undef G_ISSUE
+#undef G_ISSUE_Q
 
   // Epilogue: logits and the stats of each row over this wave's 128 columns,
   // then the two column halves of the tile merged through LDS.  One row at a
@@ -393,10 +414,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   bool bad = false;
   const int nbase = n0 + wn * 128;
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt) {
+  for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = wm * 128 + mt * 16 + grp * 4 + i;
+      const int r = wm * 64 + mt * 16 + grp * 4 + i;
       const int m = m0 + r;
       float zv[8];
       float zm = kNegInf;
@@ -435,7 +456,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
   if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
   __syncthreads();
   const int m = m0 + tid;
-  if (m < rows) {
+  if (tid < kGemmTile && m < rows) {
     Rec rc = hrec[0][tid];
     rec_merge(rc, hrec[1][tid]);
     float* pr = part + ((size_t)m * nn + nt_idx) * 4;
@@ -536,13 +557,13 @@ hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const 
   if (dtype == EAGLE_BF16 && rows >= kGemmMinRows) {
     const int nm = (rows + kGemmTile - 1) / kGemmTile, nn = lm_gemm_ntiles(V);
     ntiles = nn;
-    const int grid = nm * ((nn + 7) / 8) * 8;
-    const size_t lds = (size_t)2 * kGStage * sizeof(uint16_t);
+    const int grid = ((nm + 3) / 4 * 4) * ((nn + 63) / 64 * 64);  // whole 4 x 8 blocks on each of 8 XCDs
+    const size_t lds = 0;
     if (w_layout == EAGLE_W_PACKED)
-      lmhead_gemm_kernel<true><<<grid, 256, lds, st>>>(rows, H, V, Tp, nm, nn, (const uint16_t*)x,
+      lmhead_gemm_kernel<true><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, (const uint16_t*)x,
                                                        (const uint16_t*)w, logits, ws_part, status);
     else
-      lmhead_gemm_kernel<false><<<grid, 256, lds, st>>>(rows, H, V, Tp, nm, nn, (const uint16_t*)x,
+      lmhead_gemm_kernel<false><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, (const uint16_t*)x,
                                                         (const uint16_t*)w, logits, ws_part, status);
   } else if (dtype == EAGLE_BF16) {
     dim3 grid(ntiles, lm_mtiles(rows));
