@@ -303,8 +303,8 @@ EDEV constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 <<
 
 template <bool PACKED>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_gemm_kernel(
-    int rows, int H, int V, float Tp, int nm, int nn, const uint16_t* __restrict__ x, const uint16_t* __restrict__ w,
-    float* __restrict__ logits, float* __restrict__ part, int32_t* status) {
+    int rows, int H, int V, float Tp, int nm, int nn, int bm, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ w, float* __restrict__ logits, float* __restrict__ part, int32_t* status) {
   // the ring: four separate arrays, so that the waits for the direct loads into
   // one of them need not cover the loads still flying into the others
   __shared__ __attribute__((aligned(1024))) uint16_t ring0[32 * kGBlock];  // A 16 blocks | B 16 blocks
@@ -314,13 +314,13 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   __shared__ Rec hrec[2][kGemmTile];
 
   // XCD-aware tile order: workgroup id = xcd + 8 j.  On each XCD, runs of 32
-  // consecutive j (about what its 32 CUs hold at once) form a block of 4 row
-  // tiles x 8 vocab tiles, so every X and W slab read into the XCD's L2
-  // serves 8 or 4 workgroups; vocab tiles of XCD x are those = x mod 8.
+  // consecutive j (about what its 32 CUs hold at once) form a block of bm row
+  // tiles x 32/bm vocab tiles, so every X and W slab read into the XCD's L2
+  // serves several workgroups; vocab tiles of XCD x are those = x mod 8.
   const int bid = blockIdx.x, xcd = bid & 7, j = bid >> 3;
-  const int jb = j & 31, blk = j >> 5, nmb = (nm + 3) / 4;
-  const int mt_idx = (blk % nmb) * 4 + (jb >> 3);
-  const int nt_idx = ((blk / nmb) * 8 + (jb & 7)) * 8 + xcd;
+  const int bnb = 32 / bm, jb = j & 31, blk = j >> 5, nmb = (nm + bm - 1) / bm;
+  const int mt_idx = (blk % nmb) * bm + jb / bnb;
+  const int nt_idx = ((blk / nmb) * bnb + jb % bnb) * 8 + xcd;
   if (mt_idx >= nm || nt_idx >= nn) return;  // padding of the grid to whole blocks
   const int m0 = mt_idx * kGemmTile, n0 = nt_idx * kGemmTile;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -557,13 +557,15 @@ hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const 
   if (dtype == EAGLE_BF16 && rows >= kGemmMinRows) {
     const int nm = (rows + kGemmTile - 1) / kGemmTile, nn = lm_gemm_ntiles(V);
     ntiles = nn;
-    const int grid = ((nm + 3) / 4 * 4) * ((nn + 63) / 64 * 64);  // whole 4 x 8 blocks on each of 8 XCDs
+    // blocks of bm row tiles x 32/bm vocab tiles per XCD (16 x 2 measured best at 16 row tiles)
+    const int bm = nm >= 16 ? 16 : nm >= 8 ? 8 : 4, bn = 32 / bm;
+    const int grid = ((nm + bm - 1) / bm * bm) * ((nn + 8 * bn - 1) / (8 * bn) * (8 * bn));
     const size_t lds = 0;
     if (w_layout == EAGLE_W_PACKED)
-      lmhead_gemm_kernel<true><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, (const uint16_t*)x,
+      lmhead_gemm_kernel<true><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
                                                        (const uint16_t*)w, logits, ws_part, status);
     else
-      lmhead_gemm_kernel<false><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, (const uint16_t*)x,
+      lmhead_gemm_kernel<false><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
                                                         (const uint16_t*)w, logits, ws_part, status);
   } else if (dtype == EAGLE_BF16) {
     dim3 grid(ntiles, lm_mtiles(rows));
