@@ -55,8 +55,19 @@ def round_bytes(cfg, prefix_total):
     return draft + kv + tree + lmhead_bytes(cfg, rows)
 
 
+LMHEAD_KERNEL_START = "__global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel("
+
+
 def source_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    """Hash of the streaming LM-head kernel's source text (its template line
+    through the closing brace), so that edits elsewhere in the file do not
+    invalidate counters taken on an unchanged kernel."""
+    text = open(path, encoding="utf-8").read()
+    a = text.find(LMHEAD_KERNEL_START)
+    if a < 0:
+        return None
+    b = text.find("\n}\n", a)
+    return hashlib.sha256(text[a:b + 3].encode()).hexdigest()[:16]
 
 
 def read_traffic():
@@ -69,7 +80,8 @@ def read_traffic():
         if "=" in line and not line.startswith("#"):
             k, v = line.split("=", 1)
             kv[k.strip()] = v.strip()
-    if kv.get("source_sha256_16") != source_hash(LMHEAD_SRC):
+    h = source_hash(LMHEAD_SRC)
+    if h is None or kv.get("source_sha256_16") != h:
         return None
     try:
         return float(kv["hbm_bytes_per_launch"])
