@@ -46,6 +46,37 @@ struct Rec {
   int arg;
 };
 
+// Reductions over the 16 lanes of a DPP row (the lanes sharing one output row
+// of an MFMA tile) with DPP moves instead of LDS-routed shuffles: swap within
+// pairs, within quads, mirror within halves, mirror within the row.  Every
+// step pairs each lane with a distinct partner of the other half of its
+// current group, so all 16 lanes end with the same result.
+template <int CTRL>
+EDEV int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+EDEV float dpp_f(float v) { return __int_as_float(dpp_i<CTRL>(__float_as_int(v))); }
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
+template <int CTRL>
+EDEV void argmax_step(float& z, int& a) {
+  const float z2 = dpp_f<CTRL>(z);
+  const int a2 = dpp_i<CTRL>(a);
+  if (beats(z2, a2, z, a)) { z = z2; a = a2; }
+}
+EDEV void row16_argmax(float& z, int& a) {
+  argmax_step<kDppXor1>(z, a);
+  argmax_step<kDppXor2>(z, a);
+  argmax_step<kDppHalfMirror>(z, a);
+  argmax_step<kDppMirror>(z, a);
+}
+EDEV float row16_sum(float s) {
+  s += dpp_f<kDppXor1>(s);
+  s += dpp_f<kDppXor2>(s);
+  s += dpp_f<kDppHalfMirror>(s);
+  s += dpp_f<kDppMirror>(s);
+  return s;
+}
+
 EDEV void rec_merge(Rec& a, const Rec& b) {
   if (b.tmax == kNegInf) {
     // nothing to add to the sum; argmax still merges below
@@ -196,13 +227,8 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
         }
         acc[mt][t][i] = (n < V) ? z : kNegInf;
       }
-      // reduce over the 16 lanes sharing this row (xor 1..8 keeps grp)
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float z2 = __shfl_xor(zm, o);
-        const int a2 = __shfl_xor(ai, o);
-        if (beats(z2, a2, zm, ai)) { zm = z2; ai = a2; }
-      }
+      // reduce over the 16 lanes sharing this row (one DPP row)
+      row16_argmax(zm, ai);
       const float tmax = zm / Tp;  // division is monotone: max z/T' = fl(max z / T')
       // sum of exp(z/T' - tmax) as exp2(z * (log2e/T') - tmax * log2e): one
       // FMA and the hardware exp2 per logit (exp2(-inf) = 0)
@@ -212,8 +238,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
 #pragma unroll
         for (int t = 0; t < NT; ++t) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][t][i], c, -off));
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+      s = row16_sum(s);
       if (col == 0) wrec[wq][r] = Rec{zm == kNegInf ? kNegInf : tmax, s, zm, ai};
     }
   }
@@ -435,12 +460,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         }
         zv[nt] = z;
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        const float z2 = __shfl_xor(zm, o);
-        const int a2 = __shfl_xor(ai, o);
-        if (beats(z2, a2, zm, ai)) { zm = z2; ai = a2; }
-      }
+      row16_argmax(zm, ai);
       const float tmax = zm / Tp;
       float s = 0.f;
       if (zm != kNegInf) {
@@ -448,8 +468,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #pragma unroll
         for (int nt = 0; nt < 8; ++nt) s += __builtin_amdgcn_exp2f(fmaf(zv[nt], cc, -off));
       }
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) s += __shfl_xor(s, o);
+      s = row16_sum(s);
       if (col == 0) hrec[wn][r] = Rec{zm == kNegInf ? kNegInf : tmax, s, zm, ai};
     }
   }
