@@ -36,7 +36,10 @@
 // is needed.  Two banks alternate by step parity, so a workgroup can publish
 // step t+1 while slower ones still read step t.  The partial's value is the
 // top 40 bits of its fp64 (28-bit mantissa); every workgroup sums the G
-// decoded values in index order, so all agree bit for bit.  Spins are bounded:
+// decoded values in index order, so all agree bit for bit.  Each workgroup
+// (1024 threads) first copies the request's tree metadata (slots, pool tokens
+// and flat indices, row statistics, uniforms) to LDS, so the walk's serial
+// steps read LDS rather than global memory.  Spins are bounded:
 // a timeout sets EAGLE_STATUS_SYNC_TIMEOUT and the walk continues.
 #include "common.h"
 #include "kernels.h"
@@ -45,7 +48,7 @@ namespace eagle {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
 constexpr double kTie = 1e-6;
 constexpr int kSpinMax = 1 << 18;  // polls per wait (a fraction of a second)
@@ -191,7 +194,12 @@ EDEV double group_reduce(const Rows& R, double s, Group& gr, Smem& sm, int* time
   if (wave == 0) {
     const uint64_t tag = tag_of(gr.epoch, gr.step);
     uint64_t* bank = gr.mb->bank[gr.step & 1];
-    if (lane == 0) publish(bank + gr.g, tag | encode_val((sm.red[0] + sm.red[1]) + (sm.red[2] + sm.red[3])));
+    if (lane == 0) {
+      double part = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) part += sm.red[w];
+      publish(bank + gr.g, tag | encode_val(part));
+    }
     double v = 0.0;
     if (lane < gr.G) {
       v = decode_val(await_tag(bank + lane, tag, timed_out));
@@ -341,7 +349,8 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     const int32_t* __restrict__ targmax, const float* __restrict__ dlog, const float* __restrict__ sstats,
     const float* __restrict__ uniforms, Mailbox* __restrict__ mail, int32_t* accept_len, int32_t* accept_path,
     int32_t* committed, int32_t* n_committed, int32_t* near_tie, int32_t* status) {
-  extern __shared__ __attribute__((aligned(16))) float2 tcache[];  // [cache_tokens] when the slice fits
+  // dynamic LDS: [cache_tokens] token cache, then the request's tree metadata
+  extern __shared__ __attribute__((aligned(16))) float2 tcache[];
   __shared__ Smem sm;
   __shared__ int ties, timed_out;
   __shared__ int path[EAGLE_MAX_DEPTH + 1];
@@ -356,10 +365,6 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
   const float Tp = greedy ? 1.f : T;
   const int32_t* ntok = node_tok + (size_t)b * N;
   const int32_t* npar = node_parent + (size_t)b * N;
-  const int32_t* nslot = node_slot + (size_t)b * N;
-  const int32_t* ptok = pool_tok + (size_t)b * S * k;
-  const int32_t* pflat = pool_flat + (size_t)b * S * k;
-  const float* U = uniforms + (size_t)b * N * (k + 1);
   if (tid == 0) { ties = 0; timed_out = 0; npath = 0; ncomm = 0; cur_u = 0; zero_resid = 0; }
   __syncthreads();
 
@@ -390,38 +395,71 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     gr.step = 0;
     gr.cache = cache_tokens >= span ? tcache : nullptr;
     gr.cstate = 0;
+    // The request's tree metadata, copied to LDS once (after the token cache):
+    // node slots, pool tokens and flat indices, row statistics, uniforms.
+    const int nmeta = N + 2 * S * k + 2 * N + 2 * S + N * (k + 1);
+    int* m_slot = reinterpret_cast<int*>(tcache + cache_tokens);
+    int* m_ptok = m_slot + N;
+    int* m_pflat = m_ptok + S * k;
+    float* m_tst = reinterpret_cast<float*>(m_pflat + S * k);
+    float* m_sst = m_tst + 2 * N;
+    float* m_U = m_sst + 2 * S;
+    // four entries per thread in flight at a time (one address each, by range)
+    for (int i0 = tid; i0 < nmeta; i0 += 4 * kThreads) {
+      int v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + r * kThreads;
+        const int32_t* src;
+        if (i < N) src = node_slot + (size_t)b * N + i;
+        else if (i < N + S * k) src = pool_tok + (size_t)b * S * k + (i - N);
+        else if (i < N + 2 * S * k) src = pool_flat + (size_t)b * S * k + (i - N - S * k);
+        else if (i < 3 * N + 2 * S * k)
+          src = reinterpret_cast<const int32_t*>(tstats) + (size_t)b * N * 2 + (i - N - 2 * S * k);
+        else if (i < 3 * N + 2 * S * k + 2 * S)
+          src = reinterpret_cast<const int32_t*>(sstats) + (size_t)b * S * 2 + (i - 3 * N - 2 * S * k);
+        else
+          src = reinterpret_cast<const int32_t*>(uniforms) + (size_t)b * N * (k + 1) + (i - 3 * N - 2 * S * k - 2 * S);
+        v[r] = i < nmeta ? *src : 0;
+      }
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        if (i0 + r * kThreads < nmeta) m_slot[i0 + r * kThreads] = v[r];
+    }
     if (tid == 0) {  // retire this workgroup's stale words from earlier calls
       const uint64_t reset = tag_of(gr.epoch, 1023);
       publish(&gr.mb->bank[0][g], reset);
       publish(&gr.mb->bank[1][g], reset);
     }
+    __syncthreads();
     for (int step = 0; step <= D; ++step) {
-      if (tid == 0) cur_slot = nslot[cur_u];
+      if (tid == 0) cur_slot = m_slot[cur_u];
       __syncthreads();
       const int u = cur_u, slot = cur_slot;
       gr.cstate = 0;  // a new node: the token cache is refilled by its first pass
       Rows R;
       R.zp = tlog + ((size_t)b * N + u) * V;
       R.Tp = Tp;
-      R.Mp = tstats[((size_t)b * N + u) * 2];
-      R.invSp = 1.0 / (double)tstats[((size_t)b * N + u) * 2 + 1];
+      R.Mp = m_tst[2 * u];
+      R.invSp = 1.0 / (double)m_tst[2 * u + 1];
       R.zq = nullptr;
       R.Mq = 0.f;
       R.invSq = 0.0;
+      const float* Uu = m_U + u * (k + 1);
       if (slot < 0 || slot >= S) {
         // never expanded: bonus token from the target
         group_reduce(R, 0.0, gr, sm, &timed_out);
-        const int y = group_draw(R, 0.0, 0, (double)U[(size_t)u * (k + 1) + k], gr, sm, V, &ties, &timed_out);
+        const int y = group_draw(R, 0.0, 0, (double)Uu[k], gr, sm, V, &ties, &timed_out);
         if (g == 0 && tid == 0) comm[ncomm++] = y;
         break;
       }
       R.zq = dlog + ((size_t)b * S + slot) * V;
-      R.Mq = sstats[((size_t)b * S + slot) * 2];
-      R.invSq = 1.0 / (double)sstats[((size_t)b * S + slot) * 2 + 1];
+      R.Mq = m_sst[2 * slot];
+      R.invSq = 1.0 / (double)m_sst[2 * slot + 1];
       // The node's k children, loaded once (one thread each).  An id out of
       // range is flagged and scored as token 0.
       if (tid < k) {
-        const int x = ptok[(size_t)slot * k + tid];
+        const int x = m_ptok[slot * k + tid];
         const bool ok = x >= 0 && x < V;
         const int xc = ok ? x : 0;
         const float zpx = R.zp[xc], zqx = R.zq[xc];
@@ -447,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
             if (qx > 0.0 && st_R > 0.0) ratio = num * st_R / (st_Z * qx);
             else ratio = num > 0.0 ? __builtin_huge_val() : 0.0;
             const double a = ratio < 1.0 ? ratio : 1.0;
-            const double uu = (double)U[(size_t)u * (k + 1) + j];
+            const double uu = (double)Uu[j];
             if (fabs(uu - a) < kTie) ++ties;
             if (uu < a) acc_j = j;
           }
@@ -480,9 +518,9 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       }
       if (acc_j >= 0) {
         if (tid == 0) {
-          const int x = ptok[(size_t)slot * k + acc_j];
+          const int x = m_ptok[slot * k + acc_j];
           comm[ncomm++] = x;
-          const int f = pflat[(size_t)slot * k + acc_j];
+          const int f = m_pflat[slot * k + acc_j];
           if (f > 0 && f < N && npath < D) {
             path[npath++] = f;
             cur_u = f;
@@ -499,7 +537,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       // was not at st_s (zero-residual case), redo it.
       s_fin = st_s;
       if (stale) group_reduce(R, s_fin, gr, sm, &timed_out);
-      const int y = group_draw(R, s_fin, ntried, (double)U[(size_t)u * (k + 1) + k], gr, sm, V, &ties, &timed_out);
+      const int y = group_draw(R, s_fin, ntried, (double)Uu[k], gr, sm, V, &ties, &timed_out);
       if (g == 0 && tid == 0) comm[ncomm++] = y;
       break;
     }
@@ -521,6 +559,13 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
   }
 }
 
+// Largest dynamic LDS of one workgroup: a full token cache plus the metadata
+// of the largest tree (N = 256 nodes, pool 4096, 241 slots, k = 16).
+size_t accept_lds_max() {
+  return (size_t)kCacheMax * sizeof(float2) +
+         (size_t)(3 * EAGLE_MAX_NODES + 2 * EAGLE_MAX_POOL + 2 * 241 + EAGLE_MAX_NODES * (EAGLE_MAX_TOPK + 1)) * 4;
+}
+
 }  // namespace
 
 hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32_t* node_tok,
@@ -539,7 +584,7 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
   if (dev < 0 || dev >= 64) dev = 0;
   if (capacity[dev] == 0) {
     int per_cu = 0, cus = 0;
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_kernel, kThreads, kCacheMax * sizeof(float2));
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_kernel, kThreads, accept_lds_max());
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
@@ -553,7 +598,9 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
   // token cache: the slice's exponential terms stay in LDS across the passes at a node
   const int span = ((V + G - 1) / G + 3) / 4 * 4;
   int cache_tokens = (!greedy && span <= kCacheMax) ? span : 0;
-  const size_t lds = (size_t)cache_tokens * sizeof(float2);
+  const int S = 1 + (D - 1) * k;
+  const size_t meta = greedy ? 0 : (size_t)(3 * N + 2 * S * k + 2 * S + N * (k + 1)) * 4;
+  const size_t lds = (size_t)cache_tokens * sizeof(float2) + meta;
   Mailbox* mb = static_cast<Mailbox*>(mail);
   for (int b0 = 0; b0 < B; b0 += per_launch) {
     const int nb = B - b0 < per_launch ? B - b0 : per_launch;
