@@ -250,7 +250,8 @@ def main():
         "round_hbm_fraction": round(rb / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "lmhead_bf16 (eagle_lmhead_softmax)", "bytes_per_launch": lm_b,
+                     "kernel": "eagle_lmhead_softmax: lmhead_bf16 + lm_finalize, HIP events on its stream",
+                     "bytes_per_launch": lm_b,
                      "avg_launch_ms": round(r["lm_ms"], 5)},
         "device_status": r["status"],
     }

@@ -47,6 +47,12 @@ EDEV int wave_sum_i(int v) {
   return v;
 }
 
+EDEV int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+
 // (key desc, idx asc) order.
 EDEV bool beats(float ka, int ia, float kb, int ib) { return ka > kb || (ka == kb && ia < ib); }
 EDEV bool beats_d(double ka, int ia, double kb, int ib) { return ka > kb || (ka == kb && ia < ib); }

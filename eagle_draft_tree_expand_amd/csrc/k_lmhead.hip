@@ -12,12 +12,17 @@
 // dimension.  For the skinny shapes of a verify round (one or a few 64-row
 // tiles) the kernel streams W exactly once from HBM: each lane loads its
 // B-operand fragments straight from global memory into registers, one 64-wide
-// hidden chunk ahead of the MFMAs, and reads the small X tile through L2/L1.
-// The two hidden halves are summed through LDS; the epilogue writes the fp32
-// logits and a per-(row, tile) record (max z/T', sum exp, max z, argmax); a
-// second small launch (one workgroup per row) merges the records into the row
-// statistics and the argmax.  fp32 kernel (lmhead_f32): one thread per two
-// vocab columns, same records.
+// hidden chunk ahead of the MFMAs; the X fragments of a chunk are loaded once
+// per workgroup and shared through LDS.  The two hidden halves are summed
+// through LDS; the epilogue writes the fp32 logits and a per-(row, tile)
+// record (max z/T', sum exp, max z, tile); a second small launch (one
+// workgroup per row) merges the records into the row statistics and finds the
+// argmax column.  The tiled GEMM kernel (lmhead_gemm, many rows) and the fp32
+// kernel (lmhead_f32, one thread per two vocab columns) write the same records
+// with the argmax column itself.
+
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -31,6 +36,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kKC = 64;              // hidden values per pipeline chunk (two MFMA k-steps)
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr int kXPad = kKC + 8;       // LDS row stride of the X chunk (bf16)
+// s_waitcnt immediate for lgkmcnt(0), other counters unconstrained
+constexpr int kLgkmWait0 = 0xF | (7 << 4) | (3 << 14);
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -91,6 +98,16 @@ EDEV void rec_merge(Rec& a, const Rec& b) {
   if (beats(b.zmax, b.arg, a.zmax, a.arg)) { a.zmax = b.zmax; a.arg = b.arg; }
 }
 
+// Row reductions for the streaming kernel's epilogue: max and sum over the 16
+// lanes of a DPP row.
+EDEV float row16_max(float v) {
+  v = fmaxf(v, dpp_f<kDppXor1>(v));
+  v = fmaxf(v, dpp_f<kDppXor2>(v));
+  v = fmaxf(v, dpp_f<kDppHalfMirror>(v));
+  v = fmaxf(v, dpp_f<kDppMirror>(v));
+  return v;
+}
+
 template <bool PACKED>
 __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H, int V, float Tp,
                                                                  const uint16_t* __restrict__ x,
@@ -99,6 +116,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
                                                                  int32_t* status) {
   constexpr int NT = 8;  // 16-column n-tiles per wave: 128 vocab columns
   __shared__ floatx4 xch[4][2][NT][64];  // accumulator exchange between the two hidden halves (64 KB)
+  __shared__ u32x4 xst[2][2][8][64];     // X staging: [stage][hidden half][fragment ks*4 + mt][lane] (32 KB)
   __shared__ Rec wrec[4][kLmTileM];
 
   const int ntiles = gridDim.x;
@@ -110,70 +128,98 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
   const int m0 = mt_idx * kLmTileM;
   const int n0 = nt_idx * kLmTileN + wq * (NT * 16);  // first vocab column of this wave
   const int nch = H / kKC;
-  const int c0 = kh * (nch / 2), c1 = kh ? nch : nch / 2;
+  const int c0 = kh * (nch / 2);
+  const int nsteps = nch / 2;  // hidden is a multiple of 128: both halves have nch/2 chunks
   const int ngroups = (V + 63) / 64;
 
   // Operand sources of this lane.  A = X rows m0 + mt*16 + col (clamped), k
-  // offset grp*8 within each 32-wide k-step.  B = W: row-major rows
-  // n0 + nt*16 + col (clamped), or the packed layout, where each 64-row group
-  // is one contiguous stream: chunk c, load j of group g is the 1 KB at
-  // ((g*nch + c)*8 + j)*512 elements, lane l reading its 16 bytes at l*8.
-  // Packed addresses are a wave-uniform base plus the lane's 16 bytes.
+  // offset grp*8 within each 32-wide k-step.  B = W: the packed layout, where
+  // each 64-row group is one contiguous stream (chunk c, load j of group g is
+  // the 1 KB at ((g*nch + c)*8 + j)*512 elements, lane l reading its 16 bytes
+  // at l*8), or row-major rows n0 + t*16 + col (clamped).
   const uint16_t* wq0 = w + (size_t)min(n0 / 64, ngroups - 1) * nch * 4096;      // this wave's first group
   const uint16_t* wq1 = w + (size_t)min(n0 / 64 + 1, ngroups - 1) * nch * 4096;  // and its second
   size_t wrow[PACKED ? 1 : NT];
 #pragma unroll
   for (int t = 0; t < (PACKED ? 1 : NT); ++t) wrow[t] = (size_t)min(n0 + t * 16 + col, V - 1) * H + grp * 8;
-  uint32_t xoff[4];
-#pragma unroll
-  for (int t = 0; t < 4; ++t) xoff[t] = (uint32_t)min(m0 + t * 16 + col, rows - 1) * (uint32_t)H + grp * 8;
   floatx4 acc[4][NT];
 #pragma unroll
   for (int a = 0; a < 4; ++a)
 #pragma unroll
     for (int b = 0; b < NT; ++b) acc[a][b] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+  // X goes through LDS: per step, the 8 A fragments (4 row tiles x 2 k-steps)
+  // of each hidden half are loaded once per workgroup, two by each of the four
+  // waves of that half, instead of by all four waves.  A fragment is stored
+  // in lane order (lane l's 16 bytes at l*16), so the reads are conflict-free.
+  // Two stages: step s writes stage s&1, which was last read at step s - 2,
+  // before every wave passed the barrier of step s - 1.
+  const int xj = wq * 2;  // this wave's fragments j = xj, xj + 1 (j = ks*4 + mt)
+  uint32_t xo[2];
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int j = xj + u;
+    xo[u] = (uint32_t)min(m0 + (j & 3) * 16 + col, rows - 1) * (uint32_t)H + grp * 8 + (j >> 2) * 32;
+  }
+
   // Every wave streams its 128 W rows over one half of the hidden dimension
-  // (no LDS, no barrier in the loop) and reads the small X tile through
-  // L2/L1, one 64-wide chunk ahead of its MFMAs in two register buffers.
-  // Loads are unconditional (chunk indices clamp at the end) so the pipeline
-  // counters stay exact.
-  u32x4 wa[2 * NT], wb[2 * NT], xa[8], xb[8];
-#define LM_LOAD(wbuf, xbuf, c)                                                                                     \
-  {                                                                                                               \
-    const int k0 = (c) * kKC;                                                                                     \
-    _Pragma("unroll") for (int j = 0; j < 2 * NT; ++j) {                                                          \
-      const int t = (j >> 3) * 4 + (j & 3), ks = (j >> 2) & 1;                                                    \
-      const uint16_t* src = PACKED ? (t < 4 ? wq0 : wq1) + ((size_t)(c) * 8 + ks * 4 + (t & 3)) * 512 + lane * 8  \
-                                   : w + wrow[PACKED ? 0 : t] + k0 + ks * 32;                                     \
-      wbuf[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));                                 \
-    }                                                                                                             \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                                 \
-      xbuf[j] = *reinterpret_cast<const u32x4*>(x + xoff[j & 3] + k0 + (j >> 2) * 32);                            \
-  }
-#define LM_COMPUTE(wbuf, xbuf)                                                                    \
-  _Pragma("unroll") for (int ks = 0; ks < 2; ++ks) {                                              \
-    _Pragma("unroll") for (int mt = 0; mt < 4; ++mt) {                                            \
-      B8 a;                                                                                       \
-      a.w = xbuf[ks * 4 + mt];                                                                    \
-      _Pragma("unroll") for (int t = 0; t < NT; ++t) {                                            \
-        B8 bb;                                                                                    \
-        bb.w = wbuf[(t >> 2) * 8 + ks * 4 + (t & 3)];                                             \
-        acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, bb.v, acc[mt][t], 0, 0, 0);     \
-      }                                                                                           \
-    }                                                                                             \
-  }
-  LM_LOAD(wa, xa, c0)
-  int c = c0;
-  for (; c + 1 < c1; c += 2) {
-    LM_LOAD(wb, xb, c + 1)
-    LM_COMPUTE(wa, xa)
-    LM_LOAD(wa, xa, min(c + 2, c1 - 1))
-    LM_COMPUTE(wb, xb)
-  }
-  if (c < c1) LM_COMPUTE(wa, xa)  // odd number of chunks in this half
-#undef LM_COMPUTE
-#undef LM_LOAD
+  // straight into registers.  One buffer of 16 fragments rotates: as soon as
+  // a fragment's four MFMAs of step s are issued, the load of the same
+  // fragment for step s + 1 goes out into its registers, so each load flies
+  // about one step ahead.  The last step issues no loads.
+  u32x4 wf[2 * NT], sx[2];
+  auto w_src = [&](int step, int j) -> const u32x4* {
+    const int c = c0 + step;
+    const int t = (j >> 3) * 4 + (j & 3), ks = (j >> 2) & 1;
+    const uint16_t* src = PACKED ? (t < 4 ? wq0 : wq1) + ((size_t)c * 8 + ks * 4 + (t & 3)) * 512 + lane * 8
+                                 : w + wrow[PACKED ? 0 : t] + c * kKC + ks * 32;
+    return reinterpret_cast<const u32x4*>(src);
+  };
+  auto x_src = [&](int step, int u) -> const u32x4* {
+    return reinterpret_cast<const u32x4*>(x + xo[u] + (c0 + step) * kKC);
+  };
+  // The prologue issues in the loop's order (X, then W; the scheduling
+  // barriers keep it), so the counter waits at the loop head, which must hold
+  // for the first iteration too, stay as loose as the loop's.
+  sx[0] = *x_src(0, 0);
+  sx[1] = *x_src(0, 1);
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < 2 * NT; ++j) wf[j] = __builtin_nontemporal_load(w_src(0, j));
+  __builtin_amdgcn_sched_barrier(0);
+  // One step: publish this wave's X fragments, barrier, then 64 MFMAs with A
+  // read from LDS.  The barrier is bare: a fenced one would also wait for the
+  // next step's loads, which must stay in flight.
+  auto step_body = [&](int step, bool more) __attribute__((always_inline)) {
+    xst[step & 1][kh][xj][lane] = sx[0];
+    xst[step & 1][kh][xj + 1][lane] = sx[1];
+    __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (more) {
+      sx[0] = *x_src(step + 1, 0);
+      sx[1] = *x_src(step + 1, 1);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      B8 a[4];
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) a[mt].w = xst[step & 1][kh][ks * 4 + mt][lane];
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        const int j = (t >> 2) * 8 + ks * 4 + (t & 3);
+        B8 bb;
+        bb.w = wf[j];
+#pragma unroll
+        for (int mt = 0; mt < 4; ++mt)
+          acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt].v, bb.v, acc[mt][t], 0, 0, 0);
+        if (more) wf[j] = __builtin_nontemporal_load(w_src(step + 1, j));
+      }
+    }
+  };
+  for (int st = 0; st + 1 < nsteps; ++st) step_body(st, true);
+  step_body(nsteps - 1, false);
 
   // Sum the two hidden halves through LDS: rows 0..31 end in the kh = 0
   // waves, rows 32..63 in the kh = 1 waves, which then share the epilogue.
@@ -205,44 +251,68 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
       for (int t = 0; t < NT; ++t) acc[mt][t] = acc[mt + 2][t] + xch[wq][mt][t][lane];
   }
 
-  // Epilogue: logits + per-row record over this wave's 128 columns, rows
-  // kh*32 + [0, 32).
-  bool bad = false;
+  // Epilogue: logits and one record per row over this wave's 128 columns,
+  // rows kh*32 + mt*16 + grp*4 + i.  Non-finite logits are caught by one FMA
+  // per value (z*0 is NaN exactly for inf and NaN); a wave that has any, or
+  // that crosses the vocabulary end, masks them to -inf before the statistics.
+  const bool full = n0 + NT * 16 <= V;
+  float chk = 0.f;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = kh * 32 + mt * 16 + grp * 4 + i;
-      const int m = m0 + r;
-      float zm = kNegInf;
-      int ai = kIdxNone;
+      const int m = m0 + kh * 32 + mt * 16 + grp * 4 + i;
 #pragma unroll
       for (int t = 0; t < NT; ++t) {
         const int n = n0 + t * 16 + col;
-        float z = acc[mt][t][i];
-        if (n < V) {
+        const float z = acc[mt][t][i];
+        if (full || n < V) {
           if (m < rows) logits[(size_t)m * V + n] = z;
-          if (!isfinite(z)) { bad = true; z = kNegInf; }
-          if (beats(z, n, zm, ai)) { zm = z; ai = n; }
+          chk = fmaf(z, 0.f, chk);
         }
-        acc[mt][t][i] = (n < V) ? z : kNegInf;
       }
-      // reduce over the 16 lanes sharing this row (one DPP row)
-      row16_argmax(zm, ai);
-      const float tmax = zm / Tp;  // division is monotone: max z/T' = fl(max z / T')
-      // sum of exp(z/T' - tmax) as exp2(z * (log2e/T') - tmax * log2e): one
-      // FMA and the hardware exp2 per logit (exp2(-inf) = 0)
-      float s = 0.f;
-      if (zm != kNegInf) {
-        const float c = kLog2e / Tp, off = tmax * kLog2e;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) s += __builtin_amdgcn_exp2f(fmaf(acc[mt][t][i], c, -off));
-      }
-      s = row16_sum(s);
-      if (col == 0) wrec[wq][r] = Rec{zm == kNegInf ? kNegInf : tmax, s, zm, ai};
     }
   }
-  if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
+  const bool bad = __ballot(chk != chk) != 0;
+  if (bad || !full) {
+    if (bad && lane == 0) set_status(status, EAGLE_STATUS_NONFINITE);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int t = 0; t < NT; ++t)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float z = acc[mt][t][i];
+          acc[mt][t][i] = (n0 + t * 16 + col < V && isfinite(z)) ? z : kNegInf;
+        }
+  }
+  // Per row: max (the record's zmax; max z/T' = fl(max z / T') since division
+  // by T' > 0 is monotone), then the sum of exp(z/T' - tmax) as
+  // exp2(z * (log2e/T') - tmax * log2e): one FMA and the hardware exp2 per
+  // value (exp2(-inf) = 0).  The record's arg names the tile, not the column:
+  // the row merge scans the winning tile for the first column holding the max.
+  const float cT = kLog2e / Tp;
+#pragma unroll
+  for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float zm = acc[mt][0][i];
+#pragma unroll
+      for (int t = 1; t < NT; ++t) zm = fmaxf(zm, acc[mt][t][i]);
+      zm = row16_max(zm);
+      const float tmax = zm / Tp;
+      float sum = 0.f;
+      if (zm != kNegInf) {
+        const float off = tmax * kLog2e;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) sum += __builtin_amdgcn_exp2f(fmaf(acc[mt][t][i], cT, -off));
+      }
+      sum = row16_sum(sum);
+      if (col == 0)
+        wrec[wq][kh * 32 + mt * 16 + grp * 4 + i] =
+            Rec{zm == kNegInf ? kNegInf : tmax, sum, zm, kLmArgTile | (nt_idx * kLmTileN)};
+    }
+  }
   __syncthreads();
   const int nrows = min(kLmTileM, rows - m0);
   if (tid < nrows) {
@@ -484,11 +554,13 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 }
 
 // One workgroup per row: merge the row's per-tile records (fp64 sum).
-__global__ __launch_bounds__(256) void lm_finalize_kernel(int rows, int ntiles, const float* __restrict__ part,
-                                                          float* __restrict__ row_stats, int32_t* __restrict__ row_argmax) {
+__global__ __launch_bounds__(256) void lm_finalize_kernel(int rows, int ntiles, int V, const float* __restrict__ part,
+                                                          const float* __restrict__ logits, float* __restrict__ row_stats,
+                                                          int32_t* __restrict__ row_argmax) {
   __shared__ float shf[4];
   __shared__ double shd[4];
   __shared__ int shi[4];
+  __shared__ int shc[4];
   const int m = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* pr = part + (size_t)m * ntiles * 4;
   float tm = kNegInf, zm = kNegInf;
@@ -519,10 +591,27 @@ __global__ __launch_bounds__(256) void lm_finalize_kernel(int rows, int ntiles, 
   s = wave_sum_d(s);
   if (lane == 0) shd[wave] = s;
   __syncthreads();
+  const double ssum = (shd[0] + shd[1]) + (shd[2] + shd[3]);
+  // A tile record names the first tile holding the row max (ties between
+  // tiles go to the lower one); its first column equal to that max is the
+  // argmax.  Non-finite logits never equal the (finite) max.
+  int arg = ba == kIdxNone ? 0 : ba;
+  if (ba != kIdxNone && (ba & kLmArgTile)) {
+    const int c0 = ba & ~kLmArgTile, c1 = min(c0 + kLmTileN, V);
+    int first = kIdxNone;
+    if (bz != kNegInf)
+      for (int n = c0 + tid; n < c1; n += 256)
+        if (logits[(size_t)m * V + n] == bz) { first = n; break; }
+    first = wave_min_i(first);
+    if (lane == 0) shc[wave] = first;
+    __syncthreads();
+    first = min(min(shc[0], shc[1]), min(shc[2], shc[3]));
+    arg = first == kIdxNone ? 0 : first;
+  }
   if (tid == 0) {
     row_stats[(size_t)m * 2] = M;
-    row_stats[(size_t)m * 2 + 1] = (float)((shd[0] + shd[1]) + (shd[2] + shd[3]));
-    row_argmax[m] = ba == kIdxNone ? 0 : ba;
+    row_stats[(size_t)m * 2 + 1] = (float)ssum;
+    row_argmax[m] = arg;
   }
 }
 
@@ -604,7 +693,7 @@ hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const 
   // A separate launch merges the per-tile records: the kernel boundary makes
   // every workgroup's records visible (an in-kernel agent-scope fence would
   // write back each XCD's whole L2 per workgroup).
-  lm_finalize_kernel<<<rows, 256, 0, st>>>(rows, ntiles, ws_part, row_stats, row_argmax);
+  lm_finalize_kernel<<<rows, 256, 0, st>>>(rows, ntiles, V, ws_part, logits, row_stats, row_argmax);
   e = hipGetLastError();
   if (e != hipSuccess || probs == nullptr) return e;
   const size_t total = (size_t)rows * V;

@@ -63,6 +63,9 @@ hipError_t launch_attention(int B, int n, int hq, int hkv, int head_dim, int max
 constexpr int kLmTileN = 512;            // vocab columns per workgroup (one stats record per row)
 constexpr int kLmTileM = 64;             // rows per workgroup
 constexpr int kLmThreads = 512;          // bf16: 4 column quarters x 2 hidden halves
+// Record arg of the streaming bf16 kernel: this bit plus the tile's first
+// column; the row merge finds the column by scanning that tile's logits.
+constexpr int kLmArgTile = 1 << 30;
 inline int lm_ntiles(int V) { return (V + kLmTileN - 1) / kLmTileN; }
 inline int lm_mtiles(int rows) { return (rows + kLmTileM - 1) / kLmTileM; }
 // Large row counts (many requests per round) take a tiled GEMM: 256 x 256
