@@ -197,6 +197,9 @@ int eagle_tree_attention(int32_t batch, int32_t n, int32_t hq, int32_t hkv, int3
  *      row_stats [rows, 2] fp32: (M, S) = (max_v z_v / T', sum_v exp(z_v/T' - M));
  *      row_argmax [rows] int32: argmax_v z_v, lowest id on ties;
  *      probs [rows, vocab] fp32 or NULL: exp(z/T' - M) / S when non-NULL.
+ * Status: NONFINITE (a NaN/Inf logit stays as computed in `logits` and counts
+ * as -inf in row_stats and row_argmax; a row with no finite logit gets
+ * M = -inf and argmax 0).
  * dtype EAGLE_BF16 needs hidden % 128 == 0; fp32 needs hidden <= 16384. */
 int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dtype,
                          const void* x, const void* w, int32_t w_layout, float temperature,

@@ -190,6 +190,65 @@ def test_lmhead_matches_oracle(rt, name, kw, T, packed):
     assert dev["status"] == 0
 
 
+# columns holding one duplicated W row (an exact tie for the row max); the
+# argmax is the lowest of them: across tiles, inside one tile, across the
+# boundary of two 512-column tiles, and in the ragged last tile
+TIE_CASES = [(2999, 700, 130), (300, 260), (512, 511), (2999, 2600)]
+
+
+@pytest.mark.parametrize("B", [1, 40])  # 15 rows: streaming kernel; 600 rows: tiled GEMM
+@pytest.mark.parametrize("cols", TIE_CASES)
+def test_lmhead_argmax_ties(rt, B, cols):
+    cfg = small_cfg("mid_bf16", V=3000, H=256, hq=2, B=B)
+    inp = synth.make_inputs(cfg)
+    rng = np.random.default_rng(11)
+    u = np.where(rng.random(cfg.H) < 0.5, -1.0, 1.0).astype(np.float32)
+    X = synth.bf16_round((0.1 * rng.standard_normal((cfg.B * cfg.N, cfg.H))).astype(np.float32) + u)
+    w = inp.w.copy()
+    for c in cols:
+        w[c] = 0.0625 * u  # exact in bf16: z = 16 + O(1) for every row, far above the other columns
+    inp.w = w
+    dr = rt.DeviceRound(cfg)
+    wts = rt.DeviceWeights(inp)
+    dr.x.copy_(torch.from_numpy(X).to(dr.x.dtype).view(dr.x.shape))
+    for T in (1.0, 0.0):
+        dr.lmhead(wts, T)
+        dev = dr.host()
+        lg = dev["logits"]
+        assert (lg[:, list(cols)] == lg[:, [cols[0]]]).all()   # the tie is exact on the device too
+        assert (dev["argmax"] == min(cols)).all(), (cols, dev["argmax"][:8])
+        st, _ = olm.row_stats(lg, T)
+        np.testing.assert_allclose(dev["stats"][:, 0], st[:, 0], rtol=1e-6)
+        np.testing.assert_allclose(dev["stats"][:, 1], st[:, 1], rtol=1e-5)
+        assert dev["status"] == 0
+
+
+def test_lmhead_nonfinite(rt):
+    """A W row that overflows fp32: the logit stays inf in `logits`, the status
+    flags it, and the statistics and argmax treat it as -inf."""
+    cfg = small_cfg("mid_bf16", V=3000, H=256, hq=2)
+    inp = synth.make_inputs(cfg)
+    rng = np.random.default_rng(12)
+    X = synth.bf16_round(np.abs(rng.standard_normal((cfg.B * cfg.N, cfg.H))).astype(np.float32) + 1.0)
+    w = inp.w.copy()
+    w[1234] = 3.0e38  # bf16-exact enough: every product overflows, the sum is +inf
+    w[1234] = synth.bf16_round(w[1234])
+    inp.w = w
+    dr = rt.DeviceRound(cfg)
+    wts = rt.DeviceWeights(inp)
+    dr.x.copy_(torch.from_numpy(X).to(dr.x.dtype).view(dr.x.shape))
+    dr.lmhead(wts, 1.0)
+    dev = dr.host()
+    lg = dev["logits"]
+    assert np.isposinf(lg[:, 1234]).all()
+    assert dev["status"] & 0x2
+    fin = np.where(np.isfinite(lg), lg, -np.inf)
+    st, am = olm.row_stats(fin, 1.0)
+    np.testing.assert_allclose(dev["stats"][:, 0], st[:, 0], rtol=1e-6)
+    np.testing.assert_allclose(dev["stats"][:, 1], st[:, 1], rtol=1e-5)
+    assert np.array_equal(dev["argmax"], am)
+
+
 def test_pack_layout(rt):
     """Packed weight = the documented permutation of the row-major weight, zero past vocab."""
     from eagle_draft_tree_expand_amd import ops
