@@ -23,6 +23,17 @@ EDEV uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// DPP moves inside a row of 16 lanes, instead of LDS-routed shuffles: swap
+// within pairs, within quads, mirror within halves of 8, mirror within the
+// row.  Applied in this order, each step pairs every lane with a distinct
+// partner in the other half of its current group of 2, 4, 8, 16 lanes, so a
+// reduction over such a group ends with the same result in all its lanes.
+template <int CTRL>
+EDEV int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
+template <int CTRL>
+EDEV float dpp_f(float v) { return __int_as_float(dpp_i<CTRL>(__float_as_int(v))); }
+constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
+
 EDEV float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -482,9 +482,10 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
   for (int d = 1; d <= D; ++d) {
     const int lo = layer_lo(d, k), n = layer_n(d, k), dl = d - 1;
     const uint64_t* L = lay + dl * LS;
-    // threads per node (a lane group of a power of two <= 16 that fits the block)
-    const int tpe = n * 16 <= nt ? 16 : n * 8 <= nt ? 8 : n * 4 <= nt ? 4 : n * 2 <= nt ? 2 : 1;
-    const int x = tid / tpe, part = tid & (tpe - 1);
+    // threads per node: a lane group of 2^lt <= 16 lanes that fits the block
+    const int lt = n * 16 <= nt ? 4 : n * 8 <= nt ? 3 : n * 4 <= nt ? 2 : n * 2 <= nt ? 1 : 0;
+    const int tpe = 1 << lt;
+    const int x = tid >> lt, part = tid & (tpe - 1);
     if (x < n) {
       const uint64_t K = L[x];
       const int n2 = (n + 1) >> 1;
@@ -494,7 +495,11 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
         const ulonglong2 w = reinterpret_cast<const ulonglong2*>(L)[y2];
         r += (w.x > K ? 1 : 0) + (w.y > K ? 1 : 0);
       }
-      for (int o = 1; o < tpe; o <<= 1) r += __shfl_xor(r, o);
+      // sum over the node's lane group (aligned, inside one DPP row)
+      if (lt >= 1) r += dpp_i<kDppXor1>(r);
+      if (lt >= 2) r += dpp_i<kDppXor2>(r);
+      if (lt >= 3) r += dpp_i<kDppHalfMirror>(r);
+      if (lt >= 4) r += dpp_i<kDppMirror>(r);
       const int e = lo + x;
       if (part == 0) {
         lrank[e] = r;

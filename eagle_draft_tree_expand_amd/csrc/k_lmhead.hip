@@ -54,16 +54,7 @@ struct Rec {
 };
 
 // Reductions over the 16 lanes of a DPP row (the lanes sharing one output row
-// of an MFMA tile) with DPP moves instead of LDS-routed shuffles: swap within
-// pairs, within quads, mirror within halves, mirror within the row.  Every
-// step pairs each lane with a distinct partner of the other half of its
-// current group, so all 16 lanes end with the same result.
-template <int CTRL>
-EDEV int dpp_i(int v) { return __builtin_amdgcn_update_dpp(0, v, CTRL, 0xF, 0xF, false); }
-template <int CTRL>
-EDEV float dpp_f(float v) { return __int_as_float(dpp_i<CTRL>(__float_as_int(v))); }
-constexpr int kDppXor1 = 0xB1, kDppXor2 = 0x4E, kDppHalfMirror = 0x141, kDppMirror = 0x140;
-
+// of an MFMA tile) with the DPP moves of common.h.
 template <int CTRL>
 EDEV void argmax_step(float& z, int& a) {
   const float z2 = dpp_f<CTRL>(z);
