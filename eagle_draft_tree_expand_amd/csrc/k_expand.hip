@@ -289,10 +289,11 @@ __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
   const int U = C * kExpUnitsPerChunk;
   const int UF = 2 + 2 * KP;
   const float* z = rows + (size_t)row * V;
-  const float* ub = units + (size_t)row * U * UF;
+  const float* ubg = units + (size_t)row * U * UF;
   double* xkey = reinterpret_cast<double*>(smem_raw);          // [kExpRescanCap]
   int* xidx = reinterpret_cast<int*>(xkey + kExpRescanCap);     // [kExpRescanCap]
   float* heads = reinterpret_cast<float*>(xidx + kExpRescanCap);  // [U] best key of each record
+  float* ub = heads + U;                                           // [U * UF] the row's records
 
   __shared__ double shd[4];
   __shared__ float shf[4];
@@ -302,51 +303,91 @@ __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
   __shared__ int n_cand;
   __shared__ float head_k;
 
-  // Row statistics and record heads.
+  // The row's records go to LDS in one coalesced copy; every later pass
+  // reads them there.
   if (tid == 0) { n_cand = 0; head_k = kNegInf; }
+  {
+    // UF is even, so the records are float2-aligned; eight loads per thread
+    // go out before their stores
+    const int n2 = U * UF / 2;
+    const float2* src = reinterpret_cast<const float2*>(ubg);
+    float2* dst = reinterpret_cast<float2*>(ub);
+    for (int base = 0; base < n2; base += 8 * kExpThreads) {
+      float2 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = base + j * kExpThreads + tid;
+        if (i < n2) v[j] = src[i];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int i = base + j * kExpThreads + tid;
+        if (i < n2) dst[i] = v[j];
+      }
+    }
+  }
+  __syncthreads();
+
+  // Row statistics and record heads.
   float lm = kNegInf;
   for (int x = tid; x < U; x += kExpThreads) {
     lm = fmaxf(lm, ub[(size_t)x * UF]);
     heads[x] = __float_as_int(ub[(size_t)x * UF + 2 + KP]) == kIdxNone ? kNegInf : ub[(size_t)x * UF + 2];
   }
-  const float M = block_max_256(lm, shf);
+  const float M = block_max_256(lm, shf);  // its barriers also publish heads[]
   double ls = 0.0;
   if (M != kNegInf)
     for (int x = tid; x < U; x += kExpThreads) {
       const float um = ub[(size_t)x * UF], us = ub[(size_t)x * UF + 1];
       if (us > 0.f) ls += (double)us * exp((double)um - (double)M);
     }
-  const double Sd = block_sum_256(ls, shd);
 
   // The k-th best record head bounds the k-th best fp32 key from below (k
   // records each hold a key at least that large).  Fewer than k records: no
-  // bound.
-  for (int x = tid; x < U; x += kExpThreads) {
-    const float h = heads[x];
-    int r = 0;
-    for (int y = 0; y < U; ++y) {
-      const float w = heads[y];
-      r += (w > h || (w == h && y < x)) ? 1 : 0;
+  // bound.  Each head's rank (count of better heads) is counted by a group
+  // of 2^lt lanes, so every lane has a short loop of independent LDS reads.
+  {
+    const int lt = U * 16 <= kExpThreads ? 4 : U * 8 <= kExpThreads ? 3 : U * 4 <= kExpThreads ? 2
+                 : U * 2 <= kExpThreads ? 1 : 0;
+    const int tpe = 1 << lt;
+    for (int base = 0; base < U * tpe; base += kExpThreads) {
+      const int q = base + tid, x = q >> lt, part = q & (tpe - 1);
+      if (x < U) {
+        const float h = heads[x];
+        int r = 0;
+#pragma unroll 16
+        for (int y = part; y < U; y += tpe) {
+          const float w = heads[y];
+          r += (w > h || (w == h && y < x)) ? 1 : 0;
+        }
+        if (lt >= 1) r += dpp_i<kDppXor1>(r);
+        if (lt >= 2) r += dpp_i<kDppXor2>(r);
+        if (lt >= 3) r += dpp_i<kDppHalfMirror>(r);
+        if (lt >= 4) r += dpp_i<kDppMirror>(r);
+        if (part == 0 && r == k - 1) head_k = h;
+      }
     }
-    if (r == k - 1) head_k = h;
   }
-  __syncthreads();
+  const double Sd = block_sum_256(ls, shd);  // its barriers also publish head_k
 
   // Candidates: every record entry whose fp32 key can still reach the k-th
   // place.  Greedy keys are the logits themselves (exact); sampling keys are
   // within key_slack of the fp64 key, so the bound drops by twice the slack.
   const float Hk = head_k;
   const double thr = GREEDY ? (double)Hk : (double)Hk - 2.0 * key_slack(Hk);
-  const int ncand0 = U * KP;
-  for (int c = tid; c < ncand0; c += kExpThreads) {
-    const int x = c / KP, r = c - x * KP;
-    const int id = __float_as_int(ub[(size_t)x * UF + 2 + KP + r]);
-    const float ka = ub[(size_t)x * UF + 2 + r];
-    if (id != kIdxNone && id >= 0 && id < V && (double)ka >= thr) {
-      const int slot = atomicAdd(&n_cand, 1);
-      if (slot < kExpRescanCap) {
-        xidx[slot] = id;
-        xkey[slot] = (double)ka;
+  // A record's keys are sorted (key desc, idx asc), so its candidates are a
+  // prefix: one thread per record walks it until a key falls below the bound.
+  for (int x = tid; x < U; x += kExpThreads) {
+    for (int r = 0; r < KP; ++r) {
+      const float ka = ub[(size_t)x * UF + 2 + r];
+      if ((double)ka < thr) break;
+      const int id = __float_as_int(ub[(size_t)x * UF + 2 + KP + r]);
+      if (id != kIdxNone && id >= 0 && id < V) {
+        const int slot = atomicAdd(&n_cand, 1);
+        if (slot < kExpRescanCap) {
+          xidx[slot] = id;
+          xkey[slot] = (double)ka;
+        }
       }
     }
   }
@@ -642,7 +683,8 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int U = C * kExpUnitsPerChunk;
-  const size_t sm2 = (size_t)kExpRescanCap * (sizeof(double) + sizeof(int)) + (size_t)U * sizeof(float);
+  const size_t sm2 = (size_t)kExpRescanCap * (sizeof(double) + sizeof(int)) +
+                     (size_t)U * (1 + exp_unit_floats(k)) * sizeof(float);
   if (greedy)
     expand_merge_kernel<true><<<B * S, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, ws_units,
                                                              pool_tok, pool_q, slot_stats, status);
