@@ -94,7 +94,7 @@ size_t eagle_workspace_size(const eagle_tree_params* p, int32_t hq, int32_t hkv,
     if (a > need) need = a;
   }
   if (hidden > 0) {
-    const size_t l = lm_ws_bytes(B * N, V);
+    const size_t l = lm_ws_bytes(B * N, V, hidden);
     if (l > need) need = l;
   }
   need = (need + 255) / 256 * 256;
@@ -165,7 +165,7 @@ int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dt
   if (!(temperature >= 0.f) || !isfinite(temperature)) return EAGLE_ERR_SHAPE;
   if (!x || !w || !logits || !row_stats || !row_argmax || !ws) return EAGLE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w)) return EAGLE_ERR_ALIGN;
-  if (ws_bytes < kCounterBytes + lm_ws_bytes(rows, vocab)) return EAGLE_ERR_WORKSPACE;
+  if (ws_bytes < kCounterBytes + lm_ws_bytes(rows, vocab, hidden)) return EAGLE_ERR_WORKSPACE;
   return launch_status(launch_lmhead(rows, hidden, vocab, dtype, w_layout, x, w, temperature, logits, row_stats,
                                      row_argmax, probs, stage_area(ws), dev_status, (hipStream_t)stream));
 }

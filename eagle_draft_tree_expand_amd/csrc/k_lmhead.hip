@@ -104,7 +104,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
                                                                  const uint16_t* __restrict__ x,
                                                                  const uint16_t* __restrict__ w,
                                                                  float* __restrict__ logits, float* __restrict__ part,
-                                                                 int32_t* status) {
+                                                                 int32_t* status, int hk, float* __restrict__ partial) {
   constexpr int NT = 8;  // 16-column n-tiles per wave: 128 vocab columns
   __shared__ floatx4 xch[4][2][NT][64];  // accumulator exchange between the two hidden halves (64 KB)
   __shared__ u32x4 xst[2][2][8][64];     // X staging: [stage][hidden half][fragment ks*4 + mt][lane] (32 KB)
@@ -119,8 +119,11 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
   const int m0 = mt_idx * kLmTileM;
   const int n0 = nt_idx * kLmTileN + wq * (NT * 16);  // first vocab column of this wave
   const int nch = H / kKC;
-  const int c0 = kh * (nch / 2);
-  const int nsteps = nch / 2;  // hidden is a multiple of 128: both halves have nch/2 chunks
+  // hidden slice blockIdx.z of hk values (hk = H without a split; a multiple
+  // of 128, so both halves have the same number of chunks)
+  const int nchs = hk / kKC;
+  const int c0 = blockIdx.z * nchs + kh * (nchs / 2);
+  const int nsteps = nchs / 2;
   const int ngroups = (V + 63) / 64;
 
   // Operand sources of this lane.  A = X rows m0 + mt*16 + col (clamped), k
@@ -240,6 +243,24 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[mt][t] = acc[mt + 2][t] + xch[wq][mt][t][lane];
+  }
+
+  // A slice of a split hidden dimension: its partial logits, summed and
+  // turned into records by the combine launch.
+  if (partial != nullptr) {
+    float* pz = partial + (size_t)blockIdx.z * rows * V;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + kh * 32 + mt * 16 + grp * 4 + i;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int n = n0 + t * 16 + col;
+          if (m < rows && n < V) pz[(size_t)m * V + n] = acc[mt][t][i];
+        }
+      }
+    return;
   }
 
   // Epilogue: logits and one record per row over this wave's 128 columns,
@@ -544,6 +565,52 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   }
 }
 
+// Split hidden dimension: one workgroup per (512-column tile, row) sums the
+// KS partial logits in slice order, writes the logits and the tile's record
+// (the streaming kernel's: max z/T', sum exp, max z, tile).
+__global__ __launch_bounds__(256) void lm_combine_kernel(int rows, int V, int KS, float Tp,
+                                                         const float* __restrict__ partial, float* __restrict__ logits,
+                                                         float* __restrict__ part, int32_t* status) {
+  __shared__ float shm[4], shs[4];
+  const int tile = blockIdx.x, m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = tile * kLmTileN;
+  float z[2];
+  bool bad = false;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = n0 + h * 256 + tid;
+    float v = kNegInf;
+    if (n < V) {
+      float acc = 0.f;
+      for (int kz = 0; kz < KS; ++kz) acc += partial[((size_t)kz * rows + m) * V + n];
+      logits[(size_t)m * V + n] = acc;
+      v = acc;
+      if (!isfinite(v)) { bad = true; v = kNegInf; }
+    }
+    z[h] = v;
+  }
+  if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
+  float zm = wave_max(fmaxf(z[0], z[1]));
+  if (lane == 0) shm[wave] = zm;
+  __syncthreads();
+  zm = fmaxf(fmaxf(shm[0], shm[1]), fmaxf(shm[2], shm[3]));
+  const float tmax = zm / Tp;
+  float sum = 0.f;
+  if (zm != kNegInf) {
+    const float cT = kLog2e / Tp, off = tmax * kLog2e;
+    sum = __builtin_amdgcn_exp2f(fmaf(z[0], cT, -off)) + __builtin_amdgcn_exp2f(fmaf(z[1], cT, -off));
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) shs[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    const float s = (shs[0] + shs[1]) + (shs[2] + shs[3]);
+    float* pr = part + ((size_t)m * gridDim.x + tile) * 4;
+    *reinterpret_cast<float4*>(pr) =
+        make_float4(zm == kNegInf ? kNegInf : tmax, s, zm, __int_as_float(kLmArgTile | n0));
+  }
+}
+
 // One workgroup per row: merge the row's per-tile records (fp64 sum).
 __global__ __launch_bounds__(256) void lm_finalize_kernel(int rows, int ntiles, int V, const float* __restrict__ part,
                                                           const float* __restrict__ logits, float* __restrict__ row_stats,
@@ -667,13 +734,20 @@ hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const 
       lmhead_gemm_kernel<false><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
                                                         (const uint16_t*)w, logits, ws_part, status);
   } else if (dtype == EAGLE_BF16) {
-    dim3 grid(ntiles, lm_mtiles(rows));
+    const int ks = lm_ksplit(rows, V, H);
+    float* partial = ks > 1 ? ws_part + lm_rec_floats(rows, V) : nullptr;
+    dim3 grid(ntiles, lm_mtiles(rows), ks);
     if (w_layout == EAGLE_W_PACKED)
       lmhead_bf16_kernel<true><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
-                                                     ws_part, status);
+                                                     ws_part, status, H / ks, partial);
     else
       lmhead_bf16_kernel<false><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
-                                                      ws_part, status);
+                                                      ws_part, status, H / ks, partial);
+    if (ks > 1) {
+      hipError_t e0 = hipGetLastError();
+      if (e0 != hipSuccess) return e0;
+      lm_combine_kernel<<<dim3(ntiles, rows), 256, 0, st>>>(rows, V, ks, Tp, partial, logits, ws_part, status);
+    }
   } else {
     dim3 grid(ntiles, rows);
     lmhead_f32_kernel<<<grid, 256, (size_t)H * sizeof(float), st>>>(rows, H, V, Tp, (const float*)x,

@@ -73,7 +73,22 @@ inline int lm_mtiles(int rows) { return (rows + kLmTileM - 1) / kLmTileM; }
 constexpr int kGemmTile = 256;
 constexpr int kGemmMinRows = 193;        // from 4 row tiles of the streaming kernel on
 inline int lm_gemm_ntiles(int V) { return (V + kGemmTile - 1) / kGemmTile; }
-inline size_t lm_ws_bytes(int rows, int V) { return (size_t)rows * lm_gemm_ntiles(V) * 4 * sizeof(float); }
+// Small vocabularies leave most CUs idle with one workgroup per (row tile,
+// vocab tile): the bf16 streaming kernel then splits the hidden dimension over
+// KS workgroups (slices of H/KS, a multiple of 128) that write fp32 partial
+// logits; a combine launch sums them in a fixed order.
+inline int lm_ksplit(int rows, int V, int H) {
+  if (rows >= kGemmMinRows) return 1;
+  int ks = 256 / (lm_ntiles(V) * lm_mtiles(rows));
+  if (ks > 8) ks = 8;
+  while (ks > 1 && H % (ks * 128) != 0) --ks;
+  return ks < 1 ? 1 : ks;
+}
+inline size_t lm_rec_floats(int rows, int V) { return (size_t)rows * lm_gemm_ntiles(V) * 4; }
+inline size_t lm_ws_bytes(int rows, int V, int H) {
+  const int ks = lm_ksplit(rows, V, H);
+  return (lm_rec_floats(rows, V) + (ks > 1 ? (size_t)ks * rows * V : 0)) * sizeof(float);
+}
 hipError_t launch_lmhead(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,
                          float T, float* logits, float* row_stats, int32_t* row_argmax,
                          float* probs, float* ws_part, int32_t* status, hipStream_t st);

@@ -268,9 +268,10 @@ def test_pack_layout(rt):
         assert np.array_equal(units[u], ref)
 
 
-def test_lmhead_full_8b_sampled(rt):
-    """Full 8B LM head (61 x 4096 x 128256): sampled logits, stats invariants."""
-    cfg = synth.get_config("8b")
+@pytest.mark.parametrize("name", ["8b", "13b", "70b"])  # 13b/70b (vocab 32000): hidden split over workgroups
+def test_lmhead_full_sampled(rt, name):
+    """Full-size LM head (8b: 61 x 4096 x 128256): sampled logits, stats invariants."""
+    cfg = synth.get_config(name)
     inp = synth.make_inputs(cfg)
     rng = np.random.default_rng(8)
     X = synth.bf16_round((0.05 * rng.standard_normal((cfg.N, cfg.H))).astype(np.float32))
