@@ -384,6 +384,11 @@ AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, 
   sk = (sk + kKT - 1) / kKT * kKT;
   if (sk < 128) sk = 128;
   if (sk > 1024) sk = 1024;
+  // Few (request, kv head) pairs and long prefixes: 384-key splits measured
+  // best (13B- and 70B-shaped rounds at batch 1: 49 and 38 us against 69 and
+  // 48 us with the rule above); shorter splits write more partial rows, longer
+  // ones leave CUs idle.
+  if (per <= 64 && max_prefix > 2048) sk = 384;
   pl.split_keys = sk;
   pl.nsplit = (max_prefix + sk - 1) / sk;
   (void)head_dim;

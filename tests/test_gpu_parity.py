@@ -123,6 +123,8 @@ ATTN_CASES = [
     ("mid_bf16", dict(hq=16, hkv=1, m=20, H=2048), 2e-2),         # 336 rows: two row blocks
     ("mid_bf16", dict(hq=2, hkv=2, dh=64, H=128), 2e-2),          # head_dim 64
     ("mid_bf16", dict(L=(0, 0)), 2e-2),                           # empty prefix: tree only
+    ("mid_bf16", dict(L=(2100, 3000)), 2e-2),                     # long prefix: 384-key splits
+    ("mid_bf16", dict(hq=4, hkv=4, H=512, L=(2049, 2600)), 2e-2),  # MHA, long prefix
     ("mid_f32", {}, 1e-5),
     ("tiny", {}, 1e-5),
 ]
