@@ -23,6 +23,22 @@ EDEV uint16_t f32_to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// s_waitcnt immediate for lgkmcnt(0) (LDS operations done), other counters
+// unconstrained.
+constexpr int kLgkmWait0 = 0xF | (7 << 4) | (3 << 14);
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for
+// its global loads (a __syncthreads also waits for every load in flight, which
+// would drain a prefetch pipeline).  Callers wait for the global data they
+// publish through LDS themselves (the compiler does, before each LDS write of
+// loaded registers).
+EDEV void lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(kLgkmWait0);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // DPP moves inside a row of 16 lanes, instead of LDS-routed shuffles: swap
 // within pairs, within quads, mirror within halves of 8, mirror within the
 // row.  Applied in this order, each step pairs every lane with a distinct

@@ -83,21 +83,32 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
   // of each V^T row (no bank conflicts).
   constexpr int kPairs = (kKT / 2) * (DH / 8);                          // key-pair chunks per tile
   constexpr int kChunks = (kPairs + kAttnThreads - 1) / kAttnThreads;  // per thread
-  uint4 kreg[2 * kChunks], vreg[2 * kChunks];
-#define ATTN_LOAD_TILE(T0)                                                                   \
-  _Pragma("unroll") for (int i = 0; i < kChunks; ++i) {                                      \
-    const int x = tid + i * kAttnThreads, kp = x & 31, dc = (x >> 5) * 8;                    \
-    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                          \
-      const int key = (T0) + 2 * kp + h;                                                     \
-      kreg[2 * i + h] = make_uint4(0, 0, 0, 0);                                              \
-      vreg[2 * i + h] = make_uint4(0, 0, 0, 0);                                              \
-      if (x < kPairs && key < k_end) {                                                       \
-        kreg[2 * i + h] = *reinterpret_cast<const uint4*>(kbase + (size_t)key * kstride + dc); \
-        vreg[2 * i + h] = *reinterpret_cast<const uint4*>(vbase + (size_t)key * kstride + dc); \
-      }                                                                                      \
-    }                                                                                        \
+  // Two tiles in flight: register sets A and B alternate tile by tile.
+  uint4 kregA[2 * kChunks], vregA[2 * kChunks], kregB[2 * kChunks], vregB[2 * kChunks];
+  // K/V loads go through buffer resources whose range ends at the split's
+  // last key: keys past it read as zero, so every tile issues the same loads
+  // with no branches and the counter waits stay exact.
+  const int kbytes = k_end > k_begin ? (int)(((size_t)(k_end - 1) * kstride + DH) * 2) : 0;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, (short)0, kbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, kbytes, 0x00020000);
+#define ATTN_LOAD_TILE(T0, kreg, vreg)                                                         \
+  _Pragma("unroll") for (int i = 0; i < kChunks; ++i) {                                        \
+    const int x = tid + i * kAttnThreads, kp = x & 31, dc = (x >> 5) * 8;                      \
+    _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                            \
+      const uint32_t off = (uint32_t)(((size_t)((T0) + 2 * kp + h) * kstride + dc) * 2);       \
+      if (kPairs % kAttnThreads == 0 || x < kPairs) {                                          \
+        const auto kv = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);                 \
+        const auto vv = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);                 \
+        kreg[2 * i + h] = make_uint4(kv[0], kv[1], kv[2], kv[3]);                              \
+        vreg[2 * i + h] = make_uint4(vv[0], vv[1], vv[2], vv[3]);                              \
+      }                                                                                        \
+    }                                                                                          \
   }
-  if (k_begin < k_end) ATTN_LOAD_TILE(k_begin)  // first K/V tile in flight while Q loads
+  // the first two K/V tiles in flight while Q loads
+  if (k_begin < k_end) {
+    ATTN_LOAD_TILE(k_begin, kregA, vregA)
+    ATTN_LOAD_TILE(k_begin + kKT, kregB, vregB)
+  }
 
   // Query tiles of this wave.
   const int col = lane & 15, grp = lane >> 4;
@@ -128,8 +139,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
     for (int dt = 0; dt < DH / 16; ++dt) o[t][dt] = floatx4{0.f, 0.f, 0.f, 0.f};
   }
 
-  for (int t0 = k_begin; t0 < k_end; t0 += kKT) {
-    __syncthreads();
+  // One tile: its registers go to LDS between two barriers, the tile two
+  // ahead is loaded into the freed registers, then the wave's MFMAs.
+  auto stage_tile = [&](uint4* kreg, uint4* vreg) __attribute__((always_inline)) {
+    lds_barrier();  // every wave is done reading the previous tile
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
       const int x = tid + i * kAttnThreads, kp = x & 31, dc = (x >> 5) * 8;
@@ -142,9 +155,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
       for (int e = 0; e < 8; ++e)
         *reinterpret_cast<uint32_t*>(&Vts[(dc + e) * VPAD + 2 * kp]) = (uint32_t)v0[e] | ((uint32_t)v1[e] << 16);
     }
-    __syncthreads();
-    if (t0 + kKT < k_end) ATTN_LOAD_TILE(t0 + kKT)
-    if (!wave_active) continue;
+    lds_barrier();  // the tile is in LDS; the next tile's loads stay in flight
+  };
+  auto compute_tile = [&](int t0) __attribute__((always_inline)) {
     // Masking is needed only in the tree split and in a ragged last tile.
     const bool masked = tree || t0 + kKT > k_end;
     // S^T tiles of both query tiles: 64 keys x 16 queries each, lane holds
@@ -230,6 +243,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
         for (int t = 0; t < kQT; ++t)
           o[t][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.v, pb[t][beta].v, o[t][dt], 0, 0, 0);
       }
+    }
+  };
+  for (int t0 = k_begin; t0 < k_end; t0 += 2 * kKT) {
+    stage_tile(kregA, vregA);
+    ATTN_LOAD_TILE(t0 + 2 * kKT, kregA, vregA)
+    if (wave_active) compute_tile(t0);
+    if (t0 + kKT < k_end) {
+      stage_tile(kregB, vregB);
+      ATTN_LOAD_TILE(t0 + 3 * kKT, kregB, vregB)
+      if (wave_active) compute_tile(t0 + kKT);
     }
   }
 #undef ATTN_LOAD_TILE

@@ -36,8 +36,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 constexpr int kKC = 64;              // hidden values per pipeline chunk (two MFMA k-steps)
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr int kXPad = kKC + 8;       // LDS row stride of the X chunk (bf16)
-// s_waitcnt immediate for lgkmcnt(0), other counters unconstrained
-constexpr int kLgkmWait0 = 0xF | (7 << 4) | (3 << 14);
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
