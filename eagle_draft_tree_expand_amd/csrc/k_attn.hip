@@ -31,8 +31,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kKT = 64;            // keys per LDS tile
 constexpr int kQT = 2;             // 16-row query tiles per wave
-constexpr int kAttnThreads = 512;  // 8 waves
-constexpr int kRowsPerWG = 256;    // 8 waves x 2 tiles x 16 rows
 
 union B8 {
   bf16x8 v;
@@ -45,8 +43,10 @@ EDEV float* partial_row(float* ws, int b, int g, int hkv, int nsp1, int split, i
   return ws + ((((size_t)b * hkv + g) * nsp1 + split) * rows_pad + r) * (DH + 2);
 }
 
-template <int DH>
-__global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
+// NTH threads: 512 (8 waves, 256 query rows) or, for few rows, 256 (4 waves,
+// 128 rows), so that two workgroups share a CU and hide each other's loads.
+template <int DH, int NTH>
+__global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(512 / NTH))) void attn_split_bf16_kernel(
     int n, int hq, int hkv, int Lmax, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const int32_t* __restrict__ plen, const uint16_t* __restrict__ kt,
     const uint16_t* __restrict__ vt, const uint64_t* __restrict__ mask, float scale, float* __restrict__ ws,
@@ -57,11 +57,12 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kKT * KPAD];
   __shared__ __attribute__((aligned(16))) uint16_t Vts[DH * VPAD];
 
-  const int nrb = (rows + kRowsPerWG - 1) / kRowsPerWG;
+  constexpr int kRows = NTH / 64 * kQT * 16;  // query rows per workgroup
+  const int nrb = (rows + kRows - 1) / kRows;
   const int split = blockIdx.x, g = blockIdx.y / nrb, rb = blockIdx.y - g * nrb, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = hq / hkv;
-  const int row0 = rb * kRowsPerWG + wave * (kQT * 16);  // first query row of this wave
+  const int row0 = rb * kRows + wave * (kQT * 16);  // first query row of this wave
   const int W = (n + 63) >> 6;
   const bool tree = split == nsplit;
   const int L = min(max(plen[b], 0), Lmax);  // prefix lengths beyond the buffer are clamped
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
   // (key pair) words and the 32 threads of a chunk fill 128 contiguous bytes
   // of each V^T row (no bank conflicts).
   constexpr int kPairs = (kKT / 2) * (DH / 8);                          // key-pair chunks per tile
-  constexpr int kChunks = (kPairs + kAttnThreads - 1) / kAttnThreads;  // per thread
+  constexpr int kChunks = (kPairs + NTH - 1) / NTH;  // per thread
   // Two tiles in flight: register sets A and B alternate tile by tile.
   uint4 kregA[2 * kChunks], vregA[2 * kChunks], kregB[2 * kChunks], vregB[2 * kChunks];
   // K/V loads go through buffer resources whose range ends at the split's
@@ -93,10 +94,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vbase, (short)0, kbytes, 0x00020000);
 #define ATTN_LOAD_TILE(T0, kreg, vreg)                                                         \
   _Pragma("unroll") for (int i = 0; i < kChunks; ++i) {                                        \
-    const int x = tid + i * kAttnThreads, kp = x & 31, dc = (x >> 5) * 8;                      \
+    const int x = tid + i * NTH, kp = x & 31, dc = (x >> 5) * 8;                      \
     _Pragma("unroll") for (int h = 0; h < 2; ++h) {                                            \
       const uint32_t off = (uint32_t)(((size_t)((T0) + 2 * kp + h) * kstride + dc) * 2);       \
-      if (kPairs % kAttnThreads == 0 || x < kPairs) {                                          \
+      if (kPairs % NTH == 0 || x < kPairs) {                                          \
         const auto kv = __builtin_amdgcn_raw_buffer_load_b128(krs, off, 0, 0);                 \
         const auto vv = __builtin_amdgcn_raw_buffer_load_b128(vrs, off, 0, 0);                 \
         kreg[2 * i + h] = make_uint4(kv[0], kv[1], kv[2], kv[3]);                              \
@@ -145,7 +146,7 @@ __global__ __launch_bounds__(kAttnThreads) void attn_split_bf16_kernel(
     lds_barrier();  // every wave is done reading the previous tile
 #pragma unroll
     for (int i = 0; i < kChunks; ++i) {
-      const int x = tid + i * kAttnThreads, kp = x & 31, dc = (x >> 5) * 8;
+      const int x = tid + i * NTH, kp = x & 31, dc = (x >> 5) * 8;
       if (x >= kPairs) break;
       *reinterpret_cast<uint4*>(&Ks[(2 * kp) * KPAD + dc]) = kreg[2 * i];
       *reinterpret_cast<uint4*>(&Ks[(2 * kp + 1) * KPAD + dc]) = kreg[2 * i + 1];
@@ -424,16 +425,22 @@ hipError_t launch_attention(int B, int n, int hq, int hkv, int DH, int Lmax, int
                             float scale, void* out, float* ws, const AttnPlan& pl, int32_t* status, hipStream_t st) {
   (void)status;
   if (dtype == EAGLE_BF16) {
-    const int nrb = (pl.rows + kRowsPerWG - 1) / kRowsPerWG;
+    const int threads = pl.rows <= 128 ? 256 : 512;
+    const int rows_wg = threads / 64 * kQT * 16;
+    const int nrb = (pl.rows + rows_wg - 1) / rows_wg;
     dim3 grid(pl.nsplit + 1, hkv * nrb, B);
-    const int threads = kAttnThreads;
-#define EAGLE_ATTN_BF16(D)                                                                                           \
-  attn_split_bf16_kernel<D><<<grid, threads, 0, st>>>(n, hq, hkv, Lmax, (const uint16_t*)q, (const uint16_t*)kp,    \
-                                                      (const uint16_t*)vp, plen, (const uint16_t*)kt,               \
-                                                      (const uint16_t*)vt, mask, scale, ws, pl.rows, pl.rows_pad,   \
-                                                      pl.split_keys, pl.nsplit)
-    if (DH == 64) EAGLE_ATTN_BF16(64);
-    else EAGLE_ATTN_BF16(128);
+#define EAGLE_ATTN_BF16(D, T)                                                                                        \
+  attn_split_bf16_kernel<D, T><<<grid, T, 0, st>>>(n, hq, hkv, Lmax, (const uint16_t*)q, (const uint16_t*)kp,       \
+                                                   (const uint16_t*)vp, plen, (const uint16_t*)kt,                  \
+                                                   (const uint16_t*)vt, mask, scale, ws, pl.rows, pl.rows_pad,      \
+                                                   pl.split_keys, pl.nsplit)
+    if (DH == 64) {
+      if (threads == 256) EAGLE_ATTN_BF16(64, 256);
+      else EAGLE_ATTN_BF16(64, 512);
+    } else {
+      if (threads == 256) EAGLE_ATTN_BF16(128, 256);
+      else EAGLE_ATTN_BF16(128, 512);
+    }
 #undef EAGLE_ATTN_BF16
   } else {
     dim3 grid(pl.nsplit + 1, hkv, B);
