@@ -156,6 +156,34 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda"):
     return dict(total_ms=total_ms, wall_s=wall, lm_ms=lm_ms, committed=committed, status=status)
 
 
+def time_commit(cfg, wts, inp, rows, T, reps=50, device="cuda"):
+    """One round on a cache with room, then its post-accept commit timed `reps`
+    times with events (the prefix lengths are restored between launches)."""
+    import torch
+
+    from eagle_draft_tree_expand_amd import round as dround
+    room = cfg.D + 1
+    dr = dround.DeviceRound(cfg, device, cap=cfg.Lmax + room)
+    data = dround.DeviceInputs(inp, device, room=room)
+    data.rows.copy_(rows)
+    dr.step(wts, data, T)
+    plen0 = data.prefix_len.clone()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for i in range(reps):
+        data.prefix_len.copy_(plen0)
+        ev[i][0].record()
+        dr.commit(data)
+        ev[i][1].record()
+    torch.cuda.synchronize()
+    us = float(np.mean([a.elapsed_time(b) for a, b in ev[5:]])) * 1000.0
+    esz = 2 if cfg.dtype == "bf16" else 4
+    rows_c = dr.acc["accept_len"].cpu().numpy().astype(np.int64) + 1
+    # K and V rows read and written, feature rows read, the whole feature block written
+    nbytes = int(rows_c.sum() * (4 * cfg.hkv * cfg.dh + cfg.H) * esz + cfg.B * (cfg.D + 1) * cfg.H * esz)
+    return {"us": round(us, 2), "bytes": nbytes, "committed_rows": int(rows_c.sum()),
+            "status": int(dr.status.item())}
+
+
 def cpu_baseline(cfg_name, T, inp, budget_s=25.0):
     """The oracle, untuned, on a bounded sample: whole rounds of set 0 (pre-pass excluded)."""
     from threadpoolctl import threadpool_info
@@ -255,6 +283,8 @@ def main():
                      "avg_launch_ms": round(r["lm_ms"], 5)},
         "device_status": r["status"],
     }
+    if not args.no_extra:
+        out["commit"] = time_commit(cfg, wts, inps[0], sets[0].rows, args.temp)
     if not args.no_extra and args.config == "8b":
         gsteps = max(20, args.steps // 4)
         g = time_rounds(cfg, wts, sets, 0.0, gsteps, 5)
@@ -264,14 +294,15 @@ def main():
         del sets
         torch.cuda.empty_cache()
         try:
-            cfg64, _, wts64, sets64 = setup("b64", 1.0, 2)
+            cfg64, inps64, wts64, sets64 = setup("b64", 1.0, 2)
             b = time_rounds(cfg64, wts64, sets64, 1.0, 10, 2)
             ms64 = b["total_ms"] / 10
             flops = 2.0 * cfg64.B * cfg64.N * cfg64.H * cfg64.V
             out["b64"] = {"trees_per_s": round(1000.0 / ms64 * cfg64.B, 1), "ms_per_round": round(ms64, 3),
                           "committed_tokens_per_s": round(b["committed"] / (b["total_ms"] / 1000.0), 1),
                           "lmhead_ms": round(b["lm_ms"], 4),
-                          "lmhead_mfma_frac": round(flops / (b["lm_ms"] / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                          "lmhead_mfma_frac": round(flops / (b["lm_ms"] / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                          "commit": time_commit(cfg64, wts64, inps64[0], sets64[0].rows, 1.0)}
             del sets64, wts64
         except Exception as e:  # report, do not hide the main line
             out["b64"] = {"error": repr(e)[:200]}

@@ -17,12 +17,14 @@ ERRORS = {-1: "EAGLE_ERR_NULL", -2: "EAGLE_ERR_SHAPE", -3: "EAGLE_ERR_DTYPE",
 EAGLE_F32, EAGLE_BF16 = 0, 1
 EAGLE_W_ROWMAJOR, EAGLE_W_PACKED = 0, 1
 STATUS_BITS = {0x1: "TOKEN_RANGE", 0x2: "NONFINITE", 0x4: "ZERO_RESIDUAL", 0x8: "TOPK_RESCAN",
-               0x10: "BAD_TREE", 0x20: "CAND_OVERFLOW", 0x40: "SYNC_TIMEOUT"}
+               0x10: "BAD_TREE", 0x20: "CAND_OVERFLOW", 0x40: "SYNC_TIMEOUT",
+               0x80: "CACHE_FULL"}
 
 # Every symbol include/eagle.h declares.
 EXPORTS = ("eagle_workspace_size", "eagle_workspace_init", "eagle_expand_tree", "eagle_build_tree_mask",
            "eagle_tree_attention", "eagle_lmhead_softmax", "eagle_verify_accept", "eagle_gather_rows",
-           "eagle_gather_rows_multi", "eagle_lmhead_packed_bytes", "eagle_lmhead_pack_weight", "eagle_error_string", "eagle_abi_version")
+           "eagle_gather_rows_multi", "eagle_commit_accepted", "eagle_lmhead_packed_bytes",
+           "eagle_lmhead_pack_weight", "eagle_error_string", "eagle_abi_version")
 
 
 class TreeParams(ctypes.Structure):
@@ -52,6 +54,7 @@ _SIGS = {
     "eagle_verify_accept": (c_int32, [POINTER(TreeParams)] + [_P] * 16 + [_P, c_size_t, _P, _P]),
     "eagle_gather_rows": (c_int32, [c_int32, c_int32, c_int32, _P, c_int32, _P, _P, _P, _P]),
     "eagle_gather_rows_multi": (c_int32, [c_int32, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P]),
+    "eagle_commit_accepted": (c_int32, [c_int32] * 8 + [_P] * 9 + [_P, _P]),
     "eagle_error_string": (c_char_p, [c_int32]),
     "eagle_abi_version": (c_int32, []),
 }

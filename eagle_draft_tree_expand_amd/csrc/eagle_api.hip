@@ -65,7 +65,7 @@ float* stage_area(void* ws) { return reinterpret_cast<float*>(static_cast<char*>
 
 extern "C" {
 
-int32_t eagle_abi_version(void) { return (1 << 16) | 0; }
+int32_t eagle_abi_version(void) { return (1 << 16) | 1; }
 
 const char* eagle_error_string(int32_t code) {
   switch (code) {
@@ -244,6 +244,32 @@ int eagle_gather_rows_multi(int32_t n_tables, int32_t n_rows, int32_t dtype, int
   if (n_rows == 0) return EAGLE_OK;
   if (!idx) return EAGLE_ERR_NULL;
   return launch_status(launch_gather(n_rows, gs, table_rows, idx, dev_status, (hipStream_t)stream));
+}
+
+int eagle_commit_accepted(int32_t batch, int32_t n, int32_t hkv, int32_t head_dim, int32_t max_prefix,
+                          int32_t hidden, int32_t depth, int32_t dtype, const int32_t* accept_len,
+                          const int32_t* accept_path, const void* k_tree, const void* v_tree, const void* x,
+                          void* k_prefix, void* v_prefix, int32_t* prefix_len, void* feat, int32_t* dev_status,
+                          void* stream) {
+  if (batch < 0 || batch > (1 << 20) || n < 1 || n > EAGLE_MAX_NODES || hkv < 1 || head_dim < 1 ||
+      max_prefix < 1 || hidden < 1 || depth < 1 || depth > EAGLE_MAX_DEPTH)
+    return EAGLE_ERR_SHAPE;
+  if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
+  const int64_t esz = dtype == EAGLE_F32 ? 4 : 2;
+  if ((head_dim * esz) % 16 != 0 || (hidden * esz) % 16 != 0) return EAGLE_ERR_ALIGN;
+  // 32-bit unit offsets inside one request's tree rows; 64-bit elsewhere
+  if ((int64_t)n * hkv * head_dim * esz / 16 >= ((int64_t)1 << 31) ||
+      (int64_t)n * hidden * esz / 16 >= ((int64_t)1 << 31))
+    return EAGLE_ERR_SHAPE;
+  if (batch == 0) return EAGLE_OK;
+  if (!accept_len || !accept_path || !k_tree || !v_tree || !x || !k_prefix || !v_prefix || !prefix_len || !feat)
+    return EAGLE_ERR_NULL;
+  if (!aligned16(k_tree) || !aligned16(v_tree) || !aligned16(x) || !aligned16(k_prefix) || !aligned16(v_prefix) ||
+      !aligned16(feat))
+    return EAGLE_ERR_ALIGN;
+  return launch_status(launch_commit(batch, n, hkv, head_dim, max_prefix, hidden, depth, (int)esz, accept_len,
+                                     accept_path, k_tree, v_tree, x, k_prefix, v_prefix, prefix_len, feat,
+                                     dev_status, (hipStream_t)stream));
 }
 
 }  // extern "C"

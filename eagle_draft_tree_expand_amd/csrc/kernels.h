@@ -42,6 +42,13 @@ hipError_t launch_gather(int n_rows, GatherSet gs, int table_rows, const int32_t
                          hipStream_t st);
 hipError_t launch_zero_ints(int32_t* p, size_t n, hipStream_t st);
 
+// ---- post-accept commit (k_commit.hip) ----
+constexpr int kCommitThreads = 256;
+hipError_t launch_commit(int B, int n, int hkv, int head_dim, int max_prefix, int hidden, int D, int esz,
+                         const int32_t* accept_len, const int32_t* accept_path, const void* kt, const void* vt,
+                         const void* x, void* kp, void* vp, int32_t* prefix_len, void* feat, int32_t* status,
+                         hipStream_t st);
+
 // ---- attention (k_attn.hip) ----
 struct AttnPlan {
   int rows;        // query rows per (request, kv head) = n * (hq / hkv)

@@ -116,3 +116,14 @@ def gather_rows_multi(n_rows, idx, pairs, status=None):
     rc = _lib.load().eagle_gather_rows_multi(n, n_rows, dt, pairs[0][0].shape[0], _ptr(idx), ctypes.addressof(elems),
                                             ctypes.addressof(tabs), ctypes.addressof(outs), _ptr(status), _stream())
     check("eagle_gather_rows_multi", rc)
+
+
+def commit_accepted(batch, n, hkv, head_dim, max_prefix, hidden, depth, accept_len, accept_path, k_tree, v_tree, x,
+                    k_prefix, v_prefix, prefix_len, feat, status=None):
+    """Append the accepted path's keys/values to the prefix cache (in place), grow prefix_len,
+    and write the path's features to feat [B, depth + 1, hidden]."""
+    dt = _DT[k_tree.dtype]
+    rc = _lib.load().eagle_commit_accepted(batch, n, hkv, head_dim, max_prefix, hidden, depth, dt, _ptr(accept_len),
+                                          _ptr(accept_path), _ptr(k_tree), _ptr(v_tree), _ptr(x), _ptr(k_prefix),
+                                          _ptr(v_prefix), _ptr(prefix_len), _ptr(feat), _ptr(status), _stream())
+    check("eagle_commit_accepted", rc)

@@ -4,7 +4,8 @@
 
     expand -> mask -> (gather tree q/k/v rows) -> tree attention -> LM head -> accept
 
-on the current HIP stream, every step in libeagle's kernels.  `DeviceInputs`
+on the current HIP stream, every step in libeagle's kernels, and `commit`
+appends the accepted path to the prefix cache for the next round.  `DeviceInputs`
 holds one input set on the device.  `device_draft_rows` builds the synthetic
 draft rows "target logits + noise" slot by slot with the same kernels (the
 ancestor-only mask makes a node's target logits depend on its root path only,
@@ -45,13 +46,17 @@ class DeviceWeights:
 
 
 class DeviceInputs:
-    """One input set: prefix KV, prefix lengths, roots, uniforms, draft rows, noise."""
+    """One input set: prefix KV, prefix lengths, roots, uniforms, draft rows, noise.
 
-    def __init__(self, inp, device="cuda", with_eps=False):
+    `room` extra cache positions per request (zero-filled) leave space for
+    committed paths; the cache stride is then `cap` = Lmax + room."""
+
+    def __init__(self, inp, device="cuda", with_eps=False, room=0):
         c = inp.cfg
         dt = _TORCH_DT[c.dtype]
-        self.k_prefix = _t(inp.k_prefix, dt, device)
-        self.v_prefix = _t(inp.v_prefix, dt, device)
+        self.cap = c.Lmax + int(room)
+        self.k_prefix = self._cache(inp.k_prefix, dt, device)
+        self.v_prefix = self._cache(inp.v_prefix, dt, device)
         self.prefix_len = _t(inp.prefix_len, torch.int32, device)
         self.roots = _t(inp.roots, torch.int32, device)
         self.uniforms = _t(inp.uniforms, torch.float32, device)
@@ -60,6 +65,14 @@ class DeviceInputs:
         self.rows = torch.zeros((c.B, c.S, c.V), dtype=torch.float32, device=device)
         self.eps = _t(inp.eps, torch.float32, device) if with_eps else None
 
+    def _cache(self, a, dt, device):
+        t = _t(a, dt, device)
+        if self.cap == t.shape[2]:
+            return t
+        out = torch.zeros((t.shape[0], t.shape[1], self.cap, t.shape[3]), dtype=dt, device=device)
+        out[:, :, :t.shape[2]] = t
+        return out
+
     def set_rows(self, rows_np):
         self.rows.copy_(torch.from_numpy(np.ascontiguousarray(rows_np, dtype=np.float32)))
 
@@ -67,8 +80,9 @@ class DeviceInputs:
 class DeviceRound:
     """Device buffers + the five entry points of one round for a config."""
 
-    def __init__(self, cfg, device="cuda", n=None, B=None):
+    def __init__(self, cfg, device="cuda", n=None, B=None, cap=None):
         self.cfg = c = cfg
+        self.cap = cap or c.Lmax  # largest prefix-cache stride the workspace is sized for
         self.B = B = B or c.B
         self.N = N = n or c.N
         self.dev = device
@@ -90,6 +104,7 @@ class DeviceRound:
         self.kt = torch.zeros((B, N, c.hkv, c.dh), dtype=dt, device=device)
         self.vt = torch.zeros((B, N, c.hkv, c.dh), dtype=dt, device=device)
         self.x = torch.zeros((B, N, c.hq, c.dh), dtype=dt, device=device)
+        self.feat = torch.zeros((B, c.D + 1, c.H), dtype=dt, device=device)
         self.logits = torch.zeros((B * N, c.V), dtype=f32, device=device)
         self.stats = z(B * N, 2, dtype=f32)
         self.argmax = z(B * N)
@@ -98,7 +113,7 @@ class DeviceRound:
         self.status = z(1)
         self.scale = float(np.float32(1.0 / math.sqrt(c.dh)))
         p = self.params(1.0, m=min(max(self.N - 1, 1), c.P))  # sizing only: at least one draft node
-        nbytes = ops.workspace_size(p, c.hq, c.hkv, c.dh, c.Lmax, c.H)
+        nbytes = ops.workspace_size(p, c.hq, c.hkv, c.dh, self.cap, c.H)
         if nbytes == 0:
             raise ValueError("invalid round shape")
         self.ws = ops.new_workspace(nbytes, device)
@@ -123,7 +138,7 @@ class DeviceRound:
 
     def attention(self, data):
         c = self.cfg
-        ops.tree_attention(self.B, self.N, c.hq, c.hkv, c.dh, c.Lmax, self.q, data.k_prefix, data.v_prefix,
+        ops.tree_attention(self.B, self.N, c.hq, c.hkv, c.dh, data.cap, self.q, data.k_prefix, data.v_prefix,
                            data.prefix_len, self.kt, self.vt, self.mask, self.scale, self.x, self.ws, self.status)
 
     def lmhead(self, wts, T):
@@ -135,6 +150,14 @@ class DeviceRound:
     def accept(self, data, T, round_id=0):
         ops.verify_accept(self.params(T, round_id, data.seed), self.tree, self.logits, self.stats, self.argmax,
                           data.rows, self.tree["slot_stats"], data.uniforms, self.acc, self.ws, self.status)
+
+    def commit(self, data):
+        """Append the accepted path's keys/values to data's prefix cache, grow its
+        lengths, and write the path's features to self.feat [B, D + 1, H]."""
+        c = self.cfg
+        ops.commit_accepted(self.B, self.N, c.hkv, c.dh, data.cap, c.H, c.D, self.acc["accept_len"],
+                            self.acc["accept_path"], self.kt, self.vt, self.x, data.k_prefix, data.v_prefix,
+                            data.prefix_len, self.feat, self.status)
 
     def step(self, wts, data, T, round_id=0):
         """One whole round (all five entry points, plus the q/k/v row gathers)."""

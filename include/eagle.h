@@ -76,6 +76,7 @@ extern "C" {
 #define EAGLE_STATUS_BAD_TREE      0x10 /* parent links not a valid flattened tree       */
 #define EAGLE_STATUS_CAND_OVERFLOW 0x20 /* child re-scan candidate list overflowed       */
 #define EAGLE_STATUS_SYNC_TIMEOUT  0x40 /* a walk workgroup gave up waiting for its group */
+#define EAGLE_STATUS_CACHE_FULL    0x80 /* a prefix cache had no room for the commit     */
 
 /* ---- limits -------------------------------------------------------------- */
 #define EAGLE_MAX_TOPK   16
@@ -272,6 +273,39 @@ int eagle_gather_rows(int32_t n_rows, int32_t row_elems, int32_t dtype, const vo
 int eagle_gather_rows_multi(int32_t n_tables, int32_t n_rows, int32_t dtype, int32_t table_rows,
                             const int32_t* idx, const int32_t* row_elems, const void* const* tables,
                             void* const* outs, int32_t* dev_status, void* stream);
+
+/* Commit the accepted path to the context, after eagle_verify_accept.
+ * Source: [E1] section 3.3 (the accepted tokens and their features are kept
+ * for the next drafting round); [HW] section 5 (the longest consistent path
+ * is committed, the other branches are discarded, and drafting resumes from
+ * the longer context).
+ * Committed rows of request b: the root (flat node 0, the last token of the
+ * previous round, whose key/value the verify pass computed) and then
+ * accept_path[b, 0 .. a-1] with a = accept_len[b].  The draft token drawn
+ * after them (residual or bonus) has no key/value yet: it is the next
+ * round's root.
+ * In:  accept_len [B], accept_path [B, depth] as eagle_verify_accept writes
+ *        them (entries past a are ignored);
+ *      k_tree, v_tree [B, n, hkv, head_dim] (the verify pass's tree keys and
+ *        values); x [B, n, hidden] (the LM-head inputs of the tree nodes).
+ * In/out: k_prefix, v_prefix [B, hkv, max_prefix, head_dim] get row r of the
+ *        path at position prefix_len[b] + r (other positions untouched);
+ *      prefix_len [B] grows by a + 1.
+ * Out: feat [B, depth + 1, hidden]: row r = x[b, node r] for r <= a, zero after.
+ * Status: BAD_TREE (a outside [0, depth] or a path node outside [1, n): that
+ *        request commits nothing and its features are zero); CACHE_FULL
+ *        (prefix_len[b] + a + 1 > max_prefix: cache and length unchanged,
+ *        features still written).
+ * dtype EAGLE_BF16 or EAGLE_F32 for keys, values and features alike;
+ * head_dim and hidden must span whole 16-byte units and every tensor pointer
+ * must be 16-byte aligned (EAGLE_ERR_ALIGN).  The tree, cache and feature
+ * buffers must not overlap.  depth <= EAGLE_MAX_DEPTH, n <= EAGLE_MAX_NODES;
+ * batch 0 is a no-op. */
+int eagle_commit_accepted(int32_t batch, int32_t n, int32_t hkv, int32_t head_dim, int32_t max_prefix,
+                          int32_t hidden, int32_t depth, int32_t dtype, const int32_t* accept_len,
+                          const int32_t* accept_path, const void* k_tree, const void* v_tree, const void* x,
+                          void* k_prefix, void* v_prefix, int32_t* prefix_len, void* feat, int32_t* dev_status,
+                          void* stream);
 
 /* Human-readable name of a return code. */
 const char* eagle_error_string(int32_t code);

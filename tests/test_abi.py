@@ -162,3 +162,24 @@ def test_gather_multi_rejects(lib):
 def test_workspace_init_rejects(lib):
     assert lib.eagle_workspace_init(None, 1 << 20, None) == -1
     assert lib.eagle_workspace_init(FAKE, 100, None) == -4
+
+
+def test_commit_rejects(lib):
+    f = lib.eagle_commit_accepted
+    ok = (2, 9, 2, 128, 100, 512, 4, 1)
+    ptrs = [FAKE] * 9
+    assert f(0, *ok[1:], *ptrs, None, None) == 0                          # empty batch
+    assert f(2, 0, *ok[2:], *ptrs, None, None) == -2                      # no nodes
+    assert f(2, 257, *ok[2:], *ptrs, None, None) == -2
+    assert f(*ok[:6], 0, 1, *ptrs, None, None) == -2                      # depth
+    assert f(*ok[:6], 17, 1, *ptrs, None, None) == -2
+    assert f(*ok[:4], 0, *ok[5:], *ptrs, None, None) == -2                # no cache room at all
+    assert f(*ok[:7], 5, *ptrs, None, None) == -3                         # dtype
+    assert f(2, 9, 2, 12, 100, 512, 4, 1, *ptrs, None, None) == -6        # head_dim row not 16-byte units
+    assert f(2, 9, 2, 128, 100, 501, 4, 0, *ptrs, None, None) == -6       # hidden row (fp32) ...
+    assert f(2, 9, 2, 128, 100, 500, 4, 0, *ptrs, None, None) != -6       # ... 500 fp32 is whole units
+    assert f(2, 9, 2, 128, 100, 500, 4, 1, *ptrs, None, None) == -6       # 500 bf16 is not
+    assert f(*ok, None, *ptrs[1:], None, None) == -1
+    assert f(*ok, *ptrs[:8], None, None, None) == -1
+    assert f(*ok, *ptrs[:2], FAKE + 8, *ptrs[3:], None, None) == -6
+    assert f(*ok, *ptrs[:8], FAKE + 4, None, None) == -6
