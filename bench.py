@@ -156,31 +156,32 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda"):
     return dict(total_ms=total_ms, wall_s=wall, lm_ms=lm_ms, committed=committed, status=status)
 
 
-def time_commit(cfg, wts, inp, rows, T, reps=50, device="cuda"):
-    """One round on a cache with room, then its post-accept commit timed `reps`
-    times with events (the prefix lengths are restored between launches)."""
+def time_commit(cfg, wts, inp, rows, T, reps=40, device="cuda"):
+    """One round on a cache with room for many commits, then `reps` back-to-back
+    commits of its accepted path (each appends after the last) bracketed by
+    one pair of events: time per call, launch gaps included."""
     import torch
 
     from eagle_draft_tree_expand_amd import round as dround
-    room = cfg.D + 1
+    room = (reps + 2) * (cfg.D + 1)
     dr = dround.DeviceRound(cfg, device, cap=cfg.Lmax + room)
     data = dround.DeviceInputs(inp, device, room=room)
     data.rows.copy_(rows)
     dr.step(wts, data, T)
-    plen0 = data.prefix_len.clone()
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
-    for i in range(reps):
-        data.prefix_len.copy_(plen0)
-        ev[i][0].record()
-        dr.commit(data)
-        ev[i][1].record()
+    dr.commit(data)  # warm-up
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
-    us = float(np.mean([a.elapsed_time(b) for a, b in ev[5:]])) * 1000.0
+    e0.record()
+    for _ in range(reps):
+        dr.commit(data)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1000.0 / reps
     esz = 2 if cfg.dtype == "bf16" else 4
     rows_c = dr.acc["accept_len"].cpu().numpy().astype(np.int64) + 1
     # K and V rows read and written, feature rows read, the whole feature block written
     nbytes = int(rows_c.sum() * (4 * cfg.hkv * cfg.dh + cfg.H) * esz + cfg.B * (cfg.D + 1) * cfg.H * esz)
-    return {"us": round(us, 2), "bytes": nbytes, "committed_rows": int(rows_c.sum()),
+    return {"us_per_call": round(us, 2), "bytes": nbytes, "committed_rows": int(rows_c.sum()),
             "status": int(dr.status.item())}
 
 
