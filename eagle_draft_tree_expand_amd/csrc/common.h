@@ -62,10 +62,28 @@ EDEV float wave_sum(float v) {
   return v;
 }
 
+// fp64 sum over the wave: DPP pair/quad/half/row steps (each lane adds its
+// partner's value; addition commutes, so all lanes of a row agree bit for
+// bit), then the four row sums read from lanes 0, 16, 32, 48 and added in a
+// fixed order.  Every lane returns the same value.
+template <int CTRL>
+EDEV double dpp_d(double v) {
+  const long long x = __double_as_longlong(v);
+  const int lo = dpp_i<CTRL>((int)(x & 0xffffffffll)), hi = dpp_i<CTRL>((int)(x >> 32));
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
+EDEV double lane_d(double v, int l) {
+  const long long x = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_readlane((int)(x & 0xffffffffll), l);
+  const int hi = __builtin_amdgcn_readlane((int)(x >> 32), l);
+  return __longlong_as_double(((long long)hi << 32) | (unsigned int)lo);
+}
 EDEV double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  v += dpp_d<kDppXor1>(v);
+  v += dpp_d<kDppXor2>(v);
+  v += dpp_d<kDppHalfMirror>(v);
+  v += dpp_d<kDppMirror>(v);
+  return (lane_d(v, 0) + lane_d(v, 16)) + (lane_d(v, 32) + lane_d(v, 48));
 }
 
 EDEV int wave_sum_i(int v) {

@@ -94,12 +94,13 @@ struct Smem {
   double scan[kWaves];
   double bc_d[4];
   int bc_i[4];
-  // the current node's k children (sampling order): token, fp64 p and q, fp32 terms
-  int cx[EAGLE_MAX_TOPK];
-  double cpx[EAGLE_MAX_TOPK], cqx[EAGLE_MAX_TOPK];
+  // the current node's k children (sampling order): fp32 terms
   float cep[EAGLE_MAX_TOPK], ceq[EAGLE_MAX_TOPK];
   int tried_x[EAGLE_MAX_TOPK];  // tried token i is child i
   double tried_f[EAGLE_MAX_TOPK];
+  int ov_x[EAGLE_MAX_TOPK];     // tried tokens in this workgroup's slice, and their frozen values
+  double ov_f[EAGLE_MAX_TOPK];
+  int nov;
 };
 
 EDEV void publish(uint64_t* w, uint64_t v) { __hip_atomic_store(w, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
@@ -170,9 +171,9 @@ EDEV bool cache_ready(const Group& gr, bool need_q) {
   return gr.cache && (gr.cstate == 2 || (gr.cstate == 1 && !need_q));
 }
 
-// All threads of every workgroup of the group: Z = G(s) over the vocabulary
-// (tried tokens not corrected); per-workgroup partials left in sm.vals.
-EDEV double group_reduce(const Rows& R, double s, Group& gr, Smem& sm, int* timed_out) {
+// All threads: this workgroup's part of G(s) over its slice (tried tokens not
+// corrected), one partial per wave left in sm.red (no barrier).
+EDEV void local_partial(const Rows& R, double s, Group& gr, Smem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool need_q = s != 0.0;
   const bool from_cache = cache_ready(gr, need_q);
@@ -187,73 +188,131 @@ EDEV double group_reduce(const Rows& R, double s, Group& gr, Smem& sm, int* time
   if (gr.cache && !from_cache) gr.cstate = need_q ? 2 : 1;
   a = wave_sum_d(a);
   if (lane == 0) sm.red[wave] = a;
-  __syncthreads();
-  // Wave 0 publishes this workgroup's partial, collects all G of them and
-  // sums them with a butterfly: identical inputs and order in every
-  // workgroup, so every workgroup gets the same total bit for bit.
-  if (wave == 0) {
-    const uint64_t tag = tag_of(gr.epoch, gr.step);
-    uint64_t* bank = gr.mb->bank[gr.step & 1];
-    if (lane == 0) {
-      double part = 0.0;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) part += sm.red[w];
-      publish(bank + gr.g, tag | encode_val(part));
-    }
-    double v = 0.0;
-    if (lane < gr.G) {
-      v = decode_val(await_tag(bank + lane, tag, timed_out));
-      sm.vals[lane] = v;
-    }
-    v = wave_sum_d(v);
-    if (lane == 0) sm.bc_d[0] = v;
+}
+
+// Wave 0 only, after the wave partials are in sm.red: publishes this
+// workgroup's partial, collects the G partials (kept in sm.vals) and sums
+// them with a butterfly, so every lane of every workgroup of the group holds
+// the same total bit for bit.  The caller advances gr.step in all threads.
+EDEV double wave0_exchange(Group& gr, Smem& sm, int* timed_out) {
+  const int lane = threadIdx.x & 63;
+  const double part = wave_sum_d(lane < kWaves ? sm.red[lane] : 0.0);
+  const uint64_t tag = tag_of(gr.epoch, gr.step);
+  uint64_t* bank = gr.mb->bank[gr.step & 1];
+  if (lane == 0) publish(bank + gr.g, tag | encode_val(part));
+  double v = 0.0;
+  if (lane < gr.G) {
+    v = decode_val(await_tag(bank + lane, tag, timed_out));
+    sm.vals[lane] = v;
+  }
+  return wave_sum_d(v);
+}
+
+// All threads of every workgroup of the group: Z = G(s) over the vocabulary
+// (tried tokens not corrected); per-workgroup partials left in sm.vals.
+EDEV double group_reduce(const Rows& R, double s, Group& gr, Smem& sm, int* timed_out) {
+  local_partial(R, s, gr, sm);
+  lds_barrier();
+  if (threadIdx.x < 64) {
+    const double v = wave0_exchange(gr, sm, timed_out);
+    if (threadIdx.x == 0) sm.bc_d[0] = v;
   }
   __syncthreads();
   ++gr.step;
   return sm.bc_d[0];
 }
 
-// Inverse-CDF draw from the residual at s (partials from the group_reduce at
-// the same s), tried tokens replaced by their frozen values.  Every workgroup
-// finds the owning workgroup; that one locates the token in its slice and
-// posts it to the mailbox.  Returns the token in workgroup 0 (others: -1).
+// Fill the LDS token cache with the terms of rows R over the slice (q terms
+// too when need_q).
+EDEV void fill_cache(const Rows& R, bool need_q, Group& gr) {
+  const int tid = threadIdx.x;
+  const bool vec = ((((uintptr_t)R.zp) | (need_q ? (uintptr_t)R.zq : 0)) & 15) == 0;
+  for (int base = gr.lo + tid * 4, ci = tid * 4; base < gr.hi; base += kThreads * 4, ci += kThreads * 4) {
+    float ep[4], eq[4];
+    slice_terms(R, need_q, false, gr, base, ci, vec, ep, eq);
+  }
+  gr.cstate = need_q ? 2 : 1;
+}
+
+// Inclusive fp64 prefix sum over the wave in lane order: DPP row shifts by
+// 1, 2, 4, 8 inside each row of 16 lanes (lanes shifted in from outside the
+// row read 0), then the totals of the preceding rows added in order.
+EDEV double wave_scan_d(double v) {
+  v += dpp_d<0x111>(v);
+  v += dpp_d<0x112>(v);
+  v += dpp_d<0x114>(v);
+  v += dpp_d<0x118>(v);
+  const double r0 = lane_d(v, 15), r1 = lane_d(v, 31), r2 = lane_d(v, 47);
+  const int row = (threadIdx.x & 63) >> 4;
+  const double pre = row == 0 ? 0.0 : row == 1 ? r0 : row == 2 ? r0 + r1 : (r0 + r1) + r2;
+  return v + pre;
+}
+
+// Inverse-CDF draw from the residual at s (partials from the last exchange at
+// the same s, in sm.vals), tried tokens replaced by their frozen values.
+// Wave 0 corrects the partials, finds the owning workgroup and the mass left
+// before it; that workgroup locates the token in its slice and posts it to
+// the mailbox.  Returns the token in workgroup 0 (others: -1).
 EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr, Smem& sm, int V, int* ties,
                     int* timed_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Corrected per-workgroup sums: add (f_i - current term) to the owner of x_i.
-  if (tid == 0) {
-    for (int i = 0; i < ntried; ++i) {
-      const int x = sm.tried_x[i];
-      const int owner = min(x / gr.span, gr.G - 1);
-      sm.vals[owner] += sm.tried_f[i] - resid_e(sm.cep[i], sm.ceq[i], R, s);
+  if (wave == 0) {
+    // lane i < ntried: tried token i's owner and the change from its current
+    // term to its frozen value; those in this workgroup's slice are listed
+    int own = -1, inslice = 0, x = 0;
+    double dlt = 0.0;
+    if (lane < ntried) {
+      x = sm.tried_x[lane];
+      own = min(x / gr.span, gr.G - 1);
+      dlt = sm.tried_f[lane] - resid_e(sm.cep[lane], sm.ceq[lane], R, s);
+      inslice = x >= gr.lo && x < gr.hi;
     }
+    const uint64_t ball = __ballot(inslice);
+    if (inslice) {
+      const int pos = (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(ball >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)ball, 0u));
+      sm.ov_x[pos] = x;
+      sm.ov_f[pos] = sm.tried_f[lane];
+    }
+    // corrected partial of workgroup `lane` (corrections in tried order), clamped at 0
+    double c = lane < gr.G ? sm.vals[lane] : 0.0;
+    for (int i = 0; i < ntried; ++i) {
+      const int oi = __builtin_amdgcn_readlane(own, i);
+      const double di = lane_d(dlt, i);
+      if (lane == oi) c += di;
+    }
+    c = c > 0.0 ? c : 0.0;
+    // total, then the first workgroup whose cumulative mass passes u * total
     double tot = 0.0;
-    for (int j = 0; j < gr.G; ++j) tot += sm.vals[j] > 0.0 ? sm.vals[j] : 0.0;
+    for (int j = 0; j < gr.G; ++j) tot += lane_d(c, j);
     const double target = uval * tot;
     double cum = 0.0;
     int gstar = -1;
     for (int j = 0; j < gr.G; ++j) {
-      const double c = sm.vals[j] > 0.0 ? sm.vals[j] : 0.0;
-      if (c > 0.0 && cum + c > target) { gstar = j; break; }
-      cum += c;
+      const double cj = lane_d(c, j);
+      if (cj > 0.0 && cum + cj > target) { gstar = j; break; }
+      cum += cj;
     }
-    if (gstar < 0) {
+    if (gstar < 0) {  // rounding: the last workgroup with mass
       for (int j = gr.G - 1; j >= 0; --j)
-        if (sm.vals[j] > 0.0) { gstar = j; break; }
+        if (lane_d(c, j) > 0.0) { gstar = j; break; }
       cum = 0.0;
-      for (int j = 0; j < gstar; ++j) cum += sm.vals[j] > 0.0 ? sm.vals[j] : 0.0;
+      for (int j = 0; j < gstar; ++j) cum += lane_d(c, j);
     }
-    sm.bc_i[0] = gstar < 0 ? 0 : gstar;
-    sm.bc_d[1] = target - cum;
-    sm.bc_d[2] = tot;
+    if (lane == 0) {
+      sm.bc_i[0] = gstar < 0 ? 0 : gstar;
+      sm.bc_d[1] = target - cum;
+      sm.bc_d[2] = tot;
+      sm.nov = __popcll(ball);
+    }
   }
   __syncthreads();
   const int gstar = sm.bc_i[0];
   const double off0 = sm.bc_d[1], tot = sm.bc_d[2];
+  const int nov = sm.nov;
   const uint64_t rtag = tag_of(gr.epoch, gr.step);
   int token = -1;
   if (gr.g == gstar) {
-    // scan the own slice in id order, 1024 tokens (4 per thread) per pass
+    // scan the own slice in id order, 4096 tokens (4 per thread) per pass
     const bool need_q = s != 0.0;
     const bool from_cache = cache_ready(gr, need_q);
     const bool vec = ((((uintptr_t)R.zp) | (need_q ? (uintptr_t)R.zq : 0)) & 15) == 0;
@@ -264,35 +323,31 @@ EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr,
       double val[4], mine = 0.0;
       float ep[4] = {0.f, 0.f, 0.f, 0.f}, eq[4] = {0.f, 0.f, 0.f, 0.f};
       if (base < gr.hi) slice_terms(R, need_q, from_cache, gr, base, ci, vec, ep, eq);
+#pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int v = base + e;
-        double x = 0.0;
+        double xv = 0.0;
         if (v < gr.hi) {
-          x = resid_e(ep[e], eq[e], R, s);
-          for (int i = 0; i < ntried; ++i)
-            if (sm.tried_x[i] == v) x = sm.tried_f[i];
+          xv = resid_e(ep[e], eq[e], R, s);
+          if (nov > 0)
+            for (int i = 0; i < nov; ++i)
+              if (sm.ov_x[i] == v) xv = sm.ov_f[i];
         }
-        val[e] = x;
-        mine += x;
+        val[e] = xv;
+        mine += xv;
       }
-      double inc = mine;
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        const double y = __shfl_up(inc, o);
-        if (lane >= o) inc += y;
-      }
+      double inc = wave_scan_d(mine);
       if (lane == 63) sm.scan[wave] = inc;
-      __syncthreads();
-      if (tid == 0) {
-        double t = 0.0;
-        for (int w = 0; w < kWaves; ++w) { const double y = sm.scan[w]; sm.scan[w] = t; t += y; }
-        sm.bc_d[3] = t;  // pass total
-        sm.bc_i[1] = -1;
-        sm.bc_i[2] = 0;
-        sm.bc_i[3] = -1;
+      if (tid == 0) { sm.bc_i[1] = -1; sm.bc_i[2] = 0; sm.bc_i[3] = -1; }
+      lds_barrier();
+      double pre = 0.0, ptot = 0.0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const double t = sm.scan[w];
+        pre += w < wave ? t : 0.0;
+        ptot += t;
       }
-      __syncthreads();
-      inc += sm.scan[wave];
+      inc += pre;
       const double exc = inc - mine;
       if (mine > 0.0 && exc <= off && off < inc) {
         double c = exc;
@@ -311,17 +366,23 @@ EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr,
         atomicMax(&sm.bc_i[1], base + pick);
         if (t2) atomicOr(&sm.bc_i[2], 1);
       }
-      // remember the last positive token of the slice (rounding fallback)
+      // remember the last positive token of the slice (rounding fallback):
+      // the highest lane holding one has the wave's largest, one atomic per wave
       int lp = -1;
       for (int e = 3; e >= 0; --e)
         if (val[e] > 0.0) { lp = base + e; break; }
-      if (lp >= 0) atomicMax(&sm.bc_i[3], lp);
-      __syncthreads();
+      const uint64_t pb = __ballot(lp >= 0);
+      if (pb != 0ull) {
+        const int top = 63 - __clzll((long long)pb);
+        const int wlp = __builtin_amdgcn_readlane(lp, top);
+        if (lane == 0) atomicMax(&sm.bc_i[3], wlp);
+      }
+      lds_barrier();
       found = sm.bc_i[1];
       tie |= sm.bc_i[2];
       if (sm.bc_i[3] >= 0) last_pos = sm.bc_i[3];
-      off -= sm.bc_d[3];
-      __syncthreads();
+      off -= ptot;
+      lds_barrier();
     }
     if (found < 0) found = last_pos >= 0 ? last_pos : gr.lo;
     token = found;
@@ -343,7 +404,7 @@ EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr,
 }
 
 __global__ __launch_bounds__(kThreads) void accept_kernel(
-    int b0, int G, int N, int V, int D, int k, float T, int cache_tokens, const int32_t* __restrict__ node_tok,
+    int b0, int nb, int G, int N, int V, int D, int k, float T, int cache_tokens, const int32_t* __restrict__ node_tok,
     const int32_t* __restrict__ node_parent, const int32_t* __restrict__ node_slot, const int32_t* __restrict__ pool_tok,
     const int32_t* __restrict__ pool_flat, const float* __restrict__ tlog, const float* __restrict__ tstats,
     const int32_t* __restrict__ targmax, const float* __restrict__ dlog, const float* __restrict__ sstats,
@@ -356,10 +417,17 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
   __shared__ int path[EAGLE_MAX_DEPTH + 1];
   __shared__ int comm[EAGLE_MAX_DEPTH + 2];
   __shared__ int npath, ncomm;
-  __shared__ int cur_u, cur_slot, acc_j, zero_resid, follow, stale;
-  __shared__ double st_s, st_Z, st_R;
+  __shared__ int cur_u, cur_j, acc_j, zero_resid, follow, stale;
+  __shared__ double st_s;
 
-  const int b = b0 + (int)blockIdx.x / G, g = (int)blockIdx.x % G, tid = threadIdx.x;
+  // Workgroups go round-robin over the XCDs, so a request's group is taken
+  // from the blocks of one residue mod 8: its exchanges then stay among the
+  // compute units of one XCD (~1.4 instead of ~2 us per exchange).  Placement
+  // only affects speed: the exchange protocol is correct on any placement.
+  const int xr = (int)blockIdx.x & 7, xj = (int)blockIdx.x >> 3;
+  const int r = xr + 8 * (xj / G), g = xj % G, tid = threadIdx.x;
+  if (r >= nb) return;  // padding block of the last XCD column
+  const int b = b0 + r;
   const int S = 1 + (D - 1) * k;
   const bool greedy = !(T > 0.f);
   const float Tp = greedy ? 1.f : T;
@@ -405,38 +473,44 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     float* m_sst = m_tst + 2 * N;
     float* m_U = m_sst + 2 * S;
     // four entries per thread in flight at a time (one address each, by range)
+    auto meta_src = [&](int i) -> const int32_t* {
+      if (i < N) return node_slot + (size_t)b * N + i;
+      if (i < N + S * k) return pool_tok + (size_t)b * S * k + (i - N);
+      if (i < N + 2 * S * k) return pool_flat + (size_t)b * S * k + (i - N - S * k);
+      if (i < 3 * N + 2 * S * k) return reinterpret_cast<const int32_t*>(tstats) + (size_t)b * N * 2 + (i - N - 2 * S * k);
+      if (i < 3 * N + 2 * S * k + 2 * S)
+        return reinterpret_cast<const int32_t*>(sstats) + (size_t)b * S * 2 + (i - 3 * N - 2 * S * k);
+      return reinterpret_cast<const int32_t*>(uniforms) + (size_t)b * N * (k + 1) + (i - 3 * N - 2 * S * k - 2 * S);
+    };
     for (int i0 = tid; i0 < nmeta; i0 += 4 * kThreads) {
       int v[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int i = i0 + r * kThreads;
-        const int32_t* src;
-        if (i < N) src = node_slot + (size_t)b * N + i;
-        else if (i < N + S * k) src = pool_tok + (size_t)b * S * k + (i - N);
-        else if (i < N + 2 * S * k) src = pool_flat + (size_t)b * S * k + (i - N - S * k);
-        else if (i < 3 * N + 2 * S * k)
-          src = reinterpret_cast<const int32_t*>(tstats) + (size_t)b * N * 2 + (i - N - 2 * S * k);
-        else if (i < 3 * N + 2 * S * k + 2 * S)
-          src = reinterpret_cast<const int32_t*>(sstats) + (size_t)b * S * 2 + (i - 3 * N - 2 * S * k);
-        else
-          src = reinterpret_cast<const int32_t*>(uniforms) + (size_t)b * N * (k + 1) + (i - 3 * N - 2 * S * k - 2 * S);
-        v[r] = i < nmeta ? *src : 0;
+        v[r] = i < nmeta ? *meta_src(i) : 0;
       }
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         if (i0 + r * kThreads < nmeta) m_slot[i0 + r * kThreads] = v[r];
     }
+    int cnode = -1;  // node whose terms the token cache holds
     if (tid == 0) {  // retire this workgroup's stale words from earlier calls
       const uint64_t reset = tag_of(gr.epoch, 1023);
       publish(&gr.mb->bank[0][g], reset);
       publish(&gr.mb->bank[1][g], reset);
     }
     __syncthreads();
+
+    // Walk state.  Wave 0 holds the current node's k candidates in its lanes
+    // (lane i: candidate i) and runs every serial decision; the other waves
+    // take part in the vocabulary passes only.  Loop control goes through LDS.
+    const int lane = tid & 63;
+    double c_p = 0.0, c_q = 0.0, c_f = 0.0;  // candidate's fp64 p and q, frozen residual
+    float c_ep = 0.f, c_eq = 0.f;             // its fp32 terms
+    double w_s = 0.0, w_Z = 1.0, w_R = 1.0;   // s_j, Z_j, R_j (wave 0, uniform)
     for (int step = 0; step <= D; ++step) {
-      if (tid == 0) cur_slot = m_slot[cur_u];
-      __syncthreads();
-      const int u = cur_u, slot = cur_slot;
-      gr.cstate = 0;  // a new node: the token cache is refilled by its first pass
+      const int u = cur_u;
+      const int slot = m_slot[u];
       Rows R;
       R.zp = tlog + ((size_t)b * N + u) * V;
       R.Tp = Tp;
@@ -448,6 +522,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       const float* Uu = m_U + u * (k + 1);
       if (slot < 0 || slot >= S) {
         // never expanded: bonus token from the target
+        gr.cstate = 0;
         group_reduce(R, 0.0, gr, sm, &timed_out);
         const int y = group_draw(R, 0.0, 0, (double)Uu[k], gr, sm, V, &ties, &timed_out);
         if (g == 0 && tid == 0) comm[ncomm++] = y;
@@ -456,65 +531,126 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       R.zq = dlog + ((size_t)b * S + slot) * V;
       R.Mq = m_sst[2 * slot];
       R.invSq = 1.0 / (double)m_sst[2 * slot + 1];
-      // The node's k children, loaded once (one thread each).  An id out of
-      // range is flagged and scored as token 0.
+      // The node's k children (wave 0, lane i: child i): their loads go out
+      // first, then the token cache is filled with the node's rows while
+      // they are in flight.  An id out of range is flagged and scored as
+      // token 0.
+      int c_ok = 0, c_x = 0;
+      float zpx = 0.f, zqx = 0.f;
       if (tid < k) {
         const int x = m_ptok[slot * k + tid];
-        const bool ok = x >= 0 && x < V;
-        const int xc = ok ? x : 0;
-        const float zpx = R.zp[xc], zqx = R.zq[xc];
-        sm.cx[tid] = ok ? x : -1;
-        sm.tried_x[tid] = xc;
-        sm.cpx[tid] = prob64(zpx, R.Mp, R.invSp, Tp);
-        sm.cqx[tid] = prob64(zqx, R.Mq, R.invSq, Tp);
-        sm.cep[tid] = eterm(zpx, R.Mp, Tp);
-        sm.ceq[tid] = eterm(zqx, R.Mq, Tp);
+        c_ok = x >= 0 && x < V;
+        c_x = c_ok ? x : 0;
+        zpx = R.zp[c_x];
+        zqx = R.zq[c_x];
       }
-      if (tid == 0) { st_s = 0.0; st_Z = 1.0; st_R = 1.0; acc_j = -1; stale = 0; }
-      __syncthreads();
-      int ntried = 0;
-      double s_fin = 0.0;
-      for (int j = 0; j < k; ++j) {
-        if (tid == 0) {
-          if (sm.cx[j] < 0) {
-            set_status(status, EAGLE_STATUS_TOKEN_RANGE);
-          } else {
-            const double px = sm.cpx[j], qx = sm.cqx[j];
-            const double num = st_s == 0.0 ? px : fmax(0.0, px - st_s * qx);
-            double ratio;
-            if (qx > 0.0 && st_R > 0.0) ratio = num * st_R / (st_Z * qx);
-            else ratio = num > 0.0 ? __builtin_huge_val() : 0.0;
-            const double a = ratio < 1.0 ? ratio : 1.0;
-            const double uu = (double)Uu[j];
-            if (fabs(uu - a) < kTie) ++ties;
-            if (uu < a) acc_j = j;
+      // The node's rows for the token cache: the loads go out now, behind the
+      // children's, and the terms are stored only when a reduction needs them
+      // (a node whose first candidate is accepted never waits for them).
+      const bool fill = gr.cache != nullptr && cnode != u;
+      const bool vecr = (V & 3) == 0 && ((((uintptr_t)R.zp) | (uintptr_t)R.zq) & 15) == 0;
+      float4 rp[2], rq[2];
+      if (fill) {
+        gr.cstate = 0;
+        if (vecr) {
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const int base = gr.lo + tid * 4 + t * kThreads * 4;
+            if (base < gr.hi) {
+              rp[t] = *reinterpret_cast<const float4*>(R.zp + base);
+              rq[t] = *reinterpret_cast<const float4*>(R.zq + base);
+            }
           }
-          if (acc_j < 0) {  // rejected: s_{j+1} and R_{j+1}
-            sm.bc_d[3] = st_s + st_Z / st_R;
-            st_R = st_R - sm.cqx[j];
+        } else {
+          fill_cache(R, true, gr);
+          cnode = u;
+        }
+      }
+      auto store_rows = [&]() {
+        if (!(fill && vecr)) return;
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int ci = tid * 4 + t * kThreads * 4;
+          if (gr.lo + ci < gr.hi) {
+            *reinterpret_cast<float4*>(&gr.cache[ci]) =
+                make_float4(eterm(rp[t].x, R.Mp, Tp), eterm(rq[t].x, R.Mq, Tp), eterm(rp[t].y, R.Mp, Tp),
+                            eterm(rq[t].y, R.Mq, Tp));
+            *reinterpret_cast<float4*>(&gr.cache[ci + 2]) =
+                make_float4(eterm(rp[t].z, R.Mp, Tp), eterm(rq[t].z, R.Mq, Tp), eterm(rp[t].w, R.Mp, Tp),
+                            eterm(rq[t].w, R.Mq, Tp));
           }
         }
-        __syncthreads();
-        if (acc_j >= 0) break;
-        // Z_{j+1} by one reduction, corrected for the tried tokens; f_j frozen
-        const double snew = sm.bc_d[3];
-        const double Gs = group_reduce(R, snew, gr, sm, &timed_out);
-        if (tid == 0) {
-          double Z = Gs;
-          for (int i = 0; i < ntried; ++i) Z += sm.tried_f[i] - resid_e(sm.cep[i], sm.ceq[i], R, snew);
+        gr.cstate = 2;
+        cnode = u;
+      };
+      if (tid < k) {
+        c_p = prob64(zpx, R.Mp, R.invSp, Tp);
+        c_q = prob64(zqx, R.Mq, R.invSq, Tp);
+        c_ep = eterm(zpx, R.Mp, Tp);
+        c_eq = eterm(zqx, R.Mq, Tp);
+        c_f = 0.0;
+        sm.tried_x[tid] = c_x;
+        sm.cep[tid] = c_ep;
+        sm.ceq[tid] = c_eq;
+      }
+      // Trial j of the node, by wave 0 with (w_s, w_Z, w_R) = (s_j, Z_j, R_j):
+      // accepted, or rejected with s_{j+1}, R_{j+1} computed.
+      auto trial = [&](int j, double* s_next) -> bool {
+        const double px = lane_d(c_p, j), qx = lane_d(c_q, j);
+        bool acc = false;
+        if (!__builtin_amdgcn_readlane(c_ok, j)) {
+          if (lane == 0) set_status(status, EAGLE_STATUS_TOKEN_RANGE);
+        } else {
+          const double num = w_s == 0.0 ? px : fmax(0.0, px - w_s * qx);
+          double ratio;
+          if (qx > 0.0 && w_R > 0.0) ratio = num * w_R / (w_Z * qx);
+          else ratio = num > 0.0 ? __builtin_huge_val() : 0.0;
+          const double a = ratio < 1.0 ? ratio : 1.0;
+          const double uu = (double)Uu[j];
+          if (lane == 0 && fabs(uu - a) < kTie) ++ties;
+          acc = uu < a;
+        }
+        if (!acc) {
+          *s_next = w_s + w_Z / w_R;
+          w_R = w_R - qx;
+        }
+        return acc;
+      };
+      if (tid < 64) {
+        w_s = 0.0; w_Z = 1.0; w_R = 1.0;
+        double sn = 0.0;
+        const bool a0 = trial(0, &sn);
+        if (lane == 0) { acc_j = a0 ? 0 : -1; st_s = sn; cur_j = 0; stale = 0; }
+      }
+      lds_barrier();
+      if (acc_j < 0) store_rows();
+      // Rejections: one vocabulary reduction each.  After rejecting trial j
+      // at s_{j+1}: Z_{j+1} = G(s_{j+1}) corrected for the tokens tried before
+      // j, f_j frozen, then trial j + 1 is decided in the same wave-0 pass.
+      while (acc_j < 0 && cur_j < k - 1) {
+        const int j = cur_j;
+        const double snew = st_s;
+        local_partial(R, snew, gr, sm);
+        lds_barrier();
+        if (tid < 64) {
+          const double Gs = wave0_exchange(gr, sm, &timed_out);
+          const double corr = wave_sum_d(lane < j ? c_f - resid_e(c_ep, c_eq, R, snew) : 0.0);
+          const double Z = Gs + corr;
           if (Z > 0.0) {
-            sm.tried_f[ntried] = resid_e(sm.cep[ntried], sm.ceq[ntried], R, snew);
-            st_s = snew;
-            st_Z = Z;
-            stale = 0;
+            if (lane == j) c_f = resid_e(c_ep, c_eq, R, snew);
+            w_s = snew;
+            w_Z = Z;
           } else {  // zero residual mass: keep P
-            sm.tried_f[ntried] = resid_e(sm.cep[ntried], sm.ceq[ntried], R, st_s);
-            zero_resid = 1;
-            stale = 1;
+            if (lane == j) c_f = resid_e(c_ep, c_eq, R, w_s);
+            if (lane == 0) zero_resid = 1;
           }
+          if (lane == j) sm.tried_f[j] = c_f;
+          double sn = 0.0;
+          const bool a = trial(j + 1, &sn);
+          if (lane == 0) { acc_j = a ? j + 1 : -1; st_s = sn; cur_j = j + 1; stale = Z > 0.0 ? 0 : 1; }
         }
-        __syncthreads();
-        ++ntried;
+        lds_barrier();
+        ++gr.step;
       }
       if (acc_j >= 0) {
         if (tid == 0) {
@@ -529,15 +665,38 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
             follow = 0;
           }
         }
-        __syncthreads();
+        lds_barrier();
         if (!follow) break;
         continue;
       }
-      // all k rejected: draw from the residual at st_s.  If the last reduction
-      // was not at st_s (zero-residual case), redo it.
-      s_fin = st_s;
+      // all k rejected: the last rejection (trial k - 1) still needs its
+      // reduction, then the draw from the residual at s_k (redone at the
+      // kept s when that reduction found no residual mass)
+      {
+        const int j = k - 1;
+        const double snew = st_s;
+        local_partial(R, snew, gr, sm);
+        lds_barrier();
+        if (tid < 64) {
+          const double Gs = wave0_exchange(gr, sm, &timed_out);
+          const double corr = wave_sum_d(lane < j ? c_f - resid_e(c_ep, c_eq, R, snew) : 0.0);
+          const double Z = Gs + corr;
+          if (Z > 0.0) {
+            if (lane == j) c_f = resid_e(c_ep, c_eq, R, snew);
+            w_s = snew;
+          } else {
+            if (lane == j) c_f = resid_e(c_ep, c_eq, R, w_s);
+            if (lane == 0) zero_resid = 1;
+          }
+          if (lane == j) sm.tried_f[j] = c_f;
+          if (lane == 0) { st_s = w_s; stale = Z > 0.0 ? 0 : 1; }
+        }
+        lds_barrier();
+        ++gr.step;
+      }
+      const double s_fin = st_s;
       if (stale) group_reduce(R, s_fin, gr, sm, &timed_out);
-      const int y = group_draw(R, s_fin, ntried, (double)Uu[k], gr, sm, V, &ties, &timed_out);
+      const int y = group_draw(R, s_fin, k, (double)Uu[k], gr, sm, V, &ties, &timed_out);
       if (g == 0 && tid == 0) comm[ncomm++] = y;
       break;
     }
@@ -590,11 +749,15 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
     if (e != hipSuccess) return e;
     capacity[dev] = per_cu * cus > 0 ? per_cu * cus : 1;
   }
+  // A launch covers 8 x ceil(nb / 8) x G blocks (request r on residue r mod 8),
+  // at most the resident capacity; requests beyond it go in further launches.
   const int cap = capacity[dev];
+  const int cap_x = cap / 8 > 0 ? cap / 8 : 1;  // resident blocks per residue class
+  const int cols = (B + 7) / 8;
   int G = 1;
   if (!greedy)
-    while (G * 2 <= kAccGroupCap && (size_t)B * G * 2 <= (size_t)cap && G * 2 * 1024 <= V) G *= 2;
-  const int per_launch = cap / G > 0 ? cap / G : 1;
+    while (G * 2 <= kAccGroupCap && (size_t)cols * G * 2 <= (size_t)cap_x && G * 2 * 1024 <= V) G *= 2;
+  const int per_launch = 8 * (cap_x / G > 0 ? cap_x / G : 1);
   // token cache: the slice's exponential terms stay in LDS across the passes at a node
   const int span = ((V + G - 1) / G + 3) / 4 * 4;
   int cache_tokens = (!greedy && span <= kCacheMax) ? span : 0;
@@ -604,7 +767,8 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
   Mailbox* mb = static_cast<Mailbox*>(mail);
   for (int b0 = 0; b0 < B; b0 += per_launch) {
     const int nb = B - b0 < per_launch ? B - b0 : per_launch;
-    accept_kernel<<<dim3(nb * G), dim3(kThreads), lds, st>>>(b0, G, N, V, D, k, T, cache_tokens, node_tok, node_parent,
+    accept_kernel<<<dim3(8 * ((nb + 7) / 8) * G), dim3(kThreads), lds, st>>>(b0, nb, G, N, V, D, k, T, cache_tokens,
+        node_tok, node_parent,
         node_slot, pool_tok, pool_flat, tlog, tstats, targmax, dlog, sstats, uniforms, mb, accept_len, accept_path,
         committed, n_committed, near_tie, status);
     e = hipGetLastError();
