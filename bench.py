@@ -159,7 +159,7 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda"):
 def time_commit(cfg, wts, inp, rows, T, reps=40, device="cuda"):
     """One round on a cache with room for many commits, then `reps` back-to-back
     commits of its accepted path (each appends after the last) bracketed by
-    one pair of events: time per call, launch gaps included."""
+    one pair of events: GPU time per call, gaps between launches included."""
     import torch
 
     from eagle_draft_tree_expand_amd import round as dround
@@ -171,6 +171,9 @@ def time_commit(cfg, wts, inp, rows, T, reps=40, device="cuda"):
     dr.commit(data)  # warm-up
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    # a spin kernel keeps the GPU busy while the host queues every call, so
+    # the calls run back to back and the events time the GPU, not the host
+    torch.cuda._sleep(20_000_000)
     e0.record()
     for _ in range(reps):
         dr.commit(data)

@@ -384,8 +384,8 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(int rows, int H, int V,
 }
 
 // Tiled GEMM for many rows: logits = X W^T with 256 x 256 output tiles per
-// workgroup (4 waves, each a 128 x 128 quadrant of 8 x 8 MFMA tiles with fp32
-// accumulators).  The hidden dimension goes in steps of 32 through a 4-stage
+// workgroup (8 waves, two per SIMD, each a 64 x 128 block of 4 x 8 MFMA tiles
+// with fp32 accumulators).  The hidden dimension goes in steps of 32 through a 4-stage
 // LDS ring filled by direct global-to-LDS loads (global_load_lds_dwordx4:
 // lane l's 16 bytes land at the destination + 16 l), issued three steps
 // ahead.  Every 1 KB LDS block is one MFMA operand in lane order: A block mt =
@@ -402,6 +402,19 @@ constexpr int kGBlock = 512;   // bf16 elements of one 1 KB operand block
 constexpr int kGThreads = 512;     // 8 waves: 4 row quarters x 2 column halves, two per SIMD
 constexpr int kGLoadsPerStep = 4;  // direct loads each wave issues per step (32 blocks / 8 waves)
 
+// Direct global->LDS load of 16 bytes per lane into lds + 16 * lane, issued
+// by hand: the compiler then does not track these LDS writes, and does not
+// drain every load still in flight (a vmcnt(0)) before each read of a ring
+// stage it cannot tell apart from the stages being filled.  The kernel's own
+// vmcnt waits and barriers order them: a stage is read only after every wave
+// has waited for its loads into it.  M0 holds the LDS address; one wait state
+// separates its write from the load that reads it.
+EDEV void dma16_lds(const void* g, const void* lds) {
+  const uint32_t l = (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(l), "s"(lds)
+               : "memory", "m0");
+}
+
 // s_waitcnt immediate that waits for at most n outstanding vector memory
 // operations (other counters unconstrained): vmcnt bits [3:0] and [15:14].
 EDEV constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
@@ -410,8 +423,7 @@ template <bool PACKED>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_gemm_kernel(
     int rows, int H, int V, float Tp, int nm, int nn, int bm, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ w, float* __restrict__ logits, float* __restrict__ part, int32_t* status) {
-  // the ring: four separate arrays, so that the waits for the direct loads into
-  // one of them need not cover the loads still flying into the others
+  // the ring: one array per stage
   __shared__ __attribute__((aligned(1024))) uint16_t ring0[32 * kGBlock];  // A 16 blocks | B 16 blocks
   __shared__ __attribute__((aligned(1024))) uint16_t ring1[32 * kGBlock];
   __shared__ __attribute__((aligned(1024))) uint16_t ring2[32 * kGBlock];
@@ -456,10 +468,10 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #define G_ISSUE_Q(st, dst, q)                                                                               \
   {                                                                                                         \
     const int k0 = (st) * kGK;                                                                              \
-    __builtin_amdgcn_global_load_lds(x + xoff[q] + k0, dst + (2 * wave + (q)) * kGBlock, 16, 0, 0);        \
+    dma16_lds(x + xoff[q] + k0, dst + (2 * wave + (q)) * kGBlock);                                         \
     const uint16_t* ws_ = PACKED ? wsrc[q] + ((size_t)((st) >> 1) * 8 + ((st) & 1) * 4) * 512              \
                                  : wsrc[q] + k0;                                                            \
-    __builtin_amdgcn_global_load_lds(ws_, dst + (16 + 2 * wave + (q)) * kGBlock, 16, 0, 0);                 \
+    dma16_lds(ws_, dst + (16 + 2 * wave + (q)) * kGBlock);                                                  \
   }
 #define G_ISSUE(st, dst)                                                                                    \
   {                                                                                                         \
