@@ -154,17 +154,25 @@ def _pack(path, committed, D):
     return len(path), ap, cm, len(committed)
 
 
-def accept_request(tree, target_logits, draft_rows, T, k, D, U=None, target_argmax=None):
+def accept_request(tree, target_logits, draft_rows, T, k, D, U=None, target_argmax=None, warp=None):
     """Acceptance for one request.
 
     target_logits [N, V] fp32 (row u = verify logits at flat node u);
     draft_rows [S, V] fp32; U [N, k+1] uniforms (T > 0).
+    warp = (top_k, top_p) (T > 0 only): both distributions are warped the same
+    way before the walk (oracle/warp.py, at least k tokens kept).
     Returns dict(accept_len, accept_path[D], committed[D+1], n_committed, ties).
     """
     if T > 0:
         ch = UniformChooser(U, k)
-        path, com = walk(tree, k, lambda u: softmax(target_logits[u], T),
-                         lambda s: softmax(draft_rows[s], T), ch)
+        if warp is None:
+            p_fn = lambda u: softmax(target_logits[u], T)  # noqa: E731
+            q_fn = lambda s: softmax(draft_rows[s], T)  # noqa: E731
+        else:
+            from .warp import warped_softmax
+            p_fn = lambda u: warped_softmax(target_logits[u], T, warp[0], warp[1], k)  # noqa: E731
+            q_fn = lambda s: warped_softmax(draft_rows[s], T, warp[0], warp[1], k)  # noqa: E731
+        path, com = walk(tree, k, p_fn, q_fn, ch)
         ties = ch.ties
     else:
         if target_argmax is None:

@@ -74,18 +74,26 @@ def _rel_gap(a, b):
     return abs(a - b) / max(abs(a), abs(b), 1e-300)
 
 
-def children_of_row(z, T, k, seed=0, slot=0, req=0, round_id=0):
+def children_of_row(z, T, k, seed=0, slot=0, req=0, round_id=0, warp=None):
     """Children of one expanded slot: k tokens in sampling order and their q.
 
     Greedy (T == 0): the k largest logits ordered by (z desc, id asc).
     T > 0: the k largest Gumbel keys ordered by (key desc, id asc).
+    warp = (top_k, top_p) (T > 0 only): the draws come from the warped
+    distribution (oracle/warp.py, at least k tokens kept): keys outside its
+    support are -inf, and q and S are those of the warped distribution.
     Returns (tokens int64[k], q float32[k], M, S, n_near_ties).
     """
     z = np.asarray(z, dtype=np.float32)
     V = z.shape[0]
     ids = np.arange(V)
+    w = None
     if T > 0:
         key = gumbel_keys(z, T, seed, slot, req, round_id)
+        if warp is not None:
+            from .warp import warp_support
+            w = warp_support(z, T, warp[0], warp[1], min_keep=k)
+            key = np.where(w["mask"], key, -np.inf)
     else:
         key = z.astype(np.float64)
     order = np.lexsort((ids, -key))
@@ -96,7 +104,11 @@ def children_of_row(z, T, k, seed=0, slot=0, req=0, round_id=0):
         for i in range(min(k, V - 1)):
             if _rel_gap(srt[i], srt[i + 1]) < KEY_TIE_REL:
                 ties += 1
-    M, S = softmax_stats(z, T)
+    if w is not None:
+        M, S = w["M"], w["S"]
+        ties += int(w["tie"])
+    else:
+        M, S = softmax_stats(z, T)
     t = scaled_logits(z, T).astype(np.float64)
     q = (np.exp(t[top] - M) / S).astype(np.float32)
     return top.astype(np.int64), q, M, S, ties
@@ -218,7 +230,7 @@ def build_tree(k, D, m, root_token, children_fn, frontier_fn=None):
                 pool_flat=pool_flat, slot_src=slot_src, ties=ties)
 
 
-def expand_request(rows, root_token, T, k, D, m, seed=0, req=0, round_id=0):
+def expand_request(rows, root_token, T, k, D, m, seed=0, req=0, round_id=0, warp=None):
     """Expansion of one request from its draft rows [S, V] given by slot."""
     rows = np.asarray(rows, dtype=np.float32)
     S = 1 + (D - 1) * k
@@ -227,7 +239,7 @@ def expand_request(rows, root_token, T, k, D, m, seed=0, req=0, round_id=0):
     child_ties = [0]
 
     def children_fn(s, path):
-        toks, q, M, Ssum, t = children_of_row(rows[s], T, k, seed, s, req, round_id)
+        toks, q, M, Ssum, t = children_of_row(rows[s], T, k, seed, s, req, round_id, warp)
         stats[s] = (M, Ssum)
         child_ties[0] += t
         return toks, q
@@ -238,9 +250,9 @@ def expand_request(rows, root_token, T, k, D, m, seed=0, req=0, round_id=0):
     return out
 
 
-def expand_batch(draft_logits, roots, T, k, D, m, seed=0, round_id=0):
+def expand_batch(draft_logits, roots, T, k, D, m, seed=0, round_id=0, warp=None):
     """Expansion of every request; arrays stacked on a leading batch axis."""
-    outs = [expand_request(draft_logits[b], roots[b], T, k, D, m, seed, b, round_id)
+    outs = [expand_request(draft_logits[b], roots[b], T, k, D, m, seed, b, round_id, warp)
             for b in range(len(roots))]
     res = {key: np.stack([o[key] for o in outs]) for key in outs[0] if key != "ties"}
     res["ties"] = [o["ties"] for o in outs]
