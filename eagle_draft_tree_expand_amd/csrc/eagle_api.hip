@@ -272,4 +272,16 @@ int eagle_commit_accepted(int32_t batch, int32_t n, int32_t hkv, int32_t head_di
                                      dev_status, (hipStream_t)stream));
 }
 
+int eagle_sampling_warp(int32_t rows, int32_t vocab, int32_t top_k, float top_p, int32_t min_keep, float temperature,
+                        const float* logits, float* row_stats, uint32_t* bound, int32_t* dev_status, void* stream) {
+  if (rows < 0 || rows > (1 << 24) || vocab < 1 || vocab > EAGLE_MAX_VOCAB || top_k < 0) return EAGLE_ERR_SHAPE;
+  if (!(top_p > 0.f) || !(top_p <= 1.f) || min_keep < 1 || min_keep > vocab) return EAGLE_ERR_SHAPE;
+  if (top_k != 0 && top_k < min_keep) return EAGLE_ERR_SHAPE;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return EAGLE_ERR_SHAPE;
+  if (rows == 0) return EAGLE_OK;
+  if (!logits || !row_stats || !bound) return EAGLE_ERR_NULL;
+  return launch_status(launch_warp(rows, vocab, top_k, top_p, min_keep, temperature, logits, row_stats, bound,
+                                   dev_status, (hipStream_t)stream));
+}
+
 }  // extern "C"

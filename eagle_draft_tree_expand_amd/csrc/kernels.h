@@ -49,6 +49,11 @@ hipError_t launch_commit(int B, int n, int hkv, int head_dim, int max_prefix, in
                          const void* x, void* kp, void* vp, int32_t* prefix_len, void* feat, int32_t* status,
                          hipStream_t st);
 
+// ---- sampling warps (k_warp.hip) ----
+int warp_mass_shift(int V);
+hipError_t launch_warp(int rows, int V, int top_k, float top_p, int min_keep, float T, const float* z, float* stats,
+                       uint32_t* bound, int32_t* status, hipStream_t st);
+
 // ---- attention (k_attn.hip) ----
 struct AttnPlan {
   int rows;        // query rows per (request, kv head) = n * (hq / hkv)

@@ -127,3 +127,10 @@ def commit_accepted(batch, n, hkv, head_dim, max_prefix, hidden, depth, accept_l
                                           _ptr(accept_path), _ptr(k_tree), _ptr(v_tree), _ptr(x), _ptr(k_prefix),
                                           _ptr(v_prefix), _ptr(prefix_len), _ptr(feat), _ptr(status), _stream())
     check("eagle_commit_accepted", rc)
+
+
+def sampling_warp(rows, vocab, top_k, top_p, min_keep, temperature, logits, row_stats, bound, status=None):
+    """Warp logits rows [rows, vocab]: row_stats (M, S) of the warped softmax and the kept prefix's bound."""
+    rc = _lib.load().eagle_sampling_warp(rows, vocab, int(top_k), float(top_p), int(min_keep), float(temperature),
+                                        _ptr(logits), _ptr(row_stats), _ptr(bound), _ptr(status), _stream())
+    check("eagle_sampling_warp", rc)

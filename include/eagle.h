@@ -274,6 +274,31 @@ int eagle_gather_rows_multi(int32_t n_tables, int32_t n_rows, int32_t dtype, int
                             const int32_t* idx, const int32_t* row_elems, const void* const* tables,
                             void* const* outs, int32_t* dev_status, void* stream);
 
+/* Sampling warp of logits rows: top-k, then nucleus (top-p), keeping at least
+ * min_keep tokens.
+ * Source: [HW] section 2 (with temperature, top-k or nucleus sampling the
+ * output stays exact when both distributions are adjusted the same way
+ * before the acceptance test).
+ * Each row's tokens are ordered by (t desc, id asc), t = fp32(z / T') with
+ * T' = T (T > 0) or 1.  top-k keeps the first min(top_k, vocab) (top_k = 0:
+ * all); the nucleus keeps the shortest prefix of those whose mass
+ * exp(t - max t) reaches top_p of their total, the crossing token included
+ * (top_p = 1: no nucleus cut); at least min_keep are kept.
+ * In:  logits [rows, vocab] fp32 (NaN/Inf count as -inf, status NONFINITE).
+ * Out: row_stats [rows, 2] fp32: (M, S) = (max t, sum of exp(t - M) over the
+ *        kept tokens), the statistics of the warped softmax;
+ *      bound [rows, 2] uint32: (code_b, id_b) of the last kept token, code =
+ *        the order-preserving unsigned image of fp32 t (bits ^ 0x80000000
+ *        for t >= +0, ~bits for t < 0; -0 counts as +0).  Token v is kept iff
+ *        code_v > code_b, or code_v == code_b and v <= id_b.
+ * Needs 1 <= min_keep <= vocab, top_k == 0 or top_k >= min_keep,
+ * 0 < top_p <= 1.  A tree with top-k k draws its k children without
+ * replacement from the warped draft rows, so min_keep = k there.  Nucleus
+ * masses are summed as exact fixed-point integers (2^(62 - ceil(log2 vocab))
+ * per unit), so the cut is the same on every run. */
+int eagle_sampling_warp(int32_t rows, int32_t vocab, int32_t top_k, float top_p, int32_t min_keep, float temperature,
+                        const float* logits, float* row_stats, uint32_t* bound, int32_t* dev_status, void* stream);
+
 /* Commit the accepted path to the context, after eagle_verify_accept.
  * Source: [E1] section 3.3 (the accepted tokens and their features are kept
  * for the next drafting round); [HW] section 5 (the longest consistent path

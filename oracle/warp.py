@@ -20,7 +20,10 @@ Readings:
   (t_b, id_b): token v is kept iff t_v > t_b, or t_v == t_b and v <= id_b.
 * Masses are exp(t - max t) in fp64 summed in the order above; a nucleus whose
   crossing point lies within NUCLEUS_TIE_REL of the target (relative to the
-  top-k mass) is reported as a near tie.
+  top-k mass, which is at least 1) is reported as a near tie.  The window
+  covers an implementation that sums the masses as fixed-point integers of
+  2^(62 - ceil(log2 V)) per unit: its cumulative masses differ from exact ones
+  by at most V * 2^-(63 - ceil(log2 V)), about 2e-9 at V = 128256.
 * Greedy decoding (T = 0) takes the argmax and uses no warp.
 """
 from __future__ import annotations
@@ -29,7 +32,7 @@ import numpy as np
 
 from .expand import scaled_logits
 
-NUCLEUS_TIE_REL = 1e-9
+NUCLEUS_TIE_REL = 1e-8
 
 
 def warp_support(z, T, top_k=0, top_p=1.0, min_keep=1):

@@ -183,3 +183,19 @@ def test_commit_rejects(lib):
     assert f(*ok, *ptrs[:8], None, None, None) == -1
     assert f(*ok, *ptrs[:2], FAKE + 8, *ptrs[3:], None, None) == -6
     assert f(*ok, *ptrs[:8], FAKE + 4, None, None) == -6
+
+
+def test_warp_rejects(lib):
+    f = lib.eagle_sampling_warp
+    t = [FAKE, FAKE, FAKE, None, None]
+    assert f(0, 100, 5, 0.9, 2, 1.0, *t) == 0                 # no rows: nothing to do
+    assert f(3, 0, 5, 0.9, 2, 1.0, *t) == -2
+    assert f(3, 100, -1, 0.9, 2, 1.0, *t) == -2
+    assert f(3, 100, 5, 0.0, 2, 1.0, *t) == -2                # top_p in (0, 1]
+    assert f(3, 100, 5, 1.5, 2, 1.0, *t) == -2
+    assert f(3, 100, 5, float("nan"), 2, 1.0, *t) == -2
+    assert f(3, 100, 5, 0.9, 0, 1.0, *t) == -2                # min_keep >= 1
+    assert f(3, 100, 5, 0.9, 101, 1.0, *t) == -2
+    assert f(3, 100, 5, 0.9, 6, 1.0, *t) == -2                # top_k below min_keep
+    assert f(3, 100, 0, 0.9, 6, -1.0, *t) == -2
+    assert f(3, 100, 0, 0.9, 6, 1.0, None, FAKE, FAKE, None, None) == -1
