@@ -112,15 +112,17 @@ def setup(cfg_name, T, n_sets, device="cuda"):
 LM_EVENT_EVERY = 4  # LM-head launches bracketed by events: every 4th round (an event costs ~5 us of GPU idle)
 
 
-def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda"):
+def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda", warp=None):
     """Warm up, then time exactly `steps` rounds; within them, the LM-head
-    launch of every LM_EVENT_EVERY-th round is timed with events on its stream."""
+    launch of every LM_EVENT_EVERY-th round is timed with events on its stream.
+    warp = (top_k, top_p): rounds with both distributions warped (the two row
+    warps run inside the timed rounds)."""
     import torch
 
     from eagle_draft_tree_expand_amd import round as dround
     dr = dround.DeviceRound(cfg, device)
     for i in range(warmup):
-        dr.step(wts, sets[i % len(sets)], T, round_id=i)
+        dr.step(wts, sets[i % len(sets)], T, round_id=i, warp=warp)
     nev = (steps + LM_EVENT_EVERY - 1) // LM_EVENT_EVERY
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(nev)]
     torch.cuda.synchronize()
@@ -130,7 +132,7 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda"):
     t_start.record()
     for i in range(steps):
         d = sets[i % len(sets)]
-        dr.expand(d, T, i)
+        dr.expand(d, T, i, warp)
         dr.mask_pos(d)
         dr.gather_qkv(wts)
         dr.attention(d)
@@ -140,7 +142,7 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda"):
         dr.lmhead(wts, T)
         if timed:
             ev[i // LM_EVENT_EVERY][1].record()
-        dr.accept(d, T, i)
+        dr.accept(d, T, i, warp)
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
@@ -150,7 +152,7 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda"):
     committed = 0
     for i in range(steps):
         d = sets[i % len(sets)]
-        dr.step(wts, d, T, round_id=i)
+        dr.step(wts, d, T, round_id=i, warp=warp)
         committed += int(dr.acc["n_committed"].sum().item())
     status = int(dr.status.item())
     return dict(total_ms=total_ms, wall_s=wall, lm_ms=lm_ms, committed=committed, status=status)
@@ -289,6 +291,14 @@ def main():
     }
     if not args.no_extra:
         out["commit"] = time_commit(cfg, wts, inps[0], sets[0].rows, args.temp)
+    if not args.no_extra and args.temp > 0:
+        wsteps = max(20, args.steps // 4)
+        wr = time_rounds(cfg, wts, sets, args.temp, wsteps, 5, warp=(50, 0.9))
+        out["warped"] = {"warp": "top_k 50, top_p 0.9 on draft and target rows",
+                         "trees_per_s": round(1000.0 * wsteps / wr["total_ms"] * cfg.B, 2),
+                         "committed_tokens_per_s": round(wr["committed"] / (wr["total_ms"] / 1000.0), 1),
+                         "tau_synthetic": round(wr["committed"] / (wsteps * cfg.B), 4),
+                         "device_status": wr["status"]}
     if not args.no_extra and args.config == "8b":
         gsteps = max(20, args.steps // 4)
         g = time_rounds(cfg, wts, sets, 0.0, gsteps, 5)

@@ -121,6 +121,19 @@ EDEV void wave_argmax_d(double& key, int& idx) {
   }
 }
 
+// Order-preserving unsigned image of an fp32 value (-0 counts as +0), and the
+// sampling-warp membership test: token v with scaled logit t is kept by a
+// row's warp iff it sorts at or before the row's last kept token (code_b,
+// id_b) in the order (t desc, id asc).
+EDEV uint32_t tcode(float t) {
+  const uint32_t b = __float_as_uint(t + 0.0f);
+  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+}
+EDEV bool warp_keeps(float t, int v, uint32_t code_b, uint32_t id_b) {
+  const uint32_t c = tcode(t);
+  return c > code_b || (c == code_b && (uint32_t)v <= id_b);
+}
+
 EDEV void set_status(int32_t* st, int bits) {
   if (st) atomicOr(st, bits);
 }

@@ -112,6 +112,16 @@ int eagle_expand_tree(const eagle_tree_params* p, const float* draft_logits, con
                       int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_tok, float* pool_q,
                       int32_t* pool_flat, int32_t* slot_src, float* slot_stats, void* ws, size_t ws_bytes,
                       int32_t* dev_status, void* stream) {
+  return eagle_expand_tree_warped(p, draft_logits, nullptr, root_token, node_tok, node_parent, node_depth, node_sib,
+                                  node_slot, node_value, node_q, pool_tok, pool_q, pool_flat, slot_src, slot_stats, ws,
+                                  ws_bytes, dev_status, stream);
+}
+
+int eagle_expand_tree_warped(const eagle_tree_params* p, const float* draft_logits, const uint32_t* draft_bound,
+                             const int32_t* root_token, int32_t* node_tok, int32_t* node_parent,
+                             int32_t* node_depth, int32_t* node_sib, int32_t* node_slot, float* node_value,
+                             float* node_q, int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                             float* slot_stats, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
   int rc = check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
   if (!draft_logits || !root_token || !node_tok || !node_parent || !node_depth || !node_sib || !node_slot ||
@@ -122,7 +132,7 @@ int eagle_expand_tree(const eagle_tree_params* p, const float* draft_logits, con
   const int S = 1 + (D - 1) * k;
   if (ws_bytes < kCounterBytes + exp_ws_bytes(B, S, V, k)) return EAGLE_ERR_WORKSPACE;
   return launch_status(launch_expand(B, S, V, D, k, p->m, p->temperature, p->seed, p->round_id, draft_logits,
-                                     root_token, node_tok, node_parent, node_depth, node_sib, node_slot, node_value,
+                                     draft_bound, root_token, node_tok, node_parent, node_depth, node_sib, node_slot, node_value,
                                      node_q, pool_tok, pool_q, pool_flat, slot_src, slot_stats, stage_area(ws),
                                      dev_status, (hipStream_t)stream));
 }
@@ -191,6 +201,19 @@ int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok, con
                         const float* draft_logits, const float* slot_stats, const float* uniforms,
                         int32_t* accept_len, int32_t* accept_path, int32_t* committed, int32_t* n_committed,
                         int32_t* near_tie, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  return eagle_verify_accept_warped(p, nullptr, nullptr, node_tok, node_parent, node_slot, pool_tok, pool_flat,
+                                    target_logits, target_stats, target_argmax, draft_logits, slot_stats, uniforms,
+                                    accept_len, accept_path, committed, n_committed, near_tie, ws, ws_bytes,
+                                    dev_status, stream);
+}
+
+int eagle_verify_accept_warped(const eagle_tree_params* p, const uint32_t* target_bound, const uint32_t* draft_bound,
+                               const int32_t* node_tok, const int32_t* node_parent, const int32_t* node_slot,
+                               const int32_t* pool_tok, const int32_t* pool_flat, const float* target_logits,
+                               const float* target_stats, const int32_t* target_argmax, const float* draft_logits,
+                               const float* slot_stats, const float* uniforms, int32_t* accept_len,
+                               int32_t* accept_path, int32_t* committed, int32_t* n_committed, int32_t* near_tie,
+                               void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
   int rc = check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
   const bool greedy = !(p->temperature > 0.f);
@@ -205,7 +228,8 @@ int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok, con
   if ((size_t)(static_cast<char*>(mailbox) - static_cast<char*>(ws)) + mail > ws_bytes) return EAGLE_ERR_WORKSPACE;
   return launch_status(launch_accept(p->batch, p->m + 1, p->vocab, p->depth, p->topk, p->temperature, node_tok,
                                      node_parent, node_slot, pool_tok, pool_flat, target_logits, target_stats,
-                                     target_argmax, draft_logits, slot_stats, uniforms, mailbox, accept_len,
+                                     target_argmax, draft_logits, slot_stats, greedy ? nullptr : target_bound,
+                                     greedy ? nullptr : draft_bound, uniforms, mailbox, accept_len,
                                      accept_path, committed, n_committed, near_tie, dev_status,
                                      (hipStream_t)stream));
 }

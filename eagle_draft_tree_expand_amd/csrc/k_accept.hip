@@ -61,10 +61,21 @@ struct Rows {
   const float* zq;  // draft logits row of the node's slot (unused when s == 0)
   float Mp, Mq, Tp;
   double invSp, invSq;
+  // sampling warps of the two rows (kept prefix: code and id of its last token)
+  bool wp, wq;
+  uint32_t pc, pi, qc, qi;
 };
 
-// fp32 exponential term of one logit: exp(z/T' - M), 0 for a non-finite z.
-EDEV float eterm(float z, float M, float Tp) { return isfinite(z) ? expf(z / Tp - M) : 0.f; }
+// fp32 exponential term of token v's logit: exp(z/T' - M), 0 for a
+// non-finite z or a token the row's warp drops.
+EDEV float eterm(float z, int v, float M, float Tp, bool w, uint32_t wc, uint32_t wi) {
+  if (!isfinite(z)) return 0.f;
+  const float t = z / Tp;
+  if (w && !warp_keeps(t, v, wc, wi)) return 0.f;
+  return expf(t - M);
+}
+EDEV float eterm_p(float z, int v, const Rows& R) { return eterm(z, v, R.Mp, R.Tp, R.wp, R.pc, R.pi); }
+EDEV float eterm_q(float z, int v, const Rows& R) { return eterm(z, v, R.Mq, R.Tp, R.wq, R.qc, R.qi); }
 
 // Residual of one token at s from its two terms (s == 0: p alone), in fp64.
 EDEV double resid_e(float ep, float eq, const Rows& R, double s) {
@@ -74,10 +85,12 @@ EDEV double resid_e(float ep, float eq, const Rows& R, double s) {
   return d > 0.0 ? d : 0.0;
 }
 
-// fp64 probabilities of one token (acceptance ratios and R).
-EDEV double prob64(float z, float M, double invS, float Tp) {
+// fp64 probability of token v (acceptance ratios and R); 0 if the warp drops it.
+EDEV double prob64(float z, int v, float M, double invS, float Tp, bool w, uint32_t wc, uint32_t wi) {
   if (!isfinite(z)) return 0.0;
-  return exp((double)(z / Tp) - (double)M) * invS;
+  const float t = z / Tp;
+  if (w && !warp_keeps(t, v, wc, wi)) return 0.0;
+  return exp((double)t - (double)M) * invS;
 }
 
 // Tags always carry the top bit, so zero-filled words never match.
@@ -158,8 +171,8 @@ EDEV void slice_terms(const Rows& R, bool need_q, bool from_cache, const Group& 
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    ep[e] = base + e < gr.hi ? eterm(zp[e], R.Mp, R.Tp) : 0.f;
-    eq[e] = (need_q && base + e < gr.hi) ? eterm(zq[e], R.Mq, R.Tp) : 0.f;
+    ep[e] = base + e < gr.hi ? eterm_p(zp[e], base + e, R) : 0.f;
+    eq[e] = (need_q && base + e < gr.hi) ? eterm_q(zq[e], base + e, R) : 0.f;
   }
   if (gr.cache) {
     *reinterpret_cast<float4*>(&gr.cache[ci]) = make_float4(ep[0], eq[0], ep[1], eq[1]);
@@ -408,6 +421,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     const int32_t* __restrict__ node_parent, const int32_t* __restrict__ node_slot, const int32_t* __restrict__ pool_tok,
     const int32_t* __restrict__ pool_flat, const float* __restrict__ tlog, const float* __restrict__ tstats,
     const int32_t* __restrict__ targmax, const float* __restrict__ dlog, const float* __restrict__ sstats,
+    const uint32_t* __restrict__ tbound, const uint32_t* __restrict__ dbound,
     const float* __restrict__ uniforms, Mailbox* __restrict__ mail, int32_t* accept_len, int32_t* accept_path,
     int32_t* committed, int32_t* n_committed, int32_t* near_tie, int32_t* status) {
   // dynamic LDS: [cache_tokens] token cache, then the request's tree metadata
@@ -513,6 +527,11 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       const int slot = m_slot[u];
       Rows R;
       R.zp = tlog + ((size_t)b * N + u) * V;
+      R.wp = tbound != nullptr;
+      R.pc = R.wp ? tbound[((size_t)b * N + u) * 2] : 0u;
+      R.pi = R.wp ? tbound[((size_t)b * N + u) * 2 + 1] : 0u;
+      R.wq = false;
+      R.qc = R.qi = 0u;
       R.Tp = Tp;
       R.Mp = m_tst[2 * u];
       R.invSp = 1.0 / (double)m_tst[2 * u + 1];
@@ -529,6 +548,9 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
         break;
       }
       R.zq = dlog + ((size_t)b * S + slot) * V;
+      R.wq = dbound != nullptr;
+      R.qc = R.wq ? dbound[((size_t)b * S + slot) * 2] : 0u;
+      R.qi = R.wq ? dbound[((size_t)b * S + slot) * 2 + 1] : 0u;
       R.Mq = m_sst[2 * slot];
       R.invSq = 1.0 / (double)m_sst[2 * slot + 1];
       // The node's k children (wave 0, lane i: child i): their loads go out
@@ -571,23 +593,24 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
           const int ci = tid * 4 + t * kThreads * 4;
-          if (gr.lo + ci < gr.hi) {
+          const int v = gr.lo + ci;
+          if (v < gr.hi) {
             *reinterpret_cast<float4*>(&gr.cache[ci]) =
-                make_float4(eterm(rp[t].x, R.Mp, Tp), eterm(rq[t].x, R.Mq, Tp), eterm(rp[t].y, R.Mp, Tp),
-                            eterm(rq[t].y, R.Mq, Tp));
+                make_float4(eterm_p(rp[t].x, v, R), eterm_q(rq[t].x, v, R), eterm_p(rp[t].y, v + 1, R),
+                            eterm_q(rq[t].y, v + 1, R));
             *reinterpret_cast<float4*>(&gr.cache[ci + 2]) =
-                make_float4(eterm(rp[t].z, R.Mp, Tp), eterm(rq[t].z, R.Mq, Tp), eterm(rp[t].w, R.Mp, Tp),
-                            eterm(rq[t].w, R.Mq, Tp));
+                make_float4(eterm_p(rp[t].z, v + 2, R), eterm_q(rq[t].z, v + 2, R), eterm_p(rp[t].w, v + 3, R),
+                            eterm_q(rq[t].w, v + 3, R));
           }
         }
         gr.cstate = 2;
         cnode = u;
       };
       if (tid < k) {
-        c_p = prob64(zpx, R.Mp, R.invSp, Tp);
-        c_q = prob64(zqx, R.Mq, R.invSq, Tp);
-        c_ep = eterm(zpx, R.Mp, Tp);
-        c_eq = eterm(zqx, R.Mq, Tp);
+        c_p = prob64(zpx, c_x, R.Mp, R.invSp, Tp, R.wp, R.pc, R.pi);
+        c_q = prob64(zqx, c_x, R.Mq, R.invSq, Tp, R.wq, R.qc, R.qi);
+        c_ep = eterm_p(zpx, c_x, R);
+        c_eq = eterm_q(zqx, c_x, R);
         c_f = 0.0;
         sm.tried_x[tid] = c_x;
         sm.cep[tid] = c_ep;
@@ -730,9 +753,10 @@ size_t accept_lds_max() {
 hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32_t* node_tok,
                          const int32_t* node_parent, const int32_t* node_slot, const int32_t* pool_tok,
                          const int32_t* pool_flat, const float* tlog, const float* tstats, const int32_t* targmax,
-                         const float* dlog, const float* sstats, const float* uniforms, void* mail,
-                         int32_t* accept_len, int32_t* accept_path, int32_t* committed, int32_t* n_committed,
-                         int32_t* near_tie, int32_t* status, hipStream_t st) {
+                         const float* dlog, const float* sstats, const uint32_t* tbound, const uint32_t* dbound,
+                         const float* uniforms, void* mail, int32_t* accept_len, int32_t* accept_path,
+                         int32_t* committed, int32_t* n_committed, int32_t* near_tie, int32_t* status,
+                         hipStream_t st) {
   const bool greedy = !(T > 0.f);
   // Group size: as many workgroups per request as stay co-resident; requests
   // beyond the resident capacity go in further launches.
@@ -769,7 +793,8 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
     const int nb = B - b0 < per_launch ? B - b0 : per_launch;
     accept_kernel<<<dim3(8 * ((nb + 7) / 8) * G), dim3(kThreads), lds, st>>>(b0, nb, G, N, V, D, k, T, cache_tokens,
         node_tok, node_parent,
-        node_slot, pool_tok, pool_flat, tlog, tstats, targmax, dlog, sstats, uniforms, mb, accept_len, accept_path,
+        node_slot, pool_tok, pool_flat, tlog, tstats, targmax, dlog, sstats, tbound, dbound, uniforms, mb, accept_len,
+        accept_path,
         committed, n_committed, near_tie, status);
     e = hipGetLastError();
     if (e != hipSuccess) return e;

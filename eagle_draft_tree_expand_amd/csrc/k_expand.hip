@@ -49,10 +49,14 @@ constexpr int kGreedy = 0, kSampleT1 = 1, kSampleT = 2;
 template <int MODE>
 __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
     const float* __restrict__ rows, int S, int V, float Tp, uint32_t k0, uint32_t k1,
-    uint32_t round_lo, int KP, float* __restrict__ units, int32_t* status) {
+    uint32_t round_lo, int KP, const uint32_t* __restrict__ bound, float* __restrict__ units, int32_t* status) {
   const int row = blockIdx.y;
   const int b = row / S, s = row - b * S;
   const int chunk = blockIdx.x;
+  // sampling warp of this row (null: none): tokens it drops leave the
+  // statistics and the keys alike (t = -inf)
+  const bool warped = MODE != kGreedy && bound != nullptr;
+  const uint32_t wcode = warped ? bound[(size_t)row * 2] : 0u, wid = warped ? bound[(size_t)row * 2 + 1] : 0u;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const float* z = rows + (size_t)row * V;
 
@@ -79,6 +83,7 @@ __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
       if (valid && !isfinite(x)) { bad = true; x = kNegInf; }
       if (!valid) x = kNegInf;
       t[j] = MODE == kSampleT ? x / Tp : x;
+      if (warped && !warp_keeps(t[j], base + e, wcode, wid)) t[j] = kNegInf;
       if (MODE == kGreedy) {
         key[j] = x;
       } else {
@@ -226,11 +231,12 @@ __device__ void block_argmax_256(double& key, int& idx, double* shk, int* shi) {
 
 template <bool GREEDY>
 __device__ double exact_key(const float* z, int idx, int s, int b, float Tp, uint32_t k0, uint32_t k1,
-                            uint32_t round_lo) {
+                            uint32_t round_lo, bool warped, uint32_t wcode, uint32_t wid) {
   const float zz = z[idx];
   if (!isfinite(zz)) return -__builtin_huge_val();
   if (GREEDY) return (double)zz;
   const float t = zz / Tp;
+  if (warped && !warp_keeps(t, idx, wcode, wid)) return -__builtin_huge_val();
   return (double)t + gumbel_f64(token_uniform(idx, s, b, round_lo, k0, k1));
 }
 
@@ -279,12 +285,14 @@ __device__ void block_topk(double* xkey, int* xidx, int nc, int k, double* sel_k
 template <bool GREEDY>
 __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
     const float* __restrict__ rows, int S, int V, float Tp, uint32_t k0, uint32_t k1,
-    uint32_t round_lo, int k, int KP, int C, const float* __restrict__ units,
+    uint32_t round_lo, int k, int KP, int C, const uint32_t* __restrict__ bound, const float* __restrict__ units,
     int32_t* __restrict__ pool_tok, float* __restrict__ pool_q, float* __restrict__ slot_stats,
     int32_t* status) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int row = blockIdx.x;
   const int b = row / S, s = row - b * S;
+  const bool warped = !GREEDY && bound != nullptr;
+  const uint32_t wcode = warped ? bound[(size_t)row * 2] : 0u, wid = warped ? bound[(size_t)row * 2 + 1] : 0u;
   const int tid = threadIdx.x;
   const int U = C * kExpUnitsPerChunk;
   const int UF = 2 + 2 * KP;
@@ -394,7 +402,8 @@ __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
   __syncthreads();
   if (!GREEDY) {
     const int nc = min(n_cand, kExpRescanCap);
-    for (int c = tid; c < nc; c += kExpThreads) xkey[c] = exact_key<false>(z, xidx[c], s, b, Tp, k0, k1, round_lo);
+    for (int c = tid; c < nc; c += kExpThreads)
+      xkey[c] = exact_key<false>(z, xidx[c], s, b, Tp, k0, k1, round_lo, warped, wcode, wid);
     __syncthreads();
   }
 
@@ -424,10 +433,14 @@ __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
       const float zz = z[v];
       if (!isfinite(zz)) continue;
       const float t = zz / Tp;
+      if (warped && !warp_keeps(t, v, wcode, wid)) continue;
       const float ka = t + gumbel_f32(token_uniform(v, s, b, round_lo, k0, k1));
       if ((double)ka >= thr2) {
         const int slot = atomicAdd(&n_cand, 1);
-        if (slot < kExpRescanCap) { xidx[slot] = v; xkey[slot] = exact_key<false>(z, v, s, b, Tp, k0, k1, round_lo); }
+        if (slot < kExpRescanCap) {
+          xidx[slot] = v;
+          xkey[slot] = exact_key<false>(z, v, s, b, Tp, k0, k1, round_lo, warped, wcode, wid);
+        }
       }
     }
     __syncthreads();
@@ -662,7 +675,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
 }  // namespace
 
 hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint64_t seed,
-                         uint64_t round_id, const float* rows, const int32_t* root,
+                         uint64_t round_id, const float* rows, const uint32_t* bound, const int32_t* root,
                          int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
                          int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
                          int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
@@ -675,21 +688,21 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
   const int C = exp_chunks(V);
   dim3 g1(C, B * S);
   if (greedy)
-    expand_scan_kernel<kGreedy><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, ws_units, status);
+    expand_scan_kernel<kGreedy><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, nullptr, ws_units, status);
   else if (Tp == 1.0f)
-    expand_scan_kernel<kSampleT1><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, ws_units, status);
+    expand_scan_kernel<kSampleT1><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, bound, ws_units, status);
   else
-    expand_scan_kernel<kSampleT><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, ws_units, status);
+    expand_scan_kernel<kSampleT><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, bound, ws_units, status);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int U = C * kExpUnitsPerChunk;
   const size_t sm2 = (size_t)kExpRescanCap * (sizeof(double) + sizeof(int)) +
                      (size_t)U * (1 + exp_unit_floats(k)) * sizeof(float);
   if (greedy)
-    expand_merge_kernel<true><<<B * S, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, ws_units,
+    expand_merge_kernel<true><<<B * S, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, nullptr, ws_units,
                                                              pool_tok, pool_q, slot_stats, status);
   else
-    expand_merge_kernel<false><<<B * S, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, ws_units,
+    expand_merge_kernel<false><<<B * S, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, bound, ws_units,
                                                               pool_tok, pool_q, slot_stats, status);
   e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -12,12 +12,14 @@
 // mass (fp64 sum, stored fp32), the statistics of the warped softmax.
 //
 // One workgroup of 1024 threads per row.  Each cut is a radix select on the
-// 32-bit key ~code (ascending key = descending t) in four 8-bit passes over
-// the row: a 256-bucket histogram of the weight (1 per token for counts,
-// the mass for the nucleus) of the tokens that share the key prefix chosen
-// so far, then the bucket where the running weight reaches the target; a
-// last pass over the tokens equal to the chosen key, in id order, finds the
-// token.  Masses are summed as fixed-point integers (2^mshift per unit, at
+// 32-bit key ~code (ascending key = descending t) in three passes over the
+// row (digits of 11, 11 and 10 bits): a 2048-bucket histogram of the weight
+// (1 per token for counts, the mass for the nucleus) of the tokens that
+// share the key prefix chosen so far, then the bucket where the running
+// weight reaches the target; a last pass over the tokens equal to the chosen
+// key, in id order, finds the token.  Near-flat rows put most tokens in one
+// bucket, so a wave whose lanes share a bucket adds their summed weight with
+// one atomic instead of 64.  Masses are summed as fixed-point integers (2^mshift per unit, at
 // most V * 2^mshift < 2^63): integer sums are exact and independent of the
 // order of the atomic additions, so every run cuts at the same token.
 #include "common.h"
@@ -30,11 +32,6 @@ namespace {
 constexpr int kWThreads = 1024;
 constexpr int kWWaves = kWThreads / 64;
 
-EDEV uint32_t tcode(float t) {
-  const uint32_t b = __float_as_uint(t + 0.0f);  // -0 -> +0: equal values tie
-  return b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
-}
-
 struct Cut {
   uint32_t key;  // ascending key of the last kept token (~code)
   int32_t id;
@@ -42,11 +39,17 @@ struct Cut {
 
 EDEV bool before_eq(uint32_t key, int v, const Cut& c) { return key < c.key || (key == c.key && v <= c.id); }
 
+constexpr int kWBuckets = 2048;
+constexpr int kWList = 64;  // tokens tied at a cut key handled in wave 0
+
 struct WarpSmem {
-  unsigned long long hist[256];
+  unsigned long long hist[kWBuckets];
   unsigned long long part[kWThreads / 64];
   double dred[kWWaves];
   float fred[kWWaves];
+  int list_id[kWList], sort_id[kWList];
+  unsigned long long list_w[kWList], sort_w[kWList];
+  int nlist;
   uint32_t prefix;
   unsigned long long below;
   Cut cut;
@@ -96,16 +99,45 @@ EDEV unsigned long long block_sum_u64(unsigned long long v, WarpSmem& sm) {
 
 struct RowCtx {
   const float* z;
+  bool vec;  // row 16-byte aligned and V % 4 == 0: 16-byte loads
   int V;
   float Tp;
   float M;
   double mscale;  // fixed-point units per unit mass
 };
 
-EDEV float t_of(const RowCtx& r, int v, int* bad) {
-  const float z = r.z[v];
+EDEV float t_from(const RowCtx& r, float z, int* bad) {
   if (!isfinite(z)) { *bad = 1; return kNegInf; }
-  return z / r.Tp;
+  return r.Tp == 1.0f ? z : z / r.Tp;
+}
+EDEV float t_of(const RowCtx& r, int v, int* bad) { return t_from(r, r.z[v], bad); }
+
+// The row is walked in batches of kWE = 16 tokens per thread, all of a
+// batch's loads issued before the first is used (one memory latency per
+// batch): four 16-byte loads (token v0 + 4 (j * 1024 + tid) + e) when the
+// row allows, else 16 scalar loads (token v0 + (4 j + e) * 1024 + tid).
+constexpr int kWU = 4;
+constexpr int kWE = 4 * kWU;
+constexpr int kWBatch = kWThreads * kWE;
+EDEV int tok_of(const RowCtx& r, int v0, int i) {  // token of batch element i = 4 j + e
+  return r.vec ? v0 + ((i >> 2) * kWThreads + (int)threadIdx.x) * 4 + (i & 3) : v0 + i * kWThreads + (int)threadIdx.x;
+}
+EDEV void load_batch(const RowCtx& r, int v0, float (&zz)[kWE]) {
+  if (r.vec) {
+#pragma unroll
+    for (int j = 0; j < kWU; ++j) {
+      const int base = v0 + (j * kWThreads + (int)threadIdx.x) * 4;
+      float4 q = make_float4(kNegInf, kNegInf, kNegInf, kNegInf);
+      if (base < r.V) q = *reinterpret_cast<const float4*>(r.z + base);  // V % 4 == 0: all 4 in range
+      zz[4 * j] = q.x; zz[4 * j + 1] = q.y; zz[4 * j + 2] = q.z; zz[4 * j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kWE; ++i) {
+      const int v = tok_of(r, v0, i);
+      zz[i] = v < r.V ? r.z[v] : kNegInf;
+    }
+  }
 }
 
 // Weight of token v in the select: 1 (count) or its fixed-point mass.
@@ -121,23 +153,50 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
   const int tid = threadIdx.x, lane = tid & 63;
   int bad = 0;
   if (tid == 0) { sm.prefix = 0; sm.below = 0; }
-  for (int shift = 24; shift >= 0; shift -= 8) {
-    if (tid < 256) sm.hist[tid] = 0;
+  // digits: key bits [31:21], [20:10], [9:0]
+  for (int pass = 0; pass < 3; ++pass) {
+    const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
+    const int nb = pass == 2 ? 1024 : 2048;
+    for (int x = tid; x < kWBuckets; x += kWThreads) sm.hist[x] = 0;
     __syncthreads();
     const uint32_t pre = sm.prefix;
-    for (int v = tid; v < r.V; v += kWThreads) {
-      const float t = t_of(r, v, &bad);
-      const uint32_t key = ~tcode(t);
-      if (!before_eq(key, v, lim)) continue;
-      if (shift < 24 && (key >> (shift + 8)) != (pre >> (shift + 8))) continue;
-      const unsigned long long w = weight(r, t, mass);
-      if (w) atomicAdd(&sm.hist[(key >> shift) & 255], w);
+    const int hshift = pass == 0 ? 32 : pass == 1 ? 21 : 10;  // bits above this digit must match
+    for (int v0 = 0; v0 < r.V; v0 += kWBatch) {
+      float zz[kWE];
+      load_batch(r, v0, zz);
+#pragma unroll
+      for (int j = 0; j < kWE; ++j) {
+        const int v = tok_of(r, v0, j);
+        int d = -1;
+        unsigned long long w = 0;
+        if (v < r.V) {
+          const float t = t_from(r, zz[j], &bad);
+          const uint32_t key = ~tcode(t);
+          if (before_eq(key, v, lim) && (hshift == 32 || (key >> hshift) == (pre >> hshift))) {
+            w = weight(r, t, mass);
+            if (w) d = (int)((key >> shift) & (uint32_t)(nb - 1));
+          }
+        }
+        // one atomic per wave when every contributing lane shares the bucket
+        const uint64_t act = __ballot(d >= 0);
+        if (act == 0ull) continue;
+        const int d0 = __builtin_amdgcn_readlane(d, __ffsll((long long)act) - 1);
+        if (__ballot(d >= 0 && d != d0) == 0ull) {
+          // counts: the ballot's population; masses: below 2^(mshift + 6) < 2^53 per
+          // wave, so the DPP fp64 sum of the integer weights is exact
+          const unsigned long long tot =
+              mass ? (unsigned long long)wave_sum_d((double)w) : (unsigned long long)__popcll(act);
+          if (lane == __ffsll((long long)act) - 1) atomicAdd(&sm.hist[d0], tot);
+        } else if (d >= 0) {
+          atomicAdd(&sm.hist[d], w);
+        }
+      }
     }
     __syncthreads();
-    if (tid < 64) {  // wave 0: four buckets per lane, prefix over the lanes
-      unsigned long long h[4], s = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) { h[i] = sm.hist[lane * 4 + i]; s += h[i]; }
+    if (tid < 64) {  // wave 0: nb / 64 buckets per lane, prefix over the lanes
+      const int per = nb / 64;
+      unsigned long long s = 0;
+      for (int i = 0; i < per; ++i) s += sm.hist[lane * per + i];
       unsigned long long inc = s;
 #pragma unroll
       for (int o = 1; o < 64; o <<= 1) {
@@ -156,57 +215,101 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
       }
       if (lane == l) {
         unsigned long long c = below + inc - s;
-        int d = 3;
-        for (int i = 0; i < 4; ++i) {
-          if (h[i] > 0 && (double)(c + h[i]) >= target) { d = i; break; }
-          c += h[i];
-        }
-        if (!hit) {  // the last non-empty bucket of this lane
-          c = below + inc - s;
-          for (int i = 3; i >= 0; --i)
-            if (h[i] > 0) { d = i; break; }
-          for (int i = 0; i < d; ++i) c += h[i];
+        int dd = per - 1;
+        if (hit) {
+          for (int i = 0; i < per; ++i) {
+            const unsigned long long h = sm.hist[lane * per + i];
+            if (h > 0 && (double)(c + h) >= target) { dd = i; break; }
+            c += h;
+          }
+        } else {  // the last non-empty bucket of this lane
+          for (int i = per - 1; i >= 0; --i)
+            if (sm.hist[lane * per + i] > 0) { dd = i; break; }
+          for (int i = 0; i < dd; ++i) c += sm.hist[lane * per + i];
         }
         sm.below = c;
-        sm.prefix = pre | ((uint32_t)(lane * 4 + d) << shift);
+        sm.prefix = pre | ((uint32_t)(lane * per + dd) << shift);
       }
     }
     __syncthreads();
   }
-  // tokens equal to the chosen key, in id order: contiguous id ranges per thread
+  // Tokens equal to the chosen key, in id order.  Usually a handful: they
+  // are listed in LDS and ranked by id in wave 0.  Past kWList of them (near
+  // flat rows), each thread scans a contiguous id range instead.
   const uint32_t key = sm.prefix;
-  const int C = (r.V + kWThreads - 1) / kWThreads;
-  const int v0 = min(r.V, tid * C), v1 = min(r.V, v0 + C);
-  unsigned long long mine = 0;
-  for (int v = v0; v < v1; ++v) {
-    const float t = t_of(r, v, &bad);
-    if (~tcode(t) == key && before_eq(key, v, lim)) mine += weight(r, t, mass);
-  }
-  // exclusive prefix over threads (per wave, then wave totals)
-  unsigned long long inc = mine;
+  if (tid == 0) { sm.nlist = 0; sm.cut = Cut{key, -1}; }
+  __syncthreads();
+  for (int v0 = 0; v0 < r.V; v0 += kWBatch) {
+    float zz[kWE];
+    load_batch(r, v0, zz);
 #pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const unsigned long long y = __shfl_up(inc, o);
-    if (lane >= o) inc += y;
-  }
-  if (lane == 63) sm.part[tid >> 6] = inc;
-  __syncthreads();
-  unsigned long long wpre = 0;
-  for (int w = 0; w < (tid >> 6); ++w) wpre += sm.part[w];
-  const unsigned long long below = sm.below;
-  const unsigned long long exc = below + wpre + inc - mine;
-  if (tid == 0) sm.cut = Cut{key, -1};
-  __syncthreads();
-  if (mine > 0 && (double)exc < target && (double)(exc + mine) >= target) {
-    unsigned long long c = exc;
-    for (int v = v0; v < v1; ++v) {
-      const float t = t_of(r, v, &bad);
+    for (int j = 0; j < kWE; ++j) {
+      const int v = tok_of(r, v0, j);
+      if (v >= r.V) continue;
+      const float t = t_from(r, zz[j], &bad);
       if (~tcode(t) != key || !before_eq(key, v, lim)) continue;
-      c += weight(r, t, mass);
-      if ((double)c >= target) { sm.cut = Cut{key, v}; break; }
+      const unsigned long long w = weight(r, t, mass);
+      if (!w) continue;
+      const int i = atomicAdd(&sm.nlist, 1);
+      if (i < kWList) { sm.list_id[i] = v; sm.list_w[i] = w; }
     }
   }
   __syncthreads();
+  const int nl = sm.nlist;
+  if (nl <= kWList) {
+    if (tid < 64) {  // wave 0: lane i ranks entry i by id (ids are distinct), then a prefix in id order
+      const int myid = lane < nl ? sm.list_id[lane] : 0x7fffffff;
+      const unsigned long long myw = lane < nl ? sm.list_w[lane] : 0ull;
+      int rank = 0;
+      for (int q = 0; q < nl; ++q) rank += __builtin_amdgcn_readlane(myid, q) < myid ? 1 : 0;
+      if (lane < nl) { sm.sort_id[rank] = myid; sm.sort_w[rank] = myw; }
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      const unsigned long long w = lane < nl ? sm.sort_w[lane] : 0ull;
+      unsigned long long inc = w;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const unsigned long long y = __shfl_up(inc, o);
+        if (lane >= o) inc += y;
+      }
+      const unsigned long long below = sm.below;
+      const bool hit = lane < nl && (double)(below + inc) >= target && (double)(below + inc - w) < target;
+      const uint64_t ball = __ballot(hit);
+      if (lane == 0)
+        sm.cut = Cut{key, ball ? sm.sort_id[__ffsll((long long)ball) - 1] : (nl > 0 ? sm.sort_id[nl - 1] : -1)};
+    }
+    __syncthreads();
+  } else {
+    const int C = (r.V + kWThreads - 1) / kWThreads;
+    const int v0 = min(r.V, tid * C), v1 = min(r.V, v0 + C);
+    unsigned long long mine = 0;
+    for (int v = v0; v < v1; ++v) {
+      const float t = t_of(r, v, &bad);
+      if (~tcode(t) == key && before_eq(key, v, lim)) mine += weight(r, t, mass);
+    }
+    // exclusive prefix over threads (per wave, then wave totals)
+    unsigned long long inc = mine;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const unsigned long long y = __shfl_up(inc, o);
+      if (lane >= o) inc += y;
+    }
+    if (lane == 63) sm.part[tid >> 6] = inc;
+    __syncthreads();
+    unsigned long long wpre = 0;
+    for (int w = 0; w < (tid >> 6); ++w) wpre += sm.part[w];
+    const unsigned long long exc = sm.below + wpre + inc - mine;
+    if (mine > 0 && (double)exc < target && (double)(exc + mine) >= target) {
+      unsigned long long c = exc;
+      for (int v = v0; v < v1; ++v) {
+        const float t = t_of(r, v, &bad);
+        if (~tcode(t) != key || !before_eq(key, v, lim)) continue;
+        c += weight(r, t, mass);
+        if ((double)c >= target) { sm.cut = Cut{key, v}; break; }
+      }
+    }
+    __syncthreads();
+  }
   if (sm.cut.id < 0) {  // rounding guard: the last token with this key
     if (tid == 0) {
       int last = -1;
@@ -233,13 +336,20 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
   const int row = blockIdx.x, tid = threadIdx.x;
   RowCtx r;
   r.z = z + (size_t)row * V;
+  r.vec = (V & 3) == 0 && ((uintptr_t)z & 15) == 0;
   r.V = V;
   r.Tp = Tp;
   r.mscale = ldexp(1.0, mshift);
   if (tid == 0) sm.bad = 0;
   int bad = 0;
   float lm = kNegInf;
-  for (int v = tid; v < V; v += kWThreads) lm = fmaxf(lm, t_of(r, v, &bad));
+  for (int v0 = 0; v0 < V; v0 += kWBatch) {
+    float zz[kWE];
+    load_batch(r, v0, zz);
+#pragma unroll
+    for (int j = 0; j < kWE; ++j)
+      if (tok_of(r, v0, j) < V) lm = fmaxf(lm, t_from(r, zz[j], &bad));
+  }
   if (bad) sm.bad = 1;
   r.M = block_max(lm, sm);
   const Cut all{0xffffffffu, 0x7fffffff};
@@ -251,9 +361,16 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
   }
   if (top_p < 1.0f) {
     unsigned long long sa = 0;
-    for (int v = tid; v < V; v += kWThreads) {
-      const float t = t_of(r, v, &bad);
-      if (before_eq(~tcode(t), v, cut)) sa += weight(r, t, true);
+    for (int v0 = 0; v0 < V; v0 += kWBatch) {
+      float zz[kWE];
+      load_batch(r, v0, zz);
+#pragma unroll
+      for (int j = 0; j < kWE; ++j) {
+        const int v = tok_of(r, v0, j);
+        if (v >= V) continue;
+        const float t = t_from(r, zz[j], &bad);
+        if (before_eq(~tcode(t), v, cut)) sa += weight(r, t, true);
+      }
     }
     sa = block_sum_u64(sa, sm);
     Cut c = select_cut(r, cut, true, (double)top_p * (double)sa, sm);
@@ -265,9 +382,16 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
   }
   double s = 0.0;
   if (r.M != kNegInf)
-    for (int v = tid; v < V; v += kWThreads) {
-      const float t = t_of(r, v, &bad);
-      if (t != kNegInf && before_eq(~tcode(t), v, cut)) s += exp((double)t - (double)r.M);
+    for (int v0 = 0; v0 < V; v0 += kWBatch) {
+      float zz[kWE];
+      load_batch(r, v0, zz);
+#pragma unroll
+      for (int j = 0; j < kWE; ++j) {
+        const int v = tok_of(r, v0, j);
+        if (v >= V) continue;
+        const float t = t_from(r, zz[j], &bad);
+        if (t != kNegInf && before_eq(~tcode(t), v, cut)) s += exp((double)t - (double)r.M);
+      }
     }
   s = block_sum_d(s, sm);
   if (tid == 0) {

@@ -21,7 +21,7 @@ inline size_t exp_ws_bytes(int B, int S, int V, int k) {
 }
 
 hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint64_t seed,
-                         uint64_t round_id, const float* rows, const int32_t* root,
+                         uint64_t round_id, const float* rows, const uint32_t* bound, const int32_t* root,
                          int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
                          int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
                          int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
@@ -121,7 +121,8 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
                          const int32_t* node_parent, const int32_t* node_slot,
                          const int32_t* pool_tok, const int32_t* pool_flat, const float* tlog,
                          const float* tstats, const int32_t* targmax, const float* dlog,
-                         const float* sstats, const float* uniforms, void* mail, int32_t* accept_len,
+                         const float* sstats, const uint32_t* tbound, const uint32_t* dbound,
+                         const float* uniforms, void* mail, int32_t* accept_len,
                          int32_t* accept_path, int32_t* committed, int32_t* n_committed,
                          int32_t* near_tie, int32_t* status, hipStream_t st);
 

@@ -37,17 +37,21 @@ def new_workspace(nbytes: int, device="cuda") -> torch.Tensor:
     return ws
 
 
-def expand_tree(p: TreeParams, draft_logits, root_token, out, ws, status=None):
+def expand_tree(p: TreeParams, draft_logits, root_token, out, ws, status=None, draft_bound=None):
     """out: dict with node_tok/node_parent/node_depth/node_sib/node_slot/node_value/node_q,
-    pool_tok/pool_q/pool_flat, slot_src, slot_stats (device tensors)."""
+    pool_tok/pool_q/pool_flat, slot_src, slot_stats (device tensors).  draft_bound: the draft
+    rows' sampling-warp bounds (eagle_sampling_warp), or None."""
     assert draft_logits.dtype == torch.float32 and draft_logits.is_contiguous()
-    rc = _lib.load().eagle_expand_tree(
-        p, _ptr(draft_logits), _ptr(root_token),
+    lib = _lib.load()
+    pre = (p, _ptr(draft_logits), _ptr(draft_bound)) if draft_bound is not None else (p, _ptr(draft_logits))
+    fn = lib.eagle_expand_tree_warped if draft_bound is not None else lib.eagle_expand_tree
+    rc = fn(
+        *pre, _ptr(root_token),
         _ptr(out["node_tok"]), _ptr(out["node_parent"]), _ptr(out["node_depth"]), _ptr(out["node_sib"]),
         _ptr(out["node_slot"]), _ptr(out["node_value"]), _ptr(out["node_q"]),
         _ptr(out["pool_tok"]), _ptr(out["pool_q"]), _ptr(out["pool_flat"]), _ptr(out["slot_src"]),
         _ptr(out["slot_stats"]), _ptr(ws), ws.numel(), _ptr(status), _stream())
-    check("eagle_expand_tree", rc)
+    check("eagle_expand_tree_warped" if draft_bound is not None else "eagle_expand_tree", rc)
 
 
 def build_tree_mask(batch, n, node_parent, node_depth, prefix_len, mask, pos, status=None):
@@ -88,9 +92,12 @@ def pack_lmhead_weight(w):
 
 
 def verify_accept(p: TreeParams, tree, target_logits, target_stats, target_argmax, draft_logits, slot_stats,
-                  uniforms, out, ws, status=None):
-    rc = _lib.load().eagle_verify_accept(
-        p, _ptr(tree["node_tok"]), _ptr(tree["node_parent"]), _ptr(tree["node_slot"]), _ptr(tree["pool_tok"]),
+                  uniforms, out, ws, status=None, target_bound=None, draft_bound=None):
+    lib = _lib.load()
+    warped = target_bound is not None or draft_bound is not None
+    pre = (p, _ptr(target_bound), _ptr(draft_bound)) if warped else (p,)
+    rc = (lib.eagle_verify_accept_warped if warped else lib.eagle_verify_accept)(
+        *pre, _ptr(tree["node_tok"]), _ptr(tree["node_parent"]), _ptr(tree["node_slot"]), _ptr(tree["pool_tok"]),
         _ptr(tree["pool_flat"]), _ptr(target_logits), _ptr(target_stats), _ptr(target_argmax),
         _ptr(draft_logits), _ptr(slot_stats), _ptr(uniforms), _ptr(out["accept_len"]), _ptr(out["accept_path"]),
         _ptr(out["committed"]), _ptr(out["n_committed"]), _ptr(out["near_tie"]), _ptr(ws), ws.numel(),

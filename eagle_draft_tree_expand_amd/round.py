@@ -108,6 +108,11 @@ class DeviceRound:
         self.logits = torch.zeros((B * N, c.V), dtype=f32, device=device)
         self.stats = z(B * N, 2, dtype=f32)
         self.argmax = z(B * N)
+        # sampling-warp outputs: bounds of the draft slot rows and of the target rows, warped target stats
+        self.d_bound = z(B * c.S, 2)
+        self.d_wstats = z(B * c.S, 2, dtype=f32)
+        self.t_bound = z(B * N, 2)
+        self.t_wstats = z(B * N, 2, dtype=f32)
         self.acc = {"accept_len": z(B), "accept_path": z(B, c.D), "committed": z(B, c.D + 1),
                     "n_committed": z(B), "near_tie": z(B)}
         self.status = z(1)
@@ -123,8 +128,16 @@ class DeviceRound:
         return ops.tree_params(self.B, c.V, depth or c.D, c.k, m or (self.N - 1), T, seed, round_id)
 
     # -- the stages -----------------------------------------------------------
-    def expand(self, data, T, round_id=0):
-        ops.expand_tree(self.params(T, round_id, data.seed), data.rows, data.roots, self.tree, self.ws, self.status)
+    def expand(self, data, T, round_id=0, warp=None):
+        """warp = (top_k, top_p) with T > 0: the draft rows are warped first (at least k tokens kept)."""
+        c = self.cfg
+        bound = None
+        if warp is not None and T > 0:
+            ops.sampling_warp(self.B * c.S, c.V, warp[0], warp[1], c.k, T, data.rows, self.d_wstats, self.d_bound,
+                              self.status)
+            bound = self.d_bound
+        ops.expand_tree(self.params(T, round_id, data.seed), data.rows, data.roots, self.tree, self.ws, self.status,
+                        draft_bound=bound)
 
     def mask_pos(self, data):
         ops.build_tree_mask(self.B, self.N, self.tree["node_parent"], self.tree["node_depth"], data.prefix_len,
@@ -147,7 +160,17 @@ class DeviceRound:
         ops.lmhead_softmax(self.B * self.N, c.H, c.V, self.x.view(self.B * self.N, c.H), w, T, self.logits,
                            self.stats, self.argmax, self.ws, status=self.status, packed=wts.packed)
 
-    def accept(self, data, T, round_id=0):
+    def accept(self, data, T, round_id=0, warp=None):
+        """warp = (top_k, top_p) with T > 0: the target rows are warped first, the draft rows were
+        warped by expand (their bounds are reused)."""
+        c = self.cfg
+        if warp is not None and T > 0:
+            ops.sampling_warp(self.B * self.N, c.V, warp[0], warp[1], c.k, T, self.logits, self.t_wstats,
+                              self.t_bound, self.status)
+            ops.verify_accept(self.params(T, round_id, data.seed), self.tree, self.logits, self.t_wstats, self.argmax,
+                              data.rows, self.tree["slot_stats"], data.uniforms, self.acc, self.ws, self.status,
+                              target_bound=self.t_bound, draft_bound=self.d_bound)
+            return
         ops.verify_accept(self.params(T, round_id, data.seed), self.tree, self.logits, self.stats, self.argmax,
                           data.rows, self.tree["slot_stats"], data.uniforms, self.acc, self.ws, self.status)
 
@@ -159,14 +182,15 @@ class DeviceRound:
                             self.acc["accept_path"], self.kt, self.vt, self.x, data.k_prefix, data.v_prefix,
                             data.prefix_len, self.feat, self.status)
 
-    def step(self, wts, data, T, round_id=0):
-        """One whole round (all five entry points, plus the q/k/v row gathers)."""
-        self.expand(data, T, round_id)
+    def step(self, wts, data, T, round_id=0, warp=None):
+        """One whole round (all five entry points, plus the q/k/v row gathers; with a
+        sampling warp, also the two row warps)."""
+        self.expand(data, T, round_id, warp)
         self.mask_pos(data)
         self.gather_qkv(wts)
         self.attention(data)
         self.lmhead(wts, T)
-        self.accept(data, T, round_id)
+        self.accept(data, T, round_id, warp)
 
     def host(self):
         """Copy every output to host numpy arrays (synchronises)."""

@@ -158,6 +158,21 @@ int eagle_expand_tree(const eagle_tree_params* p, const float* draft_logits,
                       float* slot_stats, void* ws, size_t ws_bytes, int32_t* dev_status,
                       void* stream);
 
+/* eagle_expand_tree with the draft rows warped (top-k / nucleus) before the
+ * children are drawn (T > 0; greedy ignores it).
+ * Source: [HW] section 2 (both distributions are adjusted the same way
+ * before the test).
+ * draft_bound [B * S, 2] uint32: per slot row, the kept prefix written by
+ * eagle_sampling_warp on draft_logits (same temperature, min_keep = k);
+ * NULL is no warp.  Tokens the warp drops get t = -inf: they are never
+ * children and leave slot_stats, which become the warped softmax's (M, S),
+ * and pool_q, the warped confidences.  Everything else as eagle_expand_tree. */
+int eagle_expand_tree_warped(const eagle_tree_params* p, const float* draft_logits, const uint32_t* draft_bound,
+                             const int32_t* root_token, int32_t* node_tok, int32_t* node_parent,
+                             int32_t* node_depth, int32_t* node_sib, int32_t* node_slot, float* node_value,
+                             float* node_q, int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                             float* slot_stats, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
 /* Ancestor-only tree attention mask and positions.
  * Source: [E2] "Tree Attention Mask" (each token sees only its ancestors,
  * never another branch); [HW] section 5.
@@ -252,6 +267,25 @@ int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok,
                         int32_t* accept_len, int32_t* accept_path, int32_t* committed,
                         int32_t* n_committed, int32_t* near_tie, void* ws, size_t ws_bytes,
                         int32_t* dev_status, void* stream);
+
+/* eagle_verify_accept with both distributions warped (top-k / nucleus)
+ * before the walk (T > 0; greedy ignores it).
+ * Source: [HW] section 2 (temperature, top-k or nucleus sampling stays
+ * exact when both distributions are adjusted the same way before the test).
+ * target_bound [B * N, 2] and draft_bound [B * S, 2] uint32: the kept
+ * prefixes eagle_sampling_warp wrote for the target rows and the draft slot
+ * rows (same temperature and warp, min_keep = k); NULL is no warp for that
+ * side.  target_stats and slot_stats must then be the warped (M, S) (from
+ * eagle_sampling_warp and eagle_expand_tree_warped).  Tokens a warp drops
+ * have probability 0 in every acceptance ratio, residual and draw.
+ * Everything else as eagle_verify_accept. */
+int eagle_verify_accept_warped(const eagle_tree_params* p, const uint32_t* target_bound, const uint32_t* draft_bound,
+                               const int32_t* node_tok, const int32_t* node_parent, const int32_t* node_slot,
+                               const int32_t* pool_tok, const int32_t* pool_flat, const float* target_logits,
+                               const float* target_stats, const int32_t* target_argmax, const float* draft_logits,
+                               const float* slot_stats, const float* uniforms, int32_t* accept_len,
+                               int32_t* accept_path, int32_t* committed, int32_t* n_committed, int32_t* near_tie,
+                               void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
 
 /* Row gather: out[r, :] = table[idx[r], :] for r < n_rows (row_elems elements
  * of `dtype` per row).  The verify layer's tree queries/keys/values are

@@ -85,13 +85,16 @@ def target_draft_rows(inp, T, weights=None):
     return rows
 
 
-def run_round(inp, T, rows=None, round_id=0, weights=None):
-    """Every stage of one round; returns a dict of per-stage results."""
+def run_round(inp, T, rows=None, round_id=0, weights=None, warp=None):
+    """Every stage of one round; returns a dict of per-stage results.
+
+    warp = (top_k, top_p): both distributions warped before use (T > 0; see
+    oracle/warp.py), at least k tokens kept."""
     c = inp.cfg
     wts = weights or _Weights(inp)
     if rows is None:
         rows = target_draft_rows(inp, T, wts)
-    ex = expand.expand_batch(rows, inp.roots, T, c.k, c.D, c.m, inp.gumbel_seed, round_id)
+    ex = expand.expand_batch(rows, inp.roots, T, c.k, c.D, c.m, inp.gumbel_seed, round_id, warp)
     masks = np.stack([mask.pack_bits(mask.ancestor_mask(ex["node_parent"][b])) for b in range(c.B)])
     pos = np.stack([mask.positions(ex["node_depth"][b], inp.prefix_len[b]) for b in range(c.B)])
     X = np.zeros((c.B, c.N, c.H), np.float32)
@@ -105,6 +108,6 @@ def run_round(inp, T, rows=None, round_id=0, weights=None):
     for b in range(c.B):
         tree = {key: ex[key][b] for key in ("node_tok", "node_parent", "node_slot", "pool_tok", "pool_flat")}
         acc.append(accept.accept_request(tree, z32[b * c.N:(b + 1) * c.N], rows[b], T, c.k, c.D,
-                                         inp.uniforms[b], am[b * c.N:(b + 1) * c.N]))
+                                         inp.uniforms[b], am[b * c.N:(b + 1) * c.N], warp))
     return dict(rows=rows, expand=ex, mask=masks, pos=pos, attn=O64, x=X, logits64=z64,
                 logits=z32, stats=stats, argmax=am, accept=acc)

@@ -101,3 +101,122 @@ def test_warp_full_vocab_rows():
             mask = (codes[r] > bd[r, 0]) | ((codes[r] == bd[r, 0]) & (np.arange(V) <= bd[r, 1]))
             assert np.array_equal(mask, w["mask"]), (top_k, top_p, r)
             np.testing.assert_allclose(st[r, 1], w["S"], rtol=2e-7)
+
+
+# ------------------------------------------------- warped expansion and walk
+import synth  # noqa: E402
+from gpu_helpers import compare_accept, compare_expand, small_cfg  # noqa: E402
+from oracle import accept as oaccept  # noqa: E402
+
+
+def _oracle_bounds(rows2d, T, top_k, top_p, min_keep):
+    """[R, 2] uint32 bounds and [R, 2] (M, S) of the oracle's warp of each row, plus tie flags."""
+    R = rows2d.shape[0]
+    bd = np.zeros((R, 2), np.uint32)
+    st = np.zeros((R, 2), np.float64)
+    tie = np.zeros(R, bool)
+    for r in range(R):
+        w = owarp.warp_support(rows2d[r], T, top_k, top_p, min_keep)
+        bd[r, 0] = _codes(np.array([w["t_b"]], np.float32))[0]
+        bd[r, 1] = w["id_b"]
+        st[r] = (w["M"], w["S"])
+        tie[r] = w["tie"]
+    return bd, st, tie
+
+
+def _dev_int(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).cuda()
+
+
+WARP_CASES = [("mid_bf16", {}, 1.0, (40, 1.0)), ("mid_bf16", {}, 0.7, (0, 0.9)), ("mid_bf16", dict(B=6), 1.0, (200, 0.5)),
+              ("tiny", {}, 1.0, (8, 0.8)), ("mid_bf16", dict(k=16, D=3, m=40), 1.0, (16, 0.3))]
+
+
+@pytest.mark.parametrize("name,kw,T,wp", WARP_CASES)
+def test_warped_expand_matches_oracle(name, kw, T, wp):
+    from eagle_draft_tree_expand_amd import round as dround
+    cfg = small_cfg(name, **kw)
+    inp = synth.make_inputs(cfg)
+    rows = inp.iid_draft_rows()
+    ora = oexpand.expand_batch(rows, inp.roots, T, cfg.k, cfg.D, cfg.m, inp.gumbel_seed, 0, wp)
+    bd, _, _ = _oracle_bounds(rows.reshape(cfg.B * cfg.S, cfg.V), T, wp[0], wp[1], cfg.k)
+    dr = dround.DeviceRound(cfg)
+    data = dround.DeviceInputs(inp)
+    data.set_rows(rows)
+    from eagle_draft_tree_expand_amd import ops
+    ops.expand_tree(dr.params(T, 0, data.seed), data.rows, data.roots, dr.tree, dr.ws, dr.status, draft_bound=_dev_int(bd))
+    dev = dr.host()
+    flagged = compare_expand(dev, ora, cfg.k, f"warped {name}{kw}")
+    assert flagged <= max(1, cfg.B // 4)
+    # children lie in the kept prefix; slot stats are the warped softmax's
+    codes = _codes(oexpand.scaled_logits(rows.reshape(cfg.B * cfg.S, cfg.V), T))
+    for b in range(cfg.B):
+        for s in range(cfg.S):
+            r = b * cfg.S + s
+            if s == 0 or dev["slot_src"][b, s] >= 0:
+                for x in dev["pool_tok"][b, s]:
+                    assert codes[r, x] > bd[r, 0] or (codes[r, x] == bd[r, 0] and x <= bd[r, 1])
+                np.testing.assert_allclose(dev["slot_stats"][b, s, 1], ora["slot_stats"][b, s, 1], rtol=1e-5)
+
+
+@pytest.mark.parametrize("mode", ["independent", "close"])
+@pytest.mark.parametrize("name,kw,T,wp", WARP_CASES[:4])
+def test_warped_accept_matches_oracle(name, kw, T, wp, mode):
+    from eagle_draft_tree_expand_amd import round as dround
+    cfg = small_cfg(name, **kw)
+    inp = synth.make_inputs(cfg)
+    rows = inp.iid_draft_rows()
+    rng = np.random.default_rng(7)
+    ex = oexpand.expand_batch(rows, inp.roots, T, cfg.k, cfg.D, cfg.m, inp.gumbel_seed, 0, wp)
+    logits = rng.standard_normal((cfg.B * cfg.N, cfg.V)).astype(np.float32)
+    if mode == "close":
+        for b in range(cfg.B):
+            for u in range(cfg.N):
+                s = ex["node_slot"][b, u]
+                if s >= 0:
+                    logits[b * cfg.N + u] = (rows[b, s] + 0.3 * rng.standard_normal(cfg.V)).astype(np.float32)
+    tbd, tst, ttie = _oracle_bounds(logits, T, wp[0], wp[1], cfg.k)
+    dbd, _, dtie = _oracle_bounds(rows.reshape(cfg.B * cfg.S, cfg.V), T, wp[0], wp[1], cfg.k)
+    ora = []
+    for b in range(cfg.B):
+        tree = {key: ex[key][b] for key in ("node_tok", "node_parent", "node_slot", "pool_tok", "pool_flat")}
+        o = oaccept.accept_request(tree, logits[b * cfg.N:(b + 1) * cfg.N], rows[b], T, cfg.k, cfg.D, inp.uniforms[b],
+                                   warp=wp)
+        o["ties"] += int(ttie[b * cfg.N:(b + 1) * cfg.N].any() or dtie[b * cfg.S:(b + 1) * cfg.S].any())
+        ora.append(o)
+    dr = dround.DeviceRound(cfg)
+    data = dround.DeviceInputs(inp)
+    data.set_rows(rows)
+    for key in ("node_tok", "node_parent", "node_slot", "pool_tok", "pool_flat"):
+        dr.tree[key].copy_(torch.from_numpy(ex[key].astype(np.int32)))
+    dr.tree["slot_stats"].copy_(torch.from_numpy(ex["slot_stats"].astype(np.float32)))
+    dr.logits.copy_(torch.from_numpy(logits))
+    dr.t_wstats.copy_(torch.from_numpy(tst.astype(np.float32)))
+    from eagle_draft_tree_expand_amd import ops
+    ops.verify_accept(dr.params(T, 0, data.seed), dr.tree, dr.logits, dr.t_wstats, dr.argmax, data.rows,
+                      dr.tree["slot_stats"], data.uniforms, dr.acc, dr.ws, dr.status, target_bound=_dev_int(tbd),
+                      draft_bound=_dev_int(dbd))
+    dev = dr.host()
+    flagged = compare_accept(dev, ora, f"warped {name}{kw} {mode}")
+    assert flagged <= max(1, cfg.B // 4)
+    assert dev["status"] & 0x1 == 0
+
+
+@pytest.mark.parametrize("wp", [(30, 0.9), (0, 0.6)])
+def test_warped_round_end_to_end(wp):
+    """All device kernels chained (row warps, expansion, mask, attention, LM head, walk)
+    against the oracle's warped round (fp32, so paths agree unless a near tie is flagged)."""
+    from eagle_draft_tree_expand_amd import round as dround
+    from oracle import round as oround
+    cfg = synth.get_config("mid_f32")
+    inp = synth.make_inputs(cfg)
+    ora = oround.run_round(inp, 1.0, warp=wp)
+    dr = dround.DeviceRound(cfg)
+    wts = dround.DeviceWeights(inp)
+    data = dround.DeviceInputs(inp)
+    data.set_rows(ora["rows"])
+    dr.step(wts, data, 1.0, warp=wp)
+    dev = dr.host()
+    assert compare_expand(dev, ora["expand"], cfg.k, f"warped e2e {wp}") == 0
+    compare_accept(dev, ora["accept"], f"warped e2e {wp}")
+    assert dev["status"] & ~0x8 == 0
