@@ -299,6 +299,16 @@ def main():
                          "committed_tokens_per_s": round(wr["committed"] / (wr["total_ms"] / 1000.0), 1),
                          "tau_synthetic": round(wr["committed"] / (wsteps * cfg.B), 4),
                          "device_status": wr["status"]}
+    if not args.no_extra and args.config == "8b" and args.temp > 0:
+        # the same workload drafted as a chain (top-k 1, 8 draft tokens): tree vs chain
+        ccfg, _, cwts, csets = setup("8b_chain", args.temp, 4)
+        csteps = max(20, args.steps // 4)
+        cr = time_rounds(ccfg, cwts, csets, args.temp, csteps, 5)
+        out["chain"] = {"workload": "8b shape, chain draft (top-k 1, depth 8, m 8)",
+                        "trees_per_s": round(1000.0 * csteps / cr["total_ms"] * ccfg.B, 2),
+                        "committed_tokens_per_s": round(cr["committed"] / (cr["total_ms"] / 1000.0), 1),
+                        "tau_synthetic": round(cr["committed"] / (csteps * ccfg.B), 4)}
+        del csets, cwts
     if not args.no_extra and args.config == "8b":
         gsteps = max(20, args.steps // 4)
         g = time_rounds(cfg, wts, sets, 0.0, gsteps, 5)

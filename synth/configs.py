@@ -81,6 +81,10 @@ CONFIGS = {
                        sigma=(0.5, 2.0), seed=505),
 }
 
+# The 8B shape drafting a chain instead of a tree (top-k 1: each depth expands
+# its single child; m = D draft tokens), for the tree-vs-chain comparison.
+CONFIGS["8b_chain"] = CONFIGS["8b"].with_(name="8b_chain", k=1, m=8, temps=(1.0,))
+
 # Reduced shapes for element-by-element parity: several tiles and ragged tails
 # in every dimension (vocab not a multiple of the 256-column tile, prefix not a
 # multiple of the key chunk), yet small enough for the oracle in seconds.
