@@ -25,12 +25,23 @@ EXPORTS = ("eagle_workspace_size", "eagle_workspace_init", "eagle_expand_tree", 
            "eagle_tree_attention", "eagle_lmhead_softmax", "eagle_verify_accept", "eagle_gather_rows",
            "eagle_gather_rows_multi", "eagle_commit_accepted", "eagle_sampling_warp",
            "eagle_expand_tree_warped", "eagle_verify_accept_warped", "eagle_lmhead_packed_bytes",
-           "eagle_lmhead_pack_weight", "eagle_error_string", "eagle_abi_version")
+           "eagle_lmhead_pack_weight", "eagle_draft_workspace_size", "eagle_draft_forward", "eagle_expand_depth",
+           "eagle_expand_finish", "eagle_error_string", "eagle_abi_version")
 
 
 class TreeParams(ctypes.Structure):
     _fields_ = [("batch", c_int32), ("vocab", c_int32), ("depth", c_int32), ("topk", c_int32),
                 ("m", c_int32), ("temperature", c_float), ("seed", c_uint64), ("round_id", c_uint64)]
+
+
+class DraftDims(ctypes.Structure):
+    _fields_ = [("hidden", c_int32), ("hq", c_int32), ("hkv", c_int32), ("head_dim", c_int32), ("inter", c_int32),
+                ("max_prefix", c_int32)]
+
+
+class DraftWeights(ctypes.Structure):
+    _fields_ = [("embed", c_void_p), ("fc", c_void_p), ("qkv", c_void_p), ("o", c_void_p), ("gate_up", c_void_p),
+                ("down", c_void_p), ("lm_head", c_void_p)]
 
 
 class EagleError(RuntimeError):
@@ -60,6 +71,11 @@ _SIGS = {
                                  [_P, c_size_t, _P, _P]),
     "eagle_verify_accept_warped": (c_int32, [POINTER(TreeParams), _P, _P] + [_P] * 16 + [_P, c_size_t, _P, _P]),
     "eagle_sampling_warp": (c_int32, [c_int32, c_int32, c_int32, c_float, c_int32, c_float, _P, _P, _P, _P, _P]),
+    "eagle_draft_workspace_size": (c_size_t, [POINTER(TreeParams), POINTER(DraftDims)]),
+    "eagle_draft_forward": (c_int32, [POINTER(TreeParams), c_int32, POINTER(DraftDims), POINTER(DraftWeights)] +
+                            [_P] * 8 + [_P, c_size_t, _P, _P]),
+    "eagle_expand_depth": (c_int32, [POINTER(TreeParams), c_int32] + [_P] * 5 + [_P, c_size_t, _P, _P]),
+    "eagle_expand_finish": (c_int32, [POINTER(TreeParams)] + [_P] * 12 + [_P, _P]),
     "eagle_error_string": (c_char_p, [c_int32]),
     "eagle_abi_version": (c_int32, []),
 }

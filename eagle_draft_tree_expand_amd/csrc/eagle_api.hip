@@ -61,6 +61,30 @@ int launch_status(hipError_t e) { return e == hipSuccess ? EAGLE_OK : EAGLE_ERR_
 
 float* stage_area(void* ws) { return reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes); }
 
+// Shape checks of the draft head; fills the layout on success.
+int check_draft(const eagle_tree_params* p, const eagle_draft_dims* d, DraftLayout* lay) {
+  int rc = check_tree_params(p);
+  if (rc != EAGLE_OK) return rc;
+  if (!d) return EAGLE_ERR_NULL;
+  const int B = p->batch, k = p->topk, D = p->depth, V = p->vocab;
+  const int S = 1 + (D - 1) * k;
+  const int64_t H = d->hidden, I = d->inter, Q = (int64_t)d->hq * d->head_dim;
+  if (H < 128 || H % 128 != 0 || H > 65536 || I < 128 || I % 128 != 0 || I > (1 << 18)) return EAGLE_ERR_SHAPE;
+  if (d->max_prefix < 1) return EAGLE_ERR_SHAPE;
+  rc = check_attn(B, S, d->hq, d->hkv, d->head_dim, d->max_prefix, EAGLE_BF16);
+  if (rc != EAGLE_OK) return rc;
+  if (Q % 128 != 0) return EAGLE_ERR_SHAPE;
+  const int64_t QKV = Q + 2LL * d->hkv * d->head_dim;
+  const int R = B * k;
+  if (check_lm(R, (int)(2 * H), (int)H, EAGLE_BF16) != EAGLE_OK || check_lm(R, (int)H, (int)QKV, EAGLE_BF16) != EAGLE_OK ||
+      check_lm(R, (int)Q, (int)H, EAGLE_BF16) != EAGLE_OK || check_lm(R, (int)H, (int)(2 * I), EAGLE_BF16) != EAGLE_OK ||
+      check_lm(R, (int)I, (int)H, EAGLE_BF16) != EAGLE_OK || check_lm(R, (int)H, V, EAGLE_BF16) != EAGLE_OK)
+    return EAGLE_ERR_SHAPE;
+  if ((int64_t)B * S * (QKV > 2 * H ? QKV : 2 * H) >= ((int64_t)1 << 31)) return EAGLE_ERR_SHAPE;
+  *lay = draft_layout(B, S, k, V, (int)H, d->hq, d->hkv, d->head_dim, (int)I, d->max_prefix);
+  return EAGLE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -306,6 +330,90 @@ int eagle_sampling_warp(int32_t rows, int32_t vocab, int32_t top_k, float top_p,
   if (!logits || !row_stats || !bound) return EAGLE_ERR_NULL;
   return launch_status(launch_warp(rows, vocab, top_k, top_p, min_keep, temperature, logits, row_stats, bound,
                                    dev_status, (hipStream_t)stream));
+}
+
+size_t eagle_draft_workspace_size(const eagle_tree_params* p, const eagle_draft_dims* dims) {
+  DraftLayout lay;
+  if (check_draft(p, dims, &lay) != EAGLE_OK) return 0;
+  return lay.total;
+}
+
+int eagle_draft_forward(const eagle_tree_params* p, int32_t depth, const eagle_draft_dims* dims,
+                        const eagle_draft_weights* w, const int32_t* root_token, const void* root_feat,
+                        const void* k_prefix, const void* v_prefix, const int32_t* prefix_len,
+                        const int32_t* pool_tok, const int32_t* slot_src, float* draft_logits, void* ws,
+                        size_t ws_bytes, int32_t* dev_status, void* stream) {
+  DraftLayout lay;
+  int rc = check_draft(p, dims, &lay);
+  if (rc != EAGLE_OK) return rc;
+  if (depth < 0 || depth >= p->depth) return EAGLE_ERR_SHAPE;
+  if (!w || !w->embed || !w->fc || !w->qkv || !w->o || !w->gate_up || !w->down || !w->lm_head) return EAGLE_ERR_NULL;
+  if (!root_token || !root_feat || !k_prefix || !v_prefix || !prefix_len || !draft_logits || !ws)
+    return EAGLE_ERR_NULL;
+  if (depth > 0 && (!pool_tok || !slot_src)) return EAGLE_ERR_NULL;
+  const void* al[] = {w->embed, w->fc, w->qkv, w->o, w->gate_up, w->down, w->lm_head, root_feat, k_prefix, v_prefix,
+                      draft_logits, ws};
+  for (const void* q : al)
+    if (!aligned16(q)) return EAGLE_ERR_ALIGN;
+  if (ws_bytes < lay.total) return EAGLE_ERR_WORKSPACE;
+  DraftArgs a;
+  a.B = p->batch;
+  a.k = p->topk;
+  a.S = 1 + (p->depth - 1) * p->topk;
+  a.V = p->vocab;
+  a.H = dims->hidden;
+  a.hq = dims->hq;
+  a.hkv = dims->hkv;
+  a.dh = dims->head_dim;
+  a.I = dims->inter;
+  a.max_prefix = dims->max_prefix;
+  a.depth = depth;
+  a.scale = 1.0f / sqrtf((float)dims->head_dim);
+  a.w = *w;
+  a.root = root_token;
+  a.root_feat = root_feat;
+  a.k_prefix = k_prefix;
+  a.v_prefix = v_prefix;
+  a.prefix_len = prefix_len;
+  a.pool_tok = pool_tok;
+  a.slot_src = slot_src;
+  a.rows = draft_logits;
+  a.ws = ws;
+  a.lay = lay;
+  a.status = dev_status;
+  return launch_status(launch_draft_forward(a, (hipStream_t)stream));
+}
+
+int eagle_expand_depth(const eagle_tree_params* p, int32_t depth, const float* draft_logits, int32_t* pool_tok,
+                       float* pool_q, int32_t* slot_src, float* slot_stats, void* ws, size_t ws_bytes,
+                       int32_t* dev_status, void* stream) {
+  int rc = check_tree_params(p);
+  if (rc != EAGLE_OK) return rc;
+  if (depth < 0 || depth >= p->depth) return EAGLE_ERR_SHAPE;
+  if (!draft_logits || !pool_tok || !pool_q || !slot_src || !slot_stats || !ws) return EAGLE_ERR_NULL;
+  if (!aligned16(draft_logits)) return EAGLE_ERR_ALIGN;
+  const int B = p->batch, V = p->vocab, k = p->topk, D = p->depth;
+  const int S = 1 + (D - 1) * k;
+  if (ws_bytes < kCounterBytes + exp_ws_bytes(B, S, V, k)) return EAGLE_ERR_WORKSPACE;
+  return launch_status(launch_expand_depth(B, S, V, D, k, p->m, p->temperature, p->seed, p->round_id, depth,
+                                           draft_logits, pool_tok, pool_q, slot_src, slot_stats, stage_area(ws),
+                                           dev_status, (hipStream_t)stream));
+}
+
+int eagle_expand_finish(const eagle_tree_params* p, const int32_t* root_token, const int32_t* pool_tok,
+                        const float* pool_q, int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
+                        int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_flat,
+                        int32_t* slot_src, int32_t* dev_status, void* stream) {
+  int rc = check_tree_params(p);
+  if (rc != EAGLE_OK) return rc;
+  if (!root_token || !pool_tok || !pool_q || !node_tok || !node_parent || !node_depth || !node_sib || !node_slot ||
+      !node_value || !node_q || !pool_flat || !slot_src)
+    return EAGLE_ERR_NULL;
+  const int B = p->batch, V = p->vocab, k = p->topk, D = p->depth;
+  const int S = 1 + (D - 1) * k;
+  return launch_status(launch_expand_finish(B, S, V, D, k, p->m, root_token, node_tok, node_parent, node_depth,
+                                            node_sib, node_slot, node_value, node_q, pool_tok, pool_q, pool_flat,
+                                            slot_src, dev_status, (hipStream_t)stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,282 @@
+// Synthetic EAGLE draft head, one depth of the draft tree per call: the
+// decoder-layer forward of that depth's frontier nodes and their draft rows.
+//
+// Method: EAGLE-1 notes ("EAGLE: Speculative Sampling Requires Rethinking
+// Feature Uncertainty"), section 3.1: the head concatenates a feature with the
+// embedding of the token one step ahead, an FC layer maps the 2H values to H,
+// one decoder layer predicts the next feature and the target's LM head turns
+// it into the draft distribution; predicted features are fed back in.
+// EAGLE-3 notes, inference pipeline: a drafted token's feature is the head's
+// own output.  EAGLE-2 notes, "Expanding the Draft Tree": one draft forward per
+// depth, over the k nodes expanded at that depth.
+//
+// Per depth d (R = B * kd frontier rows, kd = 1 at the root, else k), every
+// step on the caller's stream:
+//   draft_in      x0 = [f ; E[x]] (bf16) of each frontier node, its slot's
+//                 ancestor mask row (the parent's row plus itself); at d = 0
+//                 also the per-round slot state (zero q/k/v rows, root-only
+//                 masks) so that not-yet-drafted slots stay finite
+//   GEMM fc       u = x0 Wfc^T                    (bf16 MFMA, fp32 out)
+//   norm          n1 = bf16(rms(u))
+//   GEMM qkv      [q k v] = n1 Wqkv^T
+//   draft_qkv     bf16 q/k/v rows into the slot-indexed tree buffers
+//   attention     tree attention over the draft prefix and the slot keys
+//                 (mask: root path only), all S slots as queries
+//   gather        the frontier rows of the attention output
+//   GEMM o        y = o Wo^T;  norm: h = u + y, n2 = bf16(rms(h))
+//   GEMM gate_up  [g u] = n2 Wgu^T;  draft_silu: bf16(silu(g) * u)
+//   GEMM down     y = m Wd^T;  norm: a = h + y -> bf16 feature of the slot
+//   LM head       draft rows z = a W^T written at their slots of [B, S, V]
+// The GEMMs are the streaming LM-head kernel (weights read once, straight
+// from HBM into registers; the hidden dimension split over workgroups for the
+// narrow outputs); at batch 1 every step is weight- or launch-bound.
+#include "common.h"
+#include "kernels.h"
+
+namespace eagle {
+
+namespace {
+
+constexpr int kDT = 256;  // threads of the row kernels
+
+EDEV uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+EDEV void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// One workgroup per frontier row r (request b = r / kd, slot s0 + r % kd).
+__global__ __launch_bounds__(kDT) void draft_in_kernel(
+    int depth, int kd, int s0, int S, int k, int P, int H, int V, int Q, int KV, int W,
+    const int32_t* __restrict__ root, const uint16_t* __restrict__ root_feat, const int32_t* __restrict__ pool_tok,
+    const int32_t* __restrict__ slot_src, const uint16_t* __restrict__ embed, uint16_t* __restrict__ slot_feat,
+    uint64_t* __restrict__ slot_mask, uint16_t* __restrict__ slot_q, uint16_t* __restrict__ slot_k,
+    uint16_t* __restrict__ slot_v, int32_t* __restrict__ idx, uint16_t* __restrict__ x0, int32_t* status) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const int b = r / kd, s = s0 + (r - b * kd);
+  const size_t srow = (size_t)b * S + s;
+  int tok, ps = -1;
+  if (depth == 0) {
+    tok = root[b];
+  } else {
+    const int e = slot_src[srow];
+    const bool ok = e >= 0 && e < P;
+    if (!ok && tid == 0) set_status(status, EAGLE_STATUS_BAD_TREE);
+    tok = ok ? pool_tok[(size_t)b * P + e] : 0;
+    ps = ok ? e / k : 0;
+  }
+  if (tok < 0 || tok >= V) {
+    if (tid == 0) set_status(status, EAGLE_STATUS_TOKEN_RANGE);
+    tok = tok < 0 ? 0 : V - 1;
+  }
+  if (tid == 0) idx[r] = (int32_t)srow;
+  // x0 = [f ; E[tok]] in 16-byte units (H is a multiple of 128)
+  const uint16_t* f = depth == 0 ? root_feat + (size_t)b * H : slot_feat + ((size_t)b * S + ps) * H;
+  const uint16_t* e = embed + (size_t)tok * H;
+  uint16_t* xr = x0 + (size_t)r * 2 * H;
+  const int hu = H / 8;
+  for (int u = tid; u < 2 * hu; u += kDT) {
+    const uint4 v = u < hu ? ld16(f + u * 8) : ld16(e + (u - hu) * 8);
+    st16(xr + u * 8, v);
+  }
+  // mask row: the parent's ancestors (a slot of an earlier depth) plus itself
+  for (int w = tid; w < W; w += kDT) {
+    uint64_t m = depth == 0 ? 0ull : slot_mask[((size_t)b * S + ps) * W + w];
+    if (w == (s >> 6)) m |= 1ull << (s & 63);
+    slot_mask[srow * W + w] = m;
+  }
+  if (depth != 0) return;
+  // Round start: slots 1..S-1 of this request are not drafted yet.  Their
+  // mask rows see the root only and their q/k/v rows are zero, so that the
+  // attention over all S slots reads finite values everywhere.
+  for (int x = tid; x < (S - 1) * W; x += kDT) {
+    const int s1 = 1 + x / W, w = x - (s1 - 1) * W;
+    slot_mask[((size_t)b * S + s1) * W + w] = w == 0 ? 1ull : 0ull;
+  }
+  const uint4 z = make_uint4(0u, 0u, 0u, 0u);
+  const size_t qn = (size_t)(S - 1) * Q / 8, kn = (size_t)(S - 1) * KV / 8;
+  uint16_t* q1 = slot_q + ((size_t)b * S + 1) * Q;
+  uint16_t* k1 = slot_k + ((size_t)b * S + 1) * KV;
+  uint16_t* v1 = slot_v + ((size_t)b * S + 1) * KV;
+  for (size_t u = tid; u < qn; u += kDT) st16(q1 + u * 8, z);
+  for (size_t u = tid; u < kn; u += kDT) {
+    st16(k1 + u * 8, z);
+    st16(v1 + u * 8, z);
+  }
+}
+
+// One workgroup per row: h = a + b (b optional); writes any of hout = h,
+// nout = bf16(h / sqrt(mean(h^2) + eps)), xout = bf16(h), and bf16(h) to the
+// slot-indexed feature row fout[idx[r]].
+__global__ __launch_bounds__(kDT) void draft_norm_kernel(int H, const float* __restrict__ a,
+                                                         const float* __restrict__ bsum, float* __restrict__ hout,
+                                                         uint16_t* __restrict__ nout, uint16_t* __restrict__ xout,
+                                                         uint16_t* __restrict__ fout,
+                                                         const int32_t* __restrict__ idx) {
+  __shared__ float red[kDT / 64];
+  const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const float* ar = a + (size_t)r * H;
+  const float* br = bsum ? bsum + (size_t)r * H : nullptr;
+  float ss = 0.f;
+  for (int i = tid * 4; i < H; i += kDT * 4) {
+    float4 v = *reinterpret_cast<const float4*>(ar + i);
+    if (br) {
+      const float4 w = *reinterpret_cast<const float4*>(br + i);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
+    if (hout) *reinterpret_cast<float4*>(hout + (size_t)r * H + i) = v;
+    const uint32_t lo = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v.z) | ((uint32_t)f32_to_bf16(v.w) << 16);
+    if (xout) *reinterpret_cast<uint2*>(xout + (size_t)r * H + i) = make_uint2(lo, hi);
+    if (fout) *reinterpret_cast<uint2*>(fout + (size_t)idx[r] * H + i) = make_uint2(lo, hi);
+  }
+  if (!nout) return;
+  ss = wave_sum(ss);
+  if (lane == 0) red[wave] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + 1e-6f);
+  for (int i = tid * 4; i < H; i += kDT * 4) {
+    float4 v = *reinterpret_cast<const float4*>(ar + i);
+    if (br) {
+      const float4 w = *reinterpret_cast<const float4*>(br + i);
+      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
+    }
+    const uint32_t lo = (uint32_t)f32_to_bf16(v.x * inv) | ((uint32_t)f32_to_bf16(v.y * inv) << 16);
+    const uint32_t hi = (uint32_t)f32_to_bf16(v.z * inv) | ((uint32_t)f32_to_bf16(v.w * inv) << 16);
+    *reinterpret_cast<uint2*>(nout + (size_t)r * H + i) = make_uint2(lo, hi);
+  }
+}
+
+// One workgroup per row: the fp32 [q | k | v] row to bf16 q/k/v rows of slot idx[r].
+__global__ __launch_bounds__(kDT) void draft_qkv_kernel(int Q, int KV, const float* __restrict__ qkv,
+                                                        const int32_t* __restrict__ idx, uint16_t* __restrict__ sq,
+                                                        uint16_t* __restrict__ sk, uint16_t* __restrict__ sv) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const size_t o = (size_t)idx[r];
+  const int n = Q + 2 * KV;
+  const float* src = qkv + (size_t)r * n;
+  for (int i = tid * 2; i < n; i += kDT * 2) {
+    const float2 v = *reinterpret_cast<const float2*>(src + i);
+    const uint32_t p = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    uint16_t* dst = i < Q ? sq + o * Q + i : i < Q + KV ? sk + o * KV + (i - Q) : sv + o * KV + (i - Q - KV);
+    *reinterpret_cast<uint32_t*>(dst) = p;
+  }
+}
+
+// One workgroup per row: bf16(silu(g) * u) from the fp32 [g | u] row (I each).
+__global__ __launch_bounds__(kDT) void draft_silu_kernel(int I, const float* __restrict__ gu,
+                                                         uint16_t* __restrict__ out) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* g = gu + (size_t)r * 2 * I;
+  const float* u = g + I;
+  for (int i = tid * 2; i < I; i += kDT * 2) {
+    const float2 gv = *reinterpret_cast<const float2*>(g + i), uv = *reinterpret_cast<const float2*>(u + i);
+    const float a = gv.x / (1.0f + expf(-gv.x)) * uv.x, c = gv.y / (1.0f + expf(-gv.y)) * uv.y;
+    *reinterpret_cast<uint32_t*>(out + (size_t)r * I + i) =
+        (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(c) << 16);
+  }
+}
+
+size_t up256(size_t x) { return (x + 255) / 256 * 256; }
+
+}  // namespace
+
+DraftLayout draft_layout(int B, int S, int k, int V, int H, int hq, int hkv, int dh, int I, int max_prefix) {
+  DraftLayout L;
+  const size_t Q = (size_t)hq * dh, KV = (size_t)hkv * dh, W = (size_t)(S + 63) / 64;
+  const size_t BS = (size_t)B * S, R = (size_t)B * (k > 1 ? k : 1);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o += up256(bytes); return at; };
+  L.slot_q = take(BS * Q * 2);
+  L.slot_k = take(BS * KV * 2);
+  L.slot_v = take(BS * KV * 2);
+  L.slot_feat = take(BS * H * 2);
+  L.slot_mask = take(BS * W * 8);
+  L.attn_out = take(BS * Q * 2);
+  L.idx = take(R * 4);
+  L.x0 = take(R * 2 * H * 2);
+  L.u = take(R * H * 4);
+  L.n1 = take(R * H * 2);
+  L.qkv = take(R * (Q + 2 * KV) * 4);
+  L.og = take(R * Q * 2);
+  L.h = take(R * H * 4);
+  L.n2 = take(R * H * 2);
+  L.gu = take(R * 2 * (size_t)I * 4);
+  L.mm = take(R * (size_t)I * 2);
+  L.y = take(R * H * 4);
+  L.xa = take(R * H * 2);
+  size_t g = 0;
+  const int rs[2] = {B, (int)R};
+  for (int t = 0; t < 2; ++t) {
+    const int r = rs[t];
+    const size_t c[6] = {lm_ws_bytes(r, H, 2 * H), lm_ws_bytes(r, (int)(Q + 2 * KV), H), lm_ws_bytes(r, H, (int)Q),
+                         lm_ws_bytes(r, 2 * I, H), lm_ws_bytes(r, H, I), lm_ws_bytes(r, V, H)};
+    for (size_t x : c) g = x > g ? x : g;
+  }
+  L.gemm = take(g);
+  L.plan = attn_plan(B, S, hq, hkv, dh, max_prefix, EAGLE_BF16);
+  L.attn = take(attn_ws_bytes(B, hkv, dh, L.plan));
+  L.total = o;
+  return L;
+}
+
+hipError_t launch_draft_forward(const DraftArgs& a, hipStream_t st) {
+  const DraftLayout& L = a.lay;
+  char* base = static_cast<char*>(a.ws);
+  auto P16 = [&](size_t off) { return reinterpret_cast<uint16_t*>(base + off); };
+  auto PF = [&](size_t off) { return reinterpret_cast<float*>(base + off); };
+  const int B = a.B, S = a.S, k = a.k, H = a.H, I = a.I;
+  const int Q = a.hq * a.dh, KV = a.hkv * a.dh, W = (S + 63) / 64, P = S * k;
+  const int kd = a.depth == 0 ? 1 : k, s0 = a.depth == 0 ? 0 : 1 + (a.depth - 1) * k;
+  const int R = B * kd;
+  int32_t* idx = reinterpret_cast<int32_t*>(base + L.idx);
+  float* gws = PF(L.gemm);
+  const RowMap id{1 << 30, 0, 0};
+  hipError_t e;
+#define EAGLE_CK(x) \
+  do {              \
+    e = (x);        \
+    if (e != hipSuccess) return e; \
+  } while (0)
+
+  draft_in_kernel<<<R, kDT, 0, st>>>(a.depth, kd, s0, S, k, P, H, a.V, Q, KV, W, a.root, (const uint16_t*)a.root_feat,
+                                     a.pool_tok, a.slot_src, (const uint16_t*)a.w.embed, P16(L.slot_feat),
+                                     reinterpret_cast<uint64_t*>(base + L.slot_mask), P16(L.slot_q), P16(L.slot_k),
+                                     P16(L.slot_v), idx, P16(L.x0), a.status);
+  EAGLE_CK(hipGetLastError());
+  EAGLE_CK(launch_lmhead_map(R, 2 * H, H, EAGLE_BF16, EAGLE_W_PACKED, P16(L.x0), a.w.fc, 1.f, PF(L.u), nullptr,
+                             nullptr, nullptr, gws, a.status, id, st));
+  draft_norm_kernel<<<R, kDT, 0, st>>>(H, PF(L.u), nullptr, nullptr, P16(L.n1), nullptr, nullptr, idx);
+  EAGLE_CK(hipGetLastError());
+  EAGLE_CK(launch_lmhead_map(R, H, Q + 2 * KV, EAGLE_BF16, EAGLE_W_PACKED, P16(L.n1), a.w.qkv, 1.f, PF(L.qkv),
+                             nullptr, nullptr, nullptr, gws, a.status, id, st));
+  draft_qkv_kernel<<<R, kDT, 0, st>>>(Q, KV, PF(L.qkv), idx, P16(L.slot_q), P16(L.slot_k), P16(L.slot_v));
+  EAGLE_CK(hipGetLastError());
+  EAGLE_CK(launch_attention(B, S, a.hq, a.hkv, a.dh, a.max_prefix, EAGLE_BF16, P16(L.slot_q), a.k_prefix,
+                            a.v_prefix, a.prefix_len, P16(L.slot_k), P16(L.slot_v),
+                            reinterpret_cast<const uint64_t*>(base + L.slot_mask), a.scale, P16(L.attn_out),
+                            PF(L.attn), L.plan, a.status, st));
+  GatherSet gs{};
+  gs.table[0] = P16(L.attn_out);
+  gs.out[0] = P16(L.og);
+  gs.row_units[0] = Q * 2;
+  gs.n = 1;
+  EAGLE_CK(launch_gather(R, gs, B * S, idx, a.status, st));
+  EAGLE_CK(launch_lmhead_map(R, Q, H, EAGLE_BF16, EAGLE_W_PACKED, P16(L.og), a.w.o, 1.f, PF(L.y), nullptr, nullptr,
+                             nullptr, gws, a.status, id, st));
+  draft_norm_kernel<<<R, kDT, 0, st>>>(H, PF(L.u), PF(L.y), PF(L.h), P16(L.n2), nullptr, nullptr, idx);
+  EAGLE_CK(hipGetLastError());
+  EAGLE_CK(launch_lmhead_map(R, H, 2 * I, EAGLE_BF16, EAGLE_W_PACKED, P16(L.n2), a.w.gate_up, 1.f, PF(L.gu), nullptr,
+                             nullptr, nullptr, gws, a.status, id, st));
+  draft_silu_kernel<<<R, kDT, 0, st>>>(I, PF(L.gu), P16(L.mm));
+  EAGLE_CK(hipGetLastError());
+  EAGLE_CK(launch_lmhead_map(R, I, H, EAGLE_BF16, EAGLE_W_PACKED, P16(L.mm), a.w.down, 1.f, PF(L.y), nullptr, nullptr,
+                             nullptr, gws, a.status, id, st));
+  draft_norm_kernel<<<R, kDT, 0, st>>>(H, PF(L.h), PF(L.y), nullptr, nullptr, P16(L.xa), P16(L.slot_feat), idx);
+  EAGLE_CK(hipGetLastError());
+  // draft rows of the frontier at their slots: row r -> (r / kd) * S + s0 + r % kd
+  EAGLE_CK(launch_lmhead_map(R, H, a.V, EAGLE_BF16, EAGLE_W_PACKED, P16(L.xa), a.w.lm_head, 1.f, a.rows, nullptr,
+                             nullptr, nullptr, gws, a.status, RowMap{kd, S, s0}, st));
+#undef EAGLE_CK
+  return hipSuccess;
+}
+
+}  // namespace eagle

@@ -32,6 +32,11 @@ namespace {
 
 constexpr int kPer = 16;  // logits per thread in the scan
 
+// The slots a launch covers: slots s0 .. s0 + n - 1 of every request.
+struct SlotRange {
+  int s0, n;
+};
+
 // Record of one wave's slice: [m, s, key[KP], idx[KP]] as floats (idx bit-cast).
 struct UnitView {
   float* p;
@@ -49,9 +54,11 @@ constexpr int kGreedy = 0, kSampleT1 = 1, kSampleT = 2;
 template <int MODE>
 __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
     const float* __restrict__ rows, int S, int V, float Tp, uint32_t k0, uint32_t k1,
-    uint32_t round_lo, int KP, const uint32_t* __restrict__ bound, float* __restrict__ units, int32_t* status) {
-  const int row = blockIdx.y;
-  const int b = row / S, s = row - b * S;
+    uint32_t round_lo, int KP, const uint32_t* __restrict__ bound, float* __restrict__ units, int32_t* status,
+    SlotRange sr) {
+  // grid row y: slot sr.s0 + y % sr.n of request y / sr.n (all slots: s0 = 0, n = S)
+  const int b = (int)blockIdx.y / sr.n, s = sr.s0 + ((int)blockIdx.y - b * sr.n);
+  const int row = b * S + s;
   const int chunk = blockIdx.x;
   // sampling warp of this row (null: none): tokens it drops leave the
   // statistics and the keys alike (t = -inf)
@@ -287,10 +294,10 @@ __global__ __launch_bounds__(kExpThreads) void expand_merge_kernel(
     const float* __restrict__ rows, int S, int V, float Tp, uint32_t k0, uint32_t k1,
     uint32_t round_lo, int k, int KP, int C, const uint32_t* __restrict__ bound, const float* __restrict__ units,
     int32_t* __restrict__ pool_tok, float* __restrict__ pool_q, float* __restrict__ slot_stats,
-    int32_t* status) {
+    int32_t* status, SlotRange sr) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
-  const int row = blockIdx.x;
-  const int b = row / S, s = row - b * S;
+  const int b = (int)blockIdx.x / sr.n, s = sr.s0 + ((int)blockIdx.x - b * sr.n);
+  const int row = b * S + s;
   const bool warped = !GREEDY && bound != nullptr;
   const uint32_t wcode = warped ? bound[(size_t)row * 2] : 0u, wid = warped ? bound[(size_t)row * 2 + 1] : 0u;
   const int tid = threadIdx.x;
@@ -503,7 +510,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     const int32_t* __restrict__ pool_tok_g, const float* __restrict__ pool_q_g,
     int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
     int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_flat_g,
-    int32_t* slot_src_g, int32_t* status) {
+    int32_t* slot_src_g, int32_t* status, int upto) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int P = S * k, N = m + 1;
@@ -532,8 +539,9 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
   if (tid == 0) n_sel = 0;
   __syncthreads();
 
-  // 1. Layers.
-  for (int d = 1; d <= D; ++d) {
+  // 1. Layers (1..upto; upto < D: only the frontiers up to depth upto are
+  // wanted, while the tree is still being drafted depth by depth).
+  for (int d = 1; d <= upto; ++d) {
     const int lo = layer_lo(d, k), n = layer_n(d, k), dl = d - 1;
     const uint64_t* L = lay + dl * LS;
     // threads per node: a lane group of 2^lt <= 16 lanes that fits the block
@@ -575,6 +583,11 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
       }
     }
     __syncthreads();
+  }
+
+  if (upto < D) {
+    for (int x = tid; x < S; x += nt) slot_src_g[(size_t)b * S + x] = slot_src[x];
+    return;
   }
 
   // 2. Rerank.
@@ -674,46 +687,87 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
 
 }  // namespace
 
-hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint64_t seed,
-                         uint64_t round_id, const float* rows, const uint32_t* bound, const int32_t* root,
-                         int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
-                         int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
-                         int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
-                         float* slot_stats, float* ws_units, int32_t* status, hipStream_t st) {
+namespace {
+
+// Children of the slots in `sr` (scan + merge).
+hipError_t launch_children(int B, int S, int V, int k, float T, uint64_t seed, uint64_t round_id, const float* rows,
+                           const uint32_t* bound, int32_t* pool_tok, float* pool_q, float* slot_stats,
+                           float* ws_units, int32_t* status, SlotRange sr, hipStream_t st) {
   const bool greedy = !(T > 0.f);
   const float Tp = greedy ? 1.0f : T;
   const uint32_t k0 = (uint32_t)(seed & 0xffffffffu), k1 = (uint32_t)(seed >> 32);
   const uint32_t rlo = (uint32_t)(round_id & 0xffffffffu);
   const int KP = exp_kp(k);
   const int C = exp_chunks(V);
-  dim3 g1(C, B * S);
+  dim3 g1(C, B * sr.n);
   if (greedy)
-    expand_scan_kernel<kGreedy><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, nullptr, ws_units, status);
+    expand_scan_kernel<kGreedy><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, nullptr, ws_units, status, sr);
   else if (Tp == 1.0f)
-    expand_scan_kernel<kSampleT1><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, bound, ws_units, status);
+    expand_scan_kernel<kSampleT1><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, bound, ws_units, status, sr);
   else
-    expand_scan_kernel<kSampleT><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, bound, ws_units, status);
+    expand_scan_kernel<kSampleT><<<g1, kExpThreads, 0, st>>>(rows, S, V, Tp, k0, k1, rlo, KP, bound, ws_units, status, sr);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int U = C * kExpUnitsPerChunk;
   const size_t sm2 = (size_t)kExpRescanCap * (sizeof(double) + sizeof(int)) +
                      (size_t)U * (1 + exp_unit_floats(k)) * sizeof(float);
   if (greedy)
-    expand_merge_kernel<true><<<B * S, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, nullptr, ws_units,
-                                                             pool_tok, pool_q, slot_stats, status);
+    expand_merge_kernel<true><<<B * sr.n, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, nullptr, ws_units,
+                                                                pool_tok, pool_q, slot_stats, status, sr);
   else
-    expand_merge_kernel<false><<<B * S, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, bound, ws_units,
-                                                              pool_tok, pool_q, slot_stats, status);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+    expand_merge_kernel<false><<<B * sr.n, kExpThreads, sm2, st>>>(rows, S, V, Tp, k0, k1, rlo, k, KP, C, bound, ws_units,
+                                                                 pool_tok, pool_q, slot_stats, status, sr);
+  return hipGetLastError();
+}
+
+hipError_t launch_assemble(int B, int S, int V, int D, int k, int m, int upto, const int32_t* root,
+                           int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
+                           int32_t* node_slot, float* node_value, float* node_q, const int32_t* pool_tok,
+                           const float* pool_q, int32_t* pool_flat, int32_t* slot_src, int32_t* status,
+                           hipStream_t st) {
   const int P = S * k;
   const size_t LS = (size_t)((k * k + 1) & ~1);
   const size_t sm3 = (2 * (size_t)D * LS + S + 2 * (size_t)m) * 8 + (size_t)P * 3 * 4 + (size_t)S * 4 +
                      (size_t)m * 2 * 4;
   tree_assemble_kernel<<<B, kTreeThreads, sm3, st>>>(S, k, D, m, V, root, pool_tok, pool_q, node_tok, node_parent,
-                                            node_depth, node_sib, node_slot, node_value, node_q, pool_flat,
-                                            slot_src, status);
+                                                     node_depth, node_sib, node_slot, node_value, node_q, pool_flat,
+                                                     slot_src, status, upto);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint64_t seed,
+                         uint64_t round_id, const float* rows, const uint32_t* bound, const int32_t* root,
+                         int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
+                         int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
+                         int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                         float* slot_stats, float* ws_units, int32_t* status, hipStream_t st) {
+  hipError_t e = launch_children(B, S, V, k, T, seed, round_id, rows, bound, pool_tok, pool_q, slot_stats, ws_units,
+                                 status, SlotRange{0, S}, st);
+  if (e != hipSuccess) return e;
+  return launch_assemble(B, S, V, D, k, m, D, root, node_tok, node_parent, node_depth, node_sib, node_slot,
+                         node_value, node_q, pool_tok, pool_q, pool_flat, slot_src, status, st);
+}
+
+hipError_t launch_expand_depth(int B, int S, int V, int D, int k, int m, float T, uint64_t seed, uint64_t round_id,
+                               int depth, const float* rows, int32_t* pool_tok, float* pool_q, int32_t* slot_src,
+                               float* slot_stats, float* ws_units, int32_t* status, hipStream_t st) {
+  const SlotRange sr = depth == 0 ? SlotRange{0, 1} : SlotRange{1 + (depth - 1) * k, k};
+  hipError_t e = launch_children(B, S, V, k, T, seed, round_id, rows, nullptr, pool_tok, pool_q, slot_stats, ws_units,
+                                 status, sr, st);
+  if (e != hipSuccess || depth + 1 >= D) return e;
+  // the next depth's frontier (slot_src of its slots); no node is written
+  return launch_assemble(B, S, V, D, k, m, depth + 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         nullptr, pool_tok, pool_q, nullptr, slot_src, status, st);
+}
+
+hipError_t launch_expand_finish(int B, int S, int V, int D, int k, int m, const int32_t* root, int32_t* node_tok,
+                                int32_t* node_parent, int32_t* node_depth, int32_t* node_sib, int32_t* node_slot,
+                                float* node_value, float* node_q, const int32_t* pool_tok, const float* pool_q,
+                                int32_t* pool_flat, int32_t* slot_src, int32_t* status, hipStream_t st) {
+  return launch_assemble(B, S, V, D, k, m, D, root, node_tok, node_parent, node_depth, node_sib, node_slot,
+                         node_value, node_q, pool_tok, pool_q, pool_flat, slot_src, status, st);
 }
 
 }  // namespace eagle

@@ -102,7 +102,8 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
                                                                  const uint16_t* __restrict__ x,
                                                                  const uint16_t* __restrict__ w,
                                                                  float* __restrict__ logits, float* __restrict__ part,
-                                                                 int32_t* status, int hk, float* __restrict__ partial) {
+                                                                 int32_t* status, int hk, float* __restrict__ partial,
+                                                                 RowMap rm) {
   constexpr int NT = 8;  // 16-column n-tiles per wave: 128 vocab columns
   __shared__ floatx4 xch[4][2][NT][64];  // accumulator exchange between the two hidden halves (64 KB)
   __shared__ u32x4 xst[2][2][8][64];     // X staging: [stage][hidden half][fragment ks*4 + mt][lane] (32 KB)
@@ -277,7 +278,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
         const int n = n0 + t * 16 + col;
         const float z = acc[mt][t][i];
         if (full || n < V) {
-          if (m < rows) logits[(size_t)m * V + n] = z;
+          if (m < rows) logits[(size_t)map_row(m, rm) * V + n] = z;
           chk = fmaf(z, 0.f, chk);
         }
       }
@@ -338,7 +339,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
 // Reference-precision path for small fp32 shapes.
 __global__ __launch_bounds__(256) void lmhead_f32_kernel(int rows, int H, int V, float Tp, const float* __restrict__ x,
                                                          const float* __restrict__ w, float* __restrict__ logits,
-                                                         float* __restrict__ part, int32_t* status) {
+                                                         float* __restrict__ part, int32_t* status, RowMap rm) {
   extern __shared__ float xs[];
   const int ntiles = gridDim.x;
   const int m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(int rows, int H, int V,
       const float* wr = w + (size_t)n * H;
       float a = 0.f;
       for (int k = 0; k < H; ++k) a = fmaf(xs[k], wr[k], a);
-      logits[(size_t)m * V + n] = a;
+      logits[(size_t)map_row(m, rm) * V + n] = a;
       z = a;
       if (!isfinite(z)) { set_status(status, EAGLE_STATUS_NONFINITE); z = kNegInf; }
       if (beats(z, n, zm, ai)) { zm = z; ai = n; }
@@ -422,7 +423,8 @@ EDEV constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 <<
 template <bool PACKED>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_gemm_kernel(
     int rows, int H, int V, float Tp, int nm, int nn, int bm, const uint16_t* __restrict__ x,
-    const uint16_t* __restrict__ w, float* __restrict__ logits, float* __restrict__ part, int32_t* status) {
+    const uint16_t* __restrict__ w, float* __restrict__ logits, float* __restrict__ part, int32_t* status,
+    RowMap rm) {
   // the ring: one array per stage
   __shared__ __attribute__((aligned(1024))) uint16_t ring0[32 * kGBlock];  // A 16 blocks | B 16 blocks
   __shared__ __attribute__((aligned(1024))) uint16_t ring1[32 * kGBlock];
@@ -544,7 +546,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int n = nbase + nt * 16 + col;
         float z = acc[mt][nt][i];
         if (n < V) {
-          if (m < rows) logits[(size_t)m * V + n] = z;
+          if (m < rows) logits[(size_t)map_row(m, rm) * V + n] = z;
           if (!isfinite(z)) { bad = true; z = kNegInf; }
           if (z > zm) { zm = z; ai = n; }  // columns ascend with nt: ties keep the lower id
         } else {
@@ -580,7 +582,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 // (the streaming kernel's: max z/T', sum exp, max z, tile).
 __global__ __launch_bounds__(256) void lm_combine_kernel(int rows, int V, int KS, float Tp,
                                                          const float* __restrict__ partial, float* __restrict__ logits,
-                                                         float* __restrict__ part, int32_t* status) {
+                                                         float* __restrict__ part, int32_t* status, RowMap rm) {
   __shared__ float shm[4], shs[4];
   const int tile = blockIdx.x, m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = tile * kLmTileN;
@@ -593,7 +595,7 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(int rows, int V, int KS
     if (n < V) {
       float acc = 0.f;
       for (int kz = 0; kz < KS; ++kz) acc += partial[((size_t)kz * rows + m) * V + n];
-      logits[(size_t)m * V + n] = acc;
+      logits[(size_t)map_row(m, rm) * V + n] = acc;
       v = acc;
       if (!isfinite(v)) { bad = true; v = kNegInf; }
     }
@@ -624,7 +626,7 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(int rows, int V, int KS
 // One workgroup per row: merge the row's per-tile records (fp64 sum).
 __global__ __launch_bounds__(256) void lm_finalize_kernel(int rows, int ntiles, int V, const float* __restrict__ part,
                                                           const float* __restrict__ logits, float* __restrict__ row_stats,
-                                                          int32_t* __restrict__ row_argmax) {
+                                                          int32_t* __restrict__ row_argmax, RowMap rm) {
   __shared__ float shf[4];
   __shared__ double shd[4];
   __shared__ int shi[4];
@@ -669,7 +671,7 @@ __global__ __launch_bounds__(256) void lm_finalize_kernel(int rows, int ntiles, 
     int first = kIdxNone;
     if (bz != kNegInf)
       for (int n = c0 + tid; n < c1; n += 256)
-        if (logits[(size_t)m * V + n] == bz) { first = n; break; }
+        if (logits[(size_t)map_row(m, rm) * V + n] == bz) { first = n; break; }
     first = wave_min_i(first);
     if (lane == 0) shc[wave] = first;
     __syncthreads();
@@ -728,6 +730,13 @@ hipError_t launch_pack_lmhead(int V, int H, const void* w, void* wp, hipStream_t
 hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const void* x, const void* w, float T,
                          float* logits, float* row_stats, int32_t* row_argmax, float* probs, float* ws_part,
                          int32_t* status, hipStream_t st) {
+  return launch_lmhead_map(rows, H, V, dtype, w_layout, x, w, T, logits, row_stats, row_argmax, probs, ws_part, status,
+                           RowMap{1 << 30, 0, 0}, st);
+}
+
+hipError_t launch_lmhead_map(int rows, int H, int V, int dtype, int w_layout, const void* x, const void* w, float T,
+                             float* logits, float* row_stats, int32_t* row_argmax, float* probs, float* ws_part,
+                             int32_t* status, RowMap rm, hipStream_t st) {
   const float Tp = (T > 0.f) ? T : 1.0f;
   int ntiles = lm_ntiles(V);
   if (dtype == EAGLE_BF16 && rows >= kGemmMinRows) {
@@ -739,36 +748,38 @@ hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const 
     const size_t lds = 0;
     if (w_layout == EAGLE_W_PACKED)
       lmhead_gemm_kernel<true><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
-                                                       (const uint16_t*)w, logits, ws_part, status);
+                                                       (const uint16_t*)w, logits, ws_part, status, rm);
     else
       lmhead_gemm_kernel<false><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
-                                                        (const uint16_t*)w, logits, ws_part, status);
+                                                        (const uint16_t*)w, logits, ws_part, status, rm);
   } else if (dtype == EAGLE_BF16) {
     const int ks = lm_ksplit(rows, V, H);
     float* partial = ks > 1 ? ws_part + lm_rec_floats(rows, V) : nullptr;
     dim3 grid(ntiles, lm_mtiles(rows), ks);
     if (w_layout == EAGLE_W_PACKED)
       lmhead_bf16_kernel<true><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
-                                                     ws_part, status, H / ks, partial);
+                                                     ws_part, status, H / ks, partial, rm);
     else
       lmhead_bf16_kernel<false><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
-                                                      ws_part, status, H / ks, partial);
+                                                      ws_part, status, H / ks, partial, rm);
     if (ks > 1) {
       hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
-      lm_combine_kernel<<<dim3(ntiles, rows), 256, 0, st>>>(rows, V, ks, Tp, partial, logits, ws_part, status);
+      lm_combine_kernel<<<dim3(ntiles, rows), 256, 0, st>>>(rows, V, ks, Tp, partial, logits, ws_part, status, rm);
     }
   } else {
     dim3 grid(ntiles, rows);
     lmhead_f32_kernel<<<grid, 256, (size_t)H * sizeof(float), st>>>(rows, H, V, Tp, (const float*)x,
-                                                                    (const float*)w, logits, ws_part, status);
+                                                                    (const float*)w, logits, ws_part, status, rm);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // Without row statistics the call is a plain product (the records stay unused).
+  if (row_stats == nullptr) return e;
   // A separate launch merges the per-tile records: the kernel boundary makes
   // every workgroup's records visible (an in-kernel agent-scope fence would
   // write back each XCD's whole L2 per workgroup).
-  lm_finalize_kernel<<<rows, 256, 0, st>>>(rows, ntiles, V, ws_part, logits, row_stats, row_argmax);
+  lm_finalize_kernel<<<rows, 256, 0, st>>>(rows, ntiles, V, ws_part, logits, row_stats, row_argmax, rm);
   e = hipGetLastError();
   if (e != hipSuccess || probs == nullptr) return e;
   const size_t total = (size_t)rows * V;

@@ -4,6 +4,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "../../include/eagle.h"
+
 namespace eagle {
 
 // ---- expansion (k_expand.hip) ----
@@ -26,6 +28,17 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
                          int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
                          int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
                          float* slot_stats, float* ws_units, int32_t* status, hipStream_t st);
+
+// Depth by depth: children of depth `depth`'s frontier slots (rows at their
+// slots of the [B, S, V] buffer), then the next depth's frontier into slot_src.
+hipError_t launch_expand_depth(int B, int S, int V, int D, int k, int m, float T, uint64_t seed, uint64_t round_id,
+                               int depth, const float* rows, int32_t* pool_tok, float* pool_q, int32_t* slot_src,
+                               float* slot_stats, float* ws_units, int32_t* status, hipStream_t st);
+// Rerank and flatten a complete pool.
+hipError_t launch_expand_finish(int B, int S, int V, int D, int k, int m, const int32_t* root, int32_t* node_tok,
+                                int32_t* node_parent, int32_t* node_depth, int32_t* node_sib, int32_t* node_slot,
+                                float* node_value, float* node_q, const int32_t* pool_tok, const float* pool_q,
+                                int32_t* pool_flat, int32_t* slot_src, int32_t* status, hipStream_t st);
 
 // ---- mask + gather (k_mask.hip) ----
 hipError_t launch_tree_mask(int B, int n, const int32_t* parent, const int32_t* depth,
@@ -92,7 +105,7 @@ inline int lm_gemm_ntiles(int V) { return (V + kGemmTile - 1) / kGemmTile; }
 inline int lm_ksplit(int rows, int V, int H) {
   if (rows >= kGemmMinRows) return 1;
   int ks = 256 / (lm_ntiles(V) * lm_mtiles(rows));
-  if (ks > 8) ks = 8;
+  if (ks > 32) ks = 32;
   while (ks > 1 && H % (ks * 128) != 0) --ks;
   return ks < 1 ? 1 : ks;
 }
@@ -104,8 +117,44 @@ inline size_t lm_ws_bytes(int rows, int V, int H) {
 hipError_t launch_lmhead(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,
                          float T, float* logits, float* row_stats, int32_t* row_argmax,
                          float* probs, float* ws_part, int32_t* status, hipStream_t st);
+// Output row of product row m: (m / grp) * gstride + off + m % grp, so that
+// rows of a few consecutive tree slots per request land in a [B, S, V] buffer.
+struct RowMap {
+  int grp, gstride, off;
+};
+__host__ __device__ inline int map_row(int m, RowMap rm) { return (m / rm.grp) * rm.gstride + rm.off + m % rm.grp; }
+// The same with an output row map; row_stats == nullptr skips the statistics
+// (a plain product X W^T), and probs must then be null as well.
+hipError_t launch_lmhead_map(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,
+                             float T, float* logits, float* row_stats, int32_t* row_argmax, float* probs,
+                             float* ws_part, int32_t* status, RowMap rm, hipStream_t st);
 size_t lm_packed_bytes(int V, int hidden);
 hipError_t launch_pack_lmhead(int V, int hidden, const void* w, void* wp, hipStream_t st);
+
+// ---- synthetic EAGLE draft head (k_draft.hip) ----
+// Byte offsets in the draft workspace: per-round slot state (kept across the
+// depths of a round) and per-depth scratch sized for B * k frontier rows.
+struct DraftLayout {
+  size_t slot_q, slot_k, slot_v, slot_feat, slot_mask, attn_out;
+  size_t idx, x0, u, n1, qkv, og, h, n2, gu, mm, y, xa, gemm, attn, total;
+  AttnPlan plan;
+};
+DraftLayout draft_layout(int B, int S, int k, int V, int H, int hq, int hkv, int dh, int I, int max_prefix);
+struct DraftArgs {
+  int B, S, k, V, H, hq, hkv, dh, I, max_prefix, depth;
+  float scale;
+  eagle_draft_weights w;
+  const int32_t* root;
+  const void* root_feat;
+  const void *k_prefix, *v_prefix;
+  const int32_t* prefix_len;
+  const int32_t *pool_tok, *slot_src;
+  float* rows;
+  void* ws;
+  DraftLayout lay;
+  int32_t* status;
+};
+hipError_t launch_draft_forward(const DraftArgs& a, hipStream_t st);
 
 // ---- acceptance (k_accept.hip) ----
 constexpr int kAccMaxGroup = 64;         // workgroups per request in the cooperative walk

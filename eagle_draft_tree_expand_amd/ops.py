@@ -9,7 +9,7 @@ from __future__ import annotations
 import torch
 
 from . import _lib
-from ._lib import EAGLE_BF16, EAGLE_F32, EAGLE_W_PACKED, EAGLE_W_ROWMAJOR, TreeParams, check
+from ._lib import EAGLE_BF16, EAGLE_F32, EAGLE_W_PACKED, EAGLE_W_ROWMAJOR, DraftDims, DraftWeights, TreeParams, check
 
 _DT = {torch.float32: EAGLE_F32, torch.bfloat16: EAGLE_BF16}
 
@@ -141,3 +141,42 @@ def sampling_warp(rows, vocab, top_k, top_p, min_keep, temperature, logits, row_
     rc = _lib.load().eagle_sampling_warp(rows, vocab, int(top_k), float(top_p), int(min_keep), float(temperature),
                                         _ptr(logits), _ptr(row_stats), _ptr(bound), _ptr(status), _stream())
     check("eagle_sampling_warp", rc)
+
+
+def draft_dims(hidden, hq, hkv, head_dim, inter, max_prefix) -> DraftDims:
+    return DraftDims(int(hidden), int(hq), int(hkv), int(head_dim), int(inter), int(max_prefix))
+
+
+def draft_weights(embed, fc, qkv, o, gate_up, down, lm_head) -> DraftWeights:
+    """Device tensors: embed row-major [V, H]; the others packed (pack_lmhead_weight)."""
+    return DraftWeights(*[_ptr(t) for t in (embed, fc, qkv, o, gate_up, down, lm_head)])
+
+
+def draft_workspace_size(p: TreeParams, dims: DraftDims) -> int:
+    return int(_lib.load().eagle_draft_workspace_size(p, dims))
+
+
+def draft_forward(p: TreeParams, depth, dims: DraftDims, w: DraftWeights, root_token, root_feat, k_prefix, v_prefix,
+                  prefix_len, pool_tok, slot_src, draft_logits, ws, status=None):
+    """The draft head's forward for one depth: rows of that depth's slots in draft_logits [B, S, V]."""
+    rc = _lib.load().eagle_draft_forward(p, int(depth), dims, w, _ptr(root_token), _ptr(root_feat), _ptr(k_prefix),
+                                        _ptr(v_prefix), _ptr(prefix_len), _ptr(pool_tok), _ptr(slot_src),
+                                        _ptr(draft_logits), _ptr(ws), ws.numel(), _ptr(status), _stream())
+    check("eagle_draft_forward", rc)
+
+
+def expand_depth(p: TreeParams, depth, draft_logits, tree, ws, status=None):
+    """Children of one depth's frontier slots (and the next frontier) into tree's pool arrays."""
+    rc = _lib.load().eagle_expand_depth(p, int(depth), _ptr(draft_logits), _ptr(tree["pool_tok"]),
+                                       _ptr(tree["pool_q"]), _ptr(tree["slot_src"]), _ptr(tree["slot_stats"]),
+                                       _ptr(ws), ws.numel(), _ptr(status), _stream())
+    check("eagle_expand_depth", rc)
+
+
+def expand_finish(p: TreeParams, root_token, tree, status=None):
+    rc = _lib.load().eagle_expand_finish(
+        p, _ptr(root_token), _ptr(tree["pool_tok"]), _ptr(tree["pool_q"]), _ptr(tree["node_tok"]),
+        _ptr(tree["node_parent"]), _ptr(tree["node_depth"]), _ptr(tree["node_sib"]), _ptr(tree["node_slot"]),
+        _ptr(tree["node_value"]), _ptr(tree["node_q"]), _ptr(tree["pool_flat"]), _ptr(tree["slot_src"]),
+        _ptr(status), _stream())
+    check("eagle_expand_finish", rc)

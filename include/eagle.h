@@ -366,6 +366,91 @@ int eagle_commit_accepted(int32_t batch, int32_t n, int32_t hkv, int32_t head_di
                           void* k_prefix, void* v_prefix, int32_t* prefix_len, void* feat, int32_t* dev_status,
                           void* stream);
 
+/* ---- per-depth drafting with a synthetic EAGLE draft head ------------------
+ * [E1] section 3.1, [E2] "Expanding the Draft Tree", [HW] EAGLE-3 inference
+ * pipeline: the tree is drafted one depth at a time.  Depth 0 drafts the root
+ * (slot 0); depth d >= 1 drafts the k frontier nodes the expansion picked,
+ * at slots 1 + (d-1)k .. dk.  Per depth, in this order:
+ *   eagle_draft_forward  the head's forward for that depth's frontier nodes,
+ *                        writing their draft rows at their slots;
+ *   eagle_expand_depth   their children (as eagle_expand_tree picks them from
+ *                        the same rows) and, below depth D-1, the next
+ *                        depth's frontier (slot_src of its slots);
+ * and after depth D-1 eagle_expand_finish reranks and flattens the pool
+ * exactly as eagle_expand_tree does.  Given the same draft rows, the three
+ * give eagle_expand_tree's outputs (no sampling warp on this path).
+ *
+ * The head (random weights; the pages name its parts, not their internals):
+ *   u = Wfc [f ; E[x]];  h = u + Wo attn(rms(u));
+ *   a = h + Wd (silu(Wg rms(h)) * Wu rms(h));  draft row z = Wlm a,
+ * rms(x) = x / sqrt(mean(x^2) + 1e-6), grouped-query attention with scale
+ * 1/sqrt(head_dim) and no positional rotation over the draft's prefix K/V of
+ * the request and the nodes of the node's own root path (itself included).
+ * f = root_feat[b] for the root, else the head's output a at the parent; x =
+ * the node's token.  Activations are bf16 at every matmul input (and a as fed
+ * on), accumulation fp32. */
+typedef struct {
+    int32_t hidden;      /* H, a multiple of 128                               */
+    int32_t hq, hkv;     /* query / key-value heads, hq % hkv == 0              */
+    int32_t head_dim;    /* 64 or 128; hq * head_dim a multiple of 128          */
+    int32_t inter;       /* MLP width I, a multiple of 128                      */
+    int32_t max_prefix;  /* position stride of the draft prefix K/V cache       */
+} eagle_draft_dims;
+
+/* Weights, DEVICE memory, bf16.  `embed` is row-major [vocab, H]; the others
+ * are in the packed layout eagle_lmhead_pack_weight makes from a row-major
+ * [out, in] matrix (out = its "vocab", in = its "hidden"). */
+typedef struct {
+    const void* embed;    /* [vocab, H] row-major                                 */
+    const void* fc;       /* [H, 2H]: columns 0..H-1 take f, H..2H-1 take E[x]    */
+    const void* qkv;      /* [(hq + 2 hkv) head_dim, H]: q rows, then k, then v   */
+    const void* o;        /* [H, hq head_dim]                                     */
+    const void* gate_up;  /* [2 I, H]: gate rows, then up rows                    */
+    const void* down;     /* [H, I]                                               */
+    const void* lm_head;  /* [vocab, H] (the target's LM head)                    */
+} eagle_draft_weights;
+
+/* Bytes of the draft workspace for p's batch/vocab/depth/k (0 if invalid).  It
+ * holds the per-slot state of a round (q/k/v, features and ancestor masks of
+ * the drafted slots) and per-depth scratch; it needs no initialisation. */
+size_t eagle_draft_workspace_size(const eagle_tree_params* p, const eagle_draft_dims* dims);
+
+/* The draft head's forward for depth `depth` (0 <= depth < D).
+ * In:  root_token [B] int32; root_feat [B, H] bf16 (the feature entering the
+ *        root's step); k_prefix, v_prefix [B, hkv, max_prefix, head_dim] bf16
+ *        (the draft's own cache) with prefix_len [B] (clamped to max_prefix);
+ *      pool_tok [B, P] and slot_src [B, S] as eagle_expand_depth left them
+ *        after depth - 1 (unused at depth 0).
+ * Out: draft_logits [B, S, V] fp32: the rows of this depth's slots.
+ * In/out: ws (draft workspace, ws_bytes >= eagle_draft_workspace_size): the
+ *        slot state of depths 0..depth-1 is read and this depth's is added;
+ *        depth 0 resets it.  One round's depths must run in order on one
+ *        stream with one workspace.
+ * Status: BAD_TREE (a frontier slot with no pool entry), TOKEN_RANGE,
+ *        NONFINITE (a non-finite product anywhere in the layer). */
+int eagle_draft_forward(const eagle_tree_params* p, int32_t depth, const eagle_draft_dims* dims,
+                        const eagle_draft_weights* w, const int32_t* root_token, const void* root_feat,
+                        const void* k_prefix, const void* v_prefix, const int32_t* prefix_len,
+                        const int32_t* pool_tok, const int32_t* slot_src, float* draft_logits, void* ws,
+                        size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* Children of depth `depth`'s frontier slots from their rows of draft_logits
+ * [B, S, V] (the same selection, confidences and statistics as
+ * eagle_expand_tree), written to pool_tok/pool_q [B, S, k] and slot_stats
+ * [B, S, 2] at those slots; for depth < D-1 also the next depth's frontier:
+ * slot_src [B, S] of its k slots (ranks of the newest layer by value, as in
+ * eagle_expand_tree).  ws: the round workspace (eagle_workspace_size). */
+int eagle_expand_depth(const eagle_tree_params* p, int32_t depth, const float* draft_logits, int32_t* pool_tok,
+                       float* pool_q, int32_t* slot_src, float* slot_stats, void* ws, size_t ws_bytes,
+                       int32_t* dev_status, void* stream);
+
+/* Rerank and flatten the complete pool (after depth D-1): the node arrays,
+ * pool_flat and slot_src exactly as eagle_expand_tree writes them. */
+int eagle_expand_finish(const eagle_tree_params* p, const int32_t* root_token, const int32_t* pool_tok,
+                        const float* pool_q, int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
+                        int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_flat,
+                        int32_t* slot_src, int32_t* dev_status, void* stream);
+
 /* Human-readable name of a return code. */
 const char* eagle_error_string(int32_t code);
 

@@ -199,3 +199,39 @@ def test_warp_rejects(lib):
     assert f(3, 100, 5, 0.9, 6, 1.0, *t) == -2                # top_k below min_keep
     assert f(3, 100, 0, 0.9, 6, -1.0, *t) == -2
     assert f(3, 100, 0, 0.9, 6, 1.0, None, FAKE, FAKE, None, None) == -1
+
+
+def test_draft_rejects(lib):
+    from eagle_draft_tree_expand_amd import _lib as L
+    p = L.TreeParams(2, 5003, 4, 3, 14, 1.0, 1, 0)
+    dims = L.DraftDims(512, 4, 2, 128, 1408, 400)
+    size = lib.eagle_draft_workspace_size(ctypes.byref(p), ctypes.byref(dims))
+    assert size > 0 and size % 256 == 0
+    assert lib.eagle_draft_workspace_size(ctypes.byref(p), None) == 0
+    for bad in (L.DraftDims(500, 4, 2, 128, 1408, 400),      # hidden not a multiple of 128
+                L.DraftDims(512, 4, 3, 128, 1408, 400),      # hq % hkv
+                L.DraftDims(512, 4, 2, 96, 1408, 400),       # head_dim
+                L.DraftDims(512, 4, 2, 128, 1400, 400),      # inter
+                L.DraftDims(512, 4, 2, 128, 1408, 0)):       # no prefix cache
+        assert lib.eagle_draft_workspace_size(ctypes.byref(p), ctypes.byref(bad)) == 0
+    w = L.DraftWeights(*([FAKE] * 7))
+    f = lib.eagle_draft_forward
+    args = lambda depth, wts=w, ws=size, ptrs=None: (ctypes.byref(p), depth, ctypes.byref(dims), ctypes.byref(wts),  # noqa: E731
+                                                     *(ptrs or [FAKE] * 7), FAKE, FAKE, ws, None, None)
+    assert f(*args(-1)) == -2
+    assert f(*args(4)) == -2                                               # depth < D
+    assert f(*args(0, ws=size - 256)) == -4
+    assert f(*args(0, wts=L.DraftWeights(*([FAKE] * 6 + [None])))) == -1
+    assert f(*args(0, wts=L.DraftWeights(*([FAKE + 8] + [FAKE] * 6)))) == -6
+    assert f(*args(1, ptrs=[FAKE] * 5 + [None, FAKE])) == -1                # pool_tok needed below the root
+    assert f(*args(0, ws=size - 256, ptrs=[FAKE] * 5 + [None, FAKE])) == -4  # ... but not at the root
+    assert f(*args(0, ptrs=[None] + [FAKE] * 6)) == -1
+    e = lib.eagle_expand_depth
+    assert e(ctypes.byref(p), 4, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None) == -2
+    assert e(ctypes.byref(p), 0, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None) == -6
+    assert e(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, None, None) == -4
+    assert e(ctypes.byref(p), 0, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None) == -1
+    g = lib.eagle_expand_finish
+    assert g(ctypes.byref(p), *([FAKE] * 11), None, None, None) == -1
+    bad_p = L.TreeParams(2, 5003, 4, 0, 14, 1.0, 1, 0)
+    assert g(ctypes.byref(bad_p), *([FAKE] * 12), None, None) == -2
