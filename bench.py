@@ -190,6 +190,80 @@ def time_commit(cfg, wts, inp, rows, T, reps=40, device="cuda"):
             "status": int(dr.status.item())}
 
 
+def draft_bytes(cfg, inter, prefix_total):
+    """Algorithmic HBM bytes of one drafting round (D depths): per depth the draft
+    layer's weights and the shared LM head once, the frontier's embedding rows,
+    the draft prefix K/V of every request, and the frontier's rows written by
+    the LM head and read back by the expansion."""
+    H, Q, KV, V = cfg.H, cfg.hq * cfg.dh, cfg.hkv * cfg.dh, cfg.V
+    w = 2 * (2 * H * H + H * (Q + 2 * KV) + Q * H + 3 * inter * H) + 2 * V * H
+    total = 0
+    for d in range(cfg.D):
+        R = cfg.B * (1 if d == 0 else cfg.k)
+        total += w + R * H * 2 + 2 * prefix_total * KV * 2 + 2 * R * V * 4
+    return total
+
+
+def time_drafting(cfg, wts, inp, T, steps, warmup, device="cuda"):
+    """Rounds with the tree drafted depth by depth by a synthetic EAGLE draft head
+    (random weights), then the verify pass and acceptance on the drafted rows:
+    drafting alone is timed over `steps` rounds, then whole rounds."""
+    import torch
+
+    from eagle_draft_tree_expand_amd import draft_head
+    from eagle_draft_tree_expand_amd import round as dround
+    from synth.draft import make_draft_inputs
+    t0 = time.time()
+    dinp = make_draft_inputs(cfg, 0)
+    head = draft_head.DeviceDraftHead(cfg, dinp, wts, device)
+    del dinp
+    dr = dround.DeviceRound(cfg, device)
+    data = dround.DeviceInputs(inp, device)  # its own row buffer: the drafted rows land there
+    torch.cuda.synchronize()
+    log(f"[bench] draft head for {cfg.name} ready in {time.time() - t0:.1f}s")
+    for i in range(warmup):
+        draft_head.draft_tree(head, dr, data, T, i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        draft_head.draft_tree(head, dr, data, T, i)
+    b.record()
+    torch.cuda.synchronize()
+    draft_ms = a.elapsed_time(b) / steps
+    a.record()
+    for i in range(steps):
+        draft_head.draft_tree(head, dr, data, T, i)
+        dr.mask_pos(data)
+        dr.gather_qkv(wts)
+        dr.attention(data)
+        dr.lmhead(wts, T)
+        dr.accept(data, T, i)
+    b.record()
+    torch.cuda.synchronize()
+    round_ms = a.elapsed_time(b) / steps
+    committed = 0
+    for i in range(min(steps, 8)):
+        draft_head.draft_tree(head, dr, data, T, i)
+        dr.mask_pos(data)
+        dr.gather_qkv(wts)
+        dr.attention(data)
+        dr.lmhead(wts, T)
+        dr.accept(data, T, i)
+        committed += int(dr.acc["n_committed"].sum().item())
+    nb = draft_bytes(cfg, head.inter, int(data.prefix_len.sum().item()))
+    out = {"workload": f"{cfg.name} shape, tree drafted depth by depth by a synthetic EAGLE draft head "
+                       f"(FC 2H->H, one decoder layer with MLP {head.inter}, shared LM head; random weights)",
+           "draft_ms_per_round": round(draft_ms, 4), "round_ms": round(round_ms, 4),
+           "trees_per_s": round(1000.0 / round_ms * cfg.B, 2),
+           "committed_tokens_per_s": round(committed / min(steps, 8) * 1000.0 / round_ms, 1),
+           "draft_bytes_per_round": nb,
+           "draft_hbm_frac": round(nb / (draft_ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+           "device_status": int(dr.status.item())}
+    del head
+    return out
+
+
 def cpu_baseline(cfg_name, T, inp, budget_s=25.0):
     """The oracle, untuned, on a bounded sample: whole rounds of set 0 (pre-pass excluded)."""
     from threadpoolctl import threadpool_info
@@ -225,6 +299,8 @@ def main():
     ap.add_argument("--sets", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the greedy and batch-64 extra lines")
+    ap.add_argument("--only-draft", action="store_true",
+                    help="only time the depth-by-depth drafting leg (8b shape) and print its JSON")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (a known-size reference for HBM "
                          "byte counters) and exit")
@@ -247,6 +323,15 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n * 4, "copies": 3}), flush=True)
+        return
+
+    if args.only_draft:
+        import synth
+        from eagle_draft_tree_expand_amd import round as dround
+        dcfg = synth.get_config(args.config)
+        dinp = synth.make_inputs(dcfg, 0)
+        print(json.dumps({"draft": time_drafting(dcfg, dround.DeviceWeights(dinp), dinp, args.temp, args.steps,
+                                                 args.warmup)}), flush=True)
         return
 
     cfg, inps, wts, sets = setup(args.config, args.temp, args.sets)
@@ -309,6 +394,9 @@ def main():
                         "committed_tokens_per_s": round(cr["committed"] / (cr["total_ms"] / 1000.0), 1),
                         "tau_synthetic": round(cr["committed"] / (csteps * ccfg.B), 4)}
         del csets, cwts
+    if not args.no_extra and args.config == "8b" and args.temp > 0:
+        out["draft"] = time_drafting(cfg, wts, inps[0], args.temp, max(10, args.steps // 10), 3)
+        torch.cuda.empty_cache()
     if not args.no_extra and args.config == "8b":
         gsteps = max(20, args.steps // 4)
         g = time_rounds(cfg, wts, sets, 0.0, gsteps, 5)

@@ -50,7 +50,7 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(512 / NTH))
     int n, int hq, int hkv, int Lmax, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const int32_t* __restrict__ plen, const uint16_t* __restrict__ kt,
     const uint16_t* __restrict__ vt, const uint64_t* __restrict__ mask, float scale, float* __restrict__ ws,
-    int rows, int rows_pad, int split_keys, int nsplit) {
+    int rows, int rows_pad, int split_keys, int nsplit, int nq, int qoff) {
   constexpr int KPAD = DH + 8;    // K row stride in LDS (bf16 elements)
   constexpr int VPAD = kKT + 8;   // V^T row stride in LDS
   constexpr float kLog2e = 1.44269504088896341f, kLn2 = 0.693147180559945309f;
@@ -120,14 +120,14 @@ __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(512 / NTH))
     const int r = row0 + t * 16 + col;
     const bool ok = r < rows;
     const int node = ok ? r / G : 0, h = g * G + (ok ? r % G : 0);
-    const uint16_t* qp = q + (((size_t)b * n + node) * hq + h) * DH;
+    const uint16_t* qp = q + (((size_t)b * nq + node) * hq + h) * DH;
 #pragma unroll
     for (int ds = 0; ds < DH / 32; ++ds) {
       B8 x;
       x.u = ok ? *reinterpret_cast<const uint4*>(qp + ds * 32 + grp * 8) : make_uint4(0, 0, 0, 0);
       qreg[t][ds] = x.v;
     }
-    mrow[t] = mask + ((size_t)b * n + node) * W;
+    mrow[t] = mask + ((size_t)b * n + qoff + node) * W;
   }
 
   floatx4 o[kQT][DH / 16];
@@ -282,7 +282,7 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(
     int n, int hq, int hkv, int Lmax, const float* __restrict__ q, const float* __restrict__ kp,
     const float* __restrict__ vp, const int32_t* __restrict__ plen, const float* __restrict__ kt,
     const float* __restrict__ vt, const uint64_t* __restrict__ mask, float scale, float* __restrict__ ws,
-    int rows, int rows_pad, int split_keys, int nsplit) {
+    int rows, int rows_pad, int split_keys, int nsplit, int nq, int qoff) {
   constexpr int TK = 32;
   __shared__ float Ks[TK * DH], Vs[TK * DH];
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -303,7 +303,7 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(
     const bool ok = r < rows;
     const int node = ok ? r / G : 0, h = g * G + (ok ? r % G : 0);
     float qv[DH], ov[DH];
-    const float* qp = q + (((size_t)b * n + node) * hq + h) * DH;
+    const float* qp = q + (((size_t)b * nq + node) * hq + h) * DH;
     for (int d = 0; d < DH; ++d) { qv[d] = ok ? qp[d] : 0.f; ov[d] = 0.f; }
     float m = kNegInf, l = 0.f;
     for (int t0 = k_begin; t0 < k_end; t0 += TK) {
@@ -319,7 +319,7 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(
       for (int kk = 0; kk < TK; ++kk) {
         const int key = t0 + kk;
         if (key >= k_end) break;
-        if (tree && !((mask[((size_t)b * n + node) * W + (key >> 6)] >> (key & 63)) & 1ull)) continue;
+        if (tree && !((mask[((size_t)b * n + qoff + node) * W + (key >> 6)] >> (key & 63)) & 1ull)) continue;
         float sc = 0.f;
         for (int d = 0; d < DH; ++d) sc = fmaf(qv[d], Ks[kk * DH + d], sc);
         sc *= scale;
@@ -345,7 +345,7 @@ __global__ __launch_bounds__(256) void attn_split_f32_kernel(
 // split); each output element then sums its splits with the resulting
 // weights, eight loads in flight at a time.
 template <bool BF16>
-__global__ __launch_bounds__(128) void attn_merge_kernel(int n, int hq, int hkv, int DH, const float* __restrict__ ws,
+__global__ __launch_bounds__(128) void attn_merge_kernel(int nq, int hq, int hkv, int DH, const float* __restrict__ ws,
                                                          int rows_pad, int nsplit, void* __restrict__ out) {
   extern __shared__ float wgt[];  // [nsplit + 1] weights exp(m_s - M)
   __shared__ float red[2][2];
@@ -388,7 +388,7 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int n, int hq, int hkv,
     }
     for (; s < nsp1; ++s) acc += p0[s * sstride + d] * wgt[s];
     const float v = L > 0.f ? acc / L : 0.f;
-    const size_t o = (((size_t)b * n + i) * hq + h) * DH + d;
+    const size_t o = (((size_t)b * nq + i) * hq + h) * DH + d;
     if (BF16) reinterpret_cast<uint16_t*>(out)[o] = f32_to_bf16(v);
     else reinterpret_cast<float*>(out)[o] = v;
   }
@@ -423,6 +423,14 @@ AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, 
 hipError_t launch_attention(int B, int n, int hq, int hkv, int DH, int Lmax, int dtype, const void* q, const void* kp,
                             const void* vp, const int32_t* plen, const void* kt, const void* vt, const uint64_t* mask,
                             float scale, void* out, float* ws, const AttnPlan& pl, int32_t* status, hipStream_t st) {
+  return launch_attention_window(B, n, n, 0, hq, hkv, DH, Lmax, dtype, q, kp, vp, plen, kt, vt, mask, scale, out, ws,
+                                 pl, status, st);
+}
+
+hipError_t launch_attention_window(int B, int n, int nq, int qoff, int hq, int hkv, int DH, int Lmax, int dtype,
+                                   const void* q, const void* kp, const void* vp, const int32_t* plen, const void* kt,
+                                   const void* vt, const uint64_t* mask, float scale, void* out, float* ws,
+                                   const AttnPlan& pl, int32_t* status, hipStream_t st) {
   (void)status;
   if (dtype == EAGLE_BF16) {
     const int threads = pl.rows <= 128 ? 256 : 512;
@@ -433,7 +441,7 @@ hipError_t launch_attention(int B, int n, int hq, int hkv, int DH, int Lmax, int
   attn_split_bf16_kernel<D, T><<<grid, T, 0, st>>>(n, hq, hkv, Lmax, (const uint16_t*)q, (const uint16_t*)kp,       \
                                                    (const uint16_t*)vp, plen, (const uint16_t*)kt,                  \
                                                    (const uint16_t*)vt, mask, scale, ws, pl.rows, pl.rows_pad,      \
-                                                   pl.split_keys, pl.nsplit)
+                                                   pl.split_keys, pl.nsplit, nq, qoff)
     if (DH == 64) {
       if (threads == 256) EAGLE_ATTN_BF16(64, 256);
       else EAGLE_ATTN_BF16(64, 512);
@@ -447,7 +455,8 @@ hipError_t launch_attention(int B, int n, int hq, int hkv, int DH, int Lmax, int
 #define EAGLE_ATTN_F32(D)                                                                                          \
   attn_split_f32_kernel<D><<<grid, 256, 0, st>>>(n, hq, hkv, Lmax, (const float*)q, (const float*)kp,             \
                                                  (const float*)vp, plen, (const float*)kt, (const float*)vt, mask, \
-                                                 scale, ws, pl.rows, pl.rows_pad, pl.split_keys, pl.nsplit)
+                                                 scale, ws, pl.rows, pl.rows_pad, pl.split_keys, pl.nsplit, nq, \
+                                                 qoff)
     if (DH <= 16) EAGLE_ATTN_F32(16);
     else if (DH <= 32) EAGLE_ATTN_F32(32);
     else if (DH <= 64) EAGLE_ATTN_F32(64);
@@ -456,11 +465,11 @@ hipError_t launch_attention(int B, int n, int hq, int hkv, int DH, int Lmax, int
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  dim3 mg(n, hq, B);
+  dim3 mg(nq, hq, B);
   const int mt = DH <= 64 ? 64 : 128;  // whole waves (the merge reduces across lanes)
   const size_t lds = (size_t)(pl.nsplit + 1) * sizeof(float);
-  if (dtype == EAGLE_BF16) attn_merge_kernel<true><<<mg, mt, lds, st>>>(n, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
-  else attn_merge_kernel<false><<<mg, mt, lds, st>>>(n, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
+  if (dtype == EAGLE_BF16) attn_merge_kernel<true><<<mg, mt, lds, st>>>(nq, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
+  else attn_merge_kernel<false><<<mg, mt, lds, st>>>(nq, hq, hkv, DH, ws, pl.rows_pad, pl.nsplit, out);
   return hipGetLastError();
 }
 

@@ -14,15 +14,15 @@
 // step on the caller's stream:
 //   draft_in      x0 = [f ; E[x]] (bf16) of each frontier node, its slot's
 //                 ancestor mask row (the parent's row plus itself); at d = 0
-//                 also the per-round slot state (zero q/k/v rows, root-only
+//                 also the per-round slot state (zero k/v rows, root-only
 //                 masks) so that not-yet-drafted slots stay finite
 //   GEMM fc       u = x0 Wfc^T                    (bf16 MFMA, fp32 out)
 //   norm          n1 = bf16(rms(u))
 //   GEMM qkv      [q k v] = n1 Wqkv^T
-//   draft_qkv     bf16 q/k/v rows into the slot-indexed tree buffers
-//   attention     tree attention over the draft prefix and the slot keys
-//                 (mask: root path only), all S slots as queries
-//   gather        the frontier rows of the attention output
+//   draft_qkv     bf16 q rows of the frontier; k/v rows into the
+//                 slot-indexed tree buffers
+//   attention     the frontier's queries over the draft prefix and the slot
+//                 keys, each under its slot's mask (its root path)
 //   GEMM o        y = o Wo^T;  norm: h = u + y, n2 = bf16(rms(h))
 //   GEMM gate_up  [g u] = n2 Wgu^T;  draft_silu: bf16(silu(g) * u)
 //   GEMM down     y = m Wd^T;  norm: a = h + y -> bf16 feature of the slot
@@ -47,8 +47,8 @@ __global__ __launch_bounds__(kDT) void draft_in_kernel(
     int depth, int kd, int s0, int S, int k, int P, int H, int V, int Q, int KV, int W,
     const int32_t* __restrict__ root, const uint16_t* __restrict__ root_feat, const int32_t* __restrict__ pool_tok,
     const int32_t* __restrict__ slot_src, const uint16_t* __restrict__ embed, uint16_t* __restrict__ slot_feat,
-    uint64_t* __restrict__ slot_mask, uint16_t* __restrict__ slot_q, uint16_t* __restrict__ slot_k,
-    uint16_t* __restrict__ slot_v, int32_t* __restrict__ idx, uint16_t* __restrict__ x0, int32_t* status) {
+    uint64_t* __restrict__ slot_mask, uint16_t* __restrict__ slot_k, uint16_t* __restrict__ slot_v,
+    int32_t* __restrict__ idx, uint16_t* __restrict__ x0, int32_t* status) {
   const int r = blockIdx.x, tid = threadIdx.x;
   const int b = r / kd, s = s0 + (r - b * kd);
   const size_t srow = (size_t)b * S + s;
@@ -84,18 +84,17 @@ __global__ __launch_bounds__(kDT) void draft_in_kernel(
   }
   if (depth != 0) return;
   // Round start: slots 1..S-1 of this request are not drafted yet.  Their
-  // mask rows see the root only and their q/k/v rows are zero, so that the
-  // attention over all S slots reads finite values everywhere.
+  // mask rows see the root only and their k/v rows are zero, so that the
+  // attention reads finite values in every slot (masked keys still pass
+  // through the MFMAs with weight 0).
   for (int x = tid; x < (S - 1) * W; x += kDT) {
     const int s1 = 1 + x / W, w = x - (s1 - 1) * W;
     slot_mask[((size_t)b * S + s1) * W + w] = w == 0 ? 1ull : 0ull;
   }
   const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-  const size_t qn = (size_t)(S - 1) * Q / 8, kn = (size_t)(S - 1) * KV / 8;
-  uint16_t* q1 = slot_q + ((size_t)b * S + 1) * Q;
+  const size_t kn = (size_t)(S - 1) * KV / 8;
   uint16_t* k1 = slot_k + ((size_t)b * S + 1) * KV;
   uint16_t* v1 = slot_v + ((size_t)b * S + 1) * KV;
-  for (size_t u = tid; u < qn; u += kDT) st16(q1 + u * 8, z);
   for (size_t u = tid; u < kn; u += kDT) {
     st16(k1 + u * 8, z);
     st16(v1 + u * 8, z);
@@ -145,7 +144,8 @@ __global__ __launch_bounds__(kDT) void draft_norm_kernel(int H, const float* __r
   }
 }
 
-// One workgroup per row: the fp32 [q | k | v] row to bf16 q/k/v rows of slot idx[r].
+// One workgroup per row: the fp32 [q | k | v] row to bf16: q to row r of the
+// frontier's queries, k and v to the rows of slot idx[r].
 __global__ __launch_bounds__(kDT) void draft_qkv_kernel(int Q, int KV, const float* __restrict__ qkv,
                                                         const int32_t* __restrict__ idx, uint16_t* __restrict__ sq,
                                                         uint16_t* __restrict__ sk, uint16_t* __restrict__ sv) {
@@ -156,19 +156,21 @@ __global__ __launch_bounds__(kDT) void draft_qkv_kernel(int Q, int KV, const flo
   for (int i = tid * 2; i < n; i += kDT * 2) {
     const float2 v = *reinterpret_cast<const float2*>(src + i);
     const uint32_t p = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
-    uint16_t* dst = i < Q ? sq + o * Q + i : i < Q + KV ? sk + o * KV + (i - Q) : sv + o * KV + (i - Q - KV);
+    uint16_t* dst = i < Q ? sq + (size_t)r * Q + i : i < Q + KV ? sk + o * KV + (i - Q) : sv + o * KV + (i - Q - KV);
     *reinterpret_cast<uint32_t*>(dst) = p;
   }
 }
 
-// One workgroup per row: bf16(silu(g) * u) from the fp32 [g | u] row (I each).
-__global__ __launch_bounds__(kDT) void draft_silu_kernel(int I, const float* __restrict__ gu,
+// bf16(silu(g) * u) from fp32 [g | u] rows (I each); one thread per pair of
+// columns over all rows.
+__global__ __launch_bounds__(kDT) void draft_silu_kernel(int R, int I, const float* __restrict__ gu,
                                                          uint16_t* __restrict__ out) {
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const float* g = gu + (size_t)r * 2 * I;
-  const float* u = g + I;
-  for (int i = tid * 2; i < I; i += kDT * 2) {
-    const float2 gv = *reinterpret_cast<const float2*>(g + i), uv = *reinterpret_cast<const float2*>(u + i);
+  const int hp = I / 2;
+  const size_t total = (size_t)R * hp;
+  for (size_t x = (size_t)blockIdx.x * kDT + threadIdx.x; x < total; x += (size_t)gridDim.x * kDT) {
+    const int r = (int)(x / hp), i = (int)(x - (size_t)r * hp) * 2;
+    const float* g = gu + (size_t)r * 2 * I + i;
+    const float2 gv = *reinterpret_cast<const float2*>(g), uv = *reinterpret_cast<const float2*>(g + I);
     const float a = gv.x / (1.0f + expf(-gv.x)) * uv.x, c = gv.y / (1.0f + expf(-gv.y)) * uv.y;
     *reinterpret_cast<uint32_t*>(out + (size_t)r * I + i) =
         (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(c) << 16);
@@ -185,17 +187,16 @@ DraftLayout draft_layout(int B, int S, int k, int V, int H, int hq, int hkv, int
   const size_t BS = (size_t)B * S, R = (size_t)B * (k > 1 ? k : 1);
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o += up256(bytes); return at; };
-  L.slot_q = take(BS * Q * 2);
   L.slot_k = take(BS * KV * 2);
   L.slot_v = take(BS * KV * 2);
   L.slot_feat = take(BS * H * 2);
   L.slot_mask = take(BS * W * 8);
-  L.attn_out = take(BS * Q * 2);
   L.idx = take(R * 4);
   L.x0 = take(R * 2 * H * 2);
   L.u = take(R * H * 4);
   L.n1 = take(R * H * 2);
   L.qkv = take(R * (Q + 2 * KV) * 4);
+  L.qc = take(R * Q * 2);
   L.og = take(R * Q * 2);
   L.h = take(R * H * 4);
   L.n2 = take(R * H * 2);
@@ -212,8 +213,8 @@ DraftLayout draft_layout(int B, int S, int k, int V, int H, int hq, int hkv, int
     for (size_t x : c) g = x > g ? x : g;
   }
   L.gemm = take(g);
-  L.plan = attn_plan(B, S, hq, hkv, dh, max_prefix, EAGLE_BF16);
-  L.attn = take(attn_ws_bytes(B, hkv, dh, L.plan));
+  // the largest query window (k frontier nodes); depth 0 plans for one
+  L.attn = take(attn_ws_bytes(B, hkv, dh, attn_plan(B, k, hq, hkv, dh, max_prefix, EAGLE_BF16)));
   L.total = o;
   return L;
 }
@@ -239,8 +240,8 @@ hipError_t launch_draft_forward(const DraftArgs& a, hipStream_t st) {
 
   draft_in_kernel<<<R, kDT, 0, st>>>(a.depth, kd, s0, S, k, P, H, a.V, Q, KV, W, a.root, (const uint16_t*)a.root_feat,
                                      a.pool_tok, a.slot_src, (const uint16_t*)a.w.embed, P16(L.slot_feat),
-                                     reinterpret_cast<uint64_t*>(base + L.slot_mask), P16(L.slot_q), P16(L.slot_k),
-                                     P16(L.slot_v), idx, P16(L.x0), a.status);
+                                     reinterpret_cast<uint64_t*>(base + L.slot_mask), P16(L.slot_k), P16(L.slot_v),
+                                     idx, P16(L.x0), a.status);
   EAGLE_CK(hipGetLastError());
   EAGLE_CK(launch_lmhead_map(R, 2 * H, H, EAGLE_BF16, EAGLE_W_PACKED, P16(L.x0), a.w.fc, 1.f, PF(L.u), nullptr,
                              nullptr, nullptr, gws, a.status, id, st));
@@ -248,25 +249,26 @@ hipError_t launch_draft_forward(const DraftArgs& a, hipStream_t st) {
   EAGLE_CK(hipGetLastError());
   EAGLE_CK(launch_lmhead_map(R, H, Q + 2 * KV, EAGLE_BF16, EAGLE_W_PACKED, P16(L.n1), a.w.qkv, 1.f, PF(L.qkv),
                              nullptr, nullptr, nullptr, gws, a.status, id, st));
-  draft_qkv_kernel<<<R, kDT, 0, st>>>(Q, KV, PF(L.qkv), idx, P16(L.slot_q), P16(L.slot_k), P16(L.slot_v));
+  draft_qkv_kernel<<<R, kDT, 0, st>>>(Q, KV, PF(L.qkv), idx, P16(L.qc), P16(L.slot_k), P16(L.slot_v));
   EAGLE_CK(hipGetLastError());
-  EAGLE_CK(launch_attention(B, S, a.hq, a.hkv, a.dh, a.max_prefix, EAGLE_BF16, P16(L.slot_q), a.k_prefix,
-                            a.v_prefix, a.prefix_len, P16(L.slot_k), P16(L.slot_v),
-                            reinterpret_cast<const uint64_t*>(base + L.slot_mask), a.scale, P16(L.attn_out),
-                            PF(L.attn), L.plan, a.status, st));
-  GatherSet gs{};
-  gs.table[0] = P16(L.attn_out);
-  gs.out[0] = P16(L.og);
-  gs.row_units[0] = Q * 2;
-  gs.n = 1;
-  EAGLE_CK(launch_gather(R, gs, B * S, idx, a.status, st));
+  // the frontier's kd queries are tree nodes s0 .. s0+kd-1 of the S slots;
+  // the output rows come out in frontier order, ready for the o product
+  EAGLE_CK(launch_attention_window(B, S, kd, s0, a.hq, a.hkv, a.dh, a.max_prefix, EAGLE_BF16, P16(L.qc), a.k_prefix,
+                                   a.v_prefix, a.prefix_len, P16(L.slot_k), P16(L.slot_v),
+                                   reinterpret_cast<const uint64_t*>(base + L.slot_mask), a.scale, P16(L.og),
+                                   PF(L.attn), attn_plan(B, kd, a.hq, a.hkv, a.dh, a.max_prefix, EAGLE_BF16),
+                                   a.status, st));
   EAGLE_CK(launch_lmhead_map(R, Q, H, EAGLE_BF16, EAGLE_W_PACKED, P16(L.og), a.w.o, 1.f, PF(L.y), nullptr, nullptr,
                              nullptr, gws, a.status, id, st));
   draft_norm_kernel<<<R, kDT, 0, st>>>(H, PF(L.u), PF(L.y), PF(L.h), P16(L.n2), nullptr, nullptr, idx);
   EAGLE_CK(hipGetLastError());
   EAGLE_CK(launch_lmhead_map(R, H, 2 * I, EAGLE_BF16, EAGLE_W_PACKED, P16(L.n2), a.w.gate_up, 1.f, PF(L.gu), nullptr,
                              nullptr, nullptr, gws, a.status, id, st));
-  draft_silu_kernel<<<R, kDT, 0, st>>>(I, PF(L.gu), P16(L.mm));
+  {
+    const size_t pairs = (size_t)R * (I / 2);
+    const int grid = (int)((pairs + kDT - 1) / kDT < 2048 ? (pairs + kDT - 1) / kDT : 2048);
+    draft_silu_kernel<<<grid, kDT, 0, st>>>(R, I, PF(L.gu), P16(L.mm));
+  }
   EAGLE_CK(hipGetLastError());
   EAGLE_CK(launch_lmhead_map(R, I, H, EAGLE_BF16, EAGLE_W_PACKED, P16(L.mm), a.w.down, 1.f, PF(L.y), nullptr, nullptr,
                              nullptr, gws, a.status, id, st));

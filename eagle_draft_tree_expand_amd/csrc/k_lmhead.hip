@@ -593,8 +593,18 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(int rows, int V, int KS
     const int n = n0 + h * 256 + tid;
     float v = kNegInf;
     if (n < V) {
+      // eight slices' loads in flight at a time; the sum keeps slice order
       float acc = 0.f;
-      for (int kz = 0; kz < KS; ++kz) acc += partial[((size_t)kz * rows + m) * V + n];
+      const float* pp = partial + (size_t)m * V + n;
+      const size_t sl = (size_t)rows * V;
+      for (int kz0 = 0; kz0 < KS; kz0 += 8) {
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) v[j] = kz0 + j < KS ? pp[(size_t)(kz0 + j) * sl] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (kz0 + j < KS) acc += v[j];
+      }
       logits[(size_t)map_row(m, rm) * V + n] = acc;
       v = acc;
       if (!isfinite(v)) { bad = true; v = kNegInf; }

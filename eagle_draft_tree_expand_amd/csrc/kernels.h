@@ -83,6 +83,14 @@ hipError_t launch_attention(int B, int n, int hq, int hkv, int head_dim, int max
                             const void* kt, const void* vt, const uint64_t* mask, float scale,
                             void* out, float* ws, const AttnPlan& pl, int32_t* status,
                             hipStream_t st);
+// Queries for a window of nq consecutive tree nodes qoff .. qoff+nq-1 only:
+// q [B, nq, hq, dh] and out [B, nq, hq, dh] hold those nodes' rows, the mask
+// rows are theirs in the [B, n, W] mask, all n tree keys stay; the plan is
+// attn_plan(B, nq, ...).
+hipError_t launch_attention_window(int B, int n, int nq, int qoff, int hq, int hkv, int head_dim, int max_prefix,
+                                   int dtype, const void* q, const void* kp, const void* vp, const int32_t* plen,
+                                   const void* kt, const void* vt, const uint64_t* mask, float scale, void* out,
+                                   float* ws, const AttnPlan& pl, int32_t* status, hipStream_t st);
 
 // ---- LM head (k_lmhead.hip) ----
 constexpr int kLmTileN = 512;            // vocab columns per workgroup (one stats record per row)
@@ -135,9 +143,8 @@ hipError_t launch_pack_lmhead(int V, int hidden, const void* w, void* wp, hipStr
 // Byte offsets in the draft workspace: per-round slot state (kept across the
 // depths of a round) and per-depth scratch sized for B * k frontier rows.
 struct DraftLayout {
-  size_t slot_q, slot_k, slot_v, slot_feat, slot_mask, attn_out;
-  size_t idx, x0, u, n1, qkv, og, h, n2, gu, mm, y, xa, gemm, attn, total;
-  AttnPlan plan;
+  size_t slot_k, slot_v, slot_feat, slot_mask;
+  size_t idx, x0, u, n1, qkv, qc, og, h, n2, gu, mm, y, xa, gemm, attn, total;
 };
 DraftLayout draft_layout(int B, int S, int k, int V, int H, int hq, int hkv, int dh, int I, int max_prefix);
 struct DraftArgs {
