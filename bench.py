@@ -411,6 +411,7 @@ def main():
             ms64 = b["total_ms"] / 10
             flops = 2.0 * cfg64.B * cfg64.N * cfg64.H * cfg64.V
             out["b64"] = {"trees_per_s": round(1000.0 / ms64 * cfg64.B, 1), "ms_per_round": round(ms64, 3),
+                          "draft": time_drafting(cfg64, wts64, inps64[0], 1.0, 3, 1),
                           "committed_tokens_per_s": round(b["committed"] / (b["total_ms"] / 1000.0), 1),
                           "lmhead_ms": round(b["lm_ms"], 4),
                           "lmhead_mfma_frac": round(flops / (b["lm_ms"] / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4),

@@ -424,7 +424,7 @@ template <bool PACKED>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_gemm_kernel(
     int rows, int H, int V, float Tp, int nm, int nn, int bm, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ w, float* __restrict__ logits, float* __restrict__ part, int32_t* status,
-    RowMap rm) {
+    RowMap rm, int gps, int hk, float* __restrict__ partial) {
   // the ring: one array per stage
   __shared__ __attribute__((aligned(1024))) uint16_t ring0[32 * kGBlock];  // A 16 blocks | B 16 blocks
   __shared__ __attribute__((aligned(1024))) uint16_t ring1[32 * kGBlock];
@@ -436,7 +436,10 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   // consecutive j (about what its 32 CUs hold at once) form a block of bm row
   // tiles x 32/bm vocab tiles, so every X and W slab read into the XCD's L2
   // serves several workgroups; vocab tiles of XCD x are those = x mod 8.
-  const int bid = blockIdx.x, xcd = bid & 7, j = bid >> 3;
+  // hidden split: workgroups kz*gps .. kz*gps + gps-1 cover hidden slice kz
+  // (hk values) of every tile and write fp32 partials (partial != null)
+  const int kz = (int)blockIdx.x / gps;
+  const int bid = (int)blockIdx.x - kz * gps, xcd = bid & 7, j = bid >> 3;
   const int bnb = 32 / bm, jb = j & 31, blk = j >> 5, nmb = (nm + bm - 1) / bm;
   const int mt_idx = (blk % nmb) * bm + jb / bnb;
   const int nt_idx = ((blk / nmb) * bnb + jb % bnb) * 8 + xcd;
@@ -447,7 +450,8 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   const int wm = wave >> 1, wn = wave & 1;  // rows 64 wm.., columns 128 wn..
   const int col = lane & 15, grp = lane >> 4;
   const int nch = H / 64;
-  const int nsteps = H / kGK;
+  const int nsteps = hk / kGK;  // a multiple of 4: hk is a multiple of 128
+  const int sb = kz * nsteps;   // first step of this slice
   const int ngroups = (V + 63) / 64;
 
   // Sources of this wave's 4 blocks per step: A blocks mt = 2 wave + q and
@@ -455,16 +459,16 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   uint32_t xoff[2];  // element offset of this lane's X row (clamped) + its 8-wide hidden offset
 #pragma unroll
   for (int q = 0; q < 2; ++q)
-    xoff[q] = (uint32_t)min(m0 + (2 * wave + q) * 16 + col, rows - 1) * (uint32_t)H + grp * 8;
+    xoff[q] = (uint32_t)min(m0 + (2 * wave + q) * 16 + col, rows - 1) * (uint32_t)H + grp * 8 + sb * kGK;
   const uint16_t* wsrc[2];
 #pragma unroll
   for (int q = 0; q < 2; ++q) {
     const int nt = 2 * wave + q;
     if (PACKED) {  // group nt / 4, load (nt % 4) of a 32-wide half chunk
       const int g = min(n0 / 64 + nt / 4, ngroups - 1);
-      wsrc[q] = w + ((size_t)g * nch * 8 + (nt & 3)) * 512 + (size_t)lane * 8;
+      wsrc[q] = w + ((size_t)g * nch * 8 + (nt & 3) + (size_t)(sb >> 1) * 8) * 512 + (size_t)lane * 8;
     } else {
-      wsrc[q] = w + (size_t)min(n0 + nt * 16 + col, V - 1) * H + grp * 8;
+      wsrc[q] = w + (size_t)min(n0 + nt * 16 + col, V - 1) * H + grp * 8 + sb * kGK;
     }
   }
 #define G_ISSUE_Q(st, dst, q)                                                                               \
@@ -527,11 +531,27 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 #undef G_ISSUE
 #undef G_ISSUE_Q
 
+  const int nbase = n0 + wn * 128;
+  if (partial != nullptr) {  // a hidden slice: fp32 partials, summed by lm_combine
+    float* pz = partial + (size_t)kz * rows * V;
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + wm * 64 + mt * 16 + grp * 4 + i;
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const int n = nbase + nt * 16 + col;
+          if (m < rows && n < V) pz[(size_t)m * V + n] = acc[mt][nt][i];
+        }
+      }
+    return;
+  }
+
   // Epilogue: logits and the stats of each row over this wave's 128 columns,
   // then the two column halves of the tile merged through LDS.  One row at a
   // time: its 8 values per lane are copied out of the accumulators.
   bool bad = false;
-  const int nbase = n0 + wn * 128;
 #pragma unroll
   for (int mt = 0; mt < 4; ++mt) {
 #pragma unroll
@@ -754,14 +774,25 @@ hipError_t launch_lmhead_map(int rows, int H, int V, int dtype, int w_layout, co
     ntiles = nn;
     // blocks of bm row tiles x 32/bm vocab tiles per XCD (16 x 2 measured best at 16 row tiles)
     const int bm = nm >= 16 ? 16 : nm >= 8 ? 8 : 4, bn = 32 / bm;
-    const int grid = ((nm + bm - 1) / bm * bm) * ((nn + 8 * bn - 1) / (8 * bn) * (8 * bn));
+    const int gps = ((nm + bm - 1) / bm * bm) * ((nn + 8 * bn - 1) / (8 * bn) * (8 * bn));
+    // plain products with few tiles split the hidden dimension (no statistics then)
+    const int ks = row_stats == nullptr ? lm_gemm_ksplit(rows, V, H) : 1;
+    float* partial = ks > 1 ? ws_part + lm_rec_floats(rows, V) : nullptr;
     const size_t lds = 0;
     if (w_layout == EAGLE_W_PACKED)
-      lmhead_gemm_kernel<true><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
-                                                       (const uint16_t*)w, logits, ws_part, status, rm);
+      lmhead_gemm_kernel<true><<<gps * ks, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
+                                                           (const uint16_t*)w, logits, ws_part, status, rm, gps,
+                                                           H / ks, partial);
     else
-      lmhead_gemm_kernel<false><<<grid, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
-                                                        (const uint16_t*)w, logits, ws_part, status, rm);
+      lmhead_gemm_kernel<false><<<gps * ks, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
+                                                            (const uint16_t*)w, logits, ws_part, status, rm, gps,
+                                                            H / ks, partial);
+    if (ks > 1) {
+      hipError_t e0 = hipGetLastError();
+      if (e0 != hipSuccess) return e0;
+      lm_combine_kernel<<<dim3(lm_ntiles(V), rows), 256, 0, st>>>(rows, V, ks, Tp, partial, logits, ws_part, status,
+                                                                  rm);
+    }
   } else if (dtype == EAGLE_BF16) {
     const int ks = lm_ksplit(rows, V, H);
     float* partial = ks > 1 ? ws_part + lm_rec_floats(rows, V) : nullptr;

@@ -117,9 +117,21 @@ inline int lm_ksplit(int rows, int V, int H) {
   while (ks > 1 && H % (ks * 128) != 0) --ks;
   return ks < 1 ? 1 : ks;
 }
+// The tiled GEMM with fewer 256 x 256 tiles than CUs splits the hidden
+// dimension too (plain products only: no row statistics), up to one
+// workgroup per CU, slices of a multiple of 128.
+inline int lm_gemm_ksplit(int rows, int V, int H) {
+  if (rows < kGemmMinRows) return 1;
+  const int tiles = ((rows + kGemmTile - 1) / kGemmTile) * lm_gemm_ntiles(V);
+  int ks = 256 / tiles;
+  if (ks > 8) ks = 8;
+  while (ks > 1 && H % (ks * 128) != 0) --ks;
+  return ks < 1 ? 1 : ks;
+}
 inline size_t lm_rec_floats(int rows, int V) { return (size_t)rows * lm_gemm_ntiles(V) * 4; }
 inline size_t lm_ws_bytes(int rows, int V, int H) {
-  const int ks = lm_ksplit(rows, V, H);
+  const int k1 = lm_ksplit(rows, V, H), k2 = lm_gemm_ksplit(rows, V, H);
+  const int ks = k1 > k2 ? k1 : k2;
   return (lm_rec_floats(rows, V) + (ks > 1 ? (size_t)ks * rows * V : 0)) * sizeof(float);
 }
 hipError_t launch_lmhead(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,

@@ -251,3 +251,25 @@ def test_drafting_8b_shape_sampled():
         err = float(np.max(np.abs(zd - zo)) / np.max(np.abs(zo)))
         print(f"8b slot {s} path {path}: row error {err:.2e}")
         assert err <= 2e-2
+
+
+def test_drafting_tiled_gemm_path():
+    """Enough requests that every product of the head (B * k >= 193 rows) takes the
+    tiled GEMM kernel with its output row map; a sample of requests is validated."""
+    from eagle_draft_tree_expand_amd import draft_head
+    cfg = synth.get_config("mid_bf16").with_(B=66, L=(40, 200))
+    T = 1.0
+    inp, dinp, rnd, data, head = _setup(cfg)
+    rnd.status.zero_()
+    draft_head.draft_tree(head, rnd, data, T)
+    dev = _host(rnd)
+    rows = data.rows.cpu().numpy()
+    assert dev["status"] & ~0x8 == 0, hex(dev["status"])
+    heads = _oracle_heads(cfg, inp, dinp)
+    worst = 0.0
+    for b in (0, 1, 31, 64, 65):
+        db = {key: dev[key][b] for key in dev if key != "status"}
+        r, _ = _validate(db, rows[b], heads[b], dinp.root_feat[b], int(inp.roots[b]), T, cfg.k, cfg.D, cfg.m,
+                         inp.gumbel_seed, b)
+        worst = max(worst, r)
+    print(f"B=66: worst row error {worst:.2e}")
