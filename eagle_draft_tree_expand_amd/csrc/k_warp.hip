@@ -42,7 +42,24 @@ EDEV bool before_eq(uint32_t key, int v, const Cut& c) { return key < c.key || (
 constexpr int kWBuckets = 2048;
 constexpr int kWList = 64;  // tokens tied at a cut key handled in wave 0
 
+// A top-k cut of at most this many tokens finishes in LDS: the kept tokens
+// are listed once, sorted, and the nucleus, min_keep cut, M and S are taken
+// from the list instead of further passes over the row.
+constexpr int kWFast = 1024;
+
+struct FastList {
+  uint32_t key[kWFast];  // gathered, unordered
+  int id[kWFast];
+  float t[kWFast];
+  uint32_t skey[kWFast];  // sorted by (key asc, id asc) = the order
+  int sid[kWFast];
+  float st[kWFast];
+  int n;
+  int ci;
+};
+
 struct WarpSmem {
+  FastList fl;
   unsigned long long hist[kWBuckets];
   unsigned long long part[kWThreads / 64];
   double dred[kWWaves];
@@ -342,6 +359,89 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
   r.mscale = ldexp(1.0, mshift);
   if (tid == 0) sm.bad = 0;
   int bad = 0;
+  const Cut all{0xffffffffu, 0x7fffffff};
+  Cut cut = all;
+  int nA = V;
+  if (top_k > 0 && top_k < V && top_k <= kWFast) {
+    // The top-k cut needs no M (counts only).  Then its tokens go to LDS.
+    cut = select_cut(r, all, false, (double)top_k, sm);
+    nA = top_k;
+    FastList& fl = sm.fl;
+    if (tid == 0) { fl.n = 0; fl.ci = 0x7fffffff; }
+    __syncthreads();
+    for (int v0 = 0; v0 < V; v0 += kWBatch) {
+      float zz[kWE];
+      load_batch(r, v0, zz);
+#pragma unroll
+      for (int j = 0; j < kWE; ++j) {
+        const int v = tok_of(r, v0, j);
+        if (v >= V) continue;
+        const float t = t_from(r, zz[j], &bad);
+        const uint32_t key = ~tcode(t);
+        if (!before_eq(key, v, cut)) continue;
+        const int i = atomicAdd(&fl.n, 1);
+        if (i < kWFast) { fl.key[i] = key; fl.id[i] = v; fl.t[i] = t; }
+      }
+    }
+    __syncthreads();
+    const int n = min(fl.n, kWFast);  // the cut keeps exactly top_k tokens
+    if (tid < n) {  // rank by (key asc, id asc); keys and ids are read from LDS
+      const uint32_t mk = fl.key[tid];
+      const int mi = fl.id[tid];
+      int rank = 0;
+      for (int q = 0; q < n; ++q) {
+        const uint32_t kq = fl.key[q];
+        rank += (kq < mk || (kq == mk && fl.id[q] < mi)) ? 1 : 0;
+      }
+      fl.skey[rank] = mk;
+      fl.sid[rank] = mi;
+      fl.st[rank] = fl.t[tid];
+    }
+    __syncthreads();
+    r.M = n > 0 ? fl.st[0] : kNegInf;  // the first of the order holds max t
+    if (r.M != kNegInf) {
+      int last = n - 1;  // index of the last kept token in the order
+      if (top_p < 1.0f) {
+        // fixed-point masses (as the row passes weigh them), inclusive prefix in order
+        const unsigned long long w = tid < n ? weight(r, fl.st[tid], true) : 0ull;
+        unsigned long long inc = w;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const unsigned long long y = __shfl_up(inc, o);
+          if ((tid & 63) >= o) inc += y;
+        }
+        if ((tid & 63) == 63) sm.part[tid >> 6] = inc;
+        __syncthreads();
+        unsigned long long wpre = 0, sa = 0;
+        for (int q = 0; q < kWWaves; ++q) {
+          if (q < (tid >> 6)) wpre += sm.part[q];
+          sa += sm.part[q];
+        }
+        inc += wpre;
+        // the first token at which the running mass reaches top_p of the top-k mass
+        const double target = (double)top_p * (double)sa;
+        if (tid < n && (double)inc >= target && (double)(inc - w) < target) atomicMin(&fl.ci, tid);
+        __syncthreads();
+        int ci = fl.ci == 0x7fffffff ? n - 1 : fl.ci;
+        if (min_keep > 1) ci = max(ci, min(min_keep, nA) - 1);
+        last = ci;
+        cut = Cut{fl.skey[ci], fl.sid[ci]};
+      }
+      double sp = (tid <= last && fl.st[tid] != kNegInf) ? exp((double)fl.st[tid] - (double)r.M) : 0.0;
+      const double sfin = block_sum_d(sp, sm);
+      if (bad) sm.bad = 1;
+      __syncthreads();
+      if (tid == 0) {
+        stats[(size_t)row * 2] = r.M;
+        stats[(size_t)row * 2 + 1] = (float)sfin;
+        bound[(size_t)row * 2] = ~cut.key;
+        bound[(size_t)row * 2 + 1] = (uint32_t)cut.id;
+        if (sm.bad) set_status(status, EAGLE_STATUS_NONFINITE);
+      }
+      return;
+    }
+    // an all -inf row: the passes below handle it as before
+  }
   float lm = kNegInf;
   for (int v0 = 0; v0 < V; v0 += kWBatch) {
     float zz[kWE];
@@ -352,10 +452,7 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
   }
   if (bad) sm.bad = 1;
   r.M = block_max(lm, sm);
-  const Cut all{0xffffffffu, 0x7fffffff};
-  Cut cut = all;
-  int nA = V;
-  if (top_k > 0 && top_k < V) {
+  if (top_k > 0 && top_k < V && nA == V) {
     cut = select_cut(r, all, false, (double)top_k, sm);
     nA = top_k;
   }
