@@ -142,7 +142,9 @@ hipError_t launch_lmhead(int rows, int hidden, int V, int dtype, int w_layout, c
 struct RowMap {
   int grp, gstride, off;
 };
-__host__ __device__ inline int map_row(int m, RowMap rm) { return (m / rm.grp) * rm.gstride + rm.off + m % rm.grp; }
+__host__ __device__ inline int map_row(int m, RowMap rm) {
+  return m < rm.grp ? rm.off + m : (m / rm.grp) * rm.gstride + rm.off + m % rm.grp;  // no division in one group
+}
 // The same with an output row map; row_stats == nullptr skips the statistics
 // (a plain product X W^T), and probs must then be null as well.
 hipError_t launch_lmhead_map(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,
