@@ -273,3 +273,34 @@ def test_drafting_tiled_gemm_path():
                          inp.gumbel_seed, b)
         worst = max(worst, r)
     print(f"B=66: worst row error {worst:.2e}")
+
+
+@pytest.mark.parametrize("kw,T,zero_prefix", [
+    (dict(D=1, k=3, m=3), 1.0, False),           # the root's children only
+    (dict(D=5, k=1, m=5), 0.0, False),           # a chain, greedy
+    (dict(D=6, k=16, m=100), 1.0, False),        # S = 81 slots: two mask words per slot
+    (dict(D=3, k=2, m=5), 0.7, True),            # one request with an empty draft prefix
+])
+def test_drafting_edge_shapes(kw, T, zero_prefix):
+    from eagle_draft_tree_expand_amd import draft_head
+    from eagle_draft_tree_expand_amd import round as rt
+    cfg = synth.get_config("mid_bf16").with_(**kw)
+    inp = synth.make_inputs(cfg, 2)
+    if zero_prefix:
+        pl = np.array(inp.prefix_len, copy=True)
+        pl[1] = 0
+        inp.prefix_len = pl
+    dinp = make_draft_inputs(cfg, 2)
+    rnd = rt.DeviceRound(cfg)
+    data = rt.DeviceInputs(inp)
+    head = draft_head.DeviceDraftHead(cfg, dinp, _Wts(inp))
+    rnd.status.zero_()
+    draft_head.draft_tree(head, rnd, data, T)
+    dev = _host(rnd)
+    rows = data.rows.cpu().numpy()
+    assert dev["status"] & ~0x8 == 0, hex(dev["status"])
+    heads = _oracle_heads(cfg, inp, dinp)
+    for b in range(cfg.B):
+        db = {key: dev[key][b] for key in dev if key != "status"}
+        _validate(db, rows[b], heads[b], dinp.root_feat[b], int(inp.roots[b]), T, cfg.k, cfg.D, cfg.m,
+                  inp.gumbel_seed, b)
