@@ -69,7 +69,7 @@ int check_draft(const eagle_tree_params* p, const eagle_draft_dims* d, DraftLayo
   const int B = p->batch, k = p->topk, D = p->depth, V = p->vocab;
   const int S = 1 + (D - 1) * k;
   const int64_t H = d->hidden, I = d->inter, Q = (int64_t)d->hq * d->head_dim;
-  if (H < 128 || H % 128 != 0 || H > 65536 || I < 128 || I % 128 != 0 || I > (1 << 18)) return EAGLE_ERR_SHAPE;
+  if (H < 128 || H % 128 != 0 || H > 16384 || I < 128 || I % 128 != 0 || I > (1 << 18)) return EAGLE_ERR_SHAPE;
   if (d->max_prefix < 1) return EAGLE_ERR_SHAPE;
   rc = check_attn(B, S, d->hq, d->hkv, d->head_dim, d->max_prefix, EAGLE_BF16);
   if (rc != EAGLE_OK) return rc;

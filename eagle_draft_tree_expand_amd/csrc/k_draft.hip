@@ -29,7 +29,10 @@
 //   LM head       draft rows z = a W^T written at their slots of [B, S, V]
 // The GEMMs are the streaming LM-head kernel (weights read once, straight
 // from HBM into registers; the hidden dimension split over workgroups for the
-// narrow outputs); at batch 1 every step is weight- or launch-bound.
+// narrow outputs), or the tiled GEMM for many rows.  A split product's fp32
+// slices are summed by the kernel that consumes it (norm, draft_qkv,
+// draft_silu), not by a launch of their own.  At batch 1 every step is
+// weight- or launch-bound.
 #include "common.h"
 #include "kernels.h"
 
@@ -101,25 +104,74 @@ __global__ __launch_bounds__(kDT) void draft_in_kernel(
   }
 }
 
-// One workgroup per row: h = a + b (b optional); writes any of hout = h,
-// nout = bf16(h / sqrt(mean(h^2) + eps)), xout = bf16(h), and bf16(h) to the
-// slot-indexed feature row fout[idx[r]].
-__global__ __launch_bounds__(kDT) void draft_norm_kernel(int H, const float* __restrict__ a,
-                                                         const float* __restrict__ bsum, float* __restrict__ hout,
-                                                         uint16_t* __restrict__ nout, uint16_t* __restrict__ xout,
-                                                         uint16_t* __restrict__ fout,
-                                                         const int32_t* __restrict__ idx) {
-  __shared__ float red[kDT / 64];
+// The products' hidden-split slices are summed here, in slice order (eight
+// slices' loads in flight), by the kernel that consumes the product: x = sum
+// over kz < ks of src[kz * slice + e].
+struct Slices {
+  const float* src;
+  int ks;
+  size_t slice;
+};
+
+EDEV float4 sum_slices4(const Slices& p, size_t e) {
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  const float* q = p.src + e;
+  for (int kz0 = 0; kz0 < p.ks; kz0 += 8) {
+    float4 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = kz0 + j < p.ks ? *reinterpret_cast<const float4*>(q + (size_t)(kz0 + j) * p.slice)
+                            : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (kz0 + j < p.ks) { acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w; }
+  }
+  return acc;
+}
+
+EDEV float2 sum_slices2(const Slices& p, size_t e) {
+  float2 acc = make_float2(0.f, 0.f);
+  const float* q = p.src + e;
+  for (int kz0 = 0; kz0 < p.ks; kz0 += 8) {
+    float2 v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      v[j] = kz0 + j < p.ks ? *reinterpret_cast<const float2*>(q + (size_t)(kz0 + j) * p.slice) : make_float2(0.f, 0.f);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (kz0 + j < p.ks) { acc.x += v[j].x; acc.y += v[j].y; }
+  }
+  return acc;
+}
+
+EDEV bool finite4(float4 v) { return isfinite(v.x) && isfinite(v.y) && isfinite(v.z) && isfinite(v.w); }
+
+constexpr int kNT = 1024;          // threads of the norm kernel
+// hidden sizes up to kNT * 16 = 16384 are held in registers (4 float4 per thread)
+
+// One workgroup per row r: h = (the product's row) + res (res optional);
+// writes any of hout = h, nout = bf16(h / sqrt(mean(h^2) + 1e-6)), xout =
+// bf16(h), and bf16(h) to the slot-indexed feature row fout[idx[r]].
+__global__ __launch_bounds__(kNT) void draft_norm_kernel(int H, Slices p, const float* __restrict__ res,
+                                                         float* __restrict__ hout, uint16_t* __restrict__ nout,
+                                                         uint16_t* __restrict__ xout, uint16_t* __restrict__ fout,
+                                                         const int32_t* __restrict__ idx, int32_t* status) {
+  __shared__ float red[kNT / 64];
   const int r = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const float* ar = a + (size_t)r * H;
-  const float* br = bsum ? bsum + (size_t)r * H : nullptr;
+  float4 h[4];
   float ss = 0.f;
-  for (int i = tid * 4; i < H; i += kDT * 4) {
-    float4 v = *reinterpret_cast<const float4*>(ar + i);
-    if (br) {
-      const float4 w = *reinterpret_cast<const float4*>(br + i);
+  bool bad = false;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = (j * kNT + tid) * 4;
+    if (i >= H) continue;
+    float4 v = sum_slices4(p, (size_t)r * H + i);
+    if (res) {
+      const float4 w = *reinterpret_cast<const float4*>(res + (size_t)r * H + i);
       v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
     }
+    bad |= !finite4(v);
+    h[j] = v;
     ss = fmaf(v.x, v.x, fmaf(v.y, v.y, fmaf(v.z, v.z, fmaf(v.w, v.w, ss))));
     if (hout) *reinterpret_cast<float4*>(hout + (size_t)r * H + i) = v;
     const uint32_t lo = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
@@ -127,55 +179,66 @@ __global__ __launch_bounds__(kDT) void draft_norm_kernel(int H, const float* __r
     if (xout) *reinterpret_cast<uint2*>(xout + (size_t)r * H + i) = make_uint2(lo, hi);
     if (fout) *reinterpret_cast<uint2*>(fout + (size_t)idx[r] * H + i) = make_uint2(lo, hi);
   }
+  if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
   if (!nout) return;
   ss = wave_sum(ss);
   if (lane == 0) red[wave] = ss;
   __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H + 1e-6f);
-  for (int i = tid * 4; i < H; i += kDT * 4) {
-    float4 v = *reinterpret_cast<const float4*>(ar + i);
-    if (br) {
-      const float4 w = *reinterpret_cast<const float4*>(br + i);
-      v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
-    }
+  float tot = 0.f;
+#pragma unroll
+  for (int w = 0; w < kNT / 64; ++w) tot += red[w];
+  const float inv = 1.0f / sqrtf(tot / (float)H + 1e-6f);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = (j * kNT + tid) * 4;
+    if (i >= H) continue;
+    const float4 v = h[j];
     const uint32_t lo = (uint32_t)f32_to_bf16(v.x * inv) | ((uint32_t)f32_to_bf16(v.y * inv) << 16);
     const uint32_t hi = (uint32_t)f32_to_bf16(v.z * inv) | ((uint32_t)f32_to_bf16(v.w * inv) << 16);
     *reinterpret_cast<uint2*>(nout + (size_t)r * H + i) = make_uint2(lo, hi);
   }
 }
 
-// One workgroup per row: the fp32 [q | k | v] row to bf16: q to row r of the
-// frontier's queries, k and v to the rows of slot idx[r].
-__global__ __launch_bounds__(kDT) void draft_qkv_kernel(int Q, int KV, const float* __restrict__ qkv,
+// The [q | k | v] product rows to bf16: q to row r of the frontier's queries,
+// k and v to the rows of slot idx[r]; one thread per pair of columns.
+__global__ __launch_bounds__(kDT) void draft_qkv_kernel(int R, int Q, int KV, Slices p,
                                                         const int32_t* __restrict__ idx, uint16_t* __restrict__ sq,
-                                                        uint16_t* __restrict__ sk, uint16_t* __restrict__ sv) {
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const size_t o = (size_t)idx[r];
-  const int n = Q + 2 * KV;
-  const float* src = qkv + (size_t)r * n;
-  for (int i = tid * 2; i < n; i += kDT * 2) {
-    const float2 v = *reinterpret_cast<const float2*>(src + i);
-    const uint32_t p = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
-    uint16_t* dst = i < Q ? sq + (size_t)r * Q + i : i < Q + KV ? sk + o * KV + (i - Q) : sv + o * KV + (i - Q - KV);
-    *reinterpret_cast<uint32_t*>(dst) = p;
-  }
-}
-
-// bf16(silu(g) * u) from fp32 [g | u] rows (I each); one thread per pair of
-// columns over all rows.
-__global__ __launch_bounds__(kDT) void draft_silu_kernel(int R, int I, const float* __restrict__ gu,
-                                                         uint16_t* __restrict__ out) {
-  const int hp = I / 2;
+                                                        uint16_t* __restrict__ sk, uint16_t* __restrict__ sv,
+                                                        int32_t* status) {
+  const int n = Q + 2 * KV, hp = n / 2;
   const size_t total = (size_t)R * hp;
+  bool bad = false;
   for (size_t x = (size_t)blockIdx.x * kDT + threadIdx.x; x < total; x += (size_t)gridDim.x * kDT) {
     const int r = (int)(x / hp), i = (int)(x - (size_t)r * hp) * 2;
-    const float* g = gu + (size_t)r * 2 * I + i;
-    const float2 gv = *reinterpret_cast<const float2*>(g), uv = *reinterpret_cast<const float2*>(g + I);
+    const float2 v = sum_slices2(p, (size_t)r * n + i);
+    bad |= !(isfinite(v.x) && isfinite(v.y));
+    const size_t o = (size_t)idx[r];
+    const uint32_t pk = (uint32_t)f32_to_bf16(v.x) | ((uint32_t)f32_to_bf16(v.y) << 16);
+    uint16_t* dst = i < Q ? sq + (size_t)r * Q + i : i < Q + KV ? sk + o * KV + (i - Q) : sv + o * KV + (i - Q - KV);
+    *reinterpret_cast<uint32_t*>(dst) = pk;
+  }
+  if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
+}
+
+// bf16(silu(g) * u) from the [g | u] product rows (I each); one thread per
+// pair of columns over all rows.
+__global__ __launch_bounds__(kDT) void draft_silu_kernel(int R, int I, Slices p, uint16_t* __restrict__ out,
+                                                         int32_t* status) {
+  const int hp = I / 2;
+  const size_t total = (size_t)R * hp;
+  bool bad = false;
+  for (size_t x = (size_t)blockIdx.x * kDT + threadIdx.x; x < total; x += (size_t)gridDim.x * kDT) {
+    const int r = (int)(x / hp), i = (int)(x - (size_t)r * hp) * 2;
+    const float2 gv = sum_slices2(p, (size_t)r * 2 * I + i), uv = sum_slices2(p, (size_t)r * 2 * I + I + i);
+    bad |= !(isfinite(gv.x) && isfinite(gv.y) && isfinite(uv.x) && isfinite(uv.y));
     const float a = gv.x / (1.0f + expf(-gv.x)) * uv.x, c = gv.y / (1.0f + expf(-gv.y)) * uv.y;
     *reinterpret_cast<uint32_t*>(out + (size_t)r * I + i) =
         (uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(c) << 16);
   }
+  if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
 }
+
+int grid_for(size_t items) { return (int)((items + kDT - 1) / kDT < 2048 ? (items + kDT - 1) / kDT : 2048); }
 
 size_t up256(size_t x) { return (x + 255) / 256 * 256; }
 
@@ -243,13 +306,15 @@ hipError_t launch_draft_forward(const DraftArgs& a, hipStream_t st) {
                                      reinterpret_cast<uint64_t*>(base + L.slot_mask), P16(L.slot_k), P16(L.slot_v),
                                      idx, P16(L.x0), a.status);
   EAGLE_CK(hipGetLastError());
-  EAGLE_CK(launch_lmhead_map(R, 2 * H, H, EAGLE_BF16, EAGLE_W_PACKED, P16(L.x0), a.w.fc, 1.f, PF(L.u), nullptr,
-                             nullptr, nullptr, gws, a.status, id, st));
-  draft_norm_kernel<<<R, kDT, 0, st>>>(H, PF(L.u), nullptr, nullptr, P16(L.n1), nullptr, nullptr, idx);
+  ProductOut po;
+  auto sl = [&]() { return Slices{po.src, po.ks, po.slice}; };
+  EAGLE_CK(launch_product(R, 2 * H, H, P16(L.x0), a.w.fc, PF(L.u), gws, a.status, &po, st));
+  // u (kept as the residual) and n1 = bf16(rms(u))
+  draft_norm_kernel<<<R, kNT, 0, st>>>(H, sl(), nullptr, PF(L.u), P16(L.n1), nullptr, nullptr, idx, a.status);
   EAGLE_CK(hipGetLastError());
-  EAGLE_CK(launch_lmhead_map(R, H, Q + 2 * KV, EAGLE_BF16, EAGLE_W_PACKED, P16(L.n1), a.w.qkv, 1.f, PF(L.qkv),
-                             nullptr, nullptr, nullptr, gws, a.status, id, st));
-  draft_qkv_kernel<<<R, kDT, 0, st>>>(Q, KV, PF(L.qkv), idx, P16(L.qc), P16(L.slot_k), P16(L.slot_v));
+  EAGLE_CK(launch_product(R, H, Q + 2 * KV, P16(L.n1), a.w.qkv, PF(L.qkv), gws, a.status, &po, st));
+  draft_qkv_kernel<<<grid_for((size_t)R * (Q + 2 * KV) / 2), kDT, 0, st>>>(R, Q, KV, sl(), idx, P16(L.qc),
+                                                                          P16(L.slot_k), P16(L.slot_v), a.status);
   EAGLE_CK(hipGetLastError());
   // the frontier's kd queries are tree nodes s0 .. s0+kd-1 of the S slots;
   // the output rows come out in frontier order, ready for the o product
@@ -258,21 +323,17 @@ hipError_t launch_draft_forward(const DraftArgs& a, hipStream_t st) {
                                    reinterpret_cast<const uint64_t*>(base + L.slot_mask), a.scale, P16(L.og),
                                    PF(L.attn), attn_plan(B, kd, a.hq, a.hkv, a.dh, a.max_prefix, EAGLE_BF16),
                                    a.status, st));
-  EAGLE_CK(launch_lmhead_map(R, Q, H, EAGLE_BF16, EAGLE_W_PACKED, P16(L.og), a.w.o, 1.f, PF(L.y), nullptr, nullptr,
-                             nullptr, gws, a.status, id, st));
-  draft_norm_kernel<<<R, kDT, 0, st>>>(H, PF(L.u), PF(L.y), PF(L.h), P16(L.n2), nullptr, nullptr, idx);
+  EAGLE_CK(launch_product(R, Q, H, P16(L.og), a.w.o, PF(L.y), gws, a.status, &po, st));
+  // h = u + o Wo^T and n2 = bf16(rms(h))
+  draft_norm_kernel<<<R, kNT, 0, st>>>(H, sl(), PF(L.u), PF(L.h), P16(L.n2), nullptr, nullptr, idx, a.status);
   EAGLE_CK(hipGetLastError());
-  EAGLE_CK(launch_lmhead_map(R, H, 2 * I, EAGLE_BF16, EAGLE_W_PACKED, P16(L.n2), a.w.gate_up, 1.f, PF(L.gu), nullptr,
-                             nullptr, nullptr, gws, a.status, id, st));
-  {
-    const size_t pairs = (size_t)R * (I / 2);
-    const int grid = (int)((pairs + kDT - 1) / kDT < 2048 ? (pairs + kDT - 1) / kDT : 2048);
-    draft_silu_kernel<<<grid, kDT, 0, st>>>(R, I, PF(L.gu), P16(L.mm));
-  }
+  EAGLE_CK(launch_product(R, H, 2 * I, P16(L.n2), a.w.gate_up, PF(L.gu), gws, a.status, &po, st));
+  draft_silu_kernel<<<grid_for((size_t)R * I / 2), kDT, 0, st>>>(R, I, sl(), P16(L.mm), a.status);
   EAGLE_CK(hipGetLastError());
-  EAGLE_CK(launch_lmhead_map(R, I, H, EAGLE_BF16, EAGLE_W_PACKED, P16(L.mm), a.w.down, 1.f, PF(L.y), nullptr, nullptr,
-                             nullptr, gws, a.status, id, st));
-  draft_norm_kernel<<<R, kDT, 0, st>>>(H, PF(L.h), PF(L.y), nullptr, nullptr, P16(L.xa), P16(L.slot_feat), idx);
+  EAGLE_CK(launch_product(R, I, H, P16(L.mm), a.w.down, PF(L.y), gws, a.status, &po, st));
+  // a = h + m Wd^T: bf16 to the LM-head input and to the slot's feature
+  draft_norm_kernel<<<R, kNT, 0, st>>>(H, sl(), PF(L.h), nullptr, nullptr, P16(L.xa), P16(L.slot_feat), idx,
+                                       a.status);
   EAGLE_CK(hipGetLastError());
   // draft rows of the frontier at their slots: row r -> (r / kd) * S + s0 + r % kd
   EAGLE_CK(launch_lmhead_map(R, H, a.V, EAGLE_BF16, EAGLE_W_PACKED, P16(L.xa), a.w.lm_head, 1.f, a.rows, nullptr,

@@ -767,6 +767,24 @@ hipError_t launch_lmhead(int rows, int H, int V, int dtype, int w_layout, const 
 hipError_t launch_lmhead_map(int rows, int H, int V, int dtype, int w_layout, const void* x, const void* w, float T,
                              float* logits, float* row_stats, int32_t* row_argmax, float* probs, float* ws_part,
                              int32_t* status, RowMap rm, hipStream_t st) {
+  return launch_lmhead_impl(rows, H, V, dtype, w_layout, x, w, T, logits, row_stats, row_argmax, probs, ws_part,
+                            status, rm, nullptr, st);
+}
+
+hipError_t launch_product(int rows, int H, int V, const void* x, const void* w_packed, float* out, float* ws_part,
+                          int32_t* status, ProductOut* po, hipStream_t st) {
+  int ks = 1;
+  hipError_t e = launch_lmhead_impl(rows, H, V, EAGLE_BF16, EAGLE_W_PACKED, x, w_packed, 1.f, out, nullptr, nullptr,
+                                    nullptr, ws_part, status, RowMap{1 << 30, 0, 0}, &ks, st);
+  po->ks = ks;
+  po->src = ks > 1 ? ws_part + lm_rec_floats(rows, V) : out;
+  po->slice = (size_t)rows * V;
+  return e;
+}
+
+hipError_t launch_lmhead_impl(int rows, int H, int V, int dtype, int w_layout, const void* x, const void* w, float T,
+                              float* logits, float* row_stats, int32_t* row_argmax, float* probs, float* ws_part,
+                              int32_t* status, RowMap rm, int* defer_ks, hipStream_t st) {
   const float Tp = (T > 0.f) ? T : 1.0f;
   int ntiles = lm_ntiles(V);
   if (dtype == EAGLE_BF16 && rows >= kGemmMinRows) {
@@ -787,7 +805,8 @@ hipError_t launch_lmhead_map(int rows, int H, int V, int dtype, int w_layout, co
       lmhead_gemm_kernel<false><<<gps * ks, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
                                                             (const uint16_t*)w, logits, ws_part, status, rm, gps,
                                                             H / ks, partial);
-    if (ks > 1) {
+    if (defer_ks) *defer_ks = ks;
+    if (ks > 1 && !defer_ks) {
       hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
       lm_combine_kernel<<<dim3(lm_ntiles(V), rows), 256, 0, st>>>(rows, V, ks, Tp, partial, logits, ws_part, status,
@@ -803,7 +822,8 @@ hipError_t launch_lmhead_map(int rows, int H, int V, int dtype, int w_layout, co
     else
       lmhead_bf16_kernel<false><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
                                                       ws_part, status, H / ks, partial, rm);
-    if (ks > 1) {
+    if (defer_ks) *defer_ks = ks;
+    if (ks > 1 && !defer_ks) {
       hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
       lm_combine_kernel<<<dim3(ntiles, rows), 256, 0, st>>>(rows, V, ks, Tp, partial, logits, ws_part, status, rm);

@@ -150,6 +150,19 @@ __host__ __device__ inline int map_row(int m, RowMap rm) {
 hipError_t launch_lmhead_map(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,
                              float T, float* logits, float* row_stats, int32_t* row_argmax, float* probs,
                              float* ws_part, int32_t* status, RowMap rm, hipStream_t st);
+hipError_t launch_lmhead_impl(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,
+                              float T, float* logits, float* row_stats, int32_t* row_argmax, float* probs,
+                              float* ws_part, int32_t* status, RowMap rm, int* defer_ks, hipStream_t st);
+// A plain bf16 product out = X W^T (W packed) whose hidden-split slices, if
+// any, are left unsummed: the result is sum over kz < ks of src[kz * slice + r * V + n]
+// (ks = 1: src = out).  The caller's next kernel sums them.
+struct ProductOut {
+  int ks;
+  const float* src;
+  size_t slice;
+};
+hipError_t launch_product(int rows, int hidden, int V, const void* x, const void* w_packed, float* out, float* ws_part,
+                          int32_t* status, ProductOut* po, hipStream_t st);
 size_t lm_packed_bytes(int V, int hidden);
 hipError_t launch_pack_lmhead(int V, int hidden, const void* w, void* wp, hipStream_t st);
 

@@ -390,7 +390,7 @@ int eagle_commit_accepted(int32_t batch, int32_t n, int32_t hkv, int32_t head_di
  * the node's token.  Activations are bf16 at every matmul input (and a as fed
  * on), accumulation fp32. */
 typedef struct {
-    int32_t hidden;      /* H, a multiple of 128                               */
+    int32_t hidden;      /* H, a multiple of 128, at most 16384                */
     int32_t hq, hkv;     /* query / key-value heads, hq % hkv == 0              */
     int32_t head_dim;    /* 64 or 128; hq * head_dim a multiple of 128          */
     int32_t inter;       /* MLP width I, a multiple of 128                      */
