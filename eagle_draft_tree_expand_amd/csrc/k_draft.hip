@@ -106,24 +106,26 @@ __global__ __launch_bounds__(kDT) void draft_in_kernel(
 
 // The products' hidden-split slices are summed here, in slice order (eight
 // slices' loads in flight), by the kernel that consumes the product: x = sum
-// over kz < ks of src[kz * slice + e].
+// over kz < ks of src[kz * slice + e].  (Slice order is kept whatever the
+// number in flight, so the sums do not depend on it.)
 struct Slices {
   const float* src;
   int ks;
   size_t slice;
 };
 
+template <int NB>  // slices' loads in flight
 EDEV float4 sum_slices4(const Slices& p, size_t e) {
   float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
   const float* q = p.src + e;
-  for (int kz0 = 0; kz0 < p.ks; kz0 += 8) {
-    float4 v[8];
+  for (int kz0 = 0; kz0 < p.ks; kz0 += NB) {
+    float4 v[NB];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NB; ++j)
       v[j] = kz0 + j < p.ks ? *reinterpret_cast<const float4*>(q + (size_t)(kz0 + j) * p.slice)
                             : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
+    for (int j = 0; j < NB; ++j)
       if (kz0 + j < p.ks) { acc.x += v[j].x; acc.y += v[j].y; acc.z += v[j].z; acc.w += v[j].w; }
   }
   return acc;
@@ -165,7 +167,7 @@ __global__ __launch_bounds__(kNT) void draft_norm_kernel(int H, Slices p, const 
   for (int j = 0; j < 4; ++j) {
     const int i = (j * kNT + tid) * 4;
     if (i >= H) continue;
-    float4 v = sum_slices4(p, (size_t)r * H + i);
+    float4 v = sum_slices4<16>(p, (size_t)r * H + i);
     if (res) {
       const float4 w = *reinterpret_cast<const float4*>(res + (size_t)r * H + i);
       v.x += w.x; v.y += w.y; v.z += w.z; v.w += w.w;
