@@ -307,8 +307,8 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(each request's round fits one GPU; see the sharding notes in DESIGN.md).", file=sys.stderr)
+        print("bench.py measures one GPU only: there is no multi-GPU path "
+              "(each request's round fits one GPU).", file=sys.stderr)
         sys.exit(2)
 
     import torch
