@@ -407,7 +407,10 @@ AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, 
   int sk = (max_prefix + target - 1) / (target > 0 ? target : 1);
   sk = (sk + kKT - 1) / kKT * kKT;
   if (sk < 128) sk = 128;
-  if (sk > 1024) sk = 1024;
+  // Many (request, kv head) pairs fill the chip by themselves: longer splits
+  // then write fewer partial rows for the merge to read back.
+  const int cap = per >= 256 ? 2048 : 1024;
+  if (sk > cap) sk = cap;
   // Few (request, kv head) pairs and long prefixes: 384-key splits measured
   // best (13B- and 70B-shaped rounds at batch 1: 49 and 38 us against 69 and
   // 48 us with the rule above); shorter splits write more partial rows, longer

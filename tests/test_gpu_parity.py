@@ -125,6 +125,8 @@ ATTN_CASES = [
     ("mid_bf16", dict(L=(0, 0)), 2e-2),                           # empty prefix: tree only
     ("mid_bf16", dict(L=(2100, 3000)), 2e-2),                     # long prefix: 384-key splits
     ("mid_bf16", dict(hq=4, hkv=4, H=512, L=(2049, 2600)), 2e-2),  # MHA, long prefix
+    # 256 (request, kv head) pairs: 2048-key splits
+    ("mid_bf16", dict(B=64, hq=4, hkv=4, dh=64, H=256, D=3, k=2, m=4, L=(1100, 3000)), 2e-2),
     ("mid_f32", {}, 1e-5),
     ("tiny", {}, 1e-5),
 ]
