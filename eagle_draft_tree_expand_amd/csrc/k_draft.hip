@@ -47,7 +47,7 @@ EDEV void st16(void* p, uint4 v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // One workgroup per frontier row r (request b = r / kd, slot s0 + r % kd).
 __global__ __launch_bounds__(kDT) void draft_in_kernel(
-    int depth, int kd, int s0, int S, int k, int P, int H, int V, int Q, int KV, int W,
+    int depth, int kd, int s0, int S, int k, int P, int H, int V, int KV, int W,
     const int32_t* __restrict__ root, const uint16_t* __restrict__ root_feat, const int32_t* __restrict__ pool_tok,
     const int32_t* __restrict__ slot_src, const uint16_t* __restrict__ embed, uint16_t* __restrict__ slot_feat,
     uint64_t* __restrict__ slot_mask, uint16_t* __restrict__ slot_k, uint16_t* __restrict__ slot_v,
@@ -303,7 +303,7 @@ hipError_t launch_draft_forward(const DraftArgs& a, hipStream_t st) {
     if (e != hipSuccess) return e; \
   } while (0)
 
-  draft_in_kernel<<<R, kDT, 0, st>>>(a.depth, kd, s0, S, k, P, H, a.V, Q, KV, W, a.root, (const uint16_t*)a.root_feat,
+  draft_in_kernel<<<R, kDT, 0, st>>>(a.depth, kd, s0, S, k, P, H, a.V, KV, W, a.root, (const uint16_t*)a.root_feat,
                                      a.pool_tok, a.slot_src, (const uint16_t*)a.w.embed, P16(L.slot_feat),
                                      reinterpret_cast<uint64_t*>(base + L.slot_mask), P16(L.slot_k), P16(L.slot_v),
                                      idx, P16(L.x0), a.status);
