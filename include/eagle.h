@@ -10,7 +10,15 @@
  *   eagle_lmhead_softmax   LM-head logits + per-row softmax statistics + argmax
  *   eagle_verify_accept    recursive speculative sampling down the tree
  *
- * plus workspace helpers and one row-gather helper.
+ * plus workspace helpers and row-gather helpers, and the steps around the
+ * round:
+ *
+ *   eagle_sampling_warp (+ the _warped variants of expand and accept)
+ *                          top-k / nucleus applied to both distributions
+ *   eagle_commit_accepted  the accepted path appended to the prefix cache
+ *   eagle_draft_forward, eagle_expand_depth, eagle_expand_finish
+ *                          the tree drafted depth by depth by a synthetic
+ *                          EAGLE draft head
  *
  * Conventions (all entry points):
  *   - Every pointer argument named as a tensor is DEVICE memory owned by the
