@@ -394,6 +394,55 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int nq, int hq, int hkv
   }
 }
 
+// grid (ceil(rows / 16), hkv, B), 256 threads: the 16 query rows r0.. of one
+// (request, kv head), four per wave, one row at a time.  Up to 64 splits: lane
+// s holds split s's max and sum; each lane then sums its DH / 64 output
+// elements over the splits in split order.
+template <bool BF16, int DH>
+__global__ __launch_bounds__(256) void attn_merge_rows_kernel(int nq, int hq, int hkv, const float* __restrict__ ws,
+                                                              int rows, int rows_pad, int nsplit,
+                                                              void* __restrict__ out) {
+  constexpr int PER = DH / 64;  // output elements per lane
+  const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int G = hq / hkv, nsp1 = nsplit + 1;
+  const size_t sstride = (size_t)rows_pad * (DH + 2);
+  for (int q = 0; q < 4; ++q) {
+    const int r = blockIdx.x * 16 + wave * 4 + q;
+    if (r >= rows) break;
+    const float* p0 = partial_row(const_cast<float*>(ws), b, g, hkv, nsp1, 0, rows_pad, r, DH);
+    const float ms = lane < nsp1 ? p0[lane * sstride + DH] : kNegInf;
+    const float ls = lane < nsp1 ? p0[lane * sstride + DH + 1] : 0.f;
+    const float M = wave_max(ms);
+    const float w = ms == kNegInf ? 0.f : expf(ms - M);
+    const float L = wave_sum(ls * w);
+    float acc[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) acc[e] = 0.f;
+    for (int s0 = 0; s0 < nsp1; s0 += 8) {
+      float v[8][PER];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[j][e] = s0 + j < nsp1 ? p0[(s0 + j) * sstride + lane * PER + e] : 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float wj = __shfl(w, s0 + j < 64 ? s0 + j : 63);
+#pragma unroll
+        for (int e = 0; e < PER; ++e)
+          if (s0 + j < nsp1) acc[e] += v[j][e] * wj;
+      }
+    }
+    const int node = r / G, h = g * G + (r - node * G);
+    const size_t o = (((size_t)b * nq + node) * hq + h) * DH + lane * PER;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const float val = L > 0.f ? acc[e] / L : 0.f;
+      if (BF16) reinterpret_cast<uint16_t*>(out)[o + e] = f32_to_bf16(val);
+      else reinterpret_cast<float*>(out)[o + e] = val;
+    }
+  }
+}
+
 }  // namespace
 
 AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, int dtype) {
@@ -468,6 +517,20 @@ hipError_t launch_attention_window(int B, int n, int nq, int qoff, int hq, int h
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (pl.nsplit + 1 <= 64 && (DH == 64 || DH == 128)) {
+    dim3 rg((pl.rows + 15) / 16, hkv, B);
+#define EAGLE_MERGE_ROWS(BF, D) \
+  attn_merge_rows_kernel<BF, D><<<rg, 256, 0, st>>>(nq, hq, hkv, ws, pl.rows, pl.rows_pad, pl.nsplit, out)
+    if (dtype == EAGLE_BF16) {
+      if (DH == 64) EAGLE_MERGE_ROWS(true, 64);
+      else EAGLE_MERGE_ROWS(true, 128);
+    } else {
+      if (DH == 64) EAGLE_MERGE_ROWS(false, 64);
+      else EAGLE_MERGE_ROWS(false, 128);
+    }
+#undef EAGLE_MERGE_ROWS
+    return hipGetLastError();
+  }
   dim3 mg(nq, hq, B);
   const int mt = DH <= 64 ? 64 : 128;  // whole waves (the merge reduces across lanes)
   const size_t lds = (size_t)(pl.nsplit + 1) * sizeof(float);
