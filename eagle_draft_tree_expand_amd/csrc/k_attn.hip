@@ -394,10 +394,10 @@ __global__ __launch_bounds__(128) void attn_merge_kernel(int nq, int hq, int hkv
   }
 }
 
-// grid (ceil(rows / 16), hkv, B), 256 threads: the 16 query rows r0.. of one
-// (request, kv head), four per wave, one row at a time.  Up to 64 splits: lane
-// s holds split s's max and sum; each lane then sums its DH / 64 output
-// elements over the splits in split order.
+// grid (ceil(rows / 4), hkv, B), 256 threads: four query rows of one
+// (request, kv head), one per wave.  Up to 64 splits: lane s holds split s's
+// max and sum; each lane then sums its DH / 64 output elements over the
+// splits in split order.
 template <bool BF16, int DH>
 __global__ __launch_bounds__(256) void attn_merge_rows_kernel(int nq, int hq, int hkv, const float* __restrict__ ws,
                                                               int rows, int rows_pad, int nsplit,
@@ -406,9 +406,9 @@ __global__ __launch_bounds__(256) void attn_merge_rows_kernel(int nq, int hq, in
   const int g = blockIdx.y, b = blockIdx.z, lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = hq / hkv, nsp1 = nsplit + 1;
   const size_t sstride = (size_t)rows_pad * (DH + 2);
-  for (int q = 0; q < 4; ++q) {
-    const int r = blockIdx.x * 16 + wave * 4 + q;
-    if (r >= rows) break;
+  {
+    const int r = blockIdx.x * 4 + wave;
+    if (r >= rows) return;
     const float* p0 = partial_row(const_cast<float*>(ws), b, g, hkv, nsp1, 0, rows_pad, r, DH);
     const float ms = lane < nsp1 ? p0[lane * sstride + DH] : kNegInf;
     const float ls = lane < nsp1 ? p0[lane * sstride + DH + 1] : 0.f;
@@ -518,7 +518,7 @@ hipError_t launch_attention_window(int B, int n, int nq, int qoff, int hq, int h
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (pl.nsplit + 1 <= 64 && (DH == 64 || DH == 128)) {
-    dim3 rg((pl.rows + 15) / 16, hkv, B);
+    dim3 rg((pl.rows + 3) / 4, hkv, B);
 #define EAGLE_MERGE_ROWS(BF, D) \
   attn_merge_rows_kernel<BF, D><<<rg, 256, 0, st>>>(nq, hq, hkv, ws, pl.rows, pl.rows_pad, pl.nsplit, out)
     if (dtype == EAGLE_BF16) {
