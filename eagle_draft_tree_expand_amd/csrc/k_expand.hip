@@ -526,11 +526,13 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
   int* slot_src = flat_of + P;                                     // [S]
   int* sel_e = slot_src + S;                                       // [m] pool index of each selected node
   int* sel_dep = sel_e + m;                                        // [m]
+  int* ptok = sel_dep + m;                                         // [P] pool tokens, read with q up front
   __shared__ int n_sel;
 
   const float* pq = pool_q_g + (size_t)b * P;
   for (int e = tid; e < P; e += nt) {
     const float qe = pq[e];
+    ptok[e] = pool_tok_g[(size_t)b * P + e];
     q[e] = qe;
     flat_of[e] = -1;
   }
@@ -660,7 +662,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     }
     const int lr = lrank[e];
     const size_t o = (size_t)b * N + f;
-    node_tok[o] = pool_tok_g[(size_t)b * P + e];
+    node_tok[o] = ptok[e];
     node_parent[o] = pf;
     node_depth[o] = de;
     node_sib[o] = e % k;
@@ -728,7 +730,7 @@ hipError_t launch_assemble(int B, int S, int V, int D, int k, int m, int upto, c
   const int P = S * k;
   const size_t LS = (size_t)((k * k + 1) & ~1);
   const size_t sm3 = (2 * (size_t)D * LS + S + 2 * (size_t)m) * 8 + (size_t)P * 3 * 4 + (size_t)S * 4 +
-                     (size_t)m * 2 * 4;
+                     (size_t)m * 2 * 4 + (size_t)P * 4;
   tree_assemble_kernel<<<B, kTreeThreads, sm3, st>>>(S, k, D, m, V, root, pool_tok, pool_q, node_tok, node_parent,
                                                      node_depth, node_sib, node_slot, node_value, node_q, pool_flat,
                                                      slot_src, status, upto);
