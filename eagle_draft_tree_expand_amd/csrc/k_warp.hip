@@ -166,7 +166,9 @@ EDEV unsigned long long weight(const RowCtx& r, float t, bool mass) {
 
 // First token of the order (restricted to tokens before_eq `lim`) at which the
 // running weight reaches `target` (all threads call; the result is uniform).
-EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, WarpSmem& sm) {
+// key_only: stop after the digit passes and return {key of the crossing
+// token, -1} (sm.below = weight of the tokens with smaller keys).
+EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, WarpSmem& sm, bool key_only = false) {
   const int tid = threadIdx.x, lane = tid & 63;
   int bad = 0;
   if (tid == 0) { sm.prefix = 0; sm.below = 0; }
@@ -249,6 +251,12 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
       }
     }
     __syncthreads();
+  }
+  if (key_only) {
+    if (bad) sm.bad = 1;
+    const Cut kc{sm.prefix, -1};
+    __syncthreads();
+    return kc;
   }
   // Tokens equal to the chosen key, in id order.  Usually a handful: they
   // are listed in LDS and ranked by id in wave 0.  Past kWList of them (near
@@ -363,9 +371,11 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
   Cut cut = all;
   int nA = V;
   if (top_k > 0 && top_k < V && top_k <= kWFast) {
-    // The top-k cut needs no M (counts only).  Then its tokens go to LDS.
-    cut = select_cut(r, all, false, (double)top_k, sm);
-    nA = top_k;
+    // The top-k cut's key needs no M (counts only).  One pass then lists
+    // every token at or before that key (the key's ties included) in LDS,
+    // where the ties are ordered by id: the list's first top_k tokens are
+    // the kept ones.
+    const Cut kc = select_cut(r, all, false, (double)top_k, sm, true);
     FastList& fl = sm.fl;
     if (tid == 0) { fl.n = 0; fl.ci = 0x7fffffff; }
     __syncthreads();
@@ -378,69 +388,74 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
         if (v >= V) continue;
         const float t = t_from(r, zz[j], &bad);
         const uint32_t key = ~tcode(t);
-        if (!before_eq(key, v, cut)) continue;
+        if (key > kc.key) continue;
         const int i = atomicAdd(&fl.n, 1);
         if (i < kWFast) { fl.key[i] = key; fl.id[i] = v; fl.t[i] = t; }
       }
     }
     __syncthreads();
-    const int n = min(fl.n, kWFast);  // the cut keeps exactly top_k tokens
-    if (tid < n) {  // rank by (key asc, id asc); keys and ids are read from LDS
-      const uint32_t mk = fl.key[tid];
-      const int mi = fl.id[tid];
-      int rank = 0;
-      for (int q = 0; q < n; ++q) {
-        const uint32_t kq = fl.key[q];
-        rank += (kq < mk || (kq == mk && fl.id[q] < mi)) ? 1 : 0;
-      }
-      fl.skey[rank] = mk;
-      fl.sid[rank] = mi;
-      fl.st[rank] = fl.t[tid];
-    }
-    __syncthreads();
-    r.M = n > 0 ? fl.st[0] : kNegInf;  // the first of the order holds max t
-    if (r.M != kNegInf) {
-      int last = n - 1;  // index of the last kept token in the order
-      if (top_p < 1.0f) {
-        // fixed-point masses (as the row passes weigh them), inclusive prefix in order
-        const unsigned long long w = tid < n ? weight(r, fl.st[tid], true) : 0ull;
-        unsigned long long inc = w;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const unsigned long long y = __shfl_up(inc, o);
-          if ((tid & 63) >= o) inc += y;
+    const int nall = fl.n;
+    if (nall <= kWFast) {  // else too many ties at the cut key: the passes below decide
+      if (tid < nall) {  // rank by (key asc, id asc); keys and ids are read from LDS
+        const uint32_t mk = fl.key[tid];
+        const int mi = fl.id[tid];
+        int rank = 0;
+        for (int q = 0; q < nall; ++q) {
+          const uint32_t kq = fl.key[q];
+          rank += (kq < mk || (kq == mk && fl.id[q] < mi)) ? 1 : 0;
         }
-        if ((tid & 63) == 63) sm.part[tid >> 6] = inc;
-        __syncthreads();
-        unsigned long long wpre = 0, sa = 0;
-        for (int q = 0; q < kWWaves; ++q) {
-          if (q < (tid >> 6)) wpre += sm.part[q];
-          sa += sm.part[q];
-        }
-        inc += wpre;
-        // the first token at which the running mass reaches top_p of the top-k mass
-        const double target = (double)top_p * (double)sa;
-        if (tid < n && (double)inc >= target && (double)(inc - w) < target) atomicMin(&fl.ci, tid);
-        __syncthreads();
-        int ci = fl.ci == 0x7fffffff ? n - 1 : fl.ci;
-        if (min_keep > 1) ci = max(ci, min(min_keep, nA) - 1);
-        last = ci;
-        cut = Cut{fl.skey[ci], fl.sid[ci]};
+        fl.skey[rank] = mk;
+        fl.sid[rank] = mi;
+        fl.st[rank] = fl.t[tid];
       }
-      double sp = (tid <= last && fl.st[tid] != kNegInf) ? exp((double)fl.st[tid] - (double)r.M) : 0.0;
-      const double sfin = block_sum_d(sp, sm);
-      if (bad) sm.bad = 1;
       __syncthreads();
-      if (tid == 0) {
-        stats[(size_t)row * 2] = r.M;
-        stats[(size_t)row * 2 + 1] = (float)sfin;
-        bound[(size_t)row * 2] = ~cut.key;
-        bound[(size_t)row * 2 + 1] = (uint32_t)cut.id;
-        if (sm.bad) set_status(status, EAGLE_STATUS_NONFINITE);
+      const int n = min(top_k, nall);  // the cut keeps exactly top_k tokens
+      cut = Cut{fl.skey[n - 1], fl.sid[n - 1]};
+      nA = top_k;
+      r.M = n > 0 ? fl.st[0] : kNegInf;  // the first of the order holds max t
+      if (r.M != kNegInf) {
+        int last = n - 1;  // index of the last kept token in the order
+        if (top_p < 1.0f) {
+          // fixed-point masses (as the row passes weigh them), inclusive prefix in order
+          const unsigned long long w = tid < n ? weight(r, fl.st[tid], true) : 0ull;
+          unsigned long long inc = w;
+  #pragma unroll
+          for (int o = 1; o < 64; o <<= 1) {
+            const unsigned long long y = __shfl_up(inc, o);
+            if ((tid & 63) >= o) inc += y;
+          }
+          if ((tid & 63) == 63) sm.part[tid >> 6] = inc;
+          __syncthreads();
+          unsigned long long wpre = 0, sa = 0;
+          for (int q = 0; q < kWWaves; ++q) {
+            if (q < (tid >> 6)) wpre += sm.part[q];
+            sa += sm.part[q];
+          }
+          inc += wpre;
+          // the first token at which the running mass reaches top_p of the top-k mass
+          const double target = (double)top_p * (double)sa;
+          if (tid < n && (double)inc >= target && (double)(inc - w) < target) atomicMin(&fl.ci, tid);
+          __syncthreads();
+          int ci = fl.ci == 0x7fffffff ? n - 1 : fl.ci;
+          if (min_keep > 1) ci = max(ci, min(min_keep, nA) - 1);
+          last = ci;
+          cut = Cut{fl.skey[ci], fl.sid[ci]};
+        }
+        double sp = (tid <= last && fl.st[tid] != kNegInf) ? exp((double)fl.st[tid] - (double)r.M) : 0.0;
+        const double sfin = block_sum_d(sp, sm);
+        if (bad) sm.bad = 1;
+        __syncthreads();
+        if (tid == 0) {
+          stats[(size_t)row * 2] = r.M;
+          stats[(size_t)row * 2 + 1] = (float)sfin;
+          bound[(size_t)row * 2] = ~cut.key;
+          bound[(size_t)row * 2 + 1] = (uint32_t)cut.id;
+          if (sm.bad) set_status(status, EAGLE_STATUS_NONFINITE);
+        }
+        return;
       }
-      return;
+      // an all -inf row: the passes below handle it as before
     }
-    // an all -inf row: the passes below handle it as before
   }
   float lm = kNegInf;
   for (int v0 = 0; v0 < V; v0 += kWBatch) {
