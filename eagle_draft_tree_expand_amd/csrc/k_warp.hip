@@ -166,14 +166,16 @@ EDEV unsigned long long weight(const RowCtx& r, float t, bool mass) {
 
 // First token of the order (restricted to tokens before_eq `lim`) at which the
 // running weight reaches `target` (all threads call; the result is uniform).
-// key_only: stop after the digit passes and return {key of the crossing
-// token, -1} (sm.below = weight of the tokens with smaller keys).
-EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, WarpSmem& sm, bool key_only = false) {
+// key_only: stop after the first npass digit passes and return {key prefix
+// of the crossing token, -1} (sm.below = weight of the tokens with smaller
+// key prefixes; after one pass sm.hist still holds the first digit's counts).
+EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, WarpSmem& sm, bool key_only = false,
+                    int npass = 3) {
   const int tid = threadIdx.x, lane = tid & 63;
   int bad = 0;
   if (tid == 0) { sm.prefix = 0; sm.below = 0; }
   // digits: key bits [31:21], [20:10], [9:0]
-  for (int pass = 0; pass < 3; ++pass) {
+  for (int pass = 0; pass < (key_only ? npass : 3); ++pass) {
     const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
     const int nb = pass == 2 ? 1024 : 2048;
     for (int x = tid; x < kWBuckets; x += kWThreads) sm.hist[x] = 0;
@@ -372,10 +374,17 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
   int nA = V;
   if (top_k > 0 && top_k < V && top_k <= kWFast) {
     // The top-k cut's key needs no M (counts only).  One pass then lists
-    // every token at or before that key (the key's ties included) in LDS,
-    // where the ties are ordered by id: the list's first top_k tokens are
-    // the kept ones.
-    const Cut kc = select_cut(r, all, false, (double)top_k, sm, true);
+    // every token at or before that key (prefix) in LDS, where they are
+    // ordered by (key, id): the list's first top_k tokens are the kept ones.
+    // Usually the first digit suffices: the tokens whose first digit is at or
+    // before the crossing one number below + hist[digit], often a few hundred.
+    Cut kc = select_cut(r, all, false, (double)top_k, sm, true, 1);
+    const unsigned long long coarse_n = sm.below + sm.hist[kc.key >> 21];
+    uint32_t lim_key = kc.key | 0x1FFFFFu;
+    if (coarse_n > (unsigned long long)kWFast) {
+      kc = select_cut(r, all, false, (double)top_k, sm, true, 3);
+      lim_key = kc.key;
+    }
     FastList& fl = sm.fl;
     if (tid == 0) { fl.n = 0; fl.ci = 0x7fffffff; }
     __syncthreads();
@@ -388,7 +397,7 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
         if (v >= V) continue;
         const float t = t_from(r, zz[j], &bad);
         const uint32_t key = ~tcode(t);
-        if (key > kc.key) continue;
+        if (key > lim_key) continue;
         const int i = atomicAdd(&fl.n, 1);
         if (i < kWFast) { fl.key[i] = key; fl.id[i] = v; fl.t[i] = t; }
       }
