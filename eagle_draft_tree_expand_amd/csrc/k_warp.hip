@@ -13,7 +13,7 @@
 //
 // One workgroup of 1024 threads per row.  Each cut is a radix select on the
 // 32-bit key ~code (ascending key = descending t) in three passes over the
-// row (digits of 11, 11 and 10 bits): a 2048-bucket histogram of the weight
+// row (digits of 12, 10 and 10 bits): a 4096- or 1024-bucket histogram of the weight
 // (1 per token for counts, the mass for the nucleus) of the tokens that
 // share the key prefix chosen so far, then the bucket where the running
 // weight reaches the target; a last pass over the tokens equal to the chosen
@@ -39,7 +39,7 @@ struct Cut {
 
 EDEV bool before_eq(uint32_t key, int v, const Cut& c) { return key < c.key || (key == c.key && v <= c.id); }
 
-constexpr int kWBuckets = 2048;
+constexpr int kWBuckets = 4096;
 constexpr int kWList = 64;  // tokens tied at a cut key handled in wave 0
 
 // A top-k cut of at most this many tokens finishes in LDS: the kept tokens
@@ -174,14 +174,14 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
   const int tid = threadIdx.x, lane = tid & 63;
   int bad = 0;
   if (tid == 0) { sm.prefix = 0; sm.below = 0; }
-  // digits: key bits [31:21], [20:10], [9:0]
+  // digits: key bits [31:20], [19:10], [9:0]
   for (int pass = 0; pass < (key_only ? npass : 3); ++pass) {
-    const int shift = pass == 0 ? 21 : pass == 1 ? 10 : 0;
-    const int nb = pass == 2 ? 1024 : 2048;
+    const int shift = pass == 0 ? 20 : pass == 1 ? 10 : 0;
+    const int nb = pass == 0 ? 4096 : 1024;
     for (int x = tid; x < kWBuckets; x += kWThreads) sm.hist[x] = 0;
     __syncthreads();
     const uint32_t pre = sm.prefix;
-    const int hshift = pass == 0 ? 32 : pass == 1 ? 21 : 10;  // bits above this digit must match
+    const int hshift = pass == 0 ? 32 : pass == 1 ? 20 : 10;  // bits above this digit must match
     for (int v0 = 0; v0 < r.V; v0 += kWBatch) {
       float zz[kWE];
       load_batch(r, v0, zz);
@@ -379,8 +379,8 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
     // Usually the first digit suffices: the tokens whose first digit is at or
     // before the crossing one number below + hist[digit], often a few hundred.
     Cut kc = select_cut(r, all, false, (double)top_k, sm, true, 1);
-    const unsigned long long coarse_n = sm.below + sm.hist[kc.key >> 21];
-    uint32_t lim_key = kc.key | 0x1FFFFFu;
+    const unsigned long long coarse_n = sm.below + sm.hist[kc.key >> 20];
+    uint32_t lim_key = kc.key | 0xFFFFFu;
     if (coarse_n > (unsigned long long)kWFast) {
       kc = select_cut(r, all, false, (double)top_k, sm, true, 3);
       lim_key = kc.key;
