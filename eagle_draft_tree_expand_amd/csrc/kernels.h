@@ -114,6 +114,7 @@ inline int lm_ksplit(int rows, int V, int H) {
   if (rows >= kGemmMinRows) return 1;
   int ks = 256 / (lm_ntiles(V) * lm_mtiles(rows));
   if (ks > 32) ks = 32;
+  if (ks > H / 256) ks = H / 256;  // slices of at least 256: two chunks per hidden half to pipeline
   while (ks > 1 && H % (ks * 128) != 0) --ks;
   return ks < 1 ? 1 : ks;
 }
