@@ -34,6 +34,8 @@ def _rows(kind, R, V, rng):
         z = (rng.standard_normal((R, V)) * 0.5).astype(np.float32)
         z[np.arange(R), rng.integers(0, V, R)] += 30.0
         return z
+    if kind == "band":  # one narrow band: the first key digit cannot separate the top tokens
+        return (5.0 + 0.01 * rng.standard_normal((R, V))).astype(np.float32)
     if kind == "neginf":
         z = rng.standard_normal((R, V)).astype(np.float32)
         z[rng.random((R, V)) < 0.3] = -np.inf
@@ -57,7 +59,7 @@ WARPS = [(50, 1.0, 1), (0, 0.9, 1), (40, 0.5, 10), (10, 0.95, 10), (1, 1.0, 1), 
          (2000, 0.99, 1)]
 
 
-@pytest.mark.parametrize("kind", ["normal", "ties", "flat", "peaked", "neginf"])
+@pytest.mark.parametrize("kind", ["normal", "ties", "flat", "peaked", "band", "neginf"])
 @pytest.mark.parametrize("V", [5003, 4096])
 def test_warp_matches_oracle(kind, V):
     rng = np.random.default_rng(hash((kind, V)) % 2**32)
