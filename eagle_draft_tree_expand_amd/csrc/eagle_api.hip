@@ -246,10 +246,12 @@ int eagle_verify_accept_warped(const eagle_tree_params* p, const uint32_t* targe
     return EAGLE_ERR_NULL;
   if (greedy ? !target_argmax : (!target_logits || !target_stats || !draft_logits || !slot_stats || !uniforms))
     return EAGLE_ERR_NULL;
+  // Mailbox b sits at a fixed distance from the 256-byte-aligned end of the
+  // workspace (b + 1 mailboxes back), whatever the batch of this call.
   const size_t mail = accept_mail_bytes(p->batch);
-  if (ws_bytes < kCounterBytes + mail) return EAGLE_ERR_WORKSPACE;
-  void* mailbox = static_cast<char*>(ws) + ((ws_bytes - mail) & ~(size_t)255) - 0;
-  if ((size_t)(static_cast<char*>(mailbox) - static_cast<char*>(ws)) + mail > ws_bytes) return EAGLE_ERR_WORKSPACE;
+  const size_t end = ws_bytes & ~(size_t)255;
+  if (end < kCounterBytes + mail) return EAGLE_ERR_WORKSPACE;
+  void* mailbox = static_cast<char*>(ws) + end;
   return launch_status(launch_accept(p->batch, p->m + 1, p->vocab, p->depth, p->topk, p->temperature, node_tok,
                                      node_parent, node_slot, pool_tok, pool_flat, target_logits, target_stats,
                                      target_argmax, draft_logits, slot_stats, greedy ? nullptr : target_bound,

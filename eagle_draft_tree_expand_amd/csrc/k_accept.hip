@@ -41,6 +41,8 @@
 // and flat indices, row statistics, uniforms) to LDS, so the walk's serial
 // steps read LDS rather than global memory.  Spins are bounded:
 // a timeout sets EAGLE_STATUS_SYNC_TIMEOUT and the walk continues.
+#include <atomic>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -472,7 +474,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     gr.lo = min(V, g * span);
     gr.hi = min(V, gr.lo + span);
     gr.span = span;
-    gr.mb = mail + b;
+    gr.mb = mail - 1 - b;  // `mail` is the end of the mailbox area: request b's is b + 1 back
     gr.epoch = __hip_atomic_load(&gr.mb->epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     gr.step = 0;
     gr.cache = cache_tokens >= span ? tcache : nullptr;
@@ -760,22 +762,26 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
   const bool greedy = !(T > 0.f);
   // Group size: as many workgroups per request as stay co-resident; requests
   // beyond the resident capacity go in further launches.
-  static int capacity[64] = {0};
+  // The capacity is a property of the device and this kernel: computed once
+  // per device and cached in an atomic (concurrent first calls compute the
+  // same value; either store wins).
+  static std::atomic<int> capacity[64];
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= 64) dev = 0;
-  if (capacity[dev] == 0) {
+  int cap = capacity[dev].load(std::memory_order_relaxed);
+  if (cap == 0) {
     int per_cu = 0, cus = 0;
     e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, accept_kernel, kThreads, accept_lds_max());
     if (e != hipSuccess) return e;
     e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
     if (e != hipSuccess) return e;
-    capacity[dev] = per_cu * cus > 0 ? per_cu * cus : 1;
+    cap = per_cu * cus > 0 ? per_cu * cus : 1;
+    capacity[dev].store(cap, std::memory_order_relaxed);
   }
   // A launch covers 8 x ceil(nb / 8) x G blocks (request r on residue r mod 8),
   // at most the resident capacity; requests beyond it go in further launches.
-  const int cap = capacity[dev];
   const int cap_x = cap / 8 > 0 ? cap / 8 : 1;  // resident blocks per residue class
   const int cols = (B + 7) / 8;
   int G = 1;

@@ -203,10 +203,9 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
         if (act == 0ull) continue;
         const int d0 = __builtin_amdgcn_readlane(d, __ffsll((long long)act) - 1);
         if (__ballot(d >= 0 && d != d0) == 0ull) {
-          // counts: the ballot's population; masses: below 2^(mshift + 6) < 2^53 per
-          // wave, so the DPP fp64 sum of the integer weights is exact
-          const unsigned long long tot =
-              mass ? (unsigned long long)wave_sum_d((double)w) : (unsigned long long)__popcll(act);
+          // counts: the ballot's population; masses: an integer sum over the
+          // wave (64-bit shuffles), exact for every vocabulary size
+          const unsigned long long tot = mass ? wave_sum_u64(w) : (unsigned long long)__popcll(act);
           if (lane == __ffsll((long long)act) - 1) atomicAdd(&sm.hist[d0], tot);
         } else if (d >= 0) {
           atomicAdd(&sm.hist[d], w);
@@ -337,7 +336,12 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
     }
     __syncthreads();
   }
-  if (sm.cut.id < 0) {  // rounding guard: the last token with this key
+  // rounding guard: the last token with this key.  The id is read into a
+  // register and the barrier passed before tid 0 may rewrite it, so every wave
+  // takes the same branch.
+  const int cut_id = sm.cut.id;
+  __syncthreads();
+  if (cut_id < 0) {
     if (tid == 0) {
       int last = -1;
       for (int v = r.V - 1; v >= 0 && last < 0; --v) {
@@ -380,6 +384,8 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
     // before the crossing one number below + hist[digit], often a few hundred.
     Cut kc = select_cut(r, all, false, (double)top_k, sm, true, 1);
     const unsigned long long coarse_n = sm.below + sm.hist[kc.key >> 20];
+    // every wave has read sm.below and sm.hist before a second select resets them
+    __syncthreads();
     uint32_t lim_key = kc.key | 0xFFFFFu;
     if (coarse_n > (unsigned long long)kWFast) {
       kc = select_cut(r, all, false, (double)top_k, sm, true, 3);

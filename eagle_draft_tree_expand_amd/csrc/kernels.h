@@ -193,7 +193,9 @@ hipError_t launch_draft_forward(const DraftArgs& a, hipStream_t st);
 
 // ---- acceptance (k_accept.hip) ----
 constexpr int kAccMaxGroup = 64;         // workgroups per request in the cooperative walk
-// Per-request mailbox of the walk (kept at the tail of the workspace).
+// Per-request mailbox of the walk.  Mailbox b sits b + 1 mailboxes before the
+// 256-byte-aligned end of the workspace, a place fixed by the workspace size
+// alone, so calls with different batches on one workspace find the same words.
 struct Mailbox {
   uint64_t bank[2][kAccMaxGroup];
   uint64_t result;

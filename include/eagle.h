@@ -37,11 +37,15 @@
  *     *dev_status (an optional device int32, may be NULL), to be read by the
  *     caller after synchronising.
  *   - Workspace: `ws` is caller-provided device scratch of `ws_bytes` bytes,
- *     sized with eagle_workspace_size(...) for the round it serves.  Before
- *     its first use it must be initialised once with eagle_workspace_init
- *     (the acceptance walk keeps per-request mailboxes at its tail that
- *     persist across calls).  Calls that share one workspace must be ordered
- *     (same stream); calls on different streams need different workspaces.
+ *     sized with eagle_workspace_size(...) for the largest round it serves.
+ *     Before its first use it must be initialised once with
+ *     eagle_workspace_init: the acceptance walk keeps per-request mailboxes
+ *     that persist across calls, mailbox b at b + 1 mailboxes before the
+ *     256-byte-aligned end of the buffer.  Their place depends on ws_bytes
+ *     only, so every call on one buffer must pass the same ws_bytes (after a
+ *     change, initialise again); a smaller batch uses a subset of the same
+ *     mailboxes.  Calls that share one workspace must be ordered (same
+ *     stream); calls on different streams need different workspaces.
  *   - Calls are deterministic: identical inputs give bit-identical outputs.
  *
  * Sources of the method (cited by page title and section):

@@ -71,6 +71,17 @@ def gumbel_keys(z, T, seed, slot, req, round_id):
 
 
 def _rel_gap(a, b):
+    """Relative gap |a - b| / max(|a|, |b|) of two adjacent keys or values.
+
+    Equal keys (infinite ones included) are a tie, gap 0; a finite key beside
+    an infinite one (a token the warp drops sits at -inf) is a decided
+    boundary, gap +inf.  Never NaN.
+    """
+    a, b = float(a), float(b)
+    if a == b:
+        return 0.0
+    if not (np.isfinite(a) and np.isfinite(b)):
+        return float("inf")
     return abs(a - b) / max(abs(a), abs(b), 1e-300)
 
 
