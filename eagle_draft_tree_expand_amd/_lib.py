@@ -25,7 +25,8 @@ EXPORTS = ("eagle_workspace_size", "eagle_workspace_init", "eagle_expand_tree", 
            "eagle_tree_attention", "eagle_lmhead_softmax", "eagle_verify_accept", "eagle_gather_rows",
            "eagle_gather_rows_multi", "eagle_commit_accepted", "eagle_sampling_warp",
            "eagle_expand_tree_warped", "eagle_verify_accept_warped", "eagle_lmhead_packed_bytes",
-           "eagle_lmhead_pack_weight", "eagle_draft_workspace_size", "eagle_draft_forward", "eagle_expand_depth",
+           "eagle_lmhead_pack_weight", "eagle_draft_workspace_size", "eagle_draft_workspace_layout",
+           "eagle_draft_forward", "eagle_expand_depth",
            "eagle_expand_finish", "eagle_error_string", "eagle_abi_version")
 
 
@@ -72,6 +73,7 @@ _SIGS = {
     "eagle_verify_accept_warped": (c_int32, [POINTER(TreeParams), _P, _P] + [_P] * 16 + [_P, c_size_t, _P, _P]),
     "eagle_sampling_warp": (c_int32, [c_int32, c_int32, c_int32, c_float, c_int32, c_float, _P, _P, _P, _P, _P]),
     "eagle_draft_workspace_size": (c_size_t, [POINTER(TreeParams), POINTER(DraftDims)]),
+    "eagle_draft_workspace_layout": (c_int32, [POINTER(TreeParams), POINTER(DraftDims), POINTER(c_size_t), c_int32]),
     "eagle_draft_forward": (c_int32, [POINTER(TreeParams), c_int32, POINTER(DraftDims), POINTER(DraftWeights)] +
                             [_P] * 8 + [_P, c_size_t, _P, _P]),
     "eagle_expand_depth": (c_int32, [POINTER(TreeParams), c_int32] + [_P] * 5 + [_P, c_size_t, _P, _P]),

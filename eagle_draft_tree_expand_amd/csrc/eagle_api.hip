@@ -89,7 +89,7 @@ int check_draft(const eagle_tree_params* p, const eagle_draft_dims* d, DraftLayo
 
 extern "C" {
 
-int32_t eagle_abi_version(void) { return (1 << 16) | 2; }
+int32_t eagle_abi_version(void) { return (1 << 16) | 3; }
 
 const char* eagle_error_string(int32_t code) {
   switch (code) {
@@ -338,6 +338,21 @@ size_t eagle_draft_workspace_size(const eagle_tree_params* p, const eagle_draft_
   DraftLayout lay;
   if (check_draft(p, dims, &lay) != EAGLE_OK) return 0;
   return lay.total;
+}
+
+int eagle_draft_workspace_layout(const eagle_tree_params* p, const eagle_draft_dims* dims, size_t* offsets,
+                                 int32_t n) {
+  DraftLayout lay;
+  int rc = check_draft(p, dims, &lay);
+  if (rc != EAGLE_OK) return rc;
+  if (n < 0) return EAGLE_ERR_SHAPE;
+  if (n > 0 && !offsets) return EAGLE_ERR_NULL;
+  const size_t all[EAGLE_DRAFT_NBUF] = {lay.slot_k, lay.slot_v, lay.slot_feat, lay.slot_mask, lay.idx, lay.x0,
+                                        lay.u,      lay.n1,     lay.qkv,       lay.qc,        lay.og,  lay.h,
+                                        lay.n2,     lay.gu,     lay.mm,        lay.y,         lay.xa};
+  const int w = n < EAGLE_DRAFT_NBUF ? n : EAGLE_DRAFT_NBUF;
+  for (int i = 0; i < w; ++i) offsets[i] = all[i];
+  return w;
 }
 
 int eagle_draft_forward(const eagle_tree_params* p, int32_t depth, const eagle_draft_dims* dims,

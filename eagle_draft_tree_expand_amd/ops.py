@@ -6,6 +6,8 @@ code.  No computation happens here.
 """
 from __future__ import annotations
 
+import ctypes
+
 import torch
 
 from . import _lib
@@ -154,6 +156,20 @@ def draft_weights(embed, fc, qkv, o, gate_up, down, lm_head) -> DraftWeights:
 
 def draft_workspace_size(p: TreeParams, dims: DraftDims) -> int:
     return int(_lib.load().eagle_draft_workspace_size(p, dims))
+
+
+DRAFT_BUFFERS = ("slot_k", "slot_v", "slot_feat", "slot_mask", "idx", "x0", "u", "n1", "qkv", "q", "attn", "h", "n2",
+                 "gu", "m", "y", "a")
+
+
+def draft_workspace_layout(p: TreeParams, dims: DraftDims) -> dict:
+    """Byte offsets of the drafting's intermediates in its workspace, by name."""
+    n = len(DRAFT_BUFFERS)
+    arr = (ctypes.c_size_t * n)()
+    rc = _lib.load().eagle_draft_workspace_layout(p, dims, arr, n)
+    if rc < 0:
+        check("eagle_draft_workspace_layout", rc)
+    return {DRAFT_BUFFERS[i]: int(arr[i]) for i in range(rc)}
 
 
 def draft_forward(p: TreeParams, depth, dims: DraftDims, w: DraftWeights, root_token, root_feat, k_prefix, v_prefix,

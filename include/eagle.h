@@ -427,6 +427,27 @@ typedef struct {
  * the drafted slots) and per-depth scratch; it needs no initialisation. */
 size_t eagle_draft_workspace_size(const eagle_tree_params* p, const eagle_draft_dims* dims);
 
+/* Where the drafting keeps each intermediate of its last eagle_draft_forward
+ * call: byte offsets into the draft workspace, for inspection (staged checks
+ * of one kernel at a time on the values the previous one wrote).  Writes
+ * min(n, EAGLE_DRAFT_NBUF) offsets to `offsets` (host memory) in this order
+ * and returns how many it wrote, or a negative EAGLE_ERR_* code:
+ *   0 slot_k, 1 slot_v [B, S, hkv*dh] bf16 (per-slot keys/values),
+ *   2 slot_feat [B, S, H] bf16 (each drafted slot's head output),
+ *   3 slot_mask [B, S, ceil(S/64)] uint64 (each slot's root path),
+ *   4 idx [R] int32 (b * S + slot of frontier row r; R = B at depth 0, else B*k),
+ *   5 x0 [R, 2H] bf16 = [feature ; embedding],
+ *   6 u [R, H] fp32 = x0 Wfc^T,      7 n1 [R, H] bf16 = rms-normalised u,
+ *   8 (product scratch),             9 q [R, hq*dh] bf16 = n1 Wq^T,
+ *  10 attention output [R, hq*dh] bf16,
+ *  11 h [R, H] fp32 = u + attention Wo^T,   12 n2 [R, H] bf16 = rms(h),
+ *  13 (product scratch),            14 m [R, I] bf16 = silu(n2 Wg^T) * (n2 Wu^T),
+ *  15 (product scratch),            16 a [R, H] bf16 = h + m Wd^T.
+ * The values stay until the next call on the workspace. */
+#define EAGLE_DRAFT_NBUF 17
+int eagle_draft_workspace_layout(const eagle_tree_params* p, const eagle_draft_dims* dims, size_t* offsets,
+                                 int32_t n);
+
 /* The draft head's forward for depth `depth` (0 <= depth < D).
  * In:  root_token [B] int32; root_feat [B, H] bf16 (the feature entering the
  *        root's step); k_prefix, v_prefix [B, hkv, max_prefix, head_dim] bf16

@@ -33,9 +33,13 @@ pytestmark = pytest.mark.gpu
 torch = pytest.importorskip("torch")
 
 # Decision gaps below these are not compared exactly: about twice the largest
-# row error measured (1.3e-2 in logit units; values carry up to D such errors).
+# row error measured (1.3e-2 in logit units); a value at depth d carries d such
+# errors (one per confidence on its path), so its margin is D times the key's.
 KEY_MARGIN = 3e-2      # logit units
-VALUE_MARGIN = 1.2e-1  # relative
+
+
+def value_margin(D):
+    return KEY_MARGIN * D  # relative
 
 
 class _Wts:
@@ -78,10 +82,10 @@ def _margin(out, T, k, D, m, seed, req):
     for d in range(1, D):
         v = np.sort(val[dep == d])[::-1][: k + 1]
         if v.size > 1:
-            gaps.append(float(np.min((v[:-1] - v[1:]) / v[:-1])) / VALUE_MARGIN)
+            gaps.append(float(np.min((v[:-1] - v[1:]) / v[:-1])) / value_margin(D))
     v = np.sort(val)[::-1]
     if m < v.size:
-        gaps.append(float((v[m - 1] - v[m]) / v[m - 1]) / VALUE_MARGIN)
+        gaps.append(float((v[m - 1] - v[m]) / v[m - 1]) / value_margin(D))
     return min(gaps)
 
 
@@ -168,13 +172,19 @@ def _validate(dev, rows, head, f_root, root, T, k, D, m, seed, b):
     return max(rel), max(dz)
 
 
-@pytest.mark.parametrize("T", [1.0, 0.0])
-def test_drafting_matches_oracle(T):
+# The small tree (depth 2, k 2, m = P = 6: no rerank cut) has few decisions,
+# so most of its trees are clear of the row error and are compared bit for bit;
+# the test asserts that some are.  On the larger tree nearly every request has
+# a decision inside the margin (values differ by the rows' small spread), so
+# there the count is reported only.
+@pytest.mark.parametrize("kw,T,min_compared", [({}, 1.0, 0), ({}, 0.0, 0),
+                                               (dict(D=2, k=2, m=6), 1.0, 1), (dict(D=2, k=2, m=6), 0.0, 1)])
+def test_drafting_matches_oracle(kw, T, min_compared):
     """Device drafting: rows and decisions validated on the device's paths; the
     trees compared bit for bit where the oracle's own decisions are clear of
     the row error."""
     from eagle_draft_tree_expand_amd import draft_head
-    cfg = synth.get_config("mid_bf16")
+    cfg = synth.get_config("mid_bf16").with_(**kw)
     compared = total = 0
     worst = worst_abs = 0.0
     for set_idx in range(3):
@@ -199,7 +209,9 @@ def test_drafting_matches_oracle(T):
             compared += 1
             for key in tree_keys():
                 assert np.array_equal(dev[key][b], o[key]), f"set {set_idx} b={b} {key}: {dev[key][b]} vs {o[key]}"
-    print(f"T={T}: {compared}/{total} trees compared exactly, worst row error {worst:.2e} (abs {worst_abs:.2e})")
+    print(f"{kw} T={T}: {compared}/{total} trees compared exactly, worst row error {worst:.2e} "
+          f"(abs {worst_abs:.2e})")
+    assert compared >= min_compared
 
 
 def _slot_path(out, s, root, k):

@@ -273,8 +273,8 @@ def test_pack_layout(rt):
 
 
 @pytest.mark.parametrize("name", ["8b", "13b", "70b"])  # 13b/70b (vocab 32000): hidden split over workgroups
-def test_lmhead_full_sampled(rt, name):
-    """Full-size LM head (8b: 61 x 4096 x 128256): sampled logits, stats invariants."""
+def test_lmhead_full_all_columns(rt, name):
+    """Full-size LM head (8b: 61 x 4096 x 128256): every logit against fp64, stats and argmax."""
     cfg = synth.get_config(name)
     inp = synth.make_inputs(cfg)
     rng = np.random.default_rng(8)
@@ -284,21 +284,22 @@ def test_lmhead_full_sampled(rt, name):
     dr.x.copy_(torch.from_numpy(X).to(dr.x.dtype).view(dr.x.shape))
     dr.lmhead(wts, 1.0)
     dev = dr.host()
-    cols = rng.integers(0, cfg.V, size=400)
-    cols[:3] = [0, cfg.V - 1, cfg.V // 2]
-    ref = X.astype(np.float64) @ inp.w[cols].astype(np.float64).T
-    err = np.abs(dev["logits"][:, cols] - ref).max() / np.abs(ref).max()
+    z64 = olm.logits(X, inp.w)
+    err = rel_err_rows(dev["logits"], z64)
+    print(f"{name}: LM head, all {cfg.N} x {cfg.V} logits, worst row error {err:.2e}")
     assert err <= 1e-5
-    # row statistics are those of the device logits themselves
-    for r in (0, 17, cfg.N - 1):
-        st, am = olm.row_stats(dev["logits"][r:r + 1], 1.0)
-        assert abs(dev["stats"][r, 0] - st[0, 0]) <= 1e-6 * abs(st[0, 0])
-        assert abs(dev["stats"][r, 1] - st[0, 1]) <= 1e-5 * st[0, 1]
-        assert dev["argmax"][r] == am[0]
+    # row statistics and argmax are those of the device logits themselves
+    st, am = olm.row_stats(dev["logits"], 1.0)
+    np.testing.assert_allclose(dev["stats"][:, 0], st[:, 0], rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(dev["stats"][:, 1], st[:, 1], rtol=1e-5)
+    assert np.array_equal(dev["argmax"], am)
+    srt = np.sort(z64, axis=1)
+    clear = (srt[:, -1] - srt[:, -2]) > 1e-5 * np.abs(srt[:, -1]).clip(1e-3)
+    assert np.array_equal(am[clear], np.argmax(z64, axis=1)[clear])
 
 
-def test_lmhead_gemm_b64_sampled(rt):
-    """Batch-64 8B LM head (3904 x 4096 x 128256) on the tiled GEMM: sampled logits and row stats."""
+def test_lmhead_gemm_b64_rows_all_columns(rt):
+    """Batch-64 8B LM head (3904 x 4096 x 128256) on the tiled GEMM: 64 sampled rows, every column."""
     cfg = synth.get_config("8b")
     inp = synth.make_inputs(cfg)
     rng = np.random.default_rng(9)
@@ -309,20 +310,20 @@ def test_lmhead_gemm_b64_sampled(rt):
     dr.x.copy_(torch.from_numpy(X).to(dr.x.dtype).view(dr.x.shape))
     dr.lmhead(wts, 1.0)
     torch.cuda.synchronize()
-    rows = rng.integers(0, B * cfg.N, size=24)
-    rows[:2] = [0, B * cfg.N - 1]
-    cols = rng.integers(0, cfg.V, size=300)
-    cols[:3] = [0, cfg.V - 1, 255]
+    rows = np.sort(rng.choice(B * cfg.N, size=64, replace=False))
+    rows[:2] = [0, B * cfg.N - 1]   # the first and the last (ragged) row tile
+    rows = np.unique(rows)
     lg = dr.logits[torch.from_numpy(rows).cuda()].cpu().numpy()
-    ref = X[rows].astype(np.float64) @ inp.w[cols].astype(np.float64).T
-    assert np.abs(lg[:, cols] - ref).max() / np.abs(ref).max() <= 1e-5
-    stats = dr.stats.cpu().numpy()
-    am = dr.argmax.cpu().numpy()
-    for j, r in enumerate(rows[:6]):
-        st, a = olm.row_stats(lg[j:j + 1], 1.0)
-        assert abs(stats[r, 0] - st[0, 0]) <= 1e-6 * abs(st[0, 0])
-        assert abs(stats[r, 1] - st[0, 1]) <= 1e-5 * st[0, 1]
-        assert am[r] == a[0]
+    z64 = olm.logits(X[rows], inp.w)
+    err = rel_err_rows(lg, z64)
+    print(f"b64 LM head: {rows.size} rows x {cfg.V} columns, worst row error {err:.2e}")
+    assert err <= 1e-5
+    stats = dr.stats.cpu().numpy()[rows]
+    am = dr.argmax.cpu().numpy()[rows]
+    st, a = olm.row_stats(lg, 1.0)
+    np.testing.assert_allclose(stats[:, 0], st[:, 0], rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(stats[:, 1], st[:, 1], rtol=1e-5)
+    assert np.array_equal(am, a)
     assert int(dr.status.item()) == 0
 
 
@@ -401,9 +402,19 @@ def test_round_end_to_end(rt, name, T):
     assert rel_err_rows(dev["logits"], z64) <= 1e-5
     for b in range(cfg.B):
         assert 1 <= dev["n_committed"][b] == dev["accept_len"][b] + 1 <= cfg.D + 1
+    # staged: the oracle's walk on the device's tree, logits and argmax gives the same paths
+    staged = oracle_accept(cfg, {key: dev[key] for key in ("node_tok", "node_parent", "node_slot", "pool_tok",
+                                                              "pool_flat")},
+                           dev["logits"], ora["rows"], T, inp.uniforms, dev["argmax"])
+    flagged = compare_accept(dev, staged, f"e2e staged {name}")
+    # end to end against the oracle's own round: the same paths wherever neither
+    # side's logits put a draw near its boundary (fp32: always; bf16: X is rounded
+    # on each side from slightly different attention sums)
+    agree = sum(int(np.array_equal(dev["committed"][b], a["committed"])) for b, a in enumerate(ora["accept"]))
+    print(f"e2e {name} T={T}: staged walk flagged {flagged}/{cfg.B}; end-to-end paths equal {agree}/{cfg.B}")
+    assert flagged <= max(1, cfg.B // 4)
     if cfg.dtype == "f32":
-        # fp32 end to end: accepted paths agree unless a near tie is flagged
-        compare_accept(dev, ora["accept"], f"e2e {name}")
+        assert compare_accept(dev, ora["accept"], f"e2e {name}") <= max(1, cfg.B // 4)
     assert dev["status"] & ~0x8 == 0
 
 
