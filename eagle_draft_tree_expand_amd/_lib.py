@@ -13,7 +13,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libe
 
 EAGLE_OK = 0
 ERRORS = {-1: "EAGLE_ERR_NULL", -2: "EAGLE_ERR_SHAPE", -3: "EAGLE_ERR_DTYPE",
-          -4: "EAGLE_ERR_WORKSPACE", -5: "EAGLE_ERR_LAUNCH", -6: "EAGLE_ERR_ALIGN"}
+          -4: "EAGLE_ERR_WORKSPACE", -5: "EAGLE_ERR_LAUNCH", -6: "EAGLE_ERR_ALIGN", -7: "EAGLE_ERR_TOO_LARGE"}
 EAGLE_F32, EAGLE_BF16 = 0, 1
 EAGLE_W_ROWMAJOR, EAGLE_W_PACKED = 0, 1
 STATUS_BITS = {0x1: "TOKEN_RANGE", 0x2: "NONFINITE", 0x4: "ZERO_RESIDUAL", 0x8: "TOPK_RESCAN",
@@ -24,7 +24,7 @@ STATUS_BITS = {0x1: "TOKEN_RANGE", 0x2: "NONFINITE", 0x4: "ZERO_RESIDUAL", 0x8: 
 EXPORTS = ("eagle_workspace_size", "eagle_workspace_init", "eagle_expand_tree", "eagle_build_tree_mask",
            "eagle_tree_attention", "eagle_lmhead_softmax", "eagle_verify_accept", "eagle_gather_rows",
            "eagle_gather_rows_multi", "eagle_commit_accepted", "eagle_sampling_warp",
-           "eagle_expand_tree_warped", "eagle_verify_accept_warped", "eagle_lmhead_packed_bytes",
+           "eagle_expand_tree_warped", "eagle_expand_tree_noalloc", "eagle_verify_accept_warped", "eagle_lmhead_packed_bytes",
            "eagle_lmhead_pack_weight", "eagle_draft_workspace_size", "eagle_draft_workspace_layout",
            "eagle_draft_forward", "eagle_expand_depth",
            "eagle_expand_finish", "eagle_error_string", "eagle_abi_version")
@@ -70,6 +70,7 @@ _SIGS = {
     "eagle_commit_accepted": (c_int32, [c_int32] * 8 + [_P] * 9 + [_P, _P]),
     "eagle_expand_tree_warped": (c_int32, [POINTER(TreeParams), _P, _P, _P] + [_P] * 7 + [_P] * 5 +
                                  [_P, c_size_t, _P, _P]),
+    "eagle_expand_tree_noalloc": (c_int32, [POINTER(TreeParams), _P, _P] + [_P] * 7 + [_P] * 5 + [_P, _P]),
     "eagle_verify_accept_warped": (c_int32, [POINTER(TreeParams), _P, _P] + [_P] * 16 + [_P, c_size_t, _P, _P]),
     "eagle_sampling_warp": (c_int32, [c_int32, c_int32, c_int32, c_float, c_int32, c_float, _P, _P, _P, _P, _P]),
     "eagle_draft_workspace_size": (c_size_t, [POINTER(TreeParams), POINTER(DraftDims)]),

@@ -4,12 +4,40 @@
 // caller's stream.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
 using namespace eagle;
 
+// Scratch of eagle_expand_tree_noalloc: one static device array per GPU
+// (64 MiB, held by every GPU the library runs on until the process ends).  In
+// host code `scratch` names a host-side stand-in, not device memory: only the
+// address hipGetSymbolAddress returns for the current device may reach a
+// kernel, a fill or a copy.
+static __device__ __align__(256) unsigned char scratch[EAGLE_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+constexpr size_t kNoAllocScratchBytes = EAGLE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and cached.  Returns null on failure.
+void* noalloc_scratch() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
 
 constexpr size_t kCounterBytes = 64 * 1024;           // ticket counters at the workspace head
 
@@ -100,6 +128,7 @@ const char* eagle_error_string(int32_t code) {
     case EAGLE_ERR_WORKSPACE: return "workspace too small";
     case EAGLE_ERR_LAUNCH: return "kernel launch failed";
     case EAGLE_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case EAGLE_ERR_TOO_LARGE: return "sizes need more than the no-allocation scratch holds";
     default: return "unknown error";
   }
 }
@@ -159,6 +188,30 @@ int eagle_expand_tree_warped(const eagle_tree_params* p, const float* draft_logi
                                      draft_bound, root_token, node_tok, node_parent, node_depth, node_sib, node_slot, node_value,
                                      node_q, pool_tok, pool_q, pool_flat, slot_src, slot_stats, stage_area(ws),
                                      dev_status, (hipStream_t)stream));
+}
+
+int eagle_expand_tree_noalloc(const eagle_tree_params* p, const float* draft_logits, const int32_t* root_token,
+                              int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
+                              int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_tok,
+                              float* pool_q, int32_t* pool_flat, int32_t* slot_src, float* slot_stats,
+                              int32_t* dev_status, void* stream) {
+  int rc = check_tree_params(p);
+  if (rc != EAGLE_OK) return rc;
+  if (!draft_logits || !root_token || !node_tok || !node_parent || !node_depth || !node_sib || !node_slot ||
+      !node_value || !node_q || !pool_tok || !pool_q || !pool_flat || !slot_src || !slot_stats)
+    return EAGLE_ERR_NULL;
+  if (!aligned16(draft_logits)) return EAGLE_ERR_ALIGN;
+  const int B = p->batch, V = p->vocab, k = p->topk, D = p->depth;
+  const int S = 1 + (D - 1) * k;
+  if (exp_ws_bytes(B, S, V, k) > kNoAllocScratchBytes) return EAGLE_ERR_TOO_LARGE;
+  // The candidate records are written by the scan before the merge reads
+  // them, so the array needs no clearing between calls.
+  void* ws = noalloc_scratch();
+  if (!ws) return EAGLE_ERR_LAUNCH;
+  return launch_status(launch_expand(B, S, V, D, k, p->m, p->temperature, p->seed, p->round_id, draft_logits,
+                                     nullptr, root_token, node_tok, node_parent, node_depth, node_sib, node_slot,
+                                     node_value, node_q, pool_tok, pool_q, pool_flat, slot_src, slot_stats,
+                                     static_cast<float*>(ws), dev_status, (hipStream_t)stream));
 }
 
 int eagle_build_tree_mask(int32_t batch, int32_t n, const int32_t* node_parent, const int32_t* node_depth,

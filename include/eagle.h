@@ -79,6 +79,7 @@ extern "C" {
 #define EAGLE_ERR_WORKSPACE -4  /* workspace missing or smaller than required    */
 #define EAGLE_ERR_LAUNCH    -5  /* the HIP runtime refused a launch              */
 #define EAGLE_ERR_ALIGN     -6  /* a tensor pointer is not 16-byte aligned       */
+#define EAGLE_ERR_TOO_LARGE -7  /* sizes beyond the no-allocation scratch limit  */
 
 /* ---- device status bits (OR-ed into *dev_status) ------------------------- */
 #define EAGLE_STATUS_TOKEN_RANGE   0x1  /* an input token id was outside [0, V)          */
@@ -184,6 +185,26 @@ int eagle_expand_tree_warped(const eagle_tree_params* p, const float* draft_logi
                              int32_t* node_depth, int32_t* node_sib, int32_t* node_slot, float* node_value,
                              float* node_q, int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
                              float* slot_stats, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* eagle_expand_tree for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): no `ws` argument; the expansion's candidate records go to a
+ * static device array of EAGLE_NOALLOC_SCRATCH_BYTES (64 MiB) that the library
+ * holds on every GPU it runs on until the process ends.  The call itself
+ * allocates nothing.  Limit: B * S * ceil(V / 4096) * 4 * (2 + 2 (k + 2)) * 4
+ * bytes of records must fit (the 8B shape: 0.95 MB per request, so up to 70
+ * requests); larger sizes return EAGLE_ERR_TOO_LARGE before any launch.
+ * Every call on one GPU shares that GPU's array: calls that overlap on one
+ * GPU (different streams, or host threads without ordering) race and must be
+ * serialised by the caller.  Outputs, status and errors as eagle_expand_tree
+ * (no sampling warp); the results are bit-identical to it. */
+#define EAGLE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int eagle_expand_tree_noalloc(const eagle_tree_params* p, const float* draft_logits,
+                              const int32_t* root_token,
+                              int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
+                              int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
+                              int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                              float* slot_stats, int32_t* dev_status, void* stream);
 
 /* Ancestor-only tree attention mask and positions.
  * Source: [E2] "Tree Attention Mask" (each token sees only its ancestors,
