@@ -65,8 +65,17 @@ def _children(node_parent, u):
 
 
 def candidates(pool_tok, pool_flat, slot, k):
-    """The k sampled children of `slot` in sampling order: (j, token, flat index or -1)."""
-    return [(j, int(pool_tok[slot, j]), int(pool_flat[slot, j])) for j in range(k)]
+    """The sampled children of `slot` in sampling order: (j, token, flat index or -1).
+
+    A dynamic tree's slot has k of them; a static tree's slot has its own
+    count k_s <= k, and its pool row is -1 past them (the list ends there)."""
+    out = []
+    for j in range(k):
+        x = int(pool_tok[slot, j])
+        if x < 0:
+            break
+        out.append((j, x, int(pool_flat[slot, j])))
+    return out
 
 
 def ratio(P, Q, x):

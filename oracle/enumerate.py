@@ -75,6 +75,41 @@ def enumerate_trees(V, k, D, m, root, q_path):
     return out
 
 
+def enumerate_static_trees(V, parent, root, q_path):
+    """All (probability, tree, slot_paths) outcomes of filling a static shape."""
+    from .static_tree import build_static_tree
+    out = []
+
+    def rec(choices):
+        calls = []
+        prob = [1.0]
+        slot_paths = {}
+
+        def children_fn(s, path, kk):
+            q = q_path(tuple(path))
+            i = len(calls)
+            if i >= len(choices):
+                raise _Need((q, kk))
+            toks = choices[i]
+            calls.append(toks)
+            slot_paths[s] = tuple(path)
+            prob[0] *= pl_prob(q, toks)
+            return np.array(toks), np.asarray(q, np.float64)[list(toks)].astype(np.float32)
+
+        try:
+            tree = build_static_tree(parent, root, children_fn)
+        except _Need as e:
+            q, kk = e.args[0]
+            for toks in itertools.permutations(range(V), kk):
+                if pl_prob(q, toks) > 0.0:
+                    rec(choices + [toks])
+            return
+        out.append((prob[0], tree, dict(slot_paths)))
+
+    rec([])
+    return out
+
+
 class _EnumChooser:
     def __init__(self, decisions):
         self.dec = decisions
@@ -138,8 +173,11 @@ def node_paths(tree):
     return paths
 
 
-def round_law(V, k, D, m, root, p_path, q_path, walk_fn=walk):
-    """Joint law of the next D+1 tokens produced by one round plus target sampling."""
+def round_law(V, k, D, m, root, p_path, q_path, walk_fn=walk, static_parent=None):
+    """Joint law of the next D+1 tokens produced by one round plus target sampling.
+
+    static_parent: a static shape (oracle/static_tree.py) instead of the
+    dynamic tree (then k is the shape's largest child count and D its depth)."""
     joint = defaultdict(float)
 
     def extend(seq, w):
@@ -151,7 +189,9 @@ def round_law(V, k, D, m, root, p_path, q_path, walk_fn=walk):
             if p[y] > 0.0:
                 extend(seq + [y], w * p[y])
 
-    for pt, tree, spaths in enumerate_trees(V, k, D, m, root, q_path):
+    trees = (enumerate_trees(V, k, D, m, root, q_path) if static_parent is None
+             else enumerate_static_trees(V, static_parent, root, q_path))
+    for pt, tree, spaths in trees:
         npaths = node_paths(tree)
         for pw, com in enumerate_walk(tree, k, lambda u: p_path(npaths[u]),
                                       lambda s: q_path(spaths[s]), walk_fn):
