@@ -99,9 +99,10 @@ def setup(cfg_name, T, n_sets, device="cuda"):
     inps = [synth.make_inputs(cfg, s) for s in range(n_sets)]
     wts = dround.DeviceWeights(inps[0], device)
     sets = []
+    prepass = dround.device_static_rows if cfg.static_parent else dround.device_draft_rows
     for inp in inps:
         d = dround.DeviceInputs(inp, device, with_eps=True)
-        dround.device_draft_rows(cfg, wts, d, T)
+        prepass(cfg, wts, d, T)
         d.eps = None  # only the rows are needed from here on
         sets.append(d)
     torch.cuda.synchronize()
@@ -394,6 +395,18 @@ def main():
                         "committed_tokens_per_s": round(cr["committed"] / (cr["total_ms"] / 1000.0), 1),
                         "tau_synthetic": round(cr["committed"] / (csteps * ccfg.B), 4)}
         del csets, cwts
+        # EAGLE-1's static tree against a chain with as many draft passes (depth 5 each)
+        for key, name, desc in (("static_tree", "8b_static", "8b shape, static EAGLE-1-style tree (root 4 children, "
+                                 "depth 5, 22 draft nodes, 14 slots)"),
+                                ("chain5", "8b_chain5", "8b shape, chain draft of depth 5 (top-k 1, m 5)")):
+            xcfg, _, xwts, xsets = setup(name, args.temp, 4)
+            xsteps = max(20, args.steps // 4)
+            xr = time_rounds(xcfg, xwts, xsets, args.temp, xsteps, 5)
+            out[key] = {"workload": desc, "trees_per_s": round(1000.0 * xsteps / xr["total_ms"] * xcfg.B, 2),
+                        "committed_tokens_per_s": round(xr["committed"] / (xr["total_ms"] / 1000.0), 1),
+                        "tau_synthetic": round(xr["committed"] / (xsteps * xcfg.B), 4),
+                        "device_status": xr["status"]}
+            del xsets, xwts
     if not args.no_extra and args.config == "8b" and args.temp > 0:
         out["draft"] = time_drafting(cfg, wts, inps[0], args.temp, max(10, args.steps // 10), 3)
         torch.cuda.empty_cache()

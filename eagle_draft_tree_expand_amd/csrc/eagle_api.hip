@@ -89,6 +89,67 @@ int launch_status(hipError_t e) { return e == hipSuccess ? EAGLE_OK : EAGLE_ERR_
 
 float* stage_area(void* ws) { return reinterpret_cast<float*>(static_cast<char*>(ws) + kCounterBytes); }
 
+// A static tree's tables from its parent array (host memory): node 0 is the
+// root (-1), 0 <= parent[i] < i; siblings rank in flat order; slots are the
+// nodes with children, in flat order.
+int static_shape(int32_t n, const int32_t* parent, StaticShape* sh) {
+  if (!parent || !sh) return EAGLE_ERR_NULL;
+  if (n < 2 || n > EAGLE_MAX_NODES) return EAGLE_ERR_SHAPE;
+  if (parent[0] != -1) return EAGLE_ERR_SHAPE;
+  int nchild[EAGLE_MAX_NODES] = {0};
+  sh->n = n;
+  sh->parent[0] = -1;
+  sh->depth[0] = 0;
+  sh->sib[0] = 0;
+  int D = 0;
+  for (int i = 1; i < n; ++i) {
+    const int a = parent[i];
+    if (a < 0 || a >= i) return EAGLE_ERR_SHAPE;
+    const int d = sh->depth[a] + 1;
+    if (d > EAGLE_MAX_DEPTH || nchild[a] >= EAGLE_MAX_TOPK) return EAGLE_ERR_SHAPE;
+    sh->parent[i] = (int16_t)a;
+    sh->depth[i] = (uint8_t)d;
+    sh->sib[i] = (uint8_t)nchild[a]++;
+    D = d > D ? d : D;
+  }
+  int S = 0, kmax = 0;
+  for (int i = 0; i < n; ++i) {
+    sh->slot[i] = -1;
+    if (nchild[i] > 0) {
+      sh->slot[i] = (int16_t)S;
+      sh->slot_node[S] = (int16_t)i;
+      sh->slot_k[S] = (uint8_t)nchild[i];
+      kmax = nchild[i] > kmax ? nchild[i] : kmax;
+      ++S;
+    }
+  }
+  sh->S = S;
+  sh->kmax = kmax;
+  sh->D = D;
+  return EAGLE_OK;
+}
+
+// Round parameters of a static tree (batch, vocabulary, k = the shape's
+// largest child count, depth, m = n - 1, temperature).
+int check_static_params(const eagle_tree_params* p) {
+  if (!p) return EAGLE_ERR_NULL;
+  if (p->batch < 1 || p->batch > (1 << 20)) return EAGLE_ERR_SHAPE;
+  if (p->topk < 1 || p->topk > EAGLE_MAX_TOPK || p->depth < 1 || p->depth > EAGLE_MAX_DEPTH) return EAGLE_ERR_SHAPE;
+  if (p->vocab < p->topk || p->vocab > EAGLE_MAX_VOCAB) return EAGLE_ERR_SHAPE;
+  if (p->m < 1 || p->m + 1 > EAGLE_MAX_NODES) return EAGLE_ERR_SHAPE;
+  if (!(p->temperature >= 0.f) || !isfinite(p->temperature)) return EAGLE_ERR_SHAPE;
+  return EAGLE_OK;
+}
+
+int check_static(const eagle_tree_params* p, int32_t n, const int32_t* parent, StaticShape* sh) {
+  int rc = check_static_params(p);
+  if (rc != EAGLE_OK) return rc;
+  rc = static_shape(n, parent, sh);
+  if (rc != EAGLE_OK) return rc;
+  if (p->m != n - 1 || p->topk != sh->kmax || p->depth != sh->D) return EAGLE_ERR_SHAPE;
+  return EAGLE_OK;
+}
+
 // Shape checks of the draft head; fills the layout on success.
 int check_draft(const eagle_tree_params* p, const eagle_draft_dims* d, DraftLayout* lay) {
   int rc = check_tree_params(p);
@@ -214,6 +275,86 @@ int eagle_expand_tree_noalloc(const eagle_tree_params* p, const float* draft_log
                                      static_cast<float*>(ws), dev_status, (hipStream_t)stream));
 }
 
+int eagle_static_tree_info(int32_t n, const int32_t* shape_parent, int32_t* n_slots, int32_t* depth, int32_t* kmax,
+                           int32_t* slot_k) {
+  StaticShape sh;
+  const int rc = static_shape(n, shape_parent, &sh);
+  if (rc != EAGLE_OK) return rc;
+  if (n_slots) *n_slots = sh.S;
+  if (depth) *depth = sh.D;
+  if (kmax) *kmax = sh.kmax;
+  if (slot_k)
+    for (int s = 0; s < sh.S; ++s) slot_k[s] = sh.slot_k[s];
+  return EAGLE_OK;
+}
+
+size_t eagle_static_workspace_size(const eagle_tree_params* p, int32_t n, const int32_t* shape_parent, int32_t hq,
+                                   int32_t hkv, int32_t head_dim, int32_t max_prefix, int32_t hidden) {
+  StaticShape sh;
+  if (check_static(p, n, shape_parent, &sh) != EAGLE_OK) return 0;
+  const int B = p->batch, V = p->vocab;
+  size_t need = exp_ws_bytes(B, sh.S, V, sh.kmax);
+  if (hq > 0 && hkv > 0 && head_dim > 0) {
+    const int dt = head_dim == 64 || head_dim == 128 ? EAGLE_BF16 : EAGLE_F32;
+    if (check_attn(B, n, hq, hkv, head_dim, max_prefix, dt) != EAGLE_OK) return 0;
+    const AttnPlan pl = attn_plan(B, n, hq, hkv, head_dim, max_prefix, dt);
+    const size_t a = attn_ws_bytes(B, hkv, head_dim, pl);
+    if (a > need) need = a;
+  }
+  if (hidden > 0) {
+    const size_t l = lm_ws_bytes(B * n, V, hidden);
+    if (l > need) need = l;
+  }
+  need = (need + 255) / 256 * 256;
+  return (kCounterBytes + need + accept_mail_bytes(B) + 255) / 256 * 256;
+}
+
+int eagle_expand_static(const eagle_tree_params* p, int32_t n, const int32_t* shape_parent,
+                        const float* draft_logits, const int32_t* root_token, int32_t* node_tok, int32_t* node_parent,
+                        int32_t* node_depth, int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
+                        int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src, float* slot_stats,
+                        void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  StaticShape sh;
+  int rc = check_static(p, n, shape_parent, &sh);
+  if (rc != EAGLE_OK) return rc;
+  if (!draft_logits || !root_token || !node_tok || !node_parent || !node_depth || !node_sib || !node_slot ||
+      !node_value || !node_q || !pool_tok || !pool_q || !pool_flat || !slot_src || !slot_stats || !ws)
+    return EAGLE_ERR_NULL;
+  if (!aligned16(draft_logits)) return EAGLE_ERR_ALIGN;
+  if (ws_bytes < kCounterBytes + exp_ws_bytes(p->batch, sh.S, p->vocab, sh.kmax)) return EAGLE_ERR_WORKSPACE;
+  return launch_status(launch_expand_static(p->batch, p->vocab, sh, p->temperature, p->seed, p->round_id,
+                                            draft_logits, root_token, node_tok, node_parent, node_depth, node_sib,
+                                            node_slot, node_value, node_q, pool_tok, pool_q, pool_flat, slot_src,
+                                            slot_stats, stage_area(ws), dev_status, (hipStream_t)stream));
+}
+
+int eagle_verify_accept_static(const eagle_tree_params* p, int32_t n_slots, const int32_t* node_tok,
+                               const int32_t* node_parent, const int32_t* node_slot, const int32_t* pool_tok,
+                               const int32_t* pool_flat, const float* target_logits, const float* target_stats,
+                               const int32_t* target_argmax, const float* draft_logits, const float* slot_stats,
+                               const float* uniforms, int32_t* accept_len, int32_t* accept_path, int32_t* committed,
+                               int32_t* n_committed, int32_t* near_tie, void* ws, size_t ws_bytes,
+                               int32_t* dev_status, void* stream) {
+  int rc = check_static_params(p);
+  if (rc != EAGLE_OK) return rc;
+  if (n_slots < 1 || n_slots > p->m + 1) return EAGLE_ERR_SHAPE;
+  const bool greedy = !(p->temperature > 0.f);
+  if (!node_tok || !node_parent || !node_slot || !pool_tok || !pool_flat || !accept_len || !accept_path ||
+      !committed || !n_committed || !near_tie || !ws)
+    return EAGLE_ERR_NULL;
+  if (greedy ? !target_argmax : (!target_logits || !target_stats || !draft_logits || !slot_stats || !uniforms))
+    return EAGLE_ERR_NULL;
+  const size_t mail = accept_mail_bytes(p->batch);
+  const size_t end = ws_bytes & ~(size_t)255;
+  if (end < kCounterBytes + mail) return EAGLE_ERR_WORKSPACE;
+  void* mailbox = static_cast<char*>(ws) + end;
+  return launch_status(launch_accept(p->batch, p->m + 1, p->vocab, p->depth, p->topk, n_slots, p->temperature,
+                                     node_tok, node_parent, node_slot, pool_tok, pool_flat, target_logits,
+                                     target_stats, target_argmax, draft_logits, slot_stats, nullptr, nullptr, uniforms,
+                                     mailbox, accept_len, accept_path, committed, n_committed, near_tie, dev_status,
+                                     (hipStream_t)stream));
+}
+
 int eagle_build_tree_mask(int32_t batch, int32_t n, const int32_t* node_parent, const int32_t* node_depth,
                           const int32_t* prefix_len, uint64_t* mask, int32_t* pos, int32_t* dev_status,
                           void* stream) {
@@ -305,7 +446,8 @@ int eagle_verify_accept_warped(const eagle_tree_params* p, const uint32_t* targe
   const size_t end = ws_bytes & ~(size_t)255;
   if (end < kCounterBytes + mail) return EAGLE_ERR_WORKSPACE;
   void* mailbox = static_cast<char*>(ws) + end;
-  return launch_status(launch_accept(p->batch, p->m + 1, p->vocab, p->depth, p->topk, p->temperature, node_tok,
+  return launch_status(launch_accept(p->batch, p->m + 1, p->vocab, p->depth, p->topk,
+                                     1 + (p->depth - 1) * p->topk, p->temperature, node_tok,
                                      node_parent, node_slot, pool_tok, pool_flat, target_logits, target_stats,
                                      target_argmax, draft_logits, slot_stats, greedy ? nullptr : target_bound,
                                      greedy ? nullptr : draft_bound, uniforms, mailbox, accept_len,

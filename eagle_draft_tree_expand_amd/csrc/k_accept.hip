@@ -419,7 +419,8 @@ EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr,
 }
 
 __global__ __launch_bounds__(kThreads) void accept_kernel(
-    int b0, int nb, int G, int N, int V, int D, int k, float T, int cache_tokens, const int32_t* __restrict__ node_tok,
+    int b0, int nb, int G, int N, int V, int D, int k, int S, float T, int cache_tokens,
+    const int32_t* __restrict__ node_tok,
     const int32_t* __restrict__ node_parent, const int32_t* __restrict__ node_slot, const int32_t* __restrict__ pool_tok,
     const int32_t* __restrict__ pool_flat, const float* __restrict__ tlog, const float* __restrict__ tstats,
     const int32_t* __restrict__ targmax, const float* __restrict__ dlog, const float* __restrict__ sstats,
@@ -444,7 +445,6 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
   const int r = xr + 8 * (xj / G), g = xj % G, tid = threadIdx.x;
   if (r >= nb) return;  // padding block of the last XCD column
   const int b = b0 + r;
-  const int S = 1 + (D - 1) * k;
   const bool greedy = !(T > 0.f);
   const float Tp = greedy ? 1.f : T;
   const int32_t* ntok = node_tok + (size_t)b * N;
@@ -541,7 +541,17 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       R.Mq = 0.f;
       R.invSq = 0.0;
       const float* Uu = m_U + u * (k + 1);
-      if (slot < 0 || slot >= S) {
+      // The slot's candidates: its pool row up to the first -1 (a static
+      // tree's slot may have fewer than k draws; a dynamic tree's has k).
+      int kk = k;
+      if (slot >= 0 && slot < S) {
+        uint32_t none = 0;
+#pragma unroll
+        for (int j = 0; j < EAGLE_MAX_TOPK; ++j)
+          if (j < k && m_ptok[slot * k + j] < 0) none |= 1u << j;
+        kk = none ? __builtin_ctz(none) : k;
+      }
+      if (slot < 0 || slot >= S || kk == 0) {
         // never expanded: bonus token from the target
         gr.cstate = 0;
         group_reduce(R, 0.0, gr, sm, &timed_out);
@@ -652,7 +662,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       // Rejections: one vocabulary reduction each.  After rejecting trial j
       // at s_{j+1}: Z_{j+1} = G(s_{j+1}) corrected for the tokens tried before
       // j, f_j frozen, then trial j + 1 is decided in the same wave-0 pass.
-      while (acc_j < 0 && cur_j < k - 1) {
+      while (acc_j < 0 && cur_j < kk - 1) {
         const int j = cur_j;
         const double snew = st_s;
         local_partial(R, snew, gr, sm);
@@ -694,11 +704,11 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
         if (!follow) break;
         continue;
       }
-      // all k rejected: the last rejection (trial k - 1) still needs its
-      // reduction, then the draw from the residual at s_k (redone at the
+      // all kk rejected: the last rejection (trial kk - 1) still needs its
+      // reduction, then the draw from the residual at s_kk (redone at the
       // kept s when that reduction found no residual mass)
       {
-        const int j = k - 1;
+        const int j = kk - 1;
         const double snew = st_s;
         local_partial(R, snew, gr, sm);
         lds_barrier();
@@ -721,7 +731,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       }
       const double s_fin = st_s;
       if (stale) group_reduce(R, s_fin, gr, sm, &timed_out);
-      const int y = group_draw(R, s_fin, k, (double)Uu[k], gr, sm, V, &ties, &timed_out);
+      const int y = group_draw(R, s_fin, kk, (double)Uu[k], gr, sm, V, &ties, &timed_out);
       if (g == 0 && tid == 0) comm[ncomm++] = y;
       break;
     }
@@ -744,15 +754,16 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
 }
 
 // Largest dynamic LDS of one workgroup: a full token cache plus the metadata
-// of the largest tree (N = 256 nodes, pool 4096, 241 slots, k = 16).
+// of the largest tree (N = 256 nodes, pool 4096, at most 256 slots, k = 16).
 size_t accept_lds_max() {
   return (size_t)kCacheMax * sizeof(float2) +
-         (size_t)(3 * EAGLE_MAX_NODES + 2 * EAGLE_MAX_POOL + 2 * 241 + EAGLE_MAX_NODES * (EAGLE_MAX_TOPK + 1)) * 4;
+         (size_t)(3 * EAGLE_MAX_NODES + 2 * EAGLE_MAX_POOL + 2 * EAGLE_MAX_NODES +
+                  EAGLE_MAX_NODES * (EAGLE_MAX_TOPK + 1)) * 4;
 }
 
 }  // namespace
 
-hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32_t* node_tok,
+hipError_t launch_accept(int B, int N, int V, int D, int k, int S, float T, const int32_t* node_tok,
                          const int32_t* node_parent, const int32_t* node_slot, const int32_t* pool_tok,
                          const int32_t* pool_flat, const float* tlog, const float* tstats, const int32_t* targmax,
                          const float* dlog, const float* sstats, const uint32_t* tbound, const uint32_t* dbound,
@@ -791,13 +802,12 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32
   // token cache: the slice's exponential terms stay in LDS across the passes at a node
   const int span = ((V + G - 1) / G + 3) / 4 * 4;
   int cache_tokens = (!greedy && span <= kCacheMax) ? span : 0;
-  const int S = 1 + (D - 1) * k;
   const size_t meta = greedy ? 0 : (size_t)(3 * N + 2 * S * k + 2 * S + N * (k + 1)) * 4;
   const size_t lds = (size_t)cache_tokens * sizeof(float2) + meta;
   Mailbox* mb = static_cast<Mailbox*>(mail);
   for (int b0 = 0; b0 < B; b0 += per_launch) {
     const int nb = B - b0 < per_launch ? B - b0 : per_launch;
-    accept_kernel<<<dim3(8 * ((nb + 7) / 8) * G), dim3(kThreads), lds, st>>>(b0, nb, G, N, V, D, k, T, cache_tokens,
+    accept_kernel<<<dim3(8 * ((nb + 7) / 8) * G), dim3(kThreads), lds, st>>>(b0, nb, G, N, V, D, k, S, T, cache_tokens,
         node_tok, node_parent,
         node_slot, pool_tok, pool_flat, tlog, tstats, targmax, dlog, sstats, tbound, dbound, uniforms, mb, accept_len,
         accept_path,

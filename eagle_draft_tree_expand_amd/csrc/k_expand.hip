@@ -722,6 +722,71 @@ hipError_t launch_children(int B, int S, int V, int k, float T, uint64_t seed, u
   return hipGetLastError();
 }
 
+// Static tree: one workgroup per request, one thread per node of the shape.
+// Node c > 0 is child sib[c] of its parent's slot: its token and confidence
+// are that pool entry's, its value the fp32 product of the confidences on its
+// root path, multiplied from the root down.  Pool entries past a slot's own
+// child count are no draws (-1, q 0); pool_flat maps each drawn child to its
+// node.
+constexpr int kStaticThreads = 256;
+__global__ __launch_bounds__(kStaticThreads) void static_assemble_kernel(
+    StaticShape sh, int k, int V, const int32_t* __restrict__ root_token, int32_t* __restrict__ pool_tok,
+    float* __restrict__ pool_q, int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
+    int32_t* node_slot, float* node_value, float* node_q, int32_t* __restrict__ pool_flat,
+    int32_t* __restrict__ slot_src, int32_t* status) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int n = sh.n, S = sh.S;
+  const size_t P = (size_t)S * k;
+  // entries that are no draws: pool rows past the slot's count (disjoint from
+  // the entries the nodes below read and map)
+  for (int e = tid; e < S * k; e += kStaticThreads) {
+    const int s = e / k, j = e - s * k;
+    if (j >= sh.slot_k[s]) {
+      pool_tok[b * P + e] = -1;
+      pool_q[b * P + e] = 0.f;
+      pool_flat[b * P + e] = -1;
+    }
+  }
+  for (int s = tid; s < S; s += kStaticThreads) {
+    const int u = sh.slot_node[s];
+    slot_src[(size_t)b * S + s] = u == 0 ? -1 : sh.slot[sh.parent[u]] * k + sh.sib[u];
+  }
+  const int c = tid;
+  if (c >= n) return;
+  const size_t o = (size_t)b * n + c;
+  if (c == 0) {
+    const int rt = root_token[b];
+    if (rt < 0 || rt >= V) set_status(status, EAGLE_STATUS_TOKEN_RANGE);
+    node_tok[o] = rt;
+    node_parent[o] = -1;
+    node_depth[o] = 0;
+    node_sib[o] = -1;
+    node_slot[o] = sh.slot[0];
+    node_value[o] = 1.f;
+    node_q[o] = 1.f;
+    return;
+  }
+  const int par = sh.parent[c];
+  const size_t e = (size_t)sh.slot[par] * k + sh.sib[c];
+  const int tok = pool_tok[b * P + e];
+  if (tok < 0 || tok >= V) set_status(status, EAGLE_STATUS_TOKEN_RANGE);
+  // confidences of the path, deepest first, then multiplied from the root down
+  float qs[EAGLE_MAX_DEPTH];
+  int nq = 0;
+  for (int a = c; a > 0 && nq < EAGLE_MAX_DEPTH; a = sh.parent[a])
+    qs[nq++] = pool_q[b * P + (size_t)sh.slot[sh.parent[a]] * k + sh.sib[a]];
+  float v = 1.f;
+  for (int i = nq - 1; i >= 0; --i) v = v * qs[i];
+  node_tok[o] = tok;
+  node_parent[o] = par;
+  node_depth[o] = sh.depth[c];
+  node_sib[o] = sh.sib[c];
+  node_slot[o] = sh.slot[c];
+  node_value[o] = v;
+  node_q[o] = qs[0];
+  pool_flat[b * P + e] = c;
+}
+
 hipError_t launch_assemble(int B, int S, int V, int D, int k, int m, int upto, const int32_t* root,
                            int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
                            int32_t* node_slot, float* node_value, float* node_q, const int32_t* pool_tok,
@@ -762,6 +827,21 @@ hipError_t launch_expand_depth(int B, int S, int V, int D, int k, int m, float T
   // the next depth's frontier (slot_src of its slots); no node is written
   return launch_assemble(B, S, V, D, k, m, depth + 1, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
                          nullptr, pool_tok, pool_q, nullptr, slot_src, status, st);
+}
+
+hipError_t launch_expand_static(int B, int V, const StaticShape& sh, float T, uint64_t seed, uint64_t round_id,
+                                const float* rows, const int32_t* root, int32_t* node_tok, int32_t* node_parent,
+                                int32_t* node_depth, int32_t* node_sib, int32_t* node_slot, float* node_value,
+                                float* node_q, int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                                float* slot_stats, float* ws_units, int32_t* status, hipStream_t st) {
+  const int S = sh.S, k = sh.kmax;
+  hipError_t e = launch_children(B, S, V, k, T, seed, round_id, rows, nullptr, pool_tok, pool_q, slot_stats, ws_units,
+                                 status, SlotRange{0, S}, st);
+  if (e != hipSuccess) return e;
+  static_assemble_kernel<<<B, kStaticThreads, 0, st>>>(sh, k, V, root, pool_tok, pool_q, node_tok, node_parent,
+                                                       node_depth, node_sib, node_slot, node_value, node_q, pool_flat,
+                                                       slot_src, status);
+  return hipGetLastError();
 }
 
 hipError_t launch_expand_finish(int B, int S, int V, int D, int k, int m, const int32_t* root, int32_t* node_tok,

@@ -40,6 +40,25 @@ hipError_t launch_expand_finish(int B, int S, int V, int D, int k, int m, const 
                                 float* node_value, float* node_q, const int32_t* pool_tok, const float* pool_q,
                                 int32_t* pool_flat, int32_t* slot_src, int32_t* status, hipStream_t st);
 
+// Static (caller-given) tree shape, derived on the host from its parent array
+// and passed to the assembly kernel by value (node tables of at most
+// EAGLE_MAX_NODES entries).
+struct StaticShape {
+  int n, S, kmax, D;
+  int16_t parent[EAGLE_MAX_NODES];     // -1 for the root
+  int16_t slot[EAGLE_MAX_NODES];       // slot of node i, -1 without children
+  int16_t slot_node[EAGLE_MAX_NODES];  // node of slot s
+  uint8_t sib[EAGLE_MAX_NODES];        // rank among its parent's children
+  uint8_t depth[EAGLE_MAX_NODES];
+  uint8_t slot_k[EAGLE_MAX_NODES];     // children of slot s
+};
+// Children of every slot (top-kmax per row), then the nodes of the shape.
+hipError_t launch_expand_static(int B, int V, const StaticShape& sh, float T, uint64_t seed, uint64_t round_id,
+                                const float* rows, const int32_t* root, int32_t* node_tok, int32_t* node_parent,
+                                int32_t* node_depth, int32_t* node_sib, int32_t* node_slot, float* node_value,
+                                float* node_q, int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                                float* slot_stats, float* ws_units, int32_t* status, hipStream_t st);
+
 // ---- mask + gather (k_mask.hip) ----
 hipError_t launch_tree_mask(int B, int n, const int32_t* parent, const int32_t* depth,
                             const int32_t* prefix_len, uint64_t* mask, int32_t* pos,
@@ -203,7 +222,7 @@ struct Mailbox {
   uint32_t pad[13];
 };
 inline size_t accept_mail_bytes(int B) { return (size_t)B * sizeof(Mailbox); }
-hipError_t launch_accept(int B, int N, int V, int D, int k, float T, const int32_t* node_tok,
+hipError_t launch_accept(int B, int N, int V, int D, int k, int S, float T, const int32_t* node_tok,
                          const int32_t* node_parent, const int32_t* node_slot,
                          const int32_t* pool_tok, const int32_t* pool_flat, const float* tlog,
                          const float* tstats, const int32_t* targmax, const float* dlog,

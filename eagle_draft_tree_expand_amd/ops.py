@@ -119,6 +119,50 @@ def verify_accept(p: TreeParams, tree, target_logits, target_stats, target_argma
     check("eagle_verify_accept", rc)
 
 
+def _shape_arg(shape_parent):
+    arr = (ctypes.c_int32 * len(shape_parent))(*[int(x) for x in shape_parent])
+    return arr
+
+
+def static_tree_info(shape_parent):
+    """(n_slots, depth, kmax, slot_k list) of a static shape (parent array, host)."""
+    n = len(shape_parent)
+    arr = _shape_arg(shape_parent)
+    ns, d, km = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    sk = (ctypes.c_int32 * n)()
+    rc = _lib.load().eagle_static_tree_info(n, arr, ctypes.byref(ns), ctypes.byref(d), ctypes.byref(km), sk)
+    check("eagle_static_tree_info", rc)
+    return ns.value, d.value, km.value, [sk[i] for i in range(ns.value)]
+
+
+def static_workspace_size(p: TreeParams, shape_parent, hq=0, hkv=0, head_dim=0, max_prefix=0, hidden=0) -> int:
+    return int(_lib.load().eagle_static_workspace_size(p, len(shape_parent), _shape_arg(shape_parent), hq, hkv,
+                                                       head_dim, max_prefix, hidden))
+
+
+def expand_static(p: TreeParams, shape_parent, draft_logits, root_token, out, ws, status=None):
+    """A static shape filled for every request (out: the same dict as expand_tree's)."""
+    assert draft_logits.dtype == torch.float32 and draft_logits.is_contiguous()
+    rc = _lib.load().eagle_expand_static(
+        p, len(shape_parent), _shape_arg(shape_parent), _ptr(draft_logits), _ptr(root_token),
+        _ptr(out["node_tok"]), _ptr(out["node_parent"]), _ptr(out["node_depth"]), _ptr(out["node_sib"]),
+        _ptr(out["node_slot"]), _ptr(out["node_value"]), _ptr(out["node_q"]),
+        _ptr(out["pool_tok"]), _ptr(out["pool_q"]), _ptr(out["pool_flat"]), _ptr(out["slot_src"]),
+        _ptr(out["slot_stats"]), _ptr(ws), ws.numel(), _ptr(status), _stream())
+    check("eagle_expand_static", rc)
+
+
+def verify_accept_static(p: TreeParams, n_slots, tree, target_logits, target_stats, target_argmax, draft_logits,
+                         slot_stats, uniforms, out, ws, status=None):
+    rc = _lib.load().eagle_verify_accept_static(
+        p, int(n_slots), _ptr(tree["node_tok"]), _ptr(tree["node_parent"]), _ptr(tree["node_slot"]),
+        _ptr(tree["pool_tok"]), _ptr(tree["pool_flat"]), _ptr(target_logits), _ptr(target_stats),
+        _ptr(target_argmax), _ptr(draft_logits), _ptr(slot_stats), _ptr(uniforms), _ptr(out["accept_len"]),
+        _ptr(out["accept_path"]), _ptr(out["committed"]), _ptr(out["n_committed"]), _ptr(out["near_tie"]), _ptr(ws),
+        ws.numel(), _ptr(status), _stream())
+    check("eagle_verify_accept_static", rc)
+
+
 def gather_rows(n_rows, row_elems, table, idx, out, status=None):
     dt = _DT[table.dtype]
     rc = _lib.load().eagle_gather_rows(n_rows, row_elems, dt, _ptr(table), table.shape[0], _ptr(idx), _ptr(out),

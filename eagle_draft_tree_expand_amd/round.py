@@ -117,8 +117,13 @@ class DeviceRound:
                     "n_committed": z(B), "near_tie": z(B)}
         self.status = z(1)
         self.scale = float(np.float32(1.0 / math.sqrt(c.dh)))
-        p = self.params(1.0, m=min(max(self.N - 1, 1), c.P))  # sizing only: at least one draft node
-        nbytes = ops.workspace_size(p, c.hq, c.hkv, c.dh, self.cap, c.H)
+        self.static = tuple(c.static_parent) if c.static_parent else None
+        if self.static:
+            p = self.params(1.0)
+            nbytes = ops.static_workspace_size(p, self.static, c.hq, c.hkv, c.dh, self.cap, c.H)
+        else:
+            p = self.params(1.0, m=min(max(self.N - 1, 1), c.P))  # sizing only: at least one draft node
+            nbytes = ops.workspace_size(p, c.hq, c.hkv, c.dh, self.cap, c.H)
         if nbytes == 0:
             raise ValueError("invalid round shape")
         self.ws = ops.new_workspace(nbytes, device)
@@ -131,6 +136,12 @@ class DeviceRound:
     def expand(self, data, T, round_id=0, warp=None):
         """warp = (top_k, top_p) with T > 0: the draft rows are warped first (at least k tokens kept)."""
         c = self.cfg
+        if self.static:
+            if warp is not None:
+                raise ValueError("static trees take no sampling warp")
+            ops.expand_static(self.params(T, round_id, data.seed), self.static, data.rows, data.roots, self.tree,
+                              self.ws, self.status)
+            return
         bound = None
         if warp is not None and T > 0:
             ops.sampling_warp(self.B * c.S, c.V, warp[0], warp[1], c.k, T, data.rows, self.d_wstats, self.d_bound,
@@ -164,6 +175,11 @@ class DeviceRound:
         """warp = (top_k, top_p) with T > 0: the target rows are warped first, the draft rows were
         warped by expand (their bounds are reused)."""
         c = self.cfg
+        if self.static:
+            ops.verify_accept_static(self.params(T, round_id, data.seed), c.S, self.tree, self.logits, self.stats,
+                                     self.argmax, data.rows, self.tree["slot_stats"], data.uniforms, self.acc,
+                                     self.ws, self.status)
+            return
         if warp is not None and T > 0:
             ops.sampling_warp(self.B * self.N, c.V, warp[0], warp[1], c.k, T, self.logits, self.t_wstats,
                               self.t_bound, self.status)
@@ -248,33 +264,75 @@ def device_draft_rows(cfg, wts, data, T, round_id=0, device="cuda"):
                         e = int(slot_src[b, e // c.k]) if e // c.k > 0 else -1
                     pb.append([int(data.roots[b].item())] + toks[::-1])
                 paths.append(pb)
-        # mini tree per request: root + one chain per frontier node (no sharing)
-        nf = len(slots)
-        n = 1 + nf * d
-        tok = np.zeros((c.B, n), np.int32)
-        par = np.full((c.B, n), -1, np.int32)
-        dep = np.zeros((c.B, n), np.int32)
-        ends = []
+        _rows_on_paths(c, wts, data, slots, paths, T, d, sig, device)
+    torch.cuda.synchronize()
+
+
+def _rows_on_paths(c, wts, data, slots, paths, T, d, sig, device):
+    """data.rows[:, s] = target logits at the end of paths[b][i] (length d + 1) + sigma_b * eps[:, s]
+    for slots[i]: one mini tree per request, the root plus one chain per path (no sharing)."""
+    nf = len(slots)
+    n = 1 + nf * d
+    tok = np.zeros((c.B, n), np.int32)
+    par = np.full((c.B, n), -1, np.int32)
+    dep = np.zeros((c.B, n), np.int32)
+    ends = []
+    for i in range(nf):
+        for t in range(d):
+            j = 1 + i * d + t
+            par[:, j] = 0 if t == 0 else j - 1
+            dep[:, j] = t + 1
+        ends.append(1 + i * d + d - 1 if d > 0 else 0)
+    for b in range(c.B):
+        tok[b, 0] = paths[b][0][0]
         for i in range(nf):
             for t in range(d):
-                j = 1 + i * d + t
-                par[:, j] = 0 if t == 0 else j - 1
-                dep[:, j] = t + 1
-            ends.append(1 + i * d + d - 1 if d > 0 else 0)
+                tok[b, 1 + i * d + t] = paths[b][i][t + 1]
+    # the mini trees are plain flattened trees (no static shape)
+    mini = DeviceRound(c.with_(static_parent=(), static_slots=0), device, n=n)
+    mini.tree["node_parent"].copy_(torch.from_numpy(par))
+    mini.tree["node_depth"].copy_(torch.from_numpy(dep))
+    mini.tree["node_tok"].copy_(torch.from_numpy(tok))
+    mini.mask_pos(data)
+    mini.gather_qkv(wts)
+    mini.attention(data)
+    mini.lmhead(wts, T)
+    z = mini.logits.view(c.B, n, c.V)
+    for i, s in enumerate(slots):
+        data.rows[:, s] = z[:, ends[i]] + sig * data.eps[:, s]
+
+
+def device_static_rows(cfg, wts, data, T, round_id=0, device="cuda"):
+    """device_draft_rows for a static shape: the rows of the slots at depth d
+    are the target logits on their nodes' root paths (plus noise), once the
+    slots above have drawn the tokens of those paths."""
+    c = cfg
+    if data.eps is None:
+        raise ValueError("input set was created without noise")
+    par = list(c.static_parent)
+    n = len(par)
+    depth = [0] * n
+    for i in range(1, n):
+        depth[i] = depth[par[i]] + 1
+    slot_node = [i for i in range(n) if any(par[j] == i for j in range(i + 1, n))]
+    sig = torch.from_numpy(np.asarray(data.sigma, np.float32)).to(device).view(c.B, 1)
+    data.rows.zero_()
+    rnd = DeviceRound(c, device)
+    for d in range(c.D):
+        slots = [s for s, u in enumerate(slot_node) if depth[u] == d]
+        if not slots:
+            continue
+        rnd.expand(data, T, round_id)
+        tok = rnd.tree["node_tok"].cpu().numpy()
+        paths = []
         for b in range(c.B):
-            tok[b, 0] = paths[b][0][0]
-            for i in range(nf):
-                for t in range(d):
-                    tok[b, 1 + i * d + t] = paths[b][i][t + 1]
-        mini = DeviceRound(c, device, n=n)
-        mini.tree["node_parent"].copy_(torch.from_numpy(par))
-        mini.tree["node_depth"].copy_(torch.from_numpy(dep))
-        mini.tree["node_tok"].copy_(torch.from_numpy(tok))
-        mini.mask_pos(data)
-        mini.gather_qkv(wts)
-        mini.attention(data)
-        mini.lmhead(wts, T)
-        z = mini.logits.view(c.B, n, c.V)
-        for i, s in enumerate(slots):
-            data.rows[:, s] = z[:, ends[i]] + sig * data.eps[:, s]
+            pb = []
+            for s in slots:
+                u, seq = slot_node[s], []
+                while u >= 0:
+                    seq.append(int(tok[b, u]))
+                    u = par[u]
+                pb.append(seq[::-1])
+            paths.append(pb)
+        _rows_on_paths(c, wts, data, slots, paths, T, d, sig, device)
     torch.cuda.synchronize()

@@ -206,6 +206,63 @@ int eagle_expand_tree_noalloc(const eagle_tree_params* p, const float* draft_log
                               int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
                               float* slot_stats, int32_t* dev_status, void* stream);
 
+/* ---- static (EAGLE-1) draft trees --------------------------------------
+ * Source: [E1] appendix A.1 (the draft tree has a fixed shape from which each
+ * node's child count k is read, k = 4 at the root; greedy drafting takes the
+ * top-k tokens as children, sampling drafts k tokens; 5 draft passes fill
+ * it) and [E1] section 4.3.1 / ablation (tree against chain drafts).
+ *
+ * A shape is given by its parent array `shape_parent` [n] (HOST memory, read
+ * during the call): node 0 is the root (parent -1), 0 <= parent[i] < i, at most
+ * EAGLE_MAX_TOPK children per node and depth at most EAGLE_MAX_DEPTH; siblings
+ * rank by flat index.  The nodes with children are the slots, numbered in flat
+ * order; slot s has k_s children and its draft row is row s of
+ * draft_logits [B, n_slots, V].  The flattened tree IS the shape: node i of
+ * every request is shape node i (its mask is the shape's ancestor relation). */
+
+/* Slots, depth and largest child count of a shape, and each slot's child
+ * count into slot_k [n_slots] (host, nullable).  EAGLE_ERR_SHAPE if the shape
+ * is not a valid flattened tree. */
+int eagle_static_tree_info(int32_t n, const int32_t* shape_parent, int32_t* n_slots, int32_t* depth,
+                           int32_t* kmax, int32_t* slot_k);
+
+/* eagle_workspace_size for a round on a static shape (the expansion's records
+ * are sized for its n_slots slots and largest child count). */
+size_t eagle_static_workspace_size(const eagle_tree_params* p, int32_t n, const int32_t* shape_parent, int32_t hq,
+                                   int32_t hkv, int32_t head_dim, int32_t max_prefix, int32_t hidden);
+
+/* Fill a static shape for every request.  p->topk must be the shape's largest
+ * child count kmax, p->depth its depth, p->m = n - 1 (else EAGLE_ERR_SHAPE).
+ * Slot s's children are the first k_s of its row's sampling order: the top
+ * k_s logits (greedy) or the k_s largest Gumbel keys, with the same keys,
+ * Philox counters (slot index s) and tie rules as eagle_expand_tree.
+ * Out: node_* [B, n] as eagle_expand_tree (node_value = fp32 product of the
+ *        confidences on the root path, node_slot = the node's slot or -1);
+ *      pool_tok, pool_q, pool_flat [B, n_slots, kmax]: slot s's draws in
+ *        sampling order in entries 0..k_s-1, -1 / 0 / -1 past them;
+ *      slot_src [B, n_slots] (pool index of the node each slot expands, -1
+ *        for the root), slot_stats [B, n_slots, 2].
+ * Workspace: eagle_static_workspace_size.  Status: TOKEN_RANGE, NONFINITE,
+ * TOPK_RESCAN, CAND_OVERFLOW. */
+int eagle_expand_static(const eagle_tree_params* p, int32_t n, const int32_t* shape_parent,
+                        const float* draft_logits, const int32_t* root_token, int32_t* node_tok, int32_t* node_parent,
+                        int32_t* node_depth, int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
+                        int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src, float* slot_stats,
+                        void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
+
+/* eagle_verify_accept on a static tree of n_slots slots (p as for
+ * eagle_expand_static; uniforms [B, n, kmax + 1], the last column for the
+ * residual or bonus draw).  A slot's candidates are its k_s draws: the walk
+ * tries them in sampling order and, when all k_s are rejected, draws from the
+ * residual.  No sampling warp. */
+int eagle_verify_accept_static(const eagle_tree_params* p, int32_t n_slots, const int32_t* node_tok,
+                               const int32_t* node_parent, const int32_t* node_slot, const int32_t* pool_tok,
+                               const int32_t* pool_flat, const float* target_logits, const float* target_stats,
+                               const int32_t* target_argmax, const float* draft_logits, const float* slot_stats,
+                               const float* uniforms, int32_t* accept_len, int32_t* accept_path, int32_t* committed,
+                               int32_t* n_committed, int32_t* near_tie, void* ws, size_t ws_bytes,
+                               int32_t* dev_status, void* stream);
+
 /* Ancestor-only tree attention mask and positions.
  * Source: [E2] "Tree Attention Mask" (each token sees only its ancestors,
  * never another branch); [HW] section 5.
@@ -275,7 +332,8 @@ int eagle_lmhead_pack_weight(int32_t vocab, int32_t hidden, int32_t dtype, const
  * to the target argmax.
  * Candidates of node u are all k sampled children of its slot, in sampling
  * order, including pruned ones; accepting a pruned child commits it and ends
- * the walk.  After rejecting x_j the draft law loses x_j and is renormalised
+ * the walk.  A pool row's candidate list ends at its first negative entry
+ * (a static tree's slot with fewer than k draws; see eagle_expand_static).  After rejecting x_j the draft law loses x_j and is renormalised
  * (draws without replacement).  Trial j at node u uses uniforms[b, u, j]; the
  * final draw (residual or bonus) uses uniforms[b, u, k] by inverse CDF in
  * token-id order (first token whose cumulative mass exceeds u * total).

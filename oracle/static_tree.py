@@ -153,3 +153,57 @@ def expand_static_batch(rows, parent, roots, T, seed=0, round_id=0):
     res = {key: np.stack([o[key] for o in outs]) for key in outs[0] if key != "ties"}
     res["ties"] = [o["ties"] for o in outs]
     return res
+
+
+def target_static_rows(inp, T, parent, weights=None):
+    """Draft rows [B, S, V] of a static shape, slot by slot (the dynamic tree's
+    reading R15): the row of slot s is the target's logits at the slot's node,
+    computed on the node's root path alone, plus sigma_b * eps[b, s]; slots are
+    filled in flat order, so each slot's path is drawn before it is needed."""
+    from .round import _Weights, attention_rows
+    c = inp.cfg
+    if c.draft == "iid":
+        return inp.iid_draft_rows()
+    wts = weights or _Weights(inp)
+    info = shape_info(parent)
+    rows = np.zeros((c.B, info["S"], c.V), np.float32)
+    for b in range(c.B):
+        sig = np.float64(inp.sigma[b])
+
+        def children_fn(s, path, kk, b=b, sig=sig):
+            x, _ = attention_rows(inp, b, path, np.arange(len(path)) - 1)
+            z = wts.logits(x[-1:])[0]
+            rows[b, s] = (z + sig * inp.eps[b, s].astype(np.float64)).astype(np.float32)
+            toks, q, _, _, _ = children_of_row(rows[b, s], T, info["kmax"], inp.gumbel_seed, s, b, 0)
+            return toks[:kk], q[:kk]
+
+        build_static_tree(parent, int(inp.roots[b]), children_fn)
+    return rows
+
+
+def run_static_round(inp, T, parent, rows=None, round_id=0, weights=None):
+    """Every stage of one round on a static shape (expand, mask, attention, LM head, accept)."""
+    from . import accept, lmhead, mask
+    from .round import _Weights, attention_rows
+    c = inp.cfg
+    wts = weights or _Weights(inp)
+    if rows is None:
+        rows = target_static_rows(inp, T, parent, wts)
+    ex = expand_static_batch(rows, parent, inp.roots, T, inp.gumbel_seed, round_id)
+    n = len(parent)
+    X = np.zeros((c.B, n, c.H), np.float32)
+    O64 = np.zeros((c.B, n, c.hq, c.dh), np.float64)
+    for b in range(c.B):
+        X[b], O64[b] = attention_rows(inp, b, ex["node_tok"][b], ex["node_parent"][b])
+    z64 = wts.logits(X.reshape(c.B * n, c.H))
+    z32 = z64.astype(np.float32)
+    stats, am = lmhead.row_stats(z32, T)
+    info = shape_info(parent)
+    acc = []
+    for b in range(c.B):
+        tree = {key: ex[key][b] for key in ("node_tok", "node_parent", "node_slot", "pool_tok", "pool_flat")}
+        acc.append(accept.accept_request(tree, z32[b * n:(b + 1) * n], rows[b], T, info["kmax"], info["D"],
+                                         inp.uniforms[b], am[b * n:(b + 1) * n]))
+    masks = np.stack([mask.pack_bits(mask.ancestor_mask(ex["node_parent"][b])) for b in range(c.B)])
+    return dict(rows=rows, expand=ex, mask=masks, attn=O64, x=X, logits64=z64, logits=z32, stats=stats, argmax=am,
+                accept=acc)

@@ -33,6 +33,11 @@ class RoundConfig:
     sigma: Tuple[float, float]  # noise std range (per request, uniform); fixed if lo == hi
     seed: int
     w_std: float = 0.02
+    # A static (EAGLE-1) tree: the parent array of its flattened shape (node 0
+    # the root) and its number of slots (nodes with children); empty for the
+    # dynamic tree.
+    static_parent: Tuple[int, ...] = ()
+    static_slots: int = 0
 
     @property
     def N(self) -> int:
@@ -40,6 +45,8 @@ class RoundConfig:
 
     @property
     def S(self) -> int:
+        if self.static_parent:
+            return self.static_slots
         return 1 + (self.D - 1) * self.k
 
     @property
@@ -85,6 +92,18 @@ CONFIGS = {
 # its single child; m = D draft tokens), for the tree-vs-chain comparison.
 CONFIGS["8b_chain"] = CONFIGS["8b"].with_(name="8b_chain", k=1, m=8, temps=(1.0,))
 
+# A static EAGLE-1-style tree (EAGLE-1 notes, appendix A.1: the root has 4
+# children, 5 draft passes fill it, branches of more probable tokens are deeper
+# and wider): 22 draft nodes over depth 5, 14 of them slots.  Flat (BFS) order;
+# node i's parent is STATIC_SHAPE[i].  This build's own shape following those
+# rules; the pages do not reproduce the figure itself.
+STATIC_SHAPE = (-1, 0, 0, 0, 0, 1, 1, 1, 2, 2, 3, 4, 5, 5, 6, 8, 10, 12, 12, 14, 15, 17, 19)
+CONFIGS["8b_static"] = CONFIGS["8b"].with_(name="8b_static", D=5, k=4, m=len(STATIC_SHAPE) - 1,
+                                          static_parent=STATIC_SHAPE, static_slots=14)
+# The chain with as many draft passes (EAGLE-1 notes, tree-attention ablation: a
+# chain and a tree drafted with the same number of forward passes).
+CONFIGS["8b_chain5"] = CONFIGS["8b"].with_(name="8b_chain5", D=5, k=1, m=5, temps=(1.0,))
+
 # Reduced shapes for element-by-element parity: several tiles and ragged tails
 # in every dimension (vocab not a multiple of the 256-column tile, prefix not a
 # multiple of the key chunk), yet small enough for the oracle in seconds.
@@ -96,6 +115,13 @@ CONFIGS.update({
                            D=4, k=3, m=9, dtype="f32", temps=(1.0, 0.0), draft="target",
                            sigma=(1.0, 1.0), seed=707),
 })
+
+
+# The static shape at the reduced parity size.
+CONFIGS["mid_static"] = CONFIGS["mid_bf16"].with_(name="mid_static", D=5, k=4, m=len(STATIC_SHAPE) - 1,
+                                                  static_parent=STATIC_SHAPE, static_slots=14)
+CONFIGS["tiny_static"] = CONFIGS["tiny"].with_(name="tiny_static", D=5, k=4, m=len(STATIC_SHAPE) - 1,
+                                               static_parent=STATIC_SHAPE, static_slots=14)
 
 
 def get_config(name: str) -> RoundConfig:

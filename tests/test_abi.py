@@ -1,6 +1,11 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol the
 header declares, and rejects bad arguments on the host with the documented
-codes before touching the device."""
+codes before touching the device.
+
+Every call below fails a host check (the fake pointers are never handed to a
+kernel): a shape that is valid is shown valid by a later check failing, such as
+a workspace that is too small or a null pointer, never by a call that could
+reach a launch."""
 import ctypes
 import os
 import re
@@ -90,7 +95,7 @@ def test_attention_rejects(lib):
     f = lib.eagle_tree_attention
     ok = (1, 5, 4, 2, 128, 100, 1)
     tail = [FAKE] * 7
-    assert f(*ok, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) != -2
+    assert f(*ok, *tail, 0.1, FAKE, FAKE, 1000, None, None) == -4   # the shape passes; the workspace does not
     assert f(1, 5, 4, 3, 128, 100, 1, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) == -2
     assert f(1, 5, 4, 2, 96, 100, 1, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) == -3
     assert f(1, 5, 4, 2, 128, 100, 7, *tail, 0.1, FAKE, FAKE, 1 << 30, None, None) == -3
@@ -177,7 +182,7 @@ def test_commit_rejects(lib):
     assert f(*ok[:7], 5, *ptrs, None, None) == -3                         # dtype
     assert f(2, 9, 2, 12, 100, 512, 4, 1, *ptrs, None, None) == -6        # head_dim row not 16-byte units
     assert f(2, 9, 2, 128, 100, 501, 4, 0, *ptrs, None, None) == -6       # hidden row (fp32) ...
-    assert f(2, 9, 2, 128, 100, 500, 4, 0, *ptrs, None, None) != -6       # ... 500 fp32 is whole units
+    assert f(2, 9, 2, 128, 100, 500, 4, 0, None, *ptrs[1:], None, None) == -1  # ... 500 fp32 is whole units
     assert f(2, 9, 2, 128, 100, 500, 4, 1, *ptrs, None, None) == -6       # 500 bf16 is not
     assert f(*ok, None, *ptrs[1:], None, None) == -1
     assert f(*ok, *ptrs[:8], None, None, None) == -1
@@ -235,3 +240,36 @@ def test_draft_rejects(lib):
     assert g(ctypes.byref(p), *([FAKE] * 11), None, None, None) == -1
     bad_p = L.TreeParams(2, 5003, 4, 0, 14, 1.0, 1, 0)
     assert g(ctypes.byref(bad_p), *([FAKE] * 12), None, None) == -2
+
+
+def test_static_tree_info_on_the_host(lib):
+    """Shape bookkeeping is host-only (no device call): the static shape's slots, depth, largest
+    child count and per-slot counts, and the rejection of invalid parent arrays."""
+    import synth
+    from eagle_draft_tree_expand_amd import _lib, ops
+    from oracle import static_tree as ost
+    par = synth.get_config("8b_static").static_parent
+    info = ost.shape_info(par)
+    S, D, kmax, slot_k = ops.static_tree_info(par)
+    assert (S, D, kmax) == (info["S"], info["D"], info["kmax"])
+    assert slot_k == [int(x) for x in info["slot_k"]]
+    for bad in ([0, 0], [-1, 1], [-1, 0, 2], [-1, -1], [-1] + [0] * 17, [-1]):
+        with pytest.raises(_lib.EagleError):
+            ops.static_tree_info(bad)
+
+
+def test_expand_static_rejects_mismatched_params(lib):
+    import synth
+    from eagle_draft_tree_expand_amd import ops
+    par = synth.get_config("8b_static").static_parent
+    arr = (ctypes.c_int32 * len(par))(*par)
+    ptrs = [FAKE] * 14
+    good = dict(batch=1, vocab=1000, depth=5, topk=4, m=len(par) - 1)
+    for kw in (dict(topk=3), dict(depth=6), dict(m=len(par)), dict(vocab=3)):
+        d = dict(good)
+        d.update(kw)
+        p = ops.tree_params(d["batch"], d["vocab"], d["depth"], d["topk"], d["m"], 1.0)
+        assert lib.eagle_expand_static(ctypes.byref(p), len(par), arr, *ptrs, FAKE, 1 << 30, None, None) == -2
+    p = ops.tree_params(1, 1000, 5, 4, len(par) - 1, 1.0)
+    assert lib.eagle_expand_static(ctypes.byref(p), len(par), arr, *ptrs, FAKE, 100, None, None) == -4
+    assert lib.eagle_static_workspace_size(ctypes.byref(p), len(par), arr, 0, 0, 0, 0, 0) > 0
