@@ -28,7 +28,8 @@ EXPORTS = ("eagle_workspace_size", "eagle_workspace_init", "eagle_expand_tree", 
            "eagle_lmhead_pack_weight", "eagle_draft_workspace_size", "eagle_draft_workspace_layout",
            "eagle_draft_forward", "eagle_expand_depth",
            "eagle_expand_finish", "eagle_static_tree_info", "eagle_static_workspace_size", "eagle_expand_static",
-           "eagle_verify_accept_static", "eagle_error_string", "eagle_abi_version")
+           "eagle_verify_accept_static", "eagle_lmhead_softmax_compact", "eagle_verify_accept_compact",
+           "eagle_error_string", "eagle_abi_version")
 
 
 class TreeParams(ctypes.Structure):
@@ -85,6 +86,9 @@ _SIGS = {
     "eagle_expand_static": (c_int32, [POINTER(TreeParams), c_int32, _P, _P, _P] + [_P] * 7 + [_P] * 5 +
                             [_P, c_size_t, _P, _P]),
     "eagle_verify_accept_static": (c_int32, [POINTER(TreeParams), c_int32] + [_P] * 16 + [_P, c_size_t, _P, _P]),
+    "eagle_lmhead_softmax_compact": (c_int32, [c_int32] * 3 + [_P, _P, c_int32, c_float] + [_P] * 4 +
+                                     [_P, c_size_t, _P, _P]),
+    "eagle_verify_accept_compact": (c_int32, [POINTER(TreeParams), c_int32] + [_P] * 17 + [_P, c_size_t, _P, _P]),
     "eagle_error_string": (c_char_p, [c_int32]),
     "eagle_abi_version": (c_int32, []),
 }

@@ -134,6 +134,20 @@ EDEV bool warp_keeps(float t, int v, uint32_t code_b, uint32_t id_b) {
   return c > code_b || (c == code_b && (uint32_t)v <= id_b);
 }
 
+// Compact target rows: a logit as the fp16 offset from its 128-column block
+// maximum m (round to nearest even; -inf for non-finite logits and for blocks
+// without a finite one), and the value every use reads, fp32(m + offset).
+constexpr int kCmpBlockShift = 7;  // 128 columns per block
+EDEV uint16_t cmp_encode(float z, float m) {
+  if (z == kNegInf || m == kNegInf) return 0xFC00u;  // fp16 -inf
+  const _Float16 h = (_Float16)(z - m);
+  return __builtin_bit_cast(uint16_t, h);
+}
+EDEV float cmp_decode(uint16_t h, float m) {
+  const float d = (float)__builtin_bit_cast(_Float16, h);
+  return d == kNegInf ? kNegInf : m + d;
+}
+
 EDEV void set_status(int32_t* st, int bits) {
   if (st) atomicOr(st, bits);
 }

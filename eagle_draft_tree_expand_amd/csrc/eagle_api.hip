@@ -350,9 +350,9 @@ int eagle_verify_accept_static(const eagle_tree_params* p, int32_t n_slots, cons
   void* mailbox = static_cast<char*>(ws) + end;
   return launch_status(launch_accept(p->batch, p->m + 1, p->vocab, p->depth, p->topk, n_slots, p->temperature,
                                      node_tok, node_parent, node_slot, pool_tok, pool_flat, target_logits,
-                                     target_stats, target_argmax, draft_logits, slot_stats, nullptr, nullptr, uniforms,
-                                     mailbox, accept_len, accept_path, committed, n_committed, near_tie, dev_status,
-                                     (hipStream_t)stream));
+                                     target_stats, target_argmax, draft_logits, slot_stats, nullptr, nullptr, nullptr,
+                                     nullptr, uniforms, mailbox, accept_len, accept_path, committed, n_committed,
+                                     near_tie, dev_status, (hipStream_t)stream));
 }
 
 int eagle_build_tree_mask(int32_t batch, int32_t n, const int32_t* node_parent, const int32_t* node_depth,
@@ -396,6 +396,53 @@ int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dt
   if (ws_bytes < kCounterBytes + lm_ws_bytes(rows, vocab, hidden)) return EAGLE_ERR_WORKSPACE;
   return launch_status(launch_lmhead(rows, hidden, vocab, dtype, w_layout, x, w, temperature, logits, row_stats,
                                      row_argmax, probs, stage_area(ws), dev_status, (hipStream_t)stream));
+}
+
+int eagle_lmhead_softmax_compact(int32_t rows, int32_t hidden, int32_t vocab, const void* x, const void* w,
+                                 int32_t w_layout, float temperature, uint16_t* target_z16, float* block_max,
+                                 float* row_stats, int32_t* row_argmax, void* ws, size_t ws_bytes,
+                                 int32_t* dev_status, void* stream) {
+  int rc = check_lm(rows, hidden, vocab, EAGLE_BF16);
+  if (rc != EAGLE_OK) return rc;
+  if (w_layout != EAGLE_W_ROWMAJOR && w_layout != EAGLE_W_PACKED) return EAGLE_ERR_SHAPE;
+  if (!(temperature >= 0.f) || !isfinite(temperature)) return EAGLE_ERR_SHAPE;
+  if (!x || !w || !target_z16 || !block_max || !row_stats || !row_argmax || !ws) return EAGLE_ERR_NULL;
+  if (!aligned16(x) || !aligned16(w) || ((uintptr_t)target_z16 & 7) != 0 || ((uintptr_t)block_max & 3) != 0)
+    return EAGLE_ERR_ALIGN;
+  if (ws_bytes < kCounterBytes + lm_ws_bytes(rows, vocab, hidden)) return EAGLE_ERR_WORKSPACE;
+  return launch_status(launch_lmhead_compact(rows, hidden, vocab, w_layout, x, w, temperature, target_z16,
+                                             block_max, row_stats, row_argmax, stage_area(ws), dev_status,
+                                             (hipStream_t)stream));
+}
+
+int eagle_verify_accept_compact(const eagle_tree_params* p, int32_t n_slots, const int32_t* node_tok,
+                                const int32_t* node_parent, const int32_t* node_slot, const int32_t* pool_tok,
+                                const int32_t* pool_flat, const uint16_t* target_z16, const float* block_max,
+                                const float* target_stats, const int32_t* target_argmax, const float* draft_logits,
+                                const float* slot_stats, const float* uniforms, int32_t* accept_len,
+                                int32_t* accept_path, int32_t* committed, int32_t* n_committed, int32_t* near_tie,
+                                void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  int rc = n_slots > 0 ? check_static_params(p) : check_tree_params(p);
+  if (rc != EAGLE_OK) return rc;
+  if (n_slots < 0 || n_slots > p->m + 1) return EAGLE_ERR_SHAPE;
+  const int S = n_slots > 0 ? n_slots : 1 + (p->depth - 1) * p->topk;
+  const bool greedy = !(p->temperature > 0.f);
+  if (!node_tok || !node_parent || !node_slot || !pool_tok || !pool_flat || !accept_len || !accept_path ||
+      !committed || !n_committed || !near_tie || !ws)
+    return EAGLE_ERR_NULL;
+  if (greedy ? !target_argmax
+             : (!target_z16 || !block_max || !target_stats || !draft_logits || !slot_stats || !uniforms))
+    return EAGLE_ERR_NULL;
+  const size_t mail = accept_mail_bytes(p->batch);
+  const size_t end = ws_bytes & ~(size_t)255;
+  if (end < kCounterBytes + mail) return EAGLE_ERR_WORKSPACE;
+  void* mailbox = static_cast<char*>(ws) + end;
+  return launch_status(launch_accept(p->batch, p->m + 1, p->vocab, p->depth, p->topk, S, p->temperature, node_tok,
+                                     node_parent, node_slot, pool_tok, pool_flat, nullptr, target_stats,
+                                     target_argmax, draft_logits, slot_stats, nullptr, nullptr,
+                                     greedy ? nullptr : target_z16, greedy ? nullptr : block_max, uniforms, mailbox,
+                                     accept_len, accept_path, committed, n_committed, near_tie, dev_status,
+                                     (hipStream_t)stream));
 }
 
 size_t eagle_lmhead_packed_bytes(int32_t vocab, int32_t hidden, int32_t dtype) {
@@ -450,7 +497,7 @@ int eagle_verify_accept_warped(const eagle_tree_params* p, const uint32_t* targe
                                      1 + (p->depth - 1) * p->topk, p->temperature, node_tok,
                                      node_parent, node_slot, pool_tok, pool_flat, target_logits, target_stats,
                                      target_argmax, draft_logits, slot_stats, greedy ? nullptr : target_bound,
-                                     greedy ? nullptr : draft_bound, uniforms, mailbox, accept_len,
+                                     greedy ? nullptr : draft_bound, nullptr, nullptr, uniforms, mailbox, accept_len,
                                      accept_path, committed, n_committed, near_tie, dev_status,
                                      (hipStream_t)stream));
 }

@@ -59,7 +59,9 @@ constexpr int kAccGroupCap = 32;   // largest group used (exchange cost grows wi
 constexpr int kCacheMax = 8192;  // slice tokens whose exponential terms fit the LDS token cache (64 KB)
 
 struct Rows {
-  const float* zp;  // target logits row of the node
+  const float* zp;  // target logits row of the node (null with a compact row)
+  const uint16_t* hp;  // compact target row of the node: fp16 offsets, and
+  const float* bp;     // its 128-column block maxima (null: fp32 row zp)
   const float* zq;  // draft logits row of the node's slot (unused when s == 0)
   float Mp, Mq, Tp;
   double invSp, invSq;
@@ -67,6 +69,23 @@ struct Rows {
   bool wp, wq;
   uint32_t pc, pi, qc, qi;
 };
+
+// Target logit of token v (a compact row decoded), and of tokens base..base+3
+// (base a multiple of 4, all inside the row) with one vector load.
+EDEV float zp_at(const Rows& R, int v) {
+  return R.hp ? cmp_decode(R.hp[v], R.bp[v >> kCmpBlockShift]) : R.zp[v];
+}
+EDEV float4 zp_at4(const Rows& R, int base) {
+  if (R.hp) {
+    const uint2 u = *reinterpret_cast<const uint2*>(R.hp + base);
+    const float m = R.bp[base >> kCmpBlockShift];  // four tokens from one block
+    return make_float4(cmp_decode((uint16_t)(u.x & 0xFFFFu), m), cmp_decode((uint16_t)(u.x >> 16), m),
+                       cmp_decode((uint16_t)(u.y & 0xFFFFu), m), cmp_decode((uint16_t)(u.y >> 16), m));
+  }
+  return *reinterpret_cast<const float4*>(R.zp + base);
+}
+// Alignment bits that forbid the vector loads of the target row.
+EDEV uintptr_t p_misalign(const Rows& R) { return R.hp ? ((uintptr_t)R.hp & 7) : ((uintptr_t)R.zp & 15); }
 
 // fp32 exponential term of token v's logit: exp(z/T' - M), 0 for a
 // non-finite z or a token the row's warp drops.
@@ -158,7 +177,7 @@ EDEV void slice_terms(const Rows& R, bool need_q, bool from_cache, const Group& 
   }
   float zp[4], zq[4];
   if (vec && base + 3 < gr.hi) {
-    const float4 p4 = *reinterpret_cast<const float4*>(R.zp + base);
+    const float4 p4 = zp_at4(R, base);
     zp[0] = p4.x; zp[1] = p4.y; zp[2] = p4.z; zp[3] = p4.w;
     if (need_q) {
       const float4 q4 = *reinterpret_cast<const float4*>(R.zq + base);
@@ -167,7 +186,7 @@ EDEV void slice_terms(const Rows& R, bool need_q, bool from_cache, const Group& 
   } else {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      zp[e] = base + e < gr.hi ? R.zp[base + e] : kNegInf;
+      zp[e] = base + e < gr.hi ? zp_at(R, base + e) : kNegInf;
       if (need_q) zq[e] = base + e < gr.hi ? R.zq[base + e] : kNegInf;
     }
   }
@@ -192,7 +211,7 @@ EDEV void local_partial(const Rows& R, double s, Group& gr, Smem& sm) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool need_q = s != 0.0;
   const bool from_cache = cache_ready(gr, need_q);
-  const bool vec = ((((uintptr_t)R.zp) | (need_q ? (uintptr_t)R.zq : 0)) & 15) == 0;
+  const bool vec = (p_misalign(R) | (need_q ? ((uintptr_t)R.zq & 15) : 0)) == 0;
   double a = 0.0;
   for (int base = gr.lo + tid * 4, ci = tid * 4; base < gr.hi; base += kThreads * 4, ci += kThreads * 4) {
     float ep[4], eq[4];
@@ -241,7 +260,7 @@ EDEV double group_reduce(const Rows& R, double s, Group& gr, Smem& sm, int* time
 // too when need_q).
 EDEV void fill_cache(const Rows& R, bool need_q, Group& gr) {
   const int tid = threadIdx.x;
-  const bool vec = ((((uintptr_t)R.zp) | (need_q ? (uintptr_t)R.zq : 0)) & 15) == 0;
+  const bool vec = (p_misalign(R) | (need_q ? ((uintptr_t)R.zq & 15) : 0)) == 0;
   for (int base = gr.lo + tid * 4, ci = tid * 4; base < gr.hi; base += kThreads * 4, ci += kThreads * 4) {
     float ep[4], eq[4];
     slice_terms(R, need_q, false, gr, base, ci, vec, ep, eq);
@@ -330,7 +349,7 @@ EDEV int group_draw(const Rows& R, double s, int ntried, double uval, Group& gr,
     // scan the own slice in id order, 4096 tokens (4 per thread) per pass
     const bool need_q = s != 0.0;
     const bool from_cache = cache_ready(gr, need_q);
-    const bool vec = ((((uintptr_t)R.zp) | (need_q ? (uintptr_t)R.zq : 0)) & 15) == 0;
+    const bool vec = (p_misalign(R) | (need_q ? ((uintptr_t)R.zq & 15) : 0)) == 0;
     double off = off0;
     int found = -1, tie = 0, last_pos = -1;
     for (int base0 = gr.lo, ci0 = 0; base0 < gr.hi && found < 0; base0 += kThreads * 4, ci0 += kThreads * 4) {
@@ -425,6 +444,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     const int32_t* __restrict__ pool_flat, const float* __restrict__ tlog, const float* __restrict__ tstats,
     const int32_t* __restrict__ targmax, const float* __restrict__ dlog, const float* __restrict__ sstats,
     const uint32_t* __restrict__ tbound, const uint32_t* __restrict__ dbound,
+    const uint16_t* __restrict__ thp, const float* __restrict__ tbm,
     const float* __restrict__ uniforms, Mailbox* __restrict__ mail, int32_t* accept_len, int32_t* accept_path,
     int32_t* committed, int32_t* n_committed, int32_t* near_tie, int32_t* status) {
   // dynamic LDS: [cache_tokens] token cache, then the request's tree metadata
@@ -528,7 +548,15 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
       const int u = cur_u;
       const int slot = m_slot[u];
       Rows R;
-      R.zp = tlog + ((size_t)b * N + u) * V;
+      if (thp) {  // compact target rows
+        R.zp = nullptr;
+        R.hp = thp + ((size_t)b * N + u) * V;
+        R.bp = tbm + ((size_t)b * N + u) * (((size_t)V + 127) >> kCmpBlockShift);
+      } else {
+        R.zp = tlog + ((size_t)b * N + u) * V;
+        R.hp = nullptr;
+        R.bp = nullptr;
+      }
       R.wp = tbound != nullptr;
       R.pc = R.wp ? tbound[((size_t)b * N + u) * 2] : 0u;
       R.pi = R.wp ? tbound[((size_t)b * N + u) * 2 + 1] : 0u;
@@ -575,14 +603,14 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
         const int x = m_ptok[slot * k + tid];
         c_ok = x >= 0 && x < V;
         c_x = c_ok ? x : 0;
-        zpx = R.zp[c_x];
+        zpx = zp_at(R, c_x);
         zqx = R.zq[c_x];
       }
       // The node's rows for the token cache: the loads go out now, behind the
       // children's, and the terms are stored only when a reduction needs them
       // (a node whose first candidate is accepted never waits for them).
       const bool fill = gr.cache != nullptr && cnode != u;
-      const bool vecr = (V & 3) == 0 && ((((uintptr_t)R.zp) | (uintptr_t)R.zq) & 15) == 0;
+      const bool vecr = (V & 3) == 0 && (p_misalign(R) | ((uintptr_t)R.zq & 15)) == 0;
       float4 rp[2], rq[2];
       if (fill) {
         gr.cstate = 0;
@@ -591,7 +619,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
           for (int t = 0; t < 2; ++t) {
             const int base = gr.lo + tid * 4 + t * kThreads * 4;
             if (base < gr.hi) {
-              rp[t] = *reinterpret_cast<const float4*>(R.zp + base);
+              rp[t] = zp_at4(R, base);
               rq[t] = *reinterpret_cast<const float4*>(R.zq + base);
             }
           }
@@ -767,9 +795,9 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, int S, float T, cons
                          const int32_t* node_parent, const int32_t* node_slot, const int32_t* pool_tok,
                          const int32_t* pool_flat, const float* tlog, const float* tstats, const int32_t* targmax,
                          const float* dlog, const float* sstats, const uint32_t* tbound, const uint32_t* dbound,
-                         const float* uniforms, void* mail, int32_t* accept_len, int32_t* accept_path,
-                         int32_t* committed, int32_t* n_committed, int32_t* near_tie, int32_t* status,
-                         hipStream_t st) {
+                         const uint16_t* thp, const float* tbm, const float* uniforms, void* mail,
+                         int32_t* accept_len, int32_t* accept_path, int32_t* committed, int32_t* n_committed,
+                         int32_t* near_tie, int32_t* status, hipStream_t st) {
   const bool greedy = !(T > 0.f);
   // Group size: as many workgroups per request as stay co-resident; requests
   // beyond the resident capacity go in further launches.
@@ -809,7 +837,8 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, int S, float T, cons
     const int nb = B - b0 < per_launch ? B - b0 : per_launch;
     accept_kernel<<<dim3(8 * ((nb + 7) / 8) * G), dim3(kThreads), lds, st>>>(b0, nb, G, N, V, D, k, S, T, cache_tokens,
         node_tok, node_parent,
-        node_slot, pool_tok, pool_flat, tlog, tstats, targmax, dlog, sstats, tbound, dbound, uniforms, mb, accept_len,
+        node_slot, pool_tok, pool_flat, tlog, tstats, targmax, dlog, sstats, tbound, dbound, thp, tbm, uniforms, mb,
+        accept_len,
         accept_path,
         committed, n_committed, near_tie, status);
     e = hipGetLastError();

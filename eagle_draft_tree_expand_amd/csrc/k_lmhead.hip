@@ -103,7 +103,8 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
                                                                  const uint16_t* __restrict__ w,
                                                                  float* __restrict__ logits, float* __restrict__ part,
                                                                  int32_t* status, int hk, float* __restrict__ partial,
-                                                                 RowMap rm) {
+                                                                 RowMap rm, uint16_t* __restrict__ z16,
+                                                                 float* __restrict__ bmax) {
   constexpr int NT = 8;  // 16-column n-tiles per wave: 128 vocab columns
   __shared__ floatx4 xch[4][2][NT][64];  // accumulator exchange between the two hidden halves (64 KB)
   __shared__ u32x4 xst[2][2][8][64];     // X staging: [stage][hidden half][fragment ks*4 + mt][lane] (32 KB)
@@ -278,7 +279,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
         const int n = n0 + t * 16 + col;
         const float z = acc[mt][t][i];
         if (full || n < V) {
-          if (m < rows) logits[(size_t)map_row(m, rm) * V + n] = z;
+          if (m < rows && z16 == nullptr) logits[(size_t)map_row(m, rm) * V + n] = z;
           chk = fmaf(z, 0.f, chk);
         }
       }
@@ -303,6 +304,40 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
   // value (exp2(-inf) = 0).  The record's arg names the tile, not the column:
   // the row merge scans the winning tile for the first column holding the max.
   const float cT = kLog2e / Tp;
+  if (z16 != nullptr) {
+    // Compact rows: this wave's 128 columns are one block.  Per row: the
+    // block maximum and the first column holding it (exact, ties to the lower
+    // id), the fp16 offsets, and the statistics of the decoded values.
+    const int nblk = (V + 127) >> 7, blk = n0 >> 7;
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = m0 + kh * 32 + mt * 16 + grp * 4 + i;
+        float zm = kNegInf;
+        int ai = kIdxNone;
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+          if (acc[mt][t][i] > zm) { zm = acc[mt][t][i]; ai = n0 + t * 16 + col; }  // columns ascend with t
+        row16_argmax(zm, ai);
+        const float tmax = zm / Tp;
+        const size_t ro = (size_t)map_row(min(m, rows - 1), rm);
+        float sum = 0.f;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+          const int n = n0 + t * 16 + col;
+          const uint16_t h = cmp_encode(acc[mt][t][i], zm);
+          if (m < rows && (full || n < V)) z16[ro * V + n] = h;
+          if (zm != kNegInf) sum += __builtin_amdgcn_exp2f(fmaf(cmp_decode(h, zm), cT, -tmax * kLog2e));
+        }
+        sum = row16_sum(sum);
+        if (col == 0) {
+          wrec[wq][kh * 32 + mt * 16 + grp * 4 + i] = Rec{zm == kNegInf ? kNegInf : tmax, sum, zm, ai};
+          if (m < rows && n0 < V) bmax[ro * nblk + blk] = zm;  // a wave past the vocabulary has no block
+        }
+      }
+    }
+  } else {
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -323,6 +358,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
         wrec[wq][kh * 32 + mt * 16 + grp * 4 + i] =
             Rec{zm == kNegInf ? kNegInf : tmax, sum, zm, kLmArgTile | (nt_idx * kLmTileN)};
     }
+  }
   }
   __syncthreads();
   const int nrows = min(kLmTileM, rows - m0);
@@ -424,7 +460,7 @@ template <bool PACKED>
 __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_gemm_kernel(
     int rows, int H, int V, float Tp, int nm, int nn, int bm, const uint16_t* __restrict__ x,
     const uint16_t* __restrict__ w, float* __restrict__ logits, float* __restrict__ part, int32_t* status,
-    RowMap rm, int gps, int hk, float* __restrict__ partial) {
+    RowMap rm, int gps, int hk, float* __restrict__ partial, uint16_t* __restrict__ z16, float* __restrict__ bmax) {
   // the ring: one array per stage
   __shared__ __attribute__((aligned(1024))) uint16_t ring0[32 * kGBlock];  // A 16 blocks | B 16 blocks
   __shared__ __attribute__((aligned(1024))) uint16_t ring1[32 * kGBlock];
@@ -566,7 +602,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
         const int n = nbase + nt * 16 + col;
         float z = acc[mt][nt][i];
         if (n < V) {
-          if (m < rows) logits[(size_t)map_row(m, rm) * V + n] = z;
+          if (m < rows && z16 == nullptr) logits[(size_t)map_row(m, rm) * V + n] = z;
           if (!isfinite(z)) { bad = true; z = kNegInf; }
           if (z > zm) { zm = z; ai = n; }  // columns ascend with nt: ties keep the lower id
         } else {
@@ -576,6 +612,19 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       }
       row16_argmax(zm, ai);
       const float tmax = zm / Tp;
+      if (z16 != nullptr) {
+        // compact rows: this wave's 128 columns are one block; the statistics
+        // are those of the decoded values
+        const size_t ro = (size_t)map_row(min(m, rows - 1), rm);
+#pragma unroll
+        for (int nt = 0; nt < 8; ++nt) {
+          const int n = nbase + nt * 16 + col;
+          const uint16_t h = cmp_encode(zv[nt], zm);
+          if (m < rows && n < V) z16[ro * V + n] = h;
+          zv[nt] = cmp_decode(h, zm);
+        }
+        if (col == 0 && m < rows && nbase < V) bmax[ro * ((V + 127) >> 7) + (nbase >> 7)] = zm;
+      }
       float s = 0.f;
       if (zm != kNegInf) {
         const float cc = kLog2e / Tp, off = tmax * kLog2e;
@@ -650,6 +699,94 @@ __global__ __launch_bounds__(256) void lm_combine_kernel(int rows, int V, int KS
     float* pr = part + ((size_t)m * gridDim.x + tile) * 4;
     *reinterpret_cast<float4*>(pr) =
         make_float4(zm == kNegInf ? kNegInf : tmax, s, zm, __int_as_float(kLmArgTile | n0));
+  }
+}
+
+// lm_combine_kernel for compact rows: the summed logits of one 512-column
+// tile of one row become four 128-column blocks (fp16 offsets + block maxima);
+// the tile's record holds the statistics of the decoded values and the exact
+// argmax column.
+__global__ __launch_bounds__(256) void lm_combine_compact_kernel(int rows, int V, int KS, float Tp,
+                                                                 const float* __restrict__ partial,
+                                                                 uint16_t* __restrict__ z16, float* __restrict__ bmax,
+                                                                 float* __restrict__ part, int32_t* status,
+                                                                 RowMap rm) {
+  __shared__ float shm[2][4], shs[4], sha[4];
+  __shared__ int shi[4];
+  const int tile = blockIdx.x, m = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n0 = tile * kLmTileN;
+  const size_t ro = (size_t)map_row(m, rm);
+  const int nblk = (V + 127) >> 7;
+  float z[2];
+  bool bad = false;
+  float bz = kNegInf;
+  int bi = kIdxNone;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int n = n0 + h * 256 + tid;
+    float v = kNegInf;
+    if (n < V) {
+      float acc = 0.f;
+      const float* pp = partial + (size_t)m * V + n;
+      const size_t sl = (size_t)rows * V;
+      for (int kz0 = 0; kz0 < KS; kz0 += 8) {
+        float x[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[j] = kz0 + j < KS ? pp[(size_t)(kz0 + j) * sl] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (kz0 + j < KS) acc += x[j];
+      }
+      v = acc;
+      if (!isfinite(v)) { bad = true; v = kNegInf; }
+    }
+    z[h] = v;
+    if (v > bz) { bz = v; bi = n; }  // h ascends with the column: ties keep the lower id
+  }
+  if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
+  // block maxima: block 2h + (wave >> 1) spans waves 2(wave >> 1), 2(wave >> 1) + 1 of half h
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float wm = wave_max(z[h]);
+    if (lane == 0) shm[h][wave] = wm;
+  }
+  wave_argmax(bz, bi);
+  if (lane == 0) { sha[wave] = bz; shi[wave] = bi; }
+  __syncthreads();
+  float sum = 0.f;
+  float zt[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int w0 = wave & ~1;
+    const float mb = fmaxf(shm[h][w0], shm[h][w0 + 1]);
+    const int n = n0 + h * 256 + tid;
+    const uint16_t code = cmp_encode(z[h], mb);
+    if (n < V) z16[ro * V + n] = code;
+    if ((tid & 127) == 0 && n < V) bmax[ro * nblk + (n >> 7)] = mb;
+    zt[h] = cmp_decode(code, mb);
+  }
+  // the tile maximum over the four blocks (equal in every thread)
+  float zmax = kNegInf;
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) zmax = fmaxf(zmax, shm[h][w]);
+  const float tmax = zmax / Tp;
+  if (zmax != kNegInf) {
+    const float cT = kLog2e / Tp, off = tmax * kLog2e;
+    sum = __builtin_amdgcn_exp2f(fmaf(zt[0], cT, -off)) + __builtin_amdgcn_exp2f(fmaf(zt[1], cT, -off));
+  }
+  sum = wave_sum(sum);
+  if (lane == 0) shs[wave] = sum;
+  __syncthreads();
+  if (tid == 0) {
+    const float s = (shs[0] + shs[1]) + (shs[2] + shs[3]);
+    float az = sha[0];
+    int ai = shi[0];
+    for (int w = 1; w < 4; ++w)
+      if (beats(sha[w], shi[w], az, ai)) { az = sha[w]; ai = shi[w]; }
+    float* pr = part + ((size_t)m * gridDim.x + tile) * 4;
+    *reinterpret_cast<float4*>(pr) = make_float4(zmax == kNegInf ? kNegInf : tmax, s, zmax, __int_as_float(ai));
   }
 }
 
@@ -768,14 +905,21 @@ hipError_t launch_lmhead_map(int rows, int H, int V, int dtype, int w_layout, co
                              float* logits, float* row_stats, int32_t* row_argmax, float* probs, float* ws_part,
                              int32_t* status, RowMap rm, hipStream_t st) {
   return launch_lmhead_impl(rows, H, V, dtype, w_layout, x, w, T, logits, row_stats, row_argmax, probs, ws_part,
-                            status, rm, nullptr, st);
+                            status, rm, nullptr, nullptr, nullptr, st);
+}
+
+hipError_t launch_lmhead_compact(int rows, int H, int V, int w_layout, const void* x, const void* w, float T,
+                                 uint16_t* z16, float* bmax, float* row_stats, int32_t* row_argmax, float* ws_part,
+                                 int32_t* status, hipStream_t st) {
+  return launch_lmhead_impl(rows, H, V, EAGLE_BF16, w_layout, x, w, T, nullptr, row_stats, row_argmax, nullptr,
+                            ws_part, status, RowMap{1 << 30, 0, 0}, nullptr, z16, bmax, st);
 }
 
 hipError_t launch_product(int rows, int H, int V, const void* x, const void* w_packed, float* out, float* ws_part,
                           int32_t* status, ProductOut* po, hipStream_t st) {
   int ks = 1;
   hipError_t e = launch_lmhead_impl(rows, H, V, EAGLE_BF16, EAGLE_W_PACKED, x, w_packed, 1.f, out, nullptr, nullptr,
-                                    nullptr, ws_part, status, RowMap{1 << 30, 0, 0}, &ks, st);
+                                    nullptr, ws_part, status, RowMap{1 << 30, 0, 0}, &ks, nullptr, nullptr, st);
   po->ks = ks;
   po->src = ks > 1 ? ws_part + lm_rec_floats(rows, V) : out;
   po->slice = (size_t)rows * V;
@@ -784,7 +928,8 @@ hipError_t launch_product(int rows, int H, int V, const void* x, const void* w_p
 
 hipError_t launch_lmhead_impl(int rows, int H, int V, int dtype, int w_layout, const void* x, const void* w, float T,
                               float* logits, float* row_stats, int32_t* row_argmax, float* probs, float* ws_part,
-                              int32_t* status, RowMap rm, int* defer_ks, hipStream_t st) {
+                              int32_t* status, RowMap rm, int* defer_ks, uint16_t* z16, float* bmax,
+                              hipStream_t st) {
   const float Tp = (T > 0.f) ? T : 1.0f;
   int ntiles = lm_ntiles(V);
   if (dtype == EAGLE_BF16 && rows >= kGemmMinRows) {
@@ -800,13 +945,13 @@ hipError_t launch_lmhead_impl(int rows, int H, int V, int dtype, int w_layout, c
     if (w_layout == EAGLE_W_PACKED)
       lmhead_gemm_kernel<true><<<gps * ks, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
                                                            (const uint16_t*)w, logits, ws_part, status, rm, gps,
-                                                           H / ks, partial);
+                                                           H / ks, partial, z16, bmax);
     else
       lmhead_gemm_kernel<false><<<gps * ks, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
                                                             (const uint16_t*)w, logits, ws_part, status, rm, gps,
-                                                            H / ks, partial);
+                                                            H / ks, partial, z16, bmax);
     if (defer_ks) *defer_ks = ks;
-    if (ks > 1 && !defer_ks) {
+    if (ks > 1 && !defer_ks) {  // plain products only (statistics take ks = 1): never compact
       hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
       lm_combine_kernel<<<dim3(lm_ntiles(V), rows), 256, 0, st>>>(rows, V, ks, Tp, partial, logits, ws_part, status,
@@ -818,15 +963,19 @@ hipError_t launch_lmhead_impl(int rows, int H, int V, int dtype, int w_layout, c
     dim3 grid(ntiles, lm_mtiles(rows), ks);
     if (w_layout == EAGLE_W_PACKED)
       lmhead_bf16_kernel<true><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
-                                                     ws_part, status, H / ks, partial, rm);
+                                                     ws_part, status, H / ks, partial, rm, z16, bmax);
     else
       lmhead_bf16_kernel<false><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
-                                                      ws_part, status, H / ks, partial, rm);
+                                                      ws_part, status, H / ks, partial, rm, z16, bmax);
     if (defer_ks) *defer_ks = ks;
     if (ks > 1 && !defer_ks) {
       hipError_t e0 = hipGetLastError();
       if (e0 != hipSuccess) return e0;
-      lm_combine_kernel<<<dim3(ntiles, rows), 256, 0, st>>>(rows, V, ks, Tp, partial, logits, ws_part, status, rm);
+      if (z16 != nullptr)
+        lm_combine_compact_kernel<<<dim3(ntiles, rows), 256, 0, st>>>(rows, V, ks, Tp, partial, z16, bmax, ws_part,
+                                                                      status, rm);
+      else
+        lm_combine_kernel<<<dim3(ntiles, rows), 256, 0, st>>>(rows, V, ks, Tp, partial, logits, ws_part, status, rm);
     }
   } else {
     dim3 grid(ntiles, rows);

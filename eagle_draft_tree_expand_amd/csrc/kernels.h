@@ -172,7 +172,14 @@ hipError_t launch_lmhead_map(int rows, int hidden, int V, int dtype, int w_layou
                              float* ws_part, int32_t* status, RowMap rm, hipStream_t st);
 hipError_t launch_lmhead_impl(int rows, int hidden, int V, int dtype, int w_layout, const void* x, const void* w,
                               float T, float* logits, float* row_stats, int32_t* row_argmax, float* probs,
-                              float* ws_part, int32_t* status, RowMap rm, int* defer_ks, hipStream_t st);
+                              float* ws_part, int32_t* status, RowMap rm, int* defer_ks, uint16_t* z16, float* bmax,
+                              hipStream_t st);
+// Compact rows instead of fp32 logits (bf16 only): z16 [rows, V] fp16 offsets
+// from the 128-column block maxima bmax [rows, ceil(V / 128)]; row statistics
+// of the decoded values and the exact argmax.
+hipError_t launch_lmhead_compact(int rows, int hidden, int V, int w_layout, const void* x, const void* w, float T,
+                                 uint16_t* z16, float* bmax, float* row_stats, int32_t* row_argmax, float* ws_part,
+                                 int32_t* status, hipStream_t st);
 // A plain bf16 product out = X W^T (W packed) whose hidden-split slices, if
 // any, are left unsummed: the result is sum over kz < ks of src[kz * slice + r * V + n]
 // (ks = 1: src = out).  The caller's next kernel sums them.
@@ -227,6 +234,7 @@ hipError_t launch_accept(int B, int N, int V, int D, int k, int S, float T, cons
                          const int32_t* pool_tok, const int32_t* pool_flat, const float* tlog,
                          const float* tstats, const int32_t* targmax, const float* dlog,
                          const float* sstats, const uint32_t* tbound, const uint32_t* dbound,
+                         const uint16_t* thp, const float* tbm,  // compact target rows (null: tlog)
                          const float* uniforms, void* mail, int32_t* accept_len,
                          int32_t* accept_path, int32_t* committed, int32_t* n_committed,
                          int32_t* near_tie, int32_t* status, hipStream_t st);

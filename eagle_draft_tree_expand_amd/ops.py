@@ -163,6 +163,29 @@ def verify_accept_static(p: TreeParams, n_slots, tree, target_logits, target_sta
     check("eagle_verify_accept_static", rc)
 
 
+def lmhead_softmax_compact(rows, hidden, vocab, x, w, temperature, z16, block_max, row_stats, row_argmax, ws,
+                           status=None, packed=False):
+    """The LM head without fp32 rows: z16 [rows, V] fp16 offsets, block_max [rows, ceil(V/128)]."""
+    assert z16.dtype == torch.float16 and block_max.dtype == torch.float32
+    layout = EAGLE_W_PACKED if packed else EAGLE_W_ROWMAJOR
+    rc = _lib.load().eagle_lmhead_softmax_compact(rows, hidden, vocab, _ptr(x), _ptr(w), layout, float(temperature),
+                                                 _ptr(z16), _ptr(block_max), _ptr(row_stats), _ptr(row_argmax),
+                                                 _ptr(ws), ws.numel(), _ptr(status), _stream())
+    check("eagle_lmhead_softmax_compact", rc)
+
+
+def verify_accept_compact(p: TreeParams, n_slots, tree, z16, block_max, target_stats, target_argmax, draft_logits,
+                          slot_stats, uniforms, out, ws, status=None):
+    """The walk on compact target rows (n_slots 0: dynamic tree; > 0: static tree)."""
+    rc = _lib.load().eagle_verify_accept_compact(
+        p, int(n_slots), _ptr(tree["node_tok"]), _ptr(tree["node_parent"]), _ptr(tree["node_slot"]),
+        _ptr(tree["pool_tok"]), _ptr(tree["pool_flat"]), _ptr(z16), _ptr(block_max), _ptr(target_stats),
+        _ptr(target_argmax), _ptr(draft_logits), _ptr(slot_stats), _ptr(uniforms), _ptr(out["accept_len"]),
+        _ptr(out["accept_path"]), _ptr(out["committed"]), _ptr(out["n_committed"]), _ptr(out["near_tie"]), _ptr(ws),
+        ws.numel(), _ptr(status), _stream())
+    check("eagle_verify_accept_compact", rc)
+
+
 def gather_rows(n_rows, row_elems, table, idx, out, status=None):
     dt = _DT[table.dtype]
     rc = _lib.load().eagle_gather_rows(n_rows, row_elems, dt, _ptr(table), table.shape[0], _ptr(idx), _ptr(out),

@@ -80,8 +80,10 @@ class DeviceInputs:
 class DeviceRound:
     """Device buffers + the five entry points of one round for a config."""
 
-    def __init__(self, cfg, device="cuda", n=None, B=None, cap=None):
+    def __init__(self, cfg, device="cuda", n=None, B=None, cap=None, compact=False):
         self.cfg = c = cfg
+        # compact target rows (fp16 offsets + 128-column block maxima) instead of fp32 logits
+        self.compact = bool(compact)
         self.cap = cap or c.Lmax  # largest prefix-cache stride the workspace is sized for
         self.B = B = B or c.B
         self.N = N = n or c.N
@@ -105,7 +107,12 @@ class DeviceRound:
         self.vt = torch.zeros((B, N, c.hkv, c.dh), dtype=dt, device=device)
         self.x = torch.zeros((B, N, c.hq, c.dh), dtype=dt, device=device)
         self.feat = torch.zeros((B, c.D + 1, c.H), dtype=dt, device=device)
-        self.logits = torch.zeros((B * N, c.V), dtype=f32, device=device)
+        if self.compact:
+            self.logits = None
+            self.z16 = torch.zeros((B * N, c.V), dtype=torch.float16, device=device)
+            self.bmax = torch.zeros((B * N, (c.V + 127) // 128), dtype=f32, device=device)
+        else:
+            self.logits = torch.zeros((B * N, c.V), dtype=f32, device=device)
         self.stats = z(B * N, 2, dtype=f32)
         self.argmax = z(B * N)
         # sampling-warp outputs: bounds of the draft slot rows and of the target rows, warped target stats
@@ -168,6 +175,11 @@ class DeviceRound:
     def lmhead(self, wts, T):
         c = self.cfg
         w = wts.w_packed if wts.packed else wts.w
+        if self.compact:
+            ops.lmhead_softmax_compact(self.B * self.N, c.H, c.V, self.x.view(self.B * self.N, c.H), w, T, self.z16,
+                                       self.bmax, self.stats, self.argmax, self.ws, status=self.status,
+                                       packed=wts.packed)
+            return
         ops.lmhead_softmax(self.B * self.N, c.H, c.V, self.x.view(self.B * self.N, c.H), w, T, self.logits,
                            self.stats, self.argmax, self.ws, status=self.status, packed=wts.packed)
 
@@ -175,6 +187,13 @@ class DeviceRound:
         """warp = (top_k, top_p) with T > 0: the target rows are warped first, the draft rows were
         warped by expand (their bounds are reused)."""
         c = self.cfg
+        if self.compact:
+            if warp is not None:
+                raise ValueError("compact target rows take no sampling warp")
+            ops.verify_accept_compact(self.params(T, round_id, data.seed), c.S if self.static else 0, self.tree,
+                                      self.z16, self.bmax, self.stats, self.argmax, data.rows,
+                                      self.tree["slot_stats"], data.uniforms, self.acc, self.ws, self.status)
+            return
         if self.static:
             ops.verify_accept_static(self.params(T, round_id, data.seed), c.S, self.tree, self.logits, self.stats,
                                      self.argmax, data.rows, self.tree["slot_stats"], data.uniforms, self.acc,
@@ -215,7 +234,11 @@ class DeviceRound:
         out["mask"] = self.mask.cpu().numpy().view(np.uint64)
         out["pos"] = self.pos.cpu().numpy()
         out["x"] = self.x.float().cpu().numpy()
-        out["logits"] = self.logits.cpu().numpy()
+        if self.compact:
+            out["z16"] = self.z16.cpu().numpy()
+            out["bmax"] = self.bmax.cpu().numpy()
+        else:
+            out["logits"] = self.logits.cpu().numpy()
         out["stats"] = self.stats.cpu().numpy()
         out["argmax"] = self.argmax.cpu().numpy()
         out["status"] = int(self.status.item())

@@ -316,6 +316,28 @@ int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dt
  * shape or dtype has no packed form). */
 size_t eagle_lmhead_packed_bytes(int32_t vocab, int32_t hidden, int32_t dtype);
 
+/* eagle_lmhead_softmax without fp32 logit rows (bf16 only): every row is
+ * stored compact, 2 bytes per logit.  Source: [E1] A3 and 3.3 (one verify
+ * pass gives the target distribution at every tree node; the walk reads it at
+ * the candidates and, after a rejection, over the whole vocabulary).
+ * Out: target_z16 [rows, vocab] (fp16 bit patterns, 8-byte aligned): logit v
+ *        as fp16(z_v - m), m the largest finite logit of its 128-column block
+ *        (columns 128 b .. 128 b + 127), rounded to nearest even; -inf for a
+ *        non-finite logit or a block without a finite one;
+ *      block_max [rows, ceil(vocab / 128)] fp32: the block maxima m;
+ *      row_stats [rows, 2]: (max, sum exp) of the DECODED row
+ *        z~ = fp32(m + fp32(offset)) at T' (the block maxima decode exactly, so
+ *        the max equals eagle_lmhead_softmax's);
+ *      row_argmax [rows]: the first column holding the row's largest logit,
+ *        exactly as eagle_lmhead_softmax (computed from the fp32 logits).
+ * For tokens whose probability is at least 1e-6 of the row's largest, the
+ * decoded row's probabilities are within 1.4% of the fp32 row's.  Everything
+ * else (workspace, status) as eagle_lmhead_softmax. */
+int eagle_lmhead_softmax_compact(int32_t rows, int32_t hidden, int32_t vocab, const void* x, const void* w,
+                                 int32_t w_layout, float temperature, uint16_t* target_z16, float* block_max,
+                                 float* row_stats, int32_t* row_argmax, void* ws, size_t ws_bytes,
+                                 int32_t* dev_status, void* stream);
+
 /* Pack a row-major bf16 LM-head weight w [vocab, hidden] into w_packed
  * (eagle_lmhead_packed_bytes bytes, 16-byte aligned; rows past vocab are
  * zero-filled).  A one-time layout transform done when weights are loaded. */
@@ -358,6 +380,21 @@ int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok,
                         int32_t* accept_len, int32_t* accept_path, int32_t* committed,
                         int32_t* n_committed, int32_t* near_tie, void* ws, size_t ws_bytes,
                         int32_t* dev_status, void* stream);
+
+/* eagle_verify_accept on compact target rows (eagle_lmhead_softmax_compact):
+ * every target probability the walk uses (acceptance ratios, residual sums,
+ * draws) is exp(z~/T' - M) / S of the decoded row z~ with the statistics of
+ * that same row, so the walk samples exactly from the decoded distribution.
+ * n_slots = 0: a dynamic tree (S = 1 + (D - 1) k); n_slots > 0: a static
+ * tree of that many slots (eagle_expand_static).  No sampling warp.
+ * Everything else as eagle_verify_accept. */
+int eagle_verify_accept_compact(const eagle_tree_params* p, int32_t n_slots, const int32_t* node_tok,
+                                const int32_t* node_parent, const int32_t* node_slot, const int32_t* pool_tok,
+                                const int32_t* pool_flat, const uint16_t* target_z16, const float* block_max,
+                                const float* target_stats, const int32_t* target_argmax, const float* draft_logits,
+                                const float* slot_stats, const float* uniforms, int32_t* accept_len,
+                                int32_t* accept_path, int32_t* committed, int32_t* n_committed, int32_t* near_tie,
+                                void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
 
 /* eagle_verify_accept with both distributions warped (top-k / nucleus)
  * before the walk (T > 0; greedy ignores it).
