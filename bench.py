@@ -113,15 +113,18 @@ def setup(cfg_name, T, n_sets, device="cuda"):
 LM_EVENT_EVERY = 4  # LM-head launches bracketed by events: every 4th round (an event costs ~5 us of GPU idle)
 
 
-def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda", warp=None):
+def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda", warp=None, compact=False, dist=False):
     """Warm up, then time exactly `steps` rounds; within them, the LM-head
     launch of every LM_EVENT_EVERY-th round is timed with events on its stream.
     warp = (top_k, top_p): rounds with both distributions warped (the two row
-    warps run inside the timed rounds)."""
+    warps run inside the timed rounds).  compact: the LM head writes compact
+    rows and the walk reads them.  dist: a second pass of as many rounds, each
+    bracketed by its own events, gives the spread of the round time (p10, p50,
+    p90; the events add their own dispatch to every round of that pass)."""
     import torch
 
     from eagle_draft_tree_expand_amd import round as dround
-    dr = dround.DeviceRound(cfg, device)
+    dr = dround.DeviceRound(cfg, device, compact=compact)
     for i in range(warmup):
         dr.step(wts, sets[i % len(sets)], T, round_id=i, warp=warp)
     nev = (steps + LM_EVENT_EVERY - 1) // LM_EVENT_EVERY
@@ -149,6 +152,16 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda", warp=None):
     wall = time.perf_counter() - wall0
     total_ms = t_start.elapsed_time(t_end)
     lm_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    spread = None
+    if dist:
+        pe = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        for i in range(steps):
+            pe[i][0].record()
+            dr.step(wts, sets[i % len(sets)], T, round_id=i, warp=warp)
+            pe[i][1].record()
+        torch.cuda.synchronize()
+        per = np.array([a.elapsed_time(b) for a, b in pe])
+        spread = {q: round(float(np.percentile(per, int(q[1:]))), 4) for q in ("p10", "p50", "p90")}
     # committed tokens: replay the same rounds untimed (results are deterministic)
     committed = 0
     for i in range(steps):
@@ -156,7 +169,7 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda", warp=None):
         dr.step(wts, d, T, round_id=i, warp=warp)
         committed += int(dr.acc["n_committed"].sum().item())
     status = int(dr.status.item())
-    return dict(total_ms=total_ms, wall_s=wall, lm_ms=lm_ms, committed=committed, status=status)
+    return dict(total_ms=total_ms, wall_s=wall, lm_ms=lm_ms, committed=committed, status=status, spread=spread)
 
 
 def time_commit(cfg, wts, inp, rows, T, reps=40, device="cuda"):
@@ -265,29 +278,49 @@ def time_drafting(cfg, wts, inp, T, steps, warmup, device="cuda"):
     return out
 
 
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(cfg_name, T, inp, budget_s=25.0):
-    """The oracle, untuned, on a bounded sample: whole rounds of set 0 (pre-pass excluded)."""
-    from threadpoolctl import threadpool_info
+    """The oracle, untuned, on a bounded sample: whole rounds of set 0 (pre-pass excluded),
+    with the BLAS threads it starts with, then again with one thread."""
+    from threadpoolctl import threadpool_info, threadpool_limits
 
     from oracle import round as oround
     wts = oround._Weights(inp)
     t0 = time.time()
     rows = oround.target_draft_rows(inp, T, wts)
     prep = time.time() - t0
-    n, committed = 0, 0
-    t0 = time.time()
-    while True:
-        r = oround.run_round(inp, T, rows=rows, round_id=n, weights=wts)
-        committed += sum(a["n_committed"] for a in r["accept"])
-        n += 1
-        el = time.time() - t0
-        if el > budget_s * 0.5 or n >= 8:
-            break
+
+    def rounds(limit_s, max_n):
+        n, committed = 0, 0
+        t0 = time.time()
+        while True:
+            r = oround.run_round(inp, T, rows=rows, round_id=n, weights=wts)
+            committed += sum(a["n_committed"] for a in r["accept"])
+            n += 1
+            el = time.time() - t0
+            if el > limit_s or n >= max_n:
+                return n, committed, el
+
+    n, committed, el = rounds(budget_s * 0.5, 8)
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    log(f"[bench] oracle: pre-pass {prep:.1f}s, {n} rounds in {el:.1f}s")
+    with threadpool_limits(limits=1):
+        n1, c1, el1 = rounds(budget_s * 0.3, 3)
+    log(f"[bench] oracle: pre-pass {prep:.1f}s, {n} rounds in {el:.1f}s; one thread: {n1} rounds in {el1:.1f}s")
     return {"value": n * inp.cfg.B / el, "unit": "trees/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{n} whole rounds of the {cfg_name} workload (input set 0, round ids 0..{n - 1}), "
-                      f"draft-row pre-pass excluded; {committed / el:.3f} committed tokens/s"}
+                      f"draft-row pre-pass excluded; {committed / el:.3f} committed tokens/s",
+            "nproc": os.cpu_count(), "cpu_model": _cpu_model(),
+            "one_thread": {"value": round(n1 * inp.cfg.B / el1, 4), "unit": "trees/s", "rounds": n1,
+                           "committed_tokens_per_s": round(c1 / el1, 3)}}
 
 
 def main():
@@ -336,7 +369,7 @@ def main():
         return
 
     cfg, inps, wts, sets = setup(args.config, args.temp, args.sets)
-    r = time_rounds(cfg, wts, sets, args.temp, args.steps, args.warmup)
+    r = time_rounds(cfg, wts, sets, args.temp, args.steps, args.warmup, dist=True)
     ms = r["total_ms"] / args.steps
     rounds_s = 1000.0 / ms
     trees_s = rounds_s * cfg.B
@@ -374,7 +407,18 @@ def main():
                      "bytes_per_launch": lm_b,
                      "avg_launch_ms": round(r["lm_ms"], 5)},
         "device_status": r["status"],
+        "per_round_ms": dict(r["spread"], note="each round bracketed by its own events in a second pass"),
     }
+    if not args.no_extra:
+        # the same rounds with compact target rows (no fp32 logit rows)
+        cr = time_rounds(cfg, wts, sets, args.temp, args.steps, args.warmup, compact=True)
+        cms = cr["total_ms"] / args.steps
+        out["compact"] = {"rows": "fp16 offsets from 128-column block maxima; LM head and walk on them",
+                          "trees_per_s": round(1000.0 / cms * cfg.B, 2), "ms_per_step": round(cms, 4),
+                          "committed_tokens_per_s": round(cr["committed"] / (cr["total_ms"] / 1000.0), 1),
+                          "round_hbm_fraction": round((rb - rows * cfg.V * 2) / (cms / 1000.0) / 1e9 / HBM_PEAK_GBS,
+                                                      4),
+                          "lmhead_ms": round(cr["lm_ms"], 5), "device_status": cr["status"]}
     if not args.no_extra:
         out["commit"] = time_commit(cfg, wts, inps[0], sets[0].rows, args.temp)
     if not args.no_extra and args.temp > 0:
@@ -411,6 +455,28 @@ def main():
         out["draft"] = time_drafting(cfg, wts, inps[0], args.temp, max(10, args.steps // 10), 3)
         torch.cuda.empty_cache()
     if not args.no_extra and args.config == "8b":
+        # the other single-GPU shapes: 13B (MHA), the 70B layer share (T = 1 and greedy), tiny fp32
+        out["configs"] = {}
+        for name, T2 in (("13b", 1.0), ("70b", 1.0), ("70b", 0.0), ("tiny", 1.0)):
+            ocfg, _, owts, osets = setup(name, T2, 4)
+            osteps = max(20, args.steps // 2)
+            o = time_rounds(ocfg, owts, osets, T2, osteps, 5)
+            oms = o["total_ms"] / osteps
+            optot = int(sum(int(x.prefix_len.sum().item()) for x in osets) / len(osets))
+            orows = ocfg.B * ocfg.N
+            olb = lmhead_bytes(ocfg, orows)
+            out["configs"][f"{name}" + ("" if T2 > 0 else "_greedy")] = {
+                "workload": f"{ocfg.name}: hidden {ocfg.H}, {ocfg.hq}q/{ocfg.hkv}kv x {ocfg.dh}, prefix {ocfg.Lmax}, "
+                            f"vocab {ocfg.V}, depth {ocfg.D}, top-k {ocfg.k}, m {ocfg.m}, T={T2}, {ocfg.dtype}",
+                "trees_per_s": round(1000.0 / oms * ocfg.B, 2), "ms_per_step": round(oms, 4),
+                "committed_tokens_per_s": round(o["committed"] / (o["total_ms"] / 1000.0), 1),
+                "tau_synthetic": round(o["committed"] / (osteps * ocfg.B), 4),
+                "round_hbm_fraction": round(round_bytes(ocfg, optot) / (oms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                "lmhead_ms": round(o["lm_ms"], 5),
+                "lmhead_hbm_frac": round(olb / (o["lm_ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                "device_status": o["status"]}
+            del osets, owts
+    if not args.no_extra and args.config == "8b":
         gsteps = max(20, args.steps // 4)
         g = time_rounds(cfg, wts, sets, 0.0, gsteps, 5)
         out["greedy"] = {"trees_per_s": round(1000.0 * gsteps / g["total_ms"] * cfg.B, 2),
@@ -423,12 +489,20 @@ def main():
             b = time_rounds(cfg64, wts64, sets64, 1.0, 10, 2)
             ms64 = b["total_ms"] / 10
             flops = 2.0 * cfg64.B * cfg64.N * cfg64.H * cfg64.V
+            bc = time_rounds(cfg64, wts64, sets64, 1.0, 10, 2, compact=True)
+            msc = bc["total_ms"] / 10
+            b64_compact = {"trees_per_s": round(1000.0 / msc * cfg64.B, 1), "ms_per_round": round(msc, 3),
+                           "committed_tokens_per_s": round(bc["committed"] / (bc["total_ms"] / 1000.0), 1),
+                           "lmhead_ms": round(bc["lm_ms"], 4),
+                           "lmhead_mfma_frac": round(flops / (bc["lm_ms"] / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                           "device_status": bc["status"]}
             out["b64"] = {"trees_per_s": round(1000.0 / ms64 * cfg64.B, 1), "ms_per_round": round(ms64, 3),
                           "draft": time_drafting(cfg64, wts64, inps64[0], 1.0, 3, 1),
                           "committed_tokens_per_s": round(b["committed"] / (b["total_ms"] / 1000.0), 1),
                           "lmhead_ms": round(b["lm_ms"], 4),
                           "lmhead_mfma_frac": round(flops / (b["lm_ms"] / 1000.0) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                          "commit": time_commit(cfg64, wts64, inps64[0], sets64[0].rows, 1.0)}
+                          "commit": time_commit(cfg64, wts64, inps64[0], sets64[0].rows, 1.0),
+                          "compact": b64_compact}
             del sets64, wts64
         except Exception as e:  # report, do not hide the main line
             out["b64"] = {"error": repr(e)[:200]}
