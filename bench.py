@@ -136,8 +136,11 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda", warp=None, comp
     t_start.record()
     for i in range(steps):
         d = sets[i % len(sets)]
-        dr.expand(d, T, i, warp)
-        dr.mask_pos(d)
+        if warp is None and not dr.static:
+            dr.expand_masked(d, T, i)
+        else:
+            dr.expand(d, T, i, warp)
+            dr.mask_pos(d)
         dr.gather_qkv(wts)
         dr.attention(d)
         timed = i % LM_EVENT_EVERY == 0

@@ -24,7 +24,7 @@ STATUS_BITS = {0x1: "TOKEN_RANGE", 0x2: "NONFINITE", 0x4: "ZERO_RESIDUAL", 0x8: 
 EXPORTS = ("eagle_workspace_size", "eagle_workspace_init", "eagle_expand_tree", "eagle_build_tree_mask",
            "eagle_tree_attention", "eagle_lmhead_softmax", "eagle_verify_accept", "eagle_gather_rows",
            "eagle_gather_rows_multi", "eagle_commit_accepted", "eagle_sampling_warp",
-           "eagle_expand_tree_warped", "eagle_expand_tree_noalloc", "eagle_verify_accept_warped", "eagle_lmhead_packed_bytes",
+           "eagle_expand_tree_warped", "eagle_expand_tree_masked", "eagle_expand_tree_noalloc", "eagle_verify_accept_warped", "eagle_lmhead_packed_bytes",
            "eagle_lmhead_pack_weight", "eagle_draft_workspace_size", "eagle_draft_workspace_layout",
            "eagle_draft_forward", "eagle_expand_depth",
            "eagle_expand_finish", "eagle_static_tree_info", "eagle_static_workspace_size", "eagle_expand_static",
@@ -71,6 +71,8 @@ _SIGS = {
     "eagle_gather_rows_multi": (c_int32, [c_int32, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P]),
     "eagle_commit_accepted": (c_int32, [c_int32] * 8 + [_P] * 9 + [_P, _P]),
     "eagle_expand_tree_warped": (c_int32, [POINTER(TreeParams), _P, _P, _P] + [_P] * 7 + [_P] * 5 +
+                                 [_P, c_size_t, _P, _P]),
+    "eagle_expand_tree_masked": (c_int32, [POINTER(TreeParams), _P, _P, _P] + [_P] * 7 + [_P] * 5 + [_P, _P] +
                                  [_P, c_size_t, _P, _P]),
     "eagle_expand_tree_noalloc": (c_int32, [POINTER(TreeParams), _P, _P] + [_P] * 7 + [_P] * 5 + [_P, _P]),
     "eagle_verify_accept_warped": (c_int32, [POINTER(TreeParams), _P, _P] + [_P] * 16 + [_P, c_size_t, _P, _P]),

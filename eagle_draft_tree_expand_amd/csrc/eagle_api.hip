@@ -251,6 +251,28 @@ int eagle_expand_tree_warped(const eagle_tree_params* p, const float* draft_logi
                                      dev_status, (hipStream_t)stream));
 }
 
+int eagle_expand_tree_masked(const eagle_tree_params* p, const float* draft_logits, const int32_t* root_token,
+                             const int32_t* prefix_len, int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
+                             int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
+                             int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                             float* slot_stats, uint64_t* mask, int32_t* pos, void* ws, size_t ws_bytes,
+                             int32_t* dev_status, void* stream) {
+  int rc = check_tree_params(p);
+  if (rc != EAGLE_OK) return rc;
+  if (!draft_logits || !root_token || !prefix_len || !node_tok || !node_parent || !node_depth || !node_sib ||
+      !node_slot || !node_value || !node_q || !pool_tok || !pool_q || !pool_flat || !slot_src || !slot_stats ||
+      !mask || !pos || !ws)
+    return EAGLE_ERR_NULL;
+  if (!aligned16(draft_logits)) return EAGLE_ERR_ALIGN;
+  const int B = p->batch, V = p->vocab, k = p->topk, D = p->depth;
+  const int S = 1 + (D - 1) * k;
+  if (ws_bytes < kCounterBytes + exp_ws_bytes(B, S, V, k)) return EAGLE_ERR_WORKSPACE;
+  return launch_status(launch_expand(B, S, V, D, k, p->m, p->temperature, p->seed, p->round_id, draft_logits,
+                                     nullptr, root_token, node_tok, node_parent, node_depth, node_sib, node_slot,
+                                     node_value, node_q, pool_tok, pool_q, pool_flat, slot_src, slot_stats,
+                                     stage_area(ws), dev_status, (hipStream_t)stream, prefix_len, mask, pos));
+}
+
 int eagle_expand_tree_noalloc(const eagle_tree_params* p, const float* draft_logits, const int32_t* root_token,
                               int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
                               int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_tok,

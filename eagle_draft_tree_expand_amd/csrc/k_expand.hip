@@ -510,7 +510,8 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     const int32_t* __restrict__ pool_tok_g, const float* __restrict__ pool_q_g,
     int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
     int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_flat_g,
-    int32_t* slot_src_g, int32_t* status, int upto) {
+    int32_t* slot_src_g, int32_t* status, int upto, const int32_t* __restrict__ prefix_len,
+    uint64_t* __restrict__ mask_out, int32_t* __restrict__ pos_out) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int P = S * k, N = m + 1;
@@ -527,6 +528,8 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
   int* sel_e = slot_src + S;                                       // [m] pool index of each selected node
   int* sel_dep = sel_e + m;                                        // [m]
   int* ptok = sel_dep + m;                                         // [P] pool tokens, read with q up front
+  int* fpar = ptok + P;                                            // [N] flat parent (the mask, when asked for)
+  int* fdep = fpar + N;                                            // [N] depth
   __shared__ int n_sel;
 
   const float* pq = pool_q_g + (size_t)b * P;
@@ -538,6 +541,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
   }
   for (int x = tid; x < D * LS; x += nt) lay[x] = x < k ? node_key(pq[x], x) : 0ull;  // layer 1: value = 1 * q
   for (int x = tid; x < S; x += nt) slot_src[x] = -1;
+  for (int x = tid; x < N; x += nt) { fpar[x] = -1; fdep[x] = 0; }
   if (tid == 0) n_sel = 0;
   __syncthreads();
 
@@ -662,6 +666,8 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     }
     const int lr = lrank[e];
     const size_t o = (size_t)b * N + f;
+    fpar[f] = pf;
+    fdep[f] = de;
     node_tok[o] = ptok[e];
     node_parent[o] = pf;
     node_depth[o] = de;
@@ -684,6 +690,24 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     node_slot[o] = 0;
     node_value[o] = 1.f;
     node_q[o] = 1.f;
+  }
+  if (mask_out == nullptr) return;
+  // 4. The ancestor-only mask and positions of the flattened tree (the rows
+  // eagle_build_tree_mask writes): bit j of row f is set iff j is f or one of
+  // its ancestors; a node the selection left unset sees itself only.
+  __syncthreads();
+  const int W = (N + 63) >> 6;
+  const int L = prefix_len[b];
+  for (int f = tid; f < N; f += nt) {
+    uint64_t w[(EAGLE_MAX_NODES + 63) / 64] = {0ull, 0ull, 0ull, 0ull};
+    int a = f;
+    for (int step = 0; a >= 0 && step <= D; ++step) {
+      w[a >> 6] |= 1ull << (a & 63);
+      a = a == 0 ? -1 : fpar[a];
+    }
+    uint64_t* row = mask_out + ((size_t)b * N + f) * W;
+    for (int x = 0; x < W; ++x) row[x] = w[x];
+    pos_out[(size_t)b * N + f] = L + fdep[f];
   }
 }
 
@@ -791,14 +815,15 @@ hipError_t launch_assemble(int B, int S, int V, int D, int k, int m, int upto, c
                            int32_t* node_tok, int32_t* node_parent, int32_t* node_depth, int32_t* node_sib,
                            int32_t* node_slot, float* node_value, float* node_q, const int32_t* pool_tok,
                            const float* pool_q, int32_t* pool_flat, int32_t* slot_src, int32_t* status,
-                           hipStream_t st) {
+                           hipStream_t st, const int32_t* prefix_len = nullptr, uint64_t* mask = nullptr,
+                           int32_t* pos = nullptr) {
   const int P = S * k;
   const size_t LS = (size_t)((k * k + 1) & ~1);
   const size_t sm3 = (2 * (size_t)D * LS + S + 2 * (size_t)m) * 8 + (size_t)P * 3 * 4 + (size_t)S * 4 +
-                     (size_t)m * 2 * 4 + (size_t)P * 4;
+                     (size_t)m * 2 * 4 + (size_t)P * 4 + 2 * (size_t)(m + 1) * 4;
   tree_assemble_kernel<<<B, kTreeThreads, sm3, st>>>(S, k, D, m, V, root, pool_tok, pool_q, node_tok, node_parent,
                                                      node_depth, node_sib, node_slot, node_value, node_q, pool_flat,
-                                                     slot_src, status, upto);
+                                                     slot_src, status, upto, prefix_len, mask, pos);
   return hipGetLastError();
 }
 
@@ -809,12 +834,14 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
                          int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
                          int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
                          int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
-                         float* slot_stats, float* ws_units, int32_t* status, hipStream_t st) {
+                         float* slot_stats, float* ws_units, int32_t* status, hipStream_t st,
+                         const int32_t* prefix_len, uint64_t* mask, int32_t* pos) {
   hipError_t e = launch_children(B, S, V, k, T, seed, round_id, rows, bound, pool_tok, pool_q, slot_stats, ws_units,
                                  status, SlotRange{0, S}, st);
   if (e != hipSuccess) return e;
   return launch_assemble(B, S, V, D, k, m, D, root, node_tok, node_parent, node_depth, node_sib, node_slot,
-                         node_value, node_q, pool_tok, pool_q, pool_flat, slot_src, status, st);
+                         node_value, node_q, pool_tok, pool_q, pool_flat, slot_src, status, st, prefix_len, mask,
+                         pos);
 }
 
 hipError_t launch_expand_depth(int B, int S, int V, int D, int k, int m, float T, uint64_t seed, uint64_t round_id,

@@ -27,7 +27,8 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
                          int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
                          int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
                          int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
-                         float* slot_stats, float* ws_units, int32_t* status, hipStream_t st);
+                         float* slot_stats, float* ws_units, int32_t* status, hipStream_t st,
+                         const int32_t* prefix_len = nullptr, uint64_t* mask = nullptr, int32_t* pos = nullptr);
 
 // Depth by depth: children of depth `depth`'s frontier slots (rows at their
 // slots of the [B, S, V] buffer), then the next depth's frontier into slot_src.

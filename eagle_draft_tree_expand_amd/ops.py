@@ -56,6 +56,18 @@ def expand_tree(p: TreeParams, draft_logits, root_token, out, ws, status=None, d
     check("eagle_expand_tree_warped" if draft_bound is not None else "eagle_expand_tree", rc)
 
 
+def expand_tree_masked(p: TreeParams, draft_logits, root_token, prefix_len, out, mask, pos, ws, status=None):
+    """expand_tree and build_tree_mask in one call (the assembly writes the mask and positions)."""
+    assert draft_logits.dtype == torch.float32 and draft_logits.is_contiguous()
+    rc = _lib.load().eagle_expand_tree_masked(
+        p, _ptr(draft_logits), _ptr(root_token), _ptr(prefix_len),
+        _ptr(out["node_tok"]), _ptr(out["node_parent"]), _ptr(out["node_depth"]), _ptr(out["node_sib"]),
+        _ptr(out["node_slot"]), _ptr(out["node_value"]), _ptr(out["node_q"]),
+        _ptr(out["pool_tok"]), _ptr(out["pool_q"]), _ptr(out["pool_flat"]), _ptr(out["slot_src"]),
+        _ptr(out["slot_stats"]), _ptr(mask), _ptr(pos), _ptr(ws), ws.numel(), _ptr(status), _stream())
+    check("eagle_expand_tree_masked", rc)
+
+
 def expand_tree_noalloc(p: TreeParams, draft_logits, root_token, out, status=None):
     """eagle_expand_tree without a workspace: the library's static scratch holds the records."""
     assert draft_logits.dtype == torch.float32 and draft_logits.is_contiguous()

@@ -217,11 +217,21 @@ class DeviceRound:
                             self.acc["accept_path"], self.kt, self.vt, self.x, data.k_prefix, data.v_prefix,
                             data.prefix_len, self.feat, self.status)
 
+    def expand_masked(self, data, T, round_id=0):
+        """expand + mask_pos in one call (dynamic trees without a warp)."""
+        ops.expand_tree_masked(self.params(T, round_id, data.seed), data.rows, data.roots, data.prefix_len,
+                               self.tree, self.mask, self.pos, self.ws, self.status)
+
     def step(self, wts, data, T, round_id=0, warp=None):
-        """One whole round (all five entry points, plus the q/k/v row gathers; with a
-        sampling warp, also the two row warps)."""
-        self.expand(data, T, round_id, warp)
-        self.mask_pos(data)
+        """One whole round (the expansion with the mask written by its assembly step,
+        the q/k/v row gathers, attention, LM head, acceptance; with a sampling warp or
+        a static tree, the expansion and the mask are separate calls, and a warp
+        adds the two row warps)."""
+        if warp is None and not self.static:
+            self.expand_masked(data, T, round_id)
+        else:
+            self.expand(data, T, round_id, warp)
+            self.mask_pos(data)
         self.gather_qkv(wts)
         self.attention(data)
         self.lmhead(wts, T)

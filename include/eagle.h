@@ -186,6 +186,20 @@ int eagle_expand_tree_warped(const eagle_tree_params* p, const float* draft_logi
                              float* node_q, int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
                              float* slot_stats, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream);
 
+/* eagle_expand_tree followed by eagle_build_tree_mask in one call: the
+ * assembly step, which already holds the flattened tree, also writes the
+ * ancestor-only mask [B, N, ceil(N/64)] and the positions [B, N]
+ * (prefix_len[b] + depth), bit for bit what eagle_build_tree_mask writes for
+ * the tree it returns.  Source: [E2] "Tree Attention Mask" (flatten the tree
+ * and mask it to ancestors).  One launch fewer per round.  No sampling warp.
+ * Everything else as eagle_expand_tree. */
+int eagle_expand_tree_masked(const eagle_tree_params* p, const float* draft_logits, const int32_t* root_token,
+                             const int32_t* prefix_len, int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
+                             int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
+                             int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
+                             float* slot_stats, uint64_t* mask, int32_t* pos, void* ws, size_t ws_bytes,
+                             int32_t* dev_status, void* stream);
+
 /* eagle_expand_tree for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc): no `ws` argument; the expansion's candidate records go to a

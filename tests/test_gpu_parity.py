@@ -82,6 +82,33 @@ def test_expand_full_vocab_8b_rows(rt):
         assert compare_expand(dev, ora, cfg.k, f"8b T={T}") == 0
 
 
+@pytest.mark.parametrize("name,kw,T", [("mid_bf16", {}, 1.0), ("mid_bf16", dict(V=1000, k=8, D=8, m=200), 0.0),
+                                       ("8b", {}, 1.0)])
+def test_expand_masked_equals_separate_calls(rt, name, kw, T):
+    """eagle_expand_tree_masked (mask and positions written by the assembly) equals
+    eagle_expand_tree followed by eagle_build_tree_mask, bit for bit."""
+    cfg = small_cfg(name, **kw)
+    inp = synth.make_inputs(cfg)
+    rows = inp.iid_draft_rows()
+    sep = rt.DeviceRound(cfg)
+    fused = rt.DeviceRound(cfg)
+    data = _dev(rt, cfg, inp, rows)
+    sep.expand(data, T, round_id=1)
+    sep.mask_pos(data)
+    fused.mask.fill_(-1)
+    fused.pos.fill_(-7)
+    fused.expand_masked(data, T, round_id=1)
+    a, b = sep.host(), fused.host()
+    for key in list(sep.tree) + ["mask", "pos", "status"]:
+        assert np.array_equal(np.asarray(a[key]).view(np.uint8) if isinstance(a[key], np.ndarray) else a[key],
+                              np.asarray(b[key]).view(np.uint8) if isinstance(b[key], np.ndarray) else b[key]), key
+    ora = oexpand.expand_batch(rows, inp.roots, T, cfg.k, cfg.D, cfg.m, inp.gumbel_seed, 1)
+    for bb in range(cfg.B):
+        assert np.array_equal(b["mask"][bb], omask.pack_bits(omask.ancestor_mask(b["node_parent"][bb])))
+        assert np.array_equal(b["pos"][bb], omask.positions(b["node_depth"][bb], inp.prefix_len[bb]))
+    assert compare_expand(b, ora, cfg.k, f"masked {name}") <= max(1, cfg.B // 4)
+
+
 def test_expand_is_deterministic(rt):
     cfg = small_cfg("mid_bf16")
     inp = synth.make_inputs(cfg)
