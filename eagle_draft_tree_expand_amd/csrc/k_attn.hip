@@ -30,7 +30,6 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kKT = 64;            // keys per LDS tile
-constexpr int kQT = 2;             // 16-row query tiles per wave
 
 union B8 {
   bf16x8 v;
@@ -43,9 +42,10 @@ EDEV float* partial_row(float* ws, int b, int g, int hkv, int nsp1, int split, i
   return ws + ((((size_t)b * hkv + g) * nsp1 + split) * rows_pad + r) * (DH + 2);
 }
 
-// NTH threads: 512 (8 waves, 256 query rows) or, for few rows, 256 (4 waves,
-// 128 rows), so that two workgroups share a CU and hide each other's loads.
-template <int DH, int NTH>
+// NTH threads (256: 4 waves, 512: 8 waves), each wave kQT 16-row query
+// tiles; a (request, kv head, split) with more query rows than one workgroup
+// holds is covered by several row blocks, which read the same K/V tiles.
+template <int DH, int NTH, int kQT>
 __global__ __launch_bounds__(NTH) __attribute__((amdgpu_waves_per_eu(512 / NTH))) void attn_split_bf16_kernel(
     int n, int hq, int hkv, int Lmax, const uint16_t* __restrict__ q, const uint16_t* __restrict__ kp,
     const uint16_t* __restrict__ vp, const int32_t* __restrict__ plen, const uint16_t* __restrict__ kt,
@@ -464,9 +464,20 @@ AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, 
   // best (13B- and 70B-shaped rounds at batch 1: 49 and 38 us against 69 and
   // 48 us with the rule above); shorter splits write more partial rows, longer
   // ones leave CUs idle.
-  if (per <= 64 && max_prefix > 2048) sk = 384;
+  if (per <= 64 && max_prefix >= 2048) sk = 384;
   pl.split_keys = sk;
   pl.nsplit = (max_prefix + sk - 1) / sk;
+  // Row blocks: 64 rows (4 waves x one 16-row tile), 128 (4 x two) or 256
+  // (8 x two).  The smallest block whose grid still fits one pass over the
+  // 256 CUs wins (batch-1 8B: 64-row blocks, 20 against 25 us for one 256-row
+  // block; 70B: 256-row blocks, 32 against 41 us with 64); grids past one pass
+  // take the smallest block that holds all rows of a kv head (13B MHA: 64),
+  // else 256 (batch 64: 370 against 520 us with 64-row blocks).
+  const int pairs = B * hkv * (pl.nsplit + 1);
+  const int nb64 = (pl.rows + 63) / 64, nb128 = (pl.rows + 127) / 128;
+  if (pairs * nb64 <= 256 || pl.rows <= 64) { pl.threads = 256; pl.qt = 1; }
+  else if (pairs * nb128 <= 256 || pl.rows <= 128) { pl.threads = 256; pl.qt = 2; }
+  else { pl.threads = 512; pl.qt = 2; }
   (void)head_dim;
   (void)dtype;
   return pl;
@@ -485,22 +496,26 @@ hipError_t launch_attention_window(int B, int n, int nq, int qoff, int hq, int h
                                    const AttnPlan& pl, int32_t* status, hipStream_t st) {
   (void)status;
   if (dtype == EAGLE_BF16) {
-    const int threads = pl.rows <= 128 ? 256 : 512;
-    const int rows_wg = threads / 64 * kQT * 16;
+    const int threads = pl.threads == 256 ? 256 : 512, qt = pl.qt == 1 ? 1 : 2;
+    const int rows_wg = threads / 64 * qt * 16;
     const int nrb = (pl.rows + rows_wg - 1) / rows_wg;
     dim3 grid(pl.nsplit + 1, hkv * nrb, B);
-#define EAGLE_ATTN_BF16(D, T)                                                                                        \
-  attn_split_bf16_kernel<D, T><<<grid, T, 0, st>>>(n, hq, hkv, Lmax, (const uint16_t*)q, (const uint16_t*)kp,       \
-                                                   (const uint16_t*)vp, plen, (const uint16_t*)kt,                  \
-                                                   (const uint16_t*)vt, mask, scale, ws, pl.rows, pl.rows_pad,      \
-                                                   pl.split_keys, pl.nsplit, nq, qoff)
+#define EAGLE_ATTN_BF16(D, T, Q)                                                                                     \
+  attn_split_bf16_kernel<D, T, Q><<<grid, T, 0, st>>>(n, hq, hkv, Lmax, (const uint16_t*)q, (const uint16_t*)kp,    \
+                                                      (const uint16_t*)vp, plen, (const uint16_t*)kt,               \
+                                                      (const uint16_t*)vt, mask, scale, ws, pl.rows, pl.rows_pad,   \
+                                                      pl.split_keys, pl.nsplit, nq, qoff)
+#define EAGLE_ATTN_BF16_T(D)                    \
+  if (threads == 256 && qt == 1) EAGLE_ATTN_BF16(D, 256, 1); \
+  else if (threads == 256) EAGLE_ATTN_BF16(D, 256, 2);      \
+  else if (qt == 1) EAGLE_ATTN_BF16(D, 512, 1);             \
+  else EAGLE_ATTN_BF16(D, 512, 2);
     if (DH == 64) {
-      if (threads == 256) EAGLE_ATTN_BF16(64, 256);
-      else EAGLE_ATTN_BF16(64, 512);
+      EAGLE_ATTN_BF16_T(64)
     } else {
-      if (threads == 256) EAGLE_ATTN_BF16(128, 256);
-      else EAGLE_ATTN_BF16(128, 512);
+      EAGLE_ATTN_BF16_T(128)
     }
+#undef EAGLE_ATTN_BF16_T
 #undef EAGLE_ATTN_BF16
   } else {
     dim3 grid(pl.nsplit + 1, hkv, B);

@@ -13,7 +13,9 @@
 //   expand_scan   grid (ceil(V/4096), B*S), 256 threads.  One pass over 4096
 //                 logits of one slot row: per-wave (max, sum exp) of t = z/T'
 //                 and the wave's k+2 best candidates by an fp32 key (greedy:
-//                 z; sampling: t + Gumbel noise from Philox).  HBM-bound.
+//                 z; sampling: t + Gumbel noise from Philox).  Bound by its
+//                 VALU work (Philox, two logarithms and an exponential per
+//                 logit when sampling), not by the row reads.
 //   expand_merge  grid B*S, 256 threads.  Merges the wave records of a row:
 //                 M, S (fp64 sum), exact fp64 keys of the candidates, the k
 //                 best in sampling order, their confidences q.  Proves that
@@ -22,6 +24,8 @@
 //   tree_assemble grid B, 1024 threads, all state in LDS.  Values, frontier
 //                 ranks per layer, rerank of the pool by merging per-layer
 //                 sorted lists, BFS flattening.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 #include "philox.h"
@@ -516,16 +520,17 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
   const int b = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int P = S * k, N = m + 1;
   const int LS = (k * k + 1) & ~1;                                 // layer stride (keys), even
-  uint64_t* lay = reinterpret_cast<uint64_t*>(smem_raw);          // [D][LS] keys in pool order, 0 padded
-  uint64_t* skeys = lay + D * LS;                                  // [D][LS] keys sorted desc
-  uint64_t* spath = skeys + D * LS;                                // [S] path of the node at each slot
-  uint64_t* sel_key = spath + S;                                   // [m] (depth, path) of each selected node
+  // [D][LS] keys in pool order, 0 padded; then 2 zero keys and 32 write sinks
+  uint64_t* lay = reinterpret_cast<uint64_t*>(smem_raw);
+  uint64_t* skeys = lay + D * LS + 2 + 32;                         // [D][LS] keys sorted desc
+  uint64_t* spath = skeys + D * LS;                                // [S + 1] path of the node at each slot; sink
+  uint64_t* sel_key = spath + S + 1;                               // [m] (depth, path) of each selected node
   uint64_t* sel_key2 = sel_key + m;                                // [m] path alone (deep trees)
   float* q = reinterpret_cast<float*>(sel_key2 + m);               // [P]
   int* lrank = reinterpret_cast<int*>(q + P);                      // [P] rank inside the layer
   int* flat_of = lrank + P;                                        // [P] flat index or -1
-  int* slot_src = flat_of + P;                                     // [S]
-  int* sel_e = slot_src + S;                                       // [m] pool index of each selected node
+  int* slot_src = flat_of + P;                                     // [S + 1] frontier node of each slot; sink
+  int* sel_e = slot_src + S + 1;                                   // [m] pool index of each selected node
   int* sel_dep = sel_e + m;                                        // [m]
   int* ptok = sel_dep + m;                                         // [P] pool tokens, read with q up front
   int* fpar = ptok + P;                                            // [N] flat parent (the mask, when asked for)
@@ -539,56 +544,130 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     q[e] = qe;
     flat_of[e] = -1;
   }
-  for (int x = tid; x < D * LS; x += nt) lay[x] = x < k ? node_key(pq[x], x) : 0ull;  // layer 1: value = 1 * q
+  for (int x = tid; x < D * LS + 2; x += nt) lay[x] = x < k ? node_key(pq[x], x) : 0ull;  // layer 1: value = 1 * q
   for (int x = tid; x < S; x += nt) slot_src[x] = -1;
   for (int x = tid; x < N; x += nt) { fpar[x] = -1; fdep[x] = 0; }
   if (tid == 0) n_sel = 0;
   __syncthreads();
 
   // 1. Layers (1..upto; upto < D: only the frontiers up to depth upto are
-  // wanted, while the tree is still being drafted depth by depth).
-  for (int d = 1; d <= upto; ++d) {
-    const int lo = layer_lo(d, k), n = layer_n(d, k), dl = d - 1;
-    const uint64_t* L = lay + dl * LS;
-    // threads per node: a lane group of 2^lt <= 16 lanes that fits the block
-    const int lt = n * 16 <= nt ? 4 : n * 8 <= nt ? 3 : n * 4 <= nt ? 2 : n * 2 <= nt ? 1 : 0;
-    const int tpe = 1 << lt;
-    const int x = tid >> lt, part = tid & (tpe - 1);
-    if (x < n) {
-      const uint64_t K = L[x];
-      const int n2 = (n + 1) >> 1;
-      int r = 0;
-#pragma unroll 4
-      for (int y2 = part; y2 < n2; y2 += tpe) {
-        const ulonglong2 w = reinterpret_cast<const ulonglong2*>(L)[y2];
-        r += (w.x > K ? 1 : 0) + (w.y > K ? 1 : 0);
+  // wanted, while the tree is still being drafted depth by depth).  A lane
+  // group of 2^lt lanes ranks two nodes of the layer: each key pair it reads
+  // is compared with both, and every read of the step (the key pairs and the
+  // paths of the two nodes' parents) is issued before the first wait, so a
+  // step costs one barrier and two LDS round trips (the keys, then the q of
+  // the new frontier's children).  The step is latency-bound: one wave's
+  // instruction stream per step is what the loop keeps short.
+  // x / k == (x * kdiv) >> 16 for every x < 65536 / k (here x < 4096)
+  const uint32_t kdiv = __builtin_amdgcn_readfirstlane(65536u / (uint32_t)k + 1u);
+  auto div_k = [&](int x) __attribute__((always_inline)) {
+    uint32_t r;
+    asm("v_mul_u32_u24 %0, %1, %2" : "=v"(r) : "v"((uint32_t)x), "s"(kdiv));
+    return (int)(r >> 16);
+  };
+  const uint32_t ku = __builtin_amdgcn_readfirstlane((uint32_t)k);
+  auto mul_k = [&](int x) __attribute__((always_inline)) {  // x * k for 0 <= x < 2^24
+    uint32_t r;
+    asm("v_mul_u32_u24 %0, %1, %2" : "=v"(r) : "v"((uint32_t)x), "s"(ku));
+    return (int)r;
+  };
+  const ulonglong2* Z2 = reinterpret_cast<const ulonglong2*>(lay + D * LS);  // a pair of zero keys
+  uint64_t* sink = lay + D * LS + 2;                                          // 32 keys nobody reads
+  // One layer step.  FAST (k <= 11): every layer has at most 61 node pairs,
+  // so every step takes 16-lane groups and one chunk of four key pairs, and
+  // the writes go without branches (lanes with nothing to write store to
+  // the sinks).
+  auto step = [&](auto fast_tag, int d) __attribute__((always_inline)) {
+    constexpr bool FAST = decltype(fast_tag)::value;
+    const int lo = layer_lo(d, k), n = layer_n(d, k), np = (n + 1) >> 1, dl = d - 1;
+    const ulonglong2* L2 = reinterpret_cast<const ulonglong2*>(lay + dl * LS);  // pairs; LS is even
+    const int lt = FAST ? 4 : np * 16 <= nt ? 4 : np * 8 <= nt ? 3 : np * 4 <= nt ? 2 : np * 2 <= nt ? 1 : 0;
+    const int tpe = 1 << lt, p1 = tpe > 1 ? 1 : 0;
+    const int g = tid >> lt, part = tid & (tpe - 1);
+    if (g >= np) return;
+    const int x0 = 2 * g, x1 = x0 + 1;
+    const bool has1 = x1 < n;
+    // parents' slots and the nodes' sibling ranks (layer 1: the root, slot 0)
+    const int q0 = div_k(x0), q1 = div_k(x1);
+    const int ps0 = d == 1 ? 0 : 1 + (d - 2) * k + q0, ps1 = d == 1 ? 0 : 1 + (d - 2) * k + q1;
+    const uint64_t pp0 = spath[ps0], pp1 = spath[has1 ? ps1 : ps0];
+    const ulonglong2 own = L2[g];  // nodes x0, x1 (a key of 0 past the layer's end)
+    const uint64_t K0 = own.x, K1 = own.y;
+    int r0 = 0, r1 = 0;
+    const int T = FAST ? 1 : (np + tpe - 1) >> lt;  // chunks of four key pairs per lane (FAST: np <= 64)
+    for (int i0 = 0; i0 < (FAST ? 4 : T); i0 += 4) {
+      ulonglong2 w[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int y2 = part + (i0 + u) * tpe;
+        w[u] = *(y2 < np ? L2 + y2 : Z2);
       }
-      // sum over the node's lane group (aligned, inside one DPP row)
-      if (lt >= 1) r += dpp_i<kDppXor1>(r);
-      if (lt >= 2) r += dpp_i<kDppXor2>(r);
-      if (lt >= 3) r += dpp_i<kDppHalfMirror>(r);
-      if (lt >= 4) r += dpp_i<kDppMirror>(r);
-      const int e = lo + x;
-      if (part == 0) {
-        lrank[e] = r;
-        skeys[dl * LS + r] = K;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        r0 += (w[u].x > K0 ? 1 : 0) + (w[u].y > K0 ? 1 : 0);
+        r1 += (w[u].x > K1 ? 1 : 0) + (w[u].y > K1 ? 1 : 0);
       }
-      if (d < D && r < k) {  // frontier: slot 1 + (d-1)k + r, children in the next layer
-        const int slot = 1 + dl * k + r;
-        if (part == 0) {
-          slot_src[slot] = e;
-          spath[slot] = d == 1 ? (uint64_t)x : ((spath[e / k] << 4) | (uint64_t)(e % k));
-        }
-        const float v = key_value(K);
+    }
+    (void)T;
+    // the parents' paths were read with the keys: keep their loads up there
+    // (left to itself the compiler sinks them below the sums, a second wait)
+    asm volatile("" ::"v"(pp0), "v"(pp1));
+    // sums over the pair's lane group (aligned, inside one DPP row)
+    if (FAST || lt >= 1) { r0 += dpp_i<kDppXor1>(r0); r1 += dpp_i<kDppXor1>(r1); }
+    if (FAST || lt >= 2) { r0 += dpp_i<kDppXor2>(r0); r1 += dpp_i<kDppXor2>(r1); }
+    if (FAST || lt >= 3) { r0 += dpp_i<kDppHalfMirror>(r0); r1 += dpp_i<kDppHalfMirror>(r1); }
+    if (FAST || lt >= 4) { r0 += dpp_i<kDppMirror>(r0); r1 += dpp_i<kDppMirror>(r1); }
+    const bool f0 = d < D && r0 < k, f1 = d < D && has1 && r1 < k;
+    const int s0 = 1 + dl * k + r0, s1 = 1 + dl * k + r1;
+    // lane 0 records node x0, lane p1 node x1: its layer rank, its key in
+    // sorted order and, for a frontier node, its slot's source and path
+    auto record = [&](int x, int r, uint64_t K, uint64_t pp, int qx, bool f, int sl) __attribute__((always_inline)) {
+      lrank[lo + x] = r;
+      skeys[dl * LS + r] = K;
+      const int ss = f ? sl : S;
+      slot_src[ss] = lo + x;
+      spath[ss] = d == 1 ? (uint64_t)x : ((pp << 4) | (uint64_t)(x - mul_k(qx)));
+    };
+    if (FAST) {
+      if (part < 2 && (part == 0 || has1)) {
+        const bool one = part == 1;
+        record(one ? x1 : x0, one ? r1 : r0, one ? K1 : K0, one ? pp1 : pp0, one ? q1 : q0, one ? f1 : f0,
+               one ? s1 : s0);
+      }
+      // the frontier's children: lane j writes child j of each frontier node
+      const int j = part;
+      const bool a0 = f0 && j < k, a1 = f1 && j < k;
+      const int rk0 = mul_k(r0) + j, rk1 = mul_k(r1) + j;  // child index inside the next layer
+      const int c0 = lo + n + rk0, c1 = lo + n + rk1;        // its pool index: the next layer starts at lo + n
+      const float qa = q[a0 ? c0 : 0], qb = q[a1 ? c1 : 0];
+      uint64_t* Ln = lay + (d < D ? d : 0) * LS;
+      *(a0 ? Ln + rk0 : sink + 2 * part) = node_key(key_value(K0) * qa, c0);
+      *(a1 ? Ln + rk1 : sink + 2 * part + 1) = node_key(key_value(K1) * qb, c1);
+    } else {
+      if (part == 0) record(x0, r0, K0, pp0, q0, f0, s0);
+      if (part == p1 && has1) record(x1, r1, K1, pp1, q1, f1, s1);
+      if (f0 || f1) {
         uint64_t* Ln = lay + d * LS;
-#pragma unroll 4
+        const float v0 = key_value(K0), v1 = key_value(K1);
         for (int j = part; j < k; j += tpe) {
-          const int c = slot * k + j;
-          Ln[r * k + j] = node_key(v * q[c], c);
+          const int c0 = s0 * k + j, c1 = s1 * k + j;
+          const float qa = q[f0 ? c0 : 0], qb = q[f1 ? c1 : 0];
+          if (f0) Ln[r0 * k + j] = node_key(v0 * qa, c0);
+          if (f1) Ln[r1 * k + j] = node_key(v1 * qb, c1);
         }
       }
     }
-    __syncthreads();
+  };
+  if (k <= 11) {
+    for (int d = 1; d <= upto; ++d) {
+      step(std::true_type{}, d);
+      __syncthreads();
+    }
+  } else {
+    for (int d = 1; d <= upto; ++d) {
+      step(std::false_type{}, d);
+      __syncthreads();
+    }
   }
 
   if (upto < D) {
@@ -596,39 +675,50 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     return;
   }
 
-  // 2. Rerank.
+  // 2. Rerank.  A candidate's global rank is its layer rank plus, for every
+  // other layer, the count of larger keys there (a binary search of that
+  // layer's sorted keys).  Two lanes per candidate, each searching every
+  // other layer, four searches interleaved.
   const int c1 = min(m, k), cm = min(m, k * k);
   const int ncand = c1 + (D - 1) * cm;
   const int iters = 32 - __clz(cm);  // halvings that cover a prefix of cm keys
-  for (int c = tid; c < ncand; c += nt) {
+  for (int c2 = tid; c2 < 2 * ncand; c2 += nt) {  // nt is even: both lanes of a candidate take the same trip
+    const int c = c2 >> 1, h = c2 & 1;
     const int dc = c < c1 ? 0 : 1 + (c - c1) / cm;
     const int r = c < c1 ? c : (c - c1) - (dc - 1) * cm;
     const uint64_t K = skeys[dc * LS + r];
-    int g = r;
-    for (int d0 = 0; d0 < D; d0 += 2) {  // two layers' searches interleaved
-      const int d1 = d0 + 1;
-      const int len0 = d0 == dc ? 0 : (d0 == 0 ? c1 : cm);
-      const int len1 = (d1 >= D || d1 == dc) ? 0 : cm;
-      const uint64_t* A = skeys + d0 * LS;
-      const uint64_t* B2 = skeys + (d1 < D ? d1 : d0) * LS;
-      int lo0 = 0, hi0 = len0, lo1 = 0, hi1 = len1;
-      for (int it = 0; it < iters; ++it) {
-        const int m0 = (lo0 + hi0) >> 1, m1 = (lo1 + hi1) >> 1;
-        const bool a0 = lo0 < hi0, a1 = lo1 < hi1;
-        const bool b0 = A[a0 ? m0 : 0] > K, b1 = B2[a1 ? m1 : 0] > K;
-        lo0 = (a0 && b0) ? m0 + 1 : lo0;
-        hi0 = (a0 && !b0) ? m0 : hi0;
-        lo1 = (a1 && b1) ? m1 + 1 : lo1;
-        hi1 = (a1 && !b1) ? m1 : hi1;
+    int above = 0;
+    for (int d0 = h; d0 < D; d0 += 8) {
+      int lo_[4], hi_[4];
+      const uint64_t* A_[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int d = d0 + 2 * u;
+        lo_[u] = 0;
+        hi_[u] = (d >= D || d == dc) ? 0 : (d == 0 ? c1 : cm);
+        A_[u] = skeys + (d < D ? d : 0) * LS;
       }
-      g += lo0 + lo1;
+      for (int it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int mid = (lo_[u] + hi_[u]) >> 1;
+          const bool act = lo_[u] < hi_[u];
+          const bool gt = A_[u][act ? mid : 0] > K;
+          lo_[u] = (act && gt) ? mid + 1 : lo_[u];
+          hi_[u] = (act && !gt) ? mid : hi_[u];
+        }
+      }
+      above += lo_[0] + lo_[1] + lo_[2] + lo_[3];
     }
-    if (g < m) {
+    above += dpp_i<kDppXor1>(above);
+    const int grank = r + above;
+    if (h == 0 && grank < m) {
       const int i = atomicAdd(&n_sel, 1);
       if (i < m) {
         const int e = key_node(K);
         const int de = dc + 1;
-        const uint64_t path = de == 1 ? (uint64_t)e : ((spath[e / k] << 4) | (uint64_t)(e % k));
+        const int ps = div_k(e);
+        const uint64_t path = de == 1 ? (uint64_t)e : ((spath[ps] << 4) | (uint64_t)(e - ps * k));
         sel_e[i] = e;
         sel_dep[i] = de;
         sel_key[i] = D < 16 ? (((uint64_t)de << 60) | path) : (uint64_t)de;
@@ -638,21 +728,22 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
   }
   __syncthreads();
 
-  // 3. Flatten.
+  // 3. Flatten: a node's flat index is 1 + the count of selected keys below
+  // its own; 16 lanes per node.
   const int cnt = n_sel < m ? n_sel : m;
-  for (int i = tid; i < cnt; i += nt) {
-    const uint64_t key = sel_key[i];
+  for (int t = tid; t < cnt * 16; t += nt) {
+    const int i = t >> 4, part = t & 15;
+    const uint64_t key = sel_key[i], key2 = sel_key2[i];
     int r = 0;
-    if (D < 16) {  // depth and path fit one word
-      for (int j = 0; j < cnt; ++j) r += sel_key[j] < key ? 1 : 0;
-    } else {
-      const uint64_t key2 = sel_key2[i];
-      for (int j = 0; j < cnt; ++j) {
-        const uint64_t kj = sel_key[j];
-        r += (kj < key || (kj == key && sel_key2[j] < key2)) ? 1 : 0;
-      }
+    for (int j = part; j < cnt; j += 16) {
+      const uint64_t kj = sel_key[j];
+      r += (kj < key || (D >= 16 && kj == key && sel_key2[j] < key2)) ? 1 : 0;
     }
-    flat_of[sel_e[i]] = 1 + r;
+    r += dpp_i<kDppXor1>(r);
+    r += dpp_i<kDppXor2>(r);
+    r += dpp_i<kDppHalfMirror>(r);
+    r += dpp_i<kDppMirror>(r);
+    if (part == 0) flat_of[sel_e[i]] = 1 + r;
   }
   __syncthreads();
   int bad = (tid == 0 && n_sel != m) ? 1 : 0;  // keys are distinct, so exactly m are selected
@@ -819,8 +910,8 @@ hipError_t launch_assemble(int B, int S, int V, int D, int k, int m, int upto, c
                            int32_t* pos = nullptr) {
   const int P = S * k;
   const size_t LS = (size_t)((k * k + 1) & ~1);
-  const size_t sm3 = (2 * (size_t)D * LS + S + 2 * (size_t)m) * 8 + (size_t)P * 3 * 4 + (size_t)S * 4 +
-                     (size_t)m * 2 * 4 + (size_t)P * 4 + 2 * (size_t)(m + 1) * 4;
+  const size_t sm3 = (2 * (size_t)D * LS + 2 + 32 + S + 1 + 2 * (size_t)m) * 8 + (size_t)P * 4 * 4 + (size_t)(S + 1) * 4 +
+                     (size_t)m * 2 * 4 + 2 * (size_t)(m + 1) * 4;
   tree_assemble_kernel<<<B, kTreeThreads, sm3, st>>>(S, k, D, m, V, root, pool_tok, pool_q, node_tok, node_parent,
                                                      node_depth, node_sib, node_slot, node_value, node_q, pool_flat,
                                                      slot_src, status, upto, prefix_len, mask, pos);

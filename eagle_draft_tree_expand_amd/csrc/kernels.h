@@ -93,6 +93,8 @@ struct AttnPlan {
   int rows_pad;    // rows rounded up to the MFMA tile
   int split_keys;  // prefix keys per split workgroup
   int nsplit;      // prefix splits (+1 split for the tree keys)
+  int threads;     // bf16 split workgroup: 256 or 512 threads
+  int qt;          // bf16: 16-row query tiles per wave (1 or 2)
 };
 AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, int dtype);
 inline size_t attn_ws_bytes(int B, int hkv, int head_dim, const AttnPlan& pl) {

@@ -147,7 +147,11 @@ def test_mask_matches_oracle(rt, name, kw):
 ATTN_CASES = [
     ("mid_bf16", {}, 2e-2),
     ("mid_bf16", dict(hq=8, hkv=2, k=4, m=40, L=(1, 700), H=1024), 2e-2),  # 160 rows, ragged prefix
-    ("mid_bf16", dict(hq=16, hkv=1, m=20, H=2048), 2e-2),         # 336 rows: two row blocks
+    ("mid_bf16", dict(hq=16, hkv=1, m=20, H=2048), 2e-2),         # 336 rows: six 64-row blocks
+    # 8B attention shape (32q/8kv x 128, 61 nodes, 244 rows per kv head):
+    # batch 2 takes 128-row blocks, batch 4 256-row blocks
+    ("mid_bf16", dict(B=2, hq=32, hkv=8, H=4096, D=8, k=10, m=60, L=(2048, 2048)), 2e-2),
+    ("mid_bf16", dict(B=4, hq=32, hkv=8, H=4096, D=8, k=10, m=60, L=(1500, 2048)), 2e-2),
     ("mid_bf16", dict(hq=2, hkv=2, dh=64, H=128), 2e-2),          # head_dim 64
     ("mid_bf16", dict(L=(0, 0)), 2e-2),                           # empty prefix: tree only
     ("mid_bf16", dict(L=(2100, 3000)), 2e-2),                     # long prefix: 384-key splits
