@@ -178,7 +178,7 @@ int check_draft(const eagle_tree_params* p, const eagle_draft_dims* d, DraftLayo
 
 extern "C" {
 
-int32_t eagle_abi_version(void) { return (1 << 16) | 3; }
+int32_t eagle_abi_version(void) { return (1 << 16) | 4; }
 
 const char* eagle_error_string(int32_t code) {
   switch (code) {
