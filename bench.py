@@ -432,6 +432,19 @@ def main():
                          "committed_tokens_per_s": round(wr["committed"] / (wr["total_ms"] / 1000.0), 1),
                          "tau_synthetic": round(wr["committed"] / (wsteps * cfg.B), 4),
                          "device_status": wr["status"]}
+        if args.config == "8b":
+            # the same warps on draft rows close to the target's, so that warped rounds accept too
+            kcfg, _, kwts, ksets = setup("8b_close", args.temp, 4)
+            kr = time_rounds(kcfg, kwts, ksets, args.temp, wsteps, 5, warp=(50, 0.9))
+            ku = time_rounds(kcfg, kwts, ksets, args.temp, wsteps, 5)
+            out["warped_close"] = {"workload": "8b shape, draft rows = target logits + N(0, 0.01^2) noise",
+                                   "warp": "top_k 50, top_p 0.9 on draft and target rows",
+                                   "trees_per_s": round(1000.0 * wsteps / kr["total_ms"] * kcfg.B, 2),
+                                   "committed_tokens_per_s": round(kr["committed"] / (kr["total_ms"] / 1000.0), 1),
+                                   "tau_synthetic": round(kr["committed"] / (wsteps * kcfg.B), 4),
+                                   "unwarped_tau_synthetic": round(ku["committed"] / (wsteps * kcfg.B), 4),
+                                   "device_status": kr["status"] | ku["status"]}
+            del kwts, ksets
     if not args.no_extra and args.config == "8b" and args.temp > 0:
         # the same workload drafted as a chain (top-k 1, 8 draft tokens): tree vs chain
         ccfg, _, cwts, csets = setup("8b_chain", args.temp, 4)

@@ -103,6 +103,12 @@ CONFIGS["8b_static"] = CONFIGS["8b"].with_(name="8b_static", D=5, k=4, m=len(STA
 # The chain with as many draft passes (EAGLE-1 notes, tree-attention ablation: a
 # chain and a tree drafted with the same number of forward passes).
 CONFIGS["8b_chain5"] = CONFIGS["8b"].with_(name="8b_chain5", D=5, k=1, m=5, temps=(1.0,))
+# The 8B workload with draft rows close to the target's: noise sigma 0.01 in
+# place of 1, against target logits that spread ~0.03 (random weights), so the
+# draft's and the target's top-50 tokens partly agree and rounds under top-k /
+# top-p warps accept draft tokens too (measured: warped tau 1.75, unwarped 2.65;
+# sigma 0 gives 2.0 and 2.55, sigma 0.02 1.5 and 2.6).
+CONFIGS["8b_close"] = CONFIGS["8b"].with_(name="8b_close", sigma=(0.01, 0.01), temps=(1.0,))
 
 # Reduced shapes for element-by-element parity: several tiles and ragged tails
 # in every dimension (vocab not a multiple of the 256-column tile, prefix not a
