@@ -434,10 +434,16 @@ __global__ __launch_bounds__(256) void lmhead_f32_kernel(int rows, int H, int V,
 // logits and a stats record per (row, 256-column tile), the same record the
 // streaming kernel writes per 512 columns.
 constexpr int kGK = 32;        // hidden values per step
-constexpr int kGStages = 4;    // LDS ring depth (loads run kGStages - 1 steps ahead)
 constexpr int kGBlock = 512;   // bf16 elements of one 1 KB operand block
-constexpr int kGThreads = 512;     // 8 waves: 4 row quarters x 2 column halves, two per SIMD
-constexpr int kGLoadsPerStep = 4;  // direct loads each wave issues per step (32 blocks / 8 waves)
+// Output tiles of TM x 256: 256 x 256 (4 row groups x 2 column groups of
+// waves, 8 waves, one workgroup per CU, 4-stage ring) or 128 x 256 (2 x 2, 4
+// waves, two workgroups per CU, 3-stage ring of 72 KB); every wave holds a
+// 64 x 128 block of 4 x 8 MFMA tiles.  256 x 256 is faster where both fit the
+// rows (41.7% against 39% of the bf16 peak at 3904 rows); 128 x 256 serves row
+// counts that 256-row tiles would pad by a sixth or more (640 rows: 768
+// computed).  A 128 x 512 tile with 8 waves (the 256 x 256 tile's MFMA work,
+// no padding at multiples of 128) ran slower than both: 25% more ring bytes
+// per step in a 3-stage ring.
 
 // Direct global->LDS load of 16 bytes per lane into lds + 16 * lane, issued
 // by hand: the compiler then does not track these LDS writes, and does not
@@ -456,50 +462,70 @@ EDEV void dma16_lds(const void* g, const void* lds) {
 // operations (other counters unconstrained): vmcnt bits [3:0] and [15:14].
 EDEV constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
-template <bool PACKED>
-__global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_gemm_kernel(
-    int rows, int H, int V, float Tp, int nm, int nn, int bm, const uint16_t* __restrict__ x,
-    const uint16_t* __restrict__ w, float* __restrict__ logits, float* __restrict__ part, int32_t* status,
-    RowMap rm, int gps, int hk, float* __restrict__ partial, uint16_t* __restrict__ z16, float* __restrict__ bmax) {
-  // the ring: one array per stage
-  __shared__ __attribute__((aligned(1024))) uint16_t ring0[32 * kGBlock];  // A 16 blocks | B 16 blocks
-  __shared__ __attribute__((aligned(1024))) uint16_t ring1[32 * kGBlock];
-  __shared__ __attribute__((aligned(1024))) uint16_t ring2[32 * kGBlock];
-  __shared__ __attribute__((aligned(1024))) uint16_t ring3[32 * kGBlock];
-  __shared__ Rec hrec[2][kGemmTile];
+// Wait until at most `ahead` steps of L loads each are still in flight
+// (ahead <= A; the immediate must be a constant, hence the chain).
+template <int L, int A>
+EDEV void wait_steps_ahead(int ahead) {
+  if constexpr (A == 0) {
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  } else {
+    if (ahead >= A) __builtin_amdgcn_s_waitcnt(vmcnt_imm(A * L));
+    else wait_steps_ahead<L, A - 1>(ahead);
+  }
+}
 
-  // XCD-aware tile order: workgroup id = xcd + 8 j.  On each XCD, runs of 32
-  // consecutive j (about what its 32 CUs hold at once) form a block of bm row
-  // tiles x 32/bm vocab tiles, so every X and W slab read into the XCD's L2
-  // serves several workgroups; vocab tiles of XCD x are those = x mod 8.
+template <bool PACKED, int TM, int STAGES>
+__global__ __launch_bounds__(TM * 2) __attribute__((amdgpu_waves_per_eu(2, 2))) void lmhead_gemm_kernel(
+    int rows, int H, int V, float Tp, int nm, int nn, int bm, int bn, const uint16_t* __restrict__ x,
+    const uint16_t* __restrict__ w, float* __restrict__ logits, float* __restrict__ part, int32_t* status,
+    RowMap rm, int gps, int ks, float* __restrict__ partial, uint16_t* __restrict__ z16, float* __restrict__ bmax) {
+  constexpr int TN = kGemmTile, WN = 2;  // two column groups of 128
+  constexpr int WAVES = (TM / 64) * WN;
+  constexpr int AB = TM / 16, BB = TN / 16;  // A and B blocks per stage
+  constexpr int QA = AB / WAVES;         // A blocks each wave loads per step
+  constexpr int QB = BB / WAVES;         // B blocks each wave loads per step
+  constexpr int kLoads = QA + QB;        // direct loads each wave issues per step
+  static_assert(QA >= 1 && QB >= 1 && QA * WAVES == AB && QB * WAVES == BB, "blocks must split evenly over waves");
+  // the ring: STAGES stages of A blocks | B blocks
+  __shared__ __attribute__((aligned(1024))) uint16_t ring[STAGES][(AB + BB) * kGBlock];
+  __shared__ Rec hrec[WN][TM];
+
+  // XCD-aware tile order: workgroup id = xcd + 8 j.  On each XCD, runs of
+  // bm x bn consecutive j (at most 32: about what its 32 CUs hold at once)
+  // form a block of bm row tiles x bn vocab tiles, so every X and W slab read
+  // into the XCD's L2 serves several workgroups; vocab tiles of XCD x are
+  // those = x mod 8.  The grid holds whole blocks: bm and bn follow the tile
+  // counts so that few of its workgroups are empty.
   // hidden split: workgroups kz*gps .. kz*gps + gps-1 cover hidden slice kz
-  // (hk values) of every tile and write fp32 partials (partial != null)
+  // of every tile (128-wide chunks kz C / ks .. (kz + 1) C / ks - 1 of the C =
+  // H / 128) and write fp32 partials (partial != null)
   const int kz = (int)blockIdx.x / gps;
   const int bid = (int)blockIdx.x - kz * gps, xcd = bid & 7, j = bid >> 3;
-  const int bnb = 32 / bm, jb = j & 31, blk = j >> 5, nmb = (nm + bm - 1) / bm;
-  const int mt_idx = (blk % nmb) * bm + jb / bnb;
-  const int nt_idx = ((blk / nmb) * bnb + jb % bnb) * 8 + xcd;
+  const int bsz = bm * bn, blk = j / bsz, jb = j - blk * bsz, nmb = (nm + bm - 1) / bm;
+  const int mt_idx = (blk % nmb) * bm + jb / bn;
+  const int nt_idx = ((blk / nmb) * bn + jb % bn) * 8 + xcd;
   if (mt_idx >= nm || nt_idx >= nn) return;  // padding of the grid to whole blocks
-  const int m0 = mt_idx * kGemmTile, n0 = nt_idx * kGemmTile;
+  const int m0 = mt_idx * TM, n0 = nt_idx * TN;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;  // rows 64 wm.., columns 128 wn..
+  const int wm = wave / WN, wn = wave % WN;  // rows 64 wm.., columns 128 wn..
   const int col = lane & 15, grp = lane >> 4;
   const int nch = H / 64;
-  const int nsteps = hk / kGK;  // a multiple of 4: hk is a multiple of 128
-  const int sb = kz * nsteps;   // first step of this slice
+  const int nch128 = H / 128, c0 = kz * nch128 / ks, c1 = (kz + 1) * nch128 / ks;
+  const int nsteps = (c1 - c0) * (128 / kGK);  // a multiple of 4
+  const int sb = c0 * (128 / kGK);             // first step of this slice
   const int ngroups = (V + 63) / 64;
 
-  // Sources of this wave's 4 blocks per step: A blocks mt = 2 wave + q and
-  // B blocks nt = 2 wave + q (q < 2).
-  uint32_t xoff[2];  // element offset of this lane's X row (clamped) + its 8-wide hidden offset
+  // Sources of this wave's blocks per step: A blocks mt = QA wave + q (q <
+  // QA) and B blocks nt = QB wave + q (q < QB).
+  uint32_t xoff[QA];  // element offset of this lane's X row (clamped) + its 8-wide hidden offset
 #pragma unroll
-  for (int q = 0; q < 2; ++q)
-    xoff[q] = (uint32_t)min(m0 + (2 * wave + q) * 16 + col, rows - 1) * (uint32_t)H + grp * 8 + sb * kGK;
-  const uint16_t* wsrc[2];
+  for (int q = 0; q < QA; ++q)
+    xoff[q] = (uint32_t)min(m0 + (QA * wave + q) * 16 + col, rows - 1) * (uint32_t)H + grp * 8 + sb * kGK;
+  const uint16_t* wsrc[QB];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int nt = 2 * wave + q;
+  for (int q = 0; q < QB; ++q) {
+    const int nt = QB * wave + q;
     if (PACKED) {  // group nt / 4, load (nt % 4) of a 32-wide half chunk
       const int g = min(n0 / 64 + nt / 4, ngroups - 1);
       wsrc[q] = w + ((size_t)g * nch * 8 + (nt & 3) + (size_t)(sb >> 1) * 8) * 512 + (size_t)lane * 8;
@@ -507,17 +533,16 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
       wsrc[q] = w + (size_t)min(n0 + nt * 16 + col, V - 1) * H + grp * 8 + sb * kGK;
     }
   }
-#define G_ISSUE_Q(st, dst, q)                                                                               \
-  {                                                                                                         \
-    const int k0 = (st) * kGK;                                                                              \
-    dma16_lds(x + xoff[q] + k0, dst + (2 * wave + (q)) * kGBlock);                                         \
-    const uint16_t* ws_ = PACKED ? wsrc[q] + ((size_t)((st) >> 1) * 8 + ((st) & 1) * 4) * 512              \
-                                 : wsrc[q] + k0;                                                            \
-    dma16_lds(ws_, dst + (16 + 2 * wave + (q)) * kGBlock);                                                  \
-  }
 #define G_ISSUE(st, dst)                                                                                    \
   {                                                                                                         \
-    _Pragma("unroll") for (int q = 0; q < 2; ++q) G_ISSUE_Q(st, dst, q)                                     \
+    const int k0 = (st) * kGK;                                                                              \
+    _Pragma("unroll") for (int q = 0; q < QA; ++q)                                                          \
+      dma16_lds(x + xoff[q] + k0, dst + (QA * wave + q) * kGBlock);                                         \
+    _Pragma("unroll") for (int q = 0; q < QB; ++q) {                                                        \
+      const uint16_t* ws_ = PACKED ? wsrc[q] + ((size_t)((st) >> 1) * 8 + ((st) & 1) * 4) * 512            \
+                                   : wsrc[q] + k0;                                                          \
+      dma16_lds(ws_, dst + (AB + QB * wave + q) * kGBlock);                                                 \
+    }                                                                                                       \
   }
 
   floatx4 acc[4][8];
@@ -528,13 +553,10 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
 
   // One step: wait for this wave's loads of step st (later steps may still
   // fly), barrier (every wave's blocks are in; the buffer of step st - 1 is
-  // free), issue step st + 3 into that buffer, then the 64 MFMAs.
+  // free), issue step st + STAGES - 1 into that buffer, then the 32 MFMAs.
 #define G_STEP(st, cur, nxt)                                                                               \
   {                                                                                                        \
-    const int ahead = min(kGStages - 2, nsteps - 1 - (st));                                                \
-    if (ahead >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * kGLoadsPerStep));                            \
-    else if (ahead == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(kGLoadsPerStep));                           \
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));                                                         \
+    wait_steps_ahead<kLoads, STAGES - 2>(min(STAGES - 2, nsteps - 1 - (st)));                              \
     /* a bare barrier: the waits above already cover this wave's loads, and a */                          \
     /* fenced barrier would also wait for the steps still in flight */                                     \
     asm volatile("" ::: "memory");                                                                         \
@@ -544,28 +566,34 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
     /* the direct loads of step st + 3 go out between the first MFMAs */                                   \
     B8 bf[8], af[4];                                                                                       \
     _Pragma("unroll") for (int t = 0; t < 8; ++t)                                                          \
-      bf[t].w = *reinterpret_cast<const u32x4*>(cur + (16 + wn * 8 + t) * kGBlock + lane * 8);            \
+      bf[t].w = *reinterpret_cast<const u32x4*>(cur + (AB + wn * 8 + t) * kGBlock + lane * 8);            \
     _Pragma("unroll") for (int t = 0; t < 4; ++t)                                                          \
       af[t].w = *reinterpret_cast<const u32x4*>(cur + (wm * 4 + t) * kGBlock + lane * 8);                 \
     _Pragma("unroll") for (int mt = 0; mt < 4; ++mt) {                                                     \
       _Pragma("unroll") for (int nt = 0; nt < 8; ++nt)                                                     \
         acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt].v, bf[nt].v, acc[mt][nt], 0, 0, 0);   \
-      if (mt == 0 && (st) + kGStages - 1 < nsteps) G_ISSUE((st) + kGStages - 1, nxt)                       \
+      if (mt == 0 && (st) + STAGES - 1 < nsteps) G_ISSUE((st) + STAGES - 1, nxt)                           \
     }                                                                                                      \
   }
   // nsteps = H / 32 is a multiple of 4 (hidden % 128 == 0)
-  G_ISSUE(0, ring0)
-  G_ISSUE(1, ring1)
-  G_ISSUE(2, ring2)
-  for (int st = 0; st < nsteps; st += 4) {
-    G_STEP(st, ring0, ring3)
-    G_STEP(st + 1, ring1, ring0)
-    G_STEP(st + 2, ring2, ring1)
-    G_STEP(st + 3, ring3, ring2)
+#pragma unroll
+  for (int st = 0; st < STAGES - 1; ++st)
+    if (st < nsteps) G_ISSUE(st, ring[st])
+  if (STAGES == 4) {
+    for (int st = 0; st < nsteps; st += 4) {
+      G_STEP(st, ring[0], ring[3])
+      G_STEP(st + 1, ring[1], ring[0])
+      G_STEP(st + 2, ring[2], ring[1])
+      G_STEP(st + 3, ring[3], ring[2])
+    }
+  } else {
+    for (int st = 0; st < nsteps; ++st) {
+      const int sc = st % STAGES;
+      G_STEP(st, ring[sc], ring[(sc + STAGES - 1) % STAGES])
+    }
   }
 #undef G_STEP
 #undef G_ISSUE
-#undef G_ISSUE_Q
 
   const int nbase = n0 + wn * 128;
   if (partial != nullptr) {  // a hidden slice: fp32 partials, summed by lm_combine
@@ -638,7 +666,7 @@ __global__ __launch_bounds__(kGThreads) __attribute__((amdgpu_waves_per_eu(2, 2)
   if (bad) set_status(status, EAGLE_STATUS_NONFINITE);
   __syncthreads();
   const int m = m0 + tid;
-  if (tid < kGemmTile && m < rows) {
+  if (tid < TM && m < rows) {
     Rec rc = hrec[0][tid];
     rec_merge(rc, hrec[1][tid]);
     float* pr = part + ((size_t)m * nn + nt_idx) * 4;
@@ -933,23 +961,41 @@ hipError_t launch_lmhead_impl(int rows, int H, int V, int dtype, int w_layout, c
   const float Tp = (T > 0.f) ? T : 1.0f;
   int ntiles = lm_ntiles(V);
   if (dtype == EAGLE_BF16 && rows >= kGemmMinRows) {
-    const int nm = (rows + kGemmTile - 1) / kGemmTile, nn = lm_gemm_ntiles(V);
-    ntiles = nn;
-    // blocks of bm row tiles x 32/bm vocab tiles per XCD (16 x 2 measured best at 16 row tiles)
-    const int bm = nm >= 16 ? 16 : nm >= 8 ? 8 : 4, bn = 32 / bm;
-    const int gps = ((nm + bm - 1) / bm * bm) * ((nn + 8 * bn - 1) / (8 * bn) * (8 * bn));
     // plain products with few tiles split the hidden dimension (no statistics then)
-    const int ks = row_stats == nullptr ? lm_gemm_ksplit(rows, V, H) : 1;
+    const GemmPlan gp = gemm_plan(rows, V, H, row_stats != nullptr);
+    const int TM = gp.tm, ks = gp.ks;
+    const int nm = (rows + TM - 1) / TM, nn = lm_gemm_ntiles(V);
+    ntiles = nn;
+    // blocks of bm row tiles x bn vocab tiles per XCD (16 x 2 measured best at
+    // 16 row tiles).  Up to 16 row tiles go in one block; more take the bm in
+    // 8..16 that pads them least.  bn is the largest width <= 32 / bm that
+    // pads the XCD's vocab tiles by at most a sixteenth, else the least padding.
+    const int nn8 = (nn + 7) / 8;  // vocab tiles of XCD 0 (the most of any XCD)
+    auto padded = [](int n, int b) { return (n + b - 1) / b * b; };
+    int bm = nm;
+    if (nm > 16) {
+      bm = 16;
+      for (int c = 15; c >= 8; --c)
+        if (padded(nm, c) < padded(nm, bm)) bm = c;
+    }
+    int bn = 1;
+    for (int c = 2; c <= 32 / bm && c <= nn8; ++c)
+      if (padded(nn8, c) < padded(nn8, bn) || 16 * (padded(nn8, c) - nn8) <= nn8) bn = c;
+    const int gps = ((nm + bm - 1) / bm * bm) * ((nn8 + bn - 1) / bn * bn) * 8;
     float* partial = ks > 1 ? ws_part + lm_rec_floats(rows, V) : nullptr;
     const size_t lds = 0;
-    if (w_layout == EAGLE_W_PACKED)
-      lmhead_gemm_kernel<true><<<gps * ks, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
-                                                           (const uint16_t*)w, logits, ws_part, status, rm, gps,
-                                                           H / ks, partial, z16, bmax);
-    else
-      lmhead_gemm_kernel<false><<<gps * ks, kGThreads, lds, st>>>(rows, H, V, Tp, nm, nn, bm, (const uint16_t*)x,
-                                                            (const uint16_t*)w, logits, ws_part, status, rm, gps,
-                                                            H / ks, partial, z16, bmax);
+#define EAGLE_GEMM(PK, M, SG)                                                                                   \
+  lmhead_gemm_kernel<PK, M, SG><<<gps * ks, M * 2, lds, st>>>(                                                   \
+      rows, H, V, Tp, nm, nn, bm, bn, (const uint16_t*)x, (const uint16_t*)w, logits, ws_part, status, rm, gps, ks, \
+      partial, z16, bmax)
+    if (w_layout == EAGLE_W_PACKED) {
+      if (TM == 256) EAGLE_GEMM(true, 256, 4);
+      else EAGLE_GEMM(true, 128, 3);
+    } else {
+      if (TM == 256) EAGLE_GEMM(false, 256, 4);
+      else EAGLE_GEMM(false, 128, 3);
+    }
+#undef EAGLE_GEMM
     if (defer_ks) *defer_ks = ks;
     if (ks > 1 && !defer_ks) {  // plain products only (statistics take ks = 1): never compact
       hipError_t e0 = hipGetLastError();

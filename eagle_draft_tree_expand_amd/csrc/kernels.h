@@ -123,7 +123,7 @@ constexpr int kLmThreads = 512;          // bf16: 4 column quarters x 2 hidden h
 constexpr int kLmArgTile = 1 << 30;
 inline int lm_ntiles(int V) { return (V + kLmTileN - 1) / kLmTileN; }
 inline int lm_mtiles(int rows) { return (rows + kLmTileM - 1) / kLmTileM; }
-// Large row counts (many requests per round) take a tiled GEMM: 256 x 256
+// Large row counts (many requests per round) take a tiled GEMM: TM x 256
 // output tiles, one stats record per (row, 256-column tile).
 constexpr int kGemmTile = 256;
 constexpr int kGemmMinRows = 193;        // from 4 row tiles of the streaming kernel on
@@ -140,16 +140,35 @@ inline int lm_ksplit(int rows, int V, int H) {
   while (ks > 1 && H % (ks * 128) != 0) --ks;
   return ks < 1 ? 1 : ks;
 }
-// The tiled GEMM with fewer 256 x 256 tiles than CUs splits the hidden
-// dimension too (plain products only: no row statistics), up to one
-// workgroup per CU, slices of a multiple of 128.
+// Tile and hidden split of the tiled GEMM.  Row tiles of 256 (8 waves, one
+// workgroup per CU) or 128 (4 waves, two per CU); products without row
+// statistics may split the hidden dimension into KS <= 8 slices of whole
+// 128-wide chunks (lengths differ by at most one chunk), each writing an fp32
+// partial that its consumer sums.  The plan minimises a measured cost model:
+// rounds of workgroup slots x chunks per slice x the time of one chunk on a
+// full CU (3.9 us at TM 256, 4.5 us at TM 128: two 128-row tiles per CU), plus
+// writing and reading each partial beyond the first at about 4 TB/s.
+struct GemmPlan {
+  int tm, ks;
+};
+inline GemmPlan gemm_plan(int rows, int V, int H, bool stats) {
+  const int C = H / 128;
+  const long nn = lm_gemm_ntiles(V);
+  GemmPlan best{256, 1};
+  double best_us = 1e300;
+  for (int tm : {256, 128}) {
+    const long tiles = (rows + tm - 1) / tm * nn, slots = tm == 128 ? 512 : 256;
+    const double chunk_us = tm == 128 ? 4.5 : 3.9;
+    for (int ks = 1; ks <= (stats ? 1 : 8) && ks <= C; ++ks) {
+      const double us = (double)((tiles * ks + slots - 1) / slots) * ((C + ks - 1) / ks) * chunk_us +
+                        (ks - 1) * (double)rows * V * 8.0 / 4e6;
+      if (us < best_us) { best = GemmPlan{tm, ks}; best_us = us; }
+    }
+  }
+  return best;
+}
 inline int lm_gemm_ksplit(int rows, int V, int H) {
-  if (rows < kGemmMinRows) return 1;
-  const int tiles = ((rows + kGemmTile - 1) / kGemmTile) * lm_gemm_ntiles(V);
-  int ks = 256 / tiles;
-  if (ks > 8) ks = 8;
-  while (ks > 1 && H % (ks * 128) != 0) --ks;
-  return ks < 1 ? 1 : ks;
+  return rows < kGemmMinRows ? 1 : gemm_plan(rows, V, H, false).ks;
 }
 inline size_t lm_rec_floats(int rows, int V) { return (size_t)rows * lm_gemm_ntiles(V) * 4; }
 inline size_t lm_ws_bytes(int rows, int V, int H) {

@@ -15,6 +15,12 @@ embedding, one decoder layer, the shared LM head):
   bf16 ulp of the fp64 value of the same formula (the device rounds an fp32
   value once), and equal to its bf16 rounding for at least 99% of entries;
 * the draft attention: 2e-2 per row against the fp64 oracle on the slot mask.
+
+At batch 64 the 640 frontier rows of depth 1 take the tiled GEMM, whose plain
+products split the hidden dimension into uneven slices (fc: 5 slices of 12 or
+13 chunks of 128; qkv: 3 of 10 or 11; down: 5 of 22 or 23); there 40 sampled
+rows (the first and the last included) and the attention of 5 requests are
+checked.
 """
 import numpy as np
 import pytest
@@ -64,7 +70,7 @@ class _Ws:
         return t.float().cpu().numpy() if dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["mid_bf16", "8b"])
+@pytest.mark.parametrize("name", ["mid_bf16", "8b", "b64"])
 def test_draft_kernels_staged(name):
     from eagle_draft_tree_expand_amd import draft_head, ops
     from eagle_draft_tree_expand_amd import round as dround
@@ -93,6 +99,11 @@ def test_draft_kernels_staged(name):
         torch.cuda.synchronize()
         kd = 1 if depth == 0 else k
         R = B * kd
+        if R <= 64:
+            samp = np.arange(R)
+        else:
+            pick = np.random.default_rng(3 + depth).choice(np.arange(1, R - 1), 38, replace=False)
+            samp = np.unique(np.concatenate([[0, R - 1], pick]))
         idx = ws.get("idx", torch.int32, (R,))
         slots = idx - (np.arange(R) // kd) * S
         # draft_in: x0 = [feature ; E[token]] bit for bit
@@ -101,7 +112,7 @@ def test_draft_kernels_staged(name):
         pool_tok = rnd.tree["pool_tok"].cpu().numpy().reshape(B, -1)
         slot_src = rnd.tree["slot_src"].cpu().numpy()
         masks = ws.get("slot_mask", torch.int64, (B, S, Wsl)).view(np.uint64)
-        for r in range(R):
+        for r in samp:
             b, s = r // kd, int(slots[r])
             if depth == 0:
                 tok, feat = int(inp.roots[b]), dinp.root_feat[b]
@@ -116,21 +127,22 @@ def test_draft_kernels_staged(name):
             assert np.array_equal(masks[b, s], want), f"mask of slot {s}"
         # fc product and the first norm
         u = ws.get("u", torch.float32, (R, H))
-        assert rel_err_rows(u, x0.astype(np.float64) @ W["fc"].astype(np.float64).T) <= 1e-5
+        assert rel_err_rows(u[samp], x0[samp].astype(np.float64) @ W["fc"].astype(np.float64).T) <= 1e-5
         n1 = ws.get("n1", bf, (R, H))
-        _bf16_close(n1, _rms(u), "n1 = rms(u)")
+        _bf16_close(n1[samp], _rms(u[samp]), "n1 = rms(u)")
         # qkv product to bf16 q rows and slot k/v rows
         q = ws.get("q", bf, (R, Q))
-        n1_64 = n1.astype(np.float64)
-        _bf16_close(q, n1_64 @ W["q"].astype(np.float64).T, "q rows")
+        n1_64 = n1[samp].astype(np.float64)
+        _bf16_close(q[samp], n1_64 @ W["q"].astype(np.float64).T, "q rows")
         sk = ws.get("slot_k", bf, (B * S, KV))
         sv = ws.get("slot_v", bf, (B * S, KV))
-        _bf16_close(sk[idx], n1_64 @ W["k"].astype(np.float64).T, "k rows")
-        _bf16_close(sv[idx], n1_64 @ W["v"].astype(np.float64).T, "v rows")
+        _bf16_close(sk[idx[samp]], n1_64 @ W["k"].astype(np.float64).T, "k rows")
+        _bf16_close(sv[idx[samp]], n1_64 @ W["v"].astype(np.float64).T, "v rows")
         # draft attention: frontier queries over the draft prefix and the slots their mask rows allow
         og = ws.get("attn", bf, (R, Q))
         scale = np.float32(1.0 / np.sqrt(cfg.dh))
-        for b in range(B):
+        reqs = range(B) if R <= 64 else sorted(set((samp[:4] // kd).tolist()) | {B - 1})
+        for b in reqs:
             qf = np.zeros((S, cfg.hq, cfg.dh), np.float32)
             rows_b = [r for r in range(R) if r // kd == b]
             for r in rows_b:
@@ -148,25 +160,27 @@ def test_draft_kernels_staged(name):
             assert rel_err_rows(got, ref) <= 2e-2, f"attention b={b}"
         # o product + residual, second norm
         h = ws.get("h", torch.float32, (R, H))
-        assert rel_err_rows(h, u.astype(np.float64) + og.astype(np.float64) @ W["o"].astype(np.float64).T) <= 1e-5
+        assert rel_err_rows(h[samp], u[samp].astype(np.float64)
+                            + og[samp].astype(np.float64) @ W["o"].astype(np.float64).T) <= 1e-5
         n2 = ws.get("n2", bf, (R, H))
-        _bf16_close(n2, _rms(h), "n2 = rms(h)")
+        _bf16_close(n2[samp], _rms(h[samp]), "n2 = rms(h)")
         # gate/up product and silu
-        n2_64 = n2.astype(np.float64)
+        n2_64 = n2[samp].astype(np.float64)
         g = n2_64 @ W["g"].astype(np.float64).T
         up = n2_64 @ W["u"].astype(np.float64).T
         m = ws.get("m", bf, (R, I))
-        _bf16_close(m, g / (1.0 + np.exp(-g)) * up, "m = silu(g) * u", min_exact=0.98)
+        _bf16_close(m[samp], g / (1.0 + np.exp(-g)) * up, "m = silu(g) * u", min_exact=0.98)
         # down product + residual: the head output a, also the slot's feature
         a = ws.get("a", bf, (R, H))
-        _bf16_close(a, h.astype(np.float64) + m.astype(np.float64) @ W["d"].astype(np.float64).T, "a")
+        _bf16_close(a[samp], h[samp].astype(np.float64) + m[samp].astype(np.float64) @ W["d"].astype(np.float64).T,
+                    "a")
         slot_feat = ws.get("slot_feat", bf, (B, S, H))
-        for r in range(R):
+        for r in samp:
             assert np.array_equal(slot_feat[r // kd, slots[r]], a[r])
         # the shared LM head: the frontier's draft rows at their slots
-        rows = data.rows.cpu().numpy()
-        zd = np.stack([rows[r // kd, slots[r]] for r in range(R)])
-        assert rel_err_rows(zd, a.astype(np.float64) @ Wlm.T) <= 1e-5
+        rows = data.rows
+        zd = np.stack([rows[r // kd, int(slots[r])].cpu().numpy() for r in samp])
+        assert rel_err_rows(zd, a[samp].astype(np.float64) @ Wlm.T) <= 1e-5
         assert int(rnd.status.item()) & ~0x8 == 0
         if depth == 0:
             ops.expand_depth(p, 0, data.rows, rnd.tree, rnd.ws, rnd.status)

@@ -329,12 +329,13 @@ def test_lmhead_full_all_columns(rt, name):
     assert np.array_equal(am[clear], np.argmax(z64, axis=1)[clear])
 
 
-def test_lmhead_gemm_b64_rows_all_columns(rt):
-    """Batch-64 8B LM head (3904 x 4096 x 128256) on the tiled GEMM: 64 sampled rows, every column."""
+@pytest.mark.parametrize("B", [64, 10])
+def test_lmhead_gemm_b64_rows_all_columns(rt, B):
+    """The 8B LM head (B x 61 rows x 4096 x 128256) on the tiled GEMM, 64 sampled rows, every column:
+    batch 64 (3904 rows) takes 256-row tiles, batch 10 (610 rows) 128-row tiles with a ragged last one."""
     cfg = synth.get_config("8b")
     inp = synth.make_inputs(cfg)
     rng = np.random.default_rng(9)
-    B = 64
     X = synth.bf16_round((0.05 * rng.standard_normal((B * cfg.N, cfg.H))).astype(np.float32))
     dr = rt.DeviceRound(cfg, B=B)
     wts = rt.DeviceWeights(inp)
@@ -347,7 +348,7 @@ def test_lmhead_gemm_b64_rows_all_columns(rt):
     lg = dr.logits[torch.from_numpy(rows).cuda()].cpu().numpy()
     z64 = olm.logits(X[rows], inp.w)
     err = rel_err_rows(lg, z64)
-    print(f"b64 LM head: {rows.size} rows x {cfg.V} columns, worst row error {err:.2e}")
+    print(f"B={B} LM head: {rows.size} rows x {cfg.V} columns, worst row error {err:.2e}")
     assert err <= 1e-5
     stats = dr.stats.cpu().numpy()[rows]
     am = dr.argmax.cpu().numpy()[rows]
