@@ -473,6 +473,16 @@ AttnPlan attn_plan(int B, int n, int hq, int hkv, int head_dim, int max_prefix, 
   // block; 70B: 256-row blocks, 32 against 41 us with 64); grids past one pass
   // take the smallest block that holds all rows of a kv head (13B MHA: 64),
   // else 256 (batch 64: 370 against 520 us with 64-row blocks).
+  // Many pairs of few rows (batch-64 drafting: 40 rows, 512 pairs, prefixes
+  // of 512-4096): 1024-key splits and 128-row blocks, 185 against 205 us
+  // with 2048-key splits and 64-row blocks; the partial rows are small.
+  if (per >= 256 && pl.rows <= 64) {
+    pl.split_keys = 1024;
+    pl.nsplit = (max_prefix + 1023) / 1024;
+    pl.threads = 256;
+    pl.qt = 2;
+    return pl;
+  }
   const int pairs = B * hkv * (pl.nsplit + 1);
   const int nb64 = (pl.rows + 63) / 64, nb128 = (pl.rows + 127) / 128;
   if (pairs * nb64 <= 256 || pl.rows <= 64) { pl.threads = 256; pl.qt = 1; }
