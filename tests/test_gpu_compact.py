@@ -77,11 +77,11 @@ def test_compact_lmhead_matches_encoding(name, kw, T):
     assert int(cmp.status.item()) == 0
 
 
-def test_compact_lmhead_b64_sampled_rows():
+@pytest.mark.parametrize("B", [64, 10])  # 3904 rows: 256-row tiles; 610 rows: 128-row tiles
+def test_compact_lmhead_b64_sampled_rows(B):
     cfg = synth.get_config("8b")
     inp = synth.make_inputs(cfg)
     rng = np.random.default_rng(22)
-    B = 64
     X = synth.bf16_round((0.05 * rng.standard_normal((B * cfg.N, cfg.H))).astype(np.float32))
     full, cmp = _both_heads(cfg, inp, X, 1.0, B=B)
     rows = np.unique(np.concatenate([[0, B * cfg.N - 1], rng.choice(B * cfg.N, 62, replace=False)]))

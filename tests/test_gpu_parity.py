@@ -329,16 +329,17 @@ def test_lmhead_full_all_columns(rt, name):
     assert np.array_equal(am[clear], np.argmax(z64, axis=1)[clear])
 
 
-@pytest.mark.parametrize("B", [64, 10])
-def test_lmhead_gemm_b64_rows_all_columns(rt, B):
+@pytest.mark.parametrize("B,packed", [(64, True), (10, True), (10, False)])
+def test_lmhead_gemm_b64_rows_all_columns(rt, B, packed):
     """The 8B LM head (B x 61 rows x 4096 x 128256) on the tiled GEMM, 64 sampled rows, every column:
-    batch 64 (3904 rows) takes 256-row tiles, batch 10 (610 rows) 128-row tiles with a ragged last one."""
+    batch 64 (3904 rows) takes 256-row tiles, batch 10 (610 rows) 128-row tiles with a ragged last one,
+    with the packed and the row-major weight."""
     cfg = synth.get_config("8b")
     inp = synth.make_inputs(cfg)
     rng = np.random.default_rng(9)
     X = synth.bf16_round((0.05 * rng.standard_normal((B * cfg.N, cfg.H))).astype(np.float32))
     dr = rt.DeviceRound(cfg, B=B)
-    wts = rt.DeviceWeights(inp)
+    wts = rt.DeviceWeights(inp, packed=packed)
     dr.x.copy_(torch.from_numpy(X).to(dr.x.dtype).view(dr.x.shape))
     dr.lmhead(wts, 1.0)
     torch.cuda.synchronize()
