@@ -281,6 +281,64 @@ def time_drafting(cfg, wts, inp, T, steps, warmup, device="cuda"):
     return out
 
 
+# One round's inputs on the device (DeviceInputs attributes), in a dump.
+DUMP_INPUTS = ("k_prefix", "v_prefix", "prefix_len", "roots", "uniforms", "rows")
+
+
+def _to_np(t):
+    import torch
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).cpu().numpy()
+
+
+def dump_round(path, cfg_name, T, round_id=0):
+    """Run one round of input set 0 and write its inputs and outputs to an .npz.
+
+    The file holds what the round read (prefix K/V, prefix lengths, roots,
+    uniforms, draft rows; bf16 arrays as their 16-bit words), the Gumbel key,
+    T and the round id, and every output of the round.  The LM-head weight and
+    the per-token q/k/v tables are not stored: the config's seeds rebuild them."""
+    from eagle_draft_tree_expand_amd import round as dround
+    cfg, _, wts, sets = setup(cfg_name, T, 1)
+    d = sets[0]
+    dr = dround.DeviceRound(cfg)
+    dr.step(wts, d, T, round_id=round_id)
+    out = dr.host()
+    arrays = {f"in_{k}": _to_np(getattr(d, k)) for k in DUMP_INPUTS}
+    arrays.update({f"out_{k}": np.asarray(v) for k, v in out.items() if k != "status"})
+    meta = {"config": cfg_name, "T": float(T), "round_id": int(round_id), "seed": int(d.seed),
+            "status": int(out["status"])}
+    np.savez_compressed(path, meta=np.array(json.dumps(meta)), **arrays)
+    return meta
+
+
+def replay_round(path):
+    """Run the round stored by dump_round again and compare every output bit for bit."""
+    import torch
+
+    import synth
+    from eagle_draft_tree_expand_amd import round as dround
+    z = np.load(path)
+    meta = json.loads(str(z["meta"]))
+    cfg = synth.get_config(meta["config"])
+    inp = synth.make_inputs(cfg, 0)
+    wts = dround.DeviceWeights(inp)
+    d = dround.DeviceInputs(inp)
+    for k in DUMP_INPUTS:
+        t = getattr(d, k)
+        a = torch.from_numpy(z[f"in_{k}"])
+        t.copy_((a.view(torch.bfloat16) if t.dtype == torch.bfloat16 else a).to(t.device))
+    d.seed = meta["seed"]
+    dr = dround.DeviceRound(cfg)
+    dr.step(wts, d, meta["T"], round_id=meta["round_id"])
+    out = dr.host()
+    diff = [k for k, v in out.items()
+            if k != "status" and np.asarray(v).tobytes() != z[f"out_{k}"].tobytes()]
+    if out["status"] != meta["status"]:
+        diff.append("status")
+    return {"replay": path, "config": meta["config"], "round_id": meta["round_id"], "outputs": len(out),
+            "match": not diff, "mismatched": diff}
+
+
 def _cpu_model():
     try:
         for line in open("/proc/cpuinfo"):
@@ -341,6 +399,11 @@ def main():
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain device-to-device copy of BYTES (a known-size reference for HBM "
                          "byte counters) and exit")
+    ap.add_argument("--dump-round", metavar="PATH",
+                    help="run one round of --config (input set 0, round 0) and write its inputs and outputs "
+                         "to PATH (.npz), then exit")
+    ap.add_argument("--replay", metavar="PATH",
+                    help="run the round stored in PATH again, compare every output bit for bit, print JSON")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
@@ -361,6 +424,15 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes": n * 4, "copies": 3}), flush=True)
         return
+
+    if args.dump_round:
+        print(json.dumps({"dumped": args.dump_round, **dump_round(args.dump_round, args.config, args.temp)}),
+              flush=True)
+        return
+    if args.replay:
+        r = replay_round(args.replay)
+        print(json.dumps(r), flush=True)
+        sys.exit(0 if r["match"] else 1)
 
     if args.only_draft:
         import synth

@@ -2,7 +2,9 @@
 // point validates its arguments on the host (before any HIP call), carves its
 // scratch out of the caller's workspace and enqueues its kernels on the
 // caller's stream.
+#include <dlfcn.h>
 #include <math.h>
+#include <stdlib.h>
 
 #include <mutex>
 
@@ -38,6 +40,46 @@ void* noalloc_scratch() {
   }
   return g_scratch_ptr[dev];
 }
+
+// Optional roctx ranges around the calls that enqueue work: with EAGLE_ROCTX
+// set (and not "0") in the environment, the first call loads the roctx
+// library of ROCm and each such call pushes a range named after itself
+// (rocprofv3 --marker-trace records them on the host timeline).  Otherwise
+// nothing is loaded and a call pays one check of a resolved pointer.
+struct RoctxApi {
+  int (*push)(const char*) = nullptr;
+  int (*pop)() = nullptr;
+};
+
+const RoctxApi& roctx_api() {
+  static const RoctxApi api = [] {
+    RoctxApi r;
+    const char* on = getenv("EAGLE_ROCTX");
+    if (!on || !*on || (on[0] == '0' && on[1] == 0)) return r;
+    void* h = dlopen("librocprofiler-sdk-roctx.so.1", RTLD_NOW | RTLD_LOCAL);
+    if (!h) h = dlopen("libroctx64.so.4", RTLD_NOW | RTLD_LOCAL);
+    if (!h) return r;
+    r.push = reinterpret_cast<int (*)(const char*)>(dlsym(h, "roctxRangePushA"));
+    r.pop = reinterpret_cast<int (*)()>(dlsym(h, "roctxRangePop"));
+    if (!r.push || !r.pop) r.push = nullptr, r.pop = nullptr;
+    return r;
+  }();
+  return api;
+}
+
+class CallRange {
+ public:
+  explicit CallRange(const char* name) : api_(roctx_api()) {
+    if (api_.push) api_.push(name);
+  }
+  ~CallRange() {
+    if (api_.push) api_.pop();
+  }
+
+ private:
+  const RoctxApi& api_;
+};
+#define EAGLE_CALL_RANGE() CallRange eagle_call_range_(__func__)
 
 constexpr size_t kCounterBytes = 64 * 1024;           // ticket counters at the workspace head
 
@@ -216,6 +258,7 @@ size_t eagle_workspace_size(const eagle_tree_params* p, int32_t hq, int32_t hkv,
 }
 
 int eagle_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  EAGLE_CALL_RANGE();
   if (!ws) return EAGLE_ERR_NULL;
   if (ws_bytes < kCounterBytes || ws_bytes % 4 != 0) return EAGLE_ERR_WORKSPACE;
   return launch_status(launch_zero_ints(static_cast<int32_t*>(ws), ws_bytes / 4, (hipStream_t)stream));
@@ -226,6 +269,7 @@ int eagle_expand_tree(const eagle_tree_params* p, const float* draft_logits, con
                       int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_tok, float* pool_q,
                       int32_t* pool_flat, int32_t* slot_src, float* slot_stats, void* ws, size_t ws_bytes,
                       int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   return eagle_expand_tree_warped(p, draft_logits, nullptr, root_token, node_tok, node_parent, node_depth, node_sib,
                                   node_slot, node_value, node_q, pool_tok, pool_q, pool_flat, slot_src, slot_stats, ws,
                                   ws_bytes, dev_status, stream);
@@ -236,6 +280,7 @@ int eagle_expand_tree_warped(const eagle_tree_params* p, const float* draft_logi
                              int32_t* node_depth, int32_t* node_sib, int32_t* node_slot, float* node_value,
                              float* node_q, int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
                              float* slot_stats, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
   if (!draft_logits || !root_token || !node_tok || !node_parent || !node_depth || !node_sib || !node_slot ||
@@ -257,6 +302,7 @@ int eagle_expand_tree_masked(const eagle_tree_params* p, const float* draft_logi
                              int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src,
                              float* slot_stats, uint64_t* mask, int32_t* pos, void* ws, size_t ws_bytes,
                              int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
   if (!draft_logits || !root_token || !prefix_len || !node_tok || !node_parent || !node_depth || !node_sib ||
@@ -278,6 +324,7 @@ int eagle_expand_tree_noalloc(const eagle_tree_params* p, const float* draft_log
                               int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_tok,
                               float* pool_q, int32_t* pool_flat, int32_t* slot_src, float* slot_stats,
                               int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
   if (!draft_logits || !root_token || !node_tok || !node_parent || !node_depth || !node_sib || !node_slot ||
@@ -336,6 +383,7 @@ int eagle_expand_static(const eagle_tree_params* p, int32_t n, const int32_t* sh
                         int32_t* node_depth, int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q,
                         int32_t* pool_tok, float* pool_q, int32_t* pool_flat, int32_t* slot_src, float* slot_stats,
                         void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   StaticShape sh;
   int rc = check_static(p, n, shape_parent, &sh);
   if (rc != EAGLE_OK) return rc;
@@ -357,6 +405,7 @@ int eagle_verify_accept_static(const eagle_tree_params* p, int32_t n_slots, cons
                                const float* uniforms, int32_t* accept_len, int32_t* accept_path, int32_t* committed,
                                int32_t* n_committed, int32_t* near_tie, void* ws, size_t ws_bytes,
                                int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_static_params(p);
   if (rc != EAGLE_OK) return rc;
   if (n_slots < 1 || n_slots > p->m + 1) return EAGLE_ERR_SHAPE;
@@ -380,6 +429,7 @@ int eagle_verify_accept_static(const eagle_tree_params* p, int32_t n_slots, cons
 int eagle_build_tree_mask(int32_t batch, int32_t n, const int32_t* node_parent, const int32_t* node_depth,
                           const int32_t* prefix_len, uint64_t* mask, int32_t* pos, int32_t* dev_status,
                           void* stream) {
+  EAGLE_CALL_RANGE();
   if (batch < 1 || n < 1 || n > EAGLE_MAX_NODES) return EAGLE_ERR_SHAPE;
   if (!node_parent || !node_depth || !prefix_len || !mask || !pos) return EAGLE_ERR_NULL;
   return launch_status(launch_tree_mask(batch, n, node_parent, node_depth, prefix_len, mask, pos, dev_status,
@@ -390,6 +440,7 @@ int eagle_tree_attention(int32_t batch, int32_t n, int32_t hq, int32_t hkv, int3
                          int32_t dtype, const void* q, const void* k_prefix, const void* v_prefix,
                          const int32_t* prefix_len, const void* k_tree, const void* v_tree, const uint64_t* mask,
                          float scale, void* out, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_attn(batch, n, hq, hkv, head_dim, max_prefix, dtype);
   if (rc != EAGLE_OK) return rc;
   if (!isfinite(scale)) return EAGLE_ERR_SHAPE;
@@ -408,6 +459,7 @@ int eagle_tree_attention(int32_t batch, int32_t n, int32_t hq, int32_t hkv, int3
 int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dtype, const void* x, const void* w,
                          int32_t w_layout, float temperature, float* logits, float* row_stats, int32_t* row_argmax,
                          float* probs, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_lm(rows, hidden, vocab, dtype);
   if (rc != EAGLE_OK) return rc;
   if (w_layout != EAGLE_W_ROWMAJOR && w_layout != EAGLE_W_PACKED) return EAGLE_ERR_SHAPE;
@@ -424,6 +476,7 @@ int eagle_lmhead_softmax_compact(int32_t rows, int32_t hidden, int32_t vocab, co
                                  int32_t w_layout, float temperature, uint16_t* target_z16, float* block_max,
                                  float* row_stats, int32_t* row_argmax, void* ws, size_t ws_bytes,
                                  int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_lm(rows, hidden, vocab, EAGLE_BF16);
   if (rc != EAGLE_OK) return rc;
   if (w_layout != EAGLE_W_ROWMAJOR && w_layout != EAGLE_W_PACKED) return EAGLE_ERR_SHAPE;
@@ -444,6 +497,7 @@ int eagle_verify_accept_compact(const eagle_tree_params* p, int32_t n_slots, con
                                 const float* slot_stats, const float* uniforms, int32_t* accept_len,
                                 int32_t* accept_path, int32_t* committed, int32_t* n_committed, int32_t* near_tie,
                                 void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = n_slots > 0 ? check_static_params(p) : check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
   if (n_slots < 0 || n_slots > p->m + 1) return EAGLE_ERR_SHAPE;
@@ -474,6 +528,7 @@ size_t eagle_lmhead_packed_bytes(int32_t vocab, int32_t hidden, int32_t dtype) {
 
 int eagle_lmhead_pack_weight(int32_t vocab, int32_t hidden, int32_t dtype, const void* w, void* w_packed,
                              void* stream) {
+  EAGLE_CALL_RANGE();
   if (dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
   int rc = check_lm(1, hidden, vocab, dtype);
   if (rc != EAGLE_OK) return rc;
@@ -488,6 +543,7 @@ int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok, con
                         const float* draft_logits, const float* slot_stats, const float* uniforms,
                         int32_t* accept_len, int32_t* accept_path, int32_t* committed, int32_t* n_committed,
                         int32_t* near_tie, void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   return eagle_verify_accept_warped(p, nullptr, nullptr, node_tok, node_parent, node_slot, pool_tok, pool_flat,
                                     target_logits, target_stats, target_argmax, draft_logits, slot_stats, uniforms,
                                     accept_len, accept_path, committed, n_committed, near_tie, ws, ws_bytes,
@@ -501,6 +557,7 @@ int eagle_verify_accept_warped(const eagle_tree_params* p, const uint32_t* targe
                                const float* slot_stats, const float* uniforms, int32_t* accept_len,
                                int32_t* accept_path, int32_t* committed, int32_t* n_committed, int32_t* near_tie,
                                void* ws, size_t ws_bytes, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
   const bool greedy = !(p->temperature > 0.f);
@@ -526,6 +583,7 @@ int eagle_verify_accept_warped(const eagle_tree_params* p, const uint32_t* targe
 
 int eagle_gather_rows(int32_t n_rows, int32_t row_elems, int32_t dtype, const void* table, int32_t table_rows,
                       const int32_t* idx, void* out, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   if (n_rows < 0 || row_elems < 1 || table_rows < 1) return EAGLE_ERR_SHAPE;
   if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
   if (n_rows == 0) return EAGLE_OK;
@@ -542,6 +600,7 @@ int eagle_gather_rows(int32_t n_rows, int32_t row_elems, int32_t dtype, const vo
 int eagle_gather_rows_multi(int32_t n_tables, int32_t n_rows, int32_t dtype, int32_t table_rows, const int32_t* idx,
                             const int32_t* row_elems, const void* const* tables, void* const* outs,
                             int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   if (n_tables < 1 || n_tables > kGatherMaxTables || n_rows < 0 || table_rows < 1) return EAGLE_ERR_SHAPE;
   if (dtype != EAGLE_F32 && dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
   if (!row_elems || !tables || !outs) return EAGLE_ERR_NULL;
@@ -565,6 +624,7 @@ int eagle_commit_accepted(int32_t batch, int32_t n, int32_t hkv, int32_t head_di
                           const int32_t* accept_path, const void* k_tree, const void* v_tree, const void* x,
                           void* k_prefix, void* v_prefix, int32_t* prefix_len, void* feat, int32_t* dev_status,
                           void* stream) {
+  EAGLE_CALL_RANGE();
   if (batch < 0 || batch > (1 << 20) || n < 1 || n > EAGLE_MAX_NODES || hkv < 1 || head_dim < 1 ||
       max_prefix < 1 || hidden < 1 || depth < 1 || depth > EAGLE_MAX_DEPTH)
     return EAGLE_ERR_SHAPE;
@@ -588,6 +648,7 @@ int eagle_commit_accepted(int32_t batch, int32_t n, int32_t hkv, int32_t head_di
 
 int eagle_sampling_warp(int32_t rows, int32_t vocab, int32_t top_k, float top_p, int32_t min_keep, float temperature,
                         const float* logits, float* row_stats, uint32_t* bound, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   if (rows < 0 || rows > (1 << 24) || vocab < 1 || vocab > EAGLE_MAX_VOCAB || top_k < 0) return EAGLE_ERR_SHAPE;
   if (!(top_p > 0.f) || !(top_p <= 1.f) || min_keep < 1 || min_keep > vocab) return EAGLE_ERR_SHAPE;
   if (top_k != 0 && top_k < min_keep) return EAGLE_ERR_SHAPE;
@@ -624,6 +685,7 @@ int eagle_draft_forward(const eagle_tree_params* p, int32_t depth, const eagle_d
                         const void* k_prefix, const void* v_prefix, const int32_t* prefix_len,
                         const int32_t* pool_tok, const int32_t* slot_src, float* draft_logits, void* ws,
                         size_t ws_bytes, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   DraftLayout lay;
   int rc = check_draft(p, dims, &lay);
   if (rc != EAGLE_OK) return rc;
@@ -668,6 +730,7 @@ int eagle_draft_forward(const eagle_tree_params* p, int32_t depth, const eagle_d
 int eagle_expand_depth(const eagle_tree_params* p, int32_t depth, const float* draft_logits, int32_t* pool_tok,
                        float* pool_q, int32_t* slot_src, float* slot_stats, void* ws, size_t ws_bytes,
                        int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
   if (depth < 0 || depth >= p->depth) return EAGLE_ERR_SHAPE;
@@ -685,6 +748,7 @@ int eagle_expand_finish(const eagle_tree_params* p, const int32_t* root_token, c
                         const float* pool_q, int32_t* node_tok, int32_t* node_parent, int32_t* node_depth,
                         int32_t* node_sib, int32_t* node_slot, float* node_value, float* node_q, int32_t* pool_flat,
                         int32_t* slot_src, int32_t* dev_status, void* stream) {
+  EAGLE_CALL_RANGE();
   int rc = check_tree_params(p);
   if (rc != EAGLE_OK) return rc;
   if (!root_token || !pool_tok || !pool_q || !node_tok || !node_parent || !node_depth || !node_sib || !node_slot ||

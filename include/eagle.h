@@ -47,6 +47,10 @@
  *     mailboxes.  Calls that share one workspace must be ordered (same
  *     stream); calls on different streams need different workspaces.
  *   - Calls are deterministic: identical inputs give bit-identical outputs.
+ *   - Tracing: with EAGLE_ROCTX set (and not "0") in the environment, every
+ *     entry point that enqueues work pushes a roctx range named after itself
+ *     (the library loads ROCm's roctx library on the first such call);
+ *     otherwise no tracing library is loaded.
  *
  * Sources of the method (cited by page title and section):
  *   [E1] "EAGLE: Speculative Sampling Requires Rethinking Feature Uncertainty"
