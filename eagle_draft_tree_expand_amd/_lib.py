@@ -5,11 +5,14 @@ library.  Loading fails loudly when the library has not been built.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 from ctypes import POINTER, c_char_p, c_float, c_int32, c_size_t, c_uint64, c_void_p
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libeagle.so")
+# the same library built with LDS index checks (build(debug=True))
+DEBUG_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib", "libeagle_debug.so")
 
 EAGLE_OK = 0
 ERRORS = {-1: "EAGLE_ERR_NULL", -2: "EAGLE_ERR_SHAPE", -3: "EAGLE_ERR_DTYPE",
@@ -111,6 +114,20 @@ def load(path: str = LIB_PATH):
         fn.argtypes = args
     _lib = lib
     return lib
+
+
+@contextlib.contextmanager
+def using(path: str):
+    """Route every call of the binding to the library at `path` (another build,
+    e.g. DEBUG_LIB_PATH) inside the block, and back to the previous one after
+    it.  Not thread-safe: for tests."""
+    global _lib
+    prev = _lib
+    _lib = None
+    try:
+        yield load(path)
+    finally:
+        _lib = prev
 
 
 def check(fn_name: str, code: int):

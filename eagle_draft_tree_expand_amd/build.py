@@ -4,7 +4,9 @@
 
 Every .hip file under csrc/ is compiled to an object in _build/ (in parallel)
 and linked into lib/libeagle.so.  Packed-fp32 instruction selection is
-disabled for all device code.
+disabled for all device code.  build(debug=True) makes lib/libeagle_debug.so
+(objects in _build_debug/): the same code with EAGLE_LDS_CHECK, whose tree
+assembly and acceptance walk check their LDS indices (EAGLE_STATUS_LDS_INDEX).
 """
 from __future__ import annotations
 
@@ -17,8 +19,10 @@ from concurrent.futures import ThreadPoolExecutor
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
+BUILD_DEBUG = os.path.join(PKG, "_build_debug")
 LIBDIR = os.path.join(PKG, "lib")
 LIB = os.path.join(LIBDIR, "libeagle.so")
+LIB_DEBUG = os.path.join(LIBDIR, "libeagle_debug.so")
 ARCH = "gfx950"
 
 FLAGS = [
@@ -39,16 +43,19 @@ def sources():
     return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link the shared library; returns its path."""
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose: bool = False, debug: bool = False) -> str:
+    """Compile every source and link the shared library (the debug library
+    with debug=True); returns its path."""
+    bdir, lib = (BUILD_DEBUG, LIB_DEBUG) if debug else (BUILD, LIB)
+    flags = FLAGS + (["-DEAGLE_LDS_CHECK"] if debug else [])
+    os.makedirs(bdir, exist_ok=True)
     os.makedirs(LIBDIR, exist_ok=True)
     hipcc = _hipcc()
     srcs = sources()
 
     def compile_one(src):
-        obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-        cmd = [hipcc, *FLAGS, "-c", src, "-o", obj]
+        obj = os.path.join(bdir, os.path.basename(src) + ".o")
+        cmd = [hipcc, *flags, "-c", src, "-o", obj]
         r = subprocess.run(cmd, capture_output=True, text=True)
         out = r.stdout + r.stderr
         # hipcc's host pass does not know the packed-fp32 feature; that warning is harmless
@@ -61,14 +68,14 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max(1, min(8, os.cpu_count() or 1))) as ex:
         objs = list(ex.map(compile_one, srcs))
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, debug="--debug" in sys.argv[1:]))

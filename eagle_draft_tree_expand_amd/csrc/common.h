@@ -152,4 +152,21 @@ EDEV void set_status(int32_t* st, int bits) {
   if (st) atomicOr(st, bits);
 }
 
+// Index i of an LDS array of n elements.  The debug library (built with
+// EAGLE_LDS_CHECK) checks it: an index outside [0, n) is clamped into the
+// array and EAGLE_STATUS_LDS_INDEX is set, so tests can assert that no access
+// of the tree assembly or the walk left its array.  Release builds return i.
+EDEV int lds_index(int i, int n, int32_t* st) {
+#ifdef EAGLE_LDS_CHECK
+  if ((unsigned)i >= (unsigned)n) {
+    set_status(st, EAGLE_STATUS_LDS_INDEX);
+    return i < 0 ? 0 : n - 1;
+  }
+#else
+  (void)n;
+  (void)st;
+#endif
+  return i;
+}
+
 }  // namespace eagle

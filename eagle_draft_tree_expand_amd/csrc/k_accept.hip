@@ -545,7 +545,7 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
     float c_ep = 0.f, c_eq = 0.f;             // its fp32 terms
     double w_s = 0.0, w_Z = 1.0, w_R = 1.0;   // s_j, Z_j, R_j (wave 0, uniform)
     for (int step = 0; step <= D; ++step) {
-      const int u = cur_u;
+      const int u = lds_index(cur_u, N, status);
       const int slot = m_slot[u];
       Rows R;
       if (thp) {  // compact target rows
@@ -632,9 +632,9 @@ __global__ __launch_bounds__(kThreads) void accept_kernel(
         if (!(fill && vecr)) return;
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const int ci = tid * 4 + t * kThreads * 4;
-          const int v = gr.lo + ci;
+          const int v = gr.lo + tid * 4 + t * kThreads * 4;
           if (v < gr.hi) {
+            const int ci = lds_index(tid * 4 + t * kThreads * 4 + 3, cache_tokens, status) - 3;
             *reinterpret_cast<float4*>(&gr.cache[ci]) =
                 make_float4(eterm_p(rp[t].x, v, R), eterm_q(rq[t].x, v, R), eterm_p(rp[t].y, v + 1, R),
                             eterm_q(rq[t].y, v + 1, R));

@@ -590,7 +590,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     // parents' slots and the nodes' sibling ranks (layer 1: the root, slot 0)
     const int q0 = div_k(x0), q1 = div_k(x1);
     const int ps0 = d == 1 ? 0 : 1 + (d - 2) * k + q0, ps1 = d == 1 ? 0 : 1 + (d - 2) * k + q1;
-    const uint64_t pp0 = spath[ps0], pp1 = spath[has1 ? ps1 : ps0];
+    const uint64_t pp0 = spath[lds_index(ps0, S + 1, status)], pp1 = spath[lds_index(has1 ? ps1 : ps0, S + 1, status)];
     const ulonglong2 own = L2[g];  // nodes x0, x1 (a key of 0 past the layer's end)
     const uint64_t K0 = own.x, K1 = own.y;
     int r0 = 0, r1 = 0;
@@ -622,9 +622,9 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     // lane 0 records node x0, lane p1 node x1: its layer rank, its key in
     // sorted order and, for a frontier node, its slot's source and path
     auto record = [&](int x, int r, uint64_t K, uint64_t pp, int qx, bool f, int sl) __attribute__((always_inline)) {
-      lrank[lo + x] = r;
-      skeys[dl * LS + r] = K;
-      const int ss = f ? sl : S;
+      lrank[lds_index(lo + x, P, status)] = r;
+      skeys[lds_index(dl * LS + r, D * LS, status)] = K;
+      const int ss = lds_index(f ? sl : S, S + 1, status);
       slot_src[ss] = lo + x;
       spath[ss] = d == 1 ? (uint64_t)x : ((pp << 4) | (uint64_t)(x - mul_k(qx)));
     };
@@ -639,10 +639,10 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
       const bool a0 = f0 && j < k, a1 = f1 && j < k;
       const int rk0 = mul_k(r0) + j, rk1 = mul_k(r1) + j;  // child index inside the next layer
       const int c0 = lo + n + rk0, c1 = lo + n + rk1;        // its pool index: the next layer starts at lo + n
-      const float qa = q[a0 ? c0 : 0], qb = q[a1 ? c1 : 0];
+      const float qa = q[lds_index(a0 ? c0 : 0, P, status)], qb = q[lds_index(a1 ? c1 : 0, P, status)];
       uint64_t* Ln = lay + (d < D ? d : 0) * LS;
-      *(a0 ? Ln + rk0 : sink + 2 * part) = node_key(key_value(K0) * qa, c0);
-      *(a1 ? Ln + rk1 : sink + 2 * part + 1) = node_key(key_value(K1) * qb, c1);
+      *(a0 ? Ln + lds_index(rk0, LS, status) : sink + 2 * part) = node_key(key_value(K0) * qa, c0);
+      *(a1 ? Ln + lds_index(rk1, LS, status) : sink + 2 * part + 1) = node_key(key_value(K1) * qb, c1);
     } else {
       if (part == 0) record(x0, r0, K0, pp0, q0, f0, s0);
       if (part == p1 && has1) record(x1, r1, K1, pp1, q1, f1, s1);
@@ -651,9 +651,9 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
         const float v0 = key_value(K0), v1 = key_value(K1);
         for (int j = part; j < k; j += tpe) {
           const int c0 = s0 * k + j, c1 = s1 * k + j;
-          const float qa = q[f0 ? c0 : 0], qb = q[f1 ? c1 : 0];
-          if (f0) Ln[r0 * k + j] = node_key(v0 * qa, c0);
-          if (f1) Ln[r1 * k + j] = node_key(v1 * qb, c1);
+          const float qa = q[lds_index(f0 ? c0 : 0, P, status)], qb = q[lds_index(f1 ? c1 : 0, P, status)];
+          if (f0) Ln[lds_index(r0 * k + j, LS, status)] = node_key(v0 * qa, c0);
+          if (f1) Ln[lds_index(r1 * k + j, LS, status)] = node_key(v1 * qb, c1);
         }
       }
     }
@@ -715,10 +715,10 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     if (h == 0 && grank < m) {
       const int i = atomicAdd(&n_sel, 1);
       if (i < m) {
-        const int e = key_node(K);
+        const int e = lds_index(key_node(K), P, status);
         const int de = dc + 1;
         const int ps = div_k(e);
-        const uint64_t path = de == 1 ? (uint64_t)e : ((spath[ps] << 4) | (uint64_t)(e - ps * k));
+        const uint64_t path = de == 1 ? (uint64_t)e : ((spath[lds_index(ps, S + 1, status)] << 4) | (uint64_t)(e - ps * k));
         sel_e[i] = e;
         sel_dep[i] = de;
         sel_key[i] = D < 16 ? (((uint64_t)de << 60) | path) : (uint64_t)de;
@@ -743,16 +743,16 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     r += dpp_i<kDppXor2>(r);
     r += dpp_i<kDppHalfMirror>(r);
     r += dpp_i<kDppMirror>(r);
-    if (part == 0) flat_of[sel_e[i]] = 1 + r;
+    if (part == 0) flat_of[lds_index(sel_e[i], P, status)] = 1 + r;
   }
   __syncthreads();
   int bad = (tid == 0 && n_sel != m) ? 1 : 0;  // keys are distinct, so exactly m are selected
   for (int i = tid; i < cnt; i += nt) {
-    const int e = sel_e[i], de = sel_dep[i], f = flat_of[e];
+    const int e = lds_index(sel_e[i], P, status), de = sel_dep[i], f = lds_index(flat_of[e], N, status);
     int pf = 0;
     if (de > 1) {
-      const int pe = slot_src[e / k];
-      pf = pe >= 0 ? flat_of[pe] : -1;
+      const int pe = slot_src[lds_index(e / k, S + 1, status)];
+      pf = pe >= 0 ? flat_of[lds_index(pe, P, status)] : -1;
       if (pf < 0) bad = 1;  // parent not selected: the tree would not be connected
     }
     const int lr = lrank[e];
@@ -764,7 +764,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     node_depth[o] = de;
     node_sib[o] = e % k;
     node_slot[o] = (de < D && lr < k) ? 1 + (de - 1) * k + lr : -1;
-    node_value[o] = key_value(skeys[(de - 1) * LS + lr]);
+    node_value[o] = key_value(skeys[lds_index((de - 1) * LS + lr, D * LS, status)]);
     node_q[o] = q[e];
   }
   if (bad) set_status(status, EAGLE_STATUS_BAD_TREE);
@@ -794,7 +794,7 @@ __global__ __launch_bounds__(kTreeThreads) void tree_assemble_kernel(
     int a = f;
     for (int step = 0; a >= 0 && step <= D; ++step) {
       w[a >> 6] |= 1ull << (a & 63);
-      a = a == 0 ? -1 : fpar[a];
+      a = a == 0 ? -1 : fpar[lds_index(a, N, status)];
     }
     uint64_t* row = mask_out + ((size_t)b * N + f) * W;
     for (int x = 0; x < W; ++x) row[x] = w[x];

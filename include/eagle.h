@@ -94,6 +94,8 @@ extern "C" {
 #define EAGLE_STATUS_CAND_OVERFLOW 0x20 /* child re-scan candidate list overflowed       */
 #define EAGLE_STATUS_SYNC_TIMEOUT  0x40 /* a walk workgroup gave up waiting for its group */
 #define EAGLE_STATUS_CACHE_FULL    0x80 /* a prefix cache had no room for the commit     */
+#define EAGLE_STATUS_LDS_INDEX     0x100 /* debug library only: an LDS index of the tree
+                                            assembly or the walk left its array (clamped) */
 
 /* ---- limits -------------------------------------------------------------- */
 #define EAGLE_MAX_TOPK   16
