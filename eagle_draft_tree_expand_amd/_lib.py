@@ -29,7 +29,7 @@ EXPORTS = ("eagle_workspace_size", "eagle_workspace_init", "eagle_expand_tree", 
            "eagle_gather_rows_multi", "eagle_commit_accepted", "eagle_sampling_warp",
            "eagle_expand_tree_warped", "eagle_expand_tree_masked", "eagle_expand_tree_noalloc", "eagle_verify_accept_warped", "eagle_lmhead_packed_bytes",
            "eagle_lmhead_pack_weight", "eagle_draft_workspace_size", "eagle_draft_workspace_layout",
-           "eagle_draft_forward", "eagle_expand_depth",
+           "eagle_draft_forward", "eagle_expand_depth", "eagle_expand_depth_warped",
            "eagle_expand_finish", "eagle_static_tree_info", "eagle_static_workspace_size", "eagle_expand_static",
            "eagle_verify_accept_static", "eagle_lmhead_softmax_compact", "eagle_verify_accept_compact",
            "eagle_error_string", "eagle_abi_version")
@@ -85,6 +85,8 @@ _SIGS = {
     "eagle_draft_forward": (c_int32, [POINTER(TreeParams), c_int32, POINTER(DraftDims), POINTER(DraftWeights)] +
                             [_P] * 8 + [_P, c_size_t, _P, _P]),
     "eagle_expand_depth": (c_int32, [POINTER(TreeParams), c_int32] + [_P] * 5 + [_P, c_size_t, _P, _P]),
+    "eagle_expand_depth_warped": (c_int32, [POINTER(TreeParams), c_int32, c_int32, c_float] + [_P] * 6 +
+                                  [_P, c_size_t, _P, _P]),
     "eagle_expand_finish": (c_int32, [POINTER(TreeParams)] + [_P] * 12 + [_P, _P]),
     "eagle_static_tree_info": (c_int32, [c_int32, _P, _P, _P, _P, _P]),
     "eagle_static_workspace_size": (c_size_t, [POINTER(TreeParams), c_int32, _P] + [c_int32] * 5),

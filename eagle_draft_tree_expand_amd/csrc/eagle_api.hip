@@ -220,7 +220,7 @@ int check_draft(const eagle_tree_params* p, const eagle_draft_dims* d, DraftLayo
 
 extern "C" {
 
-int32_t eagle_abi_version(void) { return (1 << 16) | 4; }
+int32_t eagle_abi_version(void) { return (1 << 16) | 5; }
 
 const char* eagle_error_string(int32_t code) {
   switch (code) {
@@ -241,7 +241,9 @@ size_t eagle_workspace_size(const eagle_tree_params* p, int32_t hq, int32_t hkv,
   if (check_tree_params(p) != EAGLE_OK) return 0;
   const int B = p->batch, V = p->vocab, k = p->topk, D = p->depth;
   const int S = 1 + (D - 1) * k, N = p->m + 1;
-  size_t need = exp_ws_bytes(B, S, V, k);
+  // the expansion's records, and after them the warped statistics of
+  // eagle_expand_depth_warped
+  size_t need = (exp_ws_bytes(B, S, V, k) + 255) / 256 * 256 + (size_t)B * S * 2 * sizeof(float);
   if (hq > 0 && hkv > 0 && head_dim > 0) {
     const int dt = head_dim == 64 || head_dim == 128 ? EAGLE_BF16 : EAGLE_F32;
     if (check_attn(B, N, hq, hkv, head_dim, max_prefix, dt) != EAGLE_OK) return 0;
@@ -740,8 +742,35 @@ int eagle_expand_depth(const eagle_tree_params* p, int32_t depth, const float* d
   const int S = 1 + (D - 1) * k;
   if (ws_bytes < kCounterBytes + exp_ws_bytes(B, S, V, k)) return EAGLE_ERR_WORKSPACE;
   return launch_status(launch_expand_depth(B, S, V, D, k, p->m, p->temperature, p->seed, p->round_id, depth,
-                                           draft_logits, pool_tok, pool_q, slot_src, slot_stats, stage_area(ws),
-                                           dev_status, (hipStream_t)stream));
+                                           draft_logits, nullptr, pool_tok, pool_q, slot_src, slot_stats,
+                                           stage_area(ws), dev_status, (hipStream_t)stream));
+}
+
+int eagle_expand_depth_warped(const eagle_tree_params* p, int32_t depth, int32_t top_k, float top_p,
+                              const float* draft_logits, uint32_t* draft_bound, int32_t* pool_tok, float* pool_q,
+                              int32_t* slot_src, float* slot_stats, void* ws, size_t ws_bytes, int32_t* dev_status,
+                              void* stream) {
+  EAGLE_CALL_RANGE();
+  int rc = check_tree_params(p);
+  if (rc != EAGLE_OK) return rc;
+  if (depth < 0 || depth >= p->depth) return EAGLE_ERR_SHAPE;
+  const int B = p->batch, V = p->vocab, k = p->topk, D = p->depth;
+  if (!(p->temperature > 0.f)) return EAGLE_ERR_SHAPE;  // a warp applies to sampling only
+  if (top_k < 0 || (top_k != 0 && top_k < k) || !(top_p > 0.f) || !(top_p <= 1.f)) return EAGLE_ERR_SHAPE;
+  if (!draft_logits || !draft_bound || !pool_tok || !pool_q || !slot_src || !slot_stats || !ws) return EAGLE_ERR_NULL;
+  if (!aligned16(draft_logits)) return EAGLE_ERR_ALIGN;
+  const int S = 1 + (D - 1) * k;
+  const size_t units = (exp_ws_bytes(B, S, V, k) + 255) / 256 * 256;
+  if (ws_bytes < kCounterBytes + units + (size_t)B * S * 2 * sizeof(float)) return EAGLE_ERR_WORKSPACE;
+  // this depth's frontier rows: slot s0 + i of request b for i < n
+  const int s0 = depth == 0 ? 0 : 1 + (depth - 1) * k, n = depth == 0 ? 1 : k;
+  float* wstats = reinterpret_cast<float*>(reinterpret_cast<char*>(stage_area(ws)) + units);  // [B, S, 2]
+  hipError_t e = launch_warp_map(B * n, V, top_k, top_p, k, p->temperature, draft_logits, wstats, draft_bound,
+                                 dev_status, RowMap{n, S, s0}, (hipStream_t)stream);
+  if (e != hipSuccess) return launch_status(e);
+  return launch_status(launch_expand_depth(B, S, V, D, k, p->m, p->temperature, p->seed, p->round_id, depth,
+                                           draft_logits, draft_bound, pool_tok, pool_q, slot_src, slot_stats,
+                                           stage_area(ws), dev_status, (hipStream_t)stream));
 }
 
 int eagle_expand_finish(const eagle_tree_params* p, const int32_t* root_token, const int32_t* pool_tok,

@@ -936,10 +936,10 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
 }
 
 hipError_t launch_expand_depth(int B, int S, int V, int D, int k, int m, float T, uint64_t seed, uint64_t round_id,
-                               int depth, const float* rows, int32_t* pool_tok, float* pool_q, int32_t* slot_src,
-                               float* slot_stats, float* ws_units, int32_t* status, hipStream_t st) {
+                               int depth, const float* rows, const uint32_t* bound, int32_t* pool_tok, float* pool_q,
+                               int32_t* slot_src, float* slot_stats, float* ws_units, int32_t* status, hipStream_t st) {
   const SlotRange sr = depth == 0 ? SlotRange{0, 1} : SlotRange{1 + (depth - 1) * k, k};
-  hipError_t e = launch_children(B, S, V, k, T, seed, round_id, rows, nullptr, pool_tok, pool_q, slot_stats, ws_units,
+  hipError_t e = launch_children(B, S, V, k, T, seed, round_id, rows, bound, pool_tok, pool_q, slot_stats, ws_units,
                                  status, sr, st);
   if (e != hipSuccess || depth + 1 >= D) return e;
   // the next depth's frontier (slot_src of its slots); no node is written

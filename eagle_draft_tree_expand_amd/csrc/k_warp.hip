@@ -359,12 +359,14 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
   return out;
 }
 
+// grid: one workgroup per warped row; workgroup i warps row map_row(i, rm)
+// of z (and writes that row of stats and bound).
 __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float top_p, int min_keep, float Tp,
                                                          int mshift, const float* __restrict__ z,
                                                          float* __restrict__ stats, uint32_t* __restrict__ bound,
-                                                         int32_t* status) {
+                                                         int32_t* status, RowMap rm) {
   __shared__ WarpSmem sm;
-  const int row = blockIdx.x, tid = threadIdx.x;
+  const int row = map_row((int)blockIdx.x, rm), tid = threadIdx.x;
   RowCtx r;
   r.z = z + (size_t)row * V;
   r.vec = (V & 3) == 0 && ((uintptr_t)z & 15) == 0;
@@ -538,11 +540,18 @@ int warp_mass_shift(int V) {
   return 62 - lg;
 }
 
+hipError_t launch_warp_map(int rows, int V, int top_k, float top_p, int min_keep, float T, const float* z,
+                           float* stats, uint32_t* bound, int32_t* status, RowMap rm, hipStream_t st) {
+  if (rows == 0) return hipSuccess;
+  const float Tp = T > 0.f ? T : 1.0f;
+  warp_kernel<<<rows, kWThreads, 0, st>>>(V, top_k, top_p, min_keep, Tp, warp_mass_shift(V), z, stats, bound, status,
+                                          rm);
+  return hipGetLastError();
+}
+
 hipError_t launch_warp(int rows, int V, int top_k, float top_p, int min_keep, float T, const float* z, float* stats,
                        uint32_t* bound, int32_t* status, hipStream_t st) {
-  const float Tp = T > 0.f ? T : 1.0f;
-  warp_kernel<<<rows, kWThreads, 0, st>>>(V, top_k, top_p, min_keep, Tp, warp_mass_shift(V), z, stats, bound, status);
-  return hipGetLastError();
+  return launch_warp_map(rows, V, top_k, top_p, min_keep, T, z, stats, bound, status, RowMap{1 << 30, 0, 0}, st);
 }
 
 }  // namespace eagle

@@ -32,9 +32,11 @@ hipError_t launch_expand(int B, int S, int V, int D, int k, int m, float T, uint
 
 // Depth by depth: children of depth `depth`'s frontier slots (rows at their
 // slots of the [B, S, V] buffer), then the next depth's frontier into slot_src.
+// bound: sampling-warp bounds of the [B, S] slot rows (those of this depth's
+// slots are read), or null for no warp.
 hipError_t launch_expand_depth(int B, int S, int V, int D, int k, int m, float T, uint64_t seed, uint64_t round_id,
-                               int depth, const float* rows, int32_t* pool_tok, float* pool_q, int32_t* slot_src,
-                               float* slot_stats, float* ws_units, int32_t* status, hipStream_t st);
+                               int depth, const float* rows, const uint32_t* bound, int32_t* pool_tok, float* pool_q,
+                               int32_t* slot_src, float* slot_stats, float* ws_units, int32_t* status, hipStream_t st);
 // Rerank and flatten a complete pool.
 hipError_t launch_expand_finish(int B, int S, int V, int D, int k, int m, const int32_t* root, int32_t* node_tok,
                                 int32_t* node_parent, int32_t* node_depth, int32_t* node_sib, int32_t* node_slot,
@@ -81,11 +83,6 @@ hipError_t launch_commit(int B, int n, int hkv, int head_dim, int max_prefix, in
                          const int32_t* accept_len, const int32_t* accept_path, const void* kt, const void* vt,
                          const void* x, void* kp, void* vp, int32_t* prefix_len, void* feat, int32_t* status,
                          hipStream_t st);
-
-// ---- sampling warps (k_warp.hip) ----
-int warp_mass_shift(int V);
-hipError_t launch_warp(int rows, int V, int top_k, float top_p, int min_keep, float T, const float* z, float* stats,
-                       uint32_t* bound, int32_t* status, hipStream_t st);
 
 // ---- attention (k_attn.hip) ----
 struct AttnPlan {
@@ -214,6 +211,15 @@ hipError_t launch_product(int rows, int hidden, int V, const void* x, const void
                           int32_t* status, ProductOut* po, hipStream_t st);
 size_t lm_packed_bytes(int V, int hidden);
 hipError_t launch_pack_lmhead(int V, int hidden, const void* w, void* wp, hipStream_t st);
+
+// ---- sampling warps (k_warp.hip) ----
+int warp_mass_shift(int V);
+hipError_t launch_warp(int rows, int V, int top_k, float top_p, int min_keep, float T, const float* z, float* stats,
+                       uint32_t* bound, int32_t* status, hipStream_t st);
+// The same on `rows` rows picked by a row map: workgroup i warps row
+// map_row(i, rm) of z, stats and bound.
+hipError_t launch_warp_map(int rows, int V, int top_k, float top_p, int min_keep, float T, const float* z,
+                           float* stats, uint32_t* bound, int32_t* status, RowMap rm, hipStream_t st);
 
 // ---- synthetic EAGLE draft head (k_draft.hip) ----
 // Byte offsets in the draft workspace: per-round slot state (kept across the

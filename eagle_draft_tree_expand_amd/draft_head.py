@@ -56,11 +56,13 @@ class DeviceDraftHead:
                           prefix_len, tree["pool_tok"], tree["slot_src"], rows, self.ws, status)
 
 
-def draft_tree(head, rnd, data, T, round_id=0):
+def draft_tree(head, rnd, data, T, round_id=0, warp=None, draft_bound=None):
     """Draft one round's tree depth by depth into rnd.tree, with data.rows as the
-    [B, S, V] draft-row buffer (rnd: a DeviceRound, data: its DeviceInputs)."""
+    [B, S, V] draft-row buffer (rnd: a DeviceRound, data: its DeviceInputs).
+    warp = (top_k, top_p) with T > 0: each depth's rows are warped before its
+    children are drawn, their bounds kept in draft_bound [B, S, 2] uint32."""
     p = rnd.params(T, round_id, data.seed)
     for d in range(rnd.cfg.D):
         head.forward(p, d, data.roots, data.prefix_len, rnd.tree, data.rows, rnd.status)
-        ops.expand_depth(p, d, data.rows, rnd.tree, rnd.ws, rnd.status)
+        ops.expand_depth(p, d, data.rows, rnd.tree, rnd.ws, rnd.status, warp=warp, draft_bound=draft_bound)
     ops.expand_finish(p, data.roots, rnd.tree, rnd.status)

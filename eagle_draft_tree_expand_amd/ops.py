@@ -272,8 +272,19 @@ def draft_forward(p: TreeParams, depth, dims: DraftDims, w: DraftWeights, root_t
     check("eagle_draft_forward", rc)
 
 
-def expand_depth(p: TreeParams, depth, draft_logits, tree, ws, status=None):
-    """Children of one depth's frontier slots (and the next frontier) into tree's pool arrays."""
+def expand_depth(p: TreeParams, depth, draft_logits, tree, ws, status=None, warp=None, draft_bound=None):
+    """Children of one depth's frontier slots (and the next frontier) into tree's pool arrays.
+    warp = (top_k, top_p): the depth's rows are warped first, their bounds written
+    to draft_bound [B, S, 2] uint32 at their slots (eagle_expand_depth_warped)."""
+    if warp is not None:
+        if draft_bound is None:
+            raise ValueError("a warped expansion needs a draft_bound buffer")
+        rc = _lib.load().eagle_expand_depth_warped(p, int(depth), int(warp[0]), float(warp[1]), _ptr(draft_logits),
+                                                  _ptr(draft_bound), _ptr(tree["pool_tok"]), _ptr(tree["pool_q"]),
+                                                  _ptr(tree["slot_src"]), _ptr(tree["slot_stats"]), _ptr(ws),
+                                                  ws.numel(), _ptr(status), _stream())
+        check("eagle_expand_depth_warped", rc)
+        return
     rc = _lib.load().eagle_expand_depth(p, int(depth), _ptr(draft_logits), _ptr(tree["pool_tok"]),
                                        _ptr(tree["pool_q"]), _ptr(tree["slot_src"]), _ptr(tree["slot_stats"]),
                                        _ptr(ws), ws.numel(), _ptr(status), _stream())

@@ -16,7 +16,7 @@
  *   eagle_sampling_warp (+ the _warped variants of expand and accept)
  *                          top-k / nucleus applied to both distributions
  *   eagle_commit_accepted  the accepted path appended to the prefix cache
- *   eagle_draft_forward, eagle_expand_depth, eagle_expand_finish
+ *   eagle_draft_forward, eagle_expand_depth(_warped), eagle_expand_finish
  *                          the tree drafted depth by depth by a synthetic
  *                          EAGLE draft head
  *
@@ -526,7 +526,9 @@ int eagle_commit_accepted(int32_t batch, int32_t n, int32_t hkv, int32_t head_di
  *                        depth's frontier (slot_src of its slots);
  * and after depth D-1 eagle_expand_finish reranks and flattens the pool
  * exactly as eagle_expand_tree does.  Given the same draft rows, the three
- * give eagle_expand_tree's outputs (no sampling warp on this path).
+ * give eagle_expand_tree's outputs; with eagle_expand_depth_warped in place
+ * of eagle_expand_depth, eagle_expand_tree_warped's (the depth's rows warped
+ * as eagle_sampling_warp warps them).
  *
  * The head (random weights; the pages name its parts, not their internals):
  *   u = Wfc [f ; E[x]];  h = u + Wo attn(rms(u));
@@ -612,6 +614,23 @@ int eagle_draft_forward(const eagle_tree_params* p, int32_t depth, const eagle_d
 int eagle_expand_depth(const eagle_tree_params* p, int32_t depth, const float* draft_logits, int32_t* pool_tok,
                        float* pool_q, int32_t* slot_src, float* slot_stats, void* ws, size_t ws_bytes,
                        int32_t* dev_status, void* stream);
+
+/* eagle_expand_depth with the sampling warp of [HW] section 2 on the draft
+ * rows: this depth's frontier rows (slot 0 at depth 0, slots 1 + (d-1)k ..
+ * dk at depth d >= 1, of every request) are warped first, exactly as
+ * eagle_sampling_warp(top_k, top_p, min_keep = k, temperature) warps them,
+ * their bounds written to draft_bound [B, S, 2] uint32 at those slots (the
+ * other slots are left alone; after depth D-1 the buffer holds every
+ * expanded slot's bound, as eagle_verify_accept_warped takes them), and the
+ * children are drawn from the warped rows as eagle_expand_tree_warped draws
+ * them.  Needs temperature > 0 (a warp applies to sampling), top_k == 0 or
+ * top_k >= k, 0 < top_p <= 1 (else SHAPE), and a workspace of
+ * eagle_workspace_size (it also holds the warped rows' statistics).
+ * Everything else as eagle_expand_depth. */
+int eagle_expand_depth_warped(const eagle_tree_params* p, int32_t depth, int32_t top_k, float top_p,
+                              const float* draft_logits, uint32_t* draft_bound, int32_t* pool_tok, float* pool_q,
+                              int32_t* slot_src, float* slot_stats, void* ws, size_t ws_bytes, int32_t* dev_status,
+                              void* stream);
 
 /* Rerank and flatten the complete pool (after depth D-1): the node arrays,
  * pool_flat and slot_src exactly as eagle_expand_tree writes them. */

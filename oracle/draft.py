@@ -126,10 +126,12 @@ class DraftHead:
         return (np.asarray(W, np.float64) @ a).astype(np.float32)
 
 
-def expand_with_head(head, f_root, root, T, k, D, m, seed=0, req=0, round_id=0):
+def expand_with_head(head, f_root, root, T, k, D, m, seed=0, req=0, round_id=0, warp=None):
     """EAGLE-2 expansion where the row of each expanded node is the draft head's
     row on that node's root path, computed when the node joins the frontier
-    (the tree construction, child selection and rerank of oracle.expand)."""
+    (the tree construction, child selection and rerank of oracle.expand).
+    warp = (top_k, top_p) (T > 0): children are drawn from each row's warped
+    distribution, as oracle.expand.children_of_row draws them."""
     S = 1 + (D - 1) * k
     rows = np.zeros((S, np.asarray(head.lm).shape[0]), np.float32)
     stats = np.zeros((S, 2), np.float64)
@@ -137,7 +139,7 @@ def expand_with_head(head, f_root, root, T, k, D, m, seed=0, req=0, round_id=0):
 
     def children_fn(s, path):
         rows[s] = head.row(f_root, path)
-        toks, q, M, Ssum, t = expand.children_of_row(rows[s], T, k, seed, s, req, round_id)
+        toks, q, M, Ssum, t = expand.children_of_row(rows[s], T, k, seed, s, req, round_id, warp)
         stats[s] = (M, Ssum)
         ties[0] += t
         return toks, q

@@ -118,6 +118,64 @@ def test_expand_depth_matches_oracle_on_given_rows(T):
     assert flagged <= 1
 
 
+@pytest.mark.parametrize("T,warp", [(1.0, (50, 0.9)), (0.7, (0, 0.8)), (1.0, (12, 1.0))])
+def test_expand_depth_warped_matches_oracle_on_given_rows(T, warp):
+    """The three-call expansion with a sampling warp per depth, on rows computed
+    by the oracle's head: the tree equals the oracle's warped expansion, and
+    the bounds it keeps for the expanded slots are eagle_sampling_warp's on
+    the same rows (min_keep = k)."""
+    from eagle_draft_tree_expand_amd import ops
+    cfg = synth.get_config("mid_bf16")
+    inp, dinp, rnd, data, head = _setup(cfg)
+    heads = _oracle_heads(cfg, inp, dinp)
+    ora = [odraft.expand_with_head(heads[b], dinp.root_feat[b], int(inp.roots[b]), T, cfg.k, cfg.D, cfg.m,
+                                   inp.gumbel_seed, b, warp=warp) for b in range(cfg.B)]
+    data.set_rows(np.stack([o["rows"] for o in ora]))
+    bound = torch.zeros((cfg.B, cfg.S, 2), dtype=torch.int32, device="cuda")
+    p = rnd.params(T, 0, data.seed)
+    rnd.status.zero_()
+    for d in range(cfg.D):
+        ops.expand_depth(p, d, data.rows, rnd.tree, rnd.ws, rnd.status, warp=warp, draft_bound=bound)
+    ops.expand_finish(p, data.roots, rnd.tree, rnd.status)
+    dev = _host(rnd)
+    assert dev["status"] & ~0x8 == 0, hex(dev["status"])
+    stacked = {key: np.stack([o[key] for o in ora]) for key in ora[0] if key != "ties"}
+    stacked["ties"] = [o["ties"] for o in ora]
+    flagged = compare_expand(dev, stacked, cfg.k, f"warp {warp} T={T}")
+    assert flagged <= 1
+    ref_bound = torch.zeros_like(bound)
+    ref_stats = torch.zeros((cfg.B, cfg.S, 2), dtype=torch.float32, device="cuda")
+    ops.sampling_warp(cfg.B * cfg.S, cfg.V, warp[0], warp[1], cfg.k, T, data.rows, ref_stats, ref_bound, rnd.status)
+    assert torch.equal(bound, ref_bound)
+    # the expansion's slot statistics are the warped softmax's
+    np.testing.assert_array_equal(dev["slot_stats"].reshape(cfg.B, cfg.S, 2)[..., 0],
+                                  ref_stats.cpu().numpy()[..., 0])
+
+
+@pytest.mark.parametrize("T,warp", [(1.0, (50, 0.9)), (0.7, (20, 0.95))])
+def test_drafting_warped_equals_one_shot_warped_expansion(T, warp):
+    """Drafting with a warp per depth, then the one-shot warped expansion of the
+    rows the head drafted (bounds from eagle_sampling_warp on all slot rows):
+    the same tree bit for bit, and the same bounds at every slot."""
+    from eagle_draft_tree_expand_amd import draft_head, ops
+    cfg = synth.get_config("mid_bf16")
+    inp, dinp, rnd, data, head = _setup(cfg)
+    bound = torch.zeros((cfg.B, cfg.S, 2), dtype=torch.int32, device="cuda")
+    rnd.status.zero_()
+    draft_head.draft_tree(head, rnd, data, T, warp=warp, draft_bound=bound)
+    drafted = _host(rnd)
+    assert drafted["status"] & ~0x8 == 0, hex(drafted["status"])
+    ref_bound = torch.zeros_like(bound)
+    ref_stats = torch.zeros((cfg.B, cfg.S, 2), dtype=torch.float32, device="cuda")
+    ops.sampling_warp(cfg.B * cfg.S, cfg.V, warp[0], warp[1], cfg.k, T, data.rows, ref_stats, ref_bound, rnd.status)
+    assert torch.equal(bound, ref_bound)
+    ops.expand_tree(rnd.params(T, 0, data.seed), data.rows, data.roots, rnd.tree, rnd.ws, rnd.status,
+                    draft_bound=ref_bound)
+    one = _host(rnd)
+    for key in tree_keys() + ("pool_q", "node_value", "node_q", "slot_stats"):
+        assert np.array_equal(drafted[key], one[key]), key
+
+
 def _validate(dev, rows, head, f_root, root, T, k, D, m, seed, b):
     """Check a device tree against the oracle's rows on the device's own root
     paths: every drafted row matches the oracle's row for its path, and every
