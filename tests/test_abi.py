@@ -236,6 +236,17 @@ def test_draft_rejects(lib):
     assert e(ctypes.byref(p), 0, FAKE + 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None) == -6
     assert e(ctypes.byref(p), 0, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1024, None, None) == -4
     assert e(ctypes.byref(p), 0, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None) == -1
+    ew = lib.eagle_expand_depth_warped
+    wargs = lambda prm=p, depth=0, tk=50, tp=0.9, z=FAKE, bnd=FAKE, ws=1 << 30: (  # noqa: E731
+        ctypes.byref(prm), depth, tk, tp, z, bnd, FAKE, FAKE, FAKE, FAKE, FAKE, ws, None, None)
+    assert ew(*wargs(depth=4)) == -2
+    assert ew(*wargs(prm=L.TreeParams(2, 5003, 4, 3, 14, 0.0, 1, 0))) == -2  # greedy: no warp
+    assert ew(*wargs(tk=2)) == -2                                            # top_k below k
+    assert ew(*wargs(tp=0.0)) == -2
+    assert ew(*wargs(tp=1.5)) == -2
+    assert ew(*wargs(bnd=None)) == -1
+    assert ew(*wargs(z=FAKE + 4)) == -6
+    assert ew(*wargs(ws=1024)) == -4
     g = lib.eagle_expand_finish
     assert g(ctypes.byref(p), *([FAKE] * 11), None, None, None) == -1
     bad_p = L.TreeParams(2, 5003, 4, 0, 14, 1.0, 1, 0)
