@@ -18,9 +18,10 @@ embedding, one decoder layer, the shared LM head):
 
 At batch 64 the 640 frontier rows of depth 1 take the tiled GEMM, whose plain
 products split the hidden dimension into uneven slices (fc: 5 slices of 12 or
-13 chunks of 128; qkv: 3 of 10 or 11; down: 5 of 22 or 23); there 40 sampled
-rows (the first and the last included) and the attention of 5 requests are
-checked.
+13 chunks of 128; qkv: 3 of 10 or 11; down: 5 of 22 or 23); at batch 77 (770
+rows) the qkv product takes 128-row tiles in 3 uneven slices with a ragged
+last tile.  There 40 sampled rows (the first and the last included) and the
+attention of 5 requests are checked.
 """
 import numpy as np
 import pytest
@@ -70,11 +71,11 @@ class _Ws:
         return t.float().cpu().numpy() if dtype == torch.bfloat16 else t.cpu().numpy()
 
 
-@pytest.mark.parametrize("name", ["mid_bf16", "8b", "b64"])
-def test_draft_kernels_staged(name):
+@pytest.mark.parametrize("name,kw", [("mid_bf16", {}), ("8b", {}), ("b64", {}), ("b64", dict(B=77))])
+def test_draft_kernels_staged(name, kw):
     from eagle_draft_tree_expand_amd import draft_head, ops
     from eagle_draft_tree_expand_amd import round as dround
-    cfg = synth.get_config(name)
+    cfg = synth.get_config(name).with_(**kw)
     inp = synth.make_inputs(cfg)
     dinp = make_draft_inputs(cfg)
     wts = dround.DeviceWeights(inp)
