@@ -127,20 +127,34 @@ __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
   // tail) the wave falls back to KP rounds of wave argmax.
   UnitView u{units + ((size_t)row * gridDim.x * kExpUnitsPerChunk + (size_t)chunk * kExpUnitsPerChunk + wave) * (2 + 2 * KP), KP};
   auto idx_of = [&](int j) { return chunk * kExpChunk + (j >> 2) * (kExpThreads * 4) + tid * 4 + (j & 3); };
+  // A warped row keeps few tokens (top-k 50 of 128256: most waves hold none),
+  // so its -inf keys would tie at the bound and send the wave to the slow
+  // path below.  There the search and the candidates take the finite keys
+  // only; a wave with fewer than KP of them lists them, then its -inf tokens
+  // in index order (key desc, idx asc: every -inf key ranks after every
+  // finite one).  Unwarped rows rank -inf keys like any other.
   uint32_t uk[kPer];
   uint32_t lmax = 0;
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
     const uint32_t bits = __float_as_uint(key[j] + 0.0f);  // -0 -> +0: they tie like equal keys
     const uint32_t code = bits ^ ((uint32_t)((int32_t)bits >> 31) | 0x80000000u);
-    uk[j] = idx_of(j) < V ? code : 0u;
+    uk[j] = idx_of(j) < V && (!warped || key[j] != kNegInf) ? code : 0u;
     lmax = max(lmax, uk[j]);
   }
-  uint32_t thr = 0;
+  int nfin = KP;  // finite keys of the wave (counted for warped rows only)
+  if (warped) {
+    nfin = 0;
 #pragma unroll
-  for (int bit = 31; bit >= 0; --bit) {
-    const uint32_t c = thr | (1u << bit);
-    if (__popcll(__ballot(lmax >= c)) >= (unsigned)KP) thr = c;
+    for (int j = 0; j < kPer; ++j) nfin += __popcll(__ballot(uk[j] != 0u));
+  }
+  uint32_t thr = 0;
+  if (nfin >= KP) {
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t c = thr | (1u << bit);
+      if (__popcll(__ballot(lmax >= c)) >= (unsigned)KP) thr = c;
+    }
   }
   thr = max(thr, 1u);
   __shared__ uint64_t cand[4][64];
@@ -165,7 +179,37 @@ __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
       u.key(r) = __uint_as_float(bits);
       u.set_idx(r, (int)(0xffffffffu - (uint32_t)mine));
     }
-    if (lane >= total && lane < KP) { u.key(lane) = kNegInf; u.set_idx(lane, kIdxNone); }
+    int listed = total;
+    if (nfin < KP) {
+      // entries nfin .. KP-1: the wave's -inf tokens with the smallest ids.
+      // Ids ascend with (group j / 4, lane, j % 4); per group, a lane's
+      // count of such tokens is prefix-summed over the lanes from its bits.
+      const int need = KP - nfin;
+      int before = 0;  // such tokens in earlier groups
+      for (int g = 0; g < 4 && before < need; ++g) {
+        uint32_t mk = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int j = g * 4 + e;
+          if (idx_of(j) < V && key[j] == kNegInf) mk |= 1u << e;
+        }
+        const int c = __popc(mk);
+        const uint64_t b0 = __ballot(c & 1), b1 = __ballot(c & 2), b2 = __ballot(c & 4);
+        auto below = [&](uint64_t m) {
+          return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+        };
+        int r2 = before + below(b0) + 2 * below(b1) + 4 * below(b2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if ((mk >> e) & 1u) {
+            if (r2 < need) { u.key(nfin + r2) = kNegInf; u.set_idx(nfin + r2, idx_of(g * 4 + e)); }
+            ++r2;
+          }
+        before += __popcll(b0) + 2 * __popcll(b1) + 4 * __popcll(b2);
+      }
+      listed = nfin + min(before, need);
+    }
+    if (lane >= listed && lane < KP) { u.key(lane) = kNegInf; u.set_idx(lane, kIdxNone); }
   } else {
     float bk = kNegInf;
     int bi = kIdxNone;
