@@ -46,6 +46,7 @@ constexpr int kWList = 64;  // tokens tied at a cut key handled in wave 0
 // are listed once, sorted, and the nucleus, min_keep cut, M and S are taken
 // from the list instead of further passes over the row.
 constexpr int kWFast = 1024;
+static_assert(kWFast == kWThreads, "one rank counter per thread");
 
 struct FastList {
   uint32_t key[kWFast];  // gathered, unordered
@@ -60,7 +61,12 @@ struct FastList {
 
 struct WarpSmem {
   FastList fl;
-  unsigned long long hist[kWBuckets];
+  union {
+    unsigned long long hist[kWBuckets];  // radix passes
+    unsigned long long pk[kWFast];       // one-pass list: (key << 32) | id
+  };
+  uint32_t est[kWWaves];
+  uint32_t lzc;
   unsigned long long part[kWThreads / 64];
   double dred[kWWaves];
   float fred[kWWaves];
@@ -359,6 +365,183 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
   return out;
 }
 
+// One pass for a top-k cut of at most kWFast tokens.  The first batch of the
+// row (one load per thread, kept in registers) estimates a logit bound lz
+// that about sqrt(k * kWFast) tokens of the row reach: each wave takes an
+// order statistic of its lanes' maxima, scaled to the whole row, and the
+// bound is the median of the 16 waves' values.  The row is then read once,
+// two batches' loads in flight while one is filtered, and every token with
+// z >= lz (or z NaN) is listed in LDS and ranked by (key, id).  The list
+// holds the top k exactly when its k-th token has t > t(lz): t = z / T' does
+// not decrease with z, so every token left out (z < lz) has t <= t(lz) and
+// ranks after it.  With V <= kWFast every token is listed.  Returns k with
+// fl.skey/sid/st holding the first k tokens of the order, or 0 when the bound
+// missed (too few tokens reach it, or more than kWFast): the radix passes
+// then decide.
+//
+// The loads are branch-free, so that the compiler's wait for one batch does
+// not also wait for the batches behind it: lanes past the row read its last
+// element (and are masked by index), and batch indices past the end read the
+// last batch again.
+template <bool VEC>
+EDEV int onepass_topk(const RowCtx& r, int top_k, WarpSmem& sm, int* bad) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  FastList& fl = sm.fl;
+  if (tid == 0) fl.n = 0;
+  fl.key[tid] = 0u;  // rank counters of the list (kWFast == kWThreads)
+  const int V = r.V, nb = (V + kWBatch - 1) / kWBatch;
+  auto tok = [&](int v0, int i) {
+    return VEC ? v0 + ((i >> 2) * kWThreads + tid) * 4 + (i & 3) : v0 + i * kWThreads + tid;
+  };
+  auto load = [&](int b, float (&zz)[kWE]) {
+    const int v0 = min(b, nb - 1) * kWBatch;
+    if (VEC) {
+#pragma unroll
+      for (int j = 0; j < kWU; ++j) {
+        const float4 q = *reinterpret_cast<const float4*>(r.z + min(v0 + (j * kWThreads + tid) * 4, V - 4));
+        zz[4 * j] = q.x; zz[4 * j + 1] = q.y; zz[4 * j + 2] = q.z; zz[4 * j + 3] = q.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kWE; ++i) zz[i] = r.z[min(v0 + i * kWThreads + tid, V - 1)];
+    }
+  };
+  float za[kWE], zb[kWE], zc[kWE];
+  load(0, za);
+  load(1, zb);
+  load(2, zc);
+  float lz = kNegInf;
+  if (V > kWFast) {
+    float m = kNegInf;
+#pragma unroll
+    for (int i = 0; i < kWE; ++i)
+      if (tok(0, i) < V) m = fmaxf(m, za[i]);
+    const uint32_t c = tcode(m);
+    // a wave sees about min(V, batch) / 16 tokens of the first batch
+    const float target = sqrtf((float)top_k * (float)kWFast);
+    const float share = (float)min(V, kWBatch) / (16.0f * (float)V);
+    const int jw = max(1, min(64, (int)(target * share + 0.5f)));
+    uint32_t thr = 0;  // the jw-th largest lane code of this wave
+#pragma unroll
+    for (int bit = 31; bit >= 0; --bit) {
+      const uint32_t cand = thr | (1u << bit);
+      if (__popcll(__ballot(c >= cand)) >= (unsigned)jw) thr = cand;
+    }
+    if (lane == 0) sm.est[wave] = thr;
+    __syncthreads();
+    if (tid < 64) {  // median of the 16 wave values: the 8th largest (ties by wave)
+      const uint32_t e = lane < kWWaves ? sm.est[lane] : 0u;
+      int rank = 0;
+#pragma unroll
+      for (int q = 0; q < kWWaves; ++q) {
+        const uint32_t eq = __builtin_amdgcn_readlane(e, q);
+        rank += (eq > e || (eq == e && q < lane)) ? 1 : 0;
+      }
+      if (lane < kWWaves && rank == kWWaves / 2 - 1) sm.lzc = e;
+    }
+    __syncthreads();
+    const uint32_t lc = max(sm.lzc, tcode(kNegInf));
+    lz = __uint_as_float((lc & 0x80000000u) ? (lc & 0x7fffffffu) : ~lc);
+  } else {
+    __syncthreads();  // fl.n = 0 is seen before the first listing
+  }
+  uint64_t badm = 0;
+  auto filter = [&](const float (&zz)[kWE], int b) {
+    if (b >= nb) return;
+    const int v0 = b * kWBatch;
+    uint64_t anym = 0;
+    if (v0 + kWBatch <= V) {
+#pragma unroll
+      for (int i = 0; i < kWE; ++i) {
+        badm |= __ballot(!__builtin_isfinite(zz[i]));
+        anym |= __ballot(!(zz[i] < lz));
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < kWE; ++i) {
+        const bool ok = tok(v0, i) < V;
+        badm |= __ballot(ok && !__builtin_isfinite(zz[i]));
+        anym |= __ballot(ok && !(zz[i] < lz));
+      }
+    }
+    if (anym == 0ull) return;
+#pragma unroll
+    for (int i = 0; i < kWE; ++i) {
+      const int v = tok(v0, i);
+      const bool take = v < V && !(zz[i] < lz);
+      const uint64_t mask = __ballot(take);
+      if (mask == 0ull) continue;
+      const int leader = __ffsll((long long)mask) - 1;
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&fl.n, __popcll(mask));
+      base = __builtin_amdgcn_readlane(base, leader);
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      if (take && pos < kWFast) {
+        int b2 = 0;
+        const float t = t_from(r, zz[i], &b2);
+        sm.pk[pos] = ((unsigned long long)~tcode(t) << 32) | (uint32_t)v;
+        fl.t[pos] = t;
+      }
+    }
+  };
+  // ring of three register batches: batch b sits in za, zb, zc by b % 3
+  filter(za, 0);
+  for (int b = 1; b < nb; b += 3) {
+    load(b + 2, za);
+    filter(zb, b);
+    load(b + 3, zb);
+    filter(zc, b + 1);
+    load(b + 4, zc);
+    filter(za, b + 2);
+  }
+  if (badm) *bad = 1;
+  __syncthreads();
+  const int nl = fl.n;
+  if (nl < top_k || nl > kWFast) {
+    __syncthreads();  // every thread has read fl.n before it is reused
+    return 0;
+  }
+  // Rank by (key asc, id asc) = the packed value: entry e counts the entries
+  // below it, its comparisons split over `parts` threads (as many as the
+  // workgroup allows, at most 16) whose counts meet in fl.key[e].
+  int parts = 1;
+  while (parts < 16 && nl * parts * 2 <= kWThreads) parts *= 2;
+  {
+    const int e = tid / parts, p = tid - e * parts;
+    if (e < nl) {
+      const unsigned long long my = sm.pk[e];
+      const int q0 = p * nl / parts, q1 = (p + 1) * nl / parts;
+      int r0 = 0, r1 = 0, r2 = 0, r3 = 0;
+      int q = q0;
+      for (; q + 4 <= q1; q += 4) {
+        r0 += sm.pk[q] < my ? 1 : 0;
+        r1 += sm.pk[q + 1] < my ? 1 : 0;
+        r2 += sm.pk[q + 2] < my ? 1 : 0;
+        r3 += sm.pk[q + 3] < my ? 1 : 0;
+      }
+      for (; q < q1; ++q) r0 += sm.pk[q] < my ? 1 : 0;
+      const int cnt = (r0 + r1) + (r2 + r3);
+      if (cnt) atomicAdd(&fl.key[e], (uint32_t)cnt);
+    }
+  }
+  __syncthreads();
+  if (tid < nl) {
+    const int rank = (int)fl.key[tid];
+    if (rank < top_k) {
+      const unsigned long long my = sm.pk[tid];
+      fl.skey[rank] = (uint32_t)(my >> 32);
+      fl.sid[rank] = (int)(uint32_t)my;
+      fl.st[rank] = fl.t[tid];
+    }
+  }
+  __syncthreads();
+  int b3 = 0;
+  const bool ok = lz == kNegInf || fl.st[top_k - 1] > t_from(r, lz, &b3);
+  __syncthreads();  // fl.n, pk and the sorted list are read before any reuse
+  return ok ? top_k : 0;
+}
+
 // grid: one workgroup per warped row; workgroup i warps row map_row(i, rm)
 // of z (and writes that row of stats and bound).
 __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float top_p, int min_keep, float Tp,
@@ -379,6 +562,9 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
   Cut cut = all;
   int nA = V;
   if (top_k > 0 && top_k < V && top_k <= kWFast) {
+    FastList& fl = sm.fl;
+    int n = r.vec ? onepass_topk<true>(r, top_k, sm, &bad) : onepass_topk<false>(r, top_k, sm, &bad);
+    if (n == 0) {
     // The top-k cut's key needs no M (counts only).  One pass then lists
     // every token at or before that key (prefix) in LDS, where they are
     // ordered by (key, id): the list's first top_k tokens are the kept ones.
@@ -393,8 +579,7 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
       kc = select_cut(r, all, false, (double)top_k, sm, true, 3);
       lim_key = kc.key;
     }
-    FastList& fl = sm.fl;
-    if (tid == 0) { fl.n = 0; fl.ci = 0x7fffffff; }
+    if (tid == 0) fl.n = 0;
     __syncthreads();
     for (int v0 = 0; v0 < V; v0 += kWBatch) {
       float zz[kWE];
@@ -426,10 +611,51 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
         fl.st[rank] = fl.t[tid];
       }
       __syncthreads();
-      const int n = min(top_k, nall);  // the cut keeps exactly top_k tokens
+      n = min(top_k, nall);  // the cut keeps exactly top_k tokens
+    }
+    }
+    if (n > 0) {
+      if (tid == 0) fl.ci = 0x7fffffff;
+      __syncthreads();
       cut = Cut{fl.skey[n - 1], fl.sid[n - 1]};
       nA = top_k;
       r.M = n > 0 ? fl.st[0] : kNegInf;  // the first of the order holds max t
+      if (r.M != kNegInf && n <= 64) {
+        // the kept list fits one wave: wave 0 takes the nucleus and the sum
+        // alone, with the arithmetic of the workgroup version below (the
+        // other waves only ever add zeros)
+        if (bad) sm.bad = 1;
+        __syncthreads();
+        if (tid < 64) {
+          int last = n - 1;
+          if (top_p < 1.0f) {
+            const unsigned long long w = tid < n ? weight(r, fl.st[tid], true) : 0ull;
+            unsigned long long inc = w;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+              const unsigned long long y = __shfl_up(inc, o);
+              if (tid >= o) inc += y;
+            }
+            const unsigned long long sa = __shfl(inc, 63);
+            const double target = (double)top_p * (double)sa;
+            const uint64_t hit = __ballot(tid < n && (double)inc >= target && (double)(inc - w) < target);
+            int ci = hit ? __ffsll((long long)hit) - 1 : n - 1;
+            if (min_keep > 1) ci = max(ci, min(min_keep, nA) - 1);
+            last = ci;
+            cut = Cut{fl.skey[ci], fl.sid[ci]};
+          }
+          const double sp = (tid <= last && fl.st[tid] != kNegInf) ? exp((double)fl.st[tid] - (double)r.M) : 0.0;
+          const double sfin = wave_sum_d(sp);
+          if (tid == 0) {
+            stats[(size_t)row * 2] = r.M;
+            stats[(size_t)row * 2 + 1] = (float)sfin;
+            bound[(size_t)row * 2] = ~cut.key;
+            bound[(size_t)row * 2 + 1] = (uint32_t)cut.id;
+            if (sm.bad) set_status(status, EAGLE_STATUS_NONFINITE);
+          }
+        }
+        return;
+      }
       if (r.M != kNegInf) {
         int last = n - 1;  // index of the last kept token in the order
         if (top_p < 1.0f) {

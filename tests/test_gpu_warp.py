@@ -105,6 +105,50 @@ def test_warp_full_vocab_rows():
             np.testing.assert_allclose(st[r, 1], w["S"], rtol=2e-7)
 
 
+def _big_rows(kind, R, V, rng):
+    """Rows for the one-pass top-k: the bound estimated from the first 16384
+    tokens either holds (normal), lists too many tokens (ties, flat), too few
+    (desc: the first tokens are the largest), or has the k-th token at the
+    bound itself (ties)."""
+    if kind == "desc":
+        z = np.sort(rng.standard_normal((R, V)).astype(np.float32), axis=1)[:, ::-1]
+        z[1] = z[1, ::-1]  # ascending: the largest tokens sit in the ragged last batch
+        return np.ascontiguousarray(z)
+    if kind == "sparse":  # 3% finite, the rest -inf
+        z = rng.standard_normal((R, V)).astype(np.float32)
+        z[rng.random((R, V)) < 0.97] = -np.inf
+        return z
+    if kind == "flat":
+        return (1.0 + 1e-7 * rng.integers(0, 3, (R, V))).astype(np.float32)
+    return _rows(kind, R, V, rng)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "desc", "sparse", "flat", "peaked"])
+@pytest.mark.parametrize("V", [40000, 40001])
+def test_warp_multi_batch_rows(kind, V):
+    """Rows of three 16384-token batches (vector loads at V = 40000, scalar at
+    40001): the top-k cut agrees with the oracle whichever path decides it."""
+    rng = np.random.default_rng(hash((kind, V, "big")) % 2**32)
+    z = _big_rows(kind, 4, V, rng)
+    compared = total = 0
+    for T in (1.0, 0.7):
+        for top_k, top_p, min_keep in [(50, 0.9, 10), (200, 1.0, 1), (1000, 0.95, 1), (1, 1.0, 1)]:
+            st, bd, status = _run(z, top_k, top_p, min_keep, T)
+            codes = _codes(oexpand.scaled_logits(z, T))
+            for r in range(z.shape[0]):
+                w = owarp.warp_support(z[r], T, top_k, top_p, min_keep)
+                total += 1
+                if w["tie"]:
+                    continue
+                mask = (codes[r] > bd[r, 0]) | ((codes[r] == bd[r, 0]) & (np.arange(V) <= bd[r, 1]))
+                assert np.array_equal(mask, w["mask"]), (kind, V, T, top_k, top_p, min_keep, r)
+                assert st[r, 0] == np.float32(w["M"])
+                np.testing.assert_allclose(st[r, 1], w["S"], rtol=2e-7)
+                compared += 1
+            assert bool(status & 0x2) == bool(np.any(~np.isfinite(z)))
+    assert compared >= 0.5 * total, (compared, total)
+
+
 # ------------------------------------------------- warped expansion and walk
 import synth  # noqa: E402
 from gpu_helpers import compare_accept, compare_expand, small_cfg  # noqa: E402
