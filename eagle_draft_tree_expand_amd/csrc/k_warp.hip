@@ -41,6 +41,7 @@ EDEV bool before_eq(uint32_t key, int v, const Cut& c) { return key < c.key || (
 
 constexpr int kWBuckets = 4096;
 constexpr int kWList = 64;  // tokens tied at a cut key handled in wave 0
+constexpr int kWL2 = 4096;  // tokens of a nucleus's first-digit bucket listed in LDS
 
 // A top-k cut of at most this many tokens finishes in LDS: the kept tokens
 // are listed once, sorted, and the nucleus, min_keep cut, M and S are taken
@@ -67,6 +68,13 @@ struct WarpSmem {
   };
   uint32_t est[kWWaves];
   uint32_t lzc;
+  double e2[256];            // 2^(j/256), the mass table
+  unsigned long long lk[kWL2];  // nucleus bucket list: (key << 32) | id
+  float lt[kWL2];               // and t
+  int n2;
+  double tgt;                // a select's target (set by its first pass when taken as a fraction)
+  unsigned long long cum;    // fixed-point mass through a select's cut token
+  int cum_ok;
   unsigned long long part[kWThreads / 64];
   double dred[kWWaves];
   float fred[kWWaves];
@@ -126,7 +134,8 @@ struct RowCtx {
   int V;
   float Tp;
   float M;
-  double mscale;  // fixed-point units per unit mass
+  int mshift;        // fixed-point units per unit mass: 2^mshift
+  const double* e2;  // 2^(j/256), j < 256 (LDS)
 };
 
 EDEV float t_from(const RowCtx& r, float z, int* bad) {
@@ -163,11 +172,72 @@ EDEV void load_batch(const RowCtx& r, int v0, float (&zz)[kWE]) {
   }
 }
 
+// One pass over the row, batch by batch in order, two batches' loads in
+// flight while f(zz, b) takes batch b (all threads call f for every batch).
+// The loads are branch-free, so the compiler's wait for one batch does not
+// also wait for the batches behind it: lanes past the row read its last
+// element (f masks them by index, rowscan_tok(...) < V) and batch indices
+// past the end read the last batch again.
+template <bool VEC>
+EDEV int rowscan_tok(int v0, int i) {
+  return VEC ? v0 + ((i >> 2) * kWThreads + (int)threadIdx.x) * 4 + (i & 3) : v0 + i * kWThreads + (int)threadIdx.x;
+}
+template <bool VEC>
+EDEV void rowscan_load(const RowCtx& r, int nb, int b, float (&zz)[kWE]) {
+  const int v0 = min(b, nb - 1) * kWBatch, tid = threadIdx.x;
+  if (VEC) {
+#pragma unroll
+    for (int j = 0; j < kWU; ++j) {
+      const float4 q = *reinterpret_cast<const float4*>(r.z + min(v0 + (j * kWThreads + tid) * 4, r.V - 4));
+      zz[4 * j] = q.x; zz[4 * j + 1] = q.y; zz[4 * j + 2] = q.z; zz[4 * j + 3] = q.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < kWE; ++i) zz[i] = r.z[min(v0 + i * kWThreads + tid, r.V - 1)];
+  }
+}
+template <bool VEC, class F>
+EDEV void scan_row(const RowCtx& r, F&& f) {
+  const int nb = (r.V + kWBatch - 1) / kWBatch;
+  float za[kWE], zb[kWE], zc[kWE];
+  rowscan_load<VEC>(r, nb, 0, za);
+  rowscan_load<VEC>(r, nb, 1, zb);
+  rowscan_load<VEC>(r, nb, 2, zc);
+  f(za, 0);
+  for (int b = 1; b < nb; b += 3) {  // batch b sits in za, zb, zc by b % 3
+    rowscan_load<VEC>(r, nb, b + 2, za);
+    f(zb, b);
+    rowscan_load<VEC>(r, nb, b + 3, zb);
+    if (b + 1 < nb) f(zc, b + 1);
+    rowscan_load<VEC>(r, nb, b + 4, zc);
+    if (b + 2 < nb) f(za, b + 2);
+  }
+}
+
+// Fixed-point mass round(2^mshift exp(x)) of x = t - M <= 0 (exact in fp64:
+// t and M are fp32).  Tang's table method (ACM TOMS 15(2), 1989): x =
+// (256 e + j) ln2/256 + r with |r| <= ln2/512, exp(x) = 2^e 2^(j/256) e^r, e^r
+// by its Taylor series to r^5 (truncation below 1e-20).  Relative error a few
+// 1e-16, against 2^-mshift for the rounding to an integer.
+EDEV unsigned long long mass_fixed(double x, const RowCtx& r) {
+  if (!(x > -44.0)) return 0ull;  // below 2^mshift e^-44 < 1/2 (mshift <= 62); also -inf
+  constexpr double kInvL = 369.3299304675746;       // 256 / ln 2
+  constexpr double kL1 = 0x1.62e42fefa0000p-9;      // ln 2 / 256, leading 38 bits
+  constexpr double kL2 = 0x1.cf79abc9e3b3ap-48;     // the rest
+  const double kd = rint(x * kInvL);
+  const int k = (int)kd;
+  const double rr = fma(-kd, kL2, fma(-kd, kL1, x));  // kd * kL1 is exact (|k| < 2^15)
+  const double q = rr * fma(rr, fma(rr, fma(rr, fma(rr, 1.0 / 120, 1.0 / 24), 1.0 / 6), 0.5), 1.0);  // e^r - 1
+  const double tj = r.e2[k & 255];
+  const double v = ldexp(fma(tj, q, tj), r.mshift + (k >> 8));  // <= 2^mshift
+  return __double2ull_rn(v);
+}
+
 // Weight of token v in the select: 1 (count) or its fixed-point mass.
 EDEV unsigned long long weight(const RowCtx& r, float t, bool mass) {
   if (!mass) return 1ull;
   if (t == kNegInf) return 0ull;
-  return __double2ull_rn(exp((double)t - (double)r.M) * r.mscale);
+  return mass_fixed((double)t - (double)r.M, r);
 }
 
 // First token of the order (restricted to tokens before_eq `lim`) at which the
@@ -175,46 +245,67 @@ EDEV unsigned long long weight(const RowCtx& r, float t, bool mass) {
 // key_only: stop after the first npass digit passes and return {key prefix
 // of the crossing token, -1} (sm.below = weight of the tokens with smaller
 // key prefixes; after one pass sm.hist still holds the first digit's counts).
+//
+// frac > 0: the target is frac times the total weight of the tokens before
+// `lim`, taken from the first pass's histogram (the same integer sum a
+// separate pass would give).  On return sm.cum holds the weight through the
+// cut token when sm.cum_ok (a crossing was found, not the rounding guard).
+// pass0 > 0 resumes a select whose earlier digits (sm.prefix, sm.below) are
+// settled; n2 >= 0 then takes the tokens from the LDS list sm.lk/sm.lt (every
+// token sharing those digits, n2 of them) instead of the row.
 EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, WarpSmem& sm, bool key_only = false,
-                    int npass = 3) {
+                    int npass = 3, double frac = 0.0, int pass0 = 0, int n2 = -1) {
   const int tid = threadIdx.x, lane = tid & 63;
   int bad = 0;
-  if (tid == 0) { sm.prefix = 0; sm.below = 0; }
+  if (tid == 0) {
+    if (pass0 == 0) { sm.prefix = 0; sm.below = 0; }
+    sm.cum_ok = 0;
+  }
   // digits: key bits [31:20], [19:10], [9:0]
-  for (int pass = 0; pass < (key_only ? npass : 3); ++pass) {
+  for (int pass = pass0; pass < (key_only ? npass : 3); ++pass) {
     const int shift = pass == 0 ? 20 : pass == 1 ? 10 : 0;
     const int nb = pass == 0 ? 4096 : 1024;
     for (int x = tid; x < kWBuckets; x += kWThreads) sm.hist[x] = 0;
     __syncthreads();
     const uint32_t pre = sm.prefix;
     const int hshift = pass == 0 ? 32 : pass == 1 ? 20 : 10;  // bits above this digit must match
-    for (int v0 = 0; v0 < r.V; v0 += kWBatch) {
-      float zz[kWE];
-      load_batch(r, v0, zz);
+    auto add = [&](bool valid, uint32_t key, int v, float t) {
+      int d = -1;
+      unsigned long long w = 0;
+      if (valid && before_eq(key, v, lim) && (hshift == 32 || (key >> hshift) == (pre >> hshift))) {
+        w = weight(r, t, mass);
+        if (w) d = (int)((key >> shift) & (uint32_t)(nb - 1));
+      }
+      // one atomic per wave when every contributing lane shares the bucket
+      const uint64_t act = __ballot(d >= 0);
+      if (act == 0ull) return;
+      const int d0 = __builtin_amdgcn_readlane(d, __ffsll((long long)act) - 1);
+      if (__ballot(d >= 0 && d != d0) == 0ull) {
+        // counts: the ballot's population; masses: an integer sum over the
+        // wave (64-bit shuffles), exact for every vocabulary size
+        const unsigned long long tot = mass ? wave_sum_u64(w) : (unsigned long long)__popcll(act);
+        if (lane == __ffsll((long long)act) - 1) atomicAdd(&sm.hist[d0], tot);
+      } else if (d >= 0) {
+        atomicAdd(&sm.hist[d], w);
+      }
+    };
+    if (n2 >= 0) {
+      for (int i0 = 0; i0 < n2; i0 += kWThreads) {
+        const int i = i0 + tid;
+        const bool ok = i < n2;
+        const unsigned long long e = ok ? sm.lk[i] : 0ull;
+        add(ok, (uint32_t)(e >> 32), (int)(uint32_t)e, ok ? sm.lt[i] : kNegInf);
+      }
+    } else {  // one batch in flight: a mass pass is bound by its arithmetic
+      for (int v0 = 0; v0 < r.V; v0 += kWBatch) {
+        float zz[kWE];
+        load_batch(r, v0, zz);
 #pragma unroll
-      for (int j = 0; j < kWE; ++j) {
-        const int v = tok_of(r, v0, j);
-        int d = -1;
-        unsigned long long w = 0;
-        if (v < r.V) {
-          const float t = t_from(r, zz[j], &bad);
-          const uint32_t key = ~tcode(t);
-          if (before_eq(key, v, lim) && (hshift == 32 || (key >> hshift) == (pre >> hshift))) {
-            w = weight(r, t, mass);
-            if (w) d = (int)((key >> shift) & (uint32_t)(nb - 1));
-          }
-        }
-        // one atomic per wave when every contributing lane shares the bucket
-        const uint64_t act = __ballot(d >= 0);
-        if (act == 0ull) continue;
-        const int d0 = __builtin_amdgcn_readlane(d, __ffsll((long long)act) - 1);
-        if (__ballot(d >= 0 && d != d0) == 0ull) {
-          // counts: the ballot's population; masses: an integer sum over the
-          // wave (64-bit shuffles), exact for every vocabulary size
-          const unsigned long long tot = mass ? wave_sum_u64(w) : (unsigned long long)__popcll(act);
-          if (lane == __ffsll((long long)act) - 1) atomicAdd(&sm.hist[d0], tot);
-        } else if (d >= 0) {
-          atomicAdd(&sm.hist[d], w);
+        for (int j = 0; j < kWE; ++j) {
+          const int v = tok_of(r, v0, j);
+          const bool ok = v < r.V;
+          const float t = ok ? t_from(r, zz[j], &bad) : kNegInf;
+          add(ok, ~tcode(t), v, t);
         }
       }
     }
@@ -228,6 +319,10 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
       for (int o = 1; o < 64; o <<= 1) {
         const unsigned long long y = __shfl_up(inc, o);
         if (lane >= o) inc += y;
+      }
+      if (pass == 0 && frac > 0.0) {
+        target = frac * (double)__shfl(inc, 63);
+        if (lane == 0) sm.tgt = target;
       }
       const unsigned long long below = sm.below;
       const double exc = (double)(below + inc - s);
@@ -258,6 +353,7 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
       }
     }
     __syncthreads();
+    if (pass == 0 && frac > 0.0) target = sm.tgt;
   }
   if (key_only) {
     if (bad) sm.bad = 1;
@@ -271,19 +367,29 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
   const uint32_t key = sm.prefix;
   if (tid == 0) { sm.nlist = 0; sm.cut = Cut{key, -1}; }
   __syncthreads();
-  for (int v0 = 0; v0 < r.V; v0 += kWBatch) {
-    float zz[kWE];
-    load_batch(r, v0, zz);
+  auto tie = [&](uint32_t tk, int v, float t) {
+    if (tk != key || !before_eq(key, v, lim)) return;
+    const unsigned long long w = weight(r, t, mass);
+    if (!w) return;
+    const int i = atomicAdd(&sm.nlist, 1);
+    if (i < kWList) { sm.list_id[i] = v; sm.list_w[i] = w; }
+  };
+  if (n2 >= 0) {
+    for (int i = tid; i < n2; i += kWThreads) {
+      const unsigned long long e = sm.lk[i];
+      tie((uint32_t)(e >> 32), (int)(uint32_t)e, sm.lt[i]);
+    }
+  } else {
+    for (int v0 = 0; v0 < r.V; v0 += kWBatch) {
+      float zz[kWE];
+      load_batch(r, v0, zz);
 #pragma unroll
-    for (int j = 0; j < kWE; ++j) {
-      const int v = tok_of(r, v0, j);
-      if (v >= r.V) continue;
-      const float t = t_from(r, zz[j], &bad);
-      if (~tcode(t) != key || !before_eq(key, v, lim)) continue;
-      const unsigned long long w = weight(r, t, mass);
-      if (!w) continue;
-      const int i = atomicAdd(&sm.nlist, 1);
-      if (i < kWList) { sm.list_id[i] = v; sm.list_w[i] = w; }
+      for (int j = 0; j < kWE; ++j) {
+        const int v = tok_of(r, v0, j);
+        if (v >= r.V) continue;
+        const float t = t_from(r, zz[j], &bad);
+        tie(~tcode(t), v, t);
+      }
     }
   }
   __syncthreads();
@@ -307,6 +413,11 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
       const unsigned long long below = sm.below;
       const bool hit = lane < nl && (double)(below + inc) >= target && (double)(below + inc - w) < target;
       const uint64_t ball = __ballot(hit);
+      if (ball) {
+        const int l = __ffsll((long long)ball) - 1;
+        const unsigned long long cum = below + __shfl(inc, l);
+        if (lane == 0) { sm.cum = cum; sm.cum_ok = 1; }
+      }
       if (lane == 0)
         sm.cut = Cut{key, ball ? sm.sort_id[__ffsll((long long)ball) - 1] : (nl > 0 ? sm.sort_id[nl - 1] : -1)};
     }
@@ -337,7 +448,7 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
         const float t = t_of(r, v, &bad);
         if (~tcode(t) != key || !before_eq(key, v, lim)) continue;
         c += weight(r, t, mass);
-        if ((double)c >= target) { sm.cut = Cut{key, v}; break; }
+        if ((double)c >= target) { sm.cut = Cut{key, v}; sm.cum = c; sm.cum_ok = 1; break; }
       }
     }
     __syncthreads();
@@ -365,6 +476,61 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
   return out;
 }
 
+// Every token of the row (before `lim`, t finite) whose key shares the first
+// digit of `pre` goes to the LDS list sm.lk/sm.lt (sm.n2 counts them, also
+// past kWL2).
+template <bool VEC>
+EDEV void list_bucket(const RowCtx& r, const Cut& lim, uint32_t pre, WarpSmem& sm, int* bad) {
+  const int lane = threadIdx.x & 63;
+  scan_row<VEC>(r, [&](const float (&zz)[kWE], int b) {
+#pragma unroll
+    for (int j = 0; j < kWE; ++j) {
+      const int v = rowscan_tok<VEC>(b * kWBatch, j);
+      const bool ok = v < r.V;
+      const float t = ok ? t_from(r, zz[j], bad) : kNegInf;
+      const uint32_t key = ~tcode(t);
+      const bool take = ok && t != kNegInf && (key >> 20) == (pre >> 20) && before_eq(key, v, lim);
+      const uint64_t mask = __ballot(take);
+      if (mask == 0ull) continue;
+      const int leader = __ffsll((long long)mask) - 1;
+      int base = 0;
+      if (lane == leader) base = atomicAdd(&sm.n2, __popcll(mask));
+      base = __builtin_amdgcn_readlane(base, leader);
+      const int pos = base + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                                            __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+      if (take && pos < kWL2) {
+        sm.lk[pos] = ((unsigned long long)key << 32) | (uint32_t)v;
+        sm.lt[pos] = t;
+      }
+    }
+  });
+}
+
+// The nucleus cut: the first token of the order (before `lim`) at which the
+// running mass reaches frac of the total.  The first digit pass over the row
+// gives the total, the target and the crossing 12-bit bucket; one more pass
+// lists that bucket's tokens in LDS (a bucket is an eighth of an octave of t:
+// a few thousand tokens at most on these rows), and the other two digits and
+// the tied ids are settled from the list with the same arithmetic.  A bucket
+// of more than kWL2 tokens goes on with the row passes.
+EDEV Cut select_nucleus(const RowCtx& r, const Cut& lim, double frac, WarpSmem& sm) {
+  const int tid = threadIdx.x;
+  select_cut(r, lim, true, 0.0, sm, true, 1, frac);  // sets sm.prefix (first digit), sm.below, sm.tgt
+  const uint32_t pre = sm.prefix;
+  const double target = sm.tgt;
+  if (tid == 0) sm.n2 = 0;
+  __syncthreads();
+  int bad = 0;
+  if (r.vec)
+    list_bucket<true>(r, lim, pre, sm, &bad);
+  else
+    list_bucket<false>(r, lim, pre, sm, &bad);
+  if (bad) sm.bad = 1;
+  __syncthreads();
+  const int n2 = sm.n2;
+  return select_cut(r, lim, true, target, sm, false, 3, 0.0, 1, n2 <= kWL2 ? n2 : -1);
+}
+
 // One pass for a top-k cut of at most kWFast tokens.  The first batch of the
 // row (one load per thread, kept in registers) estimates a logit bound lz
 // that about sqrt(k * kWFast) tokens of the row reach: each wave takes an
@@ -378,76 +544,54 @@ EDEV Cut select_cut(const RowCtx& r, const Cut& lim, bool mass, double target, W
 // fl.skey/sid/st holding the first k tokens of the order, or 0 when the bound
 // missed (too few tokens reach it, or more than kWFast): the radix passes
 // then decide.
-//
-// The loads are branch-free, so that the compiler's wait for one batch does
-// not also wait for the batches behind it: lanes past the row read its last
-// element (and are masked by index), and batch indices past the end read the
-// last batch again.
 template <bool VEC>
 EDEV int onepass_topk(const RowCtx& r, int top_k, WarpSmem& sm, int* bad) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   FastList& fl = sm.fl;
   if (tid == 0) fl.n = 0;
   fl.key[tid] = 0u;  // rank counters of the list (kWFast == kWThreads)
-  const int V = r.V, nb = (V + kWBatch - 1) / kWBatch;
-  auto tok = [&](int v0, int i) {
-    return VEC ? v0 + ((i >> 2) * kWThreads + tid) * 4 + (i & 3) : v0 + i * kWThreads + tid;
-  };
-  auto load = [&](int b, float (&zz)[kWE]) {
-    const int v0 = min(b, nb - 1) * kWBatch;
-    if (VEC) {
-#pragma unroll
-      for (int j = 0; j < kWU; ++j) {
-        const float4 q = *reinterpret_cast<const float4*>(r.z + min(v0 + (j * kWThreads + tid) * 4, V - 4));
-        zz[4 * j] = q.x; zz[4 * j + 1] = q.y; zz[4 * j + 2] = q.z; zz[4 * j + 3] = q.w;
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < kWE; ++i) zz[i] = r.z[min(v0 + i * kWThreads + tid, V - 1)];
-    }
-  };
-  float za[kWE], zb[kWE], zc[kWE];
-  load(0, za);
-  load(1, zb);
-  load(2, zc);
+  const int V = r.V;
   float lz = kNegInf;
-  if (V > kWFast) {
-    float m = kNegInf;
+  // the bound, from the first batch (its loads and the next two in flight)
+  auto estimate = [&](const float (&za)[kWE]) {
+    if (V > kWFast) {
+      float m = kNegInf;
 #pragma unroll
-    for (int i = 0; i < kWE; ++i)
-      if (tok(0, i) < V) m = fmaxf(m, za[i]);
-    const uint32_t c = tcode(m);
-    // a wave sees about min(V, batch) / 16 tokens of the first batch
-    const float target = sqrtf((float)top_k * (float)kWFast);
-    const float share = (float)min(V, kWBatch) / (16.0f * (float)V);
-    const int jw = max(1, min(64, (int)(target * share + 0.5f)));
-    uint32_t thr = 0;  // the jw-th largest lane code of this wave
+      for (int i = 0; i < kWE; ++i)
+        if (rowscan_tok<VEC>(0, i) < V) m = fmaxf(m, za[i]);
+      const uint32_t c = tcode(m);
+      // a wave sees about min(V, batch) / 16 tokens of the first batch
+      const float target = sqrtf((float)top_k * (float)kWFast);
+      const float share = (float)min(V, kWBatch) / (16.0f * (float)V);
+      const int jw = max(1, min(64, (int)(target * share + 0.5f)));
+      uint32_t thr = 0;  // the jw-th largest lane code of this wave
 #pragma unroll
-    for (int bit = 31; bit >= 0; --bit) {
-      const uint32_t cand = thr | (1u << bit);
-      if (__popcll(__ballot(c >= cand)) >= (unsigned)jw) thr = cand;
-    }
-    if (lane == 0) sm.est[wave] = thr;
-    __syncthreads();
-    if (tid < 64) {  // median of the 16 wave values: the 8th largest (ties by wave)
-      const uint32_t e = lane < kWWaves ? sm.est[lane] : 0u;
-      int rank = 0;
-#pragma unroll
-      for (int q = 0; q < kWWaves; ++q) {
-        const uint32_t eq = __builtin_amdgcn_readlane(e, q);
-        rank += (eq > e || (eq == e && q < lane)) ? 1 : 0;
+      for (int bit = 31; bit >= 0; --bit) {
+        const uint32_t cand = thr | (1u << bit);
+        if (__popcll(__ballot(c >= cand)) >= (unsigned)jw) thr = cand;
       }
-      if (lane < kWWaves && rank == kWWaves / 2 - 1) sm.lzc = e;
+      if (lane == 0) sm.est[wave] = thr;
+      __syncthreads();
+      if (tid < 64) {  // median of the 16 wave values: the 8th largest (ties by wave)
+        const uint32_t e = lane < kWWaves ? sm.est[lane] : 0u;
+        int rank = 0;
+#pragma unroll
+        for (int q = 0; q < kWWaves; ++q) {
+          const uint32_t eq = __builtin_amdgcn_readlane(e, q);
+          rank += (eq > e || (eq == e && q < lane)) ? 1 : 0;
+        }
+        if (lane < kWWaves && rank == kWWaves / 2 - 1) sm.lzc = e;
+      }
+      __syncthreads();
+      const uint32_t lc = max(sm.lzc, tcode(kNegInf));
+      lz = __uint_as_float((lc & 0x80000000u) ? (lc & 0x7fffffffu) : ~lc);
+    } else {
+      __syncthreads();  // fl.n = 0 is seen before the first listing
     }
-    __syncthreads();
-    const uint32_t lc = max(sm.lzc, tcode(kNegInf));
-    lz = __uint_as_float((lc & 0x80000000u) ? (lc & 0x7fffffffu) : ~lc);
-  } else {
-    __syncthreads();  // fl.n = 0 is seen before the first listing
-  }
+  };
   uint64_t badm = 0;
   auto filter = [&](const float (&zz)[kWE], int b) {
-    if (b >= nb) return;
+    if (b == 0) estimate(zz);
     const int v0 = b * kWBatch;
     uint64_t anym = 0;
     if (v0 + kWBatch <= V) {
@@ -459,7 +603,7 @@ EDEV int onepass_topk(const RowCtx& r, int top_k, WarpSmem& sm, int* bad) {
     } else {
 #pragma unroll
       for (int i = 0; i < kWE; ++i) {
-        const bool ok = tok(v0, i) < V;
+        const bool ok = rowscan_tok<VEC>(v0, i) < V;
         badm |= __ballot(ok && !__builtin_isfinite(zz[i]));
         anym |= __ballot(ok && !(zz[i] < lz));
       }
@@ -467,7 +611,7 @@ EDEV int onepass_topk(const RowCtx& r, int top_k, WarpSmem& sm, int* bad) {
     if (anym == 0ull) return;
 #pragma unroll
     for (int i = 0; i < kWE; ++i) {
-      const int v = tok(v0, i);
+      const int v = rowscan_tok<VEC>(v0, i);
       const bool take = v < V && !(zz[i] < lz);
       const uint64_t mask = __ballot(take);
       if (mask == 0ull) continue;
@@ -485,16 +629,7 @@ EDEV int onepass_topk(const RowCtx& r, int top_k, WarpSmem& sm, int* bad) {
       }
     }
   };
-  // ring of three register batches: batch b sits in za, zb, zc by b % 3
-  filter(za, 0);
-  for (int b = 1; b < nb; b += 3) {
-    load(b + 2, za);
-    filter(zb, b);
-    load(b + 3, zb);
-    filter(zc, b + 1);
-    load(b + 4, zc);
-    filter(za, b + 2);
-  }
+  scan_row<VEC>(r, filter);
   if (badm) *bad = 1;
   __syncthreads();
   const int nl = fl.n;
@@ -555,7 +690,9 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
   r.vec = (V & 3) == 0 && ((uintptr_t)z & 15) == 0;
   r.V = V;
   r.Tp = Tp;
-  r.mscale = ldexp(1.0, mshift);
+  r.mshift = mshift;
+  r.e2 = sm.e2;
+  if (tid < 256) sm.e2[tid] = exp2((double)tid * (1.0 / 256));  // published by the first barrier below
   if (tid == 0) sm.bad = 0;
   int bad = 0;
   const Cut all{0xffffffffu, 0x7fffffff};
@@ -700,40 +837,69 @@ __global__ __launch_bounds__(kWThreads) void warp_kernel(int V, int top_k, float
       // an all -inf row: the passes below handle it as before
     }
   }
-  float lm = kNegInf;
-  for (int v0 = 0; v0 < V; v0 += kWBatch) {
-    float zz[kWE];
-    load_batch(r, v0, zz);
-#pragma unroll
-    for (int j = 0; j < kWE; ++j)
-      if (tok_of(r, v0, j) < V) lm = fmaxf(lm, t_from(r, zz[j], &bad));
-  }
-  if (bad) sm.bad = 1;
-  r.M = block_max(lm, sm);
+  // The top-k cut by counts, when the list above did not decide it (no M needed).
   if (top_k > 0 && top_k < V && nA == V) {
     cut = select_cut(r, all, false, (double)top_k, sm);
     nA = top_k;
   }
-  if (top_p < 1.0f) {
-    unsigned long long sa = 0;
+  // Before a nucleus, one listing pass gives M (the first token of the order)
+  // and the min_keep cut (its kk-th token); else a max pass gives M.
+  const int kk = max(1, min(min_keep, nA));
+  bool listed = false;
+  if (top_p < 1.0f && kk <= kWFast) {
+    const int n1 = r.vec ? onepass_topk<true>(r, kk, sm, &bad) : onepass_topk<false>(r, kk, sm, &bad);
+    listed = n1 > 0 && sm.fl.st[0] != kNegInf;
+    if (listed) r.M = sm.fl.st[0];
+    if (bad) sm.bad = 1;
+  }
+  if (!listed) {
+    float lm = kNegInf;
     for (int v0 = 0; v0 < V; v0 += kWBatch) {
       float zz[kWE];
       load_batch(r, v0, zz);
 #pragma unroll
-      for (int j = 0; j < kWE; ++j) {
-        const int v = tok_of(r, v0, j);
-        if (v >= V) continue;
-        const float t = t_from(r, zz[j], &bad);
-        if (before_eq(~tcode(t), v, cut)) sa += weight(r, t, true);
+      for (int j = 0; j < kWE; ++j)
+        if (tok_of(r, v0, j) < V) lm = fmaxf(lm, t_from(r, zz[j], &bad));
+    }
+    if (bad) sm.bad = 1;
+    r.M = block_max(lm, sm);
+  }
+  if (top_p < 1.0f) {
+    // the target is top_p of the top-k mass, summed by the select's first pass
+    Cut c = select_nucleus(r, cut, (double)top_p, sm);
+    bool have_cum = sm.cum_ok != 0;
+    const unsigned long long cum = sm.cum;
+    __syncthreads();  // read before a later select resets them
+    bool list_sum = false;
+    if (min_keep > 1) {
+      const Cut cm = listed ? Cut{sm.fl.skey[kk - 1], sm.fl.sid[kk - 1]}
+                            : select_cut(r, cut, false, (double)min(min_keep, nA), sm);
+      if (cm.key > c.key || (cm.key == c.key && cm.id > c.id)) {
+        c = cm;
+        have_cum = false;
+        list_sum = listed;  // the kept set is the list's first kk tokens
       }
     }
-    sa = block_sum_u64(sa, sm);
-    Cut c = select_cut(r, cut, true, (double)top_p * (double)sa, sm);
-    if (min_keep > 1) {
-      const Cut cm = select_cut(r, cut, false, (double)min(min_keep, nA), sm);
-      if (cm.key > c.key || (cm.key == c.key && cm.id > c.id)) c = cm;
-    }
     cut = c;
+    // S without another pass: the select's fixed-point mass through the cut
+    // (within V 2^-(mshift+1) of the fp64 sum, S >= 1), or the list's sum
+    if (have_cum || list_sum) {
+      double sfin;
+      if (have_cum) {
+        sfin = ldexp((double)cum, -r.mshift);
+      } else {
+        const double sp = (tid < kk && sm.fl.st[tid] != kNegInf) ? exp((double)sm.fl.st[tid] - (double)r.M) : 0.0;
+        sfin = block_sum_d(sp, sm);
+      }
+      if (tid == 0) {
+        stats[(size_t)row * 2] = r.M;
+        stats[(size_t)row * 2 + 1] = (float)sfin;
+        bound[(size_t)row * 2] = ~cut.key;
+        bound[(size_t)row * 2 + 1] = (uint32_t)cut.id;
+        if (sm.bad) set_status(status, EAGLE_STATUS_NONFINITE);
+      }
+      return;
+    }
   }
   double s = 0.0;
   if (r.M != kNegInf)
