@@ -9,19 +9,26 @@
 // written as its last token: (code of t_b, id_b), where the code is the
 // order-preserving unsigned image of t; token v is kept iff code_v > code_b,
 // or code_v == code_b and v <= id_b.  Row stats: M = max t and S = the kept
-// mass (fp64 sum, stored fp32), the statistics of the warped softmax.
+// mass (stored fp32), the statistics of the warped softmax.
 //
-// One workgroup of 1024 threads per row.  Each cut is a radix select on the
-// 32-bit key ~code (ascending key = descending t) in three passes over the
-// row (digits of 12, 10 and 10 bits): a 4096- or 1024-bucket histogram of the weight
-// (1 per token for counts, the mass for the nucleus) of the tokens that
-// share the key prefix chosen so far, then the bucket where the running
-// weight reaches the target; a last pass over the tokens equal to the chosen
-// key, in id order, finds the token.  Near-flat rows put most tokens in one
-// bucket, so a wave whose lanes share a bucket adds their summed weight with
-// one atomic instead of 64.  Masses are summed as fixed-point integers (2^mshift per unit, at
-// most V * 2^mshift < 2^63): integer sums are exact and independent of the
-// order of the atomic additions, so every run cuts at the same token.
+// One workgroup of 1024 threads per row.  Masses are fixed-point integers
+// (2^mshift per unit, at most V * 2^mshift < 2^63): integer sums are exact and
+// independent of the order of the atomic additions, so every run cuts at the
+// same token.
+//
+// A top-k cut of at most 1024 tokens takes one pass: a bound estimated from
+// the first batch lists the tokens at or above it in LDS, where they are
+// ranked (onepass_topk); the nucleus, min_keep, M and S then come from the
+// list.  Otherwise each cut is a radix select on the 32-bit key ~code
+// (ascending key = descending t), digits of 12, 10 and 10 bits: a 4096- or
+// 1024-bucket histogram of the weight (1 per token for counts, the mass for
+// the nucleus) of the tokens sharing the key prefix chosen so far, then the
+// bucket where the running weight reaches the target; the tokens equal to
+// the chosen key, in id order, give the token.  A wave whose lanes share a
+// bucket adds their summed weight with one atomic instead of 64.  For a
+// nucleus the first digit comes from the row and the rest from an LDS list
+// of the crossing bucket's tokens (select_nucleus), and S is the fixed-point
+// mass through the cut.
 #include "common.h"
 #include "kernels.h"
 
