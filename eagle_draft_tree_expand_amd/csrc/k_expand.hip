@@ -84,8 +84,7 @@ __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
 #pragma unroll
       for (int e = 0; e < 4; ++e) zz[e] = (base + e < V) ? z[base + e] : kNegInf;
     }
-    uint4 w4 = make_uint4(0, 0, 0, 0);
-    if (MODE != kGreedy) w4 = philox4x32_10(make_uint4((uint32_t)base >> 2, (uint32_t)s, (uint32_t)b, round_lo), k0, k1);
+    bool kept = false;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       const int j = it * 4 + e;
@@ -95,11 +94,22 @@ __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
       if (!valid) x = kNegInf;
       t[j] = MODE == kSampleT ? x / Tp : x;
       if (warped && !warp_keeps(t[j], base + e, wcode, wid)) t[j] = kNegInf;
-      if (MODE == kGreedy) {
-        key[j] = x;
+      kept |= t[j] != kNegInf;
+      if (MODE == kGreedy) key[j] = x;
+    }
+    if (MODE != kGreedy) {
+      // A warp drops most of a row: a wave none of whose lanes keeps a token
+      // of these four skips their noise (every key is -inf either way).
+      if (!warped || __any(kept)) {
+        const uint4 w4 = philox4x32_10(make_uint4((uint32_t)base >> 2, (uint32_t)s, (uint32_t)b, round_lo), k0, k1);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t wd = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
+          key[it * 4 + e] = t[it * 4 + e] + gumbel_fast(wd);  // -inf stays -inf
+        }
       } else {
-        const uint32_t wd = e == 0 ? w4.x : e == 1 ? w4.y : e == 2 ? w4.z : w4.w;
-        key[j] = t[j] + gumbel_fast(wd);  // -inf stays -inf
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[it * 4 + e] = kNegInf;
       }
     }
   }
