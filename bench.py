@@ -39,22 +39,34 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def lmhead_bytes(cfg, rows):
-    """Algorithmic bytes of one LM-head launch: W once, X, fp32 logits out."""
+def w_bytes(cfg, rows, wts=None):
+    """Bytes of W one LM-head launch reads: V x H in its dtype, or, where the
+    launch reads the z-packed form (wts.w_z, at most ZPACK_MAX_ROWS rows), one
+    header byte per fragment plus 768 bytes per coded and 1024 per raw fragment."""
+    if wts is not None and getattr(wts, "w_z", None) is not None and rows <= ZPACK_MAX_ROWS:
+        nfrag = (cfg.V + 63) // 64 * (cfg.H // 8)
+        return nfrag + (nfrag - wts.z_raw) * 768 + wts.z_raw * 1024
+    return cfg.V * cfg.H * (2 if cfg.dtype == "bf16" else 4)
+
+
+def lmhead_bytes(cfg, rows, wts=None):
+    """Algorithmic bytes of one LM-head launch: W once (in the form it is read), X, fp32 logits out."""
     esz = 2 if cfg.dtype == "bf16" else 4
-    return cfg.V * cfg.H * esz + rows * cfg.H * esz + rows * cfg.V * 4
+    return w_bytes(cfg, rows, wts) + rows * cfg.H * esz + rows * cfg.V * 4
 
 
-def round_bytes(cfg, prefix_total):
-    """Algorithmic bytes of one round: draft rows, prefix KV, tree Q/K/V and O, W, X, logits."""
+def round_bytes(cfg, prefix_total, wts=None):
+    """Algorithmic bytes of one round: draft rows, prefix KV, tree Q/K/V and O, W, X, logits.
+    Without wts, W counts as bf16 (the bytes the round would move from an uncompressed W)."""
     esz = 2 if cfg.dtype == "bf16" else 4
     rows = cfg.B * cfg.N
     draft = cfg.B * cfg.S * cfg.V * 4
     kv = prefix_total * cfg.hkv * cfg.dh * esz * 2
     tree = rows * (cfg.hq + 2 * cfg.hkv) * cfg.dh * esz + rows * cfg.hq * cfg.dh * esz
-    return draft + kv + tree + lmhead_bytes(cfg, rows)
+    return draft + kv + tree + lmhead_bytes(cfg, rows, wts)
 
 
+ZPACK_MAX_ROWS = 192  # EAGLE_ZPACK_MAX_ROWS
 LMHEAD_KERNEL_START = "__global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel("
 
 
@@ -450,10 +462,13 @@ def main():
     trees_s = rounds_s * cfg.B
     tok_s = r["committed"] / (r["total_ms"] / 1000.0)
     rows = cfg.B * cfg.N
-    lm_b = lmhead_bytes(cfg, rows)
+    lm_b = lmhead_bytes(cfg, rows, wts)
     achieved = lm_b / (r["lm_ms"] / 1000.0) / 1e9
     prefix_total = int(sum(int(s.prefix_len.sum().item()) for s in sets) / len(sets))
-    rb = round_bytes(cfg, prefix_total)
+    rb = round_bytes(cfg, prefix_total, wts)
+    rb16 = round_bytes(cfg, prefix_total)
+    zp = getattr(wts, "w_z", None) is not None and rows <= ZPACK_MAX_ROWS
+    nfrag = (cfg.V + 63) // 64 * (cfg.H // 8)
     traffic = read_traffic() if args.config == "8b" else None
     out = {
         "metric": "draft-tree verify rounds/sec + committed tokens/sec (8B shape, bs=1 and 64)",
@@ -476,9 +491,15 @@ def main():
         "committed_tokens_per_s": round(tok_s, 1),
         "tau_synthetic": round(r["committed"] / (args.steps * cfg.B), 4),
         "round_hbm_fraction": round(rb / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        "round_bf16_w_fraction": round(rb16 / (ms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+        "w_layout": ({"form": "z-packed (lossless: 12 bits per weight in coded fragments)",
+                      "raw_fragments": int(wts.z_raw), "fragments": nfrag,
+                      "w_bytes_read": w_bytes(cfg, rows, wts), "w_bytes_bf16": cfg.V * cfg.H * 2}
+                     if zp else {"form": "packed bf16"}),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel": "eagle_lmhead_softmax: lmhead_bf16 + lm_finalize, HIP events on its stream",
+                     "kernel": "eagle_lmhead_softmax: lmhead_bf16 + lm_finalize, HIP events on its stream"
+                               + (" (z-packed W)" if zp else ""),
                      "bytes_per_launch": lm_b,
                      "avg_launch_ms": round(r["lm_ms"], 5)},
         "device_status": r["status"],
@@ -552,14 +573,15 @@ def main():
             oms = o["total_ms"] / osteps
             optot = int(sum(int(x.prefix_len.sum().item()) for x in osets) / len(osets))
             orows = ocfg.B * ocfg.N
-            olb = lmhead_bytes(ocfg, orows)
+            olb = lmhead_bytes(ocfg, orows, owts)
             out["configs"][f"{name}" + ("" if T2 > 0 else "_greedy")] = {
                 "workload": f"{ocfg.name}: hidden {ocfg.H}, {ocfg.hq}q/{ocfg.hkv}kv x {ocfg.dh}, prefix {ocfg.Lmax}, "
                             f"vocab {ocfg.V}, depth {ocfg.D}, top-k {ocfg.k}, m {ocfg.m}, T={T2}, {ocfg.dtype}",
                 "trees_per_s": round(1000.0 / oms * ocfg.B, 2), "ms_per_step": round(oms, 4),
                 "committed_tokens_per_s": round(o["committed"] / (o["total_ms"] / 1000.0), 1),
                 "tau_synthetic": round(o["committed"] / (osteps * ocfg.B), 4),
-                "round_hbm_fraction": round(round_bytes(ocfg, optot) / (oms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                "round_hbm_fraction": round(round_bytes(ocfg, optot, owts) / (oms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
+                "round_bf16_w_fraction": round(round_bytes(ocfg, optot) / (oms / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
                 "lmhead_ms": round(o["lm_ms"], 5),
                 "lmhead_hbm_frac": round(olb / (o["lm_ms"] / 1000.0) / 1e9 / HBM_PEAK_GBS, 4),
                 "device_status": o["status"]}

@@ -18,7 +18,7 @@ EAGLE_OK = 0
 ERRORS = {-1: "EAGLE_ERR_NULL", -2: "EAGLE_ERR_SHAPE", -3: "EAGLE_ERR_DTYPE",
           -4: "EAGLE_ERR_WORKSPACE", -5: "EAGLE_ERR_LAUNCH", -6: "EAGLE_ERR_ALIGN", -7: "EAGLE_ERR_TOO_LARGE"}
 EAGLE_F32, EAGLE_BF16 = 0, 1
-EAGLE_W_ROWMAJOR, EAGLE_W_PACKED = 0, 1
+EAGLE_W_ROWMAJOR, EAGLE_W_PACKED, EAGLE_W_ZPACKED = 0, 1, 2
 STATUS_BITS = {0x1: "TOKEN_RANGE", 0x2: "NONFINITE", 0x4: "ZERO_RESIDUAL", 0x8: "TOPK_RESCAN",
                0x10: "BAD_TREE", 0x20: "CAND_OVERFLOW", 0x40: "SYNC_TIMEOUT",
                0x80: "CACHE_FULL"}
@@ -28,7 +28,7 @@ EXPORTS = ("eagle_workspace_size", "eagle_workspace_init", "eagle_expand_tree", 
            "eagle_tree_attention", "eagle_lmhead_softmax", "eagle_verify_accept", "eagle_gather_rows",
            "eagle_gather_rows_multi", "eagle_commit_accepted", "eagle_sampling_warp",
            "eagle_expand_tree_warped", "eagle_expand_tree_masked", "eagle_expand_tree_noalloc", "eagle_verify_accept_warped", "eagle_lmhead_packed_bytes",
-           "eagle_lmhead_pack_weight", "eagle_draft_workspace_size", "eagle_draft_workspace_layout",
+           "eagle_lmhead_pack_weight", "eagle_lmhead_zpack_bytes", "eagle_lmhead_zpack_weight", "eagle_draft_workspace_size", "eagle_draft_workspace_layout",
            "eagle_draft_forward", "eagle_expand_depth", "eagle_expand_depth_warped",
            "eagle_expand_finish", "eagle_static_tree_info", "eagle_static_workspace_size", "eagle_expand_static",
            "eagle_verify_accept_static", "eagle_lmhead_softmax_compact", "eagle_verify_accept_compact",
@@ -69,6 +69,8 @@ _SIGS = {
                                                          _P]),
     "eagle_lmhead_packed_bytes": (c_size_t, [c_int32, c_int32, c_int32]),
     "eagle_lmhead_pack_weight": (c_int32, [c_int32, c_int32, c_int32, _P, _P, _P]),
+    "eagle_lmhead_zpack_bytes": (c_size_t, [c_int32, c_int32]),
+    "eagle_lmhead_zpack_weight": (c_int32, [c_int32, c_int32, _P, _P, _P, _P]),
     "eagle_verify_accept": (c_int32, [POINTER(TreeParams)] + [_P] * 16 + [_P, c_size_t, _P, _P]),
     "eagle_gather_rows": (c_int32, [c_int32, c_int32, c_int32, _P, c_int32, _P, _P, _P, _P]),
     "eagle_gather_rows_multi": (c_int32, [c_int32, c_int32, c_int32, c_int32, _P, _P, _P, _P, _P, _P]),

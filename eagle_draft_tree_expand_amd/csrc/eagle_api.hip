@@ -220,7 +220,7 @@ int check_draft(const eagle_tree_params* p, const eagle_draft_dims* d, DraftLayo
 
 extern "C" {
 
-int32_t eagle_abi_version(void) { return (1 << 16) | 5; }
+int32_t eagle_abi_version(void) { return (1 << 16) | 6; }
 
 const char* eagle_error_string(int32_t code) {
   switch (code) {
@@ -464,8 +464,9 @@ int eagle_lmhead_softmax(int32_t rows, int32_t hidden, int32_t vocab, int32_t dt
   EAGLE_CALL_RANGE();
   int rc = check_lm(rows, hidden, vocab, dtype);
   if (rc != EAGLE_OK) return rc;
-  if (w_layout != EAGLE_W_ROWMAJOR && w_layout != EAGLE_W_PACKED) return EAGLE_ERR_SHAPE;
-  if (w_layout == EAGLE_W_PACKED && dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
+  if (w_layout != EAGLE_W_ROWMAJOR && w_layout != EAGLE_W_PACKED && w_layout != EAGLE_W_ZPACKED) return EAGLE_ERR_SHAPE;
+  if (w_layout != EAGLE_W_ROWMAJOR && dtype != EAGLE_BF16) return EAGLE_ERR_DTYPE;
+  if (w_layout == EAGLE_W_ZPACKED && (rows > EAGLE_ZPACK_MAX_ROWS || hidden > 16384 || lm_zlayout(vocab, hidden).bytes > 0xffffffffu)) return EAGLE_ERR_SHAPE;
   if (!(temperature >= 0.f) || !isfinite(temperature)) return EAGLE_ERR_SHAPE;
   if (!x || !w || !logits || !row_stats || !row_argmax || !ws) return EAGLE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w)) return EAGLE_ERR_ALIGN;
@@ -481,7 +482,8 @@ int eagle_lmhead_softmax_compact(int32_t rows, int32_t hidden, int32_t vocab, co
   EAGLE_CALL_RANGE();
   int rc = check_lm(rows, hidden, vocab, EAGLE_BF16);
   if (rc != EAGLE_OK) return rc;
-  if (w_layout != EAGLE_W_ROWMAJOR && w_layout != EAGLE_W_PACKED) return EAGLE_ERR_SHAPE;
+  if (w_layout != EAGLE_W_ROWMAJOR && w_layout != EAGLE_W_PACKED && w_layout != EAGLE_W_ZPACKED) return EAGLE_ERR_SHAPE;
+  if (w_layout == EAGLE_W_ZPACKED && (rows > EAGLE_ZPACK_MAX_ROWS || hidden > 16384 || lm_zlayout(vocab, hidden).bytes > 0xffffffffu)) return EAGLE_ERR_SHAPE;
   if (!(temperature >= 0.f) || !isfinite(temperature)) return EAGLE_ERR_SHAPE;
   if (!x || !w || !target_z16 || !block_max || !row_stats || !row_argmax || !ws) return EAGLE_ERR_NULL;
   if (!aligned16(x) || !aligned16(w) || ((uintptr_t)target_z16 & 7) != 0 || ((uintptr_t)block_max & 3) != 0)
@@ -537,6 +539,23 @@ int eagle_lmhead_pack_weight(int32_t vocab, int32_t hidden, int32_t dtype, const
   if (!w || !w_packed) return EAGLE_ERR_NULL;
   if (!aligned16(w) || !aligned16(w_packed)) return EAGLE_ERR_ALIGN;
   return launch_status(launch_pack_lmhead(vocab, hidden, w, w_packed, (hipStream_t)stream));
+}
+
+size_t eagle_lmhead_zpack_bytes(int32_t vocab, int32_t hidden) {
+  if (check_lm(1, hidden, vocab, EAGLE_BF16) != EAGLE_OK || hidden > 16384) return 0;
+  if (lm_zlayout(vocab, hidden).bytes > 0xffffffffu) return 0;  // one buffer resource spans it
+  return lm_zlayout(vocab, hidden).bytes;
+}
+
+int eagle_lmhead_zpack_weight(int32_t vocab, int32_t hidden, const void* w, void* w_z, int32_t* raw_fragments,
+                              void* stream) {
+  EAGLE_CALL_RANGE();
+  int rc = check_lm(1, hidden, vocab, EAGLE_BF16);
+  if (rc != EAGLE_OK) return rc;
+  if (hidden > 16384 || lm_zlayout(vocab, hidden).bytes > 0xffffffffu) return EAGLE_ERR_SHAPE;
+  if (!w || !w_z) return EAGLE_ERR_NULL;
+  if (!aligned16(w) || ((uintptr_t)w_z & 255) != 0 || ((uintptr_t)raw_fragments & 3) != 0) return EAGLE_ERR_ALIGN;
+  return launch_status(launch_zpack_lmhead(vocab, hidden, w, w_z, raw_fragments, (hipStream_t)stream));
 }
 
 int eagle_verify_accept(const eagle_tree_params* p, const int32_t* node_tok, const int32_t* node_parent,

@@ -97,7 +97,29 @@ EDEV float row16_max(float v) {
   return v;
 }
 
-template <bool PACKED>
+// Decode one z-packed fragment's lane registers to its 8 bf16 (layout in
+// eagle.h).  v is the 16-byte load of the lane: a coded fragment's is read from
+// 4 bytes before the lane's 12 (so v = (-, low bytes 0..3, low bytes 4..7,
+// codes)); a raw fragment's is its 16 bytes (high bytes 4..7, low bytes 0..3,
+// low bytes 4..7, high bytes 0..3).  A coded weight's high byte is base plus
+// the low three bits of its code (no carry out of a byte: base + 7 <= 127),
+// plus the code's top bit moved to bit 7; hb = the fragment's header byte.
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+EDEV u32x4 zdecode(u32x4 v, uint32_t hb) {
+  const uint32_t b4 = (hb & 0x7fu) * 0x01010101u;
+  const uint32_t c = v.w;
+  uint32_t ha = (c & 0x07070707u) + ((c << 4) & 0x80808080u) + b4;
+  uint32_t hh = ((c >> 4) & 0x07070707u) + (c & 0x80808080u) + b4;
+  if (hb & 0x80u) {
+    ha = v.w;
+    hh = v.x;
+  }
+  return u32x4{__builtin_amdgcn_perm(ha, v.y, 0x05010400u), __builtin_amdgcn_perm(ha, v.y, 0x07030602u),
+               __builtin_amdgcn_perm(hh, v.z, 0x05010400u), __builtin_amdgcn_perm(hh, v.z, 0x07030602u)};
+}
+
+// WL: the weight layout (EAGLE_W_ROWMAJOR, EAGLE_W_PACKED or EAGLE_W_ZPACKED).
+template <int WL>
 __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H, int V, float Tp,
                                                                  const uint16_t* __restrict__ x,
                                                                  const uint16_t* __restrict__ w,
@@ -105,8 +127,11 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
                                                                  int32_t* status, int hk, float* __restrict__ partial,
                                                                  RowMap rm, uint16_t* __restrict__ z16,
                                                                  float* __restrict__ bmax) {
+  constexpr bool PACKED = WL != EAGLE_W_ROWMAJOR;
+  constexpr bool ZP = WL == EAGLE_W_ZPACKED;
   constexpr int NT = 8;  // 16-column n-tiles per wave: 128 vocab columns
   __shared__ floatx4 xch[4][2][NT][64];  // accumulator exchange between the two hidden halves (64 KB)
+  extern __shared__ __attribute__((aligned(16))) unsigned char zh_lds[];  // z-packed: [wave][step][16] headers
   __shared__ u32x4 xst[2][2][8][64];     // X staging: [stage][hidden half][fragment ks*4 + mt][lane] (32 KB)
   __shared__ Rec wrec[4][kLmTileM];
 
@@ -161,6 +186,47 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
   // a fragment's four MFMAs of step s are issued, the load of the same
   // fragment for step s + 1 goes out into its registers, so each load flies
   // about one step ahead.  The last step issues no loads.
+  // z-packed: the wave's two 64-row groups and the header bytes of its
+  // fragments, copied to LDS per step (16 bytes: 8 per group); a step's 16
+  // become four scalar words (byte j & 3 of word j >> 2 is fragment j's): hc
+  // for the step being multiplied, hn for the one being loaded.  Each W load
+  // is one 16-byte load per lane whichever the fragment's form (only its base
+  // and lane stride differ), so the loop's counter waits are the packed
+  // layout's.
+  const int zg0 = min(n0 / 64, ngroups - 1), zg1 = min(n0 / 64 + 1, ngroups - 1);
+  const unsigned char* zb = reinterpret_cast<const unsigned char*>(w);
+  const ZLayout zl = lm_zlayout(V, H);
+  uint32_t hc[4] = {0u, 0u, 0u, 0u}, hn[4] = {0u, 0u, 0u, 0u};
+  unsigned char* zh = zh_lds + (size_t)wave * nsteps * 16;
+  auto zheaders = [&](int step, uint32_t* h) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(zh + step * 16);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = __builtin_amdgcn_readfirstlane(v[i]);
+  };
+  auto zbyte = [&](const uint32_t* h, int j) -> uint32_t { return (h[j >> 2] >> (8 * (j & 3))) & 0xffu; };
+  // Buffer loads: the fragment's byte offset in a scalar register, the lane's
+  // offset (12 or 16 bytes a lane) in a vector register; the whole z-packed
+  // weight is below 4 GB (the host checks).
+  const uint32_t zlc = (uint32_t)lane * 12u, zlr = (uint32_t)lane * 16u;
+  const __amdgpu_buffer_rsrc_t zrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)zb, (short)0, ZP ? (int)(uint32_t)zl.bytes : 0, 0x00020000);
+  auto zload = [&](int step, int j, uint32_t hb) -> u32x4 {
+    const uint32_t f = ((uint32_t)((j < 8) ? zg0 : zg1) * (uint32_t)nch + (uint32_t)(c0 + step)) * 8u + (uint32_t)(j & 7);
+    const bool raw = (hb & 0x80u) != 0;
+    const uint32_t so = raw ? (uint32_t)zl.raw_off + f * 1024u : (uint32_t)zl.slot_off + f * 768u - 4u;
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zrs, (int)(raw ? zlr : zlc), (int)so, 2));
+  };
+  if (ZP) {
+    for (int st = lane; st < nsteps; st += 64) {
+      const u32x2 a = *reinterpret_cast<const u32x2*>(zb + ((size_t)zg0 * nch + c0 + st) * 8);
+      const u32x2 b = *reinterpret_cast<const u32x2*>(zb + ((size_t)zg1 * nch + c0 + st) * 8);
+      *reinterpret_cast<u32x4*>(zh + st * 16) = u32x4{a.x, a.y, b.x, b.y};
+    }
+    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    zheaders(0, hc);
+  }
+
   u32x4 wf[2 * NT], sx[2];
   auto w_src = [&](int step, int j) -> const u32x4* {
     const int c = c0 + step;
@@ -179,7 +245,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
   sx[1] = *x_src(0, 1);
   __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-  for (int j = 0; j < 2 * NT; ++j) wf[j] = __builtin_nontemporal_load(w_src(0, j));
+  for (int j = 0; j < 2 * NT; ++j) wf[j] = ZP ? zload(0, j, zbyte(hc, j)) : __builtin_nontemporal_load(w_src(0, j));
   __builtin_amdgcn_sched_barrier(0);
   // One step: publish this wave's X fragments, barrier, then 64 MFMAs with A
   // read from LDS.  The barrier is bare: a fenced one would also wait for the
@@ -195,6 +261,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
       sx[0] = *x_src(step + 1, 0);
       sx[1] = *x_src(step + 1, 1);
     }
+    if (ZP && more) zheaders(step + 1, hn);
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       B8 a[4];
@@ -204,12 +271,16 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
       for (int t = 0; t < NT; ++t) {
         const int j = (t >> 2) * 8 + ks * 4 + (t & 3);
         B8 bb;
-        bb.w = wf[j];
+        bb.w = ZP ? zdecode(wf[j], zbyte(hc, j)) : wf[j];
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt].v, bb.v, acc[mt][t], 0, 0, 0);
-        if (more) wf[j] = __builtin_nontemporal_load(w_src(step + 1, j));
+        if (more) wf[j] = ZP ? zload(step + 1, j, zbyte(hn, j)) : __builtin_nontemporal_load(w_src(step + 1, j));
       }
+    }
+    if (ZP && more) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) hc[i] = hn[i];
     }
   };
   for (int st = 0; st + 1 < nsteps; ++st) step_body(st, true);
@@ -911,7 +982,79 @@ __global__ __launch_bounds__(256) void pack_w_kernel(int V, int H, const uint16_
   }
 }
 
+// Row-major W [V, H] -> z-packed layout (eagle.h): one wave per fragment,
+// lane l taking the same 8 weights as in the packed layout.  The wave's
+// extremes of e >> 1 decide the fragment's form; rows beyond V are zero.
+__global__ __launch_bounds__(256) void zpack_w_kernel(int V, int H, const uint16_t* __restrict__ w,
+                                                      unsigned char* __restrict__ wz, ZLayout zl,
+                                                      int32_t* __restrict__ raw_count) {
+  const int nch = H / kKC;
+  const int l = threadIdx.x & 63;
+  for (size_t f = ((size_t)blockIdx.x * blockDim.x + threadIdx.x) >> 6; f < zl.nfrag;
+       f += ((size_t)gridDim.x * blockDim.x) >> 6) {
+    const int j = (int)(f & 7);
+    const size_t gc = f >> 3;
+    const int c = (int)(gc % nch);
+    const size_t g = gc / nch;
+    const size_t row = g * 64 + (j & 3) * 16 + (l & 15);
+    const int k = c * kKC + (j >> 2) * 32 + (l >> 4) * 8;
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (row < (size_t)V) v = *reinterpret_cast<const u32x4*>(w + row * H + k);
+    uint32_t hi[8], lo[8];
+    int emax = 0, emin = 127;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = (v[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+      lo[i] = h & 0xffu;
+      hi[i] = h >> 8;
+      emax = max(emax, (int)(hi[i] & 0x7fu));
+      emin = min(emin, (int)(hi[i] & 0x7fu));
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      emax = max(emax, __shfl_xor(emax, o));
+      emin = min(emin, __shfl_xor(emin, o));
+    }
+    const int base = max(emax - 7, 0);
+    const bool raw = emin < base;
+    const uint32_t l0 = lo[0] | lo[1] << 8 | lo[2] << 16 | lo[3] << 24;
+    const uint32_t l1 = lo[4] | lo[5] << 8 | lo[6] << 16 | lo[7] << 24;
+    if (raw) {
+      const uint32_t h0 = hi[0] | hi[1] << 8 | hi[2] << 16 | hi[3] << 24;
+      const uint32_t h1 = hi[4] | hi[5] << 8 | hi[6] << 16 | hi[7] << 24;
+      *reinterpret_cast<u32x4*>(wz + zl.raw_off + f * 1024 + l * 16) = u32x4{h1, l0, l1, h0};
+    } else {
+      uint32_t codes = 0u;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t code = ((hi[i] >> 7) << 3) | ((hi[i] & 0x7fu) - (uint32_t)base);
+        codes |= code << (8 * (i & 3) + 4 * (i >> 2));
+      }
+      uint32_t* o = reinterpret_cast<uint32_t*>(wz + zl.slot_off + f * 768 + l * 12);
+      o[0] = l0;
+      o[1] = l1;
+      o[2] = codes;
+    }
+    if (l == 0) {
+      wz[f] = (unsigned char)(raw ? 0x80 : base);
+      if (raw && raw_count != nullptr) atomicAdd(raw_count, 1);
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_zpack_lmhead(int V, int H, const void* w, void* wz, int32_t* raw_count, hipStream_t st) {
+  const ZLayout zl = lm_zlayout(V, H);
+  if (raw_count != nullptr) {
+    hipError_t e = launch_zero_ints(raw_count, 1, st);
+    if (e != hipSuccess) return e;
+  }
+  const size_t threads = zl.nfrag * 64;
+  const int grid = (int)((threads + 255) / 256 < 16384 ? (threads + 255) / 256 : 16384);
+  zpack_w_kernel<<<grid, 256, 0, st>>>(V, H, (const uint16_t*)w, (unsigned char*)wz, zl, raw_count);
+  return hipGetLastError();
+}
 
 size_t lm_packed_bytes(int V, int H) { return (size_t)((V + 63) / 64) * (H / kKC) * 8 * 64 * 16; }
 
@@ -961,6 +1104,7 @@ hipError_t launch_lmhead_impl(int rows, int H, int V, int dtype, int w_layout, c
   const float Tp = (T > 0.f) ? T : 1.0f;
   int ntiles = lm_ntiles(V);
   if (dtype == EAGLE_BF16 && rows >= kGemmMinRows) {
+    if (w_layout == EAGLE_W_ZPACKED) return hipErrorInvalidValue;  // the host checks reject this first
     // plain products with few tiles split the hidden dimension (no statistics then)
     const GemmPlan gp = gemm_plan(rows, V, H, row_stats != nullptr);
     const int TM = gp.tm, ks = gp.ks;
@@ -1007,12 +1151,15 @@ hipError_t launch_lmhead_impl(int rows, int H, int V, int dtype, int w_layout, c
     const int ks = lm_ksplit(rows, V, H);
     float* partial = ks > 1 ? ws_part + lm_rec_floats(rows, V) : nullptr;
     dim3 grid(ntiles, lm_mtiles(rows), ks);
-    if (w_layout == EAGLE_W_PACKED)
-      lmhead_bf16_kernel<true><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
-                                                     ws_part, status, H / ks, partial, rm, z16, bmax);
-    else
-      lmhead_bf16_kernel<false><<<grid, kLmThreads, 0, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, logits,
-                                                      ws_part, status, H / ks, partial, rm, z16, bmax);
+    // z-packed: the header bytes of every wave's steps in dynamic LDS
+    const size_t zlds = w_layout == EAGLE_W_ZPACKED ? (size_t)8 * (H / ks / kKC / 2) * 16 : 0;
+#define EAGLE_STREAM(WLAY)                                                                                     \
+  lmhead_bf16_kernel<WLAY><<<grid, kLmThreads, zlds, st>>>(rows, H, V, Tp, (const uint16_t*)x, (const uint16_t*)w, \
+                                                           logits, ws_part, status, H / ks, partial, rm, z16, bmax)
+    if (w_layout == EAGLE_W_ZPACKED) EAGLE_STREAM(EAGLE_W_ZPACKED);
+    else if (w_layout == EAGLE_W_PACKED) EAGLE_STREAM(EAGLE_W_PACKED);
+    else EAGLE_STREAM(EAGLE_W_ROWMAJOR);
+#undef EAGLE_STREAM
     if (defer_ks) *defer_ks = ks;
     if (ks > 1 && !defer_ks) {
       hipError_t e0 = hipGetLastError();

@@ -211,6 +211,20 @@ hipError_t launch_product(int rows, int hidden, int V, const void* x, const void
                           int32_t* status, ProductOut* po, hipStream_t st);
 size_t lm_packed_bytes(int V, int hidden);
 hipError_t launch_pack_lmhead(int V, int hidden, const void* w, void* wp, hipStream_t st);
+// Lossless 12-bit form of the packed weight (EAGLE_W_ZPACKED): byte offsets of
+// its three areas for (V, hidden) and its size.
+struct ZLayout {
+  size_t nfrag, slot_off, raw_off, bytes;
+};
+__host__ __device__ inline ZLayout lm_zlayout(int V, int hidden) {
+  ZLayout z;
+  z.nfrag = (size_t)((V + 63) / 64) * (hidden / 8);
+  z.slot_off = (z.nfrag + 16 + 255) / 256 * 256;
+  z.raw_off = (z.slot_off + z.nfrag * 768 + 16 + 255) / 256 * 256;
+  z.bytes = z.raw_off + z.nfrag * 1024;
+  return z;
+}
+hipError_t launch_zpack_lmhead(int V, int hidden, const void* w, void* wz, int32_t* raw_count, hipStream_t st);
 
 // ---- sampling warps (k_warp.hip) ----
 int warp_mass_shift(int V);

@@ -11,7 +11,7 @@ import ctypes
 import torch
 
 from . import _lib
-from ._lib import EAGLE_BF16, EAGLE_F32, EAGLE_W_PACKED, EAGLE_W_ROWMAJOR, DraftDims, DraftWeights, TreeParams, check
+from ._lib import EAGLE_BF16, EAGLE_F32, EAGLE_W_PACKED, EAGLE_W_ROWMAJOR, EAGLE_W_ZPACKED, DraftDims, DraftWeights, TreeParams, check
 
 _DT = {torch.float32: EAGLE_F32, torch.bfloat16: EAGLE_BF16}
 
@@ -98,11 +98,39 @@ def tree_attention(batch, n, hq, hkv, head_dim, max_prefix, q, k_prefix, v_prefi
 def lmhead_softmax(rows, hidden, vocab, x, w, temperature, logits, row_stats, row_argmax, ws, probs=None,
                    status=None, packed=False):
     dt = _DT[x.dtype]
-    layout = EAGLE_W_PACKED if packed else EAGLE_W_ROWMAJOR
+    layout = _layout(packed)
     rc = _lib.load().eagle_lmhead_softmax(rows, hidden, vocab, dt, _ptr(x), _ptr(w), layout, float(temperature),
                                          _ptr(logits), _ptr(row_stats), _ptr(row_argmax), _ptr(probs), _ptr(ws),
                                          ws.numel(), _ptr(status), _stream())
     check("eagle_lmhead_softmax", rc)
+
+
+def _layout(packed):
+    """packed: False (row-major), True (packed) or "z" (z-packed)."""
+    if packed == "z":
+        return EAGLE_W_ZPACKED
+    return EAGLE_W_PACKED if packed else EAGLE_W_ROWMAJOR
+
+
+ZPACK_MAX_ROWS = 192  # EAGLE_ZPACK_MAX_ROWS: the streaming kernel's row range
+
+
+def zpack_supported(vocab, hidden):
+    return int(_lib.load().eagle_lmhead_zpack_bytes(vocab, hidden)) > 0
+
+
+def zpack_lmhead_weight(w):
+    """z-packed copy of a row-major bf16 LM-head weight [vocab, hidden] (new
+    device tensor) and the number of its fragments kept raw (synchronises)."""
+    vocab, hidden = w.shape
+    n = int(_lib.load().eagle_lmhead_zpack_bytes(vocab, hidden))
+    if n == 0:
+        raise ValueError("no z-packed layout for this shape")
+    wz = torch.empty(n, dtype=torch.uint8, device=w.device)
+    raw = torch.zeros(1, dtype=torch.int32, device=w.device)
+    check("eagle_lmhead_zpack_weight",
+          _lib.load().eagle_lmhead_zpack_weight(vocab, hidden, _ptr(w), _ptr(wz), _ptr(raw), _stream()))
+    return wz, int(raw.item())
 
 
 def pack_lmhead_weight(w):
@@ -179,7 +207,7 @@ def lmhead_softmax_compact(rows, hidden, vocab, x, w, temperature, z16, block_ma
                            status=None, packed=False):
     """The LM head without fp32 rows: z16 [rows, V] fp16 offsets, block_max [rows, ceil(V/128)]."""
     assert z16.dtype == torch.float16 and block_max.dtype == torch.float32
-    layout = EAGLE_W_PACKED if packed else EAGLE_W_ROWMAJOR
+    layout = _layout(packed)
     rc = _lib.load().eagle_lmhead_softmax_compact(rows, hidden, vocab, _ptr(x), _ptr(w), layout, float(temperature),
                                                  _ptr(z16), _ptr(block_max), _ptr(row_stats), _ptr(row_argmax),
                                                  _ptr(ws), ws.numel(), _ptr(status), _stream())

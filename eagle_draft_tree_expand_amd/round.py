@@ -33,16 +33,27 @@ def _t(a, dtype=None, device="cuda"):
 class DeviceWeights:
     """Inputs shared by every input set: LM-head weight and per-token q/k/v rows."""
 
-    def __init__(self, inp, device="cuda", packed=True):
+    def __init__(self, inp, device="cuda", packed=True, zpacked=True):
         c = inp.cfg
         dt = _TORCH_DT[c.dtype]
         self.w = _t(inp.w, dt, device)
-        # bf16 weights are also packed once into the MFMA-native streaming layout
+        # bf16 weights are also packed once into the MFMA-native streaming layout,
+        # and into its lossless 12-bit form, which the streaming kernel (verify
+        # rounds of at most EAGLE_ZPACK_MAX_ROWS rows) reads instead
         self.packed = packed and c.dtype == "bf16"
         self.w_packed = ops.pack_lmhead_weight(self.w) if self.packed else None
+        self.w_z, self.z_raw = None, 0
+        if self.packed and zpacked and ops.zpack_supported(c.V, c.H):
+            self.w_z, self.z_raw = ops.zpack_lmhead_weight(self.w)
         self.q_tab = _t(inp.q_tab, dt, device)
         self.k_tab = _t(inp.k_tab, dt, device)
         self.v_tab = _t(inp.v_tab, dt, device)
+
+    def lm_weight(self, rows):
+        """(tensor, layout flag for ops) of the LM-head weight a launch of `rows` rows reads."""
+        if self.w_z is not None and rows <= ops.ZPACK_MAX_ROWS:
+            return self.w_z, "z"
+        return (self.w_packed, True) if self.packed else (self.w, False)
 
 
 class DeviceInputs:
@@ -174,14 +185,14 @@ class DeviceRound:
 
     def lmhead(self, wts, T):
         c = self.cfg
-        w = wts.w_packed if wts.packed else wts.w
+        w, layout = wts.lm_weight(self.B * self.N)
         if self.compact:
             ops.lmhead_softmax_compact(self.B * self.N, c.H, c.V, self.x.view(self.B * self.N, c.H), w, T, self.z16,
                                        self.bmax, self.stats, self.argmax, self.ws, status=self.status,
-                                       packed=wts.packed)
+                                       packed=layout)
             return
         ops.lmhead_softmax(self.B * self.N, c.H, c.V, self.x.view(self.B * self.N, c.H), w, T, self.logits,
-                           self.stats, self.argmax, self.ws, status=self.status, packed=wts.packed)
+                           self.stats, self.argmax, self.ws, status=self.status, packed=layout)
 
     def accept(self, data, T, round_id=0, warp=None):
         """warp = (top_k, top_p) with T > 0: the target rows are warped first, the draft rows were

@@ -110,7 +110,31 @@ typedef enum { EAGLE_F32 = 0, EAGLE_BF16 = 1 } eagle_dtype;
  * PACKED: produced once by eagle_lmhead_pack_weight (bf16 only): every group
  * of 64 vocab rows becomes one contiguous stream ordered exactly as the MFMA
  * operand loads consume it, so each wave reads 1 KB contiguous per load. */
-typedef enum { EAGLE_W_ROWMAJOR = 0, EAGLE_W_PACKED = 1 } eagle_w_layout;
+typedef enum { EAGLE_W_ROWMAJOR = 0, EAGLE_W_PACKED = 1, EAGLE_W_ZPACKED = 2 } eagle_w_layout;
+/* ZPACKED: the PACKED order stored losslessly in 12 bits per weight where
+ * possible, made once by eagle_lmhead_zpack_weight (bf16 only).  The packed
+ * layout's unit is a fragment of 512 weights (64 lanes x 8 consecutive hidden
+ * values).  A bf16 weight is s | e (8 bits) | f (7 bits); its low byte
+ * (e & 1, f) is kept as is, and its high byte (s, e >> 1) becomes a 4-bit code
+ * (s, then e >> 1 minus a per-fragment base, 0..7).  A fragment whose e >> 1
+ * values span more than 8 keeps its high bytes whole ("raw").  Decoding
+ * restores every bit, so products equal those of the PACKED layout exactly;
+ * the streaming kernel reads 768 bytes per coded fragment instead of 1024.
+ * Byte layout for F fragments (F = ceil(vocab / 64) * hidden / 8):
+ *   [0, F)                     one byte per fragment: bit 7 raw, bits 0..6 base;
+ *   slot area (256-aligned)    768 bytes per fragment, lane l's 12 at 12 l:
+ *                              the low bytes of weights 0..3, of 4..7, then the
+ *                              codes (weight i < 4 in the low nibble of byte i,
+ *                              weight i >= 4 in the high nibble of byte i - 4);
+ *   raw area (256-aligned)     1024 bytes per fragment, lane l's 16 at 16 l: the
+ *                              high bytes of weights 4..7, the low bytes of
+ *                              0..3, of 4..7, the high bytes of 0..3 (written
+ *                              for raw fragments only).
+ * The raw area is sized for every fragment to be raw, so the form takes about
+ * 1.75 times the PACKED bytes in memory; a launch reads only each fragment's
+ * own form.  Only eagle_lmhead_softmax and eagle_lmhead_softmax_compact with
+ * at most EAGLE_ZPACK_MAX_ROWS rows and hidden <= 16384 read this layout. */
+#define EAGLE_ZPACK_MAX_ROWS 192
 
 /* Parameters of one round (host struct).
  *   temperature > 0: sampling at temperature T (both the target and the draft
@@ -363,6 +387,20 @@ int eagle_lmhead_softmax_compact(int32_t rows, int32_t hidden, int32_t vocab, co
  * zero-filled).  A one-time layout transform done when weights are loaded. */
 int eagle_lmhead_pack_weight(int32_t vocab, int32_t hidden, int32_t dtype, const void* w,
                              void* w_packed, void* stream);
+
+/* Bytes of the z-packed LM-head weight (EAGLE_W_ZPACKED) for a bf16
+ * (vocab, hidden) shape (0 if the shape has no packed form). */
+size_t eagle_lmhead_zpack_bytes(int32_t vocab, int32_t hidden);
+
+/* Write the z-packed form of a row-major bf16 LM-head weight w [vocab, hidden]
+ * into w_z (eagle_lmhead_zpack_bytes bytes, 256-byte aligned; rows past vocab
+ * are zero).  A one-time layout transform done when weights are loaded, as
+ * eagle_lmhead_pack_weight; asynchronous on `stream`.  If raw_fragments is
+ * non-NULL the call also counts the raw fragments into *raw_fragments (device
+ * int32, set to 0 by the call before counting), so a caller can report how
+ * many fragments the 12-bit form covers. */
+int eagle_lmhead_zpack_weight(int32_t vocab, int32_t hidden, const void* w, void* w_z,
+                              int32_t* raw_fragments, void* stream);
 
 /* Recursive speculative sampling down each request's tree.
  * Source: [E1] background A3 (accept x with probability min(1, p(x)/q(x));
