@@ -9,7 +9,7 @@ per-round data (draft rows, prefix KV) is not served from the 256 MB
 Infinity Cache; the LM-head weight is one copy.  Prints one JSON line.
 
 The LM-head kernel (one launch per round) is timed with HIP events on the
-stream it runs on (every 4th round of the timed loop), giving its achieved HBM
+stream it runs on (every 8th round of the timed loop), giving its achieved HBM
 bandwidth against 8 TB/s.  The CPU
 oracle is timed on a bounded sample of the same workload as a reference point
 (never a target).
@@ -122,7 +122,7 @@ def setup(cfg_name, T, n_sets, device="cuda"):
     return cfg, inps, wts, sets
 
 
-LM_EVENT_EVERY = 4  # LM-head launches bracketed by events: every 4th round (an event costs ~5 us of GPU idle)
+LM_EVENT_EVERY = 8  # LM-head launches bracketed by events: every 8th round (a bracketed round idles the GPU ~11 us)
 
 
 def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda", warp=None, compact=False, dist=False):

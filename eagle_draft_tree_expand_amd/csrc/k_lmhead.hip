@@ -272,10 +272,13 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
         const int j = (t >> 2) * 8 + ks * 4 + (t & 3);
         B8 bb;
         bb.w = ZP ? zdecode(wf[j], zbyte(hc, j)) : wf[j];
+        // z-packed: the decode has consumed the fragment's registers, so its next
+        // load can go out before the MFMAs
+        if (ZP && more) wf[j] = zload(step + 1, j, zbyte(hn, j));
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
           acc[mt][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt].v, bb.v, acc[mt][t], 0, 0, 0);
-        if (more) wf[j] = ZP ? zload(step + 1, j, zbyte(hn, j)) : __builtin_nontemporal_load(w_src(step + 1, j));
+        if (!ZP && more) wf[j] = __builtin_nontemporal_load(w_src(step + 1, j));
       }
     }
     if (ZP && more) {
