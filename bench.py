@@ -145,6 +145,10 @@ def time_rounds(cfg, wts, sets, T, steps, warmup, device="cuda", warp=None, comp
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     wall0 = time.perf_counter()
+    # one more untimed round between the synchronisation and the start event, so
+    # that the GPU is busy when the timed rounds start instead of idling while
+    # the host enqueues the first one
+    dr.step(wts, sets[warmup % len(sets)], T, round_id=warmup, warp=warp)
     t_start.record()
     for i in range(steps):
         d = sets[i % len(sets)]
@@ -219,17 +223,18 @@ def time_commit(cfg, wts, inp, rows, T, reps=40, device="cuda"):
             "status": int(dr.status.item())}
 
 
-def draft_bytes(cfg, inter, prefix_total):
+def draft_bytes(cfg, inter, prefix_total, wts=None):
     """Algorithmic HBM bytes of one drafting round (D depths): per depth the draft
-    layer's weights and the shared LM head once, the frontier's embedding rows,
+    layer's weights and the shared LM head once (in the form that depth reads:
+    z-packed with wts.w_z at few rows, else bf16), the frontier's embedding rows,
     the draft prefix K/V of every request, and the frontier's rows written by
     the LM head and read back by the expansion."""
     H, Q, KV, V = cfg.H, cfg.hq * cfg.dh, cfg.hkv * cfg.dh, cfg.V
-    w = 2 * (2 * H * H + H * (Q + 2 * KV) + Q * H + 3 * inter * H) + 2 * V * H
+    w = 2 * (2 * H * H + H * (Q + 2 * KV) + Q * H + 3 * inter * H)
     total = 0
     for d in range(cfg.D):
         R = cfg.B * (1 if d == 0 else cfg.k)
-        total += w + R * H * 2 + 2 * prefix_total * KV * 2 + 2 * R * V * 4
+        total += w + w_bytes(cfg, R, wts) + R * H * 2 + 2 * prefix_total * KV * 2 + 2 * R * V * 4
     return total
 
 
@@ -280,7 +285,7 @@ def time_drafting(cfg, wts, inp, T, steps, warmup, device="cuda"):
         dr.lmhead(wts, T)
         dr.accept(data, T, i)
         committed += int(dr.acc["n_committed"].sum().item())
-    nb = draft_bytes(cfg, head.inter, int(data.prefix_len.sum().item()))
+    nb = draft_bytes(cfg, head.inter, int(data.prefix_len.sum().item()), wts)
     out = {"workload": f"{cfg.name} shape, tree drafted depth by depth by a synthetic EAGLE draft head "
                        f"(FC 2H->H, one decoder layer with MLP {head.inter}, shared LM head; random weights)",
            "draft_ms_per_round": round(draft_ms, 4), "round_ms": round(round_ms, 4),

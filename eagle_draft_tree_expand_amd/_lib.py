@@ -47,7 +47,7 @@ class DraftDims(ctypes.Structure):
 
 class DraftWeights(ctypes.Structure):
     _fields_ = [("embed", c_void_p), ("fc", c_void_p), ("qkv", c_void_p), ("o", c_void_p), ("gate_up", c_void_p),
-                ("down", c_void_p), ("lm_head", c_void_p)]
+                ("down", c_void_p), ("lm_head", c_void_p), ("lm_head_z", c_void_p)]
 
 
 class EagleError(RuntimeError):

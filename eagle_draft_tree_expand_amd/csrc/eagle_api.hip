@@ -719,6 +719,8 @@ int eagle_draft_forward(const eagle_tree_params* p, int32_t depth, const eagle_d
                       draft_logits, ws};
   for (const void* q : al)
     if (!aligned16(q)) return EAGLE_ERR_ALIGN;
+  if (w->lm_head_z != nullptr && (((uintptr_t)w->lm_head_z & 255) != 0)) return EAGLE_ERR_ALIGN;
+  if (w->lm_head_z != nullptr && lm_zlayout(p->vocab, dims->hidden).bytes > 0xffffffffu) return EAGLE_ERR_SHAPE;
   if (ws_bytes < lay.total) return EAGLE_ERR_WORKSPACE;
   DraftArgs a;
   a.B = p->batch;

@@ -338,8 +338,10 @@ hipError_t launch_draft_forward(const DraftArgs& a, hipStream_t st) {
                                        a.status);
   EAGLE_CK(hipGetLastError());
   // draft rows of the frontier at their slots: row r -> (r / kd) * S + s0 + r % kd
-  EAGLE_CK(launch_lmhead_map(R, H, a.V, EAGLE_BF16, EAGLE_W_PACKED, P16(L.xa), a.w.lm_head, 1.f, a.rows, nullptr,
-                             nullptr, nullptr, gws, a.status, RowMap{kd, S, s0}, st));
+  const bool lz = a.w.lm_head_z != nullptr && R <= EAGLE_ZPACK_MAX_ROWS;
+  EAGLE_CK(launch_lmhead_map(R, H, a.V, EAGLE_BF16, lz ? EAGLE_W_ZPACKED : EAGLE_W_PACKED, P16(L.xa),
+                             lz ? a.w.lm_head_z : a.w.lm_head, 1.f, a.rows, nullptr, nullptr, nullptr, gws, a.status,
+                             RowMap{kd, S, s0}, st));
 #undef EAGLE_CK
   return hipSuccess;
 }

@@ -45,7 +45,9 @@ class DeviceDraftHead:
         self.inter = dinp.inter
         self.cap = dinp.cap
         self.dims = ops.draft_dims(c.H, c.hq, c.hkv, c.dh, self.inter, self.cap)
-        self.weights = ops.draft_weights(self.embed, self.fc, self.qkv, self.o, self.gate_up, self.down, self.lm)
+        self.lm_z = getattr(wts, "w_z", None)  # the round's z-packed LM head, read by depths of few rows
+        self.weights = ops.draft_weights(self.embed, self.fc, self.qkv, self.o, self.gate_up, self.down, self.lm,
+                                         self.lm_z)
         n = ops.draft_workspace_size(ops.tree_params(c.B, c.V, c.D, c.k, c.m, 1.0), self.dims)
         if n == 0:
             raise ValueError("invalid draft-head shape")

@@ -268,9 +268,9 @@ def draft_dims(hidden, hq, hkv, head_dim, inter, max_prefix) -> DraftDims:
     return DraftDims(int(hidden), int(hq), int(hkv), int(head_dim), int(inter), int(max_prefix))
 
 
-def draft_weights(embed, fc, qkv, o, gate_up, down, lm_head) -> DraftWeights:
+def draft_weights(embed, fc, qkv, o, gate_up, down, lm_head, lm_head_z=None) -> DraftWeights:
     """Device tensors: embed row-major [V, H]; the others packed (pack_lmhead_weight)."""
-    return DraftWeights(*[_ptr(t) for t in (embed, fc, qkv, o, gate_up, down, lm_head)])
+    return DraftWeights(*[_ptr(t) for t in (embed, fc, qkv, o, gate_up, down, lm_head, lm_head_z)])
 
 
 def draft_workspace_size(p: TreeParams, dims: DraftDims) -> int:

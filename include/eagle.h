@@ -596,6 +596,10 @@ typedef struct {
     const void* gate_up;  /* [2 I, H]: gate rows, then up rows                    */
     const void* down;     /* [H, I]                                               */
     const void* lm_head;  /* [vocab, H] (the target's LM head)                    */
+    const void* lm_head_z;  /* the same in the z-packed form (EAGLE_W_ZPACKED, from
+                               eagle_lmhead_zpack_weight), or NULL: read instead of
+                               lm_head by depths of at most EAGLE_ZPACK_MAX_ROWS
+                               rows; 256-byte aligned                           */
 } eagle_draft_weights;
 
 /* Bytes of the draft workspace for p's batch/vocab/depth/k (0 if invalid).  It

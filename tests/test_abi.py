@@ -131,6 +131,32 @@ def test_packed_weight_size_and_rejects(lib):
     assert lib.eagle_lmhead_pack_weight(100, 256, 1, FAKE, FAKE + 8, None) == -6
 
 
+def test_zpacked_weight_size_and_rejects(lib):
+    """The z-packed form (EAGLE_W_ZPACKED): its size, the pack call's host checks, and the LM head's
+    refusal of the layout beyond the streaming kernel's rows or hidden size."""
+    F = (128256 + 63) // 64 * (4096 // 8)            # fragments of the 8B head
+    n = lib.eagle_lmhead_zpack_bytes(128256, 4096)
+    slot = (F + 16 + 255) // 256 * 256
+    raw = (slot + F * 768 + 16 + 255) // 256 * 256
+    assert n == raw + F * 1024
+    assert lib.eagle_lmhead_zpack_bytes(100, 100) == 0          # hidden % 128
+    assert lib.eagle_lmhead_zpack_bytes(100, 16512) == 0        # hidden above 16384
+    assert lib.eagle_lmhead_zpack_weight(100, 100, FAKE, FAKE, None, None) == -2
+    assert lib.eagle_lmhead_zpack_weight(100, 256, None, FAKE, None, None) == -1
+    assert lib.eagle_lmhead_zpack_weight(100, 256, FAKE, FAKE + 16, None, None) == -6   # w_z 256-aligned
+    assert lib.eagle_lmhead_zpack_weight(100, 256, FAKE + 8, FAKE, None, None) == -6    # w 16-aligned
+    assert lib.eagle_lmhead_zpack_weight(100, 256, FAKE, FAKE, FAKE + 2, None) == -6    # count word
+    f = lib.eagle_lmhead_softmax
+    tail = (1.0, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None, None)
+    assert f(193, 128, 500, 1, FAKE, FAKE, 2, *tail) == -2      # z-packed: at most 192 rows
+    assert f(10, 16512, 500, 1, FAKE, FAKE, 2, *tail) == -2     # ... and hidden <= 16384
+    assert f(10, 128, 500, 0, FAKE, FAKE, 2, *tail) == -3       # ... bf16 only
+    assert f(10, 128, 500, 1, FAKE, FAKE, 2, *tail[:-3], 10, None, None) == -4   # the shape passes
+    g = lib.eagle_lmhead_softmax_compact
+    ctail = (1.0, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None, None)
+    assert g(193, 128, 500, FAKE, FAKE, 2, *ctail) == -2
+
+
 def test_mask_gather_accept_reject(lib):
     assert lib.eagle_build_tree_mask(1, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
     assert lib.eagle_build_tree_mask(1, 300, FAKE, FAKE, FAKE, FAKE, FAKE, None, None) == -2
@@ -228,6 +254,8 @@ def test_draft_rejects(lib):
     assert f(*args(0, ws=size - 256)) == -4
     assert f(*args(0, wts=L.DraftWeights(*([FAKE] * 6 + [None])))) == -1
     assert f(*args(0, wts=L.DraftWeights(*([FAKE + 8] + [FAKE] * 6)))) == -6
+    assert f(*args(0, wts=L.DraftWeights(*([FAKE] * 7 + [FAKE + 16])))) == -6   # z-packed head: 256-aligned
+    assert f(*args(0, ws=size - 256, wts=L.DraftWeights(*([FAKE] * 8)))) == -4   # ... accepted otherwise
     assert f(*args(1, ptrs=[FAKE] * 5 + [None, FAKE])) == -1                # pool_tok needed below the root
     assert f(*args(0, ws=size - 256, ptrs=[FAKE] * 5 + [None, FAKE])) == -4  # ... but not at the root
     assert f(*args(0, ptrs=[None] + [FAKE] * 6)) == -1
