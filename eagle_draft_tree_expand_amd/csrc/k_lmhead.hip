@@ -98,24 +98,29 @@ EDEV float row16_max(float v) {
 }
 
 // Decode one z-packed fragment's lane registers to its 8 bf16 (layout in
-// eagle.h).  v is the 16-byte load of the lane: a coded fragment's is read from
-// 4 bytes before the lane's 12 (so v = (-, low bytes 0..3, low bytes 4..7,
-// codes)); a raw fragment's is its 16 bytes (high bytes 4..7, low bytes 0..3,
-// low bytes 4..7, high bytes 0..3).  A coded weight's high byte is base plus
-// the low three bits of its code (no carry out of a byte: base + 7 <= 127),
-// plus the code's top bit moved to bit 7; hb = the fragment's header byte.
+// eagle.h).  v is the 16-byte load of the lane: a raw fragment's 16 bytes (low
+// bytes of weights 0..3, of 4..7, high bytes of 0..3, of 4..7); a coded
+// fragment's 12 bytes from the lane's own position (low bytes 0..3, 4..7,
+// codes, then 4 bytes of the next lane), except the last lane, which reads
+// from 4 bytes before its 12 so that no load leaves the fragment; `last` marks
+// that lane, whose words are rotated into place.  A coded weight's high byte
+// is base plus the low three bits of its code (no carry out of a byte: base +
+// 7 <= 127), plus the code's top bit moved to bit 7; hb = the fragment's
+// header byte.
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-EDEV u32x4 zdecode(u32x4 v, uint32_t hb) {
+EDEV u32x4 zdecode(u32x4 v, uint32_t hb, bool last) {
+  const bool raw = (hb & 0x80u) != 0;
+  if (!raw && last) v = u32x4{v.y, v.z, v.w, v.x};
   const uint32_t b4 = (hb & 0x7fu) * 0x01010101u;
-  const uint32_t c = v.w;
+  const uint32_t c = v.z;
   uint32_t ha = (c & 0x07070707u) + ((c << 4) & 0x80808080u) + b4;
   uint32_t hh = ((c >> 4) & 0x07070707u) + (c & 0x80808080u) + b4;
-  if (hb & 0x80u) {
-    ha = v.w;
-    hh = v.x;
+  if (raw) {
+    ha = v.z;
+    hh = v.w;
   }
-  return u32x4{__builtin_amdgcn_perm(ha, v.y, 0x05010400u), __builtin_amdgcn_perm(ha, v.y, 0x07030602u),
-               __builtin_amdgcn_perm(hh, v.z, 0x05010400u), __builtin_amdgcn_perm(hh, v.z, 0x07030602u)};
+  return u32x4{__builtin_amdgcn_perm(ha, v.x, 0x05010400u), __builtin_amdgcn_perm(ha, v.x, 0x07030602u),
+               __builtin_amdgcn_perm(hh, v.y, 0x05010400u), __builtin_amdgcn_perm(hh, v.y, 0x07030602u)};
 }
 
 // WL: the weight layout (EAGLE_W_ROWMAJOR, EAGLE_W_PACKED or EAGLE_W_ZPACKED).
@@ -205,15 +210,17 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
   };
   auto zbyte = [&](const uint32_t* h, int j) -> uint32_t { return (h[j >> 2] >> (8 * (j & 3))) & 0xffu; };
   // Buffer loads: the fragment's byte offset in a scalar register, the lane's
-  // offset (12 or 16 bytes a lane) in a vector register; the whole z-packed
-  // weight is below 4 GB (the host checks).
-  const uint32_t zlc = (uint32_t)lane * 12u, zlr = (uint32_t)lane * 16u;
+  // offset (12 or 16 bytes a lane; the last lane of a coded fragment 4 bytes
+  // early) in a vector register; the whole z-packed weight is below 4 GB (the
+  // host checks).
+  const bool zlast = lane == 63;
+  const uint32_t zlc = zlast ? 63u * 12u - 4u : (uint32_t)lane * 12u, zlr = (uint32_t)lane * 16u;
   const __amdgpu_buffer_rsrc_t zrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)zb, (short)0, ZP ? (int)(uint32_t)zl.bytes : 0, 0x00020000);
   auto zload = [&](int step, int j, uint32_t hb) -> u32x4 {
     const uint32_t f = ((uint32_t)((j < 8) ? zg0 : zg1) * (uint32_t)nch + (uint32_t)(c0 + step)) * 8u + (uint32_t)(j & 7);
     const bool raw = (hb & 0x80u) != 0;
-    const uint32_t so = raw ? (uint32_t)zl.raw_off + f * 1024u : (uint32_t)zl.slot_off + f * 768u - 4u;
+    const uint32_t so = raw ? (uint32_t)zl.raw_off + f * 1024u : (uint32_t)zl.slot_off + f * 768u;
     return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(zrs, (int)(raw ? zlr : zlc), (int)so, 2));
   };
   if (ZP) {
@@ -271,7 +278,7 @@ __global__ __launch_bounds__(kLmThreads) void lmhead_bf16_kernel(int rows, int H
       for (int t = 0; t < NT; ++t) {
         const int j = (t >> 2) * 8 + ks * 4 + (t & 3);
         B8 bb;
-        bb.w = ZP ? zdecode(wf[j], zbyte(hc, j)) : wf[j];
+        bb.w = ZP ? zdecode(wf[j], zbyte(hc, j), zlast) : wf[j];
         // z-packed: the decode has consumed the fragment's registers, so its next
         // load can go out before the MFMAs
         if (ZP && more) wf[j] = zload(step + 1, j, zbyte(hn, j));
@@ -1025,7 +1032,7 @@ __global__ __launch_bounds__(256) void zpack_w_kernel(int V, int H, const uint16
     if (raw) {
       const uint32_t h0 = hi[0] | hi[1] << 8 | hi[2] << 16 | hi[3] << 24;
       const uint32_t h1 = hi[4] | hi[5] << 8 | hi[6] << 16 | hi[7] << 24;
-      *reinterpret_cast<u32x4*>(wz + zl.raw_off + f * 1024 + l * 16) = u32x4{h1, l0, l1, h0};
+      *reinterpret_cast<u32x4*>(wz + zl.raw_off + f * 1024 + l * 16) = u32x4{l0, l1, h0, h1};
     } else {
       uint32_t codes = 0u;
 #pragma unroll

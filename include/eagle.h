@@ -127,9 +127,9 @@ typedef enum { EAGLE_W_ROWMAJOR = 0, EAGLE_W_PACKED = 1, EAGLE_W_ZPACKED = 2 } e
  *                              codes (weight i < 4 in the low nibble of byte i,
  *                              weight i >= 4 in the high nibble of byte i - 4);
  *   raw area (256-aligned)     1024 bytes per fragment, lane l's 16 at 16 l: the
- *                              high bytes of weights 4..7, the low bytes of
- *                              0..3, of 4..7, the high bytes of 0..3 (written
- *                              for raw fragments only).
+ *                              low bytes of weights 0..3, of 4..7, the high
+ *                              bytes of 0..3, of 4..7 (written for raw
+ *                              fragments only).
  * The raw area is sized for every fragment to be raw, so the form takes about
  * 1.75 times the PACKED bytes in memory; a launch reads only each fragment's
  * own form.  Only eagle_lmhead_softmax and eagle_lmhead_softmax_compact with
