@@ -158,28 +158,38 @@ __global__ __launch_bounds__(kExpThreads) void expand_scan_kernel(
 #pragma unroll
     for (int j = 0; j < kPer; ++j) nfin += __popcll(__ballot(uk[j] != 0u));
   }
+  // The bound is searched on the top 16 bits of the lane maxima (a 16-bit
+  // bucket holding the KP-th largest; a lower bound all the same, at a cost of
+  // a few more candidates), and the candidates take their LDS positions from a
+  // per-wave counter, so a group of 64 elements with none at or above the
+  // bound costs one compare.
   uint32_t thr = 0;
   if (nfin >= KP) {
+    const uint32_t lm16 = lmax >> 16;
 #pragma unroll
-    for (int bit = 31; bit >= 0; --bit) {
+    for (int bit = 15; bit >= 0; --bit) {
       const uint32_t c = thr | (1u << bit);
-      if (__popcll(__ballot(lmax >= c)) >= (unsigned)KP) thr = c;
+      if (__popcll(__ballot(lm16 >= c)) >= (unsigned)KP) thr = c;
     }
+    thr <<= 16;
   }
   thr = max(thr, 1u);
   __shared__ uint64_t cand[4][64];
-  int total = 0;
+  __shared__ int ccount[4];
+  if (lane == 0) ccount[wave] = 0;
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
 #pragma unroll
   for (int j = 0; j < kPer; ++j) {
-    const bool take = uk[j] >= thr;
-    const uint64_t mask = __ballot(take);
-    const int pos = total + (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
-    if (take && pos < 64) cand[wave][pos] = ((uint64_t)uk[j] << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx_of(j));
-    total += __popcll(mask);
+    if (uk[j] >= thr) {
+      const int pos = atomicAdd(&ccount[wave], 1);
+      if (pos < 64) cand[wave][pos] = ((uint64_t)uk[j] << 32) | (uint64_t)(0xffffffffu - (uint32_t)idx_of(j));
+    }
   }
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  const int total = ccount[wave];
   if (total <= 64) {
-    __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-    __builtin_amdgcn_wave_barrier();
     const uint64_t mine = lane < total ? cand[wave][lane] : 0ull;
     int r = 0;
     for (int c = 0; c < total; ++c) r += cand[wave][c] > mine ? 1 : 0;
